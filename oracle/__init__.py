@@ -1,0 +1,179 @@
+"""CPU oracle for im2win convolution (ctypes wrapper around liboracle.so).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use this package; the HIP library never does. It shares no
+code with the HIP path. What each function computes, and the readings of the
+pages it rests on, are stated in oracle.c.
+
+All float inputs are passed as float32 arrays: fp16 inputs are widened to
+float32 first, which is exact, so the oracle multiplies the very values the
+GPU multiplies and accumulates them in float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(_p)
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a), dtype=np.float32)
+
+
+class Oracle:
+    """The oracle's functions bound to one compiled liboracle.so."""
+
+    def __init__(self, path: str):
+        L = ctypes.CDLL(path)
+        L.oracle_out_extent.argtypes = [_i, _i, _i]
+        L.oracle_out_extent.restype = _i
+        for f in (L.oracle_im2win_elems, L.oracle_im2col_elems):
+            f.argtypes = [_i] * 7
+            f.restype = _i64
+        L.oracle_im2win_pack.argtypes = [_p, _p] + [_i] * 8
+        L.oracle_im2win_pack.restype = None
+        L.oracle_conv_direct_f64.argtypes = [_p, _p, _p, _p] + [_i] * 8
+        L.oracle_conv_direct_f32acc.argtypes = [_p, _p, _p] + [_i] * 8
+        L.oracle_conv_im2win_f64.argtypes = [_p, _p, _p] + [_i] * 8
+        L.oracle_conv_im2win_f32acc.argtypes = [_p, _p, _p] + [_i] * 8
+        L.oracle_conv_points_f64.argtypes = [_p, _p, _p, _i64, _p, _p] + [_i] * 8
+        for f in (L.oracle_conv_direct_f64, L.oracle_conv_direct_f32acc,
+                  L.oracle_conv_im2win_f64, L.oracle_conv_im2win_f32acc,
+                  L.oracle_conv_points_f64):
+            f.restype = None
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = _i
+        self.L = L
+        self.path = path
+
+    # ---- sizes -----------------------------------------------------------
+    def out_extent(self, n_in: int, f: int, s: int) -> int:
+        return self.L.oracle_out_extent(n_in, f, s)
+
+    def out_hw(self, Hi, Wi, Hf, Wf, s):
+        return self.out_extent(Hi, Hf, s), self.out_extent(Wi, Wf, s)
+
+    def im2win_elems(self, N, Ci, Hi, Wi, Hf, Wf, s) -> int:
+        return self.L.oracle_im2win_elems(N, Ci, Hi, Wi, Hf, Wf, s)
+
+    def im2col_elems(self, N, Ci, Hi, Wi, Hf, Wf, s) -> int:
+        return self.L.oracle_im2col_elems(N, Ci, Hi, Wi, Hf, Wf, s)
+
+    # ---- transform -------------------------------------------------------
+    def im2win_pack(self, x: np.ndarray, Hf: int, Wf: int, s: int) -> np.ndarray:
+        """Bit copy of x (N, Ci, Hi, Wi) into the im2win tensor (N, Ci, Ho, Wi*Hf).
+
+        Any 2- or 4-byte element type (float16/uint16/float32/uint32); the
+        result has x's dtype.
+        """
+        x = np.ascontiguousarray(x)
+        N, Ci, Hi, Wi = x.shape
+        Ho, Wo = self.out_hw(Hi, Wi, Hf, Wf, s)
+        if Ho == 0 or Wo == 0:
+            raise ValueError("filter larger than input")
+        ws = np.empty((N, Ci, Ho, Wi * Hf), dtype=x.dtype)
+        self.L.oracle_im2win_pack(_ptr(x), _ptr(ws), N, Ci, Hi, Wi, Hf, Wf, s,
+                                  x.dtype.itemsize)
+        return ws
+
+    # ---- convolution -----------------------------------------------------
+    def _dims(self, x, w, s):
+        N, Ci, Hi, Wi = x.shape
+        Co, Ci2, Hf, Wf = w.shape
+        if Ci2 != Ci:
+            raise ValueError("channel mismatch")
+        Ho, Wo = self.out_hw(Hi, Wi, Hf, Wf, s)
+        if Ho == 0 or Wo == 0:
+            raise ValueError("filter larger than input")
+        return N, Ci, Hi, Wi, Co, Hf, Wf, Ho, Wo
+
+    def conv_direct(self, x, w, s: int, with_absdot: bool = False):
+        """Direct convolution in float64: y (N, Co, Ho, Wo) [, sum |x*w| per output]."""
+        x, w = _f32(x), _f32(w)
+        N, Ci, Hi, Wi, Co, Hf, Wf, Ho, Wo = self._dims(x, w, s)
+        y = np.empty((N, Co, Ho, Wo), dtype=np.float64)
+        a = np.empty_like(y) if with_absdot else None
+        self.L.oracle_conv_direct_f64(_ptr(x), _ptr(w), _ptr(y), _ptr(a),
+                                      N, Ci, Hi, Wi, Co, Hf, Wf, s)
+        return (y, a) if with_absdot else y
+
+    def conv_direct_f32acc(self, x, w, s: int):
+        x, w = _f32(x), _f32(w)
+        N, Ci, Hi, Wi, Co, Hf, Wf, Ho, Wo = self._dims(x, w, s)
+        y = np.empty((N, Co, Ho, Wo), dtype=np.float32)
+        self.L.oracle_conv_direct_f32acc(_ptr(x), _ptr(w), _ptr(y), N, Ci, Hi, Wi, Co, Hf, Wf, s)
+        return y
+
+    def _im2win_dims(self, ws, w, Hi, Wi, s):
+        N, Ci = ws.shape[0], ws.shape[1]
+        Co, Ci2, Hf, Wf = w.shape
+        Ho, Wo = self.out_hw(Hi, Wi, Hf, Wf, s)
+        if Ci2 != Ci or ws.shape != (N, Ci, Ho, Wi * Hf):
+            raise ValueError("im2win tensor does not match the shapes")
+        return N, Ci, Co, Hf, Wf, Ho, Wo
+
+    def conv_im2win(self, ws, w, Hi: int, Wi: int, s: int):
+        """im2win convolution (float64) on a packed tensor from im2win_pack."""
+        ws, w = _f32(ws), _f32(w)
+        N, Ci, Co, Hf, Wf, Ho, Wo = self._im2win_dims(ws, w, Hi, Wi, s)
+        y = np.empty((N, Co, Ho, Wo), dtype=np.float64)
+        self.L.oracle_conv_im2win_f64(_ptr(ws), _ptr(w), _ptr(y), N, Ci, Hi, Wi, Co, Hf, Wf, s)
+        return y
+
+    def conv_im2win_f32acc(self, ws, w, Hi: int, Wi: int, s: int):
+        ws, w = _f32(ws), _f32(w)
+        N, Ci, Co, Hf, Wf, Ho, Wo = self._im2win_dims(ws, w, Hi, Wi, s)
+        y = np.empty((N, Co, Ho, Wo), dtype=np.float32)
+        self.L.oracle_conv_im2win_f32acc(_ptr(ws), _ptr(w), _ptr(y), N, Ci, Hi, Wi, Co,
+                                         Hf, Wf, s)
+        return y
+
+    def conv_points(self, x, w, s: int, idx: np.ndarray):
+        """Direct convolution (float64) at flat NCHW output indices: (y, absdot)."""
+        x, w = _f32(x), _f32(w)
+        N, Ci, Hi, Wi, Co, Hf, Wf, Ho, Wo = self._dims(x, w, s)
+        idx = np.ascontiguousarray(idx, dtype=np.int64)
+        if idx.size and (idx.min() < 0 or idx.max() >= N * Co * Ho * Wo):
+            raise ValueError("output index out of range")
+        y = np.empty(idx.shape, dtype=np.float64)
+        a = np.empty(idx.shape, dtype=np.float64)
+        self.L.oracle_conv_points_f64(_ptr(x), _ptr(w), _ptr(idx), idx.size, _ptr(y), _ptr(a),
+                                      N, Ci, Hi, Wi, Co, Hf, Wf, s)
+        return y, a
+
+    def num_threads(self) -> int:
+        return self.L.oracle_num_threads()
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from oracle.c (compiled with gcc on first use if absent)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _default = Oracle(_build.LIB)
+    return _default
+
+
+def __getattr__(name):
+    # Module-level shortcuts: oracle.conv_direct(...) == oracle.default().conv_direct(...)
+    if name.startswith("_"):
+        raise AttributeError(name)
+    return getattr(default(), name)

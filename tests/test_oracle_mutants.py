@@ -1,0 +1,72 @@
+"""Plant one plausible mistake at a time in a copy of the oracle and check
+that the pins catch it (CPU only).
+
+Each mutant is a textual edit of oracle.c -- a transposed index, a dropped
+term, a flipped filter, a missing stride, a wrong extent -- compiled with the
+oracle's own flags into a temporary library. The pins run in a child process
+(a mutant may read outside its arrays) and must report a failure.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+sys.path.insert(0, ROOT)
+
+from oracle import build as obuild  # noqa: E402
+
+MUTANTS = [
+    ("x index: kh and kw swapped",
+     "(double)x[xi(n, ci, ho * s + kh, wo * s + kw",
+     "(double)x[xi(n, ci, ho * s + kw, wo * s + kh"),
+    ("filter flipped (true convolution instead of correlation)",
+     "(double)w[wi(co, ci, kh, kw, Ci, Hf, Wf)]",
+     "(double)w[wi(co, ci, Hf - 1 - kh, Wf - 1 - kw, Ci, Hf, Wf)]"),
+    ("stride missing on the column axis",
+     "(double)x[xi(n, ci, ho * s + kh, wo * s + kw",
+     "(double)x[xi(n, ci, ho * s + kh, wo + kw"),
+    ("first column of every window dropped",
+     "for (int kw = 0; kw < Wf; ++kw) {\n                double p",
+     "for (int kw = 1; kw < Wf; ++kw) {\n                double p"),
+    ("output extent rounded up",
+     "return (in - f) / s + 1;",
+     "return (in - f + s - 1) / s + 1;"),
+    ("im2win row stored row by row instead of column by column",
+     "int64_t out = ((plane * Ho + ho) * Wi + w) * Hf + kh;",
+     "int64_t out = ((plane * Ho + ho) * Hf + kh) * Wi + w;"),
+    ("im2win source row ignores the stride",
+     "int64_t in = (plane * Hi + (int64_t)ho * s + kh) * Wi + w;",
+     "int64_t in = (plane * Hi + (int64_t)ho + kh) * Wi + w;"),
+    ("im2win window read in filter order",
+     "acc += (double)win[kw * Hf + kh] *",
+     "acc += (double)win[kh * Wf + kw] *"),
+    ("absolute-product sum keeps the sign",
+     "aacc += fabs(p);",
+     "aacc += p;"),
+    ("sampled output index decoded with Ho and Wo swapped",
+     "int ho = (int)((o / Wo) % Ho);",
+     "int ho = (int)((o / Ho) % Wo);"),
+    ("output written with rows and columns transposed",
+     "int64_t o = (((int64_t)n * Co + co) * Ho + ho) * Wo + wo;",
+     "int64_t o = (((int64_t)n * Co + co) * Wo + wo) * Ho + ho;"),
+    ("float-accumulator im2win path multiplies the transposed filter tap",
+     "acc += win[kw * Hf + kh] * w[wi(co, ci, kh, kw, Ci, Hf, Wf)];",
+     "acc += win[kw * Hf + kh] * w[wi(co, ci, kw, kh, Ci, Hf, Wf)];"),
+]
+
+
+@pytest.mark.parametrize("desc,find,repl", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(desc, find, repl, tmp_path):
+    with open(obuild.SRC) as f:
+        src = f.read()
+    assert find in src, f"mutation anchor not found: {find!r}"
+    mutant_c = tmp_path / "oracle_mutant.c"
+    mutant_c.write_text(src.replace(find, repl, 1))
+    lib = obuild.compile_c(str(mutant_c), str(tmp_path / "liboracle_mutant.so"))
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, os.path.join(HERE, "oracle_pins.py"), lib],
+                       capture_output=True, text=True, timeout=300, env=env, cwd=ROOT)
+    assert r.returncode != 0, f"no pin caught: {desc}\n{r.stdout}\n{r.stderr}"
