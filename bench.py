@@ -1,0 +1,239 @@
+"""Benchmark: im2win convolution TFLOPS and workspace bytes on one MI355X.
+
+A step is one forward convolution call over one batch of seeded synthetic
+input already resident in HBM: the im2win transform, the filter staging, the
+windowed dot products and the fp32 output store, all inside the library's HIP
+kernels. The headline workload is the cv1 layer of Table I ("Enabling
+Memory-efficient Im2win Convolution with Multi-precision Support on GPU CUDA
+and Tensor Cores"): N=32, 3x227x227 input, 96 11x11 filters, stride 4, fp32
+on the vector ALUs. The other Table I layers (cv5 fp32 N=1; cv5, cv3, cv4
+fp16 on the matrix cores) are timed the same way and reported under
+"layers".
+
+Prints ONE JSON line on stdout (rank 0); progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+# Published MI355X peaks (dense) used for the roofline fractions.
+PEAK_FP32_VECTOR_TFLOPS = 157.3   # 256 CU x 2.4 GHz x 256 flop/clk (packed FMA)
+PEAK_FP16_MFMA_TFLOPS = 2516.6    # dense fp16 matrix
+PEAK_HBM_GBS = 8000.0
+
+HEADLINE = "cv1_f32_n32"
+LAYER_KEYS = ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64", "cv4_f16_n64"]
+KERNEL_SOURCES = ["conv_f32.hip", "conv_f16.hip", "pack.hip", "api.hip", "common.hpp"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def flops(sh, Ho, Wo) -> int:
+    return 2 * sh.N * sh.Co * Ho * Wo * sh.Ci * sh.Hf * sh.Wf
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "memory_efficient_im2win_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def time_layer(sh, mode, steps, warmup):
+    """Returns dict with per-launch-averaged ms and workspace bytes."""
+    import torch
+    import memory_efficient_im2win_amd as m
+    dev = torch.device("cuda:0")
+    x, w = workloads.make_inputs(sh, seed=0)
+    xt = torch.from_numpy(x).to(dev)
+    wt = torch.from_numpy(w).to(dev)
+    Ho, Wo = m.output_dims(sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s)
+    y = torch.empty((sh.N, sh.Co, Ho, Wo), dtype=torch.float32, device=dev)
+    ws = None
+    wsb = 0
+    if mode == "materialized":
+        wsb = m.workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        m.conv2d(xt, wt, sh.s, ws=ws, out=y)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record()
+    for i in range(steps):
+        starts[i].record()
+        m.conv2d(xt, wt, sh.s, ws=ws, out=y)
+        ends[i].record()
+    t_all1.record()
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    total_ms = t_all0.elapsed_time(t_all1)
+    f = flops(sh, Ho, Wo)
+    res = {
+        "ms_per_step": total_ms / steps,
+        "ms_per_launch_avg": float(np.mean(per)),
+        "ms_per_launch_min": float(np.min(per)),
+        "tflops": f / (total_ms / steps) / 1e9,
+        "flops": f,
+        "workspace_bytes": wsb,
+        "Ho": Ho, "Wo": Wo,
+    }
+    del ws, y, xt, wt
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(sh, budget_s=12.0):
+    """The oracle (plain C loops, fp64 accumulation) on the host cores, on as
+    many images of the workload as fit the time budget; scaled to TFLOPS."""
+    import oracle
+    O = oracle.default()
+    x, w = workloads.make_inputs(sh, seed=0)
+    Ho, Wo = O.out_hw(sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s)
+    t0 = time.perf_counter()
+    O.conv_direct(x[:1], w, sh.s)
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(sh.N, budget_s / max(t1, 1e-6))))
+    t0 = time.perf_counter()
+    O.conv_direct(x[:n], w, sh.s)
+    dt = time.perf_counter() - t0
+    f = 2 * n * sh.Co * Ho * Wo * sh.Ci * sh.Hf * sh.Wf
+    return {
+        "value": f / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": O.num_threads(),
+        "kind": "oracle",
+        "sample": f"{n} of {sh.N} images of {sh.name} ({sh.dtype} inputs, fp64 accumulation), "
+                  f"{dt:.2f} s",
+    }
+
+
+def load_traffic(key, mode):
+    """HBM traffic measured with rocprofv3 counters for the current kernel
+    sources, or None (no measurement, or the kernels changed since)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    ent = d.get(f"{key}:{mode}")
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(workloads.BY_KEY))
+    ap.add_argument("--mode", default="fused", choices=["fused", "materialized"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-layers", action="store_true", help="time only the headline workload")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the im2win forward convolution needs no "
+              "collective and this build runs on a single MI355X; use --gpus 1.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    import memory_efficient_im2win_amd as m
+    m.load_library()
+
+    sh = workloads.BY_KEY[args.workload]
+    log(f"[bench] headline {sh.describe()} mode={args.mode} steps={args.steps} warmup={args.warmup}")
+    head = time_layer(sh, args.mode, args.steps, args.warmup)
+    log(f"[bench] headline {head['tflops']:.2f} TFLOP/s, {head['ms_per_step']*1e3:.1f} us/step")
+
+    layers = {}
+    if not args.no_layers:
+        for key in LAYER_KEYS:
+            lsh = workloads.BY_KEY[key]
+            entry = {}
+            for mode in ("fused", "materialized"):
+                r = time_layer(lsh, mode, max(5, args.steps // 2), 3)
+                peak = PEAK_FP32_VECTOR_TFLOPS if lsh.dtype == "f32" else PEAK_FP16_MFMA_TFLOPS
+                entry[mode] = {"tflops": round(r["tflops"], 3), "us_per_call": round(r["ms_per_step"] * 1e3, 2),
+                               "frac_of_peak": round(r["tflops"] / peak, 4),
+                               "workspace_bytes": r["workspace_bytes"]}
+                log(f"[bench] {key} {mode}: {r['tflops']:.2f} TFLOP/s "
+                    f"({r['ms_per_step']*1e3:.1f} us/call, ws {r['workspace_bytes']} B)")
+            layers[key] = entry
+
+    # Roofline of the dominant kernel. In the fused mode one call is exactly
+    # one kernel launch, so the per-launch event time is that kernel's time.
+    is_f32 = sh.dtype == "f32"
+    achieved = head["flops"] / (head["ms_per_launch_avg"] * 1e-3) / 1e12
+    peak = PEAK_FP32_VECTOR_TFLOPS if is_f32 else PEAK_FP16_MFMA_TFLOPS
+    roofline = {
+        "bound": "alu" if is_f32 else "mfma",
+        "achieved": round(achieved, 3),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": load_traffic(args.workload, args.mode),
+        "kernel": "conv_f32_kernel" if is_f32 else "conv_f16_kernel",
+        "launch_avg_us": round(head["ms_per_launch_avg"] * 1e3, 2),
+    }
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(sh)
+        log(f"[bench] cpu oracle {cpu['value']*1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "conv TFLOPS (fp32 VALU, fp16 MFMA) + workspace bytes on cv1-cv5 shapes",
+        "value": round(head["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if is_f32 else "f16 in, f32 accumulate",
+        "data": "synthetic (seeded iid U[-1,1] at the Table I layer shapes)",
+        "config": {
+            "workload": f"{sh.name} forward conv, N={sh.N}, {sh.dtype}: input {sh.Ci}x{sh.Hi}x{sh.Wi}, "
+                        f"filters {sh.Co}x{sh.Ci}x{sh.Hf}x{sh.Wf}, stride {sh.s}, "
+                        f"output {sh.Co}x{head['Ho']}x{head['Wo']}",
+            "mode": args.mode,
+            "workspace_bytes": head["workspace_bytes"],
+            "global_batch": sh.N,
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "layers": layers,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,123 @@
+/*
+ * im2win convolution for AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * The operation is the forward convolution of "Enabling Memory-efficient
+ * Im2win Convolution with Multi-precision Support on GPU CUDA and Tensor
+ * Cores" (Abstract; Fig. 1; Table I): an NCHW input of N images with Ci
+ * channels of Hi x Wi, filters Co x Ci x Hf x Wf, one stride s for both axes,
+ * and an NCHW output N x Co x Ho x Wo, with
+ *     Ho = floor((Hi - Hf) / s) + 1,   Wo = floor((Wi - Wf) / s) + 1,
+ *     y[n][co][ho][wo] = sum over ci, kh, kw of
+ *                        x[n][ci][ho*s + kh][wo*s + kw] * w[co][ci][kh][kw]
+ * (cross-correlation: no filter flip, no padding, no dilation, no bias; the
+ * pages' layers are all unpadded). Full precision runs on the vector ALUs,
+ * half precision on the matrix cores, as the same page's Abstract splits the
+ * work between CUDA cores and tensor cores.
+ *
+ * The im2win transform is the one of "Im2win: Memory Efficient Convolution
+ * On SIMD Architectures" (Abstract): each row of dot-product windows is
+ * flattened, distinct elements only, into one row. Here the row for
+ * (n, ci, ho) holds input rows ho*s .. ho*s+Hf-1 over all Wi columns, column
+ * by column:
+ *     ws[n][ci][ho][w*Hf + kh] = x[n][ci][ho*s + kh][w]
+ * so the window of output (ho, wo) is the single contiguous run of Wf*Hf
+ * elements starting at wo*s*Hf. The workspace is N*Ci*Ho*(Wi*Hf) elements.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are dense, contiguous, caller-owned DEVICE memory (hipMalloc,
+ *    torch). x is N x Ci x Hi x Wi, w is Co x Ci x Hf x Wf, y is
+ *    N x Co x Ho x Wo, all row-major. Buffers must not overlap.
+ *  - fp16 data is IEEE binary16, passed as uint16_t bit patterns. Outputs of
+ *    both convolutions are fp32; the fp16 path multiplies binary16 values
+ *    exactly and accumulates in fp32.
+ *  - `stream` is a hipStream_t (NULL: the legacy default stream). Work is
+ *    enqueued and the call returns without synchronising. The library
+ *    allocates no memory and keeps no state between calls; concurrent calls
+ *    on different streams are safe when their output buffers differ.
+ *  - Shape limits: every dimension >= 1, Hf <= Hi, Wf <= Wi, s >= 1, and the
+ *    per-image element counts Ci*Hi*Wi, Co*Ho*Wo, Ci*Ho*Wi*Hf and the filter
+ *    size Co*Ci*Hf*Wf each below 2^31.
+ *  - Argument errors are reported synchronously (no work is enqueued); a
+ *    failed kernel launch returns IM2WIN_ELAUNCH. Faults inside a kernel
+ *    surface at the caller's next synchronisation, as for any HIP kernel.
+ */
+#ifndef IM2WIN_H
+#define IM2WIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    IM2WIN_OK = 0,
+    IM2WIN_EINVAL = -1,     /* bad shape, stride, element size or NULL pointer */
+    IM2WIN_EWORKSPACE = -2, /* workspace given but smaller than one image's im2win rows */
+    IM2WIN_ELAUNCH = -3     /* a kernel launch failed (message: hipGetLastError) */
+} im2win_status;
+
+/*
+ * Bytes of the im2win tensor for the whole batch:
+ *     N * Ci * Ho * (Wi * Hf) * elem_bytes.
+ * Returns 0 if the shape is invalid or elem_bytes is not 2 or 4.
+ * Pure host arithmetic; needs no GPU.
+ */
+size_t im2win_workspace_bytes(int N, int Ci, int Hi, int Wi, int Hf, int Wf, int s,
+                              size_t elem_bytes);
+
+/*
+ * Output extents Ho, Wo (either pointer may be NULL). Returns IM2WIN_OK or
+ * IM2WIN_EINVAL. Pure host arithmetic.
+ */
+int im2win_output_dims(int Hi, int Wi, int Hf, int Wf, int s, int *Ho, int *Wo);
+
+/*
+ * The im2win transform (Im2win ... SIMD Architectures, Abstract), as a bit
+ * copy of elem_bytes-wide elements (2 or 4; NaN payloads, infinities and
+ * subnormals pass unchanged):
+ *     ws[n][ci][ho][w*Hf + kh] = x[n][ci][ho*s + kh][w]
+ * x: N x Ci x Hi x Wi; ws: im2win_workspace_bytes(...) bytes, written fully.
+ * Wf only determines Ho via the shape check. HBM-bound copy kernel.
+ */
+int im2win_pack(const void *x, void *ws, int N, int Ci, int Hi, int Wi, int Hf, int Wf,
+                int s, size_t elem_bytes, void *stream);
+
+/*
+ * fp32 convolution on the vector ALUs ("full precision on CUDA cores" in the
+ * GPU page's Abstract). x, w fp32; y fp32 (written fully).
+ *
+ * Workspace selects how the im2win rows reach the kernel:
+ *  - ws == NULL and ws_bytes == 0: fused. Each workgroup builds the im2win
+ *    rows it needs in LDS straight from x; no HBM workspace.
+ *  - ws_bytes >= im2win_workspace_bytes(N, ..., 4): materialised. The whole
+ *    batch is packed into ws (im2win_pack), then convolved from it.
+ *  - one image's im2win bytes <= ws_bytes < the batch's: materialised, in
+ *    chunks of floor(ws_bytes / one image's bytes) images, in stream order.
+ *  - otherwise (or ws == NULL with ws_bytes != 0): IM2WIN_EWORKSPACE.
+ * Both modes compute each output as the same windowed dot product; their
+ * fp32 rounding is the same.
+ */
+int conv2d_im2win_fp32(const float *x, const float *w, float *y, void *ws, size_t ws_bytes,
+                       int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s,
+                       void *stream);
+
+/*
+ * fp16-input convolution on the matrix cores ("half precision on tensor
+ * cores", same Abstract): x, w binary16; products exact, fp32 accumulation;
+ * y fp32 (written fully). Workspace rules as for conv2d_im2win_fp32, with
+ * im2win_workspace_bytes(..., 2).
+ */
+int conv2d_im2win_fp16(const uint16_t *x, const uint16_t *w, float *y, void *ws,
+                       size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf,
+                       int s, void *stream);
+
+/* Static, human-readable text for a status code. */
+const char *im2win_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IM2WIN_H */

@@ -1,0 +1,118 @@
+"""im2win convolution for AMD Instinct MI355X (gfx950).
+
+A thin binding over libim2win.so: it checks tensor dtypes, devices and
+layouts, allocates outputs with torch, and passes raw device pointers and
+torch's current HIP stream to the C ABI. Every step of the computation runs
+in the library's HIP kernels.
+
+    y = conv2d(x, w, stride)                 # fused: im2win rows built in LDS
+    y = conv2d(x, w, stride, ws=workspace)   # materialised im2win tensor
+    ws = pack(x, Hf, Wf, stride)             # the im2win transform itself
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import Im2winError, status_string  # noqa: F401
+
+__all__ = ["conv2d", "pack", "workspace_bytes", "output_dims", "Im2winError", "status_string",
+           "load_library"]
+
+
+def load_library():
+    """The loaded ctypes library (raises ImportError if it was not built)."""
+    return _lib.load()
+
+
+def output_dims(Hi: int, Wi: int, Hf: int, Wf: int, s: int):
+    ho, wo = ctypes.c_int(), ctypes.c_int()
+    _lib.check(_lib.load().im2win_output_dims(Hi, Wi, Hf, Wf, s, ctypes.byref(ho),
+                                              ctypes.byref(wo)), "output_dims")
+    return ho.value, wo.value
+
+
+def workspace_bytes(N, Ci, Hi, Wi, Hf, Wf, s, elem_bytes) -> int:
+    """Bytes of the im2win tensor of the whole batch (0 for an invalid shape)."""
+    return _lib.load().im2win_workspace_bytes(N, Ci, Hi, Wi, Hf, Wf, s, elem_bytes)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_tensor(t, name, dtypes, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def pack(x, Hf: int, Wf: int, s: int, out=None):
+    """The im2win tensor of x (N, Ci, Hi, Wi) as (N, Ci, Ho, Wi*Hf), same dtype.
+
+    Any 2- or 4-byte dtype works (the transform is a bit copy).
+    """
+    torch = _torch()
+    _check_tensor(x, "x", (torch.float16, torch.float32, torch.int16, torch.int32,
+                           torch.bfloat16, torch.uint16, torch.uint32), 4)
+    N, Ci, Hi, Wi = x.shape
+    Ho, _ = output_dims(Hi, Wi, Hf, Wf, s)
+    shape = (N, Ci, Ho, Wi * Hf)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    _lib.check(_lib.load().im2win_pack(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                       N, Ci, Hi, Wi, Hf, Wf, s, x.element_size(),
+                                       _stream_handle(x)), "im2win_pack")
+    return out
+
+
+def conv2d(x, w, stride: int = 1, ws=None, ws_bytes: int | None = None, out=None):
+    """Forward convolution (cross-correlation, no padding) of x (N,Ci,Hi,Wi)
+    with w (Co,Ci,Hf,Wf); fp32 output (N,Co,Ho,Wo).
+
+    float32 inputs run on the vector ALUs, float16 inputs on the matrix cores
+    (fp32 accumulation). With ``ws`` (a device tensor of at least one image's
+    im2win bytes) the im2win tensor is materialised in it, in chunks of as
+    many images as fit; without, the im2win rows are built in LDS.
+    """
+    torch = _torch()
+    _check_tensor(x, "x", (torch.float32, torch.float16), 4)
+    _check_tensor(w, "w", (x.dtype,), 4)
+    if w.device != x.device:
+        raise ValueError("x and w must be on the same device")
+    N, Ci, Hi, Wi = x.shape
+    Co, Ci2, Hf, Wf = w.shape
+    if Ci2 != Ci:
+        raise ValueError("x and w disagree on the input channel count")
+    Ho, Wo = output_dims(Hi, Wi, Hf, Wf, stride)
+    if out is None:
+        out = torch.empty((N, Co, Ho, Wo), dtype=torch.float32, device=x.device)
+    elif (tuple(out.shape) != (N, Co, Ho, Wo) or out.dtype != torch.float32
+          or not out.is_contiguous() or out.device != x.device):
+        raise ValueError("out has the wrong shape, dtype, device or layout")
+    if ws is None:
+        ws_ptr, nbytes = None, 0
+    else:
+        if not ws.is_cuda or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous GPU tensor")
+        ws_ptr = ctypes.c_void_p(ws.data_ptr())
+        nbytes = ws.numel() * ws.element_size() if ws_bytes is None else int(ws_bytes)
+    fn = _lib.load().conv2d_im2win_fp32 if x.dtype == torch.float32 else _lib.load().conv2d_im2win_fp16
+    _lib.check(fn(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                  ctypes.c_void_p(out.data_ptr()), ws_ptr, nbytes,
+                  N, Ci, Hi, Wi, Co, Hf, Wf, stride, _stream_handle(x)), fn.__name__)
+    return out

@@ -1,0 +1,64 @@
+"""ctypes declarations of libim2win.so (the C ABI in include/im2win.h).
+
+Loading fails loudly if the library has not been built: there is no
+fallback implementation anywhere in this package.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libim2win.so")
+
+IM2WIN_OK = 0
+IM2WIN_EINVAL = -1
+IM2WIN_EWORKSPACE = -2
+IM2WIN_ELAUNCH = -3
+
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+_p = ctypes.c_void_p
+
+EXPORTS = {
+    "im2win_workspace_bytes": ([_i] * 7 + [_sz], _sz),
+    "im2win_output_dims": ([_i] * 5 + [ctypes.POINTER(_i), ctypes.POINTER(_i)], _i),
+    "im2win_pack": ([_p, _p] + [_i] * 7 + [_sz, _p], _i),
+    "conv2d_im2win_fp32": ([_p, _p, _p, _p, _sz] + [_i] * 8 + [_p], _i),
+    "conv2d_im2win_fp16": ([_p, _p, _p, _p, _sz] + [_i] * 8 + [_p], _i),
+    "im2win_status_string": ([_i], ctypes.c_char_p),
+}
+
+_lib = None
+
+
+class Im2winError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()' from the repository root)")
+    L = ctypes.CDLL(LIB_PATH)
+    for name, (args, res) in EXPORTS.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load().im2win_status_string(status).decode()
+
+
+def check(status: int, what: str) -> None:
+    if status != IM2WIN_OK:
+        raise Im2winError(status, what)

@@ -1,0 +1,136 @@
+// C ABI of the im2win library: argument checks, workspace/mode selection and
+// kernel dispatch. Declarations and the contract are in include/im2win.h.
+#include <algorithm>
+#include <stdint.h>
+
+#include "im2win.h"
+#include "kernels.hpp"
+
+namespace {
+
+using im2win::ConvShape;
+
+constexpr int64_t kMax32 = 0x7fffffff;
+
+// Derives Ho, Wo and checks every limit of the contract.
+bool check_shape(int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s, int* Ho, int* Wo)
+{
+    if (N < 1 || Ci < 1 || Hi < 1 || Wi < 1 || Co < 1 || Hf < 1 || Wf < 1 || s < 1) return false;
+    if (Hf > Hi || Wf > Wi) return false;
+    const int ho = (Hi - Hf) / s + 1, wo = (Wi - Wf) / s + 1;
+    if ((int64_t)Ci * Hi * Wi > kMax32) return false;
+    if ((int64_t)Co * ho * wo > kMax32) return false;
+    if ((int64_t)Ci * ho * Wi * Hf > kMax32) return false;
+    if ((int64_t)Co * Ci * Hf * Wf > kMax32) return false;
+    if (Ho) *Ho = ho;
+    if (Wo) *Wo = wo;
+    return true;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int status_of(int rc)
+{
+    if (rc == 0) return IM2WIN_OK;
+    if (rc == -1) return IM2WIN_EINVAL;
+    return IM2WIN_ELAUNCH;
+}
+
+// Shared driver of both precisions. T is the element type of x, w and ws.
+template <typename T>
+int conv_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int N, int Ci, int Hi,
+                int Wi, int Co, int Hf, int Wf, int s, hipStream_t stream,
+                int (*tiled)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t),
+                int (*generic)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t))
+{
+    int Ho, Wo;
+    if (!x || !w || !y) return IM2WIN_EINVAL;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, s, &Ho, &Wo)) return IM2WIN_EINVAL;
+    if (!aligned(x, sizeof(T)) || !aligned(w, sizeof(T)) || !aligned(y, sizeof(float)))
+        return IM2WIN_EINVAL;
+    ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, s, Ho, Wo};
+    auto run = [&](const T* xx, const T* wws, float* yy, const ConvShape& cc) {
+        int rc = tiled(xx, wws, w, yy, cc, stream);
+        if (rc == -1) rc = generic(xx, wws, w, yy, cc, stream);
+        return rc;
+    };
+    if (ws == nullptr) {
+        if (ws_bytes != 0) return IM2WIN_EWORKSPACE;
+        return status_of(run(x, nullptr, y, c));
+    }
+    if (!aligned(ws, sizeof(T))) return IM2WIN_EINVAL;
+    const size_t per_image = (size_t)Ci * Ho * Wi * Hf * sizeof(T);
+    if (ws_bytes < per_image) return IM2WIN_EWORKSPACE;
+    const int chunk = (int)std::min<size_t>((size_t)N, ws_bytes / per_image);
+    const int64_t x_img = (int64_t)Ci * Hi * Wi, y_img = (int64_t)Co * Ho * Wo;
+    for (int n0 = 0; n0 < N; n0 += chunk) {
+        const int nc = std::min(chunk, N - n0);
+        int rc = im2win::launch_pack(x + n0 * x_img, ws, nc, Ci, Hi, Wi, Hf, s, Ho, (int)sizeof(T),
+                                     stream);
+        if (rc != 0) return status_of(rc);
+        ConvShape cc = c;
+        cc.N = nc;
+        rc = run(x + n0 * x_img, static_cast<const T*>(ws), y + n0 * y_img, cc);
+        if (rc != 0) return status_of(rc);
+    }
+    return IM2WIN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t im2win_workspace_bytes(int N, int Ci, int Hi, int Wi, int Hf, int Wf, int s,
+                              size_t elem_bytes)
+{
+    int Ho;
+    if (elem_bytes != 2 && elem_bytes != 4) return 0;
+    if (!check_shape(N, Ci, Hi, Wi, 1, Hf, Wf, s, &Ho, nullptr)) return 0;
+    return (size_t)N * Ci * Ho * ((size_t)Wi * Hf) * elem_bytes;
+}
+
+int im2win_output_dims(int Hi, int Wi, int Hf, int Wf, int s, int* Ho, int* Wo)
+{
+    return check_shape(1, 1, Hi, Wi, 1, Hf, Wf, s, Ho, Wo) ? IM2WIN_OK : IM2WIN_EINVAL;
+}
+
+int im2win_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, int Wf, int s,
+                size_t elem_bytes, void* stream)
+{
+    int Ho;
+    if (!x || !ws) return IM2WIN_EINVAL;
+    if (elem_bytes != 2 && elem_bytes != 4) return IM2WIN_EINVAL;
+    if (!check_shape(N, Ci, Hi, Wi, 1, Hf, Wf, s, &Ho, nullptr)) return IM2WIN_EINVAL;
+    if (!aligned(x, elem_bytes) || !aligned(ws, elem_bytes)) return IM2WIN_EINVAL;
+    return status_of(im2win::launch_pack(x, ws, N, Ci, Hi, Wi, Hf, s, Ho, (int)elem_bytes,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int conv2d_im2win_fp32(const float* x, const float* w, float* y, void* ws, size_t ws_bytes, int N,
+                       int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s, void* stream)
+{
+    return conv_driver<float>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, s,
+                              static_cast<hipStream_t>(stream), im2win::launch_conv_f32,
+                              im2win::launch_conv_generic_f32);
+}
+
+int conv2d_im2win_fp16(const uint16_t* x, const uint16_t* w, float* y, void* ws, size_t ws_bytes,
+                       int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s, void* stream)
+{
+    return conv_driver<uint16_t>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, s,
+                                 static_cast<hipStream_t>(stream), im2win::launch_conv_f16,
+                                 im2win::launch_conv_generic_f16);
+}
+
+const char* im2win_status_string(int status)
+{
+    switch (status) {
+    case IM2WIN_OK: return "ok";
+    case IM2WIN_EINVAL: return "invalid argument (shape, stride, element size, alignment or NULL pointer)";
+    case IM2WIN_EWORKSPACE: return "workspace smaller than one image's im2win rows";
+    case IM2WIN_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Kernel launchers shared by the C-ABI layer. Each returns 0 on success,
+// -1 if the shape is outside what the launcher supports, -3 if the launch
+// failed. Shapes are validated by the caller first.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace im2win {
+
+// Convolution geometry of one launch (N = images in this launch).
+struct ConvShape {
+    int N, Ci, Hi, Wi, Co, Hf, Wf, s, Ho, Wo;
+};
+
+// The im2win transform of N images (bit copy of elem_bytes-wide elements).
+int launch_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, int s, int Ho,
+                int elem_bytes, hipStream_t stream);
+
+// fp32 convolution on the vector ALUs. ws == nullptr: im2win rows are built
+// in LDS from x; otherwise they are read from the packed tensor ws (N images).
+int launch_conv_f32(const float* x, const float* ws, const float* w, float* y,
+                    const ConvShape& c, hipStream_t stream);
+
+// fp16 x fp16 -> fp32 convolution on the matrix cores; ws as above.
+int launch_conv_f16(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float* y,
+                    const ConvShape& c, hipStream_t stream);
+
+// Plain fallbacks (one thread per output) for shapes the tiled kernels do
+// not take; ws as above.
+int launch_conv_generic_f32(const float* x, const float* ws, const float* w, float* y,
+                            const ConvShape& c, hipStream_t stream);
+int launch_conv_generic_f16(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float* y,
+                            const ConvShape& c, hipStream_t stream);
+
+}  // namespace im2win

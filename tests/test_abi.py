@@ -1,0 +1,121 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol,
+and rejects bad arguments before touching the GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_efficient_im2win_amd as m
+from memory_efficient_im2win_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "im2win.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(im2win_\w+|conv2d_im2win_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(
+        ["im2win_workspace_bytes", "im2win_output_dims", "im2win_pack", "conv2d_im2win_fp32",
+         "conv2d_im2win_fp16", "im2win_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    L = m.load_library()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(_lib.EXPORTS)
+
+
+def test_workspace_bytes_at_the_benchmark_layers():
+    # N*Ci*Ho*(Wi*Hf)*elem for cv5/cv1 (fp32) and cv5/cv3/cv4 (fp16)
+    assert m.workspace_bytes(1, 96, 24, 24, 5, 5, 1, 4) == 921_600
+    assert m.workspace_bytes(32, 3, 227, 227, 11, 11, 4, 4) == 52_736_640
+    assert m.workspace_bytes(128, 96, 24, 24, 5, 5, 1, 2) == 58_982_400
+    assert m.workspace_bytes(64, 3, 227, 227, 7, 7, 2, 2) == 67_729_536
+    assert m.workspace_bytes(64, 64, 224, 224, 7, 7, 2, 2) == 1_400_111_104
+
+
+def test_workspace_bytes_agrees_with_oracle(orc):
+    import random
+    rnd = random.Random(1)
+    for _ in range(200):
+        Hf, Wf, s = rnd.randint(1, 6), rnd.randint(1, 6), rnd.randint(1, 5)
+        Hi, Wi = rnd.randint(Hf, 40), rnd.randint(Wf, 40)
+        N, Ci = rnd.randint(1, 4), rnd.randint(1, 9)
+        for e in (2, 4):
+            assert m.workspace_bytes(N, Ci, Hi, Wi, Hf, Wf, s, e) == \
+                orc.im2win_elems(N, Ci, Hi, Wi, Hf, Wf, s) * e
+            assert m.output_dims(Hi, Wi, Hf, Wf, s) == orc.out_hw(Hi, Wi, Hf, Wf, s)
+
+
+@pytest.mark.parametrize("args", [
+    (0, 1, 4, 4, 2, 2, 1, 4),      # N = 0
+    (1, 1, 4, 4, 5, 2, 1, 4),      # Hf > Hi
+    (1, 1, 4, 4, 2, 5, 1, 4),      # Wf > Wi
+    (1, 1, 4, 4, 2, 2, 0, 4),      # s = 0
+    (1, 1, 4, 4, 2, 2, 1, 3),      # element size
+    (1, 1 << 16, 1 << 8, 1 << 8, 1, 1, 1, 2),  # one image beyond 2^31 elements
+])
+def test_workspace_bytes_invalid(args):
+    assert m.workspace_bytes(*args) == 0
+
+
+def test_output_dims_table1_floor():
+    assert m.output_dims(224, 224, 7, 7, 2) == (109, 109)
+    with pytest.raises(m.Im2winError):
+        m.output_dims(4, 4, 5, 5, 1)
+
+
+def test_status_strings():
+    L = m.load_library()
+    for st in (0, -1, -2, -3, 7):
+        assert L.im2win_status_string(st)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails its checks first
+
+
+@pytest.mark.parametrize("fn", ["conv2d_im2win_fp32", "conv2d_im2win_fp16"])
+def test_conv_rejects_bad_arguments_before_launch(fn):
+    L = m.load_library()
+    f = getattr(L, fn)
+    ok = (1, 3, 8, 8, 4, 3, 3, 1)
+    # NULL tensors
+    assert f(None, FAKE, FAKE, None, 0, *ok, None) == _lib.IM2WIN_EINVAL
+    assert f(FAKE, None, FAKE, None, 0, *ok, None) == _lib.IM2WIN_EINVAL
+    assert f(FAKE, FAKE, None, None, 0, *ok, None) == _lib.IM2WIN_EINVAL
+    # bad shapes
+    assert f(FAKE, FAKE, FAKE, None, 0, 1, 3, 8, 8, 4, 9, 3, 1, None) == _lib.IM2WIN_EINVAL
+    assert f(FAKE, FAKE, FAKE, None, 0, 1, 3, 8, 8, 4, 3, 3, 0, None) == _lib.IM2WIN_EINVAL
+    assert f(FAKE, FAKE, FAKE, None, 0, 1, 0, 8, 8, 4, 3, 3, 1, None) == _lib.IM2WIN_EINVAL
+    # misaligned tensors
+    odd = ctypes.c_void_p(0x10001)
+    assert f(odd, FAKE, FAKE, None, 0, *ok, None) == _lib.IM2WIN_EINVAL
+    # workspace: NULL with a size, or smaller than one image's im2win rows
+    assert f(FAKE, FAKE, FAKE, None, 64, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    per_image = m.workspace_bytes(1, 3, 8, 8, 3, 3, 1, 4 if fn.endswith("32") else 2)
+    assert f(FAKE, FAKE, FAKE, FAKE, per_image - 1, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, *ok, None) == _lib.IM2WIN_EWORKSPACE
+
+
+def test_pack_rejects_bad_arguments_before_launch():
+    L = m.load_library()
+    assert L.im2win_pack(None, FAKE, 1, 1, 4, 4, 2, 2, 1, 4, None) == _lib.IM2WIN_EINVAL
+    assert L.im2win_pack(FAKE, None, 1, 1, 4, 4, 2, 2, 1, 4, None) == _lib.IM2WIN_EINVAL
+    assert L.im2win_pack(FAKE, FAKE, 1, 1, 4, 4, 2, 2, 1, 8, None) == _lib.IM2WIN_EINVAL
+    assert L.im2win_pack(FAKE, FAKE, 1, 1, 4, 4, 5, 2, 1, 4, None) == _lib.IM2WIN_EINVAL
+    assert L.im2win_pack(ctypes.c_void_p(0x10002), FAKE, 1, 1, 4, 4, 2, 2, 1, 4, None) == \
+        _lib.IM2WIN_EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

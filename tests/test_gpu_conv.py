@@ -1,0 +1,164 @@
+"""conv2d_im2win_fp32 / _fp16 on the GPU against the fp64 oracle.
+
+Bar: bit-exact for small-integer inputs (every partial sum is an exact
+integer below 2^24, so any summation order gives the same fp32 value);
+otherwise |y - y_oracle| <= tol * sum|x*w| per output with tol 1e-5 (fp32)
+and 2e-3 (fp16 inputs, fp32 accumulation).
+"""
+import numpy as np
+import pytest
+
+import memory_efficient_im2win_amd as m
+import workloads
+from parity import TOL, assert_exact, assert_within, device, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# (N, Ci, Hi, Wi, Co, Hf, Wf, s): several workgroup tiles with ragged tails in
+# pixels and channels; each filter size the fp32 kernel specialises (11, 7, 5,
+# 3) and the generic one; Ci and Co off the MFMA tile multiples.
+SMALL = [
+    (3, 5, 19, 19, 40, 3, 3, 1),
+    (2, 3, 47, 45, 37, 11, 11, 4),
+    (2, 16, 30, 29, 70, 7, 7, 2),
+    (4, 24, 14, 14, 96, 5, 5, 1),
+    (1, 13, 21, 17, 9, 2, 3, 2),      # rectangular, generic path
+    (2, 8, 12, 40, 64, 1, 1, 1),      # 1x1
+    (1, 3, 9, 9, 5, 9, 9, 1),         # filter covers the input: one output
+    (2, 6, 23, 11, 33, 4, 6, 3),      # s < Hf, Wf; ragged (Hi-Hf) % s
+    (1, 9, 16, 16, 17, 2, 2, 5),      # s > Hf, Wf
+    (1, 64, 30, 30, 64, 7, 7, 2),     # cv4-like slice
+    (1, 96, 12, 12, 256, 5, 5, 1),    # cv5-like slice
+]
+
+
+def _run(sh, mode, x, w, ws_images=None):
+    import torch
+    dev = device()
+    xt, wt = to_dev(x, dev), to_dev(w, dev)
+    if ws_images is None:
+        y = m.conv2d(xt, wt, sh.s)
+    else:
+        per = m.workspace_bytes(1, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
+        ws = torch.empty(per * ws_images, dtype=torch.uint8, device=dev)
+        y = m.conv2d(xt, wt, sh.s, ws=ws)
+    out = y.cpu().numpy()
+    torch.cuda.synchronize()
+    return out
+
+
+def _shape(t, dt):
+    return workloads.ConvShape("t", *t, dt)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("t", SMALL, ids=str)
+def test_conv_small_uniform(t, dt, orc):
+    sh = _shape(t, dt)
+    x, w = workloads.make_inputs(sh, seed=11)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    for ws_images in (None, sh.N, 1):
+        note(f"conv uniform {sh.describe()} ws_images={ws_images}")
+        y = _run(sh, dt, x, w, ws_images)
+        assert_within(y, ref, absd, TOL[dt], f"{sh.describe()} ws_images={ws_images}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("t", SMALL, ids=str)
+def test_conv_small_integer_exact(t, dt, orc):
+    sh = _shape(t, dt)
+    x, w = workloads.make_inputs(sh, seed=12, mode="int")
+    ref = orc.conv_direct(x, w, sh.s)
+    for ws_images in (None, 2):
+        note(f"conv integer {sh.describe()} ws_images={ws_images}")
+        assert_exact(_run(sh, dt, x, w, ws_images), ref, f"{sh.describe()} ws_images={ws_images}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_conv_generic_fallback_large_filter(dt, orc):
+    """A 13x13 filter over a wide row falls outside the tiled kernels' LDS
+    budget in fp16; both precisions must still be right."""
+    sh = _shape((1, 9, 20, 600, 7, 13, 13, 2), dt)
+    x, w = workloads.make_inputs(sh, seed=13)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    for ws_images in (None, 1):
+        note(f"conv large filter {sh.describe()} ws_images={ws_images}")
+        assert_within(_run(sh, dt, x, w, ws_images), ref, absd, TOL[dt], sh.describe())
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_conv_special_values(dt, orc):
+    """NaN and infinities propagate exactly to the outputs whose windows hold
+    them (window padding never turns a neighbour's Inf into NaN)."""
+    sh = _shape((2, 8, 13, 13, 9, 3, 3, 1), dt)
+    x, w = workloads.make_inputs(sh, seed=14)
+    x[0, 1, 4, 5] = np.inf
+    x[1, 7, 12, 12] = -np.inf
+    x[1, 0, 0, 0] = np.nan
+    w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)  # no zero taps, fixed signs
+    ref = orc.conv_direct(x, w, sh.s)
+    note(f"conv special values {sh.describe()}")
+    for ws_images in (None, 1):
+        y = _run(sh, dt, x, w, ws_images).astype(np.float64)
+        assert np.array_equal(np.isnan(y), np.isnan(ref))
+        assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+        assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+        fin = np.isfinite(ref)
+        _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
+                                  with_absdot=True)
+        assert_within(y[fin], ref[fin], absd[fin], TOL[dt], "finite outputs")
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_conv_writes_only_its_output(dt, orc):
+    import torch
+    dev = device()
+    sh = _shape((2, 12, 17, 15, 41, 3, 5, 2), dt)
+    x, w = workloads.make_inputs(sh, seed=15)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    n = ref.size
+    note(f"conv guard bands {sh.describe()}")
+    for use_ws in (False, True):
+        big = torch.full((n + 2 * 129,), float("nan"), dtype=torch.float32, device=dev)
+        out = big[129:129 + n].view(ref.shape)
+        kw = {}
+        if use_ws:
+            per = m.workspace_bytes(1, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
+            wsbig = torch.full((per + 4096,), 0x7F, dtype=torch.uint8, device=dev)
+            kw = dict(ws=wsbig, ws_bytes=per)
+        m.conv2d(to_dev(x, dev), to_dev(w, dev), sh.s, out=out, **kw)
+        b = big.cpu().numpy()
+        assert np.isnan(b[:129]).all() and np.isnan(b[129 + n:]).all()
+        assert_within(b[129:129 + n].reshape(ref.shape), ref, absd, TOL[dt], "guarded output")
+        if use_ws:
+            assert (wsbig[per:].cpu().numpy() == 0x7F).all()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("key", ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64",
+                                 "cv4_f16_n64"])
+@pytest.mark.parametrize("mode", ["uniform", "int"])
+def test_conv_full_size_sampled(key, mode, orc):
+    """The benchmark layers at full size, fused and materialised (the two
+    launch configurations the benchmark times), checked at ~3000 outputs
+    the oracle computes one by one (corners included)."""
+    import torch
+    dev = device()
+    sh = workloads.BY_KEY[key]
+    x, w = workloads.make_inputs(sh, seed=0 if mode == "uniform" else 1, mode=mode)
+    Ho, Wo = m.output_dims(sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s)
+    idx = workloads.sample_output_indices(sh, Ho, Wo, 3000)
+    ref, absd = orc.conv_points(x, w, sh.s, idx)
+    xt, wt = to_dev(x, dev), to_dev(w, dev)
+    nb = m.workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
+    for ws in (None, torch.empty(nb, dtype=torch.uint8, device=dev)):
+        note(f"conv full {sh.describe()} {mode} ws={'full' if ws is not None else 'none'}")
+        y = m.conv2d(xt, wt, sh.s, ws=ws).reshape(-1)
+        got = y[torch.from_numpy(idx).to(dev)].cpu().numpy()
+        assert bool(torch.isfinite(y).all())
+        if mode == "int":
+            assert_exact(got, ref, sh.describe())
+        else:
+            assert_within(got, ref, absd, TOL[sh.dtype], sh.describe())
+        del y
+    torch.cuda.synchronize()
