@@ -140,6 +140,51 @@ def load_traffic(key, mode):
     return ent.get("bytes_per_launch")
 
 
+def calibrate_copy(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    counters (FETCH_SIZE / WRITE_SIZE) of a profiled run."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy: {reps} x {nbytes} bytes")
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def ingest_pmc(fetch_csv, write_csv, copy_bytes=1 << 30):
+    """Per-launch HBM bytes of each kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), scaled so that the calibration
+    copy reads and writes exactly its size. Writes profiles/traffic.json."""
+    def per_kernel(path, counter):
+        vals = {}
+        for r in _read_csv(path):
+            if r.get("Counter_Name") != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: float(np.mean(v)) for k, v in vals.items()}
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy_k = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    if not copy_k:
+        raise SystemExit("no copy kernel found in the counter files")
+    ck = max(copy_k, key=lambda k: fetch[k])
+    f_scale = copy_bytes / (fetch[ck] * 1024.0)
+    w_scale = copy_bytes / (write[ck] * 1024.0)
+    out = {"copy_kernel": ck, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for k in fetch:
+        if k in write:
+            out["kernels"][k] = {"fetch_bytes": fetch[k] * 1024.0 * f_scale,
+                                 "write_bytes": write[k] * 1024.0 * w_scale}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,7 +194,33 @@ def main():
     ap.add_argument("--mode", default="fused", choices=["fused", "materialized"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-layers", action="store_true", help="time only the headline workload")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (for scaling rocprofv3 HBM counters)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs of this bench into "
+                         "profiles/traffic.json for the current kernel sources, then exit")
     args = ap.parse_args()
+
+    if args.ingest_pmc:
+        t = ingest_pmc(*args.ingest_pmc)
+        kern = [k for k in t["kernels"] if "conv_f32_kernel" in k or "conv_f16_kernel" in k]
+        if len(kern) != 1:
+            raise SystemExit(f"expected one conv kernel in the counters, found {kern}")
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        d = json.load(open(path)) if os.path.exists(path) else {}
+        kb = t["kernels"][kern[0]]
+        d[f"{args.workload}:{args.mode}"] = {
+            "source_hash": kernel_source_hash(),
+            "kernel": kern[0][:120],
+            "bytes_per_launch": round(kb["fetch_bytes"] + kb["write_bytes"]),
+            "fetch_bytes": round(kb["fetch_bytes"]), "write_bytes": round(kb["write_bytes"]),
+            "copy_scale": {"fetch": t["fetch_scale"], "write": t["write_scale"],
+                           "copy_kernel": t["copy_kernel"][:120]},
+        }
+        with open(path, "w") as f:
+            json.dump(d, f, indent=1)
+        print(json.dumps(d[f"{args.workload}:{args.mode}"]))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the im2win forward convolution needs no "
@@ -163,6 +234,9 @@ def main():
         sys.exit(1)
     import memory_efficient_im2win_amd as m
     m.load_library()
+
+    if args.calibrate_copy:
+        calibrate_copy()
 
     sh = workloads.BY_KEY[args.workload]
     log(f"[bench] headline {sh.describe()} mode={args.mode} steps={args.steps} warmup={args.warmup}")
