@@ -66,9 +66,10 @@ def time_layer(sh, mode, steps, warmup):
     y = torch.empty((sh.N, sh.Co, Ho, Wo), dtype=torch.float32, device=dev)
     ws = None
     wsb = 0
-    if mode == "materialized":
-        wsb = m.workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
-        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    if mode != "fused":
+        wsb = m.conv_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
+                                     sh.elem_bytes, mode == "materialized")
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
     for _ in range(warmup):
         m.conv2d(xt, wt, sh.s, ws=ws, out=y)
     torch.cuda.synchronize()
@@ -191,7 +192,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(workloads.BY_KEY))
-    ap.add_argument("--mode", default="fused", choices=["fused", "materialized"])
+    ap.add_argument("--mode", default="fused", choices=["fused", "prepacked", "materialized"],
+                    help="fused: no workspace; prepacked: fused with the fp16 filter prepacked "
+                         "into a small workspace; materialized: im2win tensor in HBM")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-layers", action="store_true", help="time only the headline workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -248,7 +251,9 @@ def main():
         for key in LAYER_KEYS:
             lsh = workloads.BY_KEY[key]
             entry = {}
-            for mode in ("fused", "materialized"):
+            modes = ("fused", "materialized") if lsh.dtype == "f32" else \
+                ("fused", "prepacked", "materialized")
+            for mode in modes:
                 r = time_layer(lsh, mode, max(5, args.steps // 2), 3)
                 peak = PEAK_FP32_VECTOR_TFLOPS if lsh.dtype == "f32" else PEAK_FP16_MFMA_TFLOPS
                 entry[mode] = {"tflops": round(r["tflops"], 3), "us_per_call": round(r["ms_per_step"] * 1e3, 2),

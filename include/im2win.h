@@ -85,19 +85,43 @@ int im2win_pack(const void *x, void *ws, int N, int Ci, int Hi, int Wi, int Hf, 
                 int s, size_t elem_bytes, void *stream);
 
 /*
+ * Workspace of the two convolution entry points, in bytes.
+ *
+ * The workspace (optional) is one caller-owned device buffer, 16-byte
+ * aligned, laid out as
+ *     [ prepacked filter | im2win tensor of a chunk of images ]
+ * The prepacked part is the filter re-laid out for the matrix-core kernel
+ * (fp16 only; it is 0 bytes for fp32 and for fp16 shapes the fused kernel
+ * does not take); it is rounded up to a multiple of 256 bytes.
+ *
+ *  materialize == 0: bytes for the fused mode with a prepacked filter
+ *                    (0 for fp32: the fused fp32 path needs no workspace).
+ *  materialize != 0: bytes for the materialised mode over the whole batch:
+ *                    the prepacked part + N * one image's im2win bytes.
+ * Returns 0 for an invalid shape or elem_bytes not in {2, 4}. Host only.
+ */
+size_t conv2d_im2win_workspace_bytes(int materialize, int N, int Ci, int Hi, int Wi, int Co,
+                                     int Hf, int Wf, int s, size_t elem_bytes);
+
+/*
  * fp32 convolution on the vector ALUs ("full precision on CUDA cores" in the
  * GPU page's Abstract). x, w fp32; y fp32 (written fully).
  *
- * Workspace selects how the im2win rows reach the kernel:
+ * The workspace selects how the im2win rows reach the dot products; with
+ * F = the prepacked part (see conv2d_im2win_workspace_bytes, 0 for fp32)
+ * and I = one image's im2win bytes (im2win_workspace_bytes with N = 1):
  *  - ws == NULL and ws_bytes == 0: fused. Each workgroup builds the im2win
  *    rows it needs in LDS straight from x; no HBM workspace.
- *  - ws_bytes >= im2win_workspace_bytes(N, ..., 4): materialised. The whole
- *    batch is packed into ws (im2win_pack), then convolved from it.
- *  - one image's im2win bytes <= ws_bytes < the batch's: materialised, in
- *    chunks of floor(ws_bytes / one image's bytes) images, in stream order.
- *  - otherwise (or ws == NULL with ws_bytes != 0): IM2WIN_EWORKSPACE.
- * Both modes compute each output as the same windowed dot product; their
- * fp32 rounding is the same.
+ *  - F <= ws_bytes < F + I (fp16 only, F > 0): fused, the filter prepacked
+ *    once per call into the workspace.
+ *  - ws_bytes >= F + I: materialised. The im2win tensor of
+ *    floor((ws_bytes - F) / I) images at a time (at most N) is packed into
+ *    the workspace after F (im2win_pack layout) and convolved from there,
+ *    chunk by chunk in stream order.
+ *  - anything else (ws == NULL with ws_bytes != 0, or too small): returns
+ *    IM2WIN_EWORKSPACE; ws not 16-byte aligned: IM2WIN_EINVAL.
+ * All modes compute the same windowed dot products; only their fp32
+ * summation order may differ.
  */
 int conv2d_im2win_fp32(const float *x, const float *w, float *y, void *ws, size_t ws_bytes,
                        int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s,
@@ -107,7 +131,7 @@ int conv2d_im2win_fp32(const float *x, const float *w, float *y, void *ws, size_
  * fp16-input convolution on the matrix cores ("half precision on tensor
  * cores", same Abstract): x, w binary16; products exact, fp32 accumulation;
  * y fp32 (written fully). Workspace rules as for conv2d_im2win_fp32, with
- * im2win_workspace_bytes(..., 2).
+ * elem_bytes = 2.
  */
 int conv2d_im2win_fp16(const uint16_t *x, const uint16_t *w, float *y, void *ws,
                        size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf,

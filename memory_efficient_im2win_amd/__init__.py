@@ -16,8 +16,8 @@ import ctypes
 from . import _lib
 from ._lib import Im2winError, status_string  # noqa: F401
 
-__all__ = ["conv2d", "pack", "workspace_bytes", "output_dims", "Im2winError", "status_string",
-           "load_library"]
+__all__ = ["conv2d", "pack", "workspace_bytes", "conv_workspace_bytes", "output_dims",
+           "Im2winError", "status_string", "load_library"]
 
 
 def load_library():
@@ -35,6 +35,14 @@ def output_dims(Hi: int, Wi: int, Hf: int, Wf: int, s: int):
 def workspace_bytes(N, Ci, Hi, Wi, Hf, Wf, s, elem_bytes) -> int:
     """Bytes of the im2win tensor of the whole batch (0 for an invalid shape)."""
     return _lib.load().im2win_workspace_bytes(N, Ci, Hi, Wi, Hf, Wf, s, elem_bytes)
+
+
+def conv_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s, elem_bytes, materialize: bool) -> int:
+    """Workspace bytes of a convolution call: the fused mode with a prepacked
+    filter (materialize=False; 0 for fp32) or the materialised mode over the
+    whole batch (materialize=True). 0 for an invalid shape."""
+    return _lib.load().conv2d_im2win_workspace_bytes(1 if materialize else 0, N, Ci, Hi, Wi, Co,
+                                                    Hf, Wf, s, elem_bytes)
 
 
 def _torch():
@@ -85,9 +93,11 @@ def conv2d(x, w, stride: int = 1, ws=None, ws_bytes: int | None = None, out=None
     with w (Co,Ci,Hf,Wf); fp32 output (N,Co,Ho,Wo).
 
     float32 inputs run on the vector ALUs, float16 inputs on the matrix cores
-    (fp32 accumulation). With ``ws`` (a device tensor of at least one image's
-    im2win bytes) the im2win tensor is materialised in it, in chunks of as
-    many images as fit; without, the im2win rows are built in LDS.
+    (fp32 accumulation). Without ``ws`` the im2win rows are built in LDS
+    (fused). With ``ws`` (a device tensor; see conv_workspace_bytes) the
+    fp16 filter is prepacked into its head, and if the rest holds at least
+    one image's im2win tensor that tensor is materialised, in chunks of as
+    many images as fit.
     """
     torch = _torch()
     _check_tensor(x, "x", (torch.float32, torch.float16), 4)

@@ -26,6 +26,7 @@ EXPORTS = {
     "im2win_pack": ([_p, _p] + [_i] * 7 + [_sz, _p], _i),
     "conv2d_im2win_fp32": ([_p, _p, _p, _p, _sz] + [_i] * 8 + [_p], _i),
     "conv2d_im2win_fp16": ([_p, _p, _p, _p, _sz] + [_i] * 8 + [_p], _i),
+    "conv2d_im2win_workspace_bytes": ([_i] * 9 + [_sz], _sz),
     "im2win_status_string": ([_i], ctypes.c_char_p),
 }
 

@@ -36,12 +36,33 @@ int status_of(int rc)
     return IM2WIN_ELAUNCH;
 }
 
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace layout: [prepacked filter, rounded up to 256 bytes | im2win chunk].
+// The prepacked part is empty where the fused kernel does not use one (fp32,
+// or shapes outside its envelope).
+struct WsPlan {
+    size_t fbytes;     // prepacked filter bytes (aligned), 0 if none
+    size_t per_image;  // im2win bytes of one image
+};
+
+WsPlan ws_plan(const ConvShape& c, size_t elem)
+{
+    WsPlan p;
+    p.fbytes = elem == 2 ? align_up(im2win::f16_filter_pack_bytes(c)) : 0;
+    p.per_image = (size_t)c.Ci * c.Ho * c.Wi * c.Hf * elem;
+    return p;
+}
+
 // Shared driver of both precisions. T is the element type of x, w and ws.
 template <typename T>
 int conv_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int N, int Ci, int Hi,
                 int Wi, int Co, int Hf, int Wf, int s, hipStream_t stream,
-                int (*tiled)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t),
-                int (*generic)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t))
+                int (*fused)(const T*, const T*, const void*, float*, const ConvShape&, hipStream_t),
+                int (*from_ws)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t),
+                int (*generic)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t),
+                int (*filter_pack)(const T*, void*, const ConvShape&, hipStream_t))
 {
     int Ho, Wo;
     if (!x || !w || !y) return IM2WIN_EINVAL;
@@ -49,31 +70,69 @@ int conv_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int
     if (!aligned(x, sizeof(T)) || !aligned(w, sizeof(T)) || !aligned(y, sizeof(float)))
         return IM2WIN_EINVAL;
     ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, s, Ho, Wo};
-    auto run = [&](const T* xx, const T* wws, float* yy, const ConvShape& cc) {
-        int rc = tiled(xx, wws, w, yy, cc, stream);
-        if (rc == -1) rc = generic(xx, wws, w, yy, cc, stream);
-        return rc;
-    };
+    const WsPlan p = ws_plan(c, sizeof(T));
     if (ws == nullptr) {
         if (ws_bytes != 0) return IM2WIN_EWORKSPACE;
-        return status_of(run(x, nullptr, y, c));
+        int rc = fused(x, w, nullptr, y, c, stream);
+        if (rc == -1) rc = generic(x, nullptr, w, y, c, stream);
+        return status_of(rc);
     }
-    if (!aligned(ws, sizeof(T))) return IM2WIN_EINVAL;
-    const size_t per_image = (size_t)Ci * Ho * Wi * Hf * sizeof(T);
-    if (ws_bytes < per_image) return IM2WIN_EWORKSPACE;
-    const int chunk = (int)std::min<size_t>((size_t)N, ws_bytes / per_image);
+    if (!aligned(ws, 16)) return IM2WIN_EINVAL;
+    if (ws_bytes < p.fbytes + (p.fbytes ? 0 : p.per_image)) return IM2WIN_EWORKSPACE;
+    unsigned char* wsb = static_cast<unsigned char*>(ws);
+    const size_t rest = ws_bytes - p.fbytes;
+    if (rest < p.per_image) {
+        // Fused, with the filter prepacked once into the workspace.
+        int rc = filter_pack(w, wsb, c, stream);
+        if (rc != 0) return status_of(rc);
+        rc = fused(x, w, wsb, y, c, stream);
+        if (rc == -1) rc = generic(x, nullptr, w, y, c, stream);
+        return status_of(rc);
+    }
+    // Materialised: the im2win tensor of as many images as fit, chunk by chunk.
+    const T* ims = reinterpret_cast<const T*>(wsb + p.fbytes);
+    const int chunk = (int)std::min<size_t>((size_t)N, rest / p.per_image);
     const int64_t x_img = (int64_t)Ci * Hi * Wi, y_img = (int64_t)Co * Ho * Wo;
     for (int n0 = 0; n0 < N; n0 += chunk) {
         const int nc = std::min(chunk, N - n0);
-        int rc = im2win::launch_pack(x + n0 * x_img, ws, nc, Ci, Hi, Wi, Hf, s, Ho, (int)sizeof(T),
-                                     stream);
+        int rc = im2win::launch_pack(x + n0 * x_img, wsb + p.fbytes, nc, Ci, Hi, Wi, Hf, s, Ho,
+                                     (int)sizeof(T), stream);
         if (rc != 0) return status_of(rc);
         ConvShape cc = c;
         cc.N = nc;
-        rc = run(x + n0 * x_img, static_cast<const T*>(ws), y + n0 * y_img, cc);
+        rc = from_ws(x + n0 * x_img, ims, w, y + n0 * y_img, cc, stream);
+        if (rc == -1) rc = generic(x + n0 * x_img, ims, w, y + n0 * y_img, cc, stream);
         if (rc != 0) return status_of(rc);
     }
     return IM2WIN_OK;
+}
+
+// Adapters to the driver's signatures.
+int f32_fused(const float* x, const float* w, const void*, float* y, const ConvShape& c,
+              hipStream_t st)
+{
+    return im2win::launch_conv_f32(x, nullptr, w, y, c, st);
+}
+int f32_from_ws(const float* x, const float* ws, const float* w, float* y, const ConvShape& c,
+                hipStream_t st)
+{
+    return im2win::launch_conv_f32(x, ws, w, y, c, st);
+}
+int f32_generic(const float* x, const float* ws, const float* w, float* y, const ConvShape& c,
+                hipStream_t st)
+{
+    return im2win::launch_conv_generic_f32(x, ws, w, y, c, st);
+}
+int f32_no_pack(const float*, void*, const ConvShape&, hipStream_t) { return -1; }
+int f16_from_ws(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float* y,
+                const ConvShape& c, hipStream_t st)
+{
+    return im2win::launch_conv_f16(x, ws, w, y, c, st);
+}
+int f16_generic(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float* y,
+                const ConvShape& c, hipStream_t st)
+{
+    return im2win::launch_conv_generic_f16(x, ws, w, y, c, st);
 }
 
 }  // namespace
@@ -106,20 +165,30 @@ int im2win_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, 
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t conv2d_im2win_workspace_bytes(int materialize, int N, int Ci, int Hi, int Wi, int Co,
+                                     int Hf, int Wf, int s, size_t elem_bytes)
+{
+    int Ho, Wo;
+    if (elem_bytes != 2 && elem_bytes != 4) return 0;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, s, &Ho, &Wo)) return 0;
+    const WsPlan p = ws_plan(ConvShape{N, Ci, Hi, Wi, Co, Hf, Wf, s, Ho, Wo}, elem_bytes);
+    return p.fbytes + (materialize ? (size_t)N * p.per_image : 0);
+}
+
 int conv2d_im2win_fp32(const float* x, const float* w, float* y, void* ws, size_t ws_bytes, int N,
                        int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s, void* stream)
 {
     return conv_driver<float>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, s,
-                              static_cast<hipStream_t>(stream), im2win::launch_conv_f32,
-                              im2win::launch_conv_generic_f32);
+                              static_cast<hipStream_t>(stream), f32_fused, f32_from_ws,
+                              f32_generic, f32_no_pack);
 }
 
 int conv2d_im2win_fp16(const uint16_t* x, const uint16_t* w, float* y, void* ws, size_t ws_bytes,
                        int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s, void* stream)
 {
     return conv_driver<uint16_t>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, s,
-                                 static_cast<hipStream_t>(stream), im2win::launch_conv_f16,
-                                 im2win::launch_conv_generic_f16);
+                                 static_cast<hipStream_t>(stream), im2win::launch_conv_f16_fused,
+                                 f16_from_ws, f16_generic, im2win::launch_f16_filter_pack);
 }
 
 const char* im2win_status_string(int status)

@@ -201,10 +201,12 @@ __global__ __launch_bounds__(kThreads) void conv_f16_kernel(const uint16_t* __re
     }
 }
 
+// log2 of the smallest power of two >= v, but never above cap (cap >= 1):
+// the result p satisfies 1 <= (1 << p) <= cap.
 int log2_ceil_pow2(int v, int cap)
 {
     int sh = 0;
-    while ((1 << sh) < v && (1 << sh) < cap) ++sh;
+    while ((1 << sh) < v && (2 << sh) <= cap) ++sh;
     return sh;
 }
 

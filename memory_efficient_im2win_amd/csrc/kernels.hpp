@@ -26,6 +26,15 @@ int launch_conv_f32(const float* x, const float* ws, const float* w, float* y,
 int launch_conv_f16(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float* y,
                     const ConvShape& c, hipStream_t stream);
 
+// Fused fp16 convolution (im2win window tiles built in LDS). wpk is the
+// filter prepacked by launch_f16_filter_pack, or nullptr to gather the
+// filters from w inside the kernel. -1 if the shape is outside its envelope.
+int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk, float* y,
+                          const ConvShape& c, hipStream_t stream);
+// Bytes of the prepacked fp16 filter for the fused kernel (0: not used).
+size_t f16_filter_pack_bytes(const ConvShape& c);
+int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, hipStream_t stream);
+
 // Plain fallbacks (one thread per output) for shapes the tiled kernels do
 // not take; ws as above.
 int launch_conv_generic_f32(const float* x, const float* ws, const float* w, float* y,

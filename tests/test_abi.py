@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["im2win_workspace_bytes", "im2win_output_dims", "im2win_pack", "conv2d_im2win_fp32",
-         "conv2d_im2win_fp16", "im2win_status_string"])
+         "conv2d_im2win_fp16", "conv2d_im2win_workspace_bytes", "im2win_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -97,11 +97,32 @@ def test_conv_rejects_bad_arguments_before_launch(fn):
     # misaligned tensors
     odd = ctypes.c_void_p(0x10001)
     assert f(odd, FAKE, FAKE, None, 0, *ok, None) == _lib.IM2WIN_EINVAL
-    # workspace: NULL with a size, or smaller than one image's im2win rows
+    # workspace: NULL with a size, or smaller than its smallest valid size
+    e = 4 if fn.endswith("32") else 2
+    F = m.conv_workspace_bytes(1, 3, 8, 8, 4, 3, 3, 1, e, False)
+    I = m.workspace_bytes(1, 3, 8, 8, 3, 3, 1, e)
+    smallest = F if F else I
     assert f(FAKE, FAKE, FAKE, None, 64, *ok, None) == _lib.IM2WIN_EWORKSPACE
-    per_image = m.workspace_bytes(1, 3, 8, 8, 3, 3, 1, 4 if fn.endswith("32") else 2)
-    assert f(FAKE, FAKE, FAKE, FAKE, per_image - 1, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, smallest - 1, *ok, None) == _lib.IM2WIN_EWORKSPACE
     assert f(FAKE, FAKE, FAKE, FAKE, 0, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    # workspace not 16-byte aligned
+    assert f(FAKE, FAKE, FAKE, ctypes.c_void_p(0x10008), smallest, *ok, None) == _lib.IM2WIN_EINVAL
+
+
+def test_conv_workspace_query():
+    # fp32: the fused path needs nothing; materialised = the im2win tensor.
+    assert m.conv_workspace_bytes(32, 3, 227, 227, 96, 11, 11, 4, 4, False) == 0
+    assert m.conv_workspace_bytes(32, 3, 227, 227, 96, 11, 11, 4, 4, True) == 52_736_640
+    # fp16: a prepacked filter (256-byte multiple, at least the filter) ahead of the im2win part.
+    for (N, Ci, Hi, Wi, Co, Hf, Wf, s) in [(64, 64, 224, 224, 64, 7, 7, 2),
+                                           (128, 96, 24, 24, 256, 5, 5, 1),
+                                           (64, 3, 227, 227, 64, 7, 7, 2)]:
+        F = m.conv_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s, 2, False)
+        assert F % 256 == 0 and F >= Co * Ci * Hf * Wf * 2
+        assert m.conv_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s, 2, True) == \
+            F + m.workspace_bytes(N, Ci, Hi, Wi, Hf, Wf, s, 2)
+    assert m.conv_workspace_bytes(1, 3, 4, 4, 2, 5, 5, 1, 2, False) == 0   # invalid shape
+    assert m.conv_workspace_bytes(1, 3, 8, 8, 2, 3, 3, 1, 3, False) == 0   # element size
 
 
 def test_pack_rejects_bad_arguments_before_launch():

@@ -32,16 +32,34 @@ SMALL = [
 ]
 
 
-def _run(sh, mode, x, w, ws_images=None):
+WS_KINDS = [None, "filter", "full", "one"]
+
+
+def _ws(sh, kind, dev):
+    """Workspace tensor for a call: None (fused, no workspace), "filter" (fused
+    with the fp16 filter prepacked; same as None for fp32), "full" (materialised
+    over the whole batch) or "one" (materialised one image at a time)."""
+    import torch
+    if kind is None:
+        return None
+    args = (sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
+    F = m.conv_workspace_bytes(*args, False)
+    if kind == "filter":
+        nb = F
+    elif kind == "full":
+        nb = m.conv_workspace_bytes(*args, True)
+    else:
+        nb = F + m.workspace_bytes(1, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
+    if nb == 0:
+        return None
+    return torch.empty(nb, dtype=torch.uint8, device=dev)
+
+
+def _run(sh, mode, x, w, ws_kind=None):
     import torch
     dev = device()
     xt, wt = to_dev(x, dev), to_dev(w, dev)
-    if ws_images is None:
-        y = m.conv2d(xt, wt, sh.s)
-    else:
-        per = m.workspace_bytes(1, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
-        ws = torch.empty(per * ws_images, dtype=torch.uint8, device=dev)
-        y = m.conv2d(xt, wt, sh.s, ws=ws)
+    y = m.conv2d(xt, wt, sh.s, ws=_ws(sh, ws_kind, dev))
     out = y.cpu().numpy()
     torch.cuda.synchronize()
     return out
@@ -57,10 +75,10 @@ def test_conv_small_uniform(t, dt, orc):
     sh = _shape(t, dt)
     x, w = workloads.make_inputs(sh, seed=11)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
-    for ws_images in (None, sh.N, 1):
-        note(f"conv uniform {sh.describe()} ws_images={ws_images}")
-        y = _run(sh, dt, x, w, ws_images)
-        assert_within(y, ref, absd, TOL[dt], f"{sh.describe()} ws_images={ws_images}")
+    for kind in WS_KINDS:
+        note(f"conv uniform {sh.describe()} ws={kind}")
+        y = _run(sh, dt, x, w, kind)
+        assert_within(y, ref, absd, TOL[dt], f"{sh.describe()} ws={kind}")
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
@@ -69,9 +87,9 @@ def test_conv_small_integer_exact(t, dt, orc):
     sh = _shape(t, dt)
     x, w = workloads.make_inputs(sh, seed=12, mode="int")
     ref = orc.conv_direct(x, w, sh.s)
-    for ws_images in (None, 2):
-        note(f"conv integer {sh.describe()} ws_images={ws_images}")
-        assert_exact(_run(sh, dt, x, w, ws_images), ref, f"{sh.describe()} ws_images={ws_images}")
+    for kind in WS_KINDS:
+        note(f"conv integer {sh.describe()} ws={kind}")
+        assert_exact(_run(sh, dt, x, w, kind), ref, f"{sh.describe()} ws={kind}")
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
@@ -81,9 +99,9 @@ def test_conv_generic_fallback_large_filter(dt, orc):
     sh = _shape((1, 9, 20, 600, 7, 13, 13, 2), dt)
     x, w = workloads.make_inputs(sh, seed=13)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
-    for ws_images in (None, 1):
-        note(f"conv large filter {sh.describe()} ws_images={ws_images}")
-        assert_within(_run(sh, dt, x, w, ws_images), ref, absd, TOL[dt], sh.describe())
+    for kind in WS_KINDS:
+        note(f"conv large filter {sh.describe()} ws={kind}")
+        assert_within(_run(sh, dt, x, w, kind), ref, absd, TOL[dt], sh.describe())
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
@@ -98,8 +116,8 @@ def test_conv_special_values(dt, orc):
     w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)  # no zero taps, fixed signs
     ref = orc.conv_direct(x, w, sh.s)
     note(f"conv special values {sh.describe()}")
-    for ws_images in (None, 1):
-        y = _run(sh, dt, x, w, ws_images).astype(np.float64)
+    for kind in WS_KINDS:
+        y = _run(sh, dt, x, w, kind).astype(np.float64)
         assert np.array_equal(np.isnan(y), np.isnan(ref))
         assert np.array_equal(np.isposinf(y), np.isposinf(ref))
         assert np.array_equal(np.isneginf(y), np.isneginf(ref))
@@ -118,20 +136,22 @@ def test_conv_writes_only_its_output(dt, orc):
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
     n = ref.size
     note(f"conv guard bands {sh.describe()}")
-    for use_ws in (False, True):
+    for kind in WS_KINDS:
         big = torch.full((n + 2 * 129,), float("nan"), dtype=torch.float32, device=dev)
         out = big[129:129 + n].view(ref.shape)
+        ws = _ws(sh, kind, dev)
+        wsbig = None
         kw = {}
-        if use_ws:
-            per = m.workspace_bytes(1, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
-            wsbig = torch.full((per + 4096,), 0x7F, dtype=torch.uint8, device=dev)
-            kw = dict(ws=wsbig, ws_bytes=per)
+        if ws is not None:
+            nb = ws.numel()
+            wsbig = torch.full((nb + 4096,), 0x7F, dtype=torch.uint8, device=dev)
+            kw = dict(ws=wsbig, ws_bytes=nb)
         m.conv2d(to_dev(x, dev), to_dev(w, dev), sh.s, out=out, **kw)
         b = big.cpu().numpy()
         assert np.isnan(b[:129]).all() and np.isnan(b[129 + n:]).all()
-        assert_within(b[129:129 + n].reshape(ref.shape), ref, absd, TOL[dt], "guarded output")
-        if use_ws:
-            assert (wsbig[per:].cpu().numpy() == 0x7F).all()
+        assert_within(b[129:129 + n].reshape(ref.shape), ref, absd, TOL[dt], f"guarded output {kind}")
+        if wsbig is not None:
+            assert (wsbig[nb:].cpu().numpy() == 0x7F).all()
 
 
 @pytest.mark.slow
@@ -139,9 +159,10 @@ def test_conv_writes_only_its_output(dt, orc):
                                  "cv4_f16_n64"])
 @pytest.mark.parametrize("mode", ["uniform", "int"])
 def test_conv_full_size_sampled(key, mode, orc):
-    """The benchmark layers at full size, fused and materialised (the two
-    launch configurations the benchmark times), checked at ~3000 outputs
-    the oracle computes one by one (corners included)."""
+    """The benchmark layers at full size in every launch configuration the
+    benchmark times (fused; fused with a prepacked fp16 filter; materialised),
+    checked at ~3000 outputs the oracle computes one by one (corners
+    included)."""
     import torch
     dev = device()
     sh = workloads.BY_KEY[key]
@@ -150,10 +171,11 @@ def test_conv_full_size_sampled(key, mode, orc):
     idx = workloads.sample_output_indices(sh, Ho, Wo, 3000)
     ref, absd = orc.conv_points(x, w, sh.s, idx)
     xt, wt = to_dev(x, dev), to_dev(w, dev)
-    nb = m.workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
-    for ws in (None, torch.empty(nb, dtype=torch.uint8, device=dev)):
-        note(f"conv full {sh.describe()} {mode} ws={'full' if ws is not None else 'none'}")
-        y = m.conv2d(xt, wt, sh.s, ws=ws).reshape(-1)
+    for kind in (None, "filter", "full"):
+        if kind == "filter" and sh.dtype == "f32":
+            continue
+        note(f"conv full {sh.describe()} {mode} ws={kind}")
+        y = m.conv2d(xt, wt, sh.s, ws=_ws(sh, kind, dev)).reshape(-1)
         got = y[torch.from_numpy(idx).to(dev)].cpu().numpy()
         assert bool(torch.isfinite(y).all())
         if mode == "int":
