@@ -16,8 +16,10 @@
 //    interleaved (16-byte entry = 8 channels of one input pixel), each input
 //    row stored once even where the im2win rows of consecutive output rows
 //    overlap (s < Hf). Output rows of different images get separate rows.
-//    The window of a pixel is then Hf runs of Wf entries, and every lane's
-//    8-element K slice of B is one 16-byte LDS read.
+//    Within a row the columns are stored stride-phase major, so the window
+//    of a pixel is Hf x Wf entries at fixed offsets from its tap (0, 0), the
+//    32 pixels of an MFMA block read 32 consecutive entries for every tap,
+//    and every lane's 8-element K slice of B is one 16-byte LDS read.
 //  * The filters of the group are staged as entries (tap j, channel co) in
 //    the same K order, from the caller's prepacked copy when a workspace is
 //    given (contiguous 16-byte loads) or gathered from w otherwise.
@@ -45,15 +47,30 @@ struct FusedArgs {
     int64_t px_tiles, total;
     int rows_max, kmax, dup, RIN;   // output rows per tile, image breaks, s<Hf overlap, LDS rows
     int HW, HWp, CG, Copad;
-    int xentries;                   // RIN * Wi
-    int xunits;                     // RIN * Wi / 8 (vector staging)
-    bool xvec;                      // Wi % 8 == 0: rows fetched as 16-byte vectors
-    FastDiv divWo, divHo, divWi, divHWp, divCot;
+    int NU, RS;                     // columns per stride phase ceil(Wi/s); entries per LDS row s*NU
+    int xentries;                   // LDS entries of the input rows: RIN * RS
+    int xunits;                     // staging units: RIN * Wi / 2 (paired) or RIN * Wi
+    bool xpair;                     // Wi even: rows fetched 2 columns x 8 channels at a time
+    bool aligned;                   // tiles never cross images (kmax = 0)
+    int64_t tiles_per_image;        // aligned tiling: ceil(Ho*Wo / P)
+    int NWH, HPH;                   // filter stages per channel group, tap pairs per stage
+    uint32_t xbytes, ybytes;        // sizes of x and y (each below 4 GiB: buffer addressing)
+    FastDiv divWo, divHo, divWi, divHalfW, divS;
 };
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi)
 {
     return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+// Raw buffer resource over [base, base + bytes) (gfx9-family descriptor).
+// Loads at offsets >= bytes return 0 and stores there are dropped, which the
+// kernel uses instead of per-lane branches; kNoOff is always out of range.
+constexpr uint32_t kNoOff = 0xFFFFFFF0u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
 }
 
 // Filters of channel group g as 16-byte entries (tap j, channel co):
@@ -80,11 +97,14 @@ __global__ __launch_bounds__(256) void f16_filter_pack_kernel(const uint16_t* __
 }
 
 // Per-thread staging capacities (checked by the planner).
-constexpr int kXUnits = 2;    // input units of 8 columns x 8 channels (vector path)
-constexpr int kXEnt = 10;     // input entries (gather path)
+constexpr int kXUnits = 6;    // input units of 2 columns x 8 channels (paired path)
+constexpr int kXEnt = 12;     // input entries (gather path)
 constexpr int kWEnt = 8;      // filter entries
 
-template <int WCO, int WPX, int NB, bool XVEC, bool WPK>
+// LDS layout of one staged input row: column c is entry (c % s)*NU + c / s
+// (stride-phase major), so the 32 pixels of an MFMA block, whose window
+// columns are wo*s + kw, read 32 consecutive entries for every tap.
+template <int WCO, int WPX, int NB, bool XPAIR, bool WPK>
 __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint4* __restrict__ wpk, float* __restrict__ y, FusedArgs a)
@@ -98,13 +118,21 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
 
     const int Ci = a.c.Ci, Hi = a.c.Hi, Wi = a.c.Wi, Co = a.c.Co, s = a.c.s;
     const int Ho = a.c.Ho, Wo = a.c.Wo, Hf = a.c.Hf, Wf = a.c.Wf;
-    const int HW = a.HW, HWp = a.HWp;
+    const int HW = a.HW, HWp = a.HWp, RS = a.RS, NU = a.NU;
 
     const int co_t = (int)(blockIdx.x % a.co_tiles);
     const int64_t pt = blockIdx.x / a.co_tiles;
     const int co0 = co_t * COT;
-    const int64_t q0 = pt * a.P;
-    const int64_t qend = q0 + a.P < a.total ? q0 + a.P : a.total;
+    int64_t q0, qend;
+    if (a.aligned) {   // tile pt = (image, tile within the image)
+        const int64_t img = pt / a.tiles_per_image;
+        const int64_t plane = (int64_t)Ho * Wo;
+        q0 = img * plane + (pt - img * a.tiles_per_image) * a.P;
+        qend = min(q0 + a.P, (img + 1) * plane);
+    } else {
+        q0 = pt * a.P;
+        qend = q0 + a.P < a.total ? q0 + a.P : a.total;
+    }
     const int gr0 = (int)(q0 / Wo);
     const int grl = (int)((qend - 1) / Wo);
     const int n0 = (int)a.divHo.div((uint32_t)gr0);
@@ -115,8 +143,8 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     const int wave = uniform(tid >> 6);
     const int wco = wave % WCO, wpx = wave / WCO;
 
-    // LDS row of output row gr (tile-relative r = gr - gr0, image k):
-    // r*s + k*dup; its kh-th input row sits kh rows further.
+    // Entry of tap (0, 0) of each pixel: LDS row of its output row gr
+    // (tile-relative r = gr - gr0, image k: r*s + k*dup) times RS, plus wo.
     int xb[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -125,9 +153,10 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
         const int gr = (int)a.divWo.div((uint32_t)(q - (int64_t)gr0 * Wo)) + gr0;
         const int wo = (int)(q - (int64_t)gr * Wo);
         const int k = (int)a.divHo.div((uint32_t)gr) - n0;
-        xb[b] = ((gr - gr0) * s + k * a.dup) * Wi + wo * s;
+        xb[b] = ((gr - gr0) * s + k * a.dup) * RS + wo;
     }
-    const int arow = wco * 64 + l32;   // A entry column for co block 0 of this wave
+    // A entry of this lane for tap pair 0: tap hl, channel column wco*64 + l32.
+    const int abase = hl * COT + wco * 64 + l32;
 
     floatx16_t acc[2][NB];
 #pragma unroll
@@ -154,167 +183,281 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
         }
         return false;
     };
+    auto col_entry = [&](int c) {
+        const int u = (int)a.divS.div((uint32_t)c);
+        return (c - u * s) * NU + u;
+    };
 
     // ---- staging: global -> registers (group g) -> LDS --------------------------
-    // Vector path: a unit is 8 consecutive columns of one LDS row; it is
-    // fetched as 8 channels x 16 bytes and transposed into 8 entries.
-    uint4 xv[XVEC ? kXUnits * 8 : 1];
-    uint4 xg[XVEC ? 1 : kXEnt];
+    // Paired path: a unit is 2 consecutive columns of one LDS row, fetched as
+    // 8 channels x 4 bytes and split into 2 entries. Where a unit reads from
+    // and writes to does not depend on the channel group, so it is worked out
+    // once: a byte offset from channel 0 of image 0 (the channel plane is a
+    // uniform base per load) and two LDS entries.
+    constexpr int NXU = XPAIR ? kXUnits : kXEnt;
+    uint32_t xp[XPAIR ? kXUnits * 8 : 1];
+    uint4 xg[XPAIR ? 1 : kXEnt];
     uint4 wv[kWEnt];
-    const int wcols = Wi >> 3;
-
-    auto load_group = [&](int g) {
-        const int cb = 8 * g;
-        const int64_t cstride = (int64_t)Hi * Wi;
-        if (XVEC) {
+    uint32_t uoff[NXU];          // source byte offset from channel 0 (kNoOff: no source)
+    int udst0[NXU], udst1[NXU];  // LDS entries (udst0 < 0: unit not staged)
+    const int hcols = Wi >> 1;
+    const int64_t cstride = (int64_t)Hi * Wi;
 #pragma unroll
-            for (int u = 0; u < kXUnits; ++u) {
-                const int e = tid + u * NT;          // unit = (row i, column block)
-                const int i = e / wcols, cblk = e - (e / wcols) * wcols;
-                int n = 0, h = 0;
-                const bool ok = e < a.xunits && x_src(i, n, h);
-                const uint4* src = reinterpret_cast<const uint4*>(
-                    x + (((int64_t)n * Ci + cb) * Hi + h) * Wi + cblk * 8);
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    xv[u * 8 + q] = ok && cb + q < Ci ? src[q * (cstride >> 3)] : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < NXU; ++u) {
+        const int e = tid + u * NT;
+        udst0[u] = udst1[u] = -1;
+        uoff[u] = kNoOff;
+        if (e < a.xunits) {
+            int i, col;
+            if (XPAIR) {
+                i = (int)a.divHalfW.div((uint32_t)e);
+                col = 2 * (e - i * hcols);
+                udst1[u] = i * RS + col_entry(col + 1);
+            } else {
+                i = (int)a.divWi.div((uint32_t)e);
+                col = e - i * Wi;
             }
-        } else {
-#pragma unroll
-            for (int u = 0; u < kXEnt; ++u) {
-                const int e = tid + u * NT;
-                uint32_t v[4] = {0, 0, 0, 0};
-                if (e < a.xentries) {
-                    const int i = (int)a.divWi.div((uint32_t)e), col = e - i * Wi;
-                    int n, h;
-                    if (x_src(i, n, h)) {
-                        const uint16_t* src = x + (((int64_t)n * Ci + cb) * Hi + h) * Wi + col;
-#pragma unroll
-                        for (int q = 0; q < 8; ++q)
-                            if (cb + q < Ci) v[q >> 1] |= (uint32_t)src[q * cstride] << (16 * (q & 1));
-                    }
-                }
-                xg[u] = make_uint4(v[0], v[1], v[2], v[3]);
-            }
+            udst0[u] = i * RS + col_entry(col);
+            int n, h;
+            if (x_src(i, n, h))
+                uoff[u] = (uint32_t)(((((int64_t)n * Ci) * Hi + h) * Wi + col) * 2);
         }
-        const int wentries = HWp * COT;
+    }
+    // Filter entries of a stage: byte offsets from the stage's first tap.
+    const int wstage = 2 * a.HPH * COT;   // filter entries per stage
+    uint32_t woff[kWEnt];
 #pragma unroll
-        for (int u = 0; u < kWEnt; ++u) {
-            const int e = tid + u * NT;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (e < wentries) {
-                const int j = e / COT, col = e - (e / COT) * COT;
-                if (WPK) {
-                    val = wpk[((int64_t)g * HWp + j) * a.Copad + co0 + col];
-                } else if (j < HW && co0 + col < Co) {
-                    const uint16_t* src = w + ((int64_t)(co0 + col) * Ci + cb) * HW + j;
+    for (int u = 0; u < kWEnt; ++u) {
+        const int e = tid + u * NT;
+        const int jj = e / COT, col = e - (e / COT) * COT;
+        if (WPK)
+            woff[u] = e < wstage ? (uint32_t)((jj * a.Copad + co0 + col) * 16) : kNoOff;
+        else
+            woff[u] = e < wstage && co0 + col < Co
+                          ? (uint32_t)((((int64_t)(co0 + col) * Ci) * HW + jj) * 2)
+                          : kNoOff;
+    }
+
+    // Stage st = (channel group g, filter part h): the input rows of group g
+    // are staged with part 0; part h holds taps [2*h*HPH, 2*(h+1)*HPH).
+    auto load_stage = [&](int st) {
+        const int g = st / a.NWH, h = st - (st / a.NWH) * a.NWH;
+        const int cb = 8 * g;
+        if (h == 0) {
+            // One buffer per channel plane; a missing channel gets an empty buffer.
+            __amdgpu_buffer_rsrc_t pl[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int64_t first = (int64_t)(cb + q) * cstride * 2;
+                pl[q] = buf(x + (int64_t)(cb + q < Ci ? cb + q : 0) * cstride,
+                            cb + q < Ci ? (uint32_t)(a.xbytes - first) : 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < NXU; ++u) {
+                if (XPAIR) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        xp[u * 8 + q] = __builtin_amdgcn_raw_buffer_load_b32(pl[q], (int)uoff[u], 0, 0);
+                } else {
                     uint32_t v[4] = {0, 0, 0, 0};
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
-                        if (cb + q < Ci) v[q >> 1] |= (uint32_t)src[q * HW] << (16 * (q & 1));
-                    val = make_uint4(v[0], v[1], v[2], v[3]);
+                        if (cb + q < Ci)
+                            v[q >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                             pl[q], (int)uoff[u], 0, 0)
+                                         << (16 * (q & 1));
+                    xg[u] = make_uint4(v[0], v[1], v[2], v[3]);
                 }
             }
-            wv[u] = val;
         }
-    };
-    auto store_group = [&]() {
-        if (XVEC) {
+        const int j0 = 2 * h * a.HPH;
+        if (WPK) {
+            // Taps j0 .. HWp-1 of group g; entries past HWp read as zero.
+            const __amdgpu_buffer_rsrc_t wb =
+                buf(wpk + ((int64_t)g * HWp + j0) * a.Copad, (uint32_t)((HWp - j0) * a.Copad * 16));
 #pragma unroll
-            for (int u = 0; u < kXUnits; ++u) {
-                const int e = tid + u * NT;
-                if (e >= a.xunits) continue;
-                const int i = e / wcols, cblk = e - (e / wcols) * wcols;
-                uint4* dst = X + i * Wi + cblk * 8;
-                // d[c] = columns 0..7 of channel c; entry m = channels 0..7 of column m.
-                const uint32_t* d = reinterpret_cast<const uint32_t*>(&xv[u * 8]);
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const int sh = 16 * (m & 1), k = m >> 1;
-                    uint32_t e4[4];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const uint32_t lo = (d[(2 * p) * 4 + k] >> sh) & 0xffffu;
-                        const uint32_t hi = (d[(2 * p + 1) * 4 + k] >> sh) & 0xffffu;
-                        e4[p] = lo | (hi << 16);
-                    }
-                    dst[m] = make_uint4(e4[0], e4[1], e4[2], e4[3]);
-                }
+            for (int u = 0; u < kWEnt; ++u) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(wb, (int)woff[u], 0, 0);
+                wv[u] = make_uint4(v[0], v[1], v[2], v[3]);
             }
         } else {
+            // Gather from w: tap j0 + jj of channel cb + q is j0*2 + q*HW*2 bytes
+            // past the entry's offset; taps past HW read as zero (short buffer).
+            const __amdgpu_buffer_rsrc_t wb =
+                buf(w, (uint32_t)((int64_t)Co * Ci * HW * 2));
 #pragma unroll
-            for (int u = 0; u < kXEnt; ++u) {
-                const int e = tid + u * NT;
-                if (e < a.xentries) X[e] = xg[u];
+            for (int u = 0; u < kWEnt; ++u) {
+                const int jj = (tid + u * NT) / COT;
+                const bool ok = j0 + jj < HW;
+                uint32_t v[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (cb + q < Ci)
+                        v[q >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                         wb, (int)(ok ? woff[u] : kNoOff),
+                                         (int)(((int64_t)(cb + q) * HW + j0) * 2), 0)
+                                     << (16 * (q & 1));
+                wv[u] = make_uint4(v[0], v[1], v[2], v[3]);
             }
         }
-        const int wentries = HWp * COT;
+    };
+    auto store_stage = [&](int st) {
+        if (st % a.NWH == 0) {
+#pragma unroll
+            for (int u = 0; u < NXU; ++u) {
+                if (udst0[u] < 0) continue;
+                if (XPAIR) {
+                    const uint32_t* d = &xp[u * 8];   // d[c]: channel c, columns col (lo), col+1 (hi)
+                    uint4 lo, hi;
+                    lo.x = (d[0] & 0xffffu) | (d[1] << 16);
+                    lo.y = (d[2] & 0xffffu) | (d[3] << 16);
+                    lo.z = (d[4] & 0xffffu) | (d[5] << 16);
+                    lo.w = (d[6] & 0xffffu) | (d[7] << 16);
+                    hi.x = (d[0] >> 16) | (d[1] & 0xffff0000u);
+                    hi.y = (d[2] >> 16) | (d[3] & 0xffff0000u);
+                    hi.z = (d[4] >> 16) | (d[5] & 0xffff0000u);
+                    hi.w = (d[6] >> 16) | (d[7] & 0xffff0000u);
+                    X[udst0[u]] = lo;
+                    X[udst1[u]] = hi;
+                } else {
+                    X[udst0[u]] = xg[u];
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < kWEnt; ++u) {
             const int e = tid + u * NT;
-            if (e < wentries) Wl[e] = wv[u];
+            if (e < wstage) Wl[e] = wv[u];
         }
     };
 
-    const int nsteps = HWp >> 1;
+    // Taps in filter order j = kh*Wf + kw; a tap's LDS offset from the
+    // pixel's tap (0, 0) is kh*RS + (kw % s)*NU + kw / s. The walk is uniform
+    // (scalar unit) and avoids divisions.
+    struct Tap {
+        int kh, kw, ph, u;
+    };
+    auto tap_off = [&](const Tap& t) { return t.kh * RS + t.ph * NU + t.u; };
+    auto tap_next = [&](Tap& t) {
+        if (++t.kw == Wf) {
+            t.kw = 0; t.ph = 0; t.u = 0; ++t.kh;
+        } else if (++t.ph == s) {
+            t.ph = 0; ++t.u;
+        }
+    };
+    // Fragments of one tap pair: A for the two 32-channel blocks, B for the
+    // NB pixel blocks.
+    struct Frags {
+        half8_t a[2], b[NB];
+    };
+    auto fetch = [&](Frags& f, int offA, int offB, int t) {
+        const int off = hl ? offB : offA;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint4 u = Wl[abase + 2 * t * COT + i * 32];
+            __builtin_memcpy(&f.a[i], &u, 16);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint4 u = X[xb[b] + off];
+            __builtin_memcpy(&f.b[b], &u, 16);
+        }
+    };
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                acc[i][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[b], acc[i][b], 0, 0, 0);
+    };
+
+    const int nfull = HW >> 1;          // tap pairs with two real taps
     const bool odd = (HW & 1) != 0;
 
-    load_group(0);
-    store_group();
-    __syncthreads();
-    for (int g = 0; g < a.CG; ++g) {
-        if (g + 1 < a.CG) load_group(g + 1);
+    const int npairs = nfull + (odd ? 1 : 0);
+    const int nstages = a.CG * a.NWH;
+    Tap ta = {0, 0, 0, 0};
+    auto fetch_pair = [&](Frags& f, int tl) {
+        Tap tb = ta;
+        tap_next(tb);
+        fetch(f, tap_off(ta), tap_off(tb), tl);
+        ta = tb;
+        tap_next(ta);
+    };
 
-        // Tap pair t: lanes 0-31 take tap 2t, lanes 32-63 tap 2t+1, taps in
-        // filter order j = kh*Wf + kw.
-        int kh = 0, kw = hl;
-        if (kw >= Wf) { kw -= Wf; ++kh; }
-        for (int t = 0; t < nsteps; ++t) {
-            const bool zero_b = odd && hl && t == nsteps - 1;   // padding tap j = HW
-            const int off = zero_b ? 0 : kh * Wi + kw;
-            half8_t av[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint4 u = Wl[(2 * t + hl) * COT + arow + i * 32];
-                __builtin_memcpy(&av[i], &u, 16);
-            }
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int st = 0; st < nstages; ++st) {
+        const int h = st % a.NWH;
+        if (st + 1 < nstages) load_stage(st + 1);
+        if (h == 0) ta = Tap{0, 0, 0, 0};
+
+        // Pairs [t0, t1) of this stage. Pair t holds taps 2t (lanes 0-31) and
+        // 2t+1 (lanes 32-63), walked in filter order on the scalar unit; the
+        // fragments of pair t+1 are read from LDS while the MFMAs of pair t run.
+        const int t0 = h * a.HPH, t1 = min(npairs, t0 + a.HPH);
+        const int tf = min(t1, nfull);
+        Frags f0, f1;
+        int t = t0;
+        if (t < tf) fetch_pair(f0, t - t0);
+        for (; t + 2 <= tf; t += 2) {
+            fetch_pair(f1, t + 1 - t0);
+            mma(f0);
+            if (t + 2 < tf) fetch_pair(f0, t + 2 - t0);
+            mma(f1);
+        }
+        if (t < tf) {
+            mma(f0);
+            ++t;
+        }
+        if (odd && t1 > nfull) {
+            // Last tap with a zero partner: the filter entry of tap HW is zero
+            // and lanes 32-63 zero their B slice (so Inf/NaN cannot leak in).
+            const int off = tap_off(ta);
+            fetch(f0, off, off, nfull - t0);
+            const uint32_t keep = hl ? 0u : ~0u;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                uint4 u = X[xb[b] + off];
-                if (zero_b) u = make_uint4(0, 0, 0, 0);
-                half8_t bv;
-                __builtin_memcpy(&bv, &u, 16);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    acc[i][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv, acc[i][b], 0, 0, 0);
+                uint4 u;
+                __builtin_memcpy(&u, &f0.b[b], 16);
+                u.x &= keep; u.y &= keep; u.z &= keep; u.w &= keep;
+                __builtin_memcpy(&f0.b[b], &u, 16);
             }
-            kw += 2;
-            while (kw >= Wf) { kw -= Wf; ++kh; }
+            mma(f0);
         }
 
-        if (g + 1 < a.CG) {
+        if (st + 1 < nstages) {
             __syncthreads();
-            store_group();
+            store_stage(st + 1);
             __syncthreads();
         }
     }
 
     // Output: lane holds pixel l32 of each block and channels
-    // 8*(r/4) + 4*hl + r%4 of each 32-channel block.
+    // 8*(r/4) + 4*hl + r%4 of each 32-channel block. Byte offset in y =
+    // per-lane part (image, pixel, 4*hl channels) + uniform part (channel).
+    const int64_t plane = (int64_t)Ho * Wo;
+    const __amdgpu_buffer_rsrc_t yb = buf(y, a.ybytes);
+    const bool all_co = co0 + COT <= Co;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int64_t q = q0 + (wpx * NB + b) * 32 + l32;
-        if (q >= qend) continue;
         const int gr = (int)(q / Wo);
         const int wo = (int)(q - (int64_t)gr * Wo);
         const int n = (int)a.divHo.div((uint32_t)gr), ho = gr - n * Ho;
-        float* yp = y + ((int64_t)n * Co * Ho + ho) * Wo + wo;
+        const uint32_t voff =
+            q < qend ? (uint32_t)((((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo) * 4)
+                     : kNoOff;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int co = co0 + wco * 64 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                if (co < Co) yp[(int64_t)co * Ho * Wo] = acc[i][b][r];
+                const int cu = co0 + wco * 64 + i * 32 + 8 * (r >> 2) + (r & 3);  // co - 4*hl
+                const float v = acc[i][b][r];
+                if (all_co || cu + 4 * hl < Co)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yb, (int)voff,
+                                                          (int)(cu * plane * 4), 0);
             }
     }
 }
@@ -331,31 +474,58 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
     a.dup = std::max(0, c.Hf - c.s);
     if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
     nb = 2;
-    wco = c.Co > 64 ? 2 : 1;
-    a.xvec = c.Wi % 8 == 0;
-    for (wpx = 8 / wco; wpx >= 1; wpx /= 2) {
-        a.co_tile = 64 * wco;
-        a.P = 32 * nb * wpx;
-        a.rows_max = (a.P - 1) / c.Wo + 2;
-        a.kmax = a.rows_max > 1 ? ceil_div(a.rows_max - 1, c.Ho) : 0;
-        a.RIN = (a.rows_max - 1) * c.s + c.Hf + a.kmax * a.dup;
-        a.xentries = a.RIN * c.Wi;
-        const int nt = 64 * wco * wpx;
-        const int wentries = a.HWp * a.co_tile;
-        const int64_t bytes = ((int64_t)a.xentries + wentries) * 16;
-        const bool xfit = a.xvec ? a.xentries / 8 <= kXUnits * nt : a.xentries <= kXEnt * nt;
-        if (bytes <= kMaxLds && xfit && wentries <= kWEnt * nt) break;
+    wco = 1;
+    a.xpair = c.Wi % 2 == 0;
+    a.NU = ceil_div(c.Wi, c.s);
+    a.RS = c.s * a.NU;
+    const int npairs = a.HWp / 2;
+    const int64_t plane = (int64_t)c.Ho * c.Wo;
+    // Smallest workgroup LDS first: two workgroups of four waves per CU let one
+    // stage its next channel group while the other runs MFMAs.
+    bool found = false;
+    for (int budget : {80 * 1024, kMaxLds}) {
+        for (wpx = 4; wpx >= 1; wpx /= 2) {
+            a.co_tile = 64 * wco;
+            a.P = 32 * nb * wpx;
+            a.rows_max = (a.P - 1) / c.Wo + 2;
+            a.tiles_per_image = (plane + a.P - 1) / a.P;
+            a.aligned = (double)(a.tiles_per_image * a.P) <= 1.05 * (double)plane;
+            a.kmax = a.aligned || a.rows_max <= 1 ? 0 : ceil_div(a.rows_max - 1, c.Ho);
+            a.RIN = (a.rows_max - 1) * c.s + c.Hf + a.kmax * a.dup;
+            a.xentries = a.RIN * a.RS;
+            a.xunits = a.xpair ? a.RIN * (c.Wi / 2) : a.RIN * c.Wi;
+            const int nt = 64 * wco * wpx;
+            if (a.xunits > (a.xpair ? kXUnits : kXEnt) * nt) continue;
+            for (a.NWH = 1; a.NWH <= npairs; ++a.NWH) {
+                a.HPH = ceil_div(npairs, a.NWH);
+                const int wentries = 2 * a.HPH * a.co_tile;
+                const int64_t bytes = ((int64_t)a.xentries + wentries) * 16;
+                if (bytes <= budget && wentries <= kWEnt * nt) {
+                    found = true;
+                    break;
+                }
+            }
+            if (found) break;
+        }
+        if (found) break;
     }
-    if (wpx < 1) return false;
-    a.xunits = a.xentries / 8;
+    if (!found) return false;
+    if (a.aligned) a.kmax = 0;
+    // Buffer addressing: x, y and the prepacked filter each below 4 GiB.
+    const int64_t xb = (int64_t)c.N * c.Ci * c.Hi * c.Wi * 2;
+    const int64_t yb = (int64_t)c.N * c.Co * c.Ho * c.Wo * 4;
+    const int64_t wb = (int64_t)a.CG * a.HWp * a.Copad * 16;
+    if (xb >= (int64_t)kNoOff || yb >= (int64_t)kNoOff || wb >= (int64_t)kNoOff) return false;
+    a.xbytes = (uint32_t)xb;
+    a.ybytes = (uint32_t)yb;
     a.co_tiles = ceil_div(c.Co, a.co_tile);
-    a.px_tiles = (a.total + a.P - 1) / a.P;
+    a.px_tiles = a.aligned ? (int64_t)c.N * a.tiles_per_image : (a.total + a.P - 1) / a.P;
     if (a.px_tiles * a.co_tiles > 0x7fffffff) return false;
     a.divWo = FastDiv((uint32_t)c.Wo);
     a.divHo = FastDiv((uint32_t)c.Ho);
     a.divWi = FastDiv((uint32_t)c.Wi);
-    a.divHWp = FastDiv((uint32_t)a.HWp);
-    a.divCot = FastDiv((uint32_t)a.co_tile);
+    a.divHalfW = FastDiv((uint32_t)std::max(1, c.Wi / 2));
+    a.divS = FastDiv((uint32_t)c.s);
     return true;
 }
 
@@ -369,7 +539,7 @@ int launch_t(const uint16_t* x, const uint16_t* w, const uint4* wpk, float* y,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
         attr = true;
     }
-    const size_t lds = ((size_t)a.xentries + (size_t)a.HWp * a.co_tile) * 16;
+    const size_t lds = ((size_t)a.xentries + (size_t)2 * a.HPH * a.co_tile) * 16;
     hipLaunchKernelGGL((conv_f16_fused_kernel<WCO, WPX, NB, XVEC, WPK>),
                        dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(64 * WCO * WPX), lds,
                        stream, x, w, wpk, y, a);
@@ -380,7 +550,7 @@ template <int WCO, int WPX>
 int launch_w(const uint16_t* x, const uint16_t* w, const uint4* wpk, float* y,
              const FusedArgs& a, hipStream_t stream)
 {
-    if (a.xvec)
+    if (a.xpair)
         return wpk ? launch_t<WCO, WPX, 2, true, true>(x, w, wpk, y, a, stream)
                    : launch_t<WCO, WPX, 2, true, false>(x, w, wpk, y, a, stream);
     return wpk ? launch_t<WCO, WPX, 2, false, true>(x, w, wpk, y, a, stream)
