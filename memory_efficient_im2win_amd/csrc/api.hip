@@ -1,6 +1,8 @@
 // C ABI of the im2win library: argument checks, workspace/mode selection and
 // kernel dispatch. Declarations and the contract are in include/im2win.h.
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 #include <stdint.h>
 
 #include "im2win.h"
@@ -108,9 +110,20 @@ int conv_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int
 }
 
 // Adapters to the driver's signatures.
+// fp32 fused: the matrix-core kernel where the shape fits its envelope,
+// else the vector-ALU kernel. IM2WIN_F32_PATH=valu selects the latter always.
+bool f32_valu_only()
+{
+    const char* v = std::getenv("IM2WIN_F32_PATH");
+    return v && std::strcmp(v, "valu") == 0;
+}
 int f32_fused(const float* x, const float* w, const void*, float* y, const ConvShape& c,
               hipStream_t st)
 {
+    if (!f32_valu_only()) {
+        const int rc = im2win::launch_conv_f32_mfma(x, w, y, c, st);
+        if (rc != -1) return rc;
+    }
     return im2win::launch_conv_f32(x, nullptr, w, y, c, st);
 }
 int f32_from_ws(const float* x, const float* ws, const float* w, float* y, const ConvShape& c,

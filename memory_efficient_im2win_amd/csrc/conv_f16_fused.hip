@@ -64,8 +64,9 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi)
 }
 
 // Raw buffer resource over [base, base + bytes) (gfx9-family descriptor).
-// Loads at offsets >= bytes return 0 and stores there are dropped, which the
-// kernel uses instead of per-lane branches; kNoOff is always out of range.
+// Loads at soffset + voffset >= bytes return 0, which the kernel uses instead
+// of per-lane branches; every load that can miss has soffset 0 and voffset
+// kNoOff, which is out of range for any buffer the planner accepts.
 constexpr uint32_t kNoOff = 0xFFFFFFF0u;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void* base, uint32_t bytes)
 {
@@ -281,21 +282,23 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
                 wv[u] = make_uint4(v[0], v[1], v[2], v[3]);
             }
         } else {
-            // Gather from w: tap j0 + jj of channel cb + q is j0*2 + q*HW*2 bytes
-            // past the entry's offset; taps past HW read as zero (short buffer).
+            // Gather from w: tap j0 + jj of channel cb + q is (q*HW + j0)*2 bytes
+            // past the entry's offset; missing taps and channels read as zero.
             const __amdgpu_buffer_rsrc_t wb =
                 buf(w, (uint32_t)((int64_t)Co * Ci * HW * 2));
 #pragma unroll
             for (int u = 0; u < kWEnt; ++u) {
                 const int jj = (tid + u * NT) / COT;
-                const bool ok = j0 + jj < HW;
+                const bool ok = j0 + jj < HW && woff[u] != kNoOff;
                 uint32_t v[4] = {0, 0, 0, 0};
 #pragma unroll
                 for (int q = 0; q < 8; ++q)
                     if (cb + q < Ci)
                         v[q >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
-                                         wb, (int)(ok ? woff[u] : kNoOff),
-                                         (int)(((int64_t)(cb + q) * HW + j0) * 2), 0)
+                                         wb,
+                                         (int)(ok ? woff[u] + (uint32_t)(((cb + q) * HW + j0) * 2)
+                                                  : kNoOff),
+                                         0, 0)
                                      << (16 * (q & 1));
                 wv[u] = make_uint4(v[0], v[1], v[2], v[3]);
             }
@@ -447,8 +450,8 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
         const int wo = (int)(q - (int64_t)gr * Wo);
         const int n = (int)a.divHo.div((uint32_t)gr), ho = gr - n * Ho;
         const uint32_t voff =
-            q < qend ? (uint32_t)((((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo) * 4)
-                     : kNoOff;
+            (uint32_t)((((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo) * 4);
+        if (q >= qend) continue;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll

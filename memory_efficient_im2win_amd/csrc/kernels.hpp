@@ -22,6 +22,12 @@ int launch_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, 
 int launch_conv_f32(const float* x, const float* ws, const float* w, float* y,
                     const ConvShape& c, hipStream_t stream);
 
+// fp32 convolution on the matrix cores (v_mfma_f32_32x32x2_f32), window
+// tiles built in LDS from x. -1 if the shape is outside its envelope. Small
+// problems split K and clear y first (atomics add the partial sums).
+int launch_conv_f32_mfma(const float* x, const float* w, float* y, const ConvShape& c,
+                         hipStream_t stream);
+
 // fp16 x fp16 -> fp32 convolution on the matrix cores; ws as above.
 int launch_conv_f16(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float* y,
                     const ConvShape& c, hipStream_t stream);

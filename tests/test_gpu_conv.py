@@ -29,6 +29,7 @@ SMALL = [
     (1, 9, 16, 16, 17, 2, 2, 5),      # s > Hf, Wf
     (1, 64, 30, 30, 64, 7, 7, 2),     # cv4-like slice
     (1, 96, 12, 12, 256, 5, 5, 1),    # cv5-like slice
+    (2, 3, 227, 227, 96, 11, 11, 4),  # cv1 images
 ]
 
 
@@ -90,6 +91,37 @@ def test_conv_small_integer_exact(t, dt, orc):
     for kind in WS_KINDS:
         note(f"conv integer {sh.describe()} ws={kind}")
         assert_exact(_run(sh, dt, x, w, kind), ref, f"{sh.describe()} ws={kind}")
+
+
+@pytest.mark.parametrize("t", SMALL, ids=str)
+def test_conv_f32_vector_alu_path(t, orc, monkeypatch):
+    """fp32 on the vector-ALU kernel (the fallback of the matrix-core one)."""
+    monkeypatch.setenv("IM2WIN_F32_PATH", "valu")
+    sh = _shape(t, "f32")
+    x, w = workloads.make_inputs(sh, seed=16)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    for kind in (None, "one"):
+        note(f"conv fp32 vector ALU {sh.describe()} ws={kind}")
+        assert_within(_run(sh, "f32", x, w, kind), ref, absd, TOL["f32"], sh.describe())
+    xi, wi = workloads.make_inputs(sh, seed=17, mode="int")
+    note(f"conv fp32 vector ALU integer {sh.describe()}")
+    assert_exact(_run(sh, "f32", xi, wi), orc.conv_direct(xi, wi, sh.s), sh.describe())
+
+
+@pytest.mark.parametrize("ksplit", [1, 3])
+@pytest.mark.parametrize("t", [(1, 96, 12, 12, 256, 5, 5, 1), (2, 16, 20, 20, 40, 3, 3, 1),
+                               (3, 7, 26, 26, 33, 5, 5, 1)], ids=str)
+def test_conv_f32_k_split(t, ksplit, orc, monkeypatch):
+    """The matrix-core fp32 kernel with K split over workgroups (partial sums
+    added into the cleared output) and without."""
+    monkeypatch.setenv("IM2WIN_F32_KSPLIT", str(ksplit))
+    sh = _shape(t, "f32")
+    x, w = workloads.make_inputs(sh, seed=18)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    note(f"conv fp32 ksplit={ksplit} {sh.describe()}")
+    assert_within(_run(sh, "f32", x, w), ref, absd, TOL["f32"], sh.describe())
+    xi, wi = workloads.make_inputs(sh, seed=19, mode="int")
+    assert_exact(_run(sh, "f32", xi, wi), orc.conv_direct(xi, wi, sh.s), sh.describe())
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
