@@ -28,6 +28,10 @@
 //    the zero-filled output with hardware float atomics.
 #include <algorithm>
 #include <cstdlib>
+#include <map>
+#include <mutex>
+#include <set>
+#include <utility>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -37,9 +41,8 @@ namespace im2win {
 namespace {
 
 constexpr int kMaxLds = 160 * 1024;
-constexpr int kNT = 256;      // four waves
-constexpr int kP = 128;       // pixels per tile: 32 per wave
-constexpr int kRPW = 8;       // input rows per wave and stage (32 per workgroup)
+// Input rows per wave and stage for NW waves (32, 40 or 48 per workgroup).
+constexpr int rows_per_wave(int nw) { return nw == 4 ? 8 : nw == 8 ? 5 : 4; }
 constexpr uint32_t kMaxBuf = 0xFFFFFFF0u;   // buffer ranges are 32-bit
 
 struct MArgs {
@@ -48,88 +51,89 @@ struct MArgs {
     int64_t px_tiles, total, tiles_per_image;
     bool aligned;                     // tiles never cross images
     int rows_max, kmax, dup, RIN;     // output rows per tile, image breaks, s<Hf overlap, LDS rows
-    int HW, CB, nstages, KSP;         // taps; channels per stage; stages; filter row pitch (odd)
+    int HW, CB, nstages, KSP, KT;     // taps; channels per stage; stages; filter row pitch (odd);
+                                      // K offset table entries
     int NU, RS, CSX, xent;            // entries per phase, per row (s*NU), per channel; total
-    uint32_t ybytes;
+    uint32_t xbytes, wbytes, ybytes;
     FastDiv divWo, divHo, divS;
 };
 
 // Raw buffer resource over [base, base + bytes): loads at soffset + voffset
 // + offset >= bytes return 0 (the scalar offset counts in the range check).
+// The staging loads below use one resource per tensor, so a load past the
+// end of a row reads the next row (or 0 past the tensor) and is not stored.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void* base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                              0x00020000);
 }
 
-template <int WCO, int XCH, int WCH>
-__global__ __launch_bounds__(kNT) void conv_f32_mfma_kernel(const float* __restrict__ x,
-                                                            const float* __restrict__ w,
-                                                            float* __restrict__ y, MArgs a)
+template <int NW, int WCO, int XCH, int WCH>
+__global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, float* __restrict__ y, MArgs a)
 {
+    constexpr int NT = 64 * NW;
+    constexpr int P = 32 * NW;                    // pixels per tile
     constexpr int COT = 32 * WCO;
-    constexpr int WRW = COT / 4;   // filter rows per wave and stage
+    constexpr int RPW = rows_per_wave(NW);        // input rows per wave and stage
+    constexpr int WRW = (COT + NW - 1) / NW;      // filter rows per wave and stage
+    constexpr int KSP = 64 * WCH + 1;             // filter row pitch in LDS (odd)
 
     extern __shared__ __align__(16) float lds[];
     float* X = lds;
     float* Wl = lds + a.xent;
+    int* T = reinterpret_cast<int*>(Wl + WRW * NW * KSP);   // after WRW*NW filter rows
 
     const int Ci = a.c.Ci, Hi = a.c.Hi, Wi = a.c.Wi, Co = a.c.Co, s = a.c.s;
     const int Ho = a.c.Ho, Wo = a.c.Wo, Hf = a.c.Hf, Wf = a.c.Wf;
-    const int HW = a.HW, RS = a.RS, NU = a.NU, KSP = a.KSP, RIN = a.RIN, CB = a.CB;
-
-    // blockIdx.x = (pixel tile * ksplit + split) * co_tiles + channel tile
-    const int co_t = (int)(blockIdx.x % a.co_tiles);
-    const int rest = (int)(blockIdx.x / a.co_tiles);
-    const int ksi = rest % a.ksplit;
-    const int64_t pt = rest / a.ksplit;
-    const int co0 = co_t * COT;
-    const int st0 = ksi * a.spk, st1 = min(a.nstages, st0 + a.spk);
-    int64_t q0, qend;
-    if (a.aligned) {   // tile pt = (image, tile within the image)
-        const int64_t img = pt / a.tiles_per_image;
-        const int64_t plane = (int64_t)Ho * Wo;
-        q0 = img * plane + (pt - img * a.tiles_per_image) * kP;
-        qend = min(q0 + kP, (img + 1) * plane);
-    } else {
-        q0 = pt * kP;
-        qend = q0 + kP < a.total ? q0 + kP : a.total;
-    }
-    const int gr0 = (int)(q0 / Wo);
-    const int grl = (int)((qend - 1) / Wo);
-    const int n0 = (int)a.divHo.div((uint32_t)gr0);
+    const int HW = a.HW, RS = a.RS, NU = a.NU, RIN = a.RIN, CB = a.CB;
+    const int64_t plane = (int64_t)Ho * Wo;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int hl = lane >> 5, l32 = lane & 31;
     const int wave = uniform(tid >> 6);
 
-    // This lane's pixel: entry of its tap (0, 0) in a channel's LDS rows
-    // (row of output row gr: tile-relative r*s plus image breaks k*dup).
-    const int64_t qme = q0 + wave * 32 + l32;
-    int xb;
-    {
-        const int64_t q = qme < qend ? qme : qend - 1;
-        const int gr = (int)a.divWo.div((uint32_t)(q - (int64_t)gr0 * Wo)) + gr0;
-        const int wo = (int)(q - (int64_t)gr * Wo);
-        const int k = (int)a.divHo.div((uint32_t)gr) - n0;
-        xb = ((gr - gr0) * s + k * a.dup) * RS + wo;
-    }
-    const int abase = l32 * KSP + hl;   // A: channel l32 of each block, K index 2t + hl
+    // Work items (channel tile, K split, pixel tile), item =
+    // (pixel tile * ksplit + split) * co_tiles + channel tile. A workgroup
+    // takes items blockIdx.x, blockIdx.x + gridDim.x, ... and streams their
+    // stages back to back, so the next item's first stage is fetched while
+    // the current item's last stage runs.
+    const int64_t items = a.px_tiles * a.co_tiles * a.ksplit;
+    struct Item {
+        int co0, st0, st1, gr0, grl, n0;
+        int64_t q0, qend;
+    };
+    auto item_of = [&](int64_t it, Item& m) {
+        const int co_t = (int)(it % a.co_tiles);
+        const int64_t rest = it / a.co_tiles;
+        const int ksi = (int)(rest % a.ksplit);
+        const int64_t pt = rest / a.ksplit;
+        m.co0 = co_t * COT;
+        m.st0 = ksi * a.spk;
+        m.st1 = min(a.nstages, m.st0 + a.spk);
+        if (a.aligned) {   // pixel tile = (image, tile within the image)
+            const int64_t img = pt / a.tiles_per_image;
+            m.q0 = img * plane + (pt - img * a.tiles_per_image) * P;
+            m.qend = min(m.q0 + P, (img + 1) * plane);
+        } else {
+            m.q0 = pt * P;
+            m.qend = m.q0 + P < a.total ? m.q0 + P : a.total;
+        }
+        m.gr0 = (int)(m.q0 / Wo);
+        m.grl = (int)((m.qend - 1) / Wo);
+        m.n0 = (int)a.divHo.div((uint32_t)m.gr0);
+    };
 
-    floatx16_t acc[WCO];
-#pragma unroll
-    for (int i = 0; i < WCO; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-
-    // LDS row i -> (image n, input row h); false if no input row maps there.
-    auto x_src = [&](int i, int& n, int& h) -> bool {
+    // LDS row i of item m -> (image n, input row h); false if no input row
+    // maps there. Segment k holds the output rows of image n0+k in the tile,
+    // at LDS rows (first - gr0)*s + k*dup onwards.
+    auto x_src = [&](const Item& m, int i, int& n, int& h) -> bool {
         for (int k = 0; k <= a.kmax; ++k) {
-            const int nk = n0 + k;
-            const int first = max(gr0, nk * Ho), last = min(grl, nk * Ho + Ho - 1);
+            const int nk = m.n0 + k;
+            const int first = max(m.gr0, nk * Ho), last = min(m.grl, nk * Ho + Ho - 1);
             if (first > last) break;
-            const int S = (first - gr0) * s + k * a.dup;
+            const int S = (first - m.gr0) * s + k * a.dup;
             const int span = (last - first) * s + Hf;
             if (i >= S && i < S + span) {
                 n = nk;
@@ -140,206 +144,278 @@ __global__ __launch_bounds__(kNT) void conv_f32_mfma_kernel(const float* __restr
         return false;
     };
 
-    // Staging geometry, fixed for the tile. Wave v stages LDS rows
-    // r = v + 4*ii of a stage (channel r / RIN, row r % RIN), its lanes taking
-    // columns lane + 64*cc; the row's byte offset in x is the scalar offset of
-    // the load, the column the vector offset, and the buffer ends where the
-    // row does, so columns >= Wi read 0.
-    uint32_t xrow[kRPW];
-    uint32_t xvalid = 0;
-#pragma unroll
-    for (int ii = 0; ii < kRPW; ++ii) {
-        const int r = wave + 4 * ii;
-        const int cl = r / RIN, i = r - (r / RIN) * RIN;
-        int n = 0, h = 0;
-        xrow[ii] = 0;
-        if (cl < CB && x_src(i, n, h)) {
-            xrow[ii] = (uint32_t)(((((int64_t)n * Ci + cl) * Hi + h) * Wi) * 4);
-            xvalid |= 1u << ii;
+    // Offsets of the K indices of a stage (channel cl, kh, kw in filter
+    // order) from a pixel's tap (0, 0) of channel 0: cl*CSX + kh*RS +
+    // (kw % s)*NU + kw / s. Tabulated once per workgroup so that each lane
+    // reads its own index's offset (one LDS read per pair) instead of walking
+    // the taps on the scalar unit. Entries past the stage read as offset 0.
+    for (int k = tid; k < a.KT; k += NT) {
+        int off = 0;
+        if (k < CB * HW) {
+            const int cl = k / HW, j = k - (k / HW) * HW;
+            const int kh = j / Wf, kw = j - (j / Wf) * Wf;
+            off = cl * a.CSX + kh * RS + (kw % s) * NU + kw / s;
         }
+        T[k] = off;
     }
+
+    // ---- staging (load side: item L) ---------------------------------------
+    // Wave v stages LDS rows r = v + NW*ii of a stage (channel r / RIN, row
+    // r % RIN), its lanes taking columns lane + 64*cc: the row's byte offset
+    // in x is the scalar offset of the load, the column the vector offset.
+    // Filter rows co = v + NW*i, lanes taking taps lane + 64*jc. There are no
+    // per-row or per-lane branches: a row with no source gets a scalar offset
+    // past the end of x (it loads zeros) and is written to a spare LDS row;
+    // every lane column has an entry in its row (rows are padded to 64*XCH
+    // columns; those past Wi are never read); every lane tap has an entry in
+    // its filter row (pitch 64*WCH + 1).
+    Item L;
+    uint32_t xrow[RPW];   // byte offset in x from the stage's first channel, or past the end
+    int xdr[RPW];         // LDS row written (the spare row CB*RIN if none)
+    auto setup_load = [&](const Item& m) {
+#pragma unroll
+        for (int ii = 0; ii < RPW; ++ii) {
+            const int r = wave + NW * ii;
+            const int cl = r / RIN, i = r - (r / RIN) * RIN;
+            int n = 0, h = 0;
+            const bool ok = cl < CB && x_src(m, i, n, h);
+            xrow[ii] = ok ? (uint32_t)(((((int64_t)n * Ci + cl) * Hi + h) * Wi) * 4) : a.xbytes;
+            xdr[ii] = ok ? r : CB * RIN;
+        }
+    };
     const uint32_t lane4 = (uint32_t)lane * 4;
-    int xdst[XCH];   // LDS entry of column lane + 64*cc within a row; -1 past Wi
+    int xdst[XCH];   // LDS entry of column lane + 64*cc within a row
 #pragma unroll
     for (int cc = 0; cc < XCH; ++cc) {
         const int col = lane + 64 * cc;
         const int u = (int)a.divS.div((uint32_t)col);
-        xdst[cc] = col < Wi ? (col - u * s) * NU + u : -1;
+        xdst[cc] = (col - u * s) * NU + u;
     }
-
-    float xv[kRPW][XCH];
+    float xv[RPW][XCH];
     float wv[WRW][WCH];
-    const uint32_t rowb = (uint32_t)Wi * 4;
     const uint32_t wpitch = (uint32_t)Ci * HW * 4;   // bytes between filters
+    const __amdgpu_buffer_rsrc_t xr = buf(x, a.xbytes);
 
     auto load_stage = [&](int st) {
-        const int ci0 = st * CB, cbs = min(CB, Ci - ci0);
-        const uint32_t cofs = (uint32_t)ci0 * Hi * Wi * 4;
+        const int ci0 = st * CB;
+        // Opaque per stage, so the per-row offsets below are recomputed here
+        // rather than kept live across the stage loop.
+        uint32_t cofs = (uint32_t)ci0 * Hi * Wi * 4;
+        asm volatile("" : "+s"(cofs));
 #pragma unroll
-        for (int ii = 0; ii < kRPW; ++ii) {
-            if (((xvalid >> ii) & 1u) && wave + 4 * ii < cbs * RIN) {
-                const uint32_t so = xrow[ii] + cofs;
-                const __amdgpu_buffer_rsrc_t xr = buf(x, so + rowb);
+        for (int ii = 0; ii < RPW; ++ii) {
+            const uint32_t so = xrow[ii] + cofs;
 #pragma unroll
-                for (int cc = 0; cc < XCH; ++cc)
-                    xv[ii][cc] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                        xr, (int)(lane4 + 256 * cc), (int)so, 0));
-            }
+            for (int cc = 0; cc < XCH; ++cc)
+                xv[ii][cc] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    xr, (int)(lane4 + 256 * cc), (int)so, 0));
         }
         // Filters co0 + co, channels ci0 .. ci0 + cbs - 1: cbs*HW contiguous
-        // taps each; taps past that read as zero (the odd-K pad entry).
-        const float* wst = w + ((int64_t)co0 * Ci + ci0) * HW;
-        const uint32_t wlen = (uint32_t)(cbs * HW * 4);
+        // taps each (what a lane reads past them is replaced by zero when
+        // stored). Filters past Co read zeros (offset past the end).
+        const int64_t wfirst = ((int64_t)L.co0 * Ci + ci0) * HW;
+        const uint32_t wrange = a.wbytes - (uint32_t)(wfirst * 4);
+        const __amdgpu_buffer_rsrc_t wr = buf(w + wfirst, wrange);
+        int nco = Co - L.co0;   // filters left from co0
+        asm volatile("" : "+s"(nco));
 #pragma unroll
         for (int i = 0; i < WRW; ++i) {
-            const int co = wave + 4 * i;
-            if (co0 + co < Co) {
-                const uint32_t so = (uint32_t)co * wpitch;
-                const __amdgpu_buffer_rsrc_t wr = buf(wst, so + wlen);
+            const int co = wave + NW * i;
+            const uint32_t so = co < nco ? (uint32_t)co * wpitch : wrange;
 #pragma unroll
-                for (int jc = 0; jc < WCH; ++jc)
-                    wv[i][jc] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                        wr, (int)(lane4 + 256 * jc), (int)so, 0));
-            }
+            for (int jc = 0; jc < WCH; ++jc)
+                wv[i][jc] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    wr, (int)(lane4 + 256 * jc), (int)so, 0));
         }
     };
     auto store_stage = [&](int st) {
-        const int ci0 = st * CB, cbs = min(CB, Ci - ci0);
+        const int ks = min(CB, Ci - st * CB) * HW;
+        int rsb = RS * 4;   // opaque per stage (see load_stage)
+        asm volatile("" : "+s"(rsb));
 #pragma unroll
-        for (int ii = 0; ii < kRPW; ++ii) {
-            const int r = wave + 4 * ii;
-            if (((xvalid >> ii) & 1u) && r < cbs * RIN) {
-                float* row = X + r * RS;
+        for (int ii = 0; ii < RPW; ++ii) {
+            char* row = reinterpret_cast<char*>(X) + xdr[ii] * rsb;
 #pragma unroll
-                for (int cc = 0; cc < XCH; ++cc)
-                    if (xdst[cc] >= 0) row[xdst[cc]] = xv[ii][cc];
-            }
+            for (int cc = 0; cc < XCH; ++cc)
+                *reinterpret_cast<float*>(row + xdst[cc] * 4) = xv[ii][cc];
         }
 #pragma unroll
         for (int i = 0; i < WRW; ++i) {
-            const int co = wave + 4 * i;
-            if (co0 + co < Co) {
-                float* row = Wl + co * KSP;
+            float* row = Wl + (wave + NW * i) * KSP;
 #pragma unroll
-                for (int jc = 0; jc < WCH; ++jc)
-                    if (lane + 64 * jc < KSP) row[lane + 64 * jc] = wv[i][jc];
+            for (int jc = 0; jc < WCH; ++jc) {
+                const int j = lane + 64 * jc;
+                row[j] = j < ks ? wv[i][jc] : 0.f;
             }
         }
     };
 
-    // K walk in filter order (channel cl, kh, kw); the LDS offset of an index
-    // from the pixel's tap (0, 0) of channel 0 is cl*CSX + kh*RS +
-    // (kw % s)*NU + kw / s. Uniform (scalar unit), no divisions.
-    struct Tap {
-        int cl, kh, kw, ph, u;
+    // ---- compute side (item C) ----------------------------------------------
+    // This lane's pixel: entry of its tap (0, 0) in a channel's LDS rows
+    // (output row gr: tile-relative r*s plus image breaks k*dup), and where
+    // its outputs go.
+    Item C;
+    int xb = 0;
+    auto setup_compute = [&]() {
+        int64_t q = C.q0 + wave * 32 + l32;
+        if (q >= C.qend) q = C.qend - 1;
+        const int gr = (int)a.divWo.div((uint32_t)(q - (int64_t)C.gr0 * Wo)) + C.gr0;
+        const int wo = (int)(q - (int64_t)gr * Wo);
+        const int k = (int)a.divHo.div((uint32_t)gr) - C.n0;
+        xb = ((gr - C.gr0) * s + k * a.dup) * RS + wo;
     };
-    auto tap_off = [&](const Tap& t) { return t.cl * a.CSX + t.kh * RS + t.ph * NU + t.u; };
-    auto tap_next = [&](Tap& t) {
-        if (++t.kw == Wf) {
-            t.kw = 0; t.ph = 0; t.u = 0;
-            if (++t.kh == Hf) {
-                t.kh = 0; ++t.cl;
-            }
-        } else if (++t.ph == s) {
-            t.ph = 0; ++t.u;
-        }
+    const int abase = l32 * KSP + hl;   // A: channel l32 of each block, K index 2t + hl
+
+    floatx16_t acc[WCO];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < WCO; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
     };
+
     struct Frags {
         float a[WCO], b;
     };
-    auto fetch = [&](Frags& f, int offA, int offB, int kk) {
-        const int off = hl ? offB : offA;
-        f.b = X[xb + off];
+    // Fragments of pair t: this lane's K index is 2t + hl. The window offsets
+    // of pairs t and t+1 are held in on0, on1 (read from T two pairs ahead),
+    // so a window read never waits on a table read issued just before it.
+    int on0 = 0, on1 = 0;
+    auto fetch = [&](Frags& f, int t) {
+        const int o = on0;
+        on0 = on1;
+        on1 = T[2 * t + 4 + hl];
+        f.b = X[xb + o];
 #pragma unroll
-        for (int i = 0; i < WCO; ++i) f.a[i] = Wl[abase + i * 32 * KSP + kk];
+        for (int i = 0; i < WCO; ++i) f.a[i] = Wl[abase + i * 32 * KSP + 2 * t];
     };
     auto mma = [&](const Frags& f) {
 #pragma unroll
         for (int i = 0; i < WCO; ++i)
             acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i], f.b, acc[i], 0, 0, 0);
     };
-
-    load_stage(st0);
-    store_stage(st0);
-    __syncthreads();
-    for (int st = st0; st < st1; ++st) {
-        if (st + 1 < st1) load_stage(st + 1);
+    auto compute_stage = [&](int st) {
         const int ks = min(CB, Ci - st * CB) * HW;
         const int nfull = ks >> 1;   // pairs with two real K indices
-        Tap ta = {0, 0, 0, 0, 0};
-        auto fetch_pair = [&](Frags& f, int t) {
-            Tap tb = ta;
-            tap_next(tb);
-            fetch(f, tap_off(ta), tap_off(tb), 2 * t);
-            ta = tb;
-            tap_next(ta);
-        };
-        // Pair t+1 is read from LDS while the MFMAs of pair t run.
+        // Pair t+1 is read from LDS while the MFMAs of pair t run. The loop
+        // body fetches unconditionally (one pair past the end at most: an
+        // in-allocation read that is never used), so every path into an
+        // MFMA has the same reads outstanding and the waits stay exact.
         Frags f0, f1;
+        on0 = T[hl];
+        on1 = T[2 + hl];
+        fetch(f0, 0);
         int t = 0;
-        if (t < nfull) fetch_pair(f0, t);
         for (; t + 2 <= nfull; t += 2) {
-            fetch_pair(f1, t + 1);
+            fetch(f1, t + 1);
+            __builtin_amdgcn_sched_barrier(0);
             mma(f0);
-            if (t + 2 < nfull) fetch_pair(f0, t + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(f0, t + 2);
+            __builtin_amdgcn_sched_barrier(0);
             mma(f1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // Left: f0 = pair t. Pair nfull, if ks is odd, is the last K index
+        // with a zero partner: filter entry ks is zero and lanes 32-63 zero
+        // their window value.
         if (t < nfull) {
             mma(f0);
+            if (ks & 1) fetch(f0, nfull);
             ++t;
         }
         if (ks & 1) {
-            // Last K index with a zero partner: filter entry ks is zero and
-            // lanes 32-63 zero their window value.
-            const int off = tap_off(ta);
-            fetch(f0, off, off, 2 * nfull);
             f0.b = hl ? 0.f : f0.b;
             mma(f0);
         }
-        if (st + 1 < st1) {
-            __syncthreads();
-            store_stage(st + 1);
-            __syncthreads();
-        }
-    }
+    };
 
-    // Output: lane holds pixel l32 of its block and channels
+    // Output of item C: lane holds pixel l32 of its block and channels
     // 8*(r/4) + 4*hl + r%4 of each 32-channel block.
-    const int64_t plane = (int64_t)Ho * Wo;
-    const bool qok = qme < qend;
-    const int64_t q = qok ? qme : qend - 1;
-    const int gr = (int)(q / Wo);
-    const int wo = (int)(q - (int64_t)gr * Wo);
-    const int n = (int)a.divHo.div((uint32_t)gr), ho = gr - n * Ho;
-    const bool all_co = co0 + COT <= Co;
-    if (a.ksplit == 1) {
-        // Byte offset = per-lane part (image, pixel, 4*hl channels) + uniform
-        // part (channel block row).
-        const __amdgpu_buffer_rsrc_t yb = buf(y, a.ybytes);
-        const uint32_t voff =
-            (uint32_t)((((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo) * 4);
-        if (qok) {
+    auto epilogue = [&]() {
+        const int64_t qme = C.q0 + wave * 32 + l32;
+        const bool qok = qme < C.qend;
+        const int64_t q = qok ? qme : C.qend - 1;
+        const int gr = (int)(q / Wo);
+        const int wo = (int)(q - (int64_t)gr * Wo);
+        const int n = (int)a.divHo.div((uint32_t)gr), ho = gr - n * Ho;
+        const int co0 = C.co0;
+        const bool all_co = co0 + COT <= Co;
+        if (a.ksplit == 1) {
+            // Byte offset = per-lane part (image, pixel, 4*hl channels) +
+            // uniform part (channel block row).
+            const __amdgpu_buffer_rsrc_t yb = buf(y, a.ybytes);
+            const uint32_t voff =
+                (uint32_t)((((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo) * 4);
+            if (qok) {
+#pragma unroll
+                for (int i = 0; i < WCO; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int cu = co0 + i * 32 + 8 * (r >> 2) + (r & 3);   // channel - 4*hl
+                        const float v = acc[i][r];
+                        if (all_co || cu + 4 * hl < Co)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yb,
+                                                                  (int)voff,
+                                                                  (int)(cu * plane * 4), 0);
+                    }
+            }
+        } else {
+            float* yp = y + (((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo);
 #pragma unroll
             for (int i = 0; i < WCO; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int cu = co0 + i * 32 + 8 * (r >> 2) + (r & 3);   // channel - 4*hl
-                    const float v = acc[i][r];
-                    if (all_co || cu + 4 * hl < Co)
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yb, (int)voff,
-                                                              (int)(cu * plane * 4), 0);
+                    const int cu = co0 + i * 32 + 8 * (r >> 2) + (r & 3);
+                    if (qok && (all_co || cu + 4 * hl < Co))
+                        unsafeAtomicAdd(yp + (int64_t)cu * plane, acc[i][r]);
                 }
         }
-    } else {
-        float* yp = y + (((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo);
-#pragma unroll
-        for (int i = 0; i < WCO; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int cu = co0 + i * 32 + 8 * (r >> 2) + (r & 3);
-                if (qok && (all_co || cu + 4 * hl < Co))
-                    unsafeAtomicAdd(yp + (int64_t)cu * plane, acc[i][r]);
+    };
+
+    // ---- the step stream ------------------------------------------------------
+    int64_t it = blockIdx.x;
+    if (it >= items) return;
+    item_of(it, L);
+    setup_load(L);
+    load_stage(L.st0);
+    store_stage(L.st0);
+    __syncthreads();
+    C = L;
+    setup_compute();
+    zero_acc();
+    int st = C.st0;
+    for (;;) {
+        // Next step: the next stage of this item, or the first of the next.
+        const bool last = st + 1 == C.st1;
+        int nst = st + 1;
+        int64_t nit = it;
+        bool more = true;
+        if (last) {
+            nit = it + gridDim.x;
+            more = nit < items;
+            if (more) {
+                item_of(nit, L);
+                setup_load(L);
+                nst = L.st0;
             }
+        }
+        if (more) load_stage(nst);
+        compute_stage(st);
+        if (last) {
+            epilogue();
+            zero_acc();
+        }
+        if (!more) break;
+        __syncthreads();
+        store_stage(nst);
+        __syncthreads();
+        if (last) {
+            it = nit;
+            C = L;
+            setup_compute();
+        }
+        st = nst;
     }
 }
 
@@ -355,8 +431,10 @@ int env_int(const char* name, int dflt)
     return v && *v ? std::atoi(v) : dflt;
 }
 
-// Plans the launch; false if the shape is outside the kernel's envelope.
-bool plan(const ConvShape& c, MArgs& a, int& wco, int& xch, int& wch)
+// Geometry of a launch with NW waves (32*NW pixels per tile) and 32*WCO
+// channels per tile, without K split; false if the shape is outside the
+// kernel's envelope.
+bool plan(const ConvShape& c, int nw, int wco, MArgs& a, int& xch, int& wch)
 {
     a.c = c;
     a.HW = c.Hf * c.Wf;
@@ -365,68 +443,61 @@ bool plan(const ConvShape& c, MArgs& a, int& wco, int& xch, int& wch)
     if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
     xch = ceil_div(c.Wi, 64);
     if (xch == 3) xch = 4;
-    if (xch > 4) return false;
-    if (a.HW > 254) return false;
+    if (xch > 4 || a.HW > 254) return false;
+    const int P = 32 * nw, cot = 32 * wco, rows_cap = nw * rows_per_wave(nw);
+    const int wrows = (cot + nw - 1) / nw * nw;   // filter rows staged (>= cot)
 
-    // Channel tile: least padding, then the widest.
-    wco = 1;
-    int best = 1 << 30;
-    for (int cand = 4; cand >= 1; --cand) {
-        const int waste = ceil_div(c.Co, 32 * cand) * 32 * cand - c.Co;
-        if (waste < best) {
-            best = waste;
-            wco = cand;
-        }
-    }
-    wco = env_int("IM2WIN_F32_WCO", wco);
-    if (wco < 1 || wco > 4) return false;
-    const int cot = 32 * wco;
-
-    a.NU = ceil_div(c.Wi, c.s);
+    // Entries per stride phase: every lane column (64*xch of them) has one.
+    a.NU = ceil_div(64 * xch, c.s);
     a.RS = c.s * a.NU;
     const int64_t plane = (int64_t)c.Ho * c.Wo;
-    a.rows_max = (kP - 1) / c.Wo + 2;
-    a.tiles_per_image = (plane + kP - 1) / kP;
-    a.aligned = c.N == 1 || (double)(a.tiles_per_image * kP) <= 1.05 * (double)plane;
+    a.rows_max = (P - 1) / c.Wo + 2;
+    a.tiles_per_image = (plane + P - 1) / P;
+    a.aligned = c.N == 1 || (double)(a.tiles_per_image * P) <= 1.05 * (double)plane;
     a.kmax = a.aligned || a.rows_max <= 1 ? 0 : ceil_div(a.rows_max - 1, c.Ho);
     a.RIN = (a.rows_max - 1) * c.s + c.Hf + a.kmax * a.dup;
-    if (a.RIN > 4 * kRPW) return false;
+    if (a.RIN > rows_cap) return false;
     a.CSX = a.RIN * a.RS;
 
     // Channels per stage: fill the row slots, keep the filter rows within
-    // the register prefetch (WRW x WCH loads) and the LDS budget.
-    auto ksp_of = [&](int cb) { return ((cb * a.HW + 1) & ~1) + 1; };
+    // the register prefetch (instantiated chunk counts) and the LDS budget.
     auto wch_of = [&](int cb) {
-        const int v = ceil_div(ksp_of(cb), 64);
+        const int v = ceil_div(cb * a.HW + 1, 64);   // taps plus the odd-K pad entry
         return v == 3 ? 4 : v;
     };
-    auto lds_of = [&](int cb) { return ((int64_t)cb * a.CSX + (int64_t)cot * ksp_of(cb)) * 4; };
-    int cb = std::min(c.Ci, (4 * kRPW) / a.RIN);
-    while (cb > 1 && (ksp_of(cb) > 256 || wco * wch_of(cb) > 8 || lds_of(cb) > 80 * 1024)) --cb;
+    auto wregs = [&](int cb) { return wrows / nw * wch_of(cb); };
+    auto lds_of = [&](int cb) {
+        return (((int64_t)cb * a.RIN + 1) * a.RS + (int64_t)wrows * (64 * wch_of(cb) + 1) +
+                cb * a.HW + 12) * 4;
+    };
+    auto fits = [&](int cb, int64_t budget) {
+        return wch_of(cb) <= 2 && wregs(cb) <= 48 && lds_of(cb) <= budget;
+    };
+    int cb = std::min(c.Ci, rows_cap / a.RIN);
+    while (cb > 1 && !fits(cb, 80 * 1024)) --cb;
     cb = std::max(1, std::min(cb, env_int("IM2WIN_F32_CB", cb)));
-    if (ksp_of(cb) > 256 || wco * wch_of(cb) > 8 || lds_of(cb) > kMaxLds) return false;
-    a.CB = cb;
-    a.KSP = ksp_of(cb);
+    if (!fits(cb, kMaxLds)) return false;
     wch = wch_of(cb);
-    a.xent = cb * a.CSX;
+    a.CB = cb;
+    a.KSP = 64 * wch + 1;
+    a.xent = (cb * a.RIN + 1) * a.RS;   // plus one spare row
+    a.KT = (cb * a.HW + 8 + 3) & ~3;    // reads reach index ks + 7
     a.nstages = ceil_div(c.Ci, cb);
-
     a.co_tiles = ceil_div(c.Co, cot);
-    a.px_tiles = a.aligned ? (int64_t)c.N * a.tiles_per_image : (a.total + kP - 1) / kP;
-    // Split K when there are too few tiles to fill the chip.
-    const int64_t base = a.px_tiles * a.co_tiles;
-    int ksplit = 1;
-    if (base < 384 && a.nstages > 1) ksplit = (int)std::min<int64_t>(a.nstages, (512 + base - 1) / base);
-    ksplit = std::max(1, std::min(a.nstages, env_int("IM2WIN_F32_KSPLIT", ksplit)));
-    a.spk = ceil_div(a.nstages, ksplit);
-    a.ksplit = ceil_div(a.nstages, a.spk);
-    if (base * a.ksplit > 0x7fffffff) return false;
+    a.px_tiles = a.aligned ? (int64_t)c.N * a.tiles_per_image : (a.total + P - 1) / P;
+    a.ksplit = 1;
+    a.spk = a.nstages;
+    if (a.px_tiles * a.co_tiles > 0x7fffffff) return false;
 
-    // Scalar offsets and buffer ranges are 32-bit.
+    // Scalar offsets and buffer ranges are 32-bit; a row with no source uses
+    // an offset of xbytes plus a channel offset below xbytes.
     const int64_t xb = (int64_t)c.N * c.Ci * c.Hi * c.Wi * 4;
     const int64_t yb = (int64_t)c.N * c.Co * c.Ho * c.Wo * 4;
     const int64_t wb = (int64_t)c.Co * c.Ci * a.HW * 4;
-    if (xb >= (int64_t)kMaxBuf || yb >= (int64_t)kMaxBuf || wb >= (int64_t)kMaxBuf) return false;
+    if (2 * xb >= (int64_t)kMaxBuf || yb >= (int64_t)kMaxBuf || wb >= (int64_t)kMaxBuf)
+        return false;
+    a.xbytes = (uint32_t)xb;
+    a.wbytes = (uint32_t)wb;
     a.ybytes = (uint32_t)yb;
     a.divWo = FastDiv((uint32_t)c.Wo);
     a.divHo = FastDiv((uint32_t)c.Ho);
@@ -434,40 +505,183 @@ bool plan(const ConvShape& c, MArgs& a, int& wco, int& xch, int& wch)
     return true;
 }
 
-template <int WCO, int XCH, int WCH>
-int launch_t(const float* x, const float* w, float* y, const MArgs& a, hipStream_t stream)
+size_t lds_bytes(const MArgs& a, int nw, int wco)
 {
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute((const void*)conv_f32_mfma_kernel<WCO, XCH, WCH>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-        attr = true;
+    const int wrows = (32 * wco + nw - 1) / nw * nw;
+    return ((size_t)a.xent + (size_t)wrows * a.KSP + a.KT) * 4;
+}
+
+template <int NW, int WCO, int XCH>
+const void* kernel_w(int wch)
+{
+    if (wch == 1) return (const void*)conv_f32_mfma_kernel<NW, WCO, XCH, 1>;
+    if (wch == 2) return (const void*)conv_f32_mfma_kernel<NW, WCO, XCH, 2>;
+    return nullptr;
+}
+
+template <int NW, int WCO>
+const void* kernel_x(int xch, int wch)
+{
+    switch (xch) {
+    case 1: return kernel_w<NW, WCO, 1>(wch);
+    case 2: return kernel_w<NW, WCO, 2>(wch);
+    case 4: return kernel_w<NW, WCO, 4>(wch);
     }
-    const size_t lds = ((size_t)a.xent + (size_t)32 * WCO * a.KSP) * 4;
-    hipLaunchKernelGGL((conv_f32_mfma_kernel<WCO, XCH, WCH>),
-                       dim3((unsigned)(a.px_tiles * a.co_tiles * a.ksplit)), dim3(kNT), lds,
-                       stream, x, w, y, a);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return nullptr;
 }
 
-template <int WCO, int XCH>
-int launch_x(const float* x, const float* w, float* y, const MArgs& a, int wch,
-             hipStream_t stream)
+template <int NW>
+const void* kernel_c(int wco, int xch, int wch)
 {
-    if (wch == 1) return launch_t<WCO, XCH, 1>(x, w, y, a, stream);
-    if (wch == 2) return launch_t<WCO, XCH, 2>(x, w, y, a, stream);
-    if (WCO <= 2 && wch == 4) return launch_t<WCO, XCH, (WCO <= 2 ? 4 : 1)>(x, w, y, a, stream);
-    return -1;
+    switch (wco) {
+    case 1: return kernel_x<NW, 1>(xch, wch);
+    case 2: return kernel_x<NW, 2>(xch, wch);
+    case 3: return kernel_x<NW, 3>(xch, wch);
+    case 4: return kernel_x<NW, 4>(xch, wch);
+    }
+    return nullptr;
 }
 
-template <int WCO>
-int launch_w(const float* x, const float* w, float* y, const MArgs& a, int xch, int wch,
-             hipStream_t stream)
+const void* kernel_of(int nw, int wco, int xch, int wch)
 {
-    if (xch == 1) return launch_x<WCO, 1>(x, w, y, a, wch, stream);
-    if (xch == 2) return launch_x<WCO, 2>(x, w, y, a, wch, stream);
-    if (xch == 4) return launch_x<WCO, 4>(x, w, y, a, wch, stream);
-    return -1;
+    switch (nw) {
+    case 4: return kernel_c<4>(wco, xch, wch);
+    case 8: return kernel_c<8>(wco, xch, wch);
+    case 12: return kernel_c<12>(wco, xch, wch);
+    }
+    return nullptr;
+}
+
+std::mutex g_mu;
+
+// Workgroups of kernel f that fit on one CU (registers and LDS), with the
+// LDS limit raised to the CU's full 160 KB once per kernel.
+int blocks_per_cu(const void* f, int nt, size_t lds)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    static std::set<const void*> raised;
+    static std::map<std::pair<const void*, size_t>, int> cache;
+    const auto key = std::make_pair(f, lds);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    if (!raised.count(f)) {
+        if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds) !=
+            hipSuccess)
+            return 0;
+        raised.insert(f);
+    }
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, nt, lds) != hipSuccess) nb = 0;
+    cache[key] = nb;
+    return nb;
+}
+
+int cu_count()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        return 256;
+    return n;
+}
+
+struct Choice {
+    MArgs a;
+    int nw, wco, xch, wch;
+    const void* f;
+    size_t lds;
+    int occ;          // workgroups that fit on a CU
+    int64_t grid;     // persistent workgroups
+    double cost;
+    int wps;          // waves per SIMD
+};
+
+// Persistent grid for `items` work items: G = CUs*o workgroups (o <= occ),
+// each taking ceil(items/G) items in turn. A wave's work per item is the same
+// for every NW (32 pixels x the channel tile x K), and a SIMD's matrix core
+// is shared by its waves, so the time is ~ items per workgroup x waves per
+// SIMD; ties go to more waves per SIMD (more latency hiding).
+void size_grid(Choice& t, int ncu)
+{
+    const int64_t items = t.a.px_tiles * t.a.co_tiles * t.a.ksplit;
+    const int force = env_int("IM2WIN_F32_OCC", 0);
+    t.cost = 1e300;
+    t.wps = 0;
+    for (int o = 1; o <= t.occ; ++o) {
+        if (force && o != force) continue;
+        const int64_t G = std::min<int64_t>(items, (int64_t)ncu * o);
+        const int64_t per = (items + G - 1) / G;
+        const int wps = (t.nw * o + 3) / 4;
+        const double c = (double)per * wps;
+        if (c < t.cost * (1 - 1e-9) || (c < t.cost * (1 + 1e-9) && wps > t.wps)) {
+            t.cost = c;
+            t.wps = wps;
+            t.grid = (items + per - 1) / per;
+        }
+    }
+}
+
+// Picks waves per workgroup, channel tile, K split and grid.
+bool choose(const ConvShape& c, Choice& ch)
+{
+    const int ncu = cu_count();
+    int wco0 = 1, best_waste = 1 << 30;
+    for (int cand = 4; cand >= 1; --cand) {
+        const int waste = ceil_div(c.Co, 32 * cand) * 32 * cand - c.Co;
+        if (waste < best_waste) {
+            best_waste = waste;
+            wco0 = cand;
+        }
+    }
+    const int env_wco = env_int("IM2WIN_F32_WCO", 0), env_nw = env_int("IM2WIN_F32_NW", 0);
+    if (env_wco) wco0 = env_wco;
+
+    auto make = [&](int nw, int wc, Choice& t) -> bool {
+        t.nw = nw;
+        t.wco = wc;
+        if (!plan(c, nw, wc, t.a, t.xch, t.wch)) return false;
+        t.f = kernel_of(nw, wc, t.xch, t.wch);
+        if (!t.f) return false;
+        t.lds = lds_bytes(t.a, nw, wc);
+        t.occ = blocks_per_cu(t.f, 64 * nw, t.lds);
+        return t.occ >= 1;
+    };
+    // Too few tiles to fill the chip: narrow channel tiles and split K over
+    // work items (about 2.5 per CU).
+    auto split = [&](Choice& t) {
+        if (t.a.px_tiles * t.a.co_tiles < ncu && t.a.nstages > 1 && !env_wco && t.wco > 1) {
+            Choice u;
+            if (make(t.nw, 1, u)) t = u;
+        }
+        MArgs& a = t.a;
+        const int64_t b = a.px_tiles * a.co_tiles;
+        a.ksplit = 1;
+        if (b < ncu && a.nstages > 1)
+            a.ksplit = (int)std::min<int64_t>(a.nstages, (5 * (int64_t)ncu / 2 + b - 1) / b);
+        const int ks = env_int("IM2WIN_F32_KSPLIT", 0);
+        if (ks > 0) a.ksplit = std::min(a.nstages, ks);
+        a.spk = ceil_div(a.nstages, a.ksplit);
+        a.ksplit = ceil_div(a.nstages, a.spk);
+    };
+
+    bool found = false;
+    for (int wco = wco0; wco >= 1 && !found; --wco) {
+        for (int nw : {12, 8, 4}) {
+            if (env_nw && nw != env_nw) continue;
+            Choice t;
+            if (!make(nw, wco, t)) continue;
+            split(t);
+            if (t.a.px_tiles * t.a.co_tiles * t.a.ksplit > 0x7fffffff) continue;
+            size_grid(t, ncu);
+            if (!found || t.cost < ch.cost * (1 - 1e-9) ||
+                (t.cost < ch.cost * (1 + 1e-9) && t.wps > ch.wps)) {
+                ch = t;
+                found = true;
+            }
+        }
+        if (env_wco) break;
+    }
+    return found;
 }
 
 }  // namespace
@@ -475,9 +689,9 @@ int launch_w(const float* x, const float* w, float* y, const MArgs& a, int xch, 
 int launch_conv_f32_mfma(const float* x, const float* w, float* y, const ConvShape& c,
                          hipStream_t stream)
 {
-    MArgs a;
-    int wco, xch, wch;
-    if (!plan(c, a, wco, xch, wch)) return -1;
+    Choice ch;
+    if (!choose(c, ch)) return -1;
+    const MArgs& a = ch.a;
     if (a.ksplit > 1) {
         // Partial sums are added into y: clear it first (a kernel, not a
         // memset node, so the call stays capturable).
@@ -486,13 +700,11 @@ int launch_conv_f32_mfma(const float* x, const float* w, float* y, const ConvSha
         if (blocks > 0x7fffffff) return -1;
         hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y, n);
     }
-    switch (wco) {
-    case 1: return launch_w<1>(x, w, y, a, xch, wch, stream);
-    case 2: return launch_w<2>(x, w, y, a, xch, wch, stream);
-    case 3: return launch_w<3>(x, w, y, a, xch, wch, stream);
-    case 4: return launch_w<4>(x, w, y, a, xch, wch, stream);
-    }
-    return -1;
+    MArgs args = a;
+    void* params[] = {(void*)&x, (void*)&w, (void*)&y, (void*)&args};
+    const dim3 grid((unsigned)ch.grid), block(64 * ch.nw);
+    if (hipLaunchKernel(ch.f, grid, block, params, ch.lds, stream) != hipSuccess) return -3;
+    return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 }  // namespace im2win
