@@ -54,6 +54,7 @@ struct FusedArgs {
     bool aligned;                   // tiles never cross images (kmax = 0)
     int64_t tiles_per_image;        // aligned tiling: ceil(Ho*Wo / P)
     int NWH, HPH;                   // filter stages per channel group, tap pairs per stage
+    int KT;                         // entries of the tap offset table
     uint32_t xbytes, ybytes;        // sizes of x and y (each below 4 GiB: buffer addressing)
     FastDiv divWo, divHo, divWi, divHalfW, divS;
 };
@@ -101,6 +102,14 @@ __global__ __launch_bounds__(256) void f16_filter_pack_kernel(const uint16_t* __
 constexpr int kXUnits = 6;    // input units of 2 columns x 8 channels (paired path)
 constexpr int kXEnt = 12;     // input entries (gather path)
 constexpr int kWEnt = 8;      // filter entries
+constexpr int kWSlack = 4;    // spare filter-entry rows (reads one pair past a stage)
+
+// LDS bytes of a launch: input rows, filter entries (+ slack), tap table.
+size_t fused_lds_bytes(int xentries, int HPH, int co_tile, int KT)
+{
+    return ((size_t)xentries + (size_t)(2 * HPH + kWSlack) * co_tile) * 16 +
+           ((size_t)KT * 4 + 15) / 16 * 16;
+}
 
 // LDS layout of one staged input row: column c is entry (c % s)*NU + c / s
 // (stride-phase major), so the 32 pixels of an MFMA block, whose window
@@ -334,35 +343,37 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
         }
     };
 
-    // Taps in filter order j = kh*Wf + kw; a tap's LDS offset from the
-    // pixel's tap (0, 0) is kh*RS + (kw % s)*NU + kw / s. The walk is uniform
-    // (scalar unit) and avoids divisions.
-    struct Tap {
-        int kh, kw, ph, u;
-    };
-    auto tap_off = [&](const Tap& t) { return t.kh * RS + t.ph * NU + t.u; };
-    auto tap_next = [&](Tap& t) {
-        if (++t.kw == Wf) {
-            t.kw = 0; t.ph = 0; t.u = 0; ++t.kh;
-        } else if (++t.ph == s) {
-            t.ph = 0; ++t.u;
-        }
-    };
+    // Window offsets of the taps in filter order j = kh*Wf + kw (from the
+    // pixel's tap (0, 0): kh*RS + (kw % s)*NU + kw / s), tabulated once per
+    // workgroup so each lane reads its own tap's offset (one LDS read per
+    // pair, two pairs ahead) instead of walking taps on the scalar unit.
+    // Entries from HW on repeat tap HW-1 (in range; such reads are unused
+    // or zeroed).
+    int* T = reinterpret_cast<int*>(Wl + (2 * a.HPH + kWSlack) * COT);
+    for (int j = tid; j < a.KT; j += NT) {
+        const int jj = j < HW ? j : HW - 1;
+        const int kh = jj / Wf, kw = jj - (jj / Wf) * Wf;
+        T[j] = kh * RS + (kw % s) * NU + kw / s;
+    }
     // Fragments of one tap pair: A for the two 32-channel blocks, B for the
-    // NB pixel blocks.
+    // NB pixel blocks. Pair t holds taps 2t (lanes 0-31) and 2t+1 (32-63);
+    // on0, on1 hold the window offsets of this lane's taps of pairs t, t+1.
     struct Frags {
         half8_t a[2], b[NB];
     };
-    auto fetch = [&](Frags& f, int offA, int offB, int t) {
-        const int off = hl ? offB : offA;
+    int on0 = 0, on1 = 0;
+    auto fetch = [&](Frags& f, int t, int tl) {
+        const int o = on0;
+        on0 = on1;
+        on1 = T[2 * t + 4 + hl];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const uint4 u = Wl[abase + 2 * t * COT + i * 32];
+            const uint4 u = Wl[abase + 2 * tl * COT + i * 32];
             __builtin_memcpy(&f.a[i], &u, 16);
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const uint4 u = X[xb[b] + off];
+            const uint4 u = X[xb[b] + o];
             __builtin_memcpy(&f.b[b], &u, 16);
         }
     };
@@ -379,14 +390,6 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
 
     const int npairs = nfull + (odd ? 1 : 0);
     const int nstages = a.CG * a.NWH;
-    Tap ta = {0, 0, 0, 0};
-    auto fetch_pair = [&](Frags& f, int tl) {
-        Tap tb = ta;
-        tap_next(tb);
-        fetch(f, tap_off(ta), tap_off(tb), tl);
-        ta = tb;
-        tap_next(ta);
-    };
 
     load_stage(0);
     store_stage(0);
@@ -394,31 +397,39 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     for (int st = 0; st < nstages; ++st) {
         const int h = st % a.NWH;
         if (st + 1 < nstages) load_stage(st + 1);
-        if (h == 0) ta = Tap{0, 0, 0, 0};
 
-        // Pairs [t0, t1) of this stage. Pair t holds taps 2t (lanes 0-31) and
-        // 2t+1 (lanes 32-63), walked in filter order on the scalar unit; the
-        // fragments of pair t+1 are read from LDS while the MFMAs of pair t run.
+        // Pairs [t0, t1) of this stage; the fragments of pair t+1 are read
+        // from LDS while the MFMAs of pair t run. The loop body fetches
+        // unconditionally (one pair past the stage at most: in-allocation
+        // reads that are never used), so every path into an MFMA has the
+        // same reads outstanding.
         const int t0 = h * a.HPH, t1 = min(npairs, t0 + a.HPH);
         const int tf = min(t1, nfull);
+        const bool pad = odd && t1 > nfull;   // this stage ends with tap HW-1 alone
         Frags f0, f1;
+        on0 = T[2 * t0 + hl];
+        on1 = T[2 * t0 + 2 + hl];
+        fetch(f0, t0, 0);
         int t = t0;
-        if (t < tf) fetch_pair(f0, t - t0);
         for (; t + 2 <= tf; t += 2) {
-            fetch_pair(f1, t + 1 - t0);
+            fetch(f1, t + 1, t + 1 - t0);
+            __builtin_amdgcn_sched_barrier(0);
             mma(f0);
-            if (t + 2 < tf) fetch_pair(f0, t + 2 - t0);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(f0, t + 2, t + 2 - t0);
+            __builtin_amdgcn_sched_barrier(0);
             mma(f1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // Left: f0 = pair t.
         if (t < tf) {
             mma(f0);
+            if (pad) fetch(f0, nfull, nfull - t0);
             ++t;
         }
-        if (odd && t1 > nfull) {
+        if (pad) {
             // Last tap with a zero partner: the filter entry of tap HW is zero
             // and lanes 32-63 zero their B slice (so Inf/NaN cannot leak in).
-            const int off = tap_off(ta);
-            fetch(f0, off, off, nfull - t0);
             const uint32_t keep = hl ? 0u : ~0u;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
@@ -472,6 +483,7 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
     a.HW = c.Hf * c.Wf;
     a.HWp = (a.HW + 1) & ~1;
     a.CG = ceil_div(c.Ci, 8);
+    a.KT = (a.HWp + 8 + 3) & ~3;   // reads reach tap index 2*(HWp/2) + 5
     a.Copad = ceil_div(c.Co, kCoPad) * kCoPad;
     a.total = (int64_t)c.N * c.Ho * c.Wo;
     a.dup = std::max(0, c.Hf - c.s);
@@ -502,7 +514,8 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
             for (a.NWH = 1; a.NWH <= npairs; ++a.NWH) {
                 a.HPH = ceil_div(npairs, a.NWH);
                 const int wentries = 2 * a.HPH * a.co_tile;
-                const int64_t bytes = ((int64_t)a.xentries + wentries) * 16;
+                const int64_t bytes =
+                    (int64_t)fused_lds_bytes(a.xentries, a.HPH, a.co_tile, a.KT);
                 if (bytes <= budget && wentries <= kWEnt * nt) {
                     found = true;
                     break;
@@ -542,7 +555,7 @@ int launch_t(const uint16_t* x, const uint16_t* w, const uint4* wpk, float* y,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
         attr = true;
     }
-    const size_t lds = ((size_t)a.xentries + (size_t)2 * a.HPH * a.co_tile) * 16;
+    const size_t lds = fused_lds_bytes(a.xentries, a.HPH, a.co_tile, a.KT);
     hipLaunchKernelGGL((conv_f16_fused_kernel<WCO, WPX, NB, XVEC, WPK>),
                        dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(64 * WCO * WPX), lds,
                        stream, x, w, wpk, y, a);
