@@ -30,6 +30,7 @@
 //    odd tap count gets a zero filter entry and a zeroed B slice, so an
 //    infinity next to a window never turns into NaN.
 #include <algorithm>
+#include <cstdlib>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -476,7 +477,15 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     }
 }
 
+int env_int(const char* name, int dflt)
+{
+    const char* v = std::getenv(name);
+    return v && *v ? std::atoi(v) : dflt;
+}
+
 // Plans the fused launch; returns false if the shape is outside its envelope.
+// IM2WIN_F16_WPX / IM2WIN_F16_NWH override the waves along pixels and the
+// filter stages per channel group (tuning and tests only).
 bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
 {
     a.c = c;
@@ -498,8 +507,10 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
     // Smallest workgroup LDS first: two workgroups of four waves per CU let one
     // stage its next channel group while the other runs MFMAs.
     bool found = false;
+    const int env_wpx = env_int("IM2WIN_F16_WPX", 0), env_nwh = env_int("IM2WIN_F16_NWH", 0);
     for (int budget : {80 * 1024, kMaxLds}) {
-        for (wpx = 4; wpx >= 1; wpx /= 2) {
+        for (wpx = 8; wpx >= 1; wpx /= 2) {
+            if (env_wpx ? wpx != env_wpx : wpx == 8) continue;
             a.co_tile = 64 * wco;
             a.P = 32 * nb * wpx;
             a.rows_max = (a.P - 1) / c.Wo + 2;
@@ -512,6 +523,7 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
             const int nt = 64 * wco * wpx;
             if (a.xunits > (a.xpair ? kXUnits : kXEnt) * nt) continue;
             for (a.NWH = 1; a.NWH <= npairs; ++a.NWH) {
+                if (env_nwh && a.NWH < std::min(env_nwh, npairs)) continue;
                 a.HPH = ceil_div(npairs, a.NWH);
                 const int wentries = 2 * a.HPH * a.co_tile;
                 const int64_t bytes =

@@ -216,3 +216,38 @@ def test_conv_full_size_sampled(key, mode, orc):
             assert_within(got, ref, absd, TOL[sh.dtype], sh.describe())
         del y
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("nw", [4, 8, 12])
+@pytest.mark.parametrize("t", [(2, 3, 227, 227, 96, 11, 11, 4), (1, 16, 30, 30, 64, 7, 7, 2),
+                               (3, 7, 26, 26, 33, 5, 5, 1), (2, 10, 19, 37, 130, 3, 3, 2)], ids=str)
+def test_conv_f32_matrix_waves(t, nw, orc, monkeypatch):
+    """The fp32 matrix-core kernel forced to 4, 8 and 12 waves per workgroup
+    (32*NW-pixel tiles: different tilings, row counts and item streams)."""
+    monkeypatch.setenv("IM2WIN_F32_NW", str(nw))
+    sh = _shape(t, "f32")
+    x, w = workloads.make_inputs(sh, seed=20)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    note(f"conv fp32 NW={nw} {sh.describe()}")
+    assert_within(_run(sh, "f32", x, w), ref, absd, TOL["f32"], sh.describe())
+    xi, wi = workloads.make_inputs(sh, seed=21, mode="int")
+    assert_exact(_run(sh, "f32", xi, wi), orc.conv_direct(xi, wi, sh.s), sh.describe())
+
+
+@pytest.mark.parametrize("env", [{"IM2WIN_F16_WPX": "8"}, {"IM2WIN_F16_WPX": "1"},
+                                 {"IM2WIN_F16_NWH": "3"}], ids=str)
+@pytest.mark.parametrize("t", [(1, 64, 30, 30, 64, 7, 7, 2), (2, 24, 14, 14, 96, 5, 5, 1),
+                               (2, 3, 47, 45, 37, 7, 7, 2)], ids=str)
+def test_conv_f16_fused_tilings(t, env, orc, monkeypatch):
+    """The fused fp16 kernel with forced waves along pixels and filter stages
+    per channel group, with and without the prepacked filter."""
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    sh = _shape(t, "f16")
+    x, w = workloads.make_inputs(sh, seed=22)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    for kind in (None, "filter"):
+        note(f"conv fp16 {env} {sh.describe()} ws={kind}")
+        assert_within(_run(sh, "f16", x, w, kind), ref, absd, TOL["f16"], sh.describe())
+    xi, wi = workloads.make_inputs(sh, seed=23, mode="int")
+    assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
