@@ -251,17 +251,20 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
 
     // Stage st = (channel group g, filter part h): the input rows of group g
     // are staged with part 0; part h holds taps [2*h*HPH, 2*(h+1)*HPH).
-    auto load_stage = [&](int st) {
+    // Loads the filter part of stage st and, if with_x, the input rows of
+    // channel group gx (into registers).
+    auto load_stage = [&](int st, bool with_x, int gx) {
         const int g = st / a.NWH, h = st - (st / a.NWH) * a.NWH;
-        const int cb = 8 * g;
-        if (h == 0) {
+        const int cb = 8 * g;     // channel group of the filter part
+        if (with_x) {
+            const int cbx = 8 * gx;   // channel group of the input rows
             // One buffer per channel plane; a missing channel gets an empty buffer.
             __amdgpu_buffer_rsrc_t pl[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const int64_t first = (int64_t)(cb + q) * cstride * 2;
-                pl[q] = buf(x + (int64_t)(cb + q < Ci ? cb + q : 0) * cstride,
-                            cb + q < Ci ? (uint32_t)(a.xbytes - first) : 0u);
+                const int64_t first = (int64_t)(cbx + q) * cstride * 2;
+                pl[q] = buf(x + (int64_t)(cbx + q < Ci ? cbx + q : 0) * cstride,
+                            cbx + q < Ci ? (uint32_t)(a.xbytes - first) : 0u);
             }
 #pragma unroll
             for (int u = 0; u < NXU; ++u) {
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
                     uint32_t v[4] = {0, 0, 0, 0};
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
-                        if (cb + q < Ci)
+                        if (cbx + q < Ci)
                             v[q >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
                                              pl[q], (int)uoff[u], 0, 0)
                                          << (16 * (q & 1));
@@ -314,8 +317,8 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
             }
         }
     };
-    auto store_stage = [&](int st) {
-        if (st % a.NWH == 0) {
+    auto store_stage = [&](bool with_x) {
+        if (with_x) {
 #pragma unroll
             for (int u = 0; u < NXU; ++u) {
                 if (udst0[u] < 0) continue;
@@ -392,12 +395,16 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     const int npairs = nfull + (odd ? 1 : 0);
     const int nstages = a.CG * a.NWH;
 
-    load_stage(0);
-    store_stage(0);
+    // The input rows of group g+1 are fetched during the first filter part
+    // of group g (NWH >= 2: two or more stages ahead, more latency covered)
+    // and written to LDS after its last part.
+    load_stage(0, true, 0);
+    store_stage(true);
     __syncthreads();
     for (int st = 0; st < nstages; ++st) {
-        const int h = st % a.NWH;
-        if (st + 1 < nstages) load_stage(st + 1);
+        const int g = st / a.NWH, h = st % a.NWH;
+        const bool xnext = a.NWH >= 2 ? h == 0 && g + 1 < a.CG : st + 1 < nstages;
+        if (st + 1 < nstages) load_stage(st + 1, xnext, g + 1);
 
         // Pairs [t0, t1) of this stage; the fragments of pair t+1 are read
         // from LDS while the MFMAs of pair t run. The loop body fetches
@@ -444,7 +451,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
 
         if (st + 1 < nstages) {
             __syncthreads();
-            store_stage(st + 1);
+            store_stage((st + 1) % a.NWH == 0);
             __syncthreads();
         }
     }
