@@ -36,7 +36,8 @@ PEAK_FP16_MFMA_TFLOPS = 2516.6    # dense fp16 matrix
 PEAK_HBM_GBS = 8000.0
 
 HEADLINE = "cv1_f32_n32"
-LAYER_KEYS = ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64", "cv4_f16_n64"]
+LAYER_KEYS = ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64", "cv4_f16_n64",
+              "cv2_f32_n32"]
 KERNEL_SOURCES = ["conv_f32_mfma.hip", "conv_f32.hip", "conv_f16_fused.hip", "conv_f16.hip",
                   "conv_generic.hip", "pack.hip", "api.hip", "common.hpp", "kernels.hpp"]
 # Modes: fused (no workspace), fused_valu (fp32 on the vector-ALU kernel),
@@ -212,6 +213,54 @@ def ingest_pmc(fetch_csv, write_csv, copy_bytes=1 << 30):
     return out
 
 
+# Variants timed by --ablation: (label, mode, environment) per precision. The
+# environment switches are the library's own planner overrides.
+ABLATION = {
+    "f32": [("matrix cores, planner's choice", "fused", {}),
+            ("matrix cores, 4 waves/workgroup", "fused", {"IM2WIN_F32_NW": "4"}),
+            ("matrix cores, 8 waves/workgroup", "fused", {"IM2WIN_F32_NW": "8"}),
+            ("matrix cores, 12 waves/workgroup", "fused", {"IM2WIN_F32_NW": "12"}),
+            ("vector ALU", "fused", {"IM2WIN_F32_PATH": "valu"}),
+            ("materialised im2win tensor", "materialized", {})],
+    "f16": [("fused, filter gathered in-kernel", "fused", {}),
+            ("fused, filter prepacked", "prepacked", {}),
+            ("prepacked, 8 waves along pixels", "prepacked", {"IM2WIN_F16_WPX": "8"}),
+            ("prepacked, >= 2 filter parts per channel group", "prepacked", {"IM2WIN_F16_NWH": "2"}),
+            ("prepacked, >= 3 filter parts per channel group", "prepacked", {"IM2WIN_F16_NWH": "3"}),
+            ("materialised im2win tensor", "materialized", {})],
+}
+
+
+def ablation(keys, steps):
+    """Times every layer under the ABLATION variants; prints a Markdown table."""
+    import torch
+    import memory_efficient_im2win_amd as m
+    m.load_library()
+    rows = []
+    for key in keys:
+        sh = workloads.BY_KEY[key]
+        for label, mode, env in ABLATION[sh.dtype]:
+            saved = {k: os.environ.get(k) for k in env}
+            os.environ.update(env)
+            try:
+                r = time_layer(sh, mode, steps, 3)
+            finally:
+                for k, v in saved.items():
+                    if v is None:
+                        os.environ.pop(k, None)
+                    else:
+                        os.environ[k] = v
+            peak = PEAK_FP32_MFMA_TFLOPS if sh.dtype == "f32" else PEAK_FP16_MFMA_TFLOPS
+            rows.append((key, label, r["tflops"], r["ms_per_launch_avg"] * 1e3, r["tflops"] / peak,
+                         r["workspace_bytes"]))
+            log(f"[ablation] {key} {label}: {r['tflops']:.1f} TFLOP/s")
+    torch.cuda.synchronize()
+    print("| layer | variant | TFLOP/s | us per call | fraction of peak | workspace bytes |")
+    print("|---|---|---|---|---|---|")
+    for key, label, tf, us, fr, wsb in rows:
+        print(f"| {key} | {label} | {tf:.1f} | {us:.1f} | {fr:.3f} | {wsb:,} |")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,7 +278,14 @@ def main():
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of this bench into "
                          "profiles/traffic.json for the current kernel sources, then exit")
+    ap.add_argument("--ablation", action="store_true",
+                    help="time every layer under the library's variant switches and print a "
+                         "Markdown table instead of the JSON line")
     args = ap.parse_args()
+
+    if args.ablation:
+        ablation(LAYER_KEYS, max(5, args.steps // 2))
+        return
 
     if args.ingest_pmc:
         t = ingest_pmc(*args.ingest_pmc)

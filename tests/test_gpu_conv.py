@@ -188,7 +188,7 @@ def test_conv_writes_only_its_output(dt, orc):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("key", ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64",
-                                 "cv4_f16_n64"])
+                                 "cv4_f16_n64", "cv2_f32_n32"])
 @pytest.mark.parametrize("mode", ["uniform", "int"])
 def test_conv_full_size_sampled(key, mode, orc):
     """The benchmark layers at full size in every launch configuration the
@@ -220,7 +220,8 @@ def test_conv_full_size_sampled(key, mode, orc):
 
 @pytest.mark.parametrize("nw", [4, 8, 12])
 @pytest.mark.parametrize("t", [(2, 3, 227, 227, 96, 11, 11, 4), (1, 16, 30, 30, 64, 7, 7, 2),
-                               (3, 7, 26, 26, 33, 5, 5, 1), (2, 10, 19, 37, 130, 3, 3, 2)], ids=str)
+                               (3, 7, 26, 26, 33, 5, 5, 1), (2, 10, 19, 37, 130, 3, 3, 2),
+                               (2, 5, 31, 40, 48, 3, 7, 2), (1, 8, 20, 33, 40, 7, 3, 3)], ids=str)
 def test_conv_f32_matrix_waves(t, nw, orc, monkeypatch):
     """The fp32 matrix-core kernel forced to 4, 8 and 12 waves per workgroup
     (32*NW-pixel tiles: different tilings, row counts and item streams)."""
@@ -237,7 +238,8 @@ def test_conv_f32_matrix_waves(t, nw, orc, monkeypatch):
 @pytest.mark.parametrize("env", [{"IM2WIN_F16_WPX": "8"}, {"IM2WIN_F16_WPX": "1"},
                                  {"IM2WIN_F16_NWH": "3"}], ids=str)
 @pytest.mark.parametrize("t", [(1, 64, 30, 30, 64, 7, 7, 2), (2, 24, 14, 14, 96, 5, 5, 1),
-                               (2, 3, 47, 45, 37, 7, 7, 2)], ids=str)
+                               (2, 3, 47, 45, 37, 7, 7, 2), (2, 12, 26, 40, 70, 3, 7, 2),
+                               (1, 16, 22, 19, 40, 5, 2, 1)], ids=str)
 def test_conv_f16_fused_tilings(t, env, orc, monkeypatch):
     """The fused fp16 kernel with forced waves along pixels and filter stages
     per channel group, with and without the prepacked filter."""

@@ -57,7 +57,7 @@ def test_pack_leaves_bytes_outside_the_tensor_alone(orc):
 
 
 @pytest.mark.parametrize("key", ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64",
-                                 "cv4_f16_n64"])
+                                 "cv4_f16_n64", "cv2_f32_n32"])
 def test_pack_full_size(key, orc):
     """The benchmark layers at full batch; images 0, N-1 and one in between
     are compared with the oracle bit for bit, the rest by their size."""
