@@ -9,8 +9,9 @@
  *
  *  - "Enabling Memory-efficient Im2win Convolution with Multi-precision
  *    Support on GPU CUDA and Tensor Cores" (Abstract; Fig. 1; Table I):
- *    NCHW input Ci x Hi x Wi, filters Co x Ci x Hf x Wf, stride s (equal in
- *    both directions), output Co x Ho x Wo; fp32 and fp16 inputs.
+ *    NCHW input Ci x Hi x Wi, filters Co x Ci x Hf x Wf, row stride sh and
+ *    column stride sw (the table writes s_h(s_w); every row it lists has the
+ *    two equal), output Co x Ho x Wo; fp32 and fp16 inputs.
  *  - "Im2win: Memory Efficient Convolution On SIMD Architectures" (Abstract):
  *    the im2win transform takes one row of dot-product windows and flattens
  *    the distinct input elements those windows cover into one row of the
@@ -20,12 +21,12 @@
  * the function that uses it):
  *  - convolution is cross-correlation (no filter flip), no padding, no
  *    dilation, no bias;
- *  - Ho = floor((Hi - Hf) / s) + 1 and likewise Wo (Table I, cv4:
- *    224, 7, s=2 gives 109);
+ *  - Ho = floor((Hi - Hf) / sh) + 1 and Wo = floor((Wi - Wf) / sw) + 1
+ *    (Table I, cv4: 224, 7, stride 2 gives 109);
  *  - an im2win row for (image n, channel ci, output row ho) holds the Hf
- *    input rows ho*s .. ho*s+Hf-1 over all Wi columns, column by column:
- *    element w*Hf + kh is x[n][ci][ho*s+kh][w]. Then the window of output
- *    column wo is the single contiguous run starting at wo*s*Hf of length
+ *    input rows ho*sh .. ho*sh+Hf-1 over all Wi columns, column by column:
+ *    element w*Hf + kh is x[n][ci][ho*sh+kh][w]. Then the window of output
+ *    column wo is the single contiguous run starting at wo*sw*Hf of length
  *    Wf*Hf.
  *
  * Floating point: products of the rounded inputs are accumulated in double
@@ -52,20 +53,20 @@ int oracle_out_extent(int in, int f, int s)
 }
 
 /* Elements of the im2win tensor: one row of Wi*Hf per (n, ci, ho). */
-int64_t oracle_im2win_elems(int N, int Ci, int Hi, int Wi, int Hf, int Wf, int s)
+int64_t oracle_im2win_elems(int N, int Ci, int Hi, int Wi, int Hf, int Wf, int sh, int sw)
 {
-    int Ho = oracle_out_extent(Hi, Hf, s);
-    int Wo = oracle_out_extent(Wi, Wf, s);
+    int Ho = oracle_out_extent(Hi, Hf, sh);
+    int Wo = oracle_out_extent(Wi, Wf, sw);
     if (N < 1 || Ci < 1 || Ho == 0 || Wo == 0)
         return 0;
     return (int64_t)N * Ci * Ho * ((int64_t)Wi * Hf);
 }
 
 /* Elements of the im2col matrix: one column of Ci*Hf*Wf per output pixel. */
-int64_t oracle_im2col_elems(int N, int Ci, int Hi, int Wi, int Hf, int Wf, int s)
+int64_t oracle_im2col_elems(int N, int Ci, int Hi, int Wi, int Hf, int Wf, int sh, int sw)
 {
-    int Ho = oracle_out_extent(Hi, Hf, s);
-    int Wo = oracle_out_extent(Wi, Wf, s);
+    int Ho = oracle_out_extent(Hi, Hf, sh);
+    int Wo = oracle_out_extent(Wi, Wf, sw);
     if (N < 1 || Ci < 1 || Ho == 0 || Wo == 0)
         return 0;
     return (int64_t)N * Ci * Hf * Wf * Ho * (int64_t)Wo;
@@ -73,18 +74,19 @@ int64_t oracle_im2col_elems(int N, int Ci, int Hi, int Wi, int Hf, int Wf, int s
 
 /*
  * The im2win transform as a bit copy of elem_bytes-wide elements:
- *   ws[n][ci][ho][w*Hf + kh] = x[n][ci][ho*s + kh][w]
+ *   ws[n][ci][ho][w*Hf + kh] = x[n][ci][ho*sh + kh][w]
  * for every w < Wi and kh < Hf. Every column is kept, even columns no window
- * reads; rows shared by overlapping windows (s < Hf) appear in each im2win
- * row that needs them.
+ * reads; rows shared by overlapping windows (sh < Hf) appear in each im2win
+ * row that needs them. The column stride sw does not enter the transform
+ * (it only places the windows inside a row).
  */
 void oracle_im2win_pack(const void *x, void *ws, int N, int Ci, int Hi, int Wi,
-                        int Hf, int Wf, int s, int elem_bytes)
+                        int Hf, int Wf, int sh, int sw, int elem_bytes)
 {
     const unsigned char *src = (const unsigned char *)x;
     unsigned char *dst = (unsigned char *)ws;
-    int Ho = oracle_out_extent(Hi, Hf, s);
-    if (Ho == 0 || oracle_out_extent(Wi, Wf, s) == 0)
+    int Ho = oracle_out_extent(Hi, Hf, sh);
+    if (Ho == 0 || oracle_out_extent(Wi, Wf, sw) == 0)
         return;
     for (int n = 0; n < N; ++n)
         for (int ci = 0; ci < Ci; ++ci)
@@ -93,7 +95,7 @@ void oracle_im2win_pack(const void *x, void *ws, int N, int Ci, int Hi, int Wi,
                     for (int kh = 0; kh < Hf; ++kh) {
                         int64_t plane = (int64_t)n * Ci + ci;
                         int64_t out = ((plane * Ho + ho) * Wi + w) * Hf + kh;
-                        int64_t in = (plane * Hi + (int64_t)ho * s + kh) * Wi + w;
+                        int64_t in = (plane * Hi + (int64_t)ho * sh + kh) * Wi + w;
                         memcpy(dst + out * elem_bytes, src + in * elem_bytes,
                                (size_t)elem_bytes);
                     }
@@ -111,18 +113,18 @@ static inline int64_t wi(int co, int ci, int kh, int kw, int Ci, int Hf, int Wf)
 
 /*
  * One output of the direct convolution (cross-correlation), fp64:
- *   y[n][co][ho][wo] = sum_ci sum_kh sum_kw x[n][ci][ho*s+kh][wo*s+kw] * w[co][ci][kh][kw]
+ *   y[n][co][ho][wo] = sum_ci sum_kh sum_kw x[n][ci][ho*sh+kh][wo*sw+kw] * w[co][ci][kh][kw]
  * If absdot is non-NULL it also receives sum |x * w| over the same terms.
  */
 static double direct_point_f64(const float *x, const float *w, int n, int co, int ho,
-                               int wo, int Ci, int Hi, int Wi, int Hf, int Wf, int s,
+                               int wo, int Ci, int Hi, int Wi, int Hf, int Wf, int sh, int sw,
                                double *absdot)
 {
     double acc = 0.0, aacc = 0.0;
     for (int ci = 0; ci < Ci; ++ci)
         for (int kh = 0; kh < Hf; ++kh)
             for (int kw = 0; kw < Wf; ++kw) {
-                double p = (double)x[xi(n, ci, ho * s + kh, wo * s + kw, Ci, Hi, Wi)] *
+                double p = (double)x[xi(n, ci, ho * sh + kh, wo * sw + kw, Ci, Hi, Wi)] *
                            (double)w[wi(co, ci, kh, kw, Ci, Hf, Wf)];
                 acc += p;
                 aacc += fabs(p);
@@ -134,10 +136,10 @@ static double direct_point_f64(const float *x, const float *w, int n, int co, in
 
 /* Direct convolution over the whole output, fp64 accumulation. */
 void oracle_conv_direct_f64(const float *x, const float *w, double *y, double *absdot,
-                            int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s)
+                            int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw)
 {
-    int Ho = oracle_out_extent(Hi, Hf, s);
-    int Wo = oracle_out_extent(Wi, Wf, s);
+    int Ho = oracle_out_extent(Hi, Hf, sh);
+    int Wo = oracle_out_extent(Wi, Wf, sw);
     if (Ho == 0 || Wo == 0)
         return;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -147,7 +149,7 @@ void oracle_conv_direct_f64(const float *x, const float *w, double *y, double *a
                 for (int wo = 0; wo < Wo; ++wo) {
                     int64_t o = (((int64_t)n * Co + co) * Ho + ho) * Wo + wo;
                     double a;
-                    y[o] = direct_point_f64(x, w, n, co, ho, wo, Ci, Hi, Wi, Hf, Wf, s, &a);
+                    y[o] = direct_point_f64(x, w, n, co, ho, wo, Ci, Hi, Wi, Hf, Wf, sh, sw, &a);
                     if (absdot)
                         absdot[o] = a;
                 }
@@ -155,10 +157,10 @@ void oracle_conv_direct_f64(const float *x, const float *w, double *y, double *a
 
 /* Direct convolution with a float accumulator, same order (ci, kh, kw). */
 void oracle_conv_direct_f32acc(const float *x, const float *w, float *y, int N, int Ci,
-                               int Hi, int Wi, int Co, int Hf, int Wf, int s)
+                               int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw)
 {
-    int Ho = oracle_out_extent(Hi, Hf, s);
-    int Wo = oracle_out_extent(Wi, Wf, s);
+    int Ho = oracle_out_extent(Hi, Hf, sh);
+    int Wo = oracle_out_extent(Wi, Wf, sw);
     if (Ho == 0 || Wo == 0)
         return;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -170,7 +172,7 @@ void oracle_conv_direct_f32acc(const float *x, const float *w, float *y, int N, 
                     for (int ci = 0; ci < Ci; ++ci)
                         for (int kh = 0; kh < Hf; ++kh)
                             for (int kw = 0; kw < Wf; ++kw)
-                                acc += x[xi(n, ci, ho * s + kh, wo * s + kw, Ci, Hi, Wi)] *
+                                acc += x[xi(n, ci, ho * sh + kh, wo * sw + kw, Ci, Hi, Wi)] *
                                        w[wi(co, ci, kh, kw, Ci, Hf, Wf)];
                     y[(((int64_t)n * Co + co) * Ho + ho) * Wo + wo] = acc;
                 }
@@ -178,16 +180,16 @@ void oracle_conv_direct_f32acc(const float *x, const float *w, float *y, int N, 
 
 /*
  * im2win convolution on a packed im2win tensor, fp64 accumulation. The window
- * of (ho, wo) is the contiguous run ws[n][ci][ho][wo*s*Hf ...] of Wf*Hf
+ * of (ho, wo) is the contiguous run ws[n][ci][ho][wo*sw*Hf ...] of Wf*Hf
  * elements; element kw*Hf + kh of that run multiplies w[co][ci][kh][kw].
  * Terms are taken ci, then kh, then kw -- the direct order -- so the result
  * is bit-identical to oracle_conv_direct_f64.
  */
 void oracle_conv_im2win_f64(const float *ws, const float *w, double *y, int N, int Ci,
-                            int Hi, int Wi, int Co, int Hf, int Wf, int s)
+                            int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw)
 {
-    int Ho = oracle_out_extent(Hi, Hf, s);
-    int Wo = oracle_out_extent(Wi, Wf, s);
+    int Ho = oracle_out_extent(Hi, Hf, sh);
+    int Wo = oracle_out_extent(Wi, Wf, sw);
     if (Ho == 0 || Wo == 0)
         return;
     int64_t row = (int64_t)Wi * Hf;
@@ -199,7 +201,7 @@ void oracle_conv_im2win_f64(const float *ws, const float *w, double *y, int N, i
                     double acc = 0.0;
                     for (int ci = 0; ci < Ci; ++ci) {
                         const float *win = ws + (((int64_t)n * Ci + ci) * Ho + ho) * row +
-                                           (int64_t)wo * s * Hf;
+                                           (int64_t)wo * sw * Hf;
                         for (int kh = 0; kh < Hf; ++kh)
                             for (int kw = 0; kw < Wf; ++kw)
                                 acc += (double)win[kw * Hf + kh] *
@@ -211,10 +213,10 @@ void oracle_conv_im2win_f64(const float *ws, const float *w, double *y, int N, i
 
 /* im2win convolution with a float accumulator, same order as the f64 one. */
 void oracle_conv_im2win_f32acc(const float *ws, const float *w, float *y, int N, int Ci,
-                               int Hi, int Wi, int Co, int Hf, int Wf, int s)
+                               int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw)
 {
-    int Ho = oracle_out_extent(Hi, Hf, s);
-    int Wo = oracle_out_extent(Wi, Wf, s);
+    int Ho = oracle_out_extent(Hi, Hf, sh);
+    int Wo = oracle_out_extent(Wi, Wf, sw);
     if (Ho == 0 || Wo == 0)
         return;
     int64_t row = (int64_t)Wi * Hf;
@@ -226,7 +228,7 @@ void oracle_conv_im2win_f32acc(const float *ws, const float *w, float *y, int N,
                     float acc = 0.0f;
                     for (int ci = 0; ci < Ci; ++ci) {
                         const float *win = ws + (((int64_t)n * Ci + ci) * Ho + ho) * row +
-                                           (int64_t)wo * s * Hf;
+                                           (int64_t)wo * sw * Hf;
                         for (int kh = 0; kh < Hf; ++kh)
                             for (int kw = 0; kw < Wf; ++kw)
                                 acc += win[kw * Hf + kh] * w[wi(co, ci, kh, kw, Ci, Hf, Wf)];
@@ -242,10 +244,10 @@ void oracle_conv_im2win_f32acc(const float *ws, const float *w, float *y, int N,
  */
 void oracle_conv_points_f64(const float *x, const float *w, const int64_t *idx,
                             int64_t npts, double *y, double *absdot, int N, int Ci,
-                            int Hi, int Wi, int Co, int Hf, int Wf, int s)
+                            int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw)
 {
-    int Ho = oracle_out_extent(Hi, Hf, s);
-    int Wo = oracle_out_extent(Wi, Wf, s);
+    int Ho = oracle_out_extent(Hi, Hf, sh);
+    int Wo = oracle_out_extent(Wi, Wf, sw);
     if (Ho == 0 || Wo == 0)
         return;
     (void)N;
@@ -257,7 +259,7 @@ void oracle_conv_points_f64(const float *x, const float *w, const int64_t *idx,
         int co = (int)((o / ((int64_t)Wo * Ho)) % Co);
         int n = (int)(o / ((int64_t)Wo * Ho * Co));
         double a;
-        y[i] = direct_point_f64(x, w, n, co, ho, wo, Ci, Hi, Wi, Hf, Wf, s, &a);
+        y[i] = direct_point_f64(x, w, n, co, ho, wo, Ci, Hi, Wi, Hf, Wf, sh, sw, &a);
         if (absdot)
             absdot[i] = a;
     }

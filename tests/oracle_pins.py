@@ -23,8 +23,9 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 GOLDEN = os.path.join(HERE, "golden")
 
-# Small shapes covering rectangles, s > Wf, ragged (Hi-Hf) % s, Ho = 1, Ci = 1.
-# (N, Ci, Hi, Wi, Co, Hf, Wf, s)
+# Small shapes covering rectangles, s > Wf, ragged (Hi-Hf) % s, Ho = 1, Ci = 1,
+# and unequal row and column strides.
+# (N, Ci, Hi, Wi, Co, Hf, Wf, s) with s an int or (sh, sw)
 SWEEP = [
     (1, 3, 3, 3, 2, 2, 2, 1),     # the Fig. 1 shapes
     (2, 2, 7, 9, 3, 3, 2, 1),
@@ -35,7 +36,16 @@ SWEEP = [
     (2, 3, 10, 7, 1, 3, 3, 2),    # ragged (Hi-Hf) % s
     (1, 4, 6, 6, 5, 6, 6, 1),     # filter covers the whole input
     (1, 2, 13, 11, 2, 2, 3, 4),
+    (1, 2, 11, 9, 3, 3, 2, (2, 1)),
+    (2, 3, 10, 13, 2, 3, 3, (1, 3)),
+    (1, 2, 12, 7, 2, 2, 5, (3, 2)),    # sh > Hf, Wo = 2
+    (1, 1, 9, 14, 2, 4, 2, (4, 1)),
 ]
+
+
+def _st(s):
+    """(sh, sw) of a SWEEP stride entry."""
+    return (s, s) if isinstance(s, int) else tuple(s)
 
 
 def _rand(rng, shape, integer=False):
@@ -89,10 +99,11 @@ def pin_fig1_sizes(O):
 # --------------------------------------------------------------------------
 def pin_scipy_correlate(O):
     """Stride-1 'valid' cross-correlation per channel (scipy), summed over
-    channels and subsampled by s, equals the oracle (to fp64 rounding)."""
+    channels and subsampled by (sh, sw), equals the oracle (to fp64 rounding)."""
     from scipy.signal import correlate2d
     for k, cfg in enumerate(SWEEP):
         N, Ci, Hi, Wi, Co, Hf, Wf, s = cfg
+        sh, sw = _st(s)
         x, w = _case(cfg, 100 + k)
         y = O.conv_direct(x, w, s)
         ref = np.zeros_like(y)
@@ -100,7 +111,7 @@ def pin_scipy_correlate(O):
             for co in range(Co):
                 full = sum(correlate2d(x[n, ci].astype(np.float64), w[co, ci].astype(np.float64),
                                        mode="valid") for ci in range(Ci))
-                ref[n, co] = full[::s, ::s][: y.shape[2], : y.shape[3]]
+                ref[n, co] = full[::sh, ::sw][: y.shape[2], : y.shape[3]]
         assert y.shape == ref.shape, cfg
         scale = np.abs(ref).max() + 1e-30
         assert np.max(np.abs(y - ref)) <= 1e-12 * scale, cfg
@@ -113,12 +124,13 @@ def pin_torch_conv2d(O):
     import torch.nn.functional as F
     for k, cfg in enumerate(SWEEP):
         s = cfg[-1]
+        st = _st(s)
         x, w = _case(cfg, 200 + k)
         y, a = O.conv_direct(x, w, s, with_absdot=True)
         xt = torch.from_numpy(x.astype(np.float64))
         wt = torch.from_numpy(w.astype(np.float64))
-        ref = F.conv2d(xt, wt, stride=s).numpy()
-        aref = F.conv2d(xt.abs(), wt.abs(), stride=s).numpy()
+        ref = F.conv2d(xt, wt, stride=st).numpy()
+        aref = F.conv2d(xt.abs(), wt.abs(), stride=st).numpy()
         assert y.shape == ref.shape, cfg
         assert np.max(np.abs(y - ref)) <= 1e-12 * (np.abs(ref).max() + 1e-30), cfg
         assert np.max(np.abs(a - aref)) <= 1e-12 * (aref.max() + 1e-30), cfg
@@ -133,7 +145,7 @@ def pin_integer_exact(O):
         s = cfg[-1]
         x, w = _case(cfg, 300 + k, integer=True)
         ref = F.conv2d(torch.from_numpy(x.astype(np.float64)),
-                       torch.from_numpy(w.astype(np.float64)), stride=s).numpy()
+                       torch.from_numpy(w.astype(np.float64)), stride=_st(s)).numpy()
         assert np.array_equal(O.conv_direct(x, w, s), ref), cfg
         assert np.array_equal(O.conv_direct_f32acc(x, w, s), ref.astype(np.float32)), cfg
 
@@ -143,10 +155,11 @@ def pin_integer_exact(O):
 # --------------------------------------------------------------------------
 def pin_delta_filter(O):
     """A one-hot filter (channel c, tap (kh0, kw0)) turns the convolution into
-    the strided crop x[n, c, kh0::s, kw0::s] -- exactly."""
+    the strided crop x[n, c, kh0::sh, kw0::sw] -- exactly."""
     rng = np.random.default_rng(5)
     for cfg in SWEEP:
         N, Ci, Hi, Wi, Co, Hf, Wf, s = cfg
+        sh, sw = _st(s)
         x = rng.uniform(-1, 1, size=(N, Ci, Hi, Wi)).astype(np.float32)
         w = np.zeros((Co, Ci, Hf, Wf), np.float32)
         picks = []
@@ -157,7 +170,7 @@ def pin_delta_filter(O):
         y = O.conv_direct(x, w, s)
         Ho, Wo = y.shape[2:]
         for co, (c, kh0, kw0) in enumerate(picks):
-            crop = x[:, c, kh0::s, kw0::s][:, :Ho, :Wo].astype(np.float64)
+            crop = x[:, c, kh0::sh, kw0::sw][:, :Ho, :Wo].astype(np.float64)
             assert np.array_equal(y[:, co], crop), (cfg, co)
 
 
@@ -174,13 +187,14 @@ def pin_constant_input(O):
 
 def pin_ramp_input(O):
     """x[n, ci, h, w] = a*h + b*w + c[ci] is affine in (h, w), so
-    y[n, co, ho, wo] = s*(a*ho + b*wo)*S + a*Kh + b*Kw + Cc with
+    y[n, co, ho, wo] = (a*sh*ho + b*sw*wo)*S + a*Kh + b*Kw + Cc with
     S = sum w[co], Kh = sum kh*w[co,..,kh,kw], Kw = sum kw*w[co,..,kh,kw],
     Cc = sum_ci c[ci]*sum w[co,ci]. Integer values keep it exact; a != b
     separates the two axes."""
     a, b = 3.0, 7.0
     for k, cfg in enumerate(SWEEP):
         N, Ci, Hi, Wi, Co, Hf, Wf, s = cfg
+        sh, sw = _st(s)
         _, w = _case(cfg, 500 + k, integer=True)
         c = np.arange(1, Ci + 1, dtype=np.float64) * 5.0
         hh = np.arange(Hi, dtype=np.float64)[:, None]
@@ -196,7 +210,7 @@ def pin_ramp_input(O):
         Cc = (wd.sum(axis=(2, 3)) * c[None, :]).sum(axis=1)
         ho = np.arange(Ho)[:, None]
         wo = np.arange(Wo)[None, :]
-        expect = (s * (a * ho + b * wo))[None] * S[:, None, None] + \
+        expect = (a * sh * ho + b * sw * wo)[None] * S[:, None, None] + \
             (a * Kh + b * Kw + Cc)[:, None, None]
         assert np.array_equal(y, np.broadcast_to(expect[None], y.shape)), cfg
 
@@ -206,30 +220,32 @@ def pin_ramp_input(O):
 # --------------------------------------------------------------------------
 def pin_pack_rows_are_transposed_strips(O):
     """Each im2win row (n, ci, ho) is the Hf x Wi strip of input rows
-    ho*s .. ho*s+Hf-1 read column by column (numpy transpose, flattened)."""
+    ho*sh .. ho*sh+Hf-1 read column by column (numpy transpose, flattened)."""
     for k, cfg in enumerate(SWEEP):
         N, Ci, Hi, Wi, Co, Hf, Wf, s = cfg
+        sh, _ = _st(s)
         x, _ = _case(cfg, 600 + k)
         ws = O.im2win_pack(x, Hf, Wf, s)
         Ho = ws.shape[2]
         assert ws.shape == (N, Ci, Ho, Wi * Hf)
         for ho in range(Ho):
-            strip = x[:, :, ho * s: ho * s + Hf, :]            # N, Ci, Hf, Wi
+            strip = x[:, :, ho * sh: ho * sh + Hf, :]          # N, Ci, Hf, Wi
             assert np.array_equal(ws[:, :, ho, :], strip.transpose(0, 1, 3, 2).reshape(N, Ci, -1))
 
 
 def pin_pack_windows_contiguous(O):
     """The defining property: the Hf x Wf window of output (ho, wo) is the
-    one contiguous run of Wf*Hf elements at wo*s*Hf in im2win row (n, ci, ho)."""
+    one contiguous run of Wf*Hf elements at wo*sw*Hf in im2win row (n, ci, ho)."""
     for k, cfg in enumerate(SWEEP):
         N, Ci, Hi, Wi, Co, Hf, Wf, s = cfg
+        sh, sw = _st(s)
         x, _ = _case(cfg, 700 + k)
         ws = O.im2win_pack(x, Hf, Wf, s)
         Ho, Wo = O.out_hw(Hi, Wi, Hf, Wf, s)
         for ho in range(Ho):
             for wo in range(Wo):
-                run = ws[:, :, ho, wo * s * Hf: wo * s * Hf + Wf * Hf]
-                win = x[:, :, ho * s: ho * s + Hf, wo * s: wo * s + Wf]
+                run = ws[:, :, ho, wo * sw * Hf: wo * sw * Hf + Wf * Hf]
+                win = x[:, :, ho * sh: ho * sh + Hf, wo * sw: wo * sw + Wf]
                 assert np.array_equal(run.reshape(N, Ci, Wf, Hf).transpose(0, 1, 3, 2), win)
 
 
@@ -238,11 +254,12 @@ def pin_pack_is_bit_copy(O):
     2- and 4-byte elements come through unchanged."""
     rng = np.random.default_rng(9)
     for dt in (np.uint16, np.uint32):
-        for cfg in SWEEP[:4]:
+        for cfg in SWEEP[:4] + SWEEP[-2:]:
             N, Ci, Hi, Wi, Co, Hf, Wf, s = cfg
+            sh, _ = _st(s)
             x = rng.integers(0, np.iinfo(dt).max, size=(N, Ci, Hi, Wi), dtype=dt, endpoint=True)
             ws = O.im2win_pack(x, Hf, Wf, s)
-            ref = np.stack([x[:, :, ho * s: ho * s + Hf, :].transpose(0, 1, 3, 2).reshape(N, Ci, -1)
+            ref = np.stack([x[:, :, ho * sh: ho * sh + Hf, :].transpose(0, 1, 3, 2).reshape(N, Ci, -1)
                             for ho in range(ws.shape[2])], axis=2)
             assert ws.dtype == dt and np.array_equal(ws, ref)
     x = np.array([np.nan, np.inf, -np.inf, 1e-45, -0.0, 3.0, 6e-8, 65504.0, 1.0],
@@ -282,6 +299,8 @@ def pin_workspace_sizes(O):
     """Element counts: im2win N*Ci*Ho*Wi*Hf, im2col N*Ci*Hf*Wf*Ho*Wo, so their
     ratio is Wi/(Wf*Wo) -- and the byte counts at the benchmark layers."""
     expect_bytes = {  # (N, Ci, Hi, Wi, Hf, Wf, s, elem): im2win bytes
+        # sh=3, sw=2: Ho = (20-4)//3 + 1 = 6, 2*3*6*17*4 elements
+        (2, 3, 20, 17, 4, 3, (3, 2), 4): 9_792,
         (1, 96, 24, 24, 5, 5, 1, 4): 921_600,
         (32, 3, 227, 227, 11, 11, 4, 4): 52_736_640,
         (128, 96, 24, 24, 5, 5, 1, 2): 58_982_400,

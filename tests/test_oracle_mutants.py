@@ -20,25 +20,37 @@ from oracle import build as obuild  # noqa: E402
 
 MUTANTS = [
     ("x index: kh and kw swapped",
-     "(double)x[xi(n, ci, ho * s + kh, wo * s + kw",
-     "(double)x[xi(n, ci, ho * s + kw, wo * s + kh"),
+     "(double)x[xi(n, ci, ho * sh + kh, wo * sw + kw",
+     "(double)x[xi(n, ci, ho * sh + kw, wo * sw + kh"),
     ("filter flipped (true convolution instead of correlation)",
      "(double)w[wi(co, ci, kh, kw, Ci, Hf, Wf)]",
      "(double)w[wi(co, ci, Hf - 1 - kh, Wf - 1 - kw, Ci, Hf, Wf)]"),
     ("stride missing on the column axis",
-     "(double)x[xi(n, ci, ho * s + kh, wo * s + kw",
-     "(double)x[xi(n, ci, ho * s + kh, wo + kw"),
+     "(double)x[xi(n, ci, ho * sh + kh, wo * sw + kw",
+     "(double)x[xi(n, ci, ho * sh + kh, wo + kw"),
+    ("row and column strides swapped",
+     "(double)x[xi(n, ci, ho * sh + kh, wo * sw + kw",
+     "(double)x[xi(n, ci, ho * sw + kh, wo * sh + kw"),
+    ("output width taken with the row stride",
+     "int Wo = oracle_out_extent(Wi, Wf, sw);\n    if (Ho == 0 || Wo == 0)\n        return;\n#pragma omp parallel for collapse(2) schedule(dynamic)\n    for (int n = 0; n < N; ++n)\n        for (int co = 0; co < Co; ++co)\n            for (int ho = 0; ho < Ho; ++ho)\n                for (int wo = 0; wo < Wo; ++wo) {\n                    int64_t o",
+     "int Wo = oracle_out_extent(Wi, Wf, sh);\n    if (Ho == 0 || Wo == 0)\n        return;\n#pragma omp parallel for collapse(2) schedule(dynamic)\n    for (int n = 0; n < N; ++n)\n        for (int co = 0; co < Co; ++co)\n            for (int ho = 0; ho < Ho; ++ho)\n                for (int wo = 0; wo < Wo; ++wo) {\n                    int64_t o"),
+    ("im2win window start uses the row stride",
+     "(int64_t)wo * sw * Hf;\n                        for (int kh = 0; kh < Hf; ++kh)\n                            for (int kw = 0; kw < Wf; ++kw)\n                                acc += (double)",
+     "(int64_t)wo * sh * Hf;\n                        for (int kh = 0; kh < Hf; ++kh)\n                            for (int kw = 0; kw < Wf; ++kw)\n                                acc += (double)"),
     ("first column of every window dropped",
      "for (int kw = 0; kw < Wf; ++kw) {\n                double p",
      "for (int kw = 1; kw < Wf; ++kw) {\n                double p"),
     ("output extent rounded up",
      "return (in - f) / s + 1;",
      "return (in - f + s - 1) / s + 1;"),
+    ("im2win source row uses the column stride",
+     "int64_t in = (plane * Hi + (int64_t)ho * sh + kh) * Wi + w;",
+     "int64_t in = (plane * Hi + (int64_t)ho * sw + kh) * Wi + w;"),
     ("im2win row stored row by row instead of column by column",
      "int64_t out = ((plane * Ho + ho) * Wi + w) * Hf + kh;",
      "int64_t out = ((plane * Ho + ho) * Hf + kh) * Wi + w;"),
     ("im2win source row ignores the stride",
-     "int64_t in = (plane * Hi + (int64_t)ho * s + kh) * Wi + w;",
+     "int64_t in = (plane * Hi + (int64_t)ho * sh + kh) * Wi + w;",
      "int64_t in = (plane * Hi + (int64_t)ho + kh) * Wi + w;"),
     ("im2win window read in filter order",
      "acc += (double)win[kw * Hf + kh] *",
