@@ -505,7 +505,7 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
     a.dup = std::max(0, c.Hf - c.s);
     if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
     nb = 2;
-    wco = 1;
+    wco = std::max(1, std::min(2, env_int("IM2WIN_F16_WCO", 1)));
     a.xpair = c.Wi % 2 == 0;
     a.NU = ceil_div(c.Wi, c.s);
     a.RS = c.s * a.NU;
