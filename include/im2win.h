@@ -4,11 +4,12 @@
  * The operation is the forward convolution of "Enabling Memory-efficient
  * Im2win Convolution with Multi-precision Support on GPU CUDA and Tensor
  * Cores" (Abstract; Fig. 1; Table I): an NCHW input of N images with Ci
- * channels of Hi x Wi, filters Co x Ci x Hf x Wf, one stride s for both axes,
- * and an NCHW output N x Co x Ho x Wo, with
- *     Ho = floor((Hi - Hf) / s) + 1,   Wo = floor((Wi - Wf) / s) + 1,
+ * channels of Hi x Wi, filters Co x Ci x Hf x Wf, a row stride sh and a
+ * column stride sw (Table I writes the stride as s_h(s_w)), and an NCHW
+ * output N x Co x Ho x Wo, with
+ *     Ho = floor((Hi - Hf) / sh) + 1,   Wo = floor((Wi - Wf) / sw) + 1,
  *     y[n][co][ho][wo] = sum over ci, kh, kw of
- *                        x[n][ci][ho*s + kh][wo*s + kw] * w[co][ci][kh][kw]
+ *                        x[n][ci][ho*sh + kh][wo*sw + kw] * w[co][ci][kh][kw]
  * (cross-correlation: no filter flip, no padding, no dilation, no bias; the
  * pages' layers are all unpadded). Full precision runs on the vector ALUs,
  * half precision on the matrix cores, as the same page's Abstract splits the
@@ -17,11 +18,15 @@
  * The im2win transform is the one of "Im2win: Memory Efficient Convolution
  * On SIMD Architectures" (Abstract): each row of dot-product windows is
  * flattened, distinct elements only, into one row. Here the row for
- * (n, ci, ho) holds input rows ho*s .. ho*s+Hf-1 over all Wi columns, column
- * by column:
- *     ws[n][ci][ho][w*Hf + kh] = x[n][ci][ho*s + kh][w]
+ * (n, ci, ho) holds input rows ho*sh .. ho*sh+Hf-1 over all Wi columns,
+ * column by column:
+ *     ws[n][ci][ho][w*Hf + kh] = x[n][ci][ho*sh + kh][w]
  * so the window of output (ho, wo) is the single contiguous run of Wf*Hf
- * elements starting at wo*s*Hf. The workspace is N*Ci*Ho*(Wi*Hf) elements.
+ * elements starting at wo*sw*Hf. The workspace is N*Ci*Ho*(Wi*Hf) elements.
+ *
+ * Each entry point below takes one stride s used for both axes (sh = sw = s,
+ * as in every row of Table I); its *_strided twin takes sh and sw and is
+ * otherwise identical.
  *
  * Conventions for every entry point:
  *  - Tensors are dense, contiguous, caller-owned DEVICE memory (hipMalloc,
@@ -34,7 +39,7 @@
  *    enqueued and the call returns without synchronising. The library
  *    allocates no memory and keeps no state between calls; concurrent calls
  *    on different streams are safe when their output buffers differ.
- *  - Shape limits: every dimension >= 1, Hf <= Hi, Wf <= Wi, s >= 1, and the
+ *  - Shape limits: every dimension >= 1, Hf <= Hi, Wf <= Wi, strides >= 1, and the
  *    per-image element counts Ci*Hi*Wi, Co*Ho*Wo, Ci*Ho*Wi*Hf and the filter
  *    size Co*Ci*Hf*Wf each below 2^31.
  *  - Argument errors are reported synchronously (no work is enqueued); a
@@ -55,7 +60,7 @@ typedef enum {
     IM2WIN_OK = 0,
     IM2WIN_EINVAL = -1,     /* bad shape, stride, element size or NULL pointer */
     IM2WIN_EWORKSPACE = -2, /* workspace given but smaller than one image's im2win rows */
-    IM2WIN_ELAUNCH = -3     /* a kernel launch failed (message: hipGetLastError) */
+    IM2WIN_ELAUNCH = -3     /* a kernel launch failed (message: im2win_last_error) */
 } im2win_status;
 
 /*
@@ -66,23 +71,30 @@ typedef enum {
  */
 size_t im2win_workspace_bytes(int N, int Ci, int Hi, int Wi, int Hf, int Wf, int s,
                               size_t elem_bytes);
+size_t im2win_workspace_bytes_strided(int N, int Ci, int Hi, int Wi, int Hf, int Wf, int sh,
+                                      int sw, size_t elem_bytes);
 
 /*
  * Output extents Ho, Wo (either pointer may be NULL). Returns IM2WIN_OK or
  * IM2WIN_EINVAL. Pure host arithmetic.
  */
 int im2win_output_dims(int Hi, int Wi, int Hf, int Wf, int s, int *Ho, int *Wo);
+int im2win_output_dims_strided(int Hi, int Wi, int Hf, int Wf, int sh, int sw, int *Ho,
+                               int *Wo);
 
 /*
  * The im2win transform (Im2win ... SIMD Architectures, Abstract), as a bit
  * copy of elem_bytes-wide elements (2 or 4; NaN payloads, infinities and
  * subnormals pass unchanged):
- *     ws[n][ci][ho][w*Hf + kh] = x[n][ci][ho*s + kh][w]
+ *     ws[n][ci][ho][w*Hf + kh] = x[n][ci][ho*sh + kh][w]
  * x: N x Ci x Hi x Wi; ws: im2win_workspace_bytes(...) bytes, written fully.
- * Wf only determines Ho via the shape check. HBM-bound copy kernel.
+ * Wf and sw enter only the shape check (Wo >= 1); the layout of ws does not
+ * depend on them. HBM-bound copy kernel.
  */
 int im2win_pack(const void *x, void *ws, int N, int Ci, int Hi, int Wi, int Hf, int Wf,
                 int s, size_t elem_bytes, void *stream);
+int im2win_pack_strided(const void *x, void *ws, int N, int Ci, int Hi, int Wi, int Hf, int Wf,
+                        int sh, int sw, size_t elem_bytes, void *stream);
 
 /*
  * Workspace of the two convolution entry points, in bytes.
@@ -102,6 +114,9 @@ int im2win_pack(const void *x, void *ws, int N, int Ci, int Hi, int Wi, int Hf, 
  */
 size_t conv2d_im2win_workspace_bytes(int materialize, int N, int Ci, int Hi, int Wi, int Co,
                                      int Hf, int Wf, int s, size_t elem_bytes);
+size_t conv2d_im2win_workspace_bytes_strided(int materialize, int N, int Ci, int Hi, int Wi,
+                                             int Co, int Hf, int Wf, int sh, int sw,
+                                             size_t elem_bytes);
 
 /*
  * fp32 convolution on the vector ALUs ("full precision on CUDA cores" in the
@@ -126,6 +141,9 @@ size_t conv2d_im2win_workspace_bytes(int materialize, int N, int Ci, int Hi, int
 int conv2d_im2win_fp32(const float *x, const float *w, float *y, void *ws, size_t ws_bytes,
                        int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s,
                        void *stream);
+int conv2d_im2win_fp32_strided(const float *x, const float *w, float *y, void *ws,
+                               size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                               int Wf, int sh, int sw, void *stream);
 
 /*
  * fp16-input convolution on the matrix cores ("half precision on tensor
@@ -136,9 +154,18 @@ int conv2d_im2win_fp32(const float *x, const float *w, float *y, void *ws, size_
 int conv2d_im2win_fp16(const uint16_t *x, const uint16_t *w, float *y, void *ws,
                        size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf,
                        int s, void *stream);
+int conv2d_im2win_fp16_strided(const uint16_t *x, const uint16_t *w, float *y, void *ws,
+                               size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                               int Wf, int sh, int sw, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *im2win_status_string(int status);
+
+/*
+ * Text of the HIP runtime error behind the last IM2WIN_ELAUNCH returned on
+ * the calling thread ("no error" if there was none). Static storage.
+ */
+const char *im2win_last_error(void);
 
 #ifdef __cplusplus
 }

@@ -8,6 +8,10 @@ in the library's HIP kernels.
     y = conv2d(x, w, stride)                 # fused: im2win rows built in LDS
     y = conv2d(x, w, stride, ws=workspace)   # materialised im2win tensor
     ws = pack(x, Hf, Wf, stride)             # the im2win transform itself
+
+A stride is one int (both axes) or a pair (sh, sw): row stride, then column
+stride. Equal strides go through the single-stride entry points of the C ABI,
+unequal ones through their *_strided twins.
 """
 from __future__ import annotations
 
@@ -16,7 +20,7 @@ import ctypes
 from . import _lib
 from ._lib import Im2winError, status_string  # noqa: F401
 
-__all__ = ["conv2d", "pack", "workspace_bytes", "conv_workspace_bytes", "output_dims",
+__all__ = ["conv2d", "pack", "workspace_bytes", "conv_workspace_bytes", "output_dims", "strides",
            "Im2winError", "status_string", "load_library"]
 
 
@@ -25,24 +29,43 @@ def load_library():
     return _lib.load()
 
 
-def output_dims(Hi: int, Wi: int, Hf: int, Wf: int, s: int):
+def strides(s):
+    """(sh, sw) of a stride given as one int or a pair."""
+    if isinstance(s, (tuple, list)):
+        if len(s) != 2:
+            raise ValueError("a stride pair is (sh, sw)")
+        return int(s[0]), int(s[1])
+    return int(s), int(s)
+
+
+def _entry(name, s):
+    """The C entry point for stride s and the stride arguments to pass it."""
+    sh, sw = strides(s)
+    L = _lib.load()
+    if sh == sw:
+        return getattr(L, name), (sh,)
+    return getattr(L, name + "_strided"), (sh, sw)
+
+
+def output_dims(Hi: int, Wi: int, Hf: int, Wf: int, s):
     ho, wo = ctypes.c_int(), ctypes.c_int()
-    _lib.check(_lib.load().im2win_output_dims(Hi, Wi, Hf, Wf, s, ctypes.byref(ho),
-                                              ctypes.byref(wo)), "output_dims")
+    fn, st = _entry("im2win_output_dims", s)
+    _lib.check(fn(Hi, Wi, Hf, Wf, *st, ctypes.byref(ho), ctypes.byref(wo)), "output_dims")
     return ho.value, wo.value
 
 
 def workspace_bytes(N, Ci, Hi, Wi, Hf, Wf, s, elem_bytes) -> int:
     """Bytes of the im2win tensor of the whole batch (0 for an invalid shape)."""
-    return _lib.load().im2win_workspace_bytes(N, Ci, Hi, Wi, Hf, Wf, s, elem_bytes)
+    fn, st = _entry("im2win_workspace_bytes", s)
+    return fn(N, Ci, Hi, Wi, Hf, Wf, *st, elem_bytes)
 
 
 def conv_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s, elem_bytes, materialize: bool) -> int:
     """Workspace bytes of a convolution call: the fused mode with a prepacked
     filter (materialize=False; 0 for fp32) or the materialised mode over the
     whole batch (materialize=True). 0 for an invalid shape."""
-    return _lib.load().conv2d_im2win_workspace_bytes(1 if materialize else 0, N, Ci, Hi, Wi, Co,
-                                                    Hf, Wf, s, elem_bytes)
+    fn, st = _entry("conv2d_im2win_workspace_bytes", s)
+    return fn(1 if materialize else 0, N, Ci, Hi, Wi, Co, Hf, Wf, *st, elem_bytes)
 
 
 def _torch():
@@ -67,7 +90,7 @@ def _check_tensor(t, name, dtypes, ndim):
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
 
 
-def pack(x, Hf: int, Wf: int, s: int, out=None):
+def pack(x, Hf: int, Wf: int, s, out=None):
     """The im2win tensor of x (N, Ci, Hi, Wi) as (N, Ci, Ho, Wi*Hf), same dtype.
 
     Any 2- or 4-byte dtype works (the transform is a bit copy).
@@ -82,13 +105,13 @@ def pack(x, Hf: int, Wf: int, s: int, out=None):
         out = torch.empty(shape, dtype=x.dtype, device=x.device)
     elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
-    _lib.check(_lib.load().im2win_pack(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
-                                       N, Ci, Hi, Wi, Hf, Wf, s, x.element_size(),
-                                       _stream_handle(x)), "im2win_pack")
+    fn, st = _entry("im2win_pack", s)
+    _lib.check(fn(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                  N, Ci, Hi, Wi, Hf, Wf, *st, x.element_size(), _stream_handle(x)), fn.__name__)
     return out
 
 
-def conv2d(x, w, stride: int = 1, ws=None, ws_bytes: int | None = None, out=None):
+def conv2d(x, w, stride=1, ws=None, ws_bytes: int | None = None, out=None):
     """Forward convolution (cross-correlation, no padding) of x (N,Ci,Hi,Wi)
     with w (Co,Ci,Hf,Wf); fp32 output (N,Co,Ho,Wo).
 
@@ -121,8 +144,9 @@ def conv2d(x, w, stride: int = 1, ws=None, ws_bytes: int | None = None, out=None
             raise ValueError("ws must be a contiguous GPU tensor")
         ws_ptr = ctypes.c_void_p(ws.data_ptr())
         nbytes = ws.numel() * ws.element_size() if ws_bytes is None else int(ws_bytes)
-    fn = _lib.load().conv2d_im2win_fp32 if x.dtype == torch.float32 else _lib.load().conv2d_im2win_fp16
+    fn, st = _entry("conv2d_im2win_fp32" if x.dtype == torch.float32 else "conv2d_im2win_fp16",
+                    stride)
     _lib.check(fn(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
                   ctypes.c_void_p(out.data_ptr()), ws_ptr, nbytes,
-                  N, Ci, Hi, Wi, Co, Hf, Wf, stride, _stream_handle(x)), fn.__name__)
+                  N, Ci, Hi, Wi, Co, Hf, Wf, *st, _stream_handle(x)), fn.__name__)
     return out

@@ -27,7 +27,14 @@ EXPORTS = {
     "conv2d_im2win_fp32": ([_p, _p, _p, _p, _sz] + [_i] * 8 + [_p], _i),
     "conv2d_im2win_fp16": ([_p, _p, _p, _p, _sz] + [_i] * 8 + [_p], _i),
     "conv2d_im2win_workspace_bytes": ([_i] * 9 + [_sz], _sz),
+    "im2win_workspace_bytes_strided": ([_i] * 8 + [_sz], _sz),
+    "im2win_output_dims_strided": ([_i] * 6 + [ctypes.POINTER(_i), ctypes.POINTER(_i)], _i),
+    "im2win_pack_strided": ([_p, _p] + [_i] * 8 + [_sz, _p], _i),
+    "conv2d_im2win_fp32_strided": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
+    "conv2d_im2win_fp16_strided": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
+    "conv2d_im2win_workspace_bytes_strided": ([_i] * 10 + [_sz], _sz),
     "im2win_status_string": ([_i], ctypes.c_char_p),
+    "im2win_last_error": ([], ctypes.c_char_p),
 }
 
 _lib = None
@@ -36,7 +43,10 @@ _lib = None
 class Im2winError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
-        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        msg = f"{what}: {status_string(status)} (status {status})"
+        if status == IM2WIN_ELAUNCH:
+            msg += f": {load().im2win_last_error().decode()}"
+        super().__init__(msg)
 
 
 def load() -> ctypes.CDLL:
@@ -47,6 +57,12 @@ def load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
             "(python -c 'import __graft_entry__ as g; g.build()' from the repository root)")
+    # torch carries its own HIP runtime, which it loads by the unversioned
+    # file name; libim2win.so asks for the versioned soname. Loaded after
+    # torch, the library binds to torch's runtime (same soname); loaded
+    # first, it would pull in a second runtime that torch then cannot share,
+    # and device pointers and streams would not be valid across the two.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     for name, (args, res) in EXPORTS.items():
         f = getattr(L, name)

@@ -14,12 +14,15 @@ using im2win::ConvShape;
 
 constexpr int64_t kMax32 = 0x7fffffff;
 
-// Derives Ho, Wo and checks every limit of the contract.
-bool check_shape(int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s, int* Ho, int* Wo)
+// Derives Ho, Wo and checks every limit of the contract (sh, sw: row and
+// column strides).
+bool check_shape(int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw, int* Ho,
+                 int* Wo)
 {
-    if (N < 1 || Ci < 1 || Hi < 1 || Wi < 1 || Co < 1 || Hf < 1 || Wf < 1 || s < 1) return false;
+    if (N < 1 || Ci < 1 || Hi < 1 || Wi < 1 || Co < 1 || Hf < 1 || Wf < 1) return false;
+    if (sh < 1 || sw < 1) return false;
     if (Hf > Hi || Wf > Wi) return false;
-    const int ho = (Hi - Hf) / s + 1, wo = (Wi - Wf) / s + 1;
+    const int ho = (Hi - Hf) / sh + 1, wo = (Wi - Wf) / sw + 1;
     if ((int64_t)Ci * Hi * Wi > kMax32) return false;
     if ((int64_t)Co * ho * wo > kMax32) return false;
     if ((int64_t)Ci * ho * Wi * Hf > kMax32) return false;
@@ -37,6 +40,8 @@ int status_of(int rc)
     if (rc == -1) return IM2WIN_EINVAL;
     return IM2WIN_ELAUNCH;
 }
+
+thread_local hipError_t g_last_error = hipSuccess;
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -60,7 +65,7 @@ WsPlan ws_plan(const ConvShape& c, size_t elem)
 // Shared driver of both precisions. T is the element type of x, w and ws.
 template <typename T>
 int conv_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int N, int Ci, int Hi,
-                int Wi, int Co, int Hf, int Wf, int s, hipStream_t stream,
+                int Wi, int Co, int Hf, int Wf, int sh, int sw, hipStream_t stream,
                 int (*fused)(const T*, const T*, const void*, float*, const ConvShape&, hipStream_t),
                 int (*from_ws)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t),
                 int (*generic)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t),
@@ -68,10 +73,10 @@ int conv_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int
 {
     int Ho, Wo;
     if (!x || !w || !y) return IM2WIN_EINVAL;
-    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, s, &Ho, &Wo)) return IM2WIN_EINVAL;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return IM2WIN_EINVAL;
     if (!aligned(x, sizeof(T)) || !aligned(w, sizeof(T)) || !aligned(y, sizeof(float)))
         return IM2WIN_EINVAL;
-    ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, s, Ho, Wo};
+    ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo};
     const WsPlan p = ws_plan(c, sizeof(T));
     if (ws == nullptr) {
         if (ws_bytes != 0) return IM2WIN_EWORKSPACE;
@@ -97,7 +102,7 @@ int conv_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int
     const int64_t x_img = (int64_t)Ci * Hi * Wi, y_img = (int64_t)Co * Ho * Wo;
     for (int n0 = 0; n0 < N; n0 += chunk) {
         const int nc = std::min(chunk, N - n0);
-        int rc = im2win::launch_pack(x + n0 * x_img, wsb + p.fbytes, nc, Ci, Hi, Wi, Hf, s, Ho,
+        int rc = im2win::launch_pack(x + n0 * x_img, wsb + p.fbytes, nc, Ci, Hi, Wi, Hf, sh, Ho,
                                      (int)sizeof(T), stream);
         if (rc != 0) return status_of(rc);
         ConvShape cc = c;
@@ -150,58 +155,113 @@ int f16_generic(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float*
 
 }  // namespace
 
+namespace im2win {
+int launch_status(hipError_t e)
+{
+    if (e == hipSuccess) return 0;
+    g_last_error = e;
+    return -3;
+}
+}  // namespace im2win
+
 extern "C" {
+
+size_t im2win_workspace_bytes_strided(int N, int Ci, int Hi, int Wi, int Hf, int Wf, int sh,
+                                      int sw, size_t elem_bytes)
+{
+    int Ho;
+    if (elem_bytes != 2 && elem_bytes != 4) return 0;
+    if (!check_shape(N, Ci, Hi, Wi, 1, Hf, Wf, sh, sw, &Ho, nullptr)) return 0;
+    return (size_t)N * Ci * Ho * ((size_t)Wi * Hf) * elem_bytes;
+}
 
 size_t im2win_workspace_bytes(int N, int Ci, int Hi, int Wi, int Hf, int Wf, int s,
                               size_t elem_bytes)
 {
-    int Ho;
-    if (elem_bytes != 2 && elem_bytes != 4) return 0;
-    if (!check_shape(N, Ci, Hi, Wi, 1, Hf, Wf, s, &Ho, nullptr)) return 0;
-    return (size_t)N * Ci * Ho * ((size_t)Wi * Hf) * elem_bytes;
+    return im2win_workspace_bytes_strided(N, Ci, Hi, Wi, Hf, Wf, s, s, elem_bytes);
+}
+
+int im2win_output_dims_strided(int Hi, int Wi, int Hf, int Wf, int sh, int sw, int* Ho, int* Wo)
+{
+    return check_shape(1, 1, Hi, Wi, 1, Hf, Wf, sh, sw, Ho, Wo) ? IM2WIN_OK : IM2WIN_EINVAL;
 }
 
 int im2win_output_dims(int Hi, int Wi, int Hf, int Wf, int s, int* Ho, int* Wo)
 {
-    return check_shape(1, 1, Hi, Wi, 1, Hf, Wf, s, Ho, Wo) ? IM2WIN_OK : IM2WIN_EINVAL;
+    return im2win_output_dims_strided(Hi, Wi, Hf, Wf, s, s, Ho, Wo);
+}
+
+int im2win_pack_strided(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, int Wf,
+                        int sh, int sw, size_t elem_bytes, void* stream)
+{
+    int Ho;
+    if (!x || !ws) return IM2WIN_EINVAL;
+    if (elem_bytes != 2 && elem_bytes != 4) return IM2WIN_EINVAL;
+    if (!check_shape(N, Ci, Hi, Wi, 1, Hf, Wf, sh, sw, &Ho, nullptr)) return IM2WIN_EINVAL;
+    if (!aligned(x, elem_bytes) || !aligned(ws, elem_bytes)) return IM2WIN_EINVAL;
+    return status_of(im2win::launch_pack(x, ws, N, Ci, Hi, Wi, Hf, sh, Ho, (int)elem_bytes,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int im2win_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, int Wf, int s,
                 size_t elem_bytes, void* stream)
 {
-    int Ho;
-    if (!x || !ws) return IM2WIN_EINVAL;
-    if (elem_bytes != 2 && elem_bytes != 4) return IM2WIN_EINVAL;
-    if (!check_shape(N, Ci, Hi, Wi, 1, Hf, Wf, s, &Ho, nullptr)) return IM2WIN_EINVAL;
-    if (!aligned(x, elem_bytes) || !aligned(ws, elem_bytes)) return IM2WIN_EINVAL;
-    return status_of(im2win::launch_pack(x, ws, N, Ci, Hi, Wi, Hf, s, Ho, (int)elem_bytes,
-                                         static_cast<hipStream_t>(stream)));
+    return im2win_pack_strided(x, ws, N, Ci, Hi, Wi, Hf, Wf, s, s, elem_bytes, stream);
+}
+
+size_t conv2d_im2win_workspace_bytes_strided(int materialize, int N, int Ci, int Hi, int Wi,
+                                             int Co, int Hf, int Wf, int sh, int sw,
+                                             size_t elem_bytes)
+{
+    int Ho, Wo;
+    if (elem_bytes != 2 && elem_bytes != 4) return 0;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return 0;
+    const WsPlan p = ws_plan(ConvShape{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo}, elem_bytes);
+    return p.fbytes + (materialize ? (size_t)N * p.per_image : 0);
 }
 
 size_t conv2d_im2win_workspace_bytes(int materialize, int N, int Ci, int Hi, int Wi, int Co,
                                      int Hf, int Wf, int s, size_t elem_bytes)
 {
-    int Ho, Wo;
-    if (elem_bytes != 2 && elem_bytes != 4) return 0;
-    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, s, &Ho, &Wo)) return 0;
-    const WsPlan p = ws_plan(ConvShape{N, Ci, Hi, Wi, Co, Hf, Wf, s, Ho, Wo}, elem_bytes);
-    return p.fbytes + (materialize ? (size_t)N * p.per_image : 0);
+    return conv2d_im2win_workspace_bytes_strided(materialize, N, Ci, Hi, Wi, Co, Hf, Wf, s, s,
+                                                 elem_bytes);
+}
+
+int conv2d_im2win_fp32_strided(const float* x, const float* w, float* y, void* ws,
+                               size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                               int Wf, int sh, int sw, void* stream)
+{
+    return conv_driver<float>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
+                              static_cast<hipStream_t>(stream), f32_fused, f32_from_ws,
+                              f32_generic, f32_no_pack);
 }
 
 int conv2d_im2win_fp32(const float* x, const float* w, float* y, void* ws, size_t ws_bytes, int N,
                        int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s, void* stream)
 {
-    return conv_driver<float>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, s,
-                              static_cast<hipStream_t>(stream), f32_fused, f32_from_ws,
-                              f32_generic, f32_no_pack);
+    return conv2d_im2win_fp32_strided(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, s, s,
+                                      stream);
+}
+
+int conv2d_im2win_fp16_strided(const uint16_t* x, const uint16_t* w, float* y, void* ws,
+                               size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                               int Wf, int sh, int sw, void* stream)
+{
+    return conv_driver<uint16_t>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
+                                 static_cast<hipStream_t>(stream), im2win::launch_conv_f16_fused,
+                                 f16_from_ws, f16_generic, im2win::launch_f16_filter_pack);
 }
 
 int conv2d_im2win_fp16(const uint16_t* x, const uint16_t* w, float* y, void* ws, size_t ws_bytes,
                        int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s, void* stream)
 {
-    return conv_driver<uint16_t>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, s,
-                                 static_cast<hipStream_t>(stream), im2win::launch_conv_f16_fused,
-                                 f16_from_ws, f16_generic, im2win::launch_f16_filter_pack);
+    return conv2d_im2win_fp16_strided(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, s, s,
+                                      stream);
+}
+
+const char* im2win_last_error(void)
+{
+    return g_last_error == hipSuccess ? "no error" : hipGetErrorString(g_last_error);
 }
 
 const char* im2win_status_string(int status)

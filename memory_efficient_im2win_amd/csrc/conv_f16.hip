@@ -12,8 +12,8 @@
 //    32-column blocks, two per wave).
 //  * LDS holds the im2win rows of the tile, channel-interleaved: entry
 //    (th, col*Hf + kh) is 16 bytes = channels 8g..8g+7 of input pixel
-//    ((ho0+th)*s + kh, wo0*s + col). Window position j = kw*Hf + kh of tile
-//    pixel (th, tw) is entry th*XRS + tw*s*Hf + j: the window is one
+//    ((ho0+th)*sh + kh, wo0*sw + col). Window position j = kw*Hf + kh of tile
+//    pixel (th, tw) is entry th*XRS + tw*sw*Hf + j: the window is one
 //    contiguous run (the transform of "Im2win: Memory Efficient Convolution
 //    On SIMD Architectures", Abstract), so each lane's 8-element K slice of
 //    B is one 16-byte LDS read. Fused launches build the rows from x;
@@ -63,7 +63,8 @@ __global__ __launch_bounds__(kThreads) void conv_f16_kernel(const uint16_t* __re
     uint4* X = reinterpret_cast<uint4*>(smem);
     uint4* Wl = reinterpret_cast<uint4*>(smem + a.xbytes);
 
-    const int Ci = a.c.Ci, Hi = a.c.Hi, Wi = a.c.Wi, Co = a.c.Co, s = a.c.s;
+    const int Ci = a.c.Ci, Hi = a.c.Hi, Wi = a.c.Wi, Co = a.c.Co;
+    const int sh = a.c.sh, sw = a.c.sw;
     const int Ho = a.c.Ho, Wo = a.c.Wo, Hf = a.c.Hf, Wf = a.c.Wf;
     const int HW = a.HW;
 
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void conv_f16_kernel(const uint16_t* __re
         bok[m] = pb < a.npb;
         int p = min(pb * 32 + l32, a.P - 1);
         const int th = p / a.TW, tw = p - (p / a.TW) * a.TW;
-        xoff[m] = th * a.XRS + tw * s * Hf + hl;
+        xoff[m] = th * a.XRS + tw * sw * Hf + hl;
     }
     const int woff = hl * 64 + l32;
 
@@ -113,12 +114,12 @@ __global__ __launch_bounds__(kThreads) void conv_f16_kernel(const uint16_t* __re
         if (!FROM_WS) {
             const int64_t cstride = (int64_t)Hi * Wi;
             const int nrows = a.TH * Hf;
-            const int ncol = min(a.LW, Wi - wo0 * s);   // last column tile may be cut by Wi
+            const int ncol = min(a.LW, Wi - wo0 * sw);   // last column tile may be cut by Wi
             for (int r = rsub; r < nrows; r += rstep) {
                 const int th = r / Hf, kh = r - (r / Hf) * Hf;
                 if (ho0 + th >= Ho) continue;
                 const uint16_t* gb =
-                    x + (((int64_t)n * Ci + cb) * Hi + (ho0 + th) * s + kh) * Wi + wo0 * s;
+                    x + (((int64_t)n * Ci + cb) * Hi + (ho0 + th) * sh + kh) * Wi + wo0 * sw;
                 uint4* l = X + th * a.XRS + kh;
                 for (int col = csub; col < ncol; col += tpr) {
                     uint16_t v[8];
@@ -130,11 +131,11 @@ __global__ __launch_bounds__(kThreads) void conv_f16_kernel(const uint16_t* __re
             }
         } else {
             const int64_t cstride = (int64_t)Ho * a.L;
-            const int len = min(a.LW, Wi - wo0 * s) * Hf;
+            const int len = min(a.LW, Wi - wo0 * sw) * Hf;
             for (int r = rsub; r < a.TH; r += rstep) {
                 if (ho0 + r >= Ho) continue;
                 const uint16_t* gb =
-                    ws + (((int64_t)n * Ci + cb) * Ho + ho0 + r) * a.L + wo0 * s * Hf;
+                    ws + (((int64_t)n * Ci + cb) * Ho + ho0 + r) * a.L + wo0 * sw * Hf;
                 uint4* l = X + r * a.XRS;
                 for (int e = csub; e < len; e += tpr) {
                     uint16_t v[8];
@@ -224,7 +225,7 @@ int launch_conv_f16(const uint16_t* x, const uint16_t* ws, const uint16_t* w, fl
     a.TW = std::min(c.Wo, kPxTile);
     for (;;) {
         a.TH = std::max(1, std::min(c.Ho, kPxTile / a.TW));
-        a.LW = (a.TW - 1) * c.s + c.Wf;
+        a.LW = (a.TW - 1) * c.sw + c.Wf;
         a.XRS = a.LW * c.Hf;
         while (a.TH > 1 && wbytes + a.TH * a.XRS * 16 > kMaxLds) --a.TH;
         if (wbytes + a.TH * a.XRS * 16 <= kMaxLds || a.TW == 1) break;
@@ -245,12 +246,11 @@ int launch_conv_f16(const uint16_t* x, const uint16_t* ws, const uint16_t* w, fl
     // Allow the full 160 KiB of gfx950 LDS (set once per kernel).
     static bool lds_attr_set[2] = {false, false};
     if (!lds_attr_set[ws != nullptr]) {
-        if (ws)
-            (void)hipFuncSetAttribute((const void*)conv_f16_kernel<true>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-        else
-            (void)hipFuncSetAttribute((const void*)conv_f16_kernel<false>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+        // On failure the launch below reports any limit it exceeds.
+        const void* f = ws ? (const void*)conv_f16_kernel<true> : (const void*)conv_f16_kernel<false>;
+        if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds) !=
+            hipSuccess)
+            (void)hipGetLastError();
         lds_attr_set[ws != nullptr] = true;
     }
     if (ws)
@@ -259,7 +259,7 @@ int launch_conv_f16(const uint16_t* x, const uint16_t* ws, const uint16_t* w, fl
     else
         hipLaunchKernelGGL(conv_f16_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), lds,
                            stream, x, ws, w, y, a);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return launch_status();
 }
 
 }  // namespace im2win

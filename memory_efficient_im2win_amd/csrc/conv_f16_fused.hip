@@ -15,7 +15,7 @@
 //    pixels: the Hf input rows of each im2win row it needs, channel-
 //    interleaved (16-byte entry = 8 channels of one input pixel), each input
 //    row stored once even where the im2win rows of consecutive output rows
-//    overlap (s < Hf). Output rows of different images get separate rows.
+//    overlap (sh < Hf). Output rows of different images get separate rows.
 //    Within a row the columns are stored stride-phase major, so the window
 //    of a pixel is Hf x Wf entries at fixed offsets from its tap (0, 0), the
 //    32 pixels of an MFMA block read 32 consecutive entries for every tap,
@@ -46,9 +46,9 @@ struct FusedArgs {
     ConvShape c;
     int P, co_tile, co_tiles;
     int64_t px_tiles, total;
-    int rows_max, kmax, dup, RIN;   // output rows per tile, image breaks, s<Hf overlap, LDS rows
+    int rows_max, kmax, dup, RIN;   // output rows per tile, image breaks, sh<Hf overlap, LDS rows
     int HW, HWp, CG, Copad;
-    int NU, RS;                     // columns per stride phase ceil(Wi/s); entries per LDS row s*NU
+    int NU, RS;                     // columns per stride phase ceil(Wi/sw); entries per LDS row sw*NU
     int xentries;                   // LDS entries of the input rows: RIN * RS
     int xunits;                     // staging units: RIN * Wi / 2 (paired) or RIN * Wi
     bool xpair;                     // Wi even: rows fetched 2 columns x 8 channels at a time
@@ -112,9 +112,9 @@ size_t fused_lds_bytes(int xentries, int HPH, int co_tile, int KT)
            ((size_t)KT * 4 + 15) / 16 * 16;
 }
 
-// LDS layout of one staged input row: column c is entry (c % s)*NU + c / s
-// (stride-phase major), so the 32 pixels of an MFMA block, whose window
-// columns are wo*s + kw, read 32 consecutive entries for every tap.
+// LDS layout of one staged input row: column c is entry (c % sw)*NU + c / sw
+// (column-stride-phase major), so the 32 pixels of an MFMA block, whose
+// window columns are wo*sw + kw, read 32 consecutive entries for every tap.
 template <int WCO, int WPX, int NB, bool XPAIR, bool WPK>
 __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
@@ -127,7 +127,8 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     uint4* X = lds;
     uint4* Wl = lds + a.xentries;
 
-    const int Ci = a.c.Ci, Hi = a.c.Hi, Wi = a.c.Wi, Co = a.c.Co, s = a.c.s;
+    const int Ci = a.c.Ci, Hi = a.c.Hi, Wi = a.c.Wi, Co = a.c.Co;
+    const int sh = a.c.sh, sw = a.c.sw;
     const int Ho = a.c.Ho, Wo = a.c.Wo, Hf = a.c.Hf, Wf = a.c.Wf;
     const int HW = a.HW, HWp = a.HWp, RS = a.RS, NU = a.NU;
 
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     const int wco = wave % WCO, wpx = wave / WCO;
 
     // Entry of tap (0, 0) of each pixel: LDS row of its output row gr
-    // (tile-relative r = gr - gr0, image k: r*s + k*dup) times RS, plus wo.
+    // (tile-relative r = gr - gr0, image k: r*sh + k*dup) times RS, plus wo.
     int xb[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
         const int gr = (int)a.divWo.div((uint32_t)(q - (int64_t)gr0 * Wo)) + gr0;
         const int wo = (int)(q - (int64_t)gr * Wo);
         const int k = (int)a.divHo.div((uint32_t)gr) - n0;
-        xb[b] = ((gr - gr0) * s + k * a.dup) * RS + wo;
+        xb[b] = ((gr - gr0) * sh + k * a.dup) * RS + wo;
     }
     // A entry of this lane for tap pair 0: tap hl, channel column wco*64 + l32.
     const int abase = hl * COT + wco * 64 + l32;
@@ -184,11 +185,11 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
             const int nk = n0 + k;
             const int first = max(gr0, nk * Ho), last = min(grl, nk * Ho + Ho - 1);
             if (first > last) break;
-            const int S = (first - gr0) * s + k * a.dup;
-            const int span = (last - first) * s + Hf;
+            const int S = (first - gr0) * sh + k * a.dup;
+            const int span = (last - first) * sh + Hf;
             if (i >= S && i < S + span) {
                 n = nk;
-                h = (first - nk * Ho) * s + (i - S);
+                h = (first - nk * Ho) * sh + (i - S);
                 return true;
             }
         }
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     };
     auto col_entry = [&](int c) {
         const int u = (int)a.divS.div((uint32_t)c);
-        return (c - u * s) * NU + u;
+        return (c - u * sw) * NU + u;
     };
 
     // ---- staging: global -> registers (group g) -> LDS --------------------------
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     };
 
     // Window offsets of the taps in filter order j = kh*Wf + kw (from the
-    // pixel's tap (0, 0): kh*RS + (kw % s)*NU + kw / s), tabulated once per
+    // pixel's tap (0, 0): kh*RS + (kw % sw)*NU + kw / sw), tabulated once per
     // workgroup so each lane reads its own tap's offset (one LDS read per
     // pair, two pairs ahead) instead of walking taps on the scalar unit.
     // Entries from HW on repeat tap HW-1 (in range; such reads are unused
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     for (int j = tid; j < a.KT; j += NT) {
         const int jj = j < HW ? j : HW - 1;
         const int kh = jj / Wf, kw = jj - (jj / Wf) * Wf;
-        T[j] = kh * RS + (kw % s) * NU + kw / s;
+        T[j] = kh * RS + (kw % sw) * NU + kw / sw;
     }
     // Fragments of one tap pair: A for the two 32-channel blocks, B for the
     // NB pixel blocks. Pair t holds taps 2t (lanes 0-31) and 2t+1 (32-63);
@@ -502,13 +503,13 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
     a.KT = (a.HWp + 8 + 3) & ~3;   // reads reach tap index 2*(HWp/2) + 5
     a.Copad = ceil_div(c.Co, kCoPad) * kCoPad;
     a.total = (int64_t)c.N * c.Ho * c.Wo;
-    a.dup = std::max(0, c.Hf - c.s);
+    a.dup = std::max(0, c.Hf - c.sh);
     if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
     nb = 2;
     wco = std::max(1, std::min(2, env_int("IM2WIN_F16_WCO", 1)));
     a.xpair = c.Wi % 2 == 0;
-    a.NU = ceil_div(c.Wi, c.s);
-    a.RS = c.s * a.NU;
+    a.NU = ceil_div(c.Wi, c.sw);
+    a.RS = c.sw * a.NU;
     const int npairs = a.HWp / 2;
     const int64_t plane = (int64_t)c.Ho * c.Wo;
     // Smallest workgroup LDS first: two workgroups of four waves per CU let one
@@ -524,7 +525,7 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
             a.tiles_per_image = (plane + a.P - 1) / a.P;
             a.aligned = (double)(a.tiles_per_image * a.P) <= 1.05 * (double)plane;
             a.kmax = a.aligned || a.rows_max <= 1 ? 0 : ceil_div(a.rows_max - 1, c.Ho);
-            a.RIN = (a.rows_max - 1) * c.s + c.Hf + a.kmax * a.dup;
+            a.RIN = (a.rows_max - 1) * c.sh + c.Hf + a.kmax * a.dup;
             a.xentries = a.RIN * a.RS;
             a.xunits = a.xpair ? a.RIN * (c.Wi / 2) : a.RIN * c.Wi;
             const int nt = 64 * wco * wpx;
@@ -560,7 +561,7 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
     a.divHo = FastDiv((uint32_t)c.Ho);
     a.divWi = FastDiv((uint32_t)c.Wi);
     a.divHalfW = FastDiv((uint32_t)std::max(1, c.Wi / 2));
-    a.divS = FastDiv((uint32_t)c.s);
+    a.divS = FastDiv((uint32_t)c.sw);
     return true;
 }
 
@@ -570,15 +571,17 @@ int launch_t(const uint16_t* x, const uint16_t* w, const uint4* wpk, float* y,
 {
     static bool attr = false;
     if (!attr) {
-        (void)hipFuncSetAttribute((const void*)conv_f16_fused_kernel<WCO, WPX, NB, XVEC, WPK>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+        // On failure the launch below reports any limit it exceeds.
+        if (hipFuncSetAttribute((const void*)conv_f16_fused_kernel<WCO, WPX, NB, XVEC, WPK>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds) != hipSuccess)
+            (void)hipGetLastError();
         attr = true;
     }
     const size_t lds = fused_lds_bytes(a.xentries, a.HPH, a.co_tile, a.KT);
     hipLaunchKernelGGL((conv_f16_fused_kernel<WCO, WPX, NB, XVEC, WPK>),
                        dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(64 * WCO * WPX), lds,
                        stream, x, w, wpk, y, a);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return launch_status();
 }
 
 template <int WCO, int WPX>
@@ -612,7 +615,7 @@ int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, hip
     if (blocks > 0x7fffffff) return -1;
     hipLaunchKernelGGL(f16_filter_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w,
                        (uint4*)wpk, a);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return launch_status();
 }
 
 int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk, float* y,

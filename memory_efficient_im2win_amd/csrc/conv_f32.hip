@@ -11,13 +11,13 @@
 //    lanes, and the staged rows are shared by every output channel.
 //  * Per stage the workgroup holds, for CIC input channels, the im2win rows
 //    of every output row its pixels touch: LDS row (cc, r) for output row
-//    (n, ho) holds input rows ho*s .. ho*s+Hf-1 column by column, so the
-//    window of output column wo is the contiguous run starting at wo*s*Hf
+//    (n, ho) holds input rows ho*sh .. ho*sh+Hf-1 column by column, so the
+//    window of output column wo is the contiguous run starting at wo*sw*Hf
 //    (the transform of "Im2win: Memory Efficient Convolution On SIMD
 //    Architectures", Abstract). Fused launches build these rows from x (each
 //    thread owns an input column and walks its Hf taps); materialised
 //    launches copy them contiguously from the packed tensor. In LDS each row
-//    is kept phase-major (columns grouped by col mod s), which keeps every
+//    is kept phase-major (columns grouped by col mod sw), which keeps every
 //    stride-phase run of a window contiguous and puts neighbouring output
 //    columns an odd number of words apart.
 //  * For each window element a lane reads one LDS value per pixel and
@@ -43,7 +43,7 @@ struct F32Args {
     int px_tiles, co_tiles;
     int rows_max;              // output rows one tile can touch
     int CIC;                   // input channels per LDS stage
-    int NU, HFP;               // columns per stride phase ceil(Wi/s); Hf rounded up to odd
+    int NU, HFP;               // columns per stride phase ceil(Wi/sw); Hf rounded up to odd
     int RS, CS;                // LDS floats per (channel, row) and per channel
     int tpr_shift;             // log2(threads per staged segment)
     int L;                     // im2win row length Wi*Hf
@@ -52,8 +52,9 @@ struct F32Args {
 };
 
 // LDS position of im2win element (col, kh) inside one staged row. The row is
-// stored phase-major: the columns of stride phase p = col % s come first as
-// one run (col / s ascending), each column's Hf taps contiguous (HFP apart).
+// stored phase-major: the columns of column-stride phase p = col % sw come
+// first as one run (col / sw ascending), each column's Hf taps contiguous
+// (HFP apart).
 // Consecutive output columns then sit HFP (odd) floats apart, so the 64
 // lanes of a wave read distinct LDS banks.
 template <int S>
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kMaxThreads) void conv_f32_kernel(const float* __re
     const int Ho = a.c.Ho, Wo = a.c.Wo;
     const int Hf = HF ? HF : a.c.Hf;
     const int Wf = WF ? WF : a.c.Wf;
-    const int s = S ? S : a.c.s;
+    const int sw = S ? S : a.c.sw;    // S: the column stride when fixed
     const int HW = Hf * Wf;
     const int K = Ci * HW;
     // Window columns per batch of scalar tap loads: COW*KWC SGPRs per batch.
@@ -140,11 +141,11 @@ __global__ __launch_bounds__(kMaxThreads) void conv_f32_kernel(const float* __re
             const int n = (int)a.divHo.div((uint32_t)gr), ho = gr - n * Ho;
             float* l = lds + cc * a.CS + r * a.RS;
             if (!FROM_WS) {
-                // im2win element (col, kh) = x[n][c0+cc][ho*s + kh][col]: the
+                // im2win element (col, kh) = x[n][c0+cc][ho*sh + kh][col]: the
                 // Hf input rows are consecutive in x.
-                const float* g = x + (((int64_t)n * Ci + c0 + cc) * Hi + ho * s) * Wi;
+                const float* g = x + (((int64_t)n * Ci + c0 + cc) * Hi + ho * a.c.sh) * Wi;
                 for (int col = csub; col < Wi; col += tpr) {
-                    float* ld = l + lds_pos(col, 0, s, a);
+                    float* ld = l + lds_pos(col, 0, sw, a);
 #pragma unroll 4
                     for (int kh = 0; kh < Hf; ++kh) ld[kh] = g[kh * Wi + col];
                 }
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(kMaxThreads) void conv_f32_kernel(const float* __re
                 const float* g = ws + (((int64_t)n * Ci + c0 + cc) * Ho + ho) * a.L;
                 for (int e = csub; e < a.L; e += tpr) {
                     const int col = HF ? e / HF : (int)a.divHf.div((uint32_t)e);
-                    l[lds_pos(col, e - col * Hf, s, a)] = g[e];
+                    l[lds_pos(col, e - col * Hf, sw, a)] = g[e];
                 }
             }
         }
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(kMaxThreads) void conv_f32_kernel(const float* __re
                     }
                 } else {
                     for (int kw = 0; kw < Wf; ++kw) {
-                        const int ph = kw % s, adv = kw / s;
+                        const int ph = kw % sw, adv = kw / sw;
                         float xv[PX];
 #pragma unroll
                         for (int j = 0; j < PX; ++j)
@@ -276,9 +277,9 @@ int launch_conv_f32(const float* x, const float* ws, const float* w, float* y,
     a.c = c;
     a.total = (int64_t)c.N * c.Ho * c.Wo;
     a.L = c.Wi * c.Hf;
-    a.NU = ceil_div(c.Wi, c.s);
+    a.NU = ceil_div(c.Wi, c.sw);
     a.HFP = c.Hf | 1;
-    a.RS = (c.s * a.NU * a.HFP) | 1;
+    a.RS = (c.sw * a.NU * a.HFP) | 1;
     if ((int64_t)c.N * c.Ho > 0x7fffffff) return -1;
 
     // Eight output channels per wave (wider waves spill SGPRs), up to 16
@@ -312,19 +313,21 @@ int launch_conv_f32(const float* x, const float* ws, const float* w, float* y,
     a.divWo = FastDiv((uint32_t)c.Wo);
     a.divHo = FastDiv((uint32_t)c.Ho);
     a.divHf = FastDiv((uint32_t)c.Hf);
-    a.divS = FastDiv((uint32_t)c.s);
+    a.divS = FastDiv((uint32_t)c.sw);
     a.divRows = FastDiv((uint32_t)a.rows_max);
     a.px_tiles = (int)((a.total + a.P - 1) / a.P);
     const int64_t blocks = (int64_t)a.px_tiles * a.co_tiles;
     if (blocks <= 0 || blocks > 0x7fffffff) return -1;
     const size_t lds = (size_t)a.CIC * a.CS * sizeof(float);
     const unsigned nb = (unsigned)blocks, nt = (unsigned)threads;
-    if (c.Hf == 11 && c.Wf == 11 && c.s == 4) launch_px<11, 11, 4>(px, cow, x, ws, w, y, a, nb, nt, lds, stream);
-    else if (c.Hf == 7 && c.Wf == 7 && c.s == 2) launch_px<7, 7, 2>(px, cow, x, ws, w, y, a, nb, nt, lds, stream);
-    else if (c.Hf == 5 && c.Wf == 5 && c.s == 1) launch_px<5, 5, 1>(px, cow, x, ws, w, y, a, nb, nt, lds, stream);
-    else if (c.Hf == 3 && c.Wf == 3 && c.s == 1) launch_px<3, 3, 1>(px, cow, x, ws, w, y, a, nb, nt, lds, stream);
+    // Specialised on the filter and the column stride; the row stride is a
+    // run-time value in every variant.
+    if (c.Hf == 11 && c.Wf == 11 && c.sw == 4) launch_px<11, 11, 4>(px, cow, x, ws, w, y, a, nb, nt, lds, stream);
+    else if (c.Hf == 7 && c.Wf == 7 && c.sw == 2) launch_px<7, 7, 2>(px, cow, x, ws, w, y, a, nb, nt, lds, stream);
+    else if (c.Hf == 5 && c.Wf == 5 && c.sw == 1) launch_px<5, 5, 1>(px, cow, x, ws, w, y, a, nb, nt, lds, stream);
+    else if (c.Hf == 3 && c.Wf == 3 && c.sw == 1) launch_px<3, 3, 1>(px, cow, x, ws, w, y, a, nb, nt, lds, stream);
     else launch_px<0, 0, 0>(px, cow, x, ws, w, y, a, nb, nt, lds, stream);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return launch_status();
 }
 
 }  // namespace im2win

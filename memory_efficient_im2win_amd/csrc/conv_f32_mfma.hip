@@ -50,10 +50,10 @@ struct MArgs {
     int co_tiles, ksplit, spk;        // channel tiles; K splits; stages per split
     int64_t px_tiles, total, tiles_per_image;
     bool aligned;                     // tiles never cross images
-    int rows_max, kmax, dup, RIN;     // output rows per tile, image breaks, s<Hf overlap, LDS rows
+    int rows_max, kmax, dup, RIN;     // output rows per tile, image breaks, sh<Hf overlap, LDS rows
     int HW, CB, nstages, KSP, KT;     // taps; channels per stage; stages; filter row pitch (odd);
                                       // K offset table entries
-    int NU, RS, CSX, xent;            // entries per phase, per row (s*NU), per channel; total
+    int NU, RS, CSX, xent;            // entries per phase, per row (sw*NU), per channel; total
     uint32_t xbytes, wbytes, ybytes;
     FastDiv divWo, divHo, divS;
 };
@@ -84,7 +84,8 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
     float* Wl = lds + a.xent;
     int* T = reinterpret_cast<int*>(Wl + WRW * NW * KSP);   // after WRW*NW filter rows
 
-    const int Ci = a.c.Ci, Hi = a.c.Hi, Wi = a.c.Wi, Co = a.c.Co, s = a.c.s;
+    const int Ci = a.c.Ci, Hi = a.c.Hi, Wi = a.c.Wi, Co = a.c.Co;
+    const int sh = a.c.sh, sw = a.c.sw;
     const int Ho = a.c.Ho, Wo = a.c.Wo, Hf = a.c.Hf, Wf = a.c.Wf;
     const int HW = a.HW, RS = a.RS, NU = a.NU, RIN = a.RIN, CB = a.CB;
     const int64_t plane = (int64_t)Ho * Wo;
@@ -127,17 +128,17 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
 
     // LDS row i of item m -> (image n, input row h); false if no input row
     // maps there. Segment k holds the output rows of image n0+k in the tile,
-    // at LDS rows (first - gr0)*s + k*dup onwards.
+    // at LDS rows (first - gr0)*sh + k*dup onwards.
     auto x_src = [&](const Item& m, int i, int& n, int& h) -> bool {
         for (int k = 0; k <= a.kmax; ++k) {
             const int nk = m.n0 + k;
             const int first = max(m.gr0, nk * Ho), last = min(m.grl, nk * Ho + Ho - 1);
             if (first > last) break;
-            const int S = (first - m.gr0) * s + k * a.dup;
-            const int span = (last - first) * s + Hf;
+            const int S = (first - m.gr0) * sh + k * a.dup;
+            const int span = (last - first) * sh + Hf;
             if (i >= S && i < S + span) {
                 n = nk;
-                h = (first - nk * Ho) * s + (i - S);
+                h = (first - nk * Ho) * sh + (i - S);
                 return true;
             }
         }
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
 
     // Offsets of the K indices of a stage (channel cl, kh, kw in filter
     // order) from a pixel's tap (0, 0) of channel 0: cl*CSX + kh*RS +
-    // (kw % s)*NU + kw / s. Tabulated once per workgroup so that each lane
+    // (kw % sw)*NU + kw / sw. Tabulated once per workgroup so that each lane
     // reads its own index's offset (one LDS read per pair) instead of walking
     // the taps on the scalar unit. Entries past the stage read as offset 0.
     for (int k = tid; k < a.KT; k += NT) {
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
         if (k < CB * HW) {
             const int cl = k / HW, j = k - (k / HW) * HW;
             const int kh = j / Wf, kw = j - (j / Wf) * Wf;
-            off = cl * a.CSX + kh * RS + (kw % s) * NU + kw / s;
+            off = cl * a.CSX + kh * RS + (kw % sw) * NU + kw / sw;
         }
         T[k] = off;
     }
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
     for (int cc = 0; cc < XCH; ++cc) {
         const int col = lane + 64 * cc;
         const int u = (int)a.divS.div((uint32_t)col);
-        xdst[cc] = (col - u * s) * NU + u;
+        xdst[cc] = (col - u * sw) * NU + u;
     }
     float xv[RPW][XCH];
     float wv[WRW][WCH];
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
 
     // ---- compute side (item C) ----------------------------------------------
     // This lane's pixel: entry of its tap (0, 0) in a channel's LDS rows
-    // (output row gr: tile-relative r*s plus image breaks k*dup), and where
+    // (output row gr: tile-relative r*sh plus image breaks k*dup), and where
     // its outputs go.
     Item C;
     int xb = 0;
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
         const int gr = (int)a.divWo.div((uint32_t)(q - (int64_t)C.gr0 * Wo)) + C.gr0;
         const int wo = (int)(q - (int64_t)gr * Wo);
         const int k = (int)a.divHo.div((uint32_t)gr) - C.n0;
-        xb = ((gr - C.gr0) * s + k * a.dup) * RS + wo;
+        xb = ((gr - C.gr0) * sh + k * a.dup) * RS + wo;
     };
     const int abase = l32 * KSP + hl;   // A: channel l32 of each block, K index 2t + hl
 
@@ -439,7 +440,7 @@ bool plan(const ConvShape& c, int nw, int wco, MArgs& a, int& xch, int& wch)
     a.c = c;
     a.HW = c.Hf * c.Wf;
     a.total = (int64_t)c.N * c.Ho * c.Wo;
-    a.dup = std::max(0, c.Hf - c.s);
+    a.dup = std::max(0, c.Hf - c.sh);
     if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
     xch = ceil_div(c.Wi, 64);
     if (xch == 3) xch = 4;
@@ -448,14 +449,14 @@ bool plan(const ConvShape& c, int nw, int wco, MArgs& a, int& xch, int& wch)
     const int wrows = (cot + nw - 1) / nw * nw;   // filter rows staged (>= cot)
 
     // Entries per stride phase: every lane column (64*xch of them) has one.
-    a.NU = ceil_div(64 * xch, c.s);
-    a.RS = c.s * a.NU;
+    a.NU = ceil_div(64 * xch, c.sw);
+    a.RS = c.sw * a.NU;
     const int64_t plane = (int64_t)c.Ho * c.Wo;
     a.rows_max = (P - 1) / c.Wo + 2;
     a.tiles_per_image = (plane + P - 1) / P;
     a.aligned = c.N == 1 || (double)(a.tiles_per_image * P) <= 1.05 * (double)plane;
     a.kmax = a.aligned || a.rows_max <= 1 ? 0 : ceil_div(a.rows_max - 1, c.Ho);
-    a.RIN = (a.rows_max - 1) * c.s + c.Hf + a.kmax * a.dup;
+    a.RIN = (a.rows_max - 1) * c.sh + c.Hf + a.kmax * a.dup;
     if (a.RIN > rows_cap) return false;
     a.CSX = a.RIN * a.RS;
 
@@ -501,7 +502,7 @@ bool plan(const ConvShape& c, int nw, int wco, MArgs& a, int& xch, int& wch)
     a.ybytes = (uint32_t)yb;
     a.divWo = FastDiv((uint32_t)c.Wo);
     a.divHo = FastDiv((uint32_t)c.Ho);
-    a.divS = FastDiv((uint32_t)c.s);
+    a.divS = FastDiv((uint32_t)c.sw);
     return true;
 }
 
@@ -566,12 +567,17 @@ int blocks_per_cu(const void* f, int nt, size_t lds)
     if (it != cache.end()) return it->second;
     if (!raised.count(f)) {
         if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds) !=
-            hipSuccess)
+            hipSuccess) {
+            (void)hipGetLastError();   // handled: this kernel is not used
             return 0;
+        }
         raised.insert(f);
     }
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, nt, lds) != hipSuccess) nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, nt, lds) != hipSuccess) {
+        (void)hipGetLastError();   // handled: this kernel is not used
+        nb = 0;
+    }
     cache[key] = nb;
     return nb;
 }
@@ -579,10 +585,12 @@ int blocks_per_cu(const void* f, int nt, size_t lds)
 int cu_count()
 {
     int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();   // handled: assume a full MI355X
         return 256;
-    return n;
+    }
+    return n < 1 ? 256 : n;
 }
 
 struct Choice {
@@ -703,8 +711,12 @@ int launch_conv_f32_mfma(const float* x, const float* w, float* y, const ConvSha
     MArgs args = a;
     void* params[] = {(void*)&x, (void*)&w, (void*)&y, (void*)&args};
     const dim3 grid((unsigned)ch.grid), block(64 * ch.nw);
-    if (hipLaunchKernel(ch.f, grid, block, params, ch.lds, stream) != hipSuccess) return -3;
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    const hipError_t e = hipLaunchKernel(ch.f, grid, block, params, ch.lds, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return launch_status(e);
+    }
+    return launch_status();
 }
 
 }  // namespace im2win

@@ -39,13 +39,13 @@ __global__ __launch_bounds__(kThreads) void conv_generic_kernel(const T* __restr
     for (int ci = 0; ci < c.Ci; ++ci) {
         const T* wp = w + ((int64_t)co * c.Ci + ci) * HW;
         if (FROM_WS) {
-            const T* win = ws + ((n * c.Ci + ci) * c.Ho + ho) * L + (int64_t)wo * c.s * c.Hf;
+            const T* win = ws + ((n * c.Ci + ci) * c.Ho + ho) * L + (int64_t)wo * c.sw * c.Hf;
             for (int kw = 0; kw < c.Wf; ++kw)
                 for (int kh = 0; kh < c.Hf; ++kh)
                     acc = __builtin_fmaf(to_f32(win[kw * c.Hf + kh]), to_f32(wp[kh * c.Wf + kw]),
                                          acc);
         } else {
-            const T* xp = x + ((n * c.Ci + ci) * c.Hi + (int64_t)ho * c.s) * c.Wi + wo * c.s;
+            const T* xp = x + ((n * c.Ci + ci) * c.Hi + (int64_t)ho * c.sh) * c.Wi + wo * c.sw;
             for (int kw = 0; kw < c.Wf; ++kw)
                 for (int kh = 0; kh < c.Hf; ++kh)
                     acc = __builtin_fmaf(to_f32(xp[(int64_t)kh * c.Wi + kw]),
@@ -68,7 +68,7 @@ int launch_generic(const T* x, const T* ws, const T* w, float* y, const ConvShap
     else
         hipLaunchKernelGGL((conv_generic_kernel<T, false>), dim3((unsigned)blocks),
                            dim3(kThreads), 0, stream, x, ws, w, y, c, total);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return launch_status();
 }
 
 }  // namespace

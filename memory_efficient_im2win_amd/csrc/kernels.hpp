@@ -8,13 +8,20 @@
 
 namespace im2win {
 
-// Convolution geometry of one launch (N = images in this launch).
+// Result of the launches just enqueued: 0 if the runtime reports no error,
+// else -3, keeping the error for im2win_last_error() on this thread.
+int launch_status(hipError_t e);
+inline int launch_status() { return launch_status(hipGetLastError()); }
+
+// Convolution geometry of one launch (N = images in this launch); sh and sw
+// are the row and column strides.
 struct ConvShape {
-    int N, Ci, Hi, Wi, Co, Hf, Wf, s, Ho, Wo;
+    int N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo;
 };
 
 // The im2win transform of N images (bit copy of elem_bytes-wide elements).
-int launch_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, int s, int Ho,
+// Only the row stride sh enters it.
+int launch_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, int sh, int Ho,
                 int elem_bytes, hipStream_t stream);
 
 // fp32 convolution on the vector ALUs. ws == nullptr: im2win rows are built

@@ -3,11 +3,11 @@
 // The transform of "Im2win: Memory Efficient Convolution On SIMD
 // Architectures" (Abstract): each row of dot-product windows (image n,
 // channel ci, output row ho) becomes one row holding the Hf input rows
-// ho*s .. ho*s+Hf-1, column by column:
-//     ws[n][ci][ho][w*Hf + kh] = x[n][ci][ho*s + kh][w]
+// ho*sh .. ho*sh+Hf-1 (sh: the row stride), column by column:
+//     ws[n][ci][ho][w*Hf + kh] = x[n][ci][ho*sh + kh][w]
 //
 // One workgroup produces R consecutive im2win rows of one (n, ci) plane, i.e.
-// one contiguous stretch of ws. It first copies the (R-1)*s + Hf input rows
+// one contiguous stretch of ws. It first copies the (R-1)*sh + Hf input rows
 // those im2win rows draw from into LDS (each input row is read from HBM once
 // per workgroup even when windows overlap), then writes its stretch of ws
 // with 16-byte stores; the ragged head and tail of the stretch, where ws is
@@ -23,7 +23,7 @@ namespace {
 constexpr int kPackThreads = 256;
 
 struct PackArgs {
-    int Hi, Wi, Hf, s, Ho;
+    int Hi, Wi, Hf, sh, Ho;
     int R;              // im2win rows per workgroup
     int chunks;         // workgroups per (n, ci) plane = ceil(Ho / R)
     uint32_t L;         // im2win row length Wi * Hf
@@ -42,8 +42,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const T* __restrict_
     const int chunk = (int)(b - plane * a.chunks);
     const int ho0 = chunk * a.R;
     const int nr = min(a.R, a.Ho - ho0);
-    const int r0 = ho0 * a.s;
-    const int nrows = (nr - 1) * a.s + a.Hf;
+    const int r0 = ho0 * a.sh;
+    const int nrows = (nr - 1) * a.sh + a.Hf;
 
     // ---- input rows [r0, r0 + nrows) of the plane -> LDS ----------------
     const T* src = x + (plane * a.Hi + r0) * (int64_t)a.Wi;
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const T* __restrict_
     const int nvec = nout > first_vec ? (nout - first_vec) / V : 0;
 
     // Source of stretch element e: im2win row hol = e / L, r = e % L,
-    // column w = r / Hf, tap kh = r % Hf  ->  lds[(hol*s + kh)*Wi + w].
+    // column w = r / Hf, tap kh = r % Hf  ->  lds[(hol*sh + kh)*Wi + w].
     auto src_index = [&](uint32_t e, int& hol, int& w, int& kh) {
         hol = (int)a.divL.div(e);
         const uint32_t r = e - (uint32_t)hol * a.L;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const T* __restrict_
         T v[V];
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-            v[j] = lds[(hol * a.s + kh) * a.Wi + w];
+            v[j] = lds[(hol * a.sh + kh) * a.Wi + w];
             if (++kh == a.Hf) {
                 kh = 0;
                 if (++w == a.Wi) { w = 0; ++hol; }
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const T* __restrict_
         const int idx = e < nhead ? e : tail0 + (e - nhead);
         int hol, w, kh;
         src_index((uint32_t)idx, hol, w, kh);
-        dst[idx] = lds[(hol * a.s + kh) * a.Wi + w];
+        dst[idx] = lds[(hol * a.sh + kh) * a.Wi + w];
     }
 }
 
@@ -124,29 +124,29 @@ __global__ __launch_bounds__(kPackThreads) void pack_gather_kernel(const T* __re
     const int64_t plane = row / a.Ho;
     const int ho = (int)(row - plane * a.Ho);
     const int w = r / a.Hf, kh = r - (r / a.Hf) * a.Hf;
-    ws[e] = x[(plane * a.Hi + (int64_t)ho * a.s + kh) * a.Wi + w];
+    ws[e] = x[(plane * a.Hi + (int64_t)ho * a.sh + kh) * a.Wi + w];
 }
 
 }  // namespace
 
-int launch_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, int s,
+int launch_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, int sh,
                 int Ho, int elem_bytes, hipStream_t stream)
 {
     PackArgs a;
-    a.Hi = Hi; a.Wi = Wi; a.Hf = Hf; a.s = s; a.Ho = Ho;
+    a.Hi = Hi; a.Wi = Wi; a.Hf = Hf; a.sh = sh; a.Ho = Ho;
     a.L = (uint32_t)Wi * (uint32_t)Hf;
     // Aim for ~32 KiB written per workgroup, with the staged input rows
     // bounded to 48 KiB of LDS.
     const int64_t row_bytes = (int64_t)a.L * elem_bytes;
     int R = (int)std::max<int64_t>(1, (32 * 1024) / std::max<int64_t>(row_bytes, 1));
     R = std::min(R, Ho);
-    while (R > 1 && ((int64_t)((R - 1) * s + Hf) * Wi * elem_bytes + 16) > 48 * 1024) --R;
+    while (R > 1 && ((int64_t)((R - 1) * sh + Hf) * Wi * elem_bytes + 16) > 48 * 1024) --R;
     a.R = R;
     a.chunks = ceil_div(Ho, R);
     a.divL = FastDiv(a.L);
     a.divHf = FastDiv((uint32_t)Hf);
     const int64_t blocks = (int64_t)N * Ci * a.chunks;
-    const size_t lds = (size_t)((R - 1) * s + Hf) * Wi * elem_bytes + 16;
+    const size_t lds = (size_t)((R - 1) * sh + Hf) * Wi * elem_bytes + 16;
     if (blocks <= 0 || blocks > 0x7fffffff) return -1;
     if (lds > 64 * 1024) {
         const int64_t total = (int64_t)N * Ci * Ho * (int64_t)a.L;
@@ -158,7 +158,7 @@ int launch_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, 
         else
             hipLaunchKernelGGL(pack_gather_kernel<uint32_t>, dim3((unsigned)gb), dim3(kPackThreads),
                                0, stream, (const uint32_t*)x, (uint32_t*)ws, a, total);
-        return hipGetLastError() == hipSuccess ? 0 : -3;
+        return launch_status();
     }
     if (elem_bytes == 2)
         hipLaunchKernelGGL(pack_kernel<uint16_t>, dim3((unsigned)blocks), dim3(kPackThreads), lds,
@@ -166,7 +166,7 @@ int launch_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, 
     else
         hipLaunchKernelGGL(pack_kernel<uint32_t>, dim3((unsigned)blocks), dim3(kPackThreads), lds,
                            stream, (const uint32_t*)x, (uint32_t*)ws, a);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return launch_status();
 }
 
 }  // namespace im2win

@@ -20,9 +20,10 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
+    single = ["im2win_workspace_bytes", "im2win_output_dims", "im2win_pack",
+              "conv2d_im2win_fp32", "conv2d_im2win_fp16", "conv2d_im2win_workspace_bytes"]
     assert declared_functions() == sorted(
-        ["im2win_workspace_bytes", "im2win_output_dims", "im2win_pack", "conv2d_im2win_fp32",
-         "conv2d_im2win_fp16", "conv2d_im2win_workspace_bytes", "im2win_status_string"])
+        single + [f + "_strided" for f in single] + ["im2win_status_string", "im2win_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -54,6 +55,48 @@ def test_workspace_bytes_agrees_with_oracle(orc):
             assert m.output_dims(Hi, Wi, Hf, Wf, s) == orc.out_hw(Hi, Wi, Hf, Wf, s)
 
 
+def test_strided_sizes_agree_with_oracle(orc):
+    import random
+    rnd = random.Random(2)
+    for _ in range(200):
+        Hf, Wf, sh, sw = rnd.randint(1, 6), rnd.randint(1, 6), rnd.randint(1, 5), rnd.randint(1, 5)
+        Hi, Wi = rnd.randint(Hf, 40), rnd.randint(Wf, 40)
+        N, Ci = rnd.randint(1, 4), rnd.randint(1, 9)
+        st = (sh, sw)
+        assert m.output_dims(Hi, Wi, Hf, Wf, st) == orc.out_hw(Hi, Wi, Hf, Wf, st)
+        for e in (2, 4):
+            assert m.workspace_bytes(N, Ci, Hi, Wi, Hf, Wf, st, e) == \
+                orc.im2win_elems(N, Ci, Hi, Wi, Hf, Wf, st) * e
+
+
+def test_single_stride_entry_points_equal_their_strided_twins():
+    L = m.load_library()
+    for (Hi, Wi, Hf, Wf, s) in [(224, 224, 7, 7, 2), (227, 227, 11, 11, 4), (24, 24, 5, 5, 1),
+                                (13, 17, 3, 5, 3)]:
+        a, b, c, d = (ctypes.c_int() for _ in range(4))
+        assert L.im2win_output_dims(Hi, Wi, Hf, Wf, s, ctypes.byref(a), ctypes.byref(b)) == 0
+        assert L.im2win_output_dims_strided(Hi, Wi, Hf, Wf, s, s, ctypes.byref(c),
+                                            ctypes.byref(d)) == 0
+        assert (a.value, b.value) == (c.value, d.value)
+        for e in (2, 4):
+            assert L.im2win_workspace_bytes(3, 5, Hi, Wi, Hf, Wf, s, e) == \
+                L.im2win_workspace_bytes_strided(3, 5, Hi, Wi, Hf, Wf, s, s, e)
+            for mat in (0, 1):
+                assert L.conv2d_im2win_workspace_bytes(mat, 3, 5, Hi, Wi, 64, Hf, Wf, s, e) == \
+                    L.conv2d_im2win_workspace_bytes_strided(mat, 3, 5, Hi, Wi, 64, Hf, Wf, s, s, e)
+
+
+def test_unequal_strides_axes():
+    # Ho follows the row stride, Wo the column stride; the im2win tensor
+    # depends on the row stride only.
+    assert m.output_dims(20, 17, 4, 3, (3, 2)) == (6, 8)
+    assert m.output_dims(17, 20, 3, 4, (2, 3)) == (8, 6)
+    assert m.workspace_bytes(2, 3, 20, 17, 4, 3, (3, 2), 4) == 2 * 3 * 6 * 17 * 4 * 4
+    assert m.workspace_bytes(2, 3, 20, 17, 4, 3, (3, 5), 4) == 2 * 3 * 6 * 17 * 4 * 4
+    with pytest.raises(ValueError):
+        m.strides((1, 2, 3))
+
+
 @pytest.mark.parametrize("args", [
     (0, 1, 4, 4, 2, 2, 1, 4),      # N = 0
     (1, 1, 4, 4, 5, 2, 1, 4),      # Hf > Hi
@@ -66,6 +109,19 @@ def test_workspace_bytes_invalid(args):
     assert m.workspace_bytes(*args) == 0
 
 
+@pytest.mark.parametrize("sh,sw", [(0, 1), (1, 0), (-1, 2)])
+def test_strided_rejects_a_zero_or_negative_stride(sh, sw):
+    L = m.load_library()
+    assert L.im2win_workspace_bytes_strided(1, 1, 8, 8, 2, 2, sh, sw, 4) == 0
+    assert L.conv2d_im2win_workspace_bytes_strided(1, 1, 1, 8, 8, 1, 2, 2, sh, sw, 4) == 0
+    assert L.im2win_output_dims_strided(8, 8, 2, 2, sh, sw, None, None) == _lib.IM2WIN_EINVAL
+    assert L.im2win_pack_strided(FAKE, FAKE, 1, 1, 8, 8, 2, 2, sh, sw, 4, None) == \
+        _lib.IM2WIN_EINVAL
+    for f in (L.conv2d_im2win_fp32_strided, L.conv2d_im2win_fp16_strided):
+        assert f(FAKE, FAKE, FAKE, None, 0, 1, 3, 8, 8, 4, 3, 3, sh, sw, None) == \
+            _lib.IM2WIN_EINVAL
+
+
 def test_output_dims_table1_floor():
     assert m.output_dims(224, 224, 7, 7, 2) == (109, 109)
     with pytest.raises(m.Im2winError):
@@ -76,6 +132,7 @@ def test_status_strings():
     L = m.load_library()
     for st in (0, -1, -2, -3, 7):
         assert L.im2win_status_string(st)
+    assert L.im2win_last_error() == b"no error"
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails its checks first
@@ -140,3 +197,20 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_one_hip_runtime_when_the_library_loads_before_torch():
+    """Using the binding before importing torch must not map a second HIP
+    runtime into the process (the library must bind to torch's)."""
+    import subprocess
+    import sys
+    code = (
+        "import memory_efficient_im2win_amd as m\n"
+        "m.output_dims(8, 8, 3, 3, 1)\n"
+        "import torch\n"
+        "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+        "print(len(paths))\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1", r.stdout

@@ -28,7 +28,8 @@ import numpy as np
 
 @dataclass(frozen=True)
 class ConvShape:
-    """One forward convolution: NCHW input, Co x Ci x Hf x Wf filters, stride s."""
+    """One forward convolution: NCHW input, Co x Ci x Hf x Wf filters, stride s
+    (one int for both axes, or a pair (sh, sw): row stride, column stride)."""
 
     name: str
     N: int
@@ -38,7 +39,7 @@ class ConvShape:
     Co: int
     Hf: int
     Wf: int
-    s: int
+    s: "int | tuple[int, int]"
     dtype: str  # "f32" or "f16" (inputs and filters); output is always f32
 
     @property
