@@ -597,8 +597,12 @@ int launch_w(const uint16_t* x, const uint16_t* w, const uint4* wpk, float* y,
 
 }  // namespace
 
+// With a prepacked filter, shapes the row-staged kernel takes run there
+// (its own filter layout); the rest, and every call without a prepacked
+// filter, run the kernel above.
 size_t f16_filter_pack_bytes(const ConvShape& c)
 {
+    if (f16_rows_applies(c)) return f16_rows_filter_bytes(c);
     FusedArgs a;
     int wco, wpx, nb;
     if (!plan(c, a, wco, wpx, nb)) return 0;
@@ -607,6 +611,7 @@ size_t f16_filter_pack_bytes(const ConvShape& c)
 
 int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, hipStream_t stream)
 {
+    if (f16_rows_applies(c)) return launch_f16_rows_filter_pack(w, wpk, c, stream);
     FusedArgs a;
     int wco, wpx, nb;
     if (!plan(c, a, wco, wpx, nb)) return -1;
@@ -621,6 +626,7 @@ int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, hip
 int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk, float* y,
                           const ConvShape& c, hipStream_t stream)
 {
+    if (wpk && f16_rows_applies(c)) return launch_conv_f16_rows(x, wpk, y, c, stream);
     FusedArgs a;
     int wco, wpx, nb;
     if (!plan(c, a, wco, wpx, nb)) return -1;

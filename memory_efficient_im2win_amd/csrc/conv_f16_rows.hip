@@ -1,0 +1,506 @@
+// fp16 im2win convolution on the CDNA4 matrix cores, with the input rows
+// copied to LDS by direct global-to-LDS loads.
+//
+// The half-precision path of "Enabling Memory-efficient Im2win Convolution
+// with Multi-precision Support on GPU CUDA and Tensor Cores" (Abstract:
+// half-precision multiply-accumulate on matrix hardware), laid out for the
+// im2win property of "Im2win: Memory Efficient Convolution On SIMD
+// Architectures" (Abstract): the part of a window that lies in one input row
+// is one contiguous run of that row.
+//
+//  * GEMM view: rows = output channels (A = filters), columns = output
+//    pixels numbered over the batch (B = windows), K = (input channel c,
+//    filter row kh, filter column kw), with kw padded to 8. One K slice of 8
+//    is one (c, kh): for a pixel it is the 8 consecutive input columns
+//    wo*sw .. wo*sw+7 of input row ho*sh+kh, so each lane's B operand of
+//    v_mfma_f32_32x32x16_f16 is one 16-byte LDS read. Lanes 0-31 take slice
+//    2t, lanes 32-63 slice 2t+1. Filter taps kw >= Wf are zero in the
+//    prepacked filter and the matching B halves are masked to zero, so an
+//    infinity just outside a window never turns into NaN.
+//  * A workgroup owns 64 output channels (two 32-row blocks) and
+//    P = 128 * NWV consecutive pixels; each wave owns 128 pixels (four
+//    32-column blocks): a 2 x 4 register tile of accumulators, so every A
+//    read feeds four MFMAs and every B read two.
+//  * A stage is Cg input channels. Its filter slices (prepacked as
+//    [c][kh][co][8 halves], one kilobyte per slice and channel tile) and the
+//    input rows its pixels cover (copied as they lie in x, one LDS row per
+//    (channel, input row)) are fetched with buffer_load_dwordx4 ... lds: no
+//    registers, no transposition. Three stage buffers rotate; the loads of
+//    stage s+2 are issued as stage s starts, and one barrier per stage both
+//    publishes stage s and frees the buffer of stage s-1.
+//  * The loads are issued from inline assembly so that the compiler, which
+//    would otherwise wait for every outstanding LDS load before each LDS
+//    read, leaves the pipelining to the explicit waits here.
+#include <algorithm>
+#include <cstdlib>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace im2win {
+
+namespace {
+
+constexpr int kRowsLds = 160 * 1024;
+constexpr int kCoT = 64;                  // output channels per tile
+constexpr int kNB = 4;                    // 32-pixel blocks per wave
+constexpr int kBufs = 3;                  // stage buffers
+constexpr int kSlack = 2048;              // LDS past the last buffer: reads one pair past a stage
+constexpr uint32_t kMiss = 0xFFFFFFF0u;   // vector offset past every accepted buffer
+
+struct RowsArgs {
+    ConvShape c;
+    int P, co_tiles;
+    int64_t px_tiles, total, tiles_per_image;
+    bool aligned;                   // tiles never cross images
+    int rows_max, kmax, dup, RIN;   // output rows per tile, image breaks, sh<Hf overlap, LDS rows per channel
+    int RP;                         // halves per LDS row (multiple of 8)
+    int Cg, S, NX, NS, Copad;       // channels per stage, slices per stage (Cg*Hf), row kilobytes
+                                    // per stage, stages (Ci/Cg), prepacked filter channels
+    uint32_t stage_bytes;           // (S + NX) KB: filter slices, then rows
+    uint32_t dummy;                 // LDS byte offset of the landing kilobyte of unused loads
+    uint32_t lds_bytes;
+    uint32_t xbytes, ybytes, wbytes;
+    uint32_t mask[4];               // B dwords: halves kw >= Wf cleared
+    FastDiv divWo, divHo;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rbuf(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16 bytes per lane from buffer r at vector offset voff into LDS at byte
+// lds + 16*lane (lds wave-uniform); an out-of-range lane writes zeros. M0 is
+// saved and restored around the load.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff)
+{
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_loads()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Filter slices (c, kh) as 16-byte entries of the 8 taps kw of one output
+// channel: wp[(c*Hf + kh)*Copad + co] = w[co][c][kh][0..7], zero for kw >= Wf
+// and co >= Co.
+__global__ __launch_bounds__(256) void f16_rows_filter_pack_kernel(const uint16_t* __restrict__ w,
+                                                                   uint4* __restrict__ wp,
+                                                                   RowsArgs a)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)a.c.Ci * a.c.Hf * a.Copad;
+    if (e >= total) return;
+    const int co = (int)(e % a.Copad);
+    const int ck = (int)(e / a.Copad);
+    const int c = ck / a.c.Hf, kh = ck - (ck / a.c.Hf) * a.c.Hf;
+    uint32_t v[4] = {0, 0, 0, 0};
+    if (co < a.c.Co) {
+        const uint16_t* src = w + (((int64_t)co * a.c.Ci + c) * a.c.Hf + kh) * a.c.Wf;
+        for (int kw = 0; kw < a.c.Wf; ++kw) v[kw >> 1] |= (uint32_t)src[kw] << (16 * (kw & 1));
+    }
+    wp[e] = make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int NWV, int DMAX>
+__global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint4* __restrict__ wp,
+                                                                 float* __restrict__ y, RowsArgs a)
+{
+    constexpr int NT = 64 * NWV;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const uint32_t lbase =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+    const int Ci = a.c.Ci, Hi = a.c.Hi, Wi = a.c.Wi, Co = a.c.Co;
+    const int sh = a.c.sh, sw = a.c.sw;
+    const int Ho = a.c.Ho, Wo = a.c.Wo, Hf = a.c.Hf;
+
+    const int co_t = (int)(blockIdx.x % a.co_tiles);
+    const int64_t pt = blockIdx.x / a.co_tiles;
+    const int co0 = co_t * kCoT;
+    int64_t q0, qend;
+    if (a.aligned) {   // tile pt = (image, tile within the image)
+        const int64_t img = pt / a.tiles_per_image;
+        const int64_t plane = (int64_t)Ho * Wo;
+        q0 = img * plane + (pt - img * a.tiles_per_image) * a.P;
+        qend = min(q0 + a.P, (img + 1) * plane);
+    } else {
+        q0 = pt * a.P;
+        qend = q0 + a.P < a.total ? q0 + a.P : a.total;
+    }
+    const int gr0 = (int)(q0 / Wo);
+    const int grl = (int)((qend - 1) / Wo);
+    const int n0 = (int)a.divHo.div((uint32_t)gr0);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int hl = lane >> 5, l32 = lane & 31;
+    const int wave = uniform(tid >> 6);
+
+    // Byte offset, within a stage's rows, of each pixel's tap (c=0, kh=0,
+    // kw=0): LDS row of its output row gr (tile-relative r*sh plus image
+    // breaks k*dup) times the row pitch, plus its first column wo*sw.
+    int pb[kNB];
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+        int64_t q = q0 + (wave * kNB + b) * 32 + l32;
+        if (q >= qend) q = qend - 1;
+        const int gr = (int)a.divWo.div((uint32_t)(q - (int64_t)gr0 * Wo)) + gr0;
+        const int wo = (int)(q - (int64_t)gr * Wo);
+        const int k = (int)a.divHo.div((uint32_t)gr) - n0;
+        pb[b] = (((gr - gr0) * sh + k * a.dup) * a.RP + wo * sw) * 2;
+    }
+
+    // LDS row i -> (image n, input row h); false if no input row maps there.
+    // Segment k holds the output rows of image n0+k that fall in the tile.
+    auto x_src = [&](int i, int& n, int& h) -> bool {
+        for (int k = 0; k <= a.kmax; ++k) {
+            const int nk = n0 + k;
+            const int first = max(gr0, nk * Ho), last = min(grl, nk * Ho + Ho - 1);
+            if (first > last) break;
+            const int S0 = (first - gr0) * sh + k * a.dup;
+            const int span = (last - first) * sh + Hf;
+            if (i >= S0 && i < S0 + span) {
+                n = nk;
+                h = (first - nk * Ho) * sh + (i - S0);
+                return true;
+            }
+        }
+        return false;
+    };
+
+    // Load slots of a stage: slot m < S is filter slice m (one kilobyte: the
+    // tile's 64 channels), slot S + j is kilobyte j of the stage's rows, later
+    // slots land in the dummy kilobyte. Wave v issues slots v + NWV*i; the
+    // per-lane offsets do not depend on the stage (its channels enter through
+    // the buffer base), so they are worked out once.
+    uint32_t voff[DMAX];
+    const int rpc = a.RP >> 3;   // 16-byte chunks per LDS row
+#pragma unroll
+    for (int i = 0; i < DMAX; ++i) {
+        const int m = wave + NWV * i;
+        uint32_t v = kMiss;
+        if (m < a.S) {
+            v = (uint32_t)(((m * a.Copad + co0) + lane) * 16);
+        } else if (m < a.S + a.NX) {
+            const int e = (m - a.S) * 64 + lane;
+            const int row = e / rpc, cc = e - row * rpc;
+            const int cl = row / a.RIN, r = row - cl * a.RIN;
+            int n, h;
+            if (cl < a.Cg && 8 * cc < Wi && x_src(r, n, h))
+                v = (uint32_t)(((((int64_t)n * Ci + cl) * Hi + h) * Wi + 8 * cc) * 2);
+        }
+        voff[i] = v;
+    }
+    auto issue = [&](int s, int sb) {
+        const uint32_t fo = (uint32_t)s * a.S * a.Copad * 16;
+        const int64_t xo = (int64_t)s * a.Cg * Hi * Wi;
+        const __amdgpu_buffer_rsrc_t ra = rbuf(wp + (int64_t)s * a.S * a.Copad, a.wbytes - fo);
+        const __amdgpu_buffer_rsrc_t rx = rbuf(x + xo, a.xbytes - (uint32_t)(xo * 2));
+        const uint32_t base = lbase + (uint32_t)sb * a.stage_bytes;
+#pragma unroll
+        for (int i = 0; i < DMAX; ++i) {
+            const int m = wave + NWV * i;
+            const uint32_t dst = m < a.S + a.NX ? base + (uint32_t)m * 1024 : lbase + a.dummy;
+            dma16(m < a.S ? ra : rx, dst, voff[i]);
+        }
+    };
+    auto issue_none = [&]() {
+        const __amdgpu_buffer_rsrc_t rx = rbuf(x, a.xbytes);
+#pragma unroll
+        for (int i = 0; i < DMAX; ++i) dma16(rx, lbase + a.dummy, kMiss);
+    };
+
+    floatx16_t acc[2][kNB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int b = 0; b < kNB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][b][r] = 0.f;
+
+    struct Frags {
+        half8_t a[2], b[kNB];
+    };
+    const uint32_t m0 = a.mask[0], m1 = a.mask[1], m2 = a.mask[2], m3 = a.mask[3];
+    const int abase = hl * kCoT + l32;   // A entry of slice hl, channel l32
+    // This lane's slice 2t + hl = (channel cl, filter row kh) sits at byte
+    // (cl*RIN + kh)*RP*2 from a pixel's tap (0, 0, 0) within the stage's
+    // rows. It advances by two slices per pair, carrying kh into cl.
+    const int rp2 = a.RP * 2, wrap = (a.RIN - Hf) * a.RP * 2;
+    int skh = 0, soff = 0;
+    auto fetch = [&](Frags& f, const unsigned char* A, const unsigned char* X, int t) {
+        const int o = soff;
+        skh += 2;
+        soff += 2 * rp2;
+        if (skh >= Hf) { skh -= Hf; soff += wrap; }
+        if (skh >= Hf) { skh -= Hf; soff += wrap; }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_memcpy(&f.a[i], A + (size_t)(abase + 2 * t * kCoT + i * 32) * 16, 16);
+        // B addresses are 4-byte aligned (even column stride, row pitch a
+        // multiple of 8 halves) but not 16-byte aligned; stated so, the reads
+        // become aligned dword-pair reads instead of the much slower
+        // unaligned 16-byte form.
+#pragma unroll
+        for (int b = 0; b < kNB; ++b)
+            __builtin_memcpy(&f.b[b], __builtin_assume_aligned(X + pb[b] + o, 4), 16);
+    };
+    // The padded taps are masked here, just before the MFMAs, not at the
+    // read: a mask at the read would wait for that read before the previous
+    // pair's MFMAs could issue.
+    auto mma = [&](Frags& f) {
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) {
+            uint4 u;
+            __builtin_memcpy(&u, &f.b[b], 16);
+            u.x &= m0; u.y &= m1; u.z &= m2; u.w &= m3;
+            __builtin_memcpy(&f.b[b], &u, 16);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                acc[i][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[b], acc[i][b], 0, 0, 0);
+        }
+    };
+
+    const int nk = a.S >> 1;   // K steps per stage (S is even)
+    issue(0, 0);
+    if (a.NS > 1) issue(1, 1); else issue_none();
+    for (int s = 0; s < a.NS; ++s) {
+        wait_loads<DMAX>();   // this wave's loads of stage s have landed
+        __syncthreads();      // every wave's; and stage s-1's buffer is free
+        if (s + 2 < a.NS) issue(s + 2, (s + 2) % kBufs); else issue_none();
+
+        const unsigned char* A = smem + (size_t)(s % kBufs) * a.stage_bytes;
+        const unsigned char* X = A + (size_t)a.S * 1024;
+        Frags f0, f1;
+        skh = hl < Hf ? hl : hl - Hf;       // slice hl (Hf = 1: channel 1, row 0)
+        soff = hl < Hf ? hl * rp2 : a.RIN * rp2;
+        fetch(f0, A, X, 0);
+        // The fragments of pair t+1 are read while the MFMAs of pair t run.
+        // Reads are unconditional (the last ones fall one pair past the
+        // stage, inside the allocation, and are never used), so every path
+        // into an MFMA has the same reads outstanding and the waits stay
+        // exact.
+        int t = 0;
+        for (; t + 2 <= nk; t += 2) {
+            fetch(f1, A, X, t + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(f0);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(f0, A, X, t + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(f1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (t < nk) mma(f0);
+    }
+    wait_loads<0>();   // the last (unused) loads have landed before the workgroup ends
+
+    // Output: lane holds pixel l32 of each block and channels
+    // 8*(r/4) + 4*hl + r%4 of each 32-channel block.
+    const int64_t plane = (int64_t)Ho * Wo;
+    const __amdgpu_buffer_rsrc_t yb = rbuf(y, a.ybytes);
+    const bool all_co = co0 + kCoT <= Co;
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+        const int64_t q = q0 + (wave * kNB + b) * 32 + l32;
+        const int gr = (int)(q / Wo);
+        const int wo = (int)(q - (int64_t)gr * Wo);
+        const int n = (int)a.divHo.div((uint32_t)gr), ho = gr - n * Ho;
+        const uint32_t vo =
+            (uint32_t)((((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo) * 4);
+        if (q >= qend) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int cu = co0 + i * 32 + 8 * (r >> 2) + (r & 3);   // co - 4*hl
+                const float v = acc[i][b][r];
+                if (all_co || cu + 4 * hl < Co)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yb, (int)vo,
+                                                          (int)(cu * plane * 4), 0);
+            }
+    }
+}
+
+int env_int(const char* name, int dflt)
+{
+    const char* v = std::getenv(name);
+    return v && *v ? std::atoi(v) : dflt;
+}
+
+// Load instructions per wave and stage the kernel is built for.
+constexpr int kDmax[] = {4, 5, 6, 8, 12, 16};
+
+// Plans a launch; false if the shape is outside the kernel's envelope:
+// even column stride, Wf <= 8, Wi a multiple of 8 (16-byte row chunks),
+// Ci a multiple of the stage's channel count, tensors addressable with
+// 32-bit buffer offsets. IM2WIN_F16_ROWS=0 turns the kernel off and
+// IM2WIN_F16_ROWS_NWV picks the waves per workgroup (tuning and tests).
+bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax)
+{
+    if (env_int("IM2WIN_F16_ROWS", 1) == 0) return false;
+    if (c.Wf > 8 || c.sw % 2 != 0 || c.Wi % 8 != 0) return false;
+    a.c = c;
+    a.total = (int64_t)c.N * c.Ho * c.Wo;
+    a.dup = std::max(0, c.Hf - c.sh);
+    a.RP = ((std::max(c.Wi, (c.Wo - 1) * c.sw + 8) + 7) / 8) * 8;
+    a.Copad = ceil_div(c.Co, kCoT) * kCoT;
+    if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
+    const int64_t plane = (int64_t)c.Ho * c.Wo;
+    const int env_nwv = env_int("IM2WIN_F16_ROWS_NWV", 0);
+    bool found = false;
+    for (int v : {8, 4}) {
+        if (env_nwv && v != env_nwv) continue;
+        a.P = 32 * kNB * v;
+        // Output rows a tile touches (never more than the batch has) and
+        // image breaks inside a tile (never more than N - 1).
+        a.rows_max = (int)std::min<int64_t>((a.P - 1) / c.Wo + 2, (int64_t)c.N * c.Ho);
+        a.tiles_per_image = (plane + a.P - 1) / a.P;
+        a.aligned = (double)(a.tiles_per_image * a.P) <= 1.05 * (double)plane;
+        a.kmax = a.aligned || a.rows_max <= 1 ? 0
+                                              : std::min(c.N - 1, ceil_div(a.rows_max - 1, c.Ho));
+        a.RIN = (a.rows_max - 1) * c.sh + c.Hf + a.kmax * a.dup;
+        for (int cg : {4, 2}) {
+            if (c.Ci % cg != 0 || (cg * c.Hf) % 2 != 0) continue;
+            const int S = cg * c.Hf;
+            const int NX = (int)ceil_div(cg * a.RIN * a.RP * 2, 1024);
+            const int need = ceil_div(S + NX, v);
+            int dm = 0;
+            for (int d : kDmax)
+                if (d >= need) {
+                    dm = d;
+                    break;
+                }
+            if (!dm) continue;
+            const int64_t stage = (int64_t)(S + NX) * 1024;
+            const int64_t lds = kBufs * stage + 1024 + kSlack;
+            if (lds > kRowsLds) continue;
+            a.Cg = cg;
+            a.S = S;
+            a.NX = NX;
+            a.stage_bytes = (uint32_t)stage;
+            a.dummy = (uint32_t)(kBufs * stage);
+            a.lds_bytes = (uint32_t)lds;
+            nwv = v;
+            dmax = dm;
+            found = true;
+            break;
+        }
+        if (found) break;
+    }
+    if (!found) return false;
+    if (a.aligned) a.kmax = 0;
+    a.NS = c.Ci / a.Cg;
+    a.co_tiles = ceil_div(c.Co, kCoT);
+    a.px_tiles = a.aligned ? (int64_t)c.N * a.tiles_per_image : (a.total + a.P - 1) / a.P;
+    if (a.px_tiles * a.co_tiles > 0x7fffffff) return false;
+    // Buffer ranges are 32-bit and the miss offset must lie past every one.
+    const int64_t xb = (int64_t)c.N * c.Ci * c.Hi * c.Wi * 2;
+    const int64_t yb = (int64_t)c.N * c.Co * c.Ho * c.Wo * 4;
+    const int64_t wb = (int64_t)c.Ci * c.Hf * a.Copad * 16;
+    if (xb >= 0x7fffffff || yb >= (int64_t)kMiss || wb >= 0x7fffffff) return false;
+    a.xbytes = (uint32_t)xb;
+    a.ybytes = (uint32_t)yb;
+    a.wbytes = (uint32_t)wb;
+    for (int d = 0; d < 4; ++d) {
+        uint32_t m = 0;
+        if (2 * d < c.Wf) m |= 0xFFFFu;
+        if (2 * d + 1 < c.Wf) m |= 0xFFFF0000u;
+        a.mask[d] = m;
+    }
+    a.divWo = FastDiv((uint32_t)c.Wo);
+    a.divHo = FastDiv((uint32_t)c.Ho);
+    return true;
+}
+
+template <int NWV, int DMAX>
+int launch_t(const uint16_t* x, const uint4* wp, float* y, const RowsArgs& a, hipStream_t stream)
+{
+    static bool attr = false;
+    if (!attr) {
+        // On failure the launch below reports any limit it exceeds.
+        if (hipFuncSetAttribute((const void*)conv_f16_rows_kernel<NWV, DMAX>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kRowsLds) != hipSuccess)
+            (void)hipGetLastError();
+        attr = true;
+    }
+    hipLaunchKernelGGL((conv_f16_rows_kernel<NWV, DMAX>),
+                       dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(64 * NWV), a.lds_bytes,
+                       stream, x, wp, y, a);
+    return launch_status();
+}
+
+template <int NWV>
+int launch_d(int dmax, const uint16_t* x, const uint4* wp, float* y, const RowsArgs& a,
+             hipStream_t stream)
+{
+    switch (dmax) {
+    case 4: return launch_t<NWV, 4>(x, wp, y, a, stream);
+    case 5: return launch_t<NWV, 5>(x, wp, y, a, stream);
+    case 6: return launch_t<NWV, 6>(x, wp, y, a, stream);
+    case 8: return launch_t<NWV, 8>(x, wp, y, a, stream);
+    case 12: return launch_t<NWV, 12>(x, wp, y, a, stream);
+    case 16: return launch_t<NWV, 16>(x, wp, y, a, stream);
+    }
+    return -1;
+}
+
+}  // namespace
+
+bool f16_rows_applies(const ConvShape& c)
+{
+    RowsArgs a;
+    int nwv, dmax;
+    return plan(c, a, nwv, dmax);
+}
+
+size_t f16_rows_filter_bytes(const ConvShape& c)
+{
+    RowsArgs a;
+    int nwv, dmax;
+    if (!plan(c, a, nwv, dmax)) return 0;
+    return (size_t)a.wbytes;
+}
+
+int launch_f16_rows_filter_pack(const uint16_t* w, void* wp, const ConvShape& c, hipStream_t stream)
+{
+    RowsArgs a;
+    int nwv, dmax;
+    if (!plan(c, a, nwv, dmax)) return -1;
+    const int64_t total = (int64_t)c.Ci * c.Hf * a.Copad;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks > 0x7fffffff) return -1;
+    hipLaunchKernelGGL(f16_rows_filter_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w,
+                       static_cast<uint4*>(wp), a);
+    return launch_status();
+}
+
+int launch_conv_f16_rows(const uint16_t* x, const void* wp, float* y, const ConvShape& c,
+                         hipStream_t stream)
+{
+    RowsArgs a;
+    int nwv, dmax;
+    if (!plan(c, a, nwv, dmax)) return -1;
+    // Rows are fetched in 16-byte chunks from 16-byte boundaries.
+    if ((uintptr_t)x % 16 != 0 || (uintptr_t)wp % 16 != 0) return -1;
+    const uint4* w4 = static_cast<const uint4*>(wp);
+    if (nwv == 8) return launch_d<8>(dmax, x, w4, y, a, stream);
+    return launch_d<4>(dmax, x, w4, y, a, stream);
+}
+
+}  // namespace im2win

@@ -48,6 +48,17 @@ int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk,
 size_t f16_filter_pack_bytes(const ConvShape& c);
 int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, hipStream_t stream);
 
+// fp16 convolution with the input rows copied to LDS by direct loads and the
+// filter prepacked by launch_f16_rows_filter_pack (its own layout). Used by
+// the three calls above, with a prepacked filter, for the shapes it takes
+// (f16_rows_applies). -1 if the shape or x's alignment is outside its envelope.
+bool f16_rows_applies(const ConvShape& c);
+size_t f16_rows_filter_bytes(const ConvShape& c);
+int launch_f16_rows_filter_pack(const uint16_t* w, void* wp, const ConvShape& c,
+                                hipStream_t stream);
+int launch_conv_f16_rows(const uint16_t* x, const void* wp, float* y, const ConvShape& c,
+                         hipStream_t stream);
+
 // Plain fallbacks (one thread per output) for shapes the tiled kernels do
 // not take; ws as above.
 int launch_conv_generic_f32(const float* x, const float* ws, const float* w, float* y,

@@ -253,3 +253,64 @@ def test_conv_f16_fused_tilings(t, env, orc, monkeypatch):
         assert_within(_run(sh, "f16", x, w, kind), ref, absd, TOL["f16"], sh.describe())
     xi, wi = workloads.make_inputs(sh, seed=23, mode="int")
     assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
+
+
+# Shapes the row-staged fp16 kernel takes with a prepacked filter (even column
+# stride, Wf <= 8, Wi a multiple of 8, Ci even): several tiles and channel
+# tiles, image breaks inside tiles, rectangles, Wf = 8 (no padded taps).
+ROWS = [
+    (2, 16, 30, 32, 70, 7, 7, 2),
+    (1, 64, 40, 40, 64, 7, 7, 2),
+    (3, 6, 23, 24, 33, 3, 5, (1, 2)),
+    (2, 4, 17, 48, 40, 4, 8, (3, 4)),
+    (4, 2, 9, 16, 64, 2, 2, 2),
+    (5, 4, 12, 16, 64, 3, 3, 2),
+    (2, 8, 20, 64, 128, 5, 3, (2, 2)),
+    (2, 2, 65, 64, 40, 3, 3, 2),      # tiles aligned to images
+]
+
+
+def _filter_bytes(sh):
+    return m.conv_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 2, False)
+
+
+@pytest.mark.parametrize("nwv", ["8", "4"])
+@pytest.mark.parametrize("t", ROWS, ids=str)
+def test_conv_f16_row_staged(t, nwv, orc, monkeypatch):
+    """The fp16 kernel that copies input rows to LDS with direct loads (used
+    with a prepacked filter): uniform and integer inputs, 8 and 4 waves."""
+    monkeypatch.setenv("IM2WIN_F16_ROWS_NWV", nwv)
+    sh = _shape(t, "f16")
+    on = _filter_bytes(sh)
+    monkeypatch.setenv("IM2WIN_F16_ROWS", "0")
+    off = _filter_bytes(sh)
+    monkeypatch.setenv("IM2WIN_F16_ROWS", "1")
+    assert on == sh.Ci * sh.Hf * ((sh.Co + 63) // 64 * 64) * 16 and on != off, (on, off)
+    x, w = workloads.make_inputs(sh, seed=40)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    note(f"conv fp16 row-staged NWV={nwv} {sh.describe()}")
+    assert_within(_run(sh, "f16", x, w, "filter"), ref, absd, TOL["f16"], sh.describe())
+    xi, wi = workloads.make_inputs(sh, seed=41, mode="int")
+    assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
+
+
+def test_conv_f16_row_staged_special_values(orc):
+    """Infinities and NaN in the input reach exactly the outputs whose windows
+    hold them: the padded taps kw >= Wf never multiply a neighbour's Inf."""
+    sh = _shape((2, 4, 14, 16, 40, 3, 5, 2), "f16")
+    x, w = workloads.make_inputs(sh, seed=42)
+    x[0, 1, 4, 5] = np.inf
+    x[0, 2, 7, 13] = -np.inf
+    x[1, 3, 0, 6] = np.nan
+    x[1, 0, 13, 15] = np.inf
+    w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
+    ref = orc.conv_direct(x, w, sh.s)
+    note(f"conv fp16 row-staged special values {sh.describe()}")
+    y = _run(sh, "f16", x, w, "filter").astype(np.float64)
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
+                              with_absdot=True)
+    assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
