@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void f16_rows_filter_pack_kernel(const uint16_
     wp[e] = make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-template <int NWV, int DMAX>
+template <int NWV, int DMAX, bool M3>
 __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t* __restrict__ x,
                                                                  const uint4* __restrict__ wp,
                                                                  float* __restrict__ y, RowsArgs a)
@@ -262,13 +262,19 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
     };
     // The padded taps are masked here, just before the MFMAs, not at the
     // read: a mask at the read would wait for that read before the previous
-    // pair's MFMAs could issue.
+    // pair's MFMAs could issue. With Wf >= 6 (M3) only the last dword holds
+    // padded taps.
     auto mma = [&](Frags& f) {
 #pragma unroll
         for (int b = 0; b < kNB; ++b) {
             uint4 u;
             __builtin_memcpy(&u, &f.b[b], 16);
-            u.x &= m0; u.y &= m1; u.z &= m2; u.w &= m3;
+            if (!M3) {
+                u.x &= m0;
+                u.y &= m1;
+                u.z &= m2;
+            }
+            u.w &= m3;
             __builtin_memcpy(&f.b[b], &u, 16);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -428,34 +434,34 @@ bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax)
     return true;
 }
 
-template <int NWV, int DMAX>
+template <int NWV, int DMAX, bool M3>
 int launch_t(const uint16_t* x, const uint4* wp, float* y, const RowsArgs& a, hipStream_t stream)
 {
     static bool attr = false;
     if (!attr) {
         // On failure the launch below reports any limit it exceeds.
-        if (hipFuncSetAttribute((const void*)conv_f16_rows_kernel<NWV, DMAX>,
+        if (hipFuncSetAttribute((const void*)conv_f16_rows_kernel<NWV, DMAX, M3>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kRowsLds) != hipSuccess)
             (void)hipGetLastError();
         attr = true;
     }
-    hipLaunchKernelGGL((conv_f16_rows_kernel<NWV, DMAX>),
+    hipLaunchKernelGGL((conv_f16_rows_kernel<NWV, DMAX, M3>),
                        dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(64 * NWV), a.lds_bytes,
                        stream, x, wp, y, a);
     return launch_status();
 }
 
-template <int NWV>
+template <int NWV, bool M3>
 int launch_d(int dmax, const uint16_t* x, const uint4* wp, float* y, const RowsArgs& a,
              hipStream_t stream)
 {
     switch (dmax) {
-    case 4: return launch_t<NWV, 4>(x, wp, y, a, stream);
-    case 5: return launch_t<NWV, 5>(x, wp, y, a, stream);
-    case 6: return launch_t<NWV, 6>(x, wp, y, a, stream);
-    case 8: return launch_t<NWV, 8>(x, wp, y, a, stream);
-    case 12: return launch_t<NWV, 12>(x, wp, y, a, stream);
-    case 16: return launch_t<NWV, 16>(x, wp, y, a, stream);
+    case 4: return launch_t<NWV, 4, M3>(x, wp, y, a, stream);
+    case 5: return launch_t<NWV, 5, M3>(x, wp, y, a, stream);
+    case 6: return launch_t<NWV, 6, M3>(x, wp, y, a, stream);
+    case 8: return launch_t<NWV, 8, M3>(x, wp, y, a, stream);
+    case 12: return launch_t<NWV, 12, M3>(x, wp, y, a, stream);
+    case 16: return launch_t<NWV, 16, M3>(x, wp, y, a, stream);
     }
     return -1;
 }
@@ -499,8 +505,9 @@ int launch_conv_f16_rows(const uint16_t* x, const void* wp, float* y, const Conv
     // Rows are fetched in 16-byte chunks from 16-byte boundaries.
     if ((uintptr_t)x % 16 != 0 || (uintptr_t)wp % 16 != 0) return -1;
     const uint4* w4 = static_cast<const uint4*>(wp);
-    if (nwv == 8) return launch_d<8>(dmax, x, w4, y, a, stream);
-    return launch_d<4>(dmax, x, w4, y, a, stream);
+    if (nwv == 8 && c.Wf >= 6) return launch_d<8, true>(dmax, x, w4, y, a, stream);
+    if (nwv == 8) return launch_d<8, false>(dmax, x, w4, y, a, stream);
+    return launch_d<4, false>(dmax, x, w4, y, a, stream);
 }
 
 }  // namespace im2win

@@ -294,15 +294,18 @@ def test_conv_f16_row_staged(t, nwv, orc, monkeypatch):
     assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
 
 
-def test_conv_f16_row_staged_special_values(orc):
+@pytest.mark.parametrize("t", [(2, 4, 14, 16, 40, 3, 5, 2), (2, 4, 15, 24, 40, 3, 7, 2)], ids=str)
+def test_conv_f16_row_staged_special_values(t, orc):
     """Infinities and NaN in the input reach exactly the outputs whose windows
-    hold them: the padded taps kw >= Wf never multiply a neighbour's Inf."""
-    sh = _shape((2, 4, 14, 16, 40, 3, 5, 2), "f16")
+    hold them: the padded taps kw >= Wf never multiply a neighbour's Inf
+    (Wf = 5 masks three dwords of each slice, Wf = 7 only the last)."""
+    sh = _shape(t, "f16")
     x, w = workloads.make_inputs(sh, seed=42)
     x[0, 1, 4, 5] = np.inf
     x[0, 2, 7, 13] = -np.inf
     x[1, 3, 0, 6] = np.nan
     x[1, 0, 13, 15] = np.inf
+    x[0, 0, 2, 7] = np.inf
     w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
     ref = orc.conv_direct(x, w, sh.s)
     note(f"conv fp16 row-staged special values {sh.describe()}")
