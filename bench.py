@@ -38,8 +38,9 @@ PEAK_HBM_GBS = 8000.0
 HEADLINE = "cv1_f32_n32"
 LAYER_KEYS = ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64", "cv4_f16_n64",
               "cv2_f32_n32"]
-KERNEL_SOURCES = ["conv_f32_mfma.hip", "conv_f32.hip", "conv_f16_fused.hip", "conv_f16.hip",
-                  "conv_generic.hip", "pack.hip", "api.hip", "common.hpp", "kernels.hpp"]
+KERNEL_SOURCES = ["conv_f32_mfma.hip", "conv_f32.hip", "conv_f16_fused.hip", "conv_f16_rows.hip",
+                  "conv_f16.hip", "conv_generic.hip", "pack.hip", "api.hip", "common.hpp",
+                  "kernels.hpp"]
 # Modes: fused (no workspace), fused_valu (fp32 on the vector-ALU kernel),
 # prepacked (fp16 filter prepacked into a small workspace), materialized
 # (im2win tensor in HBM).
@@ -47,7 +48,7 @@ MODES = ["fused", "fused_valu", "prepacked", "materialized"]
 
 
 CONV_KERNELS = ("conv_f32_mfma_kernel", "conv_f32_kernel", "conv_f16_fused_kernel",
-                "conv_f16_kernel")
+                "conv_f16_rows_kernel", "conv_f16_kernel")
 
 
 def log(msg):
@@ -223,10 +224,13 @@ ABLATION = {
             ("vector ALU", "fused", {"IM2WIN_F32_PATH": "valu"}),
             ("materialised im2win tensor", "materialized", {})],
     "f16": [("fused, filter gathered in-kernel", "fused", {}),
-            ("fused, filter prepacked", "prepacked", {}),
-            ("prepacked, 8 waves along pixels", "prepacked", {"IM2WIN_F16_WPX": "8"}),
-            ("prepacked, >= 2 filter parts per channel group", "prepacked", {"IM2WIN_F16_NWH": "2"}),
-            ("prepacked, >= 3 filter parts per channel group", "prepacked", {"IM2WIN_F16_NWH": "3"}),
+            ("fused, filter prepacked (planner's kernel)", "prepacked", {}),
+            ("prepacked, row-staged kernel with 4 waves", "prepacked", {"IM2WIN_F16_ROWS_NWV": "4"}),
+            ("prepacked, channel-interleaved kernel", "prepacked", {"IM2WIN_F16_ROWS": "0"}),
+            ("channel-interleaved, 8 waves along pixels", "prepacked",
+             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_WPX": "8"}),
+            ("channel-interleaved, >= 2 filter parts per group", "prepacked",
+             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_NWH": "2"}),
             ("materialised im2win tensor", "materialized", {})],
 }
 
@@ -354,8 +358,14 @@ def main():
     achieved = head["flops"] / (head["ms_per_launch_avg"] * 1e-3) / 1e12
     peak = (PEAK_FP32_VECTOR_TFLOPS if valu else PEAK_FP32_MFMA_TFLOPS) if is_f32 \
         else PEAK_FP16_MFMA_TFLOPS
+    # With a prepacked filter the library runs the row-staged fp16 kernel on
+    # shapes with an even column stride, Wf <= 8, Wi % 8 == 0 and even Ci.
+    sw = sh.s[1] if isinstance(sh.s, tuple) else sh.s
+    rows = (args.mode == "prepacked" and sh.Wf <= 8 and sw % 2 == 0 and sh.Wi % 8 == 0
+            and sh.Ci % 2 == 0)
     kernel = ("conv_f32_kernel" if valu else "conv_f32_mfma_kernel") if is_f32 else \
-        ("conv_f16_kernel" if args.mode == "materialized" else "conv_f16_fused_kernel")
+        ("conv_f16_kernel" if args.mode == "materialized" else
+         "conv_f16_rows_kernel" if rows else "conv_f16_fused_kernel")
     roofline = {
         "bound": "alu" if valu else "mfma",
         "achieved": round(achieved, 3),
