@@ -226,6 +226,8 @@ ABLATION = {
     "f16": [("fused, filter gathered in-kernel", "fused", {}),
             ("fused, filter prepacked (planner's kernel)", "prepacked", {}),
             ("prepacked, row-staged kernel with 4 waves", "prepacked", {"IM2WIN_F16_ROWS_NWV": "4"}),
+            ("prepacked, row-staged, tiles in launch order", "prepacked",
+             {"IM2WIN_F16_ROWS_SWIZZLE": "0"}),
             ("prepacked, channel-interleaved kernel", "prepacked", {"IM2WIN_F16_ROWS": "0"}),
             ("channel-interleaved, 8 waves along pixels", "prepacked",
              {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_WPX": "8"}),

@@ -62,6 +62,7 @@ struct RowsArgs {
     uint32_t lds_bytes;
     uint32_t xbytes, ybytes, wbytes;
     uint32_t mask[4];               // B dwords: halves kw >= Wf cleared
+    bool swz;                       // XCD-grouped tile order
     FastDiv divWo, divHo;
 };
 
@@ -129,8 +130,17 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
     const int sh = a.c.sh, sw = a.c.sw;
     const int Ho = a.c.Ho, Wo = a.c.Wo, Hf = a.c.Hf;
 
-    const int co_t = (int)(blockIdx.x % a.co_tiles);
-    const int64_t pt = blockIdx.x / a.co_tiles;
+    // Workgroups are handed to the 8 XCDs in turn (block b on XCD b % 8).
+    // With swz, XCD x takes the contiguous tiles [x*G8, (x+1)*G8), so tiles
+    // that share halo input rows share that XCD's L2; the last partial round
+    // keeps launch order.
+    int64_t bid = blockIdx.x;
+    if (a.swz) {
+        const int64_t G8 = (int64_t)gridDim.x / 8;
+        if (bid < 8 * G8) bid = (bid % 8) * G8 + bid / 8;
+    }
+    const int co_t = (int)(bid % a.co_tiles);
+    const int64_t pt = bid / a.co_tiles;
     const int co0 = co_t * kCoT;
     int64_t q0, qend;
     if (a.aligned) {   // tile pt = (image, tile within the image)
@@ -355,8 +365,9 @@ constexpr int kDmax[] = {4, 5, 6, 8, 12, 16};
 // Plans a launch; false if the shape is outside the kernel's envelope:
 // even column stride, Wf <= 8, Wi a multiple of 8 (16-byte row chunks),
 // Ci a multiple of the stage's channel count, tensors addressable with
-// 32-bit buffer offsets. IM2WIN_F16_ROWS=0 turns the kernel off and
-// IM2WIN_F16_ROWS_NWV picks the waves per workgroup (tuning and tests).
+// 32-bit buffer offsets. IM2WIN_F16_ROWS=0 turns the kernel off,
+// IM2WIN_F16_ROWS_NWV picks the waves per workgroup and
+// IM2WIN_F16_ROWS_SWIZZLE=0 keeps tiles in launch order (tuning and tests).
 bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax)
 {
     if (env_int("IM2WIN_F16_ROWS", 1) == 0) return false;
@@ -431,6 +442,7 @@ bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax)
     }
     a.divWo = FastDiv((uint32_t)c.Wo);
     a.divHo = FastDiv((uint32_t)c.Ho);
+    a.swz = env_int("IM2WIN_F16_ROWS_SWIZZLE", 1) != 0;
     return true;
 }
 

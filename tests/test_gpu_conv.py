@@ -317,3 +317,15 @@ def test_conv_f16_row_staged_special_values(t, orc):
     _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
                               with_absdot=True)
     assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
+
+
+@pytest.mark.parametrize("swz", ["1", "0"])
+@pytest.mark.parametrize("t", [(11, 2, 65, 64, 40, 3, 3, 2), (40, 4, 21, 32, 70, 5, 5, 2)], ids=str)
+def test_conv_f16_row_staged_tile_order(t, swz, orc, monkeypatch):
+    """XCD-grouped and launch-order tiling give the same (exact) results,
+    with grids that are not a multiple of the 8 XCDs (partial last round)."""
+    monkeypatch.setenv("IM2WIN_F16_ROWS_SWIZZLE", swz)
+    sh = _shape(t, "f16")
+    xi, wi = workloads.make_inputs(sh, seed=43, mode="int")
+    note(f"conv fp16 row-staged swizzle={swz} {sh.describe()}")
+    assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
