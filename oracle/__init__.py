@@ -57,6 +57,8 @@ class Oracle:
             f.restype = _i64
         L.oracle_im2win_pack.argtypes = [_p, _p] + [_i] * 9
         L.oracle_im2win_pack.restype = None
+        L.oracle_im2col_pack.argtypes = [_p, _p] + [_i] * 10
+        L.oracle_im2col_pack.restype = None
         L.oracle_conv_direct_f64.argtypes = [_p, _p, _p, _p] + [_i] * 9
         L.oracle_conv_direct_f32acc.argtypes = [_p, _p, _p] + [_i] * 9
         L.oracle_conv_im2win_f64.argtypes = [_p, _p, _p] + [_i] * 9
@@ -101,6 +103,24 @@ class Oracle:
         self.L.oracle_im2win_pack(_ptr(x), _ptr(ws), N, Ci, Hi, Wi, Hf, Wf, *strides(s),
                                   x.dtype.itemsize)
         return ws
+
+    def im2col_pack(self, x: np.ndarray, Hf: int, Wf: int, s, KP: int | None = None) -> np.ndarray:
+        """Bit copy of x (N, Ci, Hi, Wi) into the im2col matrix (N*Ho*Wo, KP):
+        each row one output pixel's receptive field in (ci, kh, kw) order, then
+        zeros (KP defaults to Ci*Hf*Wf)."""
+        x = np.ascontiguousarray(x)
+        N, Ci, Hi, Wi = x.shape
+        Ho, Wo = self.out_hw(Hi, Wi, Hf, Wf, s)
+        if Ho == 0 or Wo == 0:
+            raise ValueError("filter larger than input")
+        K = Ci * Hf * Wf
+        KP = K if KP is None else KP
+        if KP < K:
+            raise ValueError("row pitch below Ci*Hf*Wf")
+        col = np.empty((N * Ho * Wo, KP), dtype=x.dtype)
+        self.L.oracle_im2col_pack(_ptr(x), _ptr(col), N, Ci, Hi, Wi, Hf, Wf, *strides(s), KP,
+                                  x.dtype.itemsize)
+        return col
 
     # ---- convolution -----------------------------------------------------
     def _dims(self, x, w, s):

@@ -101,6 +101,41 @@ void oracle_im2win_pack(const void *x, void *ws, int N, int Ci, int Hi, int Wi,
                     }
 }
 
+/*
+ * The im2col transform (the unfolding the GEMM-based baseline of the GPU page,
+ * Fig. 1 right, multiplies): one row per output pixel q = (n*Ho + ho)*Wo + wo
+ * holding its receptive field in (ci, kh, kw) order, K = Ci*Hf*Wf elements,
+ * then zeros up to the row pitch KP >= K:
+ *   col[q][(ci*Hf + kh)*Wf + kw] = x[n][ci][ho*sh + kh][wo*sw + kw]
+ * A bit copy of elem_bytes-wide elements.
+ */
+void oracle_im2col_pack(const void *x, void *col, int N, int Ci, int Hi, int Wi, int Hf, int Wf,
+                        int sh, int sw, int KP, int elem_bytes)
+{
+    const unsigned char *src = (const unsigned char *)x;
+    unsigned char *dst = (unsigned char *)col;
+    int Ho = oracle_out_extent(Hi, Hf, sh);
+    int Wo = oracle_out_extent(Wi, Wf, sw);
+    int64_t K = (int64_t)Ci * Hf * Wf;
+    if (Ho == 0 || Wo == 0 || KP < K)
+        return;
+    for (int n = 0; n < N; ++n)
+        for (int ho = 0; ho < Ho; ++ho)
+            for (int wo = 0; wo < Wo; ++wo) {
+                int64_t q = ((int64_t)n * Ho + ho) * Wo + wo;
+                unsigned char *row = dst + q * KP * elem_bytes;
+                memset(row, 0, (size_t)KP * elem_bytes);
+                for (int ci = 0; ci < Ci; ++ci)
+                    for (int kh = 0; kh < Hf; ++kh)
+                        for (int kw = 0; kw < Wf; ++kw) {
+                            int64_t k = ((int64_t)ci * Hf + kh) * Wf + kw;
+                            int64_t in = (((int64_t)n * Ci + ci) * Hi + (int64_t)ho * sh + kh) * Wi +
+                                         (int64_t)wo * sw + kw;
+                            memcpy(row + k * elem_bytes, src + in * elem_bytes, (size_t)elem_bytes);
+                        }
+            }
+}
+
 /* Index helpers for the NCHW tensors. */
 static inline int64_t xi(int n, int ci, int h, int w, int Ci, int Hi, int Wi)
 {

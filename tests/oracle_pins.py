@@ -272,6 +272,31 @@ def pin_pack_is_bit_copy(O):
         assert np.array_equal(ws.view(np.uint8), ref.view(np.uint8))
 
 
+def pin_im2col_rows_are_windows(O):
+    """Each im2col row is one output pixel's receptive field x[n, :, ho*sh:+Hf,
+    wo*sw:+Wf] flattened in (ci, kh, kw) order (numpy slicing), then zeros;
+    and the im2col matrix times the flattened filters is the convolution."""
+    for k, cfg in enumerate(SWEEP):
+        N, Ci, Hi, Wi, Co, Hf, Wf, s = cfg
+        sh, sw = _st(s)
+        x, w = _case(cfg, 1000 + k, integer=True)
+        K = Ci * Hf * Wf
+        col = O.im2col_pack(x, Hf, Wf, s, KP=K + 3)
+        Ho, Wo = O.out_hw(Hi, Wi, Hf, Wf, s)
+        assert col.shape == (N * Ho * Wo, K + 3)
+        assert not col[:, K:].any()
+        q = 0
+        for n in range(N):
+            for ho in range(Ho):
+                for wo in range(Wo):
+                    win = x[n, :, ho * sh: ho * sh + Hf, wo * sw: wo * sw + Wf].reshape(-1)
+                    assert np.array_equal(col[q, :K], win), (cfg, q)
+                    q += 1
+        y = (col[:, :K].astype(np.float64) @ w.reshape(Co, K).astype(np.float64).T)
+        y = y.reshape(N, Ho, Wo, Co).transpose(0, 3, 1, 2)
+        assert np.array_equal(y, O.conv_direct(x, w, s)), cfg
+
+
 def pin_im2win_conv_equals_direct(O):
     """Convolving the packed tensor gives bit-identical results to the direct
     loops (same terms, same order), in fp64 and with a float accumulator."""

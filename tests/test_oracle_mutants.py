@@ -64,6 +64,12 @@ MUTANTS = [
     ("output written with rows and columns transposed",
      "int64_t o = (((int64_t)n * Co + co) * Ho + ho) * Wo + wo;",
      "int64_t o = (((int64_t)n * Co + co) * Wo + wo) * Ho + ho;"),
+    ("im2col row holds the window in (ci, kw, kh) order",
+     "int64_t k = ((int64_t)ci * Hf + kh) * Wf + kw;",
+     "int64_t k = ((int64_t)ci * Wf + kw) * Hf + kh;"),
+    ("im2col source column ignores the column stride",
+     "(int64_t)wo * sw + kw;\n                            memcpy(row",
+     "(int64_t)wo + kw;\n                            memcpy(row"),
     ("float-accumulator im2win path multiplies the transposed filter tap",
      "acc += win[kw * Hf + kh] * w[wi(co, ci, kh, kw, Ci, Hf, Wf)];",
      "acc += win[kw * Hf + kh] * w[wi(co, ci, kw, kh, Ci, Hf, Wf)];"),
