@@ -89,12 +89,24 @@ def time_layer(sh, mode, steps, warmup):
     y = torch.empty((sh.N, sh.Co, Ho, Wo), dtype=torch.float32, device=dev)
     ws = None
     wsb = 0
-    if mode != "fused":
+    if mode == "im2col":
+        wsb = m.im2col_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
+                                       sh.elem_bytes)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    elif mode != "fused" and mode != "direct":
         wsb = m.conv_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
                                      sh.elem_bytes, mode == "materialized")
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+
+    def call():
+        if mode == "im2col":
+            m.conv2d_im2col(xt, wt, sh.s, ws=ws, out=y)
+        elif mode == "direct":
+            m.conv2d_direct(xt, wt, sh.s, out=y)
+        else:
+            m.conv2d(xt, wt, sh.s, ws=ws, out=y)
     for _ in range(warmup):
-        m.conv2d(xt, wt, sh.s, ws=ws, out=y)
+        call()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -104,7 +116,7 @@ def time_layer(sh, mode, steps, warmup):
     t_all0.record()
     for i in range(steps):
         starts[i].record()
-        m.conv2d(xt, wt, sh.s, ws=ws, out=y)
+        call()
         ends[i].record()
     t_all1.record()
     torch.cuda.synchronize()
@@ -185,6 +197,41 @@ def _read_csv(path):
     import csv
     with open(path, newline="") as f:
         return list(csv.DictReader(f))
+
+
+def baselines(sh, entry):
+    """Times the im2col + GEMM and direct-convolution baselines on a layer and
+    adds them, and the im2win/im2col ratios, to its entry. Memory is the bytes
+    a call touches in HBM: x + w + y + workspace."""
+    peak = PEAK_FP32_MFMA_TFLOPS if sh.dtype == "f32" else PEAK_FP16_MFMA_TFLOPS
+    for mode in ("im2col", "direct"):
+        r = time_layer(sh, mode, 3, 1)
+        entry[mode] = {"tflops": round(r["tflops"], 3), "us_per_call": round(r["ms_per_step"] * 1e3, 2),
+                       "frac_of_peak": round(r["tflops"] / peak, 4),
+                       "workspace_bytes": r["workspace_bytes"]}
+        log(f"[bench] {sh.name} baseline {mode}: {r['tflops']:.2f} TFLOP/s "
+            f"({r['ms_per_step']*1e3:.1f} us/call, ws {r['workspace_bytes']} B)")
+    Ho = (sh.Hi - sh.Hf) // workloads_stride(sh)[0] + 1
+    Wo = (sh.Wi - sh.Wf) // workloads_stride(sh)[1] + 1
+    base = (sh.N * sh.Ci * sh.Hi * sh.Wi + sh.Co * sh.Ci * sh.Hf * sh.Wf) * sh.elem_bytes + \
+        sh.N * sh.Co * Ho * Wo * 4
+    im2win_modes = [k for k in ("fused", "prepacked", "materialized") if k in entry]
+    best = max(im2win_modes, key=lambda k: entry[k]["tflops"])
+    col = base + entry["im2col"]["workspace_bytes"]
+    entry["vs_baselines"] = {
+        "best_im2win_mode": best,
+        "tflops_vs_im2col": round(entry[best]["tflops"] / entry["im2col"]["tflops"], 3),
+        "tflops_vs_direct": round(entry[best]["tflops"] / entry["direct"]["tflops"], 3),
+        "memory_vs_im2col_best_mode": round((base + entry[best]["workspace_bytes"]) / col, 4),
+        "memory_vs_im2col_materialized": round((base + entry["materialized"]["workspace_bytes"]) / col, 4),
+    }
+    log(f"[bench] {sh.name} im2win {best} vs im2col: {entry['vs_baselines']['tflops_vs_im2col']}x TFLOP/s, "
+        f"memory {entry['vs_baselines']['memory_vs_im2col_best_mode']:.3f} "
+        f"(materialised im2win {entry['vs_baselines']['memory_vs_im2col_materialized']:.3f})")
+
+
+def workloads_stride(sh):
+    return sh.s if isinstance(sh.s, tuple) else (sh.s, sh.s)
 
 
 def ingest_pmc(fetch_csv, write_csv, copy_bytes=1 << 30):
@@ -279,6 +326,8 @@ def main():
                          "workspace; materialized: im2win tensor in HBM")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-layers", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-baselines", action="store_true",
+                    help="skip the im2col + GEMM and direct-convolution baselines per layer")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for scaling rocprofv3 HBM counters)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -350,6 +399,8 @@ def main():
                                "workspace_bytes": r["workspace_bytes"]}
                 log(f"[bench] {key} {mode}: {r['tflops']:.2f} TFLOP/s "
                     f"({r['ms_per_step']*1e3:.1f} us/call, ws {r['workspace_bytes']} B)")
+            if not args.no_baselines:
+                baselines(lsh, entry)
             layers[key] = entry
 
     # Roofline of the dominant kernel. For the headline (cv1, fused) one call

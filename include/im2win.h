@@ -158,6 +158,44 @@ int conv2d_im2win_fp16_strided(const uint16_t *x, const uint16_t *w, float *y, v
                                size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf,
                                int Wf, int sh, int sw, void *stream);
 
+/*
+ * Baselines the pages compare im2win against, built here on the same
+ * hardware paths (they carry the row and column strides directly):
+ *
+ * im2col + GEMM ("Enabling Memory-efficient Im2win Convolution ...", Fig. 1
+ * right; Abstract: GEMM-based convolution). The im2col matrix holds, for every
+ * output pixel q = (n*Ho + ho)*Wo + wo, its receptive field as one row of
+ * K = Ci*Hf*Wf elements in (ci, kh, kw) order, zero-padded to KP elements
+ * (K rounded up to 32 bytes):
+ *     col[q][(ci*Hf + kh)*Wf + kw] = x[n][ci][ho*sh + kh][wo*sw + kw]
+ * (the transpose of the K x P layout, same size). im2col_pack writes it for N
+ * images (N*Ho*Wo*KP elements; elem_bytes 2 or 4, bit copy).
+ * conv2d_im2col_workspace_bytes: bytes for the whole batch, laid out as
+ * [filter padded to KP per channel, rounded up to 256 bytes | im2col rows].
+ * conv2d_im2col_fp32 / _fp16: the convolution as im2col then a matrix-core
+ * GEMM (same MFMA instructions and accumulation as the im2win kernels); ws
+ * is required (16-byte aligned) and must hold the padded filter and at least
+ * one image's rows; the batch is processed in chunks of as many images as
+ * fit. Smaller: IM2WIN_EWORKSPACE. Results as conv2d_im2win_fp32 / _fp16
+ * (fp32 output; only the summation order differs).
+ *
+ * conv2d_direct_fp32 / _fp16: direct convolution, one thread per output,
+ * reading x and w in place (no workspace).
+ */
+size_t conv2d_im2col_workspace_bytes(int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh,
+                                     int sw, size_t elem_bytes);
+int im2col_pack(const void *x, void *col, int N, int Ci, int Hi, int Wi, int Hf, int Wf, int sh,
+                int sw, size_t elem_bytes, void *stream);
+int conv2d_im2col_fp32(const float *x, const float *w, float *y, void *ws, size_t ws_bytes, int N,
+                       int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw, void *stream);
+int conv2d_im2col_fp16(const uint16_t *x, const uint16_t *w, float *y, void *ws, size_t ws_bytes,
+                       int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw,
+                       void *stream);
+int conv2d_direct_fp32(const float *x, const float *w, float *y, int N, int Ci, int Hi, int Wi,
+                       int Co, int Hf, int Wf, int sh, int sw, void *stream);
+int conv2d_direct_fp16(const uint16_t *x, const uint16_t *w, float *y, int N, int Ci, int Hi,
+                       int Wi, int Co, int Hf, int Wf, int sh, int sw, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *im2win_status_string(int status);
 

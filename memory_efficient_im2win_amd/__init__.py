@@ -21,6 +21,7 @@ from . import _lib
 from ._lib import Im2winError, status_string  # noqa: F401
 
 __all__ = ["conv2d", "pack", "workspace_bytes", "conv_workspace_bytes", "output_dims", "strides",
+           "im2col", "im2col_workspace_bytes", "conv2d_im2col", "conv2d_direct",
            "Im2winError", "status_string", "load_library"]
 
 
@@ -149,4 +150,75 @@ def conv2d(x, w, stride=1, ws=None, ws_bytes: int | None = None, out=None):
     _lib.check(fn(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
                   ctypes.c_void_p(out.data_ptr()), ws_ptr, nbytes,
                   N, Ci, Hi, Wi, Co, Hf, Wf, *st, _stream_handle(x)), fn.__name__)
+    return out
+
+
+# ---- baselines: im2col + GEMM and direct convolution ------------------------
+def im2col_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s, elem_bytes) -> int:
+    """Workspace of conv2d_im2col for the whole batch (padded filter + im2col
+    rows); 0 for an invalid shape."""
+    sh, sw = strides(s)
+    return _lib.load().conv2d_im2col_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, elem_bytes)
+
+
+def im2col(x, Hf: int, Wf: int, s):
+    """The im2col matrix of x (N, Ci, Hi, Wi): (N*Ho*Wo, KP) rows of
+    Ci*Hf*Wf elements in (ci, kh, kw) order, zero-padded to 32 bytes."""
+    torch = _torch()
+    _check_tensor(x, "x", (torch.float16, torch.float32, torch.int16, torch.int32,
+                           torch.bfloat16, torch.uint16, torch.uint32), 4)
+    N, Ci, Hi, Wi = x.shape
+    Ho, Wo = output_dims(Hi, Wi, Hf, Wf, s)
+    e = x.element_size()
+    K = Ci * Hf * Wf
+    KP = -(-K // (32 // e)) * (32 // e)
+    out = torch.empty((N * Ho * Wo, KP), dtype=x.dtype, device=x.device)
+    sh, sw = strides(s)
+    _lib.check(_lib.load().im2col_pack(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                       N, Ci, Hi, Wi, Hf, Wf, sh, sw, e, _stream_handle(x)),
+               "im2col_pack")
+    return out
+
+
+def _conv_args(x, w, stride, out=None):
+    torch = _torch()
+    _check_tensor(x, "x", (torch.float32, torch.float16), 4)
+    _check_tensor(w, "w", (x.dtype,), 4)
+    if w.device != x.device:
+        raise ValueError("x and w must be on the same device")
+    N, Ci, Hi, Wi = x.shape
+    Co, Ci2, Hf, Wf = w.shape
+    if Ci2 != Ci:
+        raise ValueError("x and w disagree on the input channel count")
+    Ho, Wo = output_dims(Hi, Wi, Hf, Wf, stride)
+    if out is None:
+        out = torch.empty((N, Co, Ho, Wo), dtype=torch.float32, device=x.device)
+    elif (tuple(out.shape) != (N, Co, Ho, Wo) or out.dtype != torch.float32
+          or not out.is_contiguous() or out.device != x.device):
+        raise ValueError("out has the wrong shape, dtype, device or layout")
+    return (N, Ci, Hi, Wi, Co, Hf, Wf) + strides(stride), out
+
+
+def conv2d_im2col(x, w, stride=1, ws=None, out=None):
+    """Baseline: im2col into the workspace, then a matrix-core GEMM (fp32
+    output). ws defaults to the whole batch's im2col_workspace_bytes."""
+    torch = _torch()
+    dims, out = _conv_args(x, w, stride, out)
+    if ws is None:
+        nb = _lib.load().conv2d_im2col_workspace_bytes(*dims, x.element_size())
+        ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    fn = _lib.load().conv2d_im2col_fp32 if x.dtype == torch.float32 else _lib.load().conv2d_im2col_fp16
+    _lib.check(fn(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                  ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                  ws.numel() * ws.element_size(), *dims, _stream_handle(x)), fn.__name__)
+    return out
+
+
+def conv2d_direct(x, w, stride=1, out=None):
+    """Baseline: direct convolution, one thread per output (fp32 output)."""
+    torch = _torch()
+    dims, out = _conv_args(x, w, stride, out)
+    fn = _lib.load().conv2d_direct_fp32 if x.dtype == torch.float32 else _lib.load().conv2d_direct_fp16
+    _lib.check(fn(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                  ctypes.c_void_p(out.data_ptr()), *dims, _stream_handle(x)), fn.__name__)
     return out

@@ -35,6 +35,12 @@ EXPORTS = {
     "conv2d_im2win_workspace_bytes_strided": ([_i] * 10 + [_sz], _sz),
     "im2win_status_string": ([_i], ctypes.c_char_p),
     "im2win_last_error": ([], ctypes.c_char_p),
+    "conv2d_im2col_workspace_bytes": ([_i] * 9 + [_sz], _sz),
+    "im2col_pack": ([_p, _p] + [_i] * 8 + [_sz, _p], _i),
+    "conv2d_im2col_fp32": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
+    "conv2d_im2col_fp16": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
+    "conv2d_direct_fp32": ([_p, _p, _p] + [_i] * 9 + [_p], _i),
+    "conv2d_direct_fp16": ([_p, _p, _p] + [_i] * 9 + [_p], _i),
 }
 
 _lib = None

@@ -153,6 +153,67 @@ int f16_generic(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float*
     return im2win::launch_conv_generic_f16(x, ws, w, y, c, st);
 }
 
+// im2col baseline workspace: [padded filter, rounded up to 256 bytes | im2col
+// rows of a chunk of images].
+struct ColPlan {
+    size_t fbytes;     // padded filter bytes (aligned)
+    size_t per_image;  // im2col bytes of one image
+};
+
+ColPlan col_plan(const ConvShape& c, size_t elem)
+{
+    const size_t kp = im2win::im2col_row_elems(c, (int)elem);
+    return ColPlan{align_up((size_t)c.Co * kp * elem), (size_t)c.Ho * c.Wo * kp * elem};
+}
+
+template <typename T>
+int im2col_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int N, int Ci,
+                  int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw, hipStream_t stream)
+{
+    int Ho, Wo;
+    if (!x || !w || !y) return IM2WIN_EINVAL;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return IM2WIN_EINVAL;
+    if (!aligned(x, sizeof(T)) || !aligned(w, sizeof(T)) || !aligned(y, sizeof(float)))
+        return IM2WIN_EINVAL;
+    const ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo};
+    const ColPlan p = col_plan(c, sizeof(T));
+    if (ws == nullptr || ws_bytes < p.fbytes + p.per_image) return IM2WIN_EWORKSPACE;
+    if (!aligned(ws, 16)) return IM2WIN_EINVAL;
+    unsigned char* wsb = static_cast<unsigned char*>(ws);
+    const int64_t x_img = (int64_t)Ci * Hi * Wi, y_img = (int64_t)Co * Ho * Wo;
+    // A launch addresses its rows and outputs with 32-bit offsets: below 4 GiB each.
+    const size_t lim = 0xFFFFFFF0u;
+    size_t cap = std::min<size_t>((size_t)N, (ws_bytes - p.fbytes) / p.per_image);
+    cap = std::min(cap, (lim - 1) / p.per_image);
+    cap = std::min(cap, (lim - 1) / ((size_t)y_img * 4));
+    if (cap < 1) return IM2WIN_EINVAL;
+    const int chunk = (int)cap;
+    for (int n0 = 0; n0 < N; n0 += chunk) {
+        ConvShape cc = c;
+        cc.N = std::min(chunk, N - n0);
+        int rc = im2win::launch_im2col(x + n0 * x_img, wsb + p.fbytes, cc, (int)sizeof(T), stream);
+        if (rc != 0) return status_of(rc);
+        rc = im2win::launch_im2col_gemm(wsb + p.fbytes, w, wsb, y + n0 * y_img, cc, (int)sizeof(T),
+                                        stream);
+        if (rc != 0) return status_of(rc);
+    }
+    return IM2WIN_OK;
+}
+
+template <typename T>
+int direct_driver(const T* x, const T* w, float* y, int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                  int Wf, int sh, int sw, hipStream_t stream,
+                  int (*generic)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t))
+{
+    int Ho, Wo;
+    if (!x || !w || !y) return IM2WIN_EINVAL;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return IM2WIN_EINVAL;
+    if (!aligned(x, sizeof(T)) || !aligned(w, sizeof(T)) || !aligned(y, sizeof(float)))
+        return IM2WIN_EINVAL;
+    return status_of(generic(x, nullptr, w, y, ConvShape{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo},
+                             stream));
+}
+
 }  // namespace
 
 namespace im2win {
@@ -257,6 +318,57 @@ int conv2d_im2win_fp16(const uint16_t* x, const uint16_t* w, float* y, void* ws,
 {
     return conv2d_im2win_fp16_strided(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, s, s,
                                       stream);
+}
+
+size_t conv2d_im2col_workspace_bytes(int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh,
+                                     int sw, size_t elem_bytes)
+{
+    int Ho, Wo;
+    if (elem_bytes != 2 && elem_bytes != 4) return 0;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return 0;
+    const ColPlan p = col_plan(ConvShape{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo}, elem_bytes);
+    return p.fbytes + (size_t)N * p.per_image;
+}
+
+int im2col_pack(const void* x, void* col, int N, int Ci, int Hi, int Wi, int Hf, int Wf, int sh,
+                int sw, size_t elem_bytes, void* stream)
+{
+    int Ho, Wo;
+    if (!x || !col) return IM2WIN_EINVAL;
+    if (elem_bytes != 2 && elem_bytes != 4) return IM2WIN_EINVAL;
+    if (!check_shape(N, Ci, Hi, Wi, 1, Hf, Wf, sh, sw, &Ho, &Wo)) return IM2WIN_EINVAL;
+    if (!aligned(x, elem_bytes) || !aligned(col, elem_bytes)) return IM2WIN_EINVAL;
+    return status_of(im2win::launch_im2col(x, col, ConvShape{N, Ci, Hi, Wi, 1, Hf, Wf, sh, sw, Ho, Wo},
+                                           (int)elem_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int conv2d_im2col_fp32(const float* x, const float* w, float* y, void* ws, size_t ws_bytes, int N,
+                       int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw, void* stream)
+{
+    return im2col_driver<float>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
+                                static_cast<hipStream_t>(stream));
+}
+
+int conv2d_im2col_fp16(const uint16_t* x, const uint16_t* w, float* y, void* ws, size_t ws_bytes,
+                       int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw,
+                       void* stream)
+{
+    return im2col_driver<uint16_t>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
+                                   static_cast<hipStream_t>(stream));
+}
+
+int conv2d_direct_fp32(const float* x, const float* w, float* y, int N, int Ci, int Hi, int Wi,
+                       int Co, int Hf, int Wf, int sh, int sw, void* stream)
+{
+    return direct_driver<float>(x, w, y, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
+                                static_cast<hipStream_t>(stream), f32_generic);
+}
+
+int conv2d_direct_fp16(const uint16_t* x, const uint16_t* w, float* y, int N, int Ci, int Hi,
+                       int Wi, int Co, int Hf, int Wf, int sh, int sw, void* stream)
+{
+    return direct_driver<uint16_t>(x, w, y, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
+                                   static_cast<hipStream_t>(stream), f16_generic);
 }
 
 const char* im2win_last_error(void)

@@ -59,6 +59,14 @@ int launch_f16_rows_filter_pack(const uint16_t* w, void* wp, const ConvShape& c,
 int launch_conv_f16_rows(const uint16_t* x, const void* wp, float* y, const ConvShape& c,
                          hipStream_t stream);
 
+// im2col + GEMM baseline: elements per im2col row (Ci*Hf*Wf padded to 32
+// bytes); the transform of N images into N*Ho*Wo rows; the GEMM over those
+// rows, after copying the filters into wpad (Co rows of the padded length).
+size_t im2col_row_elems(const ConvShape& c, int elem);
+int launch_im2col(const void* x, void* col, const ConvShape& c, int elem, hipStream_t stream);
+int launch_im2col_gemm(const void* col, const void* w, void* wpad, float* y, const ConvShape& c,
+                       int elem, hipStream_t stream);
+
 // Plain fallbacks (one thread per output) for shapes the tiled kernels do
 // not take; ws as above.
 int launch_conv_generic_f32(const float* x, const float* ws, const float* w, float* y,

@@ -16,14 +16,16 @@ HEADER = os.path.join(ROOT, "include", "im2win.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(im2win_\w+|conv2d_im2win_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(im2win_\w+|im2col_\w+|conv2d_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     single = ["im2win_workspace_bytes", "im2win_output_dims", "im2win_pack",
               "conv2d_im2win_fp32", "conv2d_im2win_fp16", "conv2d_im2win_workspace_bytes"]
     assert declared_functions() == sorted(
-        single + [f + "_strided" for f in single] + ["im2win_status_string", "im2win_last_error"])
+        single + [f + "_strided" for f in single] + ["im2win_status_string", "im2win_last_error"] +
+        ["conv2d_im2col_workspace_bytes", "im2col_pack", "conv2d_im2col_fp32", "conv2d_im2col_fp16",
+         "conv2d_direct_fp32", "conv2d_direct_fp16"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -214,3 +216,36 @@ def test_one_hip_runtime_when_the_library_loads_before_torch():
                        timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip().splitlines()[-1] == "1", r.stdout
+
+
+def test_im2col_workspace_bytes():
+    # [filter padded to KP, 256-byte aligned | N*Ho*Wo rows of KP]; K = Ci*Hf*Wf
+    # padded to 32 bytes. cv4 fp16: K = 3136 (already a multiple of 16).
+    fb = -(-64 * 3136 * 2 // 256) * 256
+    assert m.im2col_workspace_bytes(64, 64, 224, 224, 64, 7, 7, 2, 2) == fb + 64 * 109 * 109 * 3136 * 2
+    # cv1 fp32: K = 363 -> 368
+    fb = -(-96 * 368 * 4 // 256) * 256
+    assert m.im2col_workspace_bytes(32, 3, 227, 227, 96, 11, 11, 4, 4) == fb + 32 * 55 * 55 * 368 * 4
+    assert m.im2col_workspace_bytes(1, 3, 4, 4, 2, 5, 5, 1, 2) == 0
+    assert m.im2col_workspace_bytes(1, 3, 8, 8, 2, 3, 3, (2, 1), 3) == 0
+
+
+@pytest.mark.parametrize("fn", ["conv2d_im2col_fp32", "conv2d_im2col_fp16"])
+def test_im2col_conv_rejects_bad_arguments(fn):
+    L = m.load_library()
+    f = getattr(L, fn)
+    ok = (1, 3, 8, 8, 4, 3, 3, 1, 1)
+    assert f(None, FAKE, FAKE, FAKE, 1 << 20, *ok, None) == _lib.IM2WIN_EINVAL
+    assert f(FAKE, FAKE, FAKE, None, 0, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, 64, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, 1 << 20, 1, 3, 8, 8, 4, 3, 3, 0, 1, None) == _lib.IM2WIN_EINVAL
+    assert f(FAKE, FAKE, FAKE, ctypes.c_void_p(0x10008), 1 << 20, *ok, None) == _lib.IM2WIN_EINVAL
+
+
+def test_direct_and_im2col_pack_reject_bad_arguments():
+    L = m.load_library()
+    for f in (L.conv2d_direct_fp32, L.conv2d_direct_fp16):
+        assert f(None, FAKE, FAKE, 1, 3, 8, 8, 4, 3, 3, 1, 1, None) == _lib.IM2WIN_EINVAL
+        assert f(FAKE, FAKE, FAKE, 1, 3, 8, 8, 4, 9, 3, 1, 1, None) == _lib.IM2WIN_EINVAL
+    assert L.im2col_pack(FAKE, None, 1, 1, 4, 4, 2, 2, 1, 1, 4, None) == _lib.IM2WIN_EINVAL
+    assert L.im2col_pack(FAKE, FAKE, 1, 1, 4, 4, 2, 2, 1, 1, 8, None) == _lib.IM2WIN_EINVAL
