@@ -218,14 +218,20 @@ def baselines(sh, entry):
     im2win_modes = [k for k in ("fused", "prepacked", "materialized") if k in entry]
     best = max(im2win_modes, key=lambda k: entry[k]["tflops"])
     col = base + entry["im2col"]["workspace_bytes"]
+    # Whatever the GEMM, an im2col convolution writes and then reads its
+    # matrix: at the HBM peak that alone bounds its time from below.
+    col_bound_us = (base + 2 * entry["im2col"]["workspace_bytes"]) / (PEAK_HBM_GBS * 1e9) * 1e6
     entry["vs_baselines"] = {
         "best_im2win_mode": best,
         "tflops_vs_im2col": round(entry[best]["tflops"] / entry["im2col"]["tflops"], 3),
+        "im2col_hbm_bound_us": round(col_bound_us, 2),
+        "speed_vs_im2col_hbm_bound": round(col_bound_us / entry[best]["us_per_call"], 3),
         "tflops_vs_direct": round(entry[best]["tflops"] / entry["direct"]["tflops"], 3),
         "memory_vs_im2col_best_mode": round((base + entry[best]["workspace_bytes"]) / col, 4),
         "memory_vs_im2col_materialized": round((base + entry["materialized"]["workspace_bytes"]) / col, 4),
     }
-    log(f"[bench] {sh.name} im2win {best} vs im2col: {entry['vs_baselines']['tflops_vs_im2col']}x TFLOP/s, "
+    log(f"[bench] {sh.name} im2win {best} vs im2col: {entry['vs_baselines']['tflops_vs_im2col']}x TFLOP/s "
+        f"({entry['vs_baselines']['speed_vs_im2col_hbm_bound']}x its HBM bound), "
         f"memory {entry['vs_baselines']['memory_vs_im2col_best_mode']:.3f} "
         f"(materialised im2win {entry['vs_baselines']['memory_vs_im2col_materialized']:.3f})")
 
