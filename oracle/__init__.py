@@ -58,6 +58,8 @@ class Oracle:
         L.oracle_im2win_pack.argtypes = [_p, _p] + [_i] * 9
         L.oracle_im2win_pack.restype = None
         L.oracle_im2col_pack.argtypes = [_p, _p] + [_i] * 10
+        L.oracle_im2win_pack_nhwc.argtypes = [_p, _p] + [_i] * 9
+        L.oracle_im2win_pack_nhwc.restype = None
         L.oracle_im2col_pack.restype = None
         L.oracle_conv_direct_f64.argtypes = [_p, _p, _p, _p] + [_i] * 9
         L.oracle_conv_direct_f32acc.argtypes = [_p, _p, _p] + [_i] * 9
@@ -102,6 +104,19 @@ class Oracle:
         ws = np.empty((N, Ci, Ho, Wi * Hf), dtype=x.dtype)
         self.L.oracle_im2win_pack(_ptr(x), _ptr(ws), N, Ci, Hi, Wi, Hf, Wf, *strides(s),
                                   x.dtype.itemsize)
+        return ws
+
+    def im2win_pack_nhwc(self, x: np.ndarray, Hf: int, Wf: int, s) -> np.ndarray:
+        """Bit copy of an NHWC x (N, Hi, Wi, Ci) into the NHWC im2win tensor
+        (N, Ho, Wi, Hf, Ci): ws[n, ho, w, kh, c] = x[n, ho*sh + kh, w, c]."""
+        x = np.ascontiguousarray(x)
+        N, Hi, Wi, Ci = x.shape
+        Ho, Wo = self.out_hw(Hi, Wi, Hf, Wf, s)
+        if Ho == 0 or Wo == 0:
+            raise ValueError("filter larger than input")
+        ws = np.empty((N, Ho, Wi, Hf, Ci), dtype=x.dtype)
+        self.L.oracle_im2win_pack_nhwc(_ptr(x), _ptr(ws), N, Ci, Hi, Wi, Hf, Wf, *strides(s),
+                                       x.dtype.itemsize)
         return ws
 
     def im2col_pack(self, x: np.ndarray, Hf: int, Wf: int, s, KP: int | None = None) -> np.ndarray:

@@ -102,6 +102,33 @@ void oracle_im2win_pack(const void *x, void *ws, int N, int Ci, int Hi, int Wi,
 }
 
 /*
+ * The im2win transform for NHWC tensors (x is N x Hi x Wi x Ci): the same
+ * flattening of a row of windows, channels innermost:
+ *   ws[n][ho][w][kh][c] = x[n][ho*sh + kh][w][c]
+ * so the window of output (ho, wo) is the single contiguous run of
+ * Wf*Hf*Ci elements starting at wo*sw*Hf*Ci in row (n, ho); its element
+ * (kw*Hf + kh)*Ci + c is x[n][ho*sh + kh][wo*sw + kw][c]. A bit copy.
+ */
+void oracle_im2win_pack_nhwc(const void *x, void *ws, int N, int Ci, int Hi, int Wi, int Hf,
+                             int Wf, int sh, int sw, int elem_bytes)
+{
+    const unsigned char *src = (const unsigned char *)x;
+    unsigned char *dst = (unsigned char *)ws;
+    int Ho = oracle_out_extent(Hi, Hf, sh);
+    if (Ho == 0 || oracle_out_extent(Wi, Wf, sw) == 0)
+        return;
+    for (int n = 0; n < N; ++n)
+        for (int ho = 0; ho < Ho; ++ho)
+            for (int w = 0; w < Wi; ++w)
+                for (int kh = 0; kh < Hf; ++kh)
+                    for (int c = 0; c < Ci; ++c) {
+                        int64_t out = ((((int64_t)n * Ho + ho) * Wi + w) * Hf + kh) * Ci + c;
+                        int64_t in = (((int64_t)n * Hi + (int64_t)ho * sh + kh) * Wi + w) * Ci + c;
+                        memcpy(dst + out * elem_bytes, src + in * elem_bytes, (size_t)elem_bytes);
+                    }
+}
+
+/*
  * The im2col transform (the unfolding the GEMM-based baseline of the GPU page,
  * Fig. 1 right, multiplies): one row per output pixel q = (n*Ho + ho)*Wo + wo
  * holding its receptive field in (ci, kh, kw) order, K = Ci*Hf*Wf elements,

@@ -272,6 +272,38 @@ def pin_pack_is_bit_copy(O):
         assert np.array_equal(ws.view(np.uint8), ref.view(np.uint8))
 
 
+def pin_pack_nhwc_is_nchw_pack_permuted(O):
+    """The NHWC transform of x.transpose(0, 2, 3, 1) is the NCHW transform of x
+    with its axes permuted: ws_nhwc[n, ho, w, kh, c] = ws[n, c, ho, w*Hf + kh]."""
+    for k, cfg in enumerate(SWEEP):
+        N, Ci, Hi, Wi, Co, Hf, Wf, s = cfg
+        x, _ = _case(cfg, 1100 + k)
+        nchw = O.im2win_pack(x, Hf, Wf, s)
+        Ho = nchw.shape[2]
+        nhwc = O.im2win_pack_nhwc(np.ascontiguousarray(x.transpose(0, 2, 3, 1)), Hf, Wf, s)
+        assert nhwc.shape == (N, Ho, Wi, Hf, Ci)
+        assert np.array_equal(nhwc, nchw.reshape(N, Ci, Ho, Wi, Hf).transpose(0, 2, 3, 4, 1)), cfg
+
+
+def pin_pack_nhwc_windows_contiguous(O):
+    """NHWC: the window of output (ho, wo) is the contiguous run of Wf*Hf*Ci
+    elements at wo*sw*Hf*Ci in row (n, ho), ordered (kw, kh, c)."""
+    for k, cfg in enumerate(SWEEP):
+        N, Ci, Hi, Wi, Co, Hf, Wf, s = cfg
+        sh, sw = _st(s)
+        x, _ = _case(cfg, 1200 + k)
+        ws = O.im2win_pack_nhwc(np.ascontiguousarray(x.transpose(0, 2, 3, 1)), Hf, Wf, s)
+        Ho, Wo = O.out_hw(Hi, Wi, Hf, Wf, s)
+        L = Wf * Hf * Ci
+        for n in range(N):
+            for ho in range(Ho):
+                row = ws[n, ho].reshape(-1)
+                for wo in range(Wo):
+                    run = row[wo * sw * Hf * Ci: wo * sw * Hf * Ci + L].reshape(Wf, Hf, Ci)
+                    win = x[n, :, ho * sh: ho * sh + Hf, wo * sw: wo * sw + Wf]   # Ci, Hf, Wf
+                    assert np.array_equal(run.transpose(2, 1, 0), win), (cfg, n, ho, wo)
+
+
 def pin_im2col_rows_are_windows(O):
     """Each im2col row is one output pixel's receptive field x[n, :, ho*sh:+Hf,
     wo*sw:+Wf] flattened in (ci, kh, kw) order (numpy slicing), then zeros;

@@ -64,6 +64,12 @@ MUTANTS = [
     ("output written with rows and columns transposed",
      "int64_t o = (((int64_t)n * Co + co) * Ho + ho) * Wo + wo;",
      "int64_t o = (((int64_t)n * Co + co) * Wo + wo) * Ho + ho;"),
+    ("NHWC im2win row stored (kh, w) instead of (w, kh)",
+     "int64_t out = ((((int64_t)n * Ho + ho) * Wi + w) * Hf + kh) * Ci + c;",
+     "int64_t out = ((((int64_t)n * Ho + ho) * Hf + kh) * Wi + w) * Ci + c;"),
+    ("NHWC im2win source row ignores the row stride",
+     "int64_t in = (((int64_t)n * Hi + (int64_t)ho * sh + kh) * Wi + w) * Ci + c;",
+     "int64_t in = (((int64_t)n * Hi + (int64_t)ho + kh) * Wi + w) * Ci + c;"),
     ("im2col row holds the window in (ci, kw, kh) order",
      "int64_t k = ((int64_t)ci * Hf + kh) * Wf + kw;",
      "int64_t k = ((int64_t)ci * Wf + kw) * Hf + kh;"),
