@@ -83,13 +83,20 @@ def time_layer(sh, mode, steps, warmup):
     import memory_efficient_im2win_amd as m
     dev = torch.device("cuda:0")
     x, w = workloads.make_inputs(sh, seed=0)
+    if mode == "nhwc_materialized":
+        x = np.ascontiguousarray(x.transpose(0, 2, 3, 1))
     xt = torch.from_numpy(x).to(dev)
     wt = torch.from_numpy(w).to(dev)
     Ho, Wo = m.output_dims(sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s)
     y = torch.empty((sh.N, sh.Co, Ho, Wo), dtype=torch.float32, device=dev)
     ws = None
     wsb = 0
-    if mode == "im2col":
+    if mode == "nhwc_materialized":
+        y = torch.empty((sh.N, Ho, Wo, sh.Co), dtype=torch.float32, device=dev)
+        wsb = m.nhwc_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
+                                     sh.elem_bytes)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    elif mode == "im2col":
         wsb = m.im2col_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
                                        sh.elem_bytes)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
@@ -99,7 +106,9 @@ def time_layer(sh, mode, steps, warmup):
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
 
     def call():
-        if mode == "im2col":
+        if mode == "nhwc_materialized":
+            m.conv2d_nhwc(xt, wt, sh.s, ws=ws, out=y)
+        elif mode == "im2col":
             m.conv2d_im2col(xt, wt, sh.s, ws=ws, out=y)
         elif mode == "direct":
             m.conv2d_direct(xt, wt, sh.s, out=y)
@@ -200,16 +209,17 @@ def _read_csv(path):
 
 
 def baselines(sh, entry):
-    """Times the im2col + GEMM and direct-convolution baselines on a layer and
-    adds them, and the im2win/im2col ratios, to its entry. Memory is the bytes
-    a call touches in HBM: x + w + y + workspace."""
+    """Times the im2col + GEMM and direct-convolution baselines and the NHWC
+    materialised im2win mode on a layer and adds them, and the im2win/im2col
+    ratios, to its entry. Memory is the bytes a call touches in HBM:
+    x + w + y + workspace."""
     peak = PEAK_FP32_MFMA_TFLOPS if sh.dtype == "f32" else PEAK_FP16_MFMA_TFLOPS
-    for mode in ("im2col", "direct"):
+    for mode in ("im2col", "direct", "nhwc_materialized"):
         r = time_layer(sh, mode, 3, 1)
         entry[mode] = {"tflops": round(r["tflops"], 3), "us_per_call": round(r["ms_per_step"] * 1e3, 2),
                        "frac_of_peak": round(r["tflops"] / peak, 4),
                        "workspace_bytes": r["workspace_bytes"]}
-        log(f"[bench] {sh.name} baseline {mode}: {r['tflops']:.2f} TFLOP/s "
+        log(f"[bench] {sh.name} {mode}: {r['tflops']:.2f} TFLOP/s "
             f"({r['ms_per_step']*1e3:.1f} us/call, ws {r['workspace_bytes']} B)")
     Ho = (sh.Hi - sh.Hf) // workloads_stride(sh)[0] + 1
     Wo = (sh.Wi - sh.Wf) // workloads_stride(sh)[1] + 1
@@ -333,7 +343,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-layers", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-baselines", action="store_true",
-                    help="skip the im2col + GEMM and direct-convolution baselines per layer")
+                    help="skip the im2col + GEMM and direct-convolution baselines and the "
+                         "NHWC lines per layer")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for scaling rocprofv3 HBM counters)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),

@@ -196,6 +196,39 @@ int conv2d_direct_fp32(const float *x, const float *w, float *y, int N, int Ci, 
 int conv2d_direct_fp16(const uint16_t *x, const uint16_t *w, float *y, int N, int Ci, int Hi,
                        int Wi, int Co, int Hf, int Wf, int sh, int sw, void *stream);
 
+/*
+ * NHWC tensors: x is N x Hi x Wi x Ci, y is N x Ho x Wo x Co (fp32), w stays
+ * Co x Ci x Hf x Wf. The im2win transform keeps the channels innermost
+ * (the flattening of "Im2win: Memory Efficient Convolution On SIMD
+ * Architectures", Abstract, in this layout):
+ *     ws[n][ho][w][kh][c] = x[n][ho*sh + kh][w][c]
+ * so the window of output (ho, wo) is the one contiguous run of Wf*Hf*Ci
+ * elements at wo*sw*Hf*Ci in row (n, ho). Same size as the NCHW tensor
+ * (im2win_workspace_bytes_strided).
+ *
+ * im2win_pack_nhwc: that transform (bit copy, elem_bytes 2 or 4).
+ * conv2d_im2win_nhwc_workspace_bytes: 0 without materialize; with it, the
+ *     bytes of [filter in window order, rounded up to 256 | the NHWC im2win
+ *     tensor of the whole batch].
+ * conv2d_im2win_nhwc_fp32 / _fp16: ws == NULL and ws_bytes == 0: direct
+ *     convolution (one thread per output). ws (16-byte aligned) with at least
+ *     the filter part and one image's tensor: materialised; the tensor of as
+ *     many images as fit is packed and multiplied on the matrix cores, window
+ *     runs as GEMM rows, when Ci is a multiple of 16 (fp16) or 8 (fp32) and x
+ *     is 16-byte aligned; other shapes take the direct kernel. A workspace
+ *     given but too small: IM2WIN_EWORKSPACE.
+ */
+size_t conv2d_im2win_nhwc_workspace_bytes(int materialize, int N, int Ci, int Hi, int Wi, int Co,
+                                          int Hf, int Wf, int sh, int sw, size_t elem_bytes);
+int im2win_pack_nhwc(const void *x, void *ws, int N, int Ci, int Hi, int Wi, int Hf, int Wf,
+                     int sh, int sw, size_t elem_bytes, void *stream);
+int conv2d_im2win_nhwc_fp32(const float *x, const float *w, float *y, void *ws, size_t ws_bytes,
+                            int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw,
+                            void *stream);
+int conv2d_im2win_nhwc_fp16(const uint16_t *x, const uint16_t *w, float *y, void *ws,
+                            size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf,
+                            int sh, int sw, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *im2win_status_string(int status);
 

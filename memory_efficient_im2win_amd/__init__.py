@@ -22,6 +22,7 @@ from ._lib import Im2winError, status_string  # noqa: F401
 
 __all__ = ["conv2d", "pack", "workspace_bytes", "conv_workspace_bytes", "output_dims", "strides",
            "im2col", "im2col_workspace_bytes", "conv2d_im2col", "conv2d_direct",
+           "pack_nhwc", "conv2d_nhwc", "nhwc_workspace_bytes",
            "Im2winError", "status_string", "load_library"]
 
 
@@ -221,4 +222,63 @@ def conv2d_direct(x, w, stride=1, out=None):
     fn = _lib.load().conv2d_direct_fp32 if x.dtype == torch.float32 else _lib.load().conv2d_direct_fp16
     _lib.check(fn(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
                   ctypes.c_void_p(out.data_ptr()), *dims, _stream_handle(x)), fn.__name__)
+    return out
+
+
+# ---- NHWC tensors ------------------------------------------------------------
+def nhwc_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s, elem_bytes, materialize: bool = True) -> int:
+    """Workspace of conv2d_nhwc: 0 without materialize, else the filter in
+    window order plus the NHWC im2win tensor of the whole batch."""
+    sh, sw = strides(s)
+    return _lib.load().conv2d_im2win_nhwc_workspace_bytes(1 if materialize else 0, N, Ci, Hi, Wi, Co,
+                                                          Hf, Wf, sh, sw, elem_bytes)
+
+
+def pack_nhwc(x, Hf: int, Wf: int, s):
+    """The NHWC im2win tensor of x (N, Hi, Wi, Ci) as (N, Ho, Wi, Hf, Ci)."""
+    torch = _torch()
+    _check_tensor(x, "x", (torch.float16, torch.float32, torch.int16, torch.int32,
+                           torch.bfloat16, torch.uint16, torch.uint32), 4)
+    N, Hi, Wi, Ci = x.shape
+    Ho, _ = output_dims(Hi, Wi, Hf, Wf, s)
+    out = torch.empty((N, Ho, Wi, Hf, Ci), dtype=x.dtype, device=x.device)
+    sh, sw = strides(s)
+    _lib.check(_lib.load().im2win_pack_nhwc(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                            N, Ci, Hi, Wi, Hf, Wf, sh, sw, x.element_size(),
+                                            _stream_handle(x)), "im2win_pack_nhwc")
+    return out
+
+
+def conv2d_nhwc(x, w, stride=1, ws=None, out=None):
+    """Convolution of an NHWC x (N, Hi, Wi, Ci) with w (Co, Ci, Hf, Wf); fp32
+    NHWC output (N, Ho, Wo, Co). Without ws: direct; with ws (see
+    nhwc_workspace_bytes): the NHWC im2win tensor is materialised and
+    multiplied on the matrix cores."""
+    torch = _torch()
+    _check_tensor(x, "x", (torch.float32, torch.float16), 4)
+    _check_tensor(w, "w", (x.dtype,), 4)
+    if w.device != x.device:
+        raise ValueError("x and w must be on the same device")
+    N, Hi, Wi, Ci = x.shape
+    Co, Ci2, Hf, Wf = w.shape
+    if Ci2 != Ci:
+        raise ValueError("x and w disagree on the input channel count")
+    Ho, Wo = output_dims(Hi, Wi, Hf, Wf, stride)
+    if out is None:
+        out = torch.empty((N, Ho, Wo, Co), dtype=torch.float32, device=x.device)
+    elif (tuple(out.shape) != (N, Ho, Wo, Co) or out.dtype != torch.float32
+          or not out.is_contiguous() or out.device != x.device):
+        raise ValueError("out has the wrong shape, dtype, device or layout")
+    if ws is None:
+        ws_ptr, nbytes = None, 0
+    else:
+        if not ws.is_cuda or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous GPU tensor")
+        ws_ptr, nbytes = ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+    sh, sw = strides(stride)
+    fn = _lib.load().conv2d_im2win_nhwc_fp32 if x.dtype == torch.float32 else \
+        _lib.load().conv2d_im2win_nhwc_fp16
+    _lib.check(fn(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                  ctypes.c_void_p(out.data_ptr()), ws_ptr, nbytes, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
+                  _stream_handle(x)), fn.__name__)
     return out

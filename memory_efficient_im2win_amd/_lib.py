@@ -41,6 +41,10 @@ EXPORTS = {
     "conv2d_im2col_fp16": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
     "conv2d_direct_fp32": ([_p, _p, _p] + [_i] * 9 + [_p], _i),
     "conv2d_direct_fp16": ([_p, _p, _p] + [_i] * 9 + [_p], _i),
+    "conv2d_im2win_nhwc_workspace_bytes": ([_i] * 10 + [_sz], _sz),
+    "im2win_pack_nhwc": ([_p, _p] + [_i] * 8 + [_sz, _p], _i),
+    "conv2d_im2win_nhwc_fp32": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
+    "conv2d_im2win_nhwc_fp16": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
 }
 
 _lib = None

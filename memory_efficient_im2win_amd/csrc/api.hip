@@ -214,6 +214,57 @@ int direct_driver(const T* x, const T* w, float* y, int N, int Ci, int Hi, int W
                              stream));
 }
 
+// NHWC workspace: [filter in window order, rounded up to 256 bytes | NHWC
+// im2win tensor of a chunk of images].
+ColPlan nhwc_plan(const ConvShape& c, size_t elem)
+{
+    return ColPlan{align_up((size_t)c.Co * c.Ci * c.Hf * c.Wf * elem),
+                   (size_t)c.Ho * c.Wi * c.Hf * c.Ci * elem};
+}
+
+template <typename T>
+int nhwc_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int N, int Ci, int Hi,
+                int Wi, int Co, int Hf, int Wf, int sh, int sw, hipStream_t stream)
+{
+    int Ho, Wo;
+    if (!x || !w || !y) return IM2WIN_EINVAL;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return IM2WIN_EINVAL;
+    if (!aligned(x, sizeof(T)) || !aligned(w, sizeof(T)) || !aligned(y, sizeof(float)))
+        return IM2WIN_EINVAL;
+    const ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo};
+    const int e = (int)sizeof(T);
+    if (ws == nullptr) {
+        if (ws_bytes != 0) return IM2WIN_EWORKSPACE;
+        return status_of(im2win::launch_conv_direct_nhwc(x, w, y, c, e, stream));
+    }
+    const ColPlan p = nhwc_plan(c, sizeof(T));
+    if (ws_bytes < p.fbytes + p.per_image) return IM2WIN_EWORKSPACE;
+    if (!aligned(ws, 16)) return IM2WIN_EINVAL;
+    // Window slices must be whole 16-byte loads (Ci a multiple of 16 halves or
+    // 8 floats, x 16-byte aligned); other shapes take the direct kernel.
+    if (!im2win::nhwc_gemm_applies(c, e) || !aligned(x, 16))
+        return status_of(im2win::launch_conv_direct_nhwc(x, w, y, c, e, stream));
+    unsigned char* wsb = static_cast<unsigned char*>(ws);
+    int rc = im2win::launch_filter_khwc(w, wsb, c, e, stream);
+    if (rc != 0) return status_of(rc);
+    const int64_t x_img = (int64_t)Hi * Wi * Ci, y_img = (int64_t)Ho * Wo * Co;
+    const size_t lim = 0xFFFFFFF0u;
+    size_t cap = std::min<size_t>((size_t)N, (ws_bytes - p.fbytes) / p.per_image);
+    cap = std::min(cap, (lim - 1) / p.per_image);
+    cap = std::min(cap, (lim - 1) / ((size_t)y_img * 4));
+    if (cap < 1) return IM2WIN_EINVAL;
+    const int chunk = (int)cap;
+    for (int n0 = 0; n0 < N; n0 += chunk) {
+        ConvShape cc = c;
+        cc.N = std::min(chunk, N - n0);
+        rc = im2win::launch_pack_nhwc(x + n0 * x_img, wsb + p.fbytes, cc, e, stream);
+        if (rc != 0) return status_of(rc);
+        rc = im2win::launch_nhwc_gemm(wsb + p.fbytes, wsb, y + n0 * y_img, cc, e, stream);
+        if (rc != 0) return status_of(rc);
+    }
+    return IM2WIN_OK;
+}
+
 }  // namespace
 
 namespace im2win {
@@ -369,6 +420,46 @@ int conv2d_direct_fp16(const uint16_t* x, const uint16_t* w, float* y, int N, in
 {
     return direct_driver<uint16_t>(x, w, y, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
                                    static_cast<hipStream_t>(stream), f16_generic);
+}
+
+size_t conv2d_im2win_nhwc_workspace_bytes(int materialize, int N, int Ci, int Hi, int Wi, int Co,
+                                          int Hf, int Wf, int sh, int sw, size_t elem_bytes)
+{
+    int Ho, Wo;
+    if (elem_bytes != 2 && elem_bytes != 4) return 0;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return 0;
+    if (!materialize) return 0;
+    const ColPlan p = nhwc_plan(ConvShape{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo}, elem_bytes);
+    return p.fbytes + (size_t)N * p.per_image;
+}
+
+int im2win_pack_nhwc(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, int Wf, int sh,
+                     int sw, size_t elem_bytes, void* stream)
+{
+    int Ho, Wo;
+    if (!x || !ws) return IM2WIN_EINVAL;
+    if (elem_bytes != 2 && elem_bytes != 4) return IM2WIN_EINVAL;
+    if (!check_shape(N, Ci, Hi, Wi, 1, Hf, Wf, sh, sw, &Ho, &Wo)) return IM2WIN_EINVAL;
+    if (!aligned(x, elem_bytes) || !aligned(ws, elem_bytes)) return IM2WIN_EINVAL;
+    return status_of(im2win::launch_pack_nhwc(
+        x, ws, ConvShape{N, Ci, Hi, Wi, 1, Hf, Wf, sh, sw, Ho, Wo}, (int)elem_bytes,
+        static_cast<hipStream_t>(stream)));
+}
+
+int conv2d_im2win_nhwc_fp32(const float* x, const float* w, float* y, void* ws, size_t ws_bytes,
+                            int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw,
+                            void* stream)
+{
+    return nhwc_driver<float>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
+                              static_cast<hipStream_t>(stream));
+}
+
+int conv2d_im2win_nhwc_fp16(const uint16_t* x, const uint16_t* w, float* y, void* ws,
+                            size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf,
+                            int sh, int sw, void* stream)
+{
+    return nhwc_driver<uint16_t>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
+                                 static_cast<hipStream_t>(stream));
 }
 
 const char* im2win_last_error(void)

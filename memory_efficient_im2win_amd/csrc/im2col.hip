@@ -74,9 +74,13 @@ __global__ __launch_bounds__(256) void filter_pad_kernel(const T* __restrict__ w
 }
 
 struct GemmArgs {
-    int Co, KP, P;            // channels, padded K, pixels per image
+    int Co, KP, P;            // channels, K per row (a multiple of the slice), pixels per image
     int64_t rows;             // N*P
     uint64_t colbytes, wbytes, ybytes;
+    // Rows of the B matrix: im2col rows (q*KP), or the overlapping window runs
+    // of an NHWC im2win tensor (((n*Ho + ho)*Wi + wo*sw)*HfC). Output NCHW or NHWC.
+    bool win_rows, y_nhwc;
+    int Ho, Wo, Wi, sw, HfC;
 };
 
 // One MFMA slice: fp16 16 K values (lanes 0-31 the first 8, 32-63 the next 8),
@@ -105,7 +109,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(const void* __res
         const int co = co0 + i * 32 + l32;
         ao[i] = co < a.Co ? (uint32_t)(((int64_t)co * a.KP + (SK / 2) * hl) * E) : kMissOff;
         const int64_t q = q0 + i * 32 + l32;
-        const uint64_t b = (uint64_t)(q * a.KP + (SK / 2) * hl) * E;
+        int64_t row = q * a.KP;
+        if (a.win_rows) {
+            const int64_t n = q / a.P;
+            const int pix = (int)(q - n * a.P);
+            const int ho = pix / a.Wo, wo = pix - ho * a.Wo;
+            row = ((n * a.Ho + ho) * a.Wi + (int64_t)wo * a.sw) * a.HfC;
+        }
+        const uint64_t b = (uint64_t)(row + (SK / 2) * hl) * E;
         bo[i] = q < a.rows && b < 0xFFFFFFF0ull ? (uint32_t)b : kMissOff;
     }
 
@@ -187,12 +198,29 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(const void* __res
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int co = co0 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                const int64_t off = a.y_nhwc ? q * a.Co + co : (n * a.Co + co) * a.P + p;
                 if (co < a.Co)
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        __float_as_uint(acc[i][j][r]), ry,
-                        (int)(((n * a.Co + co) * a.P + p) * 4), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ry,
+                                                          (int)(off * 4), 0, 0);
             }
     }
+}
+
+int launch_gemm(const void* b, const void* a, float* y, const GemmArgs& g, int Co, int elem,
+                hipStream_t stream)
+{
+    // 32-bit buffer offsets: the chunk's matrix and output below 4 GiB.
+    if (g.colbytes >= 0xFFFFFFF0ull || g.ybytes >= 0xFFFFFFF0ull || g.wbytes >= 0xFFFFFFF0ull)
+        return -1;
+    const int64_t blocks = ((g.rows + 255) / 256) * ((Co + 63) / 64);
+    if (blocks <= 0 || blocks > 0x7fffffff) return -1;
+    if (elem == 2)
+        hipLaunchKernelGGL(gemm_nt_kernel<true>, dim3((unsigned)blocks), dim3(kGemmThreads), 0,
+                           stream, b, a, y, g);
+    else
+        hipLaunchKernelGGL(gemm_nt_kernel<false>, dim3((unsigned)blocks), dim3(kGemmThreads), 0,
+                           stream, b, a, y, g);
+    return launch_status();
 }
 
 int64_t padded_k(const ConvShape& c, int elem)
@@ -239,7 +267,7 @@ int launch_im2col_gemm(const void* col, const void* w, void* wpad, float* y, con
     else
         hipLaunchKernelGGL(filter_pad_kernel<uint32_t>, dim3((unsigned)wblocks), dim3(256), 0, stream,
                            (const uint32_t*)w, (uint32_t*)wpad, c.Co, K, KP);
-    GemmArgs g;
+    GemmArgs g{};
     g.Co = c.Co;
     g.KP = KP;
     g.P = c.Ho * c.Wo;
@@ -247,17 +275,37 @@ int launch_im2col_gemm(const void* col, const void* w, void* wpad, float* y, con
     g.colbytes = (uint64_t)g.rows * KP * elem;
     g.wbytes = (uint64_t)wtotal * elem;
     g.ybytes = (uint64_t)g.rows * c.Co * 4;
-    // 32-bit buffer offsets: the chunk's matrix and output below 4 GiB.
-    if (g.colbytes >= 0xFFFFFFF0ull || g.ybytes >= 0xFFFFFFF0ull) return -1;
-    const int64_t blocks = ((g.rows + 255) / 256) * ((c.Co + 63) / 64);
-    if (blocks <= 0 || blocks > 0x7fffffff) return -1;
-    if (elem == 2)
-        hipLaunchKernelGGL(gemm_nt_kernel<true>, dim3((unsigned)blocks), dim3(kGemmThreads), 0,
-                           stream, col, (const void*)wpad, y, g);
-    else
-        hipLaunchKernelGGL(gemm_nt_kernel<false>, dim3((unsigned)blocks), dim3(kGemmThreads), 0,
-                           stream, col, (const void*)wpad, y, g);
-    return launch_status();
+    g.win_rows = false;
+    g.y_nhwc = false;
+    return launch_gemm(col, wpad, y, g, c.Co, elem, stream);
+}
+
+bool nhwc_gemm_applies(const ConvShape& c, int elem)
+{
+    // Window runs of whole slices (K = Wf*Hf*Ci), each slice 16 aligned bytes.
+    return c.Ci % (elem == 2 ? 16 : 8) == 0;
+}
+
+int launch_nhwc_gemm(const void* ws, const void* wr, float* y, const ConvShape& c, int elem,
+                     hipStream_t stream)
+{
+    if (!nhwc_gemm_applies(c, elem)) return -1;
+    GemmArgs g{};
+    g.Co = c.Co;
+    g.HfC = c.Hf * c.Ci;
+    g.KP = c.Wf * g.HfC;
+    g.P = c.Ho * c.Wo;
+    g.rows = (int64_t)c.N * g.P;
+    g.colbytes = (uint64_t)c.N * c.Ho * c.Wi * g.HfC * elem;
+    g.wbytes = (uint64_t)c.Co * g.KP * elem;
+    g.ybytes = (uint64_t)g.rows * c.Co * 4;
+    g.win_rows = true;
+    g.y_nhwc = true;
+    g.Ho = c.Ho;
+    g.Wo = c.Wo;
+    g.Wi = c.Wi;
+    g.sw = c.sw;
+    return launch_gemm(ws, wr, y, g, c.Co, elem, stream);
 }
 
 }  // namespace im2win

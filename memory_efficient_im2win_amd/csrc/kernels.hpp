@@ -67,6 +67,18 @@ int launch_im2col(const void* x, void* col, const ConvShape& c, int elem, hipStr
 int launch_im2col_gemm(const void* col, const void* w, void* wpad, float* y, const ConvShape& c,
                        int elem, hipStream_t stream);
 
+// NHWC (x: N x Hi x Wi x Ci, y: N x Ho x Wo x Co): the im2win transform
+// ws[n][ho][w][kh][c] = x[n][ho*sh + kh][w][c]; the filters reordered to
+// the window order wr[co][(kw*Hf + kh)*Ci + c]; the GEMM over the window
+// runs of ws (when nhwc_gemm_applies); the direct kernel.
+int launch_pack_nhwc(const void* x, void* ws, const ConvShape& c, int elem, hipStream_t stream);
+int launch_filter_khwc(const void* w, void* wr, const ConvShape& c, int elem, hipStream_t stream);
+bool nhwc_gemm_applies(const ConvShape& c, int elem);
+int launch_nhwc_gemm(const void* ws, const void* wr, float* y, const ConvShape& c, int elem,
+                     hipStream_t stream);
+int launch_conv_direct_nhwc(const void* x, const void* w, float* y, const ConvShape& c, int elem,
+                            hipStream_t stream);
+
 // Plain fallbacks (one thread per output) for shapes the tiled kernels do
 // not take; ws as above.
 int launch_conv_generic_f32(const float* x, const float* ws, const float* w, float* y,

@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         single + [f + "_strided" for f in single] + ["im2win_status_string", "im2win_last_error"] +
         ["conv2d_im2col_workspace_bytes", "im2col_pack", "conv2d_im2col_fp32", "conv2d_im2col_fp16",
-         "conv2d_direct_fp32", "conv2d_direct_fp16"])
+         "conv2d_direct_fp32", "conv2d_direct_fp16", "conv2d_im2win_nhwc_workspace_bytes",
+         "im2win_pack_nhwc", "conv2d_im2win_nhwc_fp32", "conv2d_im2win_nhwc_fp16"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -249,3 +250,25 @@ def test_direct_and_im2col_pack_reject_bad_arguments():
         assert f(FAKE, FAKE, FAKE, 1, 3, 8, 8, 4, 9, 3, 1, 1, None) == _lib.IM2WIN_EINVAL
     assert L.im2col_pack(FAKE, None, 1, 1, 4, 4, 2, 2, 1, 1, 4, None) == _lib.IM2WIN_EINVAL
     assert L.im2col_pack(FAKE, FAKE, 1, 1, 4, 4, 2, 2, 1, 1, 8, None) == _lib.IM2WIN_EINVAL
+
+
+def test_nhwc_workspace_bytes():
+    # [filter in window order, 256-aligned | N * Ho*Wi*Hf*Ci]: the NHWC im2win
+    # tensor has the size of the NCHW one.
+    fb = -(-64 * 64 * 49 * 2 // 256) * 256
+    assert m.nhwc_workspace_bytes(64, 64, 224, 224, 64, 7, 7, 2, 2) == \
+        fb + m.workspace_bytes(64, 64, 224, 224, 7, 7, 2, 2)
+    assert m.nhwc_workspace_bytes(64, 64, 224, 224, 64, 7, 7, 2, 2, materialize=False) == 0
+    assert m.nhwc_workspace_bytes(1, 3, 4, 4, 2, 5, 5, 1, 2) == 0
+
+
+@pytest.mark.parametrize("fn", ["conv2d_im2win_nhwc_fp32", "conv2d_im2win_nhwc_fp16"])
+def test_nhwc_conv_rejects_bad_arguments(fn):
+    L = m.load_library()
+    f = getattr(L, fn)
+    ok = (1, 16, 8, 8, 4, 3, 3, 1, 1)
+    assert f(None, FAKE, FAKE, None, 0, *ok, None) == _lib.IM2WIN_EINVAL
+    assert f(FAKE, FAKE, FAKE, None, 64, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, 64, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    assert f(FAKE, FAKE, FAKE, None, 0, 1, 16, 8, 8, 4, 3, 3, 1, 0, None) == _lib.IM2WIN_EINVAL
+    assert L.im2win_pack_nhwc(FAKE, None, 1, 1, 4, 4, 2, 2, 1, 1, 4, None) == _lib.IM2WIN_EINVAL
