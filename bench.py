@@ -39,8 +39,8 @@ HEADLINE = "cv1_f32_n32"
 LAYER_KEYS = ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64", "cv4_f16_n64",
               "cv2_f32_n32"]
 KERNEL_SOURCES = ["conv_f32_mfma.hip", "conv_f32.hip", "conv_f16_fused.hip", "conv_f16_rows.hip",
-                  "conv_f16.hip", "conv_generic.hip", "pack.hip", "api.hip", "common.hpp",
-                  "kernels.hpp"]
+                  "conv_f16.hip", "conv_generic.hip", "pack.hip", "im2col.hip", "nhwc.hip",
+                  "api.hip", "common.hpp", "kernels.hpp"]
 # Modes: fused (no workspace), fused_valu (fp32 on the vector-ALU kernel),
 # prepacked (fp16 filter prepacked into a small workspace), materialized
 # (im2win tensor in HBM).
