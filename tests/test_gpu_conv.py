@@ -329,3 +329,91 @@ def test_conv_f16_row_staged_tile_order(t, swz, orc, monkeypatch):
     xi, wi = workloads.make_inputs(sh, seed=43, mode="int")
     note(f"conv fp16 row-staged swizzle={swz} {sh.describe()}")
     assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
+
+
+# Shapes the wide-tile fp16 kernel takes with a prepacked filter (Co >= 128,
+# or any Co with IM2WIN_F16_WIDE=2; not taken by the row-staged kernel):
+# tiles crossing images, Ci and Co off the multiples of 8 and 128, odd Wi
+# (single-column staging), column strides 2 and 3, unequal strides, tiles
+# aligned to images, a 1x1 filter, odd and even tap counts.
+WIDE = [
+    (2, 96, 24, 24, 256, 5, 5, 1),      # cv5 images
+    (3, 13, 19, 21, 130, 3, 3, 1),
+    (2, 16, 30, 28, 136, 3, 5, 2),
+    (1, 8, 40, 40, 128, 4, 4, 3),
+    (2, 24, 36, 36, 160, 2, 6, (1, 3)),
+    (2, 8, 32, 36, 128, 3, 3, 1),       # tiles aligned to images
+    (2, 8, 12, 40, 200, 1, 1, 1),
+    (2, 24, 14, 14, 96, 5, 5, 1),       # Co < 128 (forced)
+]
+
+
+def _wide_plan(sh):
+    """The wide kernel's envelope, worked out independently of the library:
+    (applies, LDS bytes, staging units)."""
+    sh_, sw = sh.s if isinstance(sh.s, tuple) else (sh.s, sh.s)
+    Ho, Wo = (sh.Hi - sh.Hf) // sh_ + 1, (sh.Wi - sh.Wf) // sw + 1
+    P = 512
+    plane = Ho * Wo
+    rows_max = min((P - 1) // Wo + 2, sh.N * Ho)
+    tpi = -(-plane // P)
+    aligned = tpi * P <= 1.05 * plane
+    kmax = 0 if aligned or rows_max <= 1 else min(sh.N - 1, -(-(rows_max - 1) // Ho))
+    rin = (rows_max - 1) * sh_ + sh.Hf + kmax * max(0, sh.Hf - sh_)
+    rs = sw * -(-sh.Wi // sw)
+    units = rin * (sh.Wi // 2) if sh.Wi % 2 == 0 else rin * sh.Wi
+    cap = 4 * 256 if sh.Wi % 2 == 0 else 6 * 256
+    hwp = (sh.Hf * sh.Wf + 1) & ~1
+    kt = (hwp + 8 + 3) & ~3
+    lds = 2 * (hwp * 128 * 16 + rin * rs * 16) + (kt * 4 + 15) // 16 * 16 + 8192
+    return units <= cap and lds <= 160 * 1024, lds, units
+
+
+@pytest.mark.parametrize("nw", ["8", "4"])
+@pytest.mark.parametrize("t", WIDE, ids=str)
+def test_conv_f16_wide_tiles(t, nw, orc, monkeypatch):
+    """The fp16 kernel with 128-channel wave tiles (8 waves of 4 x 2 blocks or
+    4 waves of 4 x 4) and the filter copied to LDS by direct loads: uniform
+    and integer inputs; switching it off (IM2WIN_F16_WIDE=0) gives the
+    channel-interleaved kernel's results."""
+    monkeypatch.setenv("IM2WIN_F16_WIDE_NW", nw)
+    sh = _shape(t, "f16")
+    ok, lds, units = _wide_plan(sh)
+    assert ok, (lds, units)
+    if sh.Co < 128:
+        monkeypatch.setenv("IM2WIN_F16_WIDE", "2")
+    x, w = workloads.make_inputs(sh, seed=50)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    note(f"conv fp16 wide tiles NW={nw} {sh.describe()} (LDS {lds} B)")
+    assert_within(_run(sh, "f16", x, w, "filter"), ref, absd, TOL["f16"], sh.describe())
+    xi, wi = workloads.make_inputs(sh, seed=51, mode="int")
+    yi = _run(sh, "f16", xi, wi, "filter")
+    assert_exact(yi, orc.conv_direct(xi, wi, sh.s), sh.describe())
+    monkeypatch.setenv("IM2WIN_F16_WIDE", "0")
+    assert_exact(_run(sh, "f16", xi, wi, "filter"), yi, "channel-interleaved kernel")
+
+
+@pytest.mark.parametrize("t", [(2, 13, 19, 21, 130, 3, 3, 1), (2, 16, 14, 14, 128, 5, 5, 1)],
+                         ids=str)
+def test_conv_f16_wide_special_values(t, orc):
+    """Infinities and NaN reach exactly the outputs whose windows hold them;
+    the zero partner of the last tap (odd tap count) never multiplies one."""
+    sh = _shape(t, "f16")
+    assert _wide_plan(sh)[0]
+    x, w = workloads.make_inputs(sh, seed=52)
+    x[0, 1, 4, 5] = np.inf
+    x[0, 2, 7, 13] = -np.inf
+    x[1, 3, 0, 6] = np.nan
+    x[1, 0, 13, 13] = np.inf
+    x[0, 0, 2, 7] = np.inf
+    w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
+    ref = orc.conv_direct(x, w, sh.s)
+    note(f"conv fp16 wide special values {sh.describe()}")
+    y = _run(sh, "f16", x, w, "filter").astype(np.float64)
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
+                              with_absdot=True)
+    assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
