@@ -78,9 +78,55 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void* base, uint32_t
 
 // Filters of channel group g as 16-byte entries (tap j, channel co):
 // wpk[(g*HWp + j)*Copad + co] = w[co][8g..8g+7][j], zero beyond Co, Ci, HW.
+// A workgroup packs channels co0 .. co0+3 of group g: for each channel the
+// 8*HW elements w[co][8g..8g+7][0..HW) are contiguous in w, so they are read
+// in order into LDS and each entry's 8 taps are gathered from there.
+constexpr int kPackCo = 4;
 __global__ __launch_bounds__(256) void f16_filter_pack_kernel(const uint16_t* __restrict__ w,
                                                               uint4* __restrict__ wpk,
                                                               FusedArgs a)
+{
+    extern __shared__ uint16_t fs[];   // [kPackCo][8 * HW]
+    const int g = blockIdx.y, co0 = blockIdx.x * kPackCo;
+    const int HW = a.HW, Ci = a.c.Ci, Co = a.c.Co;
+    const int nc = min(8, Ci - 8 * g);
+    const int per = 8 * HW;
+    // Sixteen independent loads per thread in flight at a time.
+    for (int i0 = 0; i0 < kPackCo * per; i0 += 16 * 256) {
+        uint16_t v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int i = i0 + k * 256 + threadIdx.x;
+            const int col = i / per, r = i - col * per;   // r = q*HW + j
+            const int co = co0 + col;
+            v[k] = i < kPackCo * per && co < Co && r < nc * HW
+                       ? w[((int64_t)co * Ci + 8 * g) * HW + r]
+                       : (uint16_t)0;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int i = i0 + k * 256 + threadIdx.x;
+            if (i < kPackCo * per) fs[i] = v[k];
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kPackCo * a.HWp; i += 256) {
+        const int j = i / kPackCo, col = i - j * kPackCo;
+        uint32_t v[4] = {0, 0, 0, 0};
+        if (j < HW) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                v[q >> 1] |= (uint32_t)fs[col * per + q * HW + j] << (16 * (q & 1));
+        }
+        wpk[((int64_t)g * a.HWp + j) * a.Copad + co0 + col] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// The same entries, one thread each, gathered straight from w (filters with
+// more than 256 taps).
+__global__ __launch_bounds__(256) void f16_filter_gather_kernel(const uint16_t* __restrict__ w,
+                                                                uint4* __restrict__ wpk,
+                                                                FusedArgs a)
 {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total = (int64_t)a.CG * a.HWp * a.Copad;
@@ -616,10 +662,18 @@ int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, hip
     FusedArgs a;
     int wco, wpx, nb;
     if (!plan(c, a, wco, wpx, nb)) return -1;
+    // LDS of one workgroup: kPackCo channels x 8 x HW taps (HW <= 256: 16 KB).
+    const size_t lds = (size_t)kPackCo * 8 * a.HW * 2;
+    if (a.HW <= 256 && a.CG <= 65535) {
+        hipLaunchKernelGGL(f16_filter_pack_kernel,
+                           dim3((unsigned)(a.Copad / kPackCo), (unsigned)a.CG), dim3(256), lds,
+                           stream, w, (uint4*)wpk, a);
+        return launch_status();
+    }
     const int64_t total = (int64_t)a.CG * a.HWp * a.Copad;
     const int64_t blocks = (total + 255) / 256;
     if (blocks > 0x7fffffff) return -1;
-    hipLaunchKernelGGL(f16_filter_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w,
+    hipLaunchKernelGGL(f16_filter_gather_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w,
                        (uint4*)wpk, a);
     return launch_status();
 }

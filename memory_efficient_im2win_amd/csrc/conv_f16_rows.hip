@@ -97,23 +97,46 @@ __device__ __forceinline__ void wait_loads()
 
 // Filter slices (c, kh) as 16-byte entries of the 8 taps kw of one output
 // channel: wp[(c*Hf + kh)*Copad + co] = w[co][c][kh][0..7], zero for kw >= Wf
-// and co >= Co.
+// and co >= Co. A workgroup packs channels co0 .. co0+3 and input channels
+// c0 .. c0+7: for each output channel those input channels' Hf*Wf taps are
+// contiguous in w, so they are read in order into LDS and each entry's taps
+// are gathered from there.
+constexpr int kPackCo = 4;
 __global__ __launch_bounds__(256) void f16_rows_filter_pack_kernel(const uint16_t* __restrict__ w,
                                                                    uint4* __restrict__ wp,
                                                                    RowsArgs a)
 {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)a.c.Ci * a.c.Hf * a.Copad;
-    if (e >= total) return;
-    const int co = (int)(e % a.Copad);
-    const int ck = (int)(e / a.Copad);
-    const int c = ck / a.c.Hf, kh = ck - (ck / a.c.Hf) * a.c.Hf;
-    uint32_t v[4] = {0, 0, 0, 0};
-    if (co < a.c.Co) {
-        const uint16_t* src = w + (((int64_t)co * a.c.Ci + c) * a.c.Hf + kh) * a.c.Wf;
-        for (int kw = 0; kw < a.c.Wf; ++kw) v[kw >> 1] |= (uint32_t)src[kw] << (16 * (kw & 1));
+    extern __shared__ uint16_t fs[];   // [kPackCo][8 * Hf * Wf]
+    const int Ci = a.c.Ci, Co = a.c.Co, Hf = a.c.Hf, Wf = a.c.Wf;
+    const int co0 = blockIdx.x * kPackCo, c0 = 8 * blockIdx.y;
+    const int nc = min(8, Ci - c0);
+    const int per = 8 * Hf * Wf;
+    // Sixteen independent loads per thread in flight at a time.
+    for (int i0 = 0; i0 < kPackCo * per; i0 += 16 * 256) {
+        uint16_t v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int i = i0 + k * 256 + threadIdx.x;
+            const int col = i / per, r = i - col * per;   // r = (c - c0)*Hf*Wf + kh*Wf + kw
+            const int co = co0 + col;
+            v[k] = i < kPackCo * per && co < Co && r < nc * Hf * Wf
+                       ? w[((int64_t)co * Ci + c0) * Hf * Wf + r]
+                       : (uint16_t)0;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int i = i0 + k * 256 + threadIdx.x;
+            if (i < kPackCo * per) fs[i] = v[k];
+        }
     }
-    wp[e] = make_uint4(v[0], v[1], v[2], v[3]);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kPackCo * nc * Hf; i += 256) {
+        const int ck = i / kPackCo, col = i - ck * kPackCo;   // ck = (c - c0)*Hf + kh
+        uint32_t v[4] = {0, 0, 0, 0};
+        for (int kw = 0; kw < Wf; ++kw)
+            v[kw >> 1] |= (uint32_t)fs[col * per + ck * Wf + kw] << (16 * (kw & 1));
+        wp[((int64_t)c0 * Hf + ck) * a.Copad + co0 + col] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
 }
 
 template <int NWV, int DMAX, bool M3>
@@ -363,7 +386,8 @@ int env_int(const char* name, int dflt)
 constexpr int kDmax[] = {4, 5, 6, 8, 12, 16};
 
 // Plans a launch; false if the shape is outside the kernel's envelope:
-// even column stride, Wf <= 8, Wi a multiple of 8 (16-byte row chunks),
+// even column stride, Wf <= 8, Hf*Wf <= 256 (the filter pack's LDS), Wi a
+// multiple of 8 (16-byte row chunks),
 // Ci a multiple of the stage's channel count, tensors addressable with
 // 32-bit buffer offsets. IM2WIN_F16_ROWS=0 turns the kernel off,
 // IM2WIN_F16_ROWS_NWV picks the waves per workgroup and
@@ -371,7 +395,7 @@ constexpr int kDmax[] = {4, 5, 6, 8, 12, 16};
 bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax)
 {
     if (env_int("IM2WIN_F16_ROWS", 1) == 0) return false;
-    if (c.Wf > 8 || c.sw % 2 != 0 || c.Wi % 8 != 0) return false;
+    if (c.Wf > 8 || c.sw % 2 != 0 || c.Wi % 8 != 0 || c.Hf * c.Wf > 256) return false;
     a.c = c;
     a.total = (int64_t)c.N * c.Ho * c.Wo;
     a.dup = std::max(0, c.Hf - c.sh);
@@ -500,11 +524,13 @@ int launch_f16_rows_filter_pack(const uint16_t* w, void* wp, const ConvShape& c,
     RowsArgs a;
     int nwv, dmax;
     if (!plan(c, a, nwv, dmax)) return -1;
-    const int64_t total = (int64_t)c.Ci * c.Hf * a.Copad;
-    const int64_t blocks = (total + 255) / 256;
-    if (blocks > 0x7fffffff) return -1;
-    hipLaunchKernelGGL(f16_rows_filter_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w,
-                       static_cast<uint4*>(wp), a);
+    // LDS of one workgroup: kPackCo channels x 8 input channels x Hf*Wf taps
+    // (Hf*Wf <= 256 in this kernel's envelope: 16 KB).
+    const size_t lds = (size_t)kPackCo * 8 * c.Hf * c.Wf * 2;
+    if (ceil_div(c.Ci, 8) > 65535) return -1;
+    hipLaunchKernelGGL(f16_rows_filter_pack_kernel,
+                       dim3((unsigned)(a.Copad / kPackCo), (unsigned)ceil_div(c.Ci, 8)), dim3(256),
+                       lds, stream, w, static_cast<uint4*>(wp), a);
     return launch_status();
 }
 

@@ -417,3 +417,16 @@ def test_conv_f16_wide_special_values(t, orc):
     _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
                               with_absdot=True)
     assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
+
+
+@pytest.mark.parametrize("t", [(1, 10, 40, 40, 24, 17, 17, 1), (2, 12, 21, 40, 136, 16, 16, 1),
+                               (1, 20, 30, 32, 70, 16, 8, 2)], ids=str)
+def test_conv_f16_filter_pack_tap_counts(t, orc):
+    """The filter packs on both sides of their LDS limit (256 taps): 17 x 17
+    (289 taps, packed one entry per thread), 16 x 16 (256 taps, through LDS)
+    and a 16 x 8 filter for the row-staged layout, bit-exact on integer
+    inputs."""
+    sh = _shape(t, "f16")
+    xi, wi = workloads.make_inputs(sh, seed=53, mode="int")
+    note(f"conv fp16 filter pack taps={sh.Hf * sh.Wf} {sh.describe()}")
+    assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
