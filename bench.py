@@ -292,11 +292,14 @@ ABLATION = {
             ("prepacked, row-staged kernel with 4 waves", "prepacked", {"IM2WIN_F16_ROWS_NWV": "4"}),
             ("prepacked, row-staged, tiles in launch order", "prepacked",
              {"IM2WIN_F16_ROWS_SWIZZLE": "0"}),
-            ("prepacked, channel-interleaved kernel", "prepacked", {"IM2WIN_F16_ROWS": "0"}),
+            ("prepacked, wide-tile kernel with 4 waves of 4 x 4 blocks", "prepacked",
+             {"IM2WIN_F16_WIDE_NW": "4"}),
+            ("prepacked, channel-interleaved kernel", "prepacked",
+             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_WIDE": "0"}),
             ("channel-interleaved, 8 waves along pixels", "prepacked",
-             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_WPX": "8"}),
+             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_WIDE": "0", "IM2WIN_F16_WPX": "8"}),
             ("channel-interleaved, >= 2 filter parts per group", "prepacked",
-             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_NWH": "2"}),
+             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_WIDE": "0", "IM2WIN_F16_NWH": "2"}),
             ("materialised im2win tensor", "materialized", {})],
 }
 
