@@ -312,23 +312,27 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
     dma_w(0, 0);
     load_x(0);
     store_x(0);
+    __syncthreads();   // the tap table
+    // Window offsets of the first two pairs, the same in every group.
+    const int t0 = T[hl], t1 = T[2 + hl];
     for (int g = 0; g < a.CG; ++g) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's filter loads of group g
         __syncthreads();   // every wave's loads and input rows; buffer (g+1)%2 is free
-        if (g + 1 < a.CG) {
-            dma_w(g + 1, (g + 1) & 1);
-            load_x(g + 1);
-        }
         A = reinterpret_cast<const uint4*>(smem + (size_t)(g & 1) * a.stage_bytes);
         X = reinterpret_cast<const uint4*>(smem + (size_t)(g & 1) * a.stage_bytes + a.fbytes);
 
         // The fragments of pair t+1 are read while the MFMAs of pair t run;
         // reads run at most two pairs past the group (inside the allocation,
-        // never used).
+        // never used). The first pair's reads go out before the next group's
+        // loads are issued.
         Frags f0, f1;
-        on0 = T[hl];
-        on1 = T[2 + hl];
+        on0 = t0;
+        on1 = t1;
         fetch(f0, 0);
+        if (g + 1 < a.CG) {
+            dma_w(g + 1, (g + 1) & 1);
+            load_x(g + 1);
+        }
         int t = 0;
         for (; t + 2 <= nfull; t += 2) {
             fetch(f1, t + 1);
