@@ -39,7 +39,7 @@ HEADLINE = "cv1_f32_n32"
 LAYER_KEYS = ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64", "cv4_f16_n64",
               "cv2_f32_n32"]
 KERNEL_SOURCES = ["conv_f32_mfma.hip", "conv_f32.hip", "conv_f16_fused.hip", "conv_f16_rows.hip",
-                  "conv_f16_wide.hip",
+                  "conv_f16_wide.hip", "conv_f16_thin.hip",
                   "conv_f16.hip", "conv_generic.hip", "pack.hip", "im2col.hip", "nhwc.hip",
                   "api.hip", "common.hpp", "kernels.hpp"]
 # Modes: fused (no workspace), fused_valu (fp32 on the vector-ALU kernel),
@@ -49,7 +49,8 @@ MODES = ["fused", "fused_valu", "prepacked", "materialized"]
 
 
 CONV_KERNELS = ("conv_f32_mfma_kernel", "conv_f32_kernel", "conv_f16_fused_kernel",
-                "conv_f16_rows_kernel", "conv_f16_wide_kernel", "conv_f16_kernel")
+                "conv_f16_rows_kernel", "conv_f16_thin_kernel", "conv_f16_wide_kernel",
+                "conv_f16_kernel")
 
 
 def log(msg):
@@ -295,11 +296,13 @@ ABLATION = {
             ("prepacked, wide-tile kernel with 4 waves of 4 x 4 blocks", "prepacked",
              {"IM2WIN_F16_WIDE_NW": "4"}),
             ("prepacked, channel-interleaved kernel", "prepacked",
-             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_WIDE": "0"}),
+             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_THIN": "0", "IM2WIN_F16_WIDE": "0"}),
             ("channel-interleaved, 8 waves along pixels", "prepacked",
-             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_WIDE": "0", "IM2WIN_F16_WPX": "8"}),
+             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_THIN": "0", "IM2WIN_F16_WIDE": "0",
+              "IM2WIN_F16_WPX": "8"}),
             ("channel-interleaved, >= 2 filter parts per group", "prepacked",
-             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_WIDE": "0", "IM2WIN_F16_NWH": "2"}),
+             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_THIN": "0", "IM2WIN_F16_WIDE": "0",
+              "IM2WIN_F16_NWH": "2"}),
             ("materialised im2win tensor", "materialized", {})],
 }
 
@@ -437,12 +440,15 @@ def main():
     sw = sh.s[1] if isinstance(sh.s, tuple) else sh.s
     rows = (args.mode == "prepacked" and sh.Wf <= 8 and sw % 2 == 0 and sh.Wi % 8 == 0
             and sh.Ci % 2 == 0)
-    # Otherwise, with a prepacked filter, layers with at least 128 output
-    # channels run the wide-tile kernel (when its stage fits LDS).
-    wide = args.mode == "prepacked" and not rows and sh.Co >= 128
+    # Otherwise, with a prepacked filter, layers with fewer than 8 input
+    # channels run the thin-layer kernel and layers with at least 128 output
+    # channels the wide-tile kernel (when their tiles fit LDS).
+    thin = (args.mode == "prepacked" and not rows and sh.Ci < 8 and sh.Wf <= 8 and sw % 2 == 0
+            and sh.Ci * sh.Hf <= 64)
+    wide = args.mode == "prepacked" and not rows and not thin and sh.Co >= 128
     kernel = ("conv_f32_kernel" if valu else "conv_f32_mfma_kernel") if is_f32 else \
         ("conv_f16_kernel" if args.mode == "materialized" else
-         "conv_f16_rows_kernel" if rows else
+         "conv_f16_rows_kernel" if rows else "conv_f16_thin_kernel" if thin else
          "conv_f16_wide_kernel" if wide else "conv_f16_fused_kernel")
     roofline = {
         "bound": "alu" if valu else "mfma",

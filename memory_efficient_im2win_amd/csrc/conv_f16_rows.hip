@@ -524,10 +524,24 @@ int launch_f16_rows_filter_pack(const uint16_t* w, void* wp, const ConvShape& c,
     RowsArgs a;
     int nwv, dmax;
     if (!plan(c, a, nwv, dmax)) return -1;
+    return launch_f16_slices_filter_pack(w, wp, c, stream);
+}
+
+size_t f16_slices_filter_bytes(const ConvShape& c)
+{
+    return (size_t)c.Ci * c.Hf * (size_t)(ceil_div(c.Co, kCoT) * kCoT) * 16;
+}
+
+int launch_f16_slices_filter_pack(const uint16_t* w, void* wp, const ConvShape& c,
+                                  hipStream_t stream)
+{
+    if (c.Wf > 8 || c.Hf * c.Wf > 256 || ceil_div(c.Ci, 8) > 65535) return -1;
+    RowsArgs a{};
+    a.c = c;
+    a.Copad = ceil_div(c.Co, kCoT) * kCoT;
     // LDS of one workgroup: kPackCo channels x 8 input channels x Hf*Wf taps
-    // (Hf*Wf <= 256 in this kernel's envelope: 16 KB).
+    // (at most 16 KB).
     const size_t lds = (size_t)kPackCo * 8 * c.Hf * c.Wf * 2;
-    if (ceil_div(c.Ci, 8) > 65535) return -1;
     hipLaunchKernelGGL(f16_rows_filter_pack_kernel,
                        dim3((unsigned)(a.Copad / kPackCo), (unsigned)ceil_div(c.Ci, 8)), dim3(256),
                        lds, stream, w, static_cast<uint4*>(wp), a);

@@ -1,0 +1,432 @@
+// fp16 im2win convolution on the CDNA4 matrix cores for thin layers: few
+// input channels, so the whole filter stays in LDS (fp32 accumulate,
+// prepacked filter).
+//
+// The half-precision path of "Enabling Memory-efficient Im2win Convolution
+// with Multi-precision Support on GPU CUDA and Tensor Cores" (Abstract: half
+// precision on matrix hardware; Table I, cv3: 3 input channels, 64 filters
+// of 7 x 7, stride 2), on the im2win property of "Im2win: Memory Efficient
+// Convolution On SIMD Architectures" (Abstract): the part of a window in one
+// input row is one contiguous run of that row.
+//
+//  * GEMM view: rows = output channels (A = filters), columns = output
+//    pixels numbered over the batch (B = windows), K = (input channel c,
+//    filter row kh, filter column kw) with kw padded to 8, as in the
+//    row-staged kernel: a K slice of 8 is one (c, kh), for a pixel the 8
+//    consecutive input columns wo*sw .. wo*sw+7 of input row ho*sh+kh. With
+//    an even column stride each lane's B operand is one 4-byte-aligned
+//    16-byte LDS read. Channel-interleaved slices would pad 3 channels to 8;
+//    these pad 7 taps to 8.
+//  * The whole contraction is one stage: a workgroup copies the filter
+//    slices of its 64 output channels (direct global-to-LDS loads) and the
+//    input rows of its 512 pixels, for every input channel (through
+//    registers, so rows of any width and alignment are taken), then runs
+//    all the MFMAs and stores. Four waves each hold a 2 x 4 tile of 32 x 32
+//    accumulators (64 channels x 128 pixels); two workgroups share a CU, so
+//    one's loads and stores overlap the other's MFMAs.
+//  * An odd slice count gets a zero partner slice: its filter entries are
+//    written as zeros and lanes 32-63 zero their B slice, and taps kw >= Wf
+//    are zero in the filter and masked in B, so an infinity next to a window
+//    never turns into NaN.
+#include <algorithm>
+#include <cstdlib>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace im2win {
+
+namespace {
+
+constexpr int kThinLds = 160 * 1024;
+constexpr int kCoT = 64;                  // output channels per tile
+constexpr int kNB = 4;                    // 32-pixel blocks per wave
+constexpr int kNW = 4;                    // waves per workgroup
+constexpr int kNT = 64 * kNW;
+constexpr int kP = 32 * kNB * kNW;        // pixels per tile
+constexpr int kMaxSlices = 64;            // filter slices (c, kh) held in LDS
+constexpr int kBatch = 8;                 // row chunks a thread has in flight
+constexpr int kSlackT = 2048;             // A reads run one pair past the filter
+constexpr uint32_t kMissT = 0xFFFFFFF0u;  // vector offset past every accepted buffer
+
+struct ThinArgs {
+    ConvShape c;
+    int co_tiles;
+    int64_t px_tiles, total, tiles_per_image;
+    bool aligned;                   // tiles never cross images
+    int rows_max, kmax, dup, RIN;   // output rows per tile, image breaks, sh<Hf overlap, LDS rows per channel
+    int RP, CH;                     // halves per LDS row (multiple of 8); its 16-byte chunks
+    int S, Sp;                      // filter slices Ci*Hf; rounded up to even
+    int Copad;                      // prepacked filter channels (multiple of 64)
+    int chunks;                     // row chunks of a tile: Ci * RIN * CH
+    int KT;                         // entries of the slice offset table
+    uint32_t xoff, tab, lds_bytes;  // LDS byte offsets of the rows and the table; total
+    uint32_t xbytes, ybytes, wbytes;
+    uint32_t mask[4];               // B dwords: halves kw >= Wf cleared
+    FastDiv divWo, divHo, divCH, divRIN;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tbuf(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16 bytes per lane from buffer r at vector offset voff into LDS at byte
+// lds + 16*lane (lds wave-uniform); M0 is saved and restored around it.
+__device__ __forceinline__ void dma16t(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff)
+{
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
+}
+
+// XVEC: Wi % 8 == 0 and x 16-byte aligned, so a row chunk is one 16-byte
+// load; otherwise 8 two-byte loads. M3: Wf >= 6, only the last B dword
+// holds padded taps.
+template <bool XVEC, bool M3>
+__global__ __launch_bounds__(kNT, 2) void conv_f16_thin_kernel(const uint16_t* __restrict__ x,
+                                                               const uint4* __restrict__ wp,
+                                                               float* __restrict__ y, ThinArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const uint32_t lbase =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+    const int Ci = a.c.Ci, Hi = a.c.Hi, Wi = a.c.Wi, Co = a.c.Co;
+    const int sh = a.c.sh, sw = a.c.sw;
+    const int Ho = a.c.Ho, Wo = a.c.Wo, Hf = a.c.Hf;
+
+    const int co_t = (int)(blockIdx.x % a.co_tiles);
+    const int64_t pt = blockIdx.x / a.co_tiles;
+    const int co0 = co_t * kCoT;
+    int64_t q0, qend;
+    if (a.aligned) {   // tile pt = (image, tile within the image)
+        const int64_t img = pt / a.tiles_per_image;
+        const int64_t plane = (int64_t)Ho * Wo;
+        q0 = img * plane + (pt - img * a.tiles_per_image) * kP;
+        qend = min(q0 + kP, (img + 1) * plane);
+    } else {
+        q0 = pt * kP;
+        qend = q0 + kP < a.total ? q0 + kP : a.total;
+    }
+    const int gr0 = (int)(q0 / Wo);
+    const int grl = (int)((qend - 1) / Wo);
+    const int n0 = (int)a.divHo.div((uint32_t)gr0);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int hl = lane >> 5, l32 = lane & 31;
+    const int wave = uniform(tid >> 6);
+
+    // Byte offset, within the rows, of each pixel's tap (c=0, kh=0, kw=0):
+    // LDS row of its output row gr (tile-relative r*sh plus image breaks
+    // k*dup) times the row pitch, plus its first column wo*sw.
+    int pb[kNB];
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+        int64_t q = q0 + (wave * kNB + b) * 32 + l32;
+        if (q >= qend) q = qend - 1;
+        const int gr = (int)a.divWo.div((uint32_t)(q - (int64_t)gr0 * Wo)) + gr0;
+        const int wo = (int)(q - (int64_t)gr * Wo);
+        const int k = (int)a.divHo.div((uint32_t)gr) - n0;
+        pb[b] = (((gr - gr0) * sh + k * a.dup) * a.RP + wo * sw) * 2;
+    }
+
+    // LDS row i (of a channel) -> (image n, input row h); false if no input
+    // row maps there. Segment k holds the output rows of image n0+k that
+    // fall in the tile.
+    auto x_src = [&](int i, int& n, int& h) -> bool {
+        for (int k = 0; k <= a.kmax; ++k) {
+            const int nk = n0 + k;
+            const int first = max(gr0, nk * Ho), last = min(grl, nk * Ho + Ho - 1);
+            if (first > last) break;
+            const int S0 = (first - gr0) * sh + k * a.dup;
+            const int span = (last - first) * sh + Hf;
+            if (i >= S0 && i < S0 + span) {
+                n = nk;
+                h = (first - nk * Ho) * sh + (i - S0);
+                return true;
+            }
+        }
+        return false;
+    };
+
+    // Filter: kilobyte m of LDS = slice m (c, kh) for the tile's 64 channels,
+    // entries (m*Copad + co0 + lane) of the prepacked filter.
+    {
+        const __amdgpu_buffer_rsrc_t r = tbuf(wp, a.wbytes);
+        for (int m = wave; m < a.S; m += kNW)
+            dma16t(r, lbase + (uint32_t)m * 1024, (uint32_t)((m * a.Copad + co0 + lane) * 16));
+        if (a.Sp > a.S && wave == kNW - 1)
+            reinterpret_cast<uint4*>(smem)[a.S * 64 + lane] = make_uint4(0, 0, 0, 0);
+    }
+    // Slice s = (c, kh) starts (c*RIN + kh) rows into the rows; entries from
+    // S on point at row 0 (their reads are unused or zeroed).
+    int* T = reinterpret_cast<int*>(smem + a.tab);
+    for (int j = tid; j < a.KT; j += kNT) {
+        int v = 0;
+        if (j < a.S) {
+            const int c = j / Hf, kh = j - (j / Hf) * Hf;
+            v = (c * a.RIN + kh) * a.RP * 2;
+        }
+        T[j] = v;
+    }
+    // Rows: chunk e = (cl*RIN + i)*CH + cc holds columns 8cc .. 8cc+7 of LDS
+    // row i of channel cl (zeros past Wi and where no input row maps).
+    {
+        uint4* X = reinterpret_cast<uint4*>(smem + a.xoff);
+        const __amdgpu_buffer_rsrc_t rx = tbuf(x, a.xbytes);
+        for (int e0 = 0; e0 < a.chunks; e0 += kBatch * kNT) {
+            uint4 v[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const int e = e0 + k * kNT + tid;
+                uint32_t src = kMissT;
+                int ncol = 0;
+                if (e < a.chunks) {
+                    const int row = (int)a.divCH.div((uint32_t)e);
+                    const int cc = e - row * a.CH;
+                    const int cl = (int)a.divRIN.div((uint32_t)row);
+                    const int i = row - cl * a.RIN;
+                    int n, h;
+                    if (8 * cc < Wi && x_src(i, n, h)) {
+                        src = (uint32_t)(((((int64_t)n * Ci + cl) * Hi + h) * Wi + 8 * cc) * 2);
+                        ncol = min(8, Wi - 8 * cc);
+                    }
+                }
+                if (XVEC) {
+                    const auto u = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)src, 0, 0);
+                    v[k] = make_uint4(u[0], u[1], u[2], u[3]);
+                } else {
+                    uint32_t d[4] = {0, 0, 0, 0};
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        d[q >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                         rx, (int)(q < ncol ? src + 2 * q : kMissT), 0, 0)
+                                     << (16 * (q & 1));
+                    v[k] = make_uint4(d[0], d[1], d[2], d[3]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const int e = e0 + k * kNT + tid;
+                if (e < a.chunks) X[e] = v[k];
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's filter loads
+    __syncthreads();
+
+    floatx16_t acc[2][kNB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int b = 0; b < kNB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][b][r] = 0.f;
+
+    struct Frags {
+        half8_t a[2], b[kNB];
+    };
+    const unsigned char* X = smem + a.xoff;
+    const uint4* A = reinterpret_cast<const uint4*>(smem);
+    int on0 = T[hl], on1 = T[2 + hl];
+    // Pair t: slices 2t (lanes 0-31) and 2t+1 (lanes 32-63).
+    auto fetch = [&](Frags& f, int t) {
+        const int o = on0;
+        on0 = on1;
+        on1 = T[2 * t + 4 + hl];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint4 u = A[(2 * t + hl) * kCoT + i * 32 + l32];
+            __builtin_memcpy(&f.a[i], &u, 16);
+        }
+        // B addresses are 4-byte aligned (even column stride, row pitch a
+        // multiple of 8 halves), not 16-byte aligned: stated so, the reads
+        // become aligned dword-pair reads instead of the slow unaligned form.
+#pragma unroll
+        for (int b = 0; b < kNB; ++b)
+            __builtin_memcpy(&f.b[b], __builtin_assume_aligned(X + pb[b] + o, 4), 16);
+    };
+    const uint32_t m0 = a.mask[0], m1 = a.mask[1], m2 = a.mask[2], m3 = a.mask[3];
+    auto mma = [&](Frags& f, uint32_t keep) {
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) {
+            uint4 u;
+            __builtin_memcpy(&u, &f.b[b], 16);
+            if (!M3) {
+                u.x &= m0 & keep;
+                u.y &= m1 & keep;
+                u.z &= m2 & keep;
+            } else {
+                u.x &= keep;
+                u.y &= keep;
+                u.z &= keep;
+            }
+            u.w &= m3 & keep;
+            __builtin_memcpy(&f.b[b], &u, 16);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                acc[i][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[b], acc[i][b], 0, 0, 0);
+        }
+    };
+
+    const int nfull = a.S >> 1;   // pairs of two real slices
+    const bool odd = (a.S & 1) != 0;
+    Frags f0, f1;
+    fetch(f0, 0);
+    int t = 0;
+    for (; t + 2 <= nfull; t += 2) {
+        fetch(f1, t + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f0, ~0u);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(f0, t + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f1, ~0u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Left: f0 = pair t.
+    if (t < nfull) {
+        if (odd) fetch(f1, t + 1);
+        mma(f0, ~0u);
+        f0 = f1;
+    }
+    // The last slice's zero partner: lanes 32-63 zero their B slice.
+    if (odd) mma(f0, hl ? 0u : ~0u);
+
+    // Output: lane holds pixel l32 of each block and channels
+    // 8*(r/4) + 4*hl + r%4 of each 32-channel block.
+    const int64_t plane = (int64_t)Ho * Wo;
+    const __amdgpu_buffer_rsrc_t yb = tbuf(y, a.ybytes);
+    const bool all_co = co0 + kCoT <= Co;
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+        const int64_t q = q0 + (wave * kNB + b) * 32 + l32;
+        const int gr = (int)(q / Wo);
+        const int wo = (int)(q - (int64_t)gr * Wo);
+        const int n = (int)a.divHo.div((uint32_t)gr), ho = gr - n * Ho;
+        const uint32_t vo =
+            (uint32_t)((((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo) * 4);
+        if (q >= qend) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int cu = co0 + i * 32 + 8 * (r >> 2) + (r & 3);   // co - 4*hl
+                if (all_co || cu + 4 * hl < Co)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][b][r]), yb, (int)vo,
+                                                          (int)(cu * plane * 4), 0);
+            }
+    }
+}
+
+int env_int(const char* name, int dflt)
+{
+    const char* v = std::getenv(name);
+    return v && *v ? std::atoi(v) : dflt;
+}
+
+// Plans a launch; false if the shape is outside the kernel's envelope:
+// fewer than 8 input channels, Ci*Hf <= 64 filter slices, Wf <= 8, an even
+// column stride, LDS for the tile, tensors addressable with 32-bit buffer
+// offsets. IM2WIN_F16_THIN=0 turns the kernel off (tuning and tests).
+bool plan(const ConvShape& c, ThinArgs& a)
+{
+    if (env_int("IM2WIN_F16_THIN", 1) == 0) return false;
+    if (c.Ci >= 8 || c.Wf > 8 || c.sw % 2 != 0 || c.Hf * c.Wf > 256) return false;
+    a.c = c;
+    a.S = c.Ci * c.Hf;
+    if (a.S > kMaxSlices) return false;
+    a.Sp = (a.S + 1) & ~1;
+    a.total = (int64_t)c.N * c.Ho * c.Wo;
+    a.dup = std::max(0, c.Hf - c.sh);
+    if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
+    const int64_t plane = (int64_t)c.Ho * c.Wo;
+    a.rows_max = (int)std::min<int64_t>((kP - 1) / c.Wo + 2, (int64_t)c.N * c.Ho);
+    a.tiles_per_image = (plane + kP - 1) / kP;
+    a.aligned = (double)(a.tiles_per_image * kP) <= 1.05 * (double)plane;
+    a.kmax = a.aligned || a.rows_max <= 1 ? 0 : std::min(c.N - 1, ceil_div(a.rows_max - 1, c.Ho));
+    a.RIN = (a.rows_max - 1) * c.sh + c.Hf + a.kmax * a.dup;
+    a.RP = ((std::max(c.Wi, (c.Wo - 1) * c.sw + 8) + 7) / 8) * 8;
+    a.CH = a.RP / 8;
+    const int64_t chunks = (int64_t)c.Ci * a.RIN * a.CH;
+    a.KT = (a.Sp + 8 + 3) & ~3;
+    a.xoff = (uint32_t)a.Sp * 1024;
+    const int64_t tab = a.xoff + chunks * 16;
+    const int64_t lds = tab + (a.KT * 4 + 15) / 16 * 16 + kSlackT;
+    if (lds > kThinLds) return false;
+    a.chunks = (int)chunks;
+    a.tab = (uint32_t)tab;
+    a.lds_bytes = (uint32_t)lds;
+    a.Copad = ceil_div(c.Co, kCoT) * kCoT;
+    a.co_tiles = a.Copad / kCoT;
+    a.px_tiles = a.aligned ? (int64_t)c.N * a.tiles_per_image : (a.total + kP - 1) / kP;
+    if (a.px_tiles * a.co_tiles > 0x7fffffff) return false;
+    const int64_t xb = (int64_t)c.N * c.Ci * c.Hi * c.Wi * 2;
+    const int64_t yb = (int64_t)c.N * c.Co * c.Ho * c.Wo * 4;
+    const int64_t wb = (int64_t)a.S * a.Copad * 16;
+    if (xb >= (int64_t)kMissT - 16 || yb >= (int64_t)kMissT || wb >= (int64_t)kMissT) return false;
+    a.xbytes = (uint32_t)xb;
+    a.ybytes = (uint32_t)yb;
+    a.wbytes = (uint32_t)wb;
+    for (int d = 0; d < 4; ++d) {
+        uint32_t m = 0;
+        if (2 * d < c.Wf) m |= 0xFFFFu;
+        if (2 * d + 1 < c.Wf) m |= 0xFFFF0000u;
+        a.mask[d] = m;
+    }
+    a.divWo = FastDiv((uint32_t)c.Wo);
+    a.divHo = FastDiv((uint32_t)c.Ho);
+    a.divCH = FastDiv((uint32_t)a.CH);
+    a.divRIN = FastDiv((uint32_t)a.RIN);
+    return true;
+}
+
+template <bool XVEC, bool M3>
+int launch_t(const uint16_t* x, const uint4* wp, float* y, const ThinArgs& a, hipStream_t stream)
+{
+    static bool attr = false;
+    if (!attr) {
+        // On failure the launch below reports any limit it exceeds.
+        if (hipFuncSetAttribute((const void*)conv_f16_thin_kernel<XVEC, M3>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kThinLds) != hipSuccess)
+            (void)hipGetLastError();
+        attr = true;
+    }
+    hipLaunchKernelGGL((conv_f16_thin_kernel<XVEC, M3>), dim3((unsigned)(a.px_tiles * a.co_tiles)),
+                       dim3(kNT), a.lds_bytes, stream, x, wp, y, a);
+    return launch_status();
+}
+
+}  // namespace
+
+bool f16_thin_applies(const ConvShape& c)
+{
+    ThinArgs a;
+    return plan(c, a);
+}
+
+int launch_conv_f16_thin(const uint16_t* x, const void* wp, float* y, const ConvShape& c,
+                         hipStream_t stream)
+{
+    ThinArgs a;
+    if (!plan(c, a)) return -1;
+    if ((uintptr_t)wp % 16 != 0) return -1;
+    const uint4* w4 = static_cast<const uint4*>(wp);
+    const bool xvec = c.Wi % 8 == 0 && (uintptr_t)x % 16 == 0;
+    const bool m3 = c.Wf >= 6;
+    if (xvec) return m3 ? launch_t<true, true>(x, w4, y, a, stream)
+                        : launch_t<true, false>(x, w4, y, a, stream);
+    return m3 ? launch_t<false, true>(x, w4, y, a, stream)
+              : launch_t<false, false>(x, w4, y, a, stream);
+}
+
+}  // namespace im2win

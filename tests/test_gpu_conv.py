@@ -242,9 +242,12 @@ def test_conv_f32_matrix_waves(t, nw, orc, monkeypatch):
                                (1, 16, 22, 19, 40, 5, 2, 1)], ids=str)
 def test_conv_f16_fused_tilings(t, env, orc, monkeypatch):
     """The fused fp16 kernel with forced waves along pixels and filter stages
-    per channel group, with and without the prepacked filter."""
+    per channel group, with and without the prepacked filter (the thin-layer
+    and wide-tile kernels switched off, so the prepacked calls reach it)."""
     for k, v in env.items():
         monkeypatch.setenv(k, v)
+    monkeypatch.setenv("IM2WIN_F16_THIN", "0")
+    monkeypatch.setenv("IM2WIN_F16_WIDE", "0")
     sh = _shape(t, "f16")
     x, w = workloads.make_inputs(sh, seed=22)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
@@ -282,9 +285,13 @@ def test_conv_f16_row_staged(t, nwv, orc, monkeypatch):
     monkeypatch.setenv("IM2WIN_F16_ROWS_NWV", nwv)
     sh = _shape(t, "f16")
     on = _filter_bytes(sh)
+    # Off, thin layers would take the thin-layer kernel, which packs the
+    # filter the same way; with both off the layout differs.
     monkeypatch.setenv("IM2WIN_F16_ROWS", "0")
+    monkeypatch.setenv("IM2WIN_F16_THIN", "0")
     off = _filter_bytes(sh)
     monkeypatch.setenv("IM2WIN_F16_ROWS", "1")
+    monkeypatch.delenv("IM2WIN_F16_THIN")
     assert on == sh.Ci * sh.Hf * ((sh.Co + 63) // 64 * 64) * 16 and on != off, (on, off)
     x, w = workloads.make_inputs(sh, seed=40)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
@@ -430,3 +437,89 @@ def test_conv_f16_filter_pack_tap_counts(t, orc):
     xi, wi = workloads.make_inputs(sh, seed=53, mode="int")
     note(f"conv fp16 filter pack taps={sh.Hf * sh.Wf} {sh.describe()}")
     assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
+
+
+# Shapes the thin-layer fp16 kernel takes with a prepacked filter (Ci < 8,
+# Ci*Hf <= 64, Wf <= 8, even column stride; not taken by the row-staged
+# kernel): odd and even slice counts, odd widths (two-byte row loads) and
+# widths that are multiples of 8 (16-byte row loads), several channel tiles,
+# row strides below and above the filter height, a 1x1 filter, cv3 images.
+THIN = [
+    (2, 3, 47, 45, 37, 7, 7, 2),
+    (3, 3, 35, 64, 64, 7, 7, 2),
+    (2, 1, 30, 31, 70, 5, 3, (1, 2)),
+    (2, 5, 20, 40, 130, 3, 8, 2),
+    (1, 7, 19, 25, 16, 1, 1, 2),
+    (4, 2, 15, 17, 64, 6, 4, (3, 2)),
+    (3, 3, 227, 227, 64, 7, 7, 2),    # cv3 images
+]
+
+
+def _thin_plan(sh):
+    """The thin-layer kernel's envelope, worked out independently of the
+    library: (applies, LDS bytes)."""
+    sh_, sw = sh.s if isinstance(sh.s, tuple) else (sh.s, sh.s)
+    if sh.Ci >= 8 or sh.Wf > 8 or sw % 2 or sh.Hf * sh.Wf > 256 or sh.Ci * sh.Hf > 64:
+        return False, 0
+    S = sh.Ci * sh.Hf
+    Sp = (S + 1) & ~1
+    Ho, Wo = (sh.Hi - sh.Hf) // sh_ + 1, (sh.Wi - sh.Wf) // sw + 1
+    P = 512
+    plane = Ho * Wo
+    rows_max = min((P - 1) // Wo + 2, sh.N * Ho)
+    tpi = -(-plane // P)
+    aligned = tpi * P <= 1.05 * plane
+    kmax = 0 if aligned or rows_max <= 1 else min(sh.N - 1, -(-(rows_max - 1) // Ho))
+    rin = (rows_max - 1) * sh_ + sh.Hf + kmax * max(0, sh.Hf - sh_)
+    rp = -(-max(sh.Wi, (Wo - 1) * sw + 8) // 8) * 8
+    kt = (Sp + 8 + 3) & ~3
+    lds = Sp * 1024 + sh.Ci * rin * (rp // 8) * 16 + (kt * 4 + 15) // 16 * 16 + 2048
+    return lds <= 160 * 1024, lds
+
+
+@pytest.mark.parametrize("t", THIN, ids=str)
+def test_conv_f16_thin_layers(t, orc, monkeypatch):
+    """The fp16 kernel that keeps a thin layer's whole filter in LDS as
+    (channel, filter row) slices: uniform and integer inputs, and the same
+    exact results as the kernel it replaces (IM2WIN_F16_THIN=0)."""
+    sh = _shape(t, "f16")
+    ok, lds = _thin_plan(sh)
+    assert ok, lds
+    on = _filter_bytes(sh)
+    assert on == sh.Ci * sh.Hf * ((sh.Co + 63) // 64 * 64) * 16, on
+    x, w = workloads.make_inputs(sh, seed=60)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    note(f"conv fp16 thin {sh.describe()} (LDS {lds} B)")
+    assert_within(_run(sh, "f16", x, w, "filter"), ref, absd, TOL["f16"], sh.describe())
+    xi, wi = workloads.make_inputs(sh, seed=61, mode="int")
+    yi = _run(sh, "f16", xi, wi, "filter")
+    assert_exact(yi, orc.conv_direct(xi, wi, sh.s), sh.describe())
+    monkeypatch.setenv("IM2WIN_F16_THIN", "0")
+    assert _filter_bytes(sh) != on
+    assert_exact(_run(sh, "f16", xi, wi, "filter"), yi, "kernel without the thin path")
+
+
+@pytest.mark.parametrize("t", [(2, 3, 15, 17, 40, 7, 7, 2), (2, 2, 14, 17, 40, 3, 5, 2)], ids=str)
+def test_conv_f16_thin_special_values(t, orc):
+    """Infinities and NaN reach exactly the outputs whose windows hold them:
+    padded taps (kw >= Wf) and the zero partner of an odd slice count never
+    multiply one."""
+    sh = _shape(t, "f16")
+    assert _thin_plan(sh)[0]
+    x, w = workloads.make_inputs(sh, seed=62)
+    x[0, 1, 4, 5] = np.inf
+    x[0, 0, 7, 13] = -np.inf
+    x[1, 1, 0, 6] = np.nan
+    x[1, 0, 13, 15] = np.inf
+    x[0, 0, 2, 7] = np.inf
+    w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
+    ref = orc.conv_direct(x, w, sh.s)
+    note(f"conv fp16 thin special values {sh.describe()}")
+    y = _run(sh, "f16", x, w, "filter").astype(np.float64)
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
+                              with_absdot=True)
+    assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")

@@ -110,6 +110,9 @@ def test_conv_strided_f32_matrix_waves(t, nw, orc, monkeypatch):
 def test_conv_strided_f16_fused_tilings(t, env, orc, monkeypatch):
     for k, v in env.items():
         monkeypatch.setenv(k, v)
+    # The prepacked calls reach the channel-interleaved kernel.
+    monkeypatch.setenv("IM2WIN_F16_THIN", "0")
+    monkeypatch.setenv("IM2WIN_F16_WIDE", "0")
     sh = _shape(t, "f16")
     xi, wi = workloads.make_inputs(sh, seed=36, mode="int")
     refi = orc.conv_direct(xi, wi, sh.s)
