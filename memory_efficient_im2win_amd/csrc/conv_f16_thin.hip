@@ -19,11 +19,13 @@
 //    these pad 7 taps to 8.
 //  * The whole contraction is one stage: a workgroup copies the filter
 //    slices of its 64 output channels (direct global-to-LDS loads) and the
-//    input rows of its 512 pixels, for every input channel (through
-//    registers, so rows of any width and alignment are taken), then runs
-//    all the MFMAs and stores. Four waves each hold a 2 x 4 tile of 32 x 32
-//    accumulators (64 channels x 128 pixels); two workgroups share a CU, so
-//    one's loads and stores overlap the other's MFMAs.
+//    input rows of its pixels, for every input channel (through registers,
+//    so rows of any width and alignment are taken), then runs all the MFMAs
+//    and stores. Four waves each hold a 2 x NB tile of 32 x 32 accumulators
+//    (64 channels x 32*NB pixels). With NB = 2 (256-pixel tiles, the
+//    default) up to four workgroups share a CU, so some load or store while
+//    others run MFMAs; the layer is bound by its fp32 output, not by the
+//    matrix cores.
 //  * An odd slice count gets a zero partner slice: its filter entries are
 //    written as zeros and lanes 32-63 zero their B slice, and taps kw >= Wf
 //    are zero in the filter and masked in B, so an infinity next to a window
@@ -40,10 +42,8 @@ namespace {
 
 constexpr int kThinLds = 160 * 1024;
 constexpr int kCoT = 64;                  // output channels per tile
-constexpr int kNB = 4;                    // 32-pixel blocks per wave
 constexpr int kNW = 4;                    // waves per workgroup
 constexpr int kNT = 64 * kNW;
-constexpr int kP = 32 * kNB * kNW;        // pixels per tile
 constexpr int kMaxSlices = 64;            // filter slices (c, kh) held in LDS
 constexpr int kBatch = 8;                 // row chunks a thread has in flight
 constexpr int kSlackT = 2048;             // A reads run one pair past the filter
@@ -51,6 +51,7 @@ constexpr uint32_t kMissT = 0xFFFFFFF0u;  // vector offset past every accepted b
 
 struct ThinArgs {
     ConvShape c;
+    int P;                          // pixels per tile: 32 * NB * kNW
     int co_tiles;
     int64_t px_tiles, total, tiles_per_image;
     bool aligned;                   // tiles never cross images
@@ -87,14 +88,16 @@ __device__ __forceinline__ void dma16t(__amdgpu_buffer_rsrc_t r, uint32_t lds, u
         : "memory");
 }
 
-// XVEC: Wi % 8 == 0 and x 16-byte aligned, so a row chunk is one 16-byte
-// load; otherwise 8 two-byte loads. M3: Wf >= 6, only the last B dword
-// holds padded taps.
-template <bool XVEC, bool M3>
-__global__ __launch_bounds__(kNT, 2) void conv_f16_thin_kernel(const uint16_t* __restrict__ x,
+// NB: 32-pixel blocks per wave (2 x NB register tiles; NB = 2 leaves room
+// for four workgroups per CU, NB = 4 for two). XVEC: Wi % 8 == 0 and x
+// 16-byte aligned, so a row chunk is one 16-byte load; otherwise 8 two-byte
+// loads. M3: Wf >= 6, only the last B dword holds padded taps.
+template <int NB, bool XVEC, bool M3>
+__global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16_t* __restrict__ x,
                                                                const uint4* __restrict__ wp,
                                                                float* __restrict__ y, ThinArgs a)
 {
+    constexpr int kNB = NB, kP = 32 * NB * kNW;
     extern __shared__ __align__(16) unsigned char smem[];
     const uint32_t lbase =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
@@ -337,7 +340,8 @@ int env_int(const char* name, int dflt)
 // Plans a launch; false if the shape is outside the kernel's envelope:
 // fewer than 8 input channels, Ci*Hf <= 64 filter slices, Wf <= 8, an even
 // column stride, LDS for the tile, tensors addressable with 32-bit buffer
-// offsets. IM2WIN_F16_THIN=0 turns the kernel off (tuning and tests).
+// offsets. IM2WIN_F16_THIN=0 turns the kernel off and IM2WIN_F16_THIN_NB
+// picks 2 or 4 pixel blocks per wave (tuning and tests).
 bool plan(const ConvShape& c, ThinArgs& a)
 {
     if (env_int("IM2WIN_F16_THIN", 1) == 0) return false;
@@ -350,6 +354,7 @@ bool plan(const ConvShape& c, ThinArgs& a)
     a.dup = std::max(0, c.Hf - c.sh);
     if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
     const int64_t plane = (int64_t)c.Ho * c.Wo;
+    const int kP = a.P = 32 * kNW * (env_int("IM2WIN_F16_THIN_NB", 2) == 4 ? 4 : 2);
     a.rows_max = (int)std::min<int64_t>((kP - 1) / c.Wo + 2, (int64_t)c.N * c.Ho);
     a.tiles_per_image = (plane + kP - 1) / kP;
     a.aligned = (double)(a.tiles_per_image * kP) <= 1.05 * (double)plane;
@@ -390,20 +395,32 @@ bool plan(const ConvShape& c, ThinArgs& a)
     return true;
 }
 
-template <bool XVEC, bool M3>
+template <int NB, bool XVEC, bool M3>
 int launch_t(const uint16_t* x, const uint4* wp, float* y, const ThinArgs& a, hipStream_t stream)
 {
     static bool attr = false;
     if (!attr) {
         // On failure the launch below reports any limit it exceeds.
-        if (hipFuncSetAttribute((const void*)conv_f16_thin_kernel<XVEC, M3>,
+        if (hipFuncSetAttribute((const void*)conv_f16_thin_kernel<NB, XVEC, M3>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kThinLds) != hipSuccess)
             (void)hipGetLastError();
         attr = true;
     }
-    hipLaunchKernelGGL((conv_f16_thin_kernel<XVEC, M3>), dim3((unsigned)(a.px_tiles * a.co_tiles)),
-                       dim3(kNT), a.lds_bytes, stream, x, wp, y, a);
+    hipLaunchKernelGGL((conv_f16_thin_kernel<NB, XVEC, M3>),
+                       dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(kNT), a.lds_bytes, stream, x,
+                       wp, y, a);
     return launch_status();
+}
+
+template <int NB>
+int launch_nb(const uint16_t* x, const uint4* wp, float* y, const ThinArgs& a, bool xvec,
+              hipStream_t stream)
+{
+    const bool m3 = a.c.Wf >= 6;
+    if (xvec) return m3 ? launch_t<NB, true, true>(x, wp, y, a, stream)
+                        : launch_t<NB, true, false>(x, wp, y, a, stream);
+    return m3 ? launch_t<NB, false, true>(x, wp, y, a, stream)
+              : launch_t<NB, false, false>(x, wp, y, a, stream);
 }
 
 }  // namespace
@@ -422,11 +439,8 @@ int launch_conv_f16_thin(const uint16_t* x, const void* wp, float* y, const Conv
     if ((uintptr_t)wp % 16 != 0) return -1;
     const uint4* w4 = static_cast<const uint4*>(wp);
     const bool xvec = c.Wi % 8 == 0 && (uintptr_t)x % 16 == 0;
-    const bool m3 = c.Wf >= 6;
-    if (xvec) return m3 ? launch_t<true, true>(x, w4, y, a, stream)
-                        : launch_t<true, false>(x, w4, y, a, stream);
-    return m3 ? launch_t<false, true>(x, w4, y, a, stream)
-              : launch_t<false, false>(x, w4, y, a, stream);
+    return a.P == 32 * kNW * 2 ? launch_nb<2>(x, w4, y, a, xvec, stream)
+                               : launch_nb<4>(x, w4, y, a, xvec, stream);
 }
 
 }  // namespace im2win

@@ -455,16 +455,15 @@ THIN = [
 ]
 
 
-def _thin_plan(sh):
-    """The thin-layer kernel's envelope, worked out independently of the
-    library: (applies, LDS bytes)."""
+def _thin_plan(sh, P=512):
+    """The thin-layer kernel's envelope for tiles of P pixels, worked out
+    independently of the library: (applies, LDS bytes)."""
     sh_, sw = sh.s if isinstance(sh.s, tuple) else (sh.s, sh.s)
     if sh.Ci >= 8 or sh.Wf > 8 or sw % 2 or sh.Hf * sh.Wf > 256 or sh.Ci * sh.Hf > 64:
         return False, 0
     S = sh.Ci * sh.Hf
     Sp = (S + 1) & ~1
     Ho, Wo = (sh.Hi - sh.Hf) // sh_ + 1, (sh.Wi - sh.Wf) // sw + 1
-    P = 512
     plane = Ho * Wo
     rows_max = min((P - 1) // Wo + 2, sh.N * Ho)
     tpi = -(-plane // P)
@@ -477,13 +476,16 @@ def _thin_plan(sh):
     return lds <= 160 * 1024, lds
 
 
+@pytest.mark.parametrize("nb", ["4", "2"])
 @pytest.mark.parametrize("t", THIN, ids=str)
-def test_conv_f16_thin_layers(t, orc, monkeypatch):
+def test_conv_f16_thin_layers(t, nb, orc, monkeypatch):
     """The fp16 kernel that keeps a thin layer's whole filter in LDS as
-    (channel, filter row) slices: uniform and integer inputs, and the same
-    exact results as the kernel it replaces (IM2WIN_F16_THIN=0)."""
+    (channel, filter row) slices, with 4 and 2 pixel blocks per wave: uniform
+    and integer inputs, and the same exact results as the kernel it replaces
+    (IM2WIN_F16_THIN=0)."""
+    monkeypatch.setenv("IM2WIN_F16_THIN_NB", nb)
     sh = _shape(t, "f16")
-    ok, lds = _thin_plan(sh)
+    ok, lds = _thin_plan(sh, 32 * 4 * int(nb))
     assert ok, lds
     on = _filter_bytes(sh)
     assert on == sh.Ci * sh.Hf * ((sh.Co + 63) // 64 * 64) * 16, on
