@@ -293,6 +293,8 @@ ABLATION = {
             ("prepacked, row-staged kernel with 4 waves", "prepacked", {"IM2WIN_F16_ROWS_NWV": "4"}),
             ("prepacked, row-staged, tiles in launch order", "prepacked",
              {"IM2WIN_F16_ROWS_SWIZZLE": "0"}),
+            ("prepacked, thin-layer kernel with 512-pixel tiles", "prepacked",
+             {"IM2WIN_F16_THIN_NB": "4"}),
             ("prepacked, wide-tile kernel with 4 waves of 4 x 4 blocks", "prepacked",
              {"IM2WIN_F16_WIDE_NW": "4"}),
             ("prepacked, channel-interleaved kernel", "prepacked",

@@ -352,6 +352,8 @@ WIDE = [
     (2, 8, 32, 36, 128, 3, 3, 1),       # tiles aligned to images
     (2, 8, 12, 40, 200, 1, 1, 1),
     (2, 24, 14, 14, 96, 5, 5, 1),       # Co < 128 (forced)
+    (1, 16, 20, 20, 384, 3, 3, 1),      # one image, three channel tiles
+    (3, 9, 5, 64, 128, 5, 3, 1),        # one output row per image
 ]
 
 
@@ -452,6 +454,8 @@ THIN = [
     (1, 7, 19, 25, 16, 1, 1, 2),
     (4, 2, 15, 17, 64, 6, 4, (3, 2)),
     (3, 3, 227, 227, 64, 7, 7, 2),    # cv3 images
+    (1, 3, 7, 40, 64, 7, 7, 2),       # one output row
+    (5, 4, 9, 9, 200, 9, 8, 2),       # filter covers the input height: one output per image
 ]
 
 
