@@ -117,8 +117,10 @@ def conv2d(x, w, stride=1, ws=None, ws_bytes: int | None = None, out=None):
     """Forward convolution (cross-correlation, no padding) of x (N,Ci,Hi,Wi)
     with w (Co,Ci,Hf,Wf); fp32 output (N,Co,Ho,Wo).
 
-    float32 inputs run on the vector ALUs, float16 inputs on the matrix cores
-    (fp32 accumulation). Without ``ws`` the im2win rows are built in LDS
+    float32 inputs run on the fp32 matrix instructions (the vector-ALU kernel
+    with IM2WIN_F32_PATH=valu), float16 inputs on the fp16 matrix
+    instructions with fp32 accumulation. Without ``ws`` the im2win rows are
+    built in LDS
     (fused). With ``ws`` (a device tensor; see conv_workspace_bytes) the
     fp16 filter is prepacked into its head, and if the rest holds at least
     one image's im2win tensor that tensor is materialised, in chunks of as

@@ -529,3 +529,29 @@ def test_conv_f16_thin_special_values(t, orc):
     _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
                               with_absdot=True)
     assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
+
+
+@pytest.mark.parametrize("t", [(2, 24, 14, 14, 96, 5, 5, 1), (2, 16, 14, 14, 128, 5, 5, 1),
+                               (2, 3, 47, 45, 37, 7, 7, 2), (3, 3, 35, 64, 64, 7, 7, 2),
+                               (1, 64, 40, 40, 64, 7, 7, 2), (2, 9, 13, 21, 40, 3, 3, 1)],
+                         ids=str)
+def test_conv_f16_input_at_odd_element_offset(t, orc):
+    """An fp16 input that starts 2 bytes past a 4-byte boundary (a view at an
+    odd element offset) gives the exact results with every kernel a call can
+    reach: fused, prepacked (channel-interleaved, wide-tile, thin-layer,
+    row-staged) and materialised."""
+    import torch
+    dev = device()
+    sh = _shape(t, "f16")
+    xi, wi = workloads.make_inputs(sh, seed=63, mode="int")
+    ref = orc.conv_direct(xi, wi, sh.s)
+    big = torch.zeros(xi.size + 1, dtype=torch.float16, device=dev)
+    big[1:] = torch.from_numpy(np.ascontiguousarray(xi).reshape(-1)).to(dev)
+    xv = big[1:].view(xi.shape)
+    assert xv.data_ptr() % 4 == 2
+    wt = to_dev(wi, dev)
+    for kind in (None, "filter", "full"):
+        note(f"conv fp16 input at odd offset {sh.describe()} ws={kind}")
+        y = m.conv2d(xv, wt, sh.s, ws=_ws(sh, kind, dev)).cpu().numpy()
+        assert_exact(y, ref, f"{sh.describe()} ws={kind}")
+    torch.cuda.synchronize()
