@@ -62,7 +62,7 @@ struct ThinArgs {
     int chunks;                     // row chunks of a tile: Ci * RIN * CH
     int KT;                         // entries of the slice offset table
     uint32_t xoff, tab, lds_bytes;  // LDS byte offsets of the rows and the table; total
-    uint32_t xbytes, ybytes, wbytes;
+    uint32_t xbytes, ybytes, wbytes, worig;   // x, y, prepacked filter, filter in w's layout
     uint32_t mask[4];               // B dwords: halves kw >= Wf cleared
     FastDiv divWo, divHo, divCH, divRIN;
 };
@@ -91,10 +91,13 @@ __device__ __forceinline__ void dma16t(__amdgpu_buffer_rsrc_t r, uint32_t lds, u
 // NB: 32-pixel blocks per wave (2 x NB register tiles; NB = 2 leaves room
 // for four workgroups per CU, NB = 4 for two). XVEC: Wi % 8 == 0 and x
 // 16-byte aligned, so a row chunk is one 16-byte load; otherwise 8 two-byte
-// loads. M3: Wf >= 6, only the last B dword holds padded taps.
-template <int NB, bool XVEC, bool M3>
+// loads. M3: Wf >= 6, only the last B dword holds padded taps. WPK: the
+// filter comes prepacked (wp); otherwise each workgroup gathers its slices
+// from w.
+template <int NB, bool XVEC, bool M3, bool WPK>
 __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16_t* __restrict__ x,
                                                                const uint4* __restrict__ wp,
+                                                               const uint16_t* __restrict__ w,
                                                                float* __restrict__ y, ThinArgs a)
 {
     constexpr int kNB = NB, kP = 32 * NB * kNW;
@@ -162,14 +165,43 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
     };
 
     // Filter: kilobyte m of LDS = slice m (c, kh) for the tile's 64 channels,
-    // entries (m*Copad + co0 + lane) of the prepacked filter.
-    {
+    // entry m*64 + j = taps kw 0..7 of w[co0 + j][c][kh][*] (zeros past Wf
+    // and Co): from the prepacked filter, entries m*Copad + co0 + j, or
+    // gathered from w, whose taps of slice m of channel co start at element
+    // (co*Ci*Hf + m)*Wf.
+    if (WPK) {
         const __amdgpu_buffer_rsrc_t r = tbuf(wp, a.wbytes);
         for (int m = wave; m < a.S; m += kNW)
             dma16t(r, lbase + (uint32_t)m * 1024, (uint32_t)((m * a.Copad + co0 + lane) * 16));
-        if (a.Sp > a.S && wave == kNW - 1)
-            reinterpret_cast<uint4*>(smem)[a.S * 64 + lane] = make_uint4(0, 0, 0, 0);
+    } else {
+        const __amdgpu_buffer_rsrc_t r = tbuf(w, a.worig);
+        uint4* F = reinterpret_cast<uint4*>(smem);
+        const int ne = a.S * 64;
+        for (int e0 = 0; e0 < ne; e0 += 4 * kNT) {
+            uint32_t hv[4][8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int e = e0 + k * kNT + tid;
+                const int m = e >> 6, co = co0 + (e & 63);
+                const uint32_t src = e < ne && co < Co
+                                         ? (uint32_t)((co * Ci * Hf + m) * a.c.Wf * 2)
+                                         : kMissT;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    hv[k][q] = __builtin_amdgcn_raw_buffer_load_b16(
+                        r, (int)(q < a.c.Wf ? src + 2 * q : kMissT), 0, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int e = e0 + k * kNT + tid;
+                if (e < ne)
+                    F[e] = make_uint4(hv[k][0] | (hv[k][1] << 16), hv[k][2] | (hv[k][3] << 16),
+                                      hv[k][4] | (hv[k][5] << 16), hv[k][6] | (hv[k][7] << 16));
+            }
+        }
     }
+    if (a.Sp > a.S && wave == kNW - 1)
+        reinterpret_cast<uint4*>(smem)[a.S * 64 + lane] = make_uint4(0, 0, 0, 0);
     // Slice s = (c, kh) starts (c*RIN + kh) rows into the rows; entries from
     // S on point at row 0 (their reads are unused or zeroed).
     int* T = reinterpret_cast<int*>(smem + a.tab);
@@ -378,7 +410,11 @@ bool plan(const ConvShape& c, ThinArgs& a)
     const int64_t xb = (int64_t)c.N * c.Ci * c.Hi * c.Wi * 2;
     const int64_t yb = (int64_t)c.N * c.Co * c.Ho * c.Wo * 4;
     const int64_t wb = (int64_t)a.S * a.Copad * 16;
-    if (xb >= (int64_t)kMissT - 16 || yb >= (int64_t)kMissT || wb >= (int64_t)kMissT) return false;
+    const int64_t wo = (int64_t)c.Co * c.Ci * c.Hf * c.Wf * 2;
+    if (xb >= (int64_t)kMissT - 16 || yb >= (int64_t)kMissT || wb >= (int64_t)kMissT ||
+        wo >= 0x7fffffff)
+        return false;
+    a.worig = (uint32_t)wo;
     a.xbytes = (uint32_t)xb;
     a.ybytes = (uint32_t)yb;
     a.wbytes = (uint32_t)wb;
@@ -395,32 +431,33 @@ bool plan(const ConvShape& c, ThinArgs& a)
     return true;
 }
 
-template <int NB, bool XVEC, bool M3>
-int launch_t(const uint16_t* x, const uint4* wp, float* y, const ThinArgs& a, hipStream_t stream)
+template <int NB, bool XVEC, bool M3, bool WPK>
+int launch_t(const uint16_t* x, const uint4* wp, const uint16_t* w, float* y, const ThinArgs& a,
+             hipStream_t stream)
 {
     static bool attr = false;
     if (!attr) {
         // On failure the launch below reports any limit it exceeds.
-        if (hipFuncSetAttribute((const void*)conv_f16_thin_kernel<NB, XVEC, M3>,
+        if (hipFuncSetAttribute((const void*)conv_f16_thin_kernel<NB, XVEC, M3, WPK>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kThinLds) != hipSuccess)
             (void)hipGetLastError();
         attr = true;
     }
-    hipLaunchKernelGGL((conv_f16_thin_kernel<NB, XVEC, M3>),
+    hipLaunchKernelGGL((conv_f16_thin_kernel<NB, XVEC, M3, WPK>),
                        dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(kNT), a.lds_bytes, stream, x,
-                       wp, y, a);
+                       wp, w, y, a);
     return launch_status();
 }
 
-template <int NB>
-int launch_nb(const uint16_t* x, const uint4* wp, float* y, const ThinArgs& a, bool xvec,
-              hipStream_t stream)
+template <int NB, bool WPK>
+int launch_nb(const uint16_t* x, const uint4* wp, const uint16_t* w, float* y, const ThinArgs& a,
+              bool xvec, hipStream_t stream)
 {
     const bool m3 = a.c.Wf >= 6;
-    if (xvec) return m3 ? launch_t<NB, true, true>(x, wp, y, a, stream)
-                        : launch_t<NB, true, false>(x, wp, y, a, stream);
-    return m3 ? launch_t<NB, false, true>(x, wp, y, a, stream)
-              : launch_t<NB, false, false>(x, wp, y, a, stream);
+    if (xvec) return m3 ? launch_t<NB, true, true, WPK>(x, wp, w, y, a, stream)
+                        : launch_t<NB, true, false, WPK>(x, wp, w, y, a, stream);
+    return m3 ? launch_t<NB, false, true, WPK>(x, wp, w, y, a, stream)
+              : launch_t<NB, false, false, WPK>(x, wp, w, y, a, stream);
 }
 
 }  // namespace
@@ -431,16 +468,19 @@ bool f16_thin_applies(const ConvShape& c)
     return plan(c, a);
 }
 
-int launch_conv_f16_thin(const uint16_t* x, const void* wp, float* y, const ConvShape& c,
-                         hipStream_t stream)
+int launch_conv_f16_thin(const uint16_t* x, const void* wp, const uint16_t* w, float* y,
+                         const ConvShape& c, hipStream_t stream)
 {
     ThinArgs a;
     if (!plan(c, a)) return -1;
     if ((uintptr_t)wp % 16 != 0) return -1;
     const uint4* w4 = static_cast<const uint4*>(wp);
     const bool xvec = c.Wi % 8 == 0 && (uintptr_t)x % 16 == 0;
-    return a.P == 32 * kNW * 2 ? launch_nb<2>(x, w4, y, a, xvec, stream)
-                               : launch_nb<4>(x, w4, y, a, xvec, stream);
+    const bool nb2 = a.P == 32 * kNW * 2;
+    if (w4) return nb2 ? launch_nb<2, true>(x, w4, w, y, a, xvec, stream)
+                       : launch_nb<4, true>(x, w4, w, y, a, xvec, stream);
+    return nb2 ? launch_nb<2, false>(x, w4, w, y, a, xvec, stream)
+               : launch_nb<4, false>(x, w4, w, y, a, xvec, stream);
 }
 
 }  // namespace im2win

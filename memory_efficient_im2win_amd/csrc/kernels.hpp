@@ -66,12 +66,12 @@ int launch_f16_slices_filter_pack(const uint16_t* w, void* wp, const ConvShape& 
 
 // fp16 convolution for thin layers (few input channels: the whole filter
 // stays in LDS as slices (c, kh) of 8 taps), reading the filter packed by
-// launch_f16_slices_filter_pack. Used by launch_conv_f16_fused, with a
-// prepacked filter, for the shapes it takes (f16_thin_applies) that the
-// row-staged kernel does not.
+// launch_f16_slices_filter_pack (wp), or gathering it from w when wp is
+// nullptr. Used by launch_conv_f16_fused for the shapes it takes
+// (f16_thin_applies) that the row-staged kernel does not.
 bool f16_thin_applies(const ConvShape& c);
-int launch_conv_f16_thin(const uint16_t* x, const void* wp, float* y, const ConvShape& c,
-                         hipStream_t stream);
+int launch_conv_f16_thin(const uint16_t* x, const void* wp, const uint16_t* w, float* y,
+                         const ConvShape& c, hipStream_t stream);
 
 // fp16 convolution for layers with many output channels (128-channel x
 // 128-pixel register tiles per wave), reading the filter prepacked by

@@ -484,8 +484,9 @@ def _thin_plan(sh, P=512):
 @pytest.mark.parametrize("t", THIN, ids=str)
 def test_conv_f16_thin_layers(t, nb, orc, monkeypatch):
     """The fp16 kernel that keeps a thin layer's whole filter in LDS as
-    (channel, filter row) slices, with 4 and 2 pixel blocks per wave: uniform
-    and integer inputs, and the same exact results as the kernel it replaces
+    (channel, filter row) slices, with 4 and 2 pixel blocks per wave, the
+    filter prepacked or gathered in the kernel (no workspace): uniform and
+    integer inputs, and the same exact results as the kernels it replaces
     (IM2WIN_F16_THIN=0)."""
     monkeypatch.setenv("IM2WIN_F16_THIN_NB", nb)
     sh = _shape(t, "f16")
@@ -495,14 +496,18 @@ def test_conv_f16_thin_layers(t, nb, orc, monkeypatch):
     assert on == sh.Ci * sh.Hf * ((sh.Co + 63) // 64 * 64) * 16, on
     x, w = workloads.make_inputs(sh, seed=60)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
-    note(f"conv fp16 thin {sh.describe()} (LDS {lds} B)")
-    assert_within(_run(sh, "f16", x, w, "filter"), ref, absd, TOL["f16"], sh.describe())
     xi, wi = workloads.make_inputs(sh, seed=61, mode="int")
-    yi = _run(sh, "f16", xi, wi, "filter")
-    assert_exact(yi, orc.conv_direct(xi, wi, sh.s), sh.describe())
+    refi = orc.conv_direct(xi, wi, sh.s)
+    yi = {}
+    for kind in ("filter", None):
+        note(f"conv fp16 thin {sh.describe()} ws={kind} (LDS {lds} B)")
+        assert_within(_run(sh, "f16", x, w, kind), ref, absd, TOL["f16"], sh.describe())
+        yi[kind] = _run(sh, "f16", xi, wi, kind)
+        assert_exact(yi[kind], refi, sh.describe())
     monkeypatch.setenv("IM2WIN_F16_THIN", "0")
     assert _filter_bytes(sh) != on
-    assert_exact(_run(sh, "f16", xi, wi, "filter"), yi, "kernel without the thin path")
+    for kind in ("filter", None):
+        assert_exact(_run(sh, "f16", xi, wi, kind), yi[kind], "kernels without the thin path")
 
 
 @pytest.mark.parametrize("t", [(2, 3, 15, 17, 40, 7, 7, 2), (2, 2, 14, 17, 40, 3, 5, 2)], ids=str)
@@ -520,15 +525,16 @@ def test_conv_f16_thin_special_values(t, orc):
     x[0, 0, 2, 7] = np.inf
     w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
     ref = orc.conv_direct(x, w, sh.s)
-    note(f"conv fp16 thin special values {sh.describe()}")
-    y = _run(sh, "f16", x, w, "filter").astype(np.float64)
-    assert np.array_equal(np.isnan(y), np.isnan(ref))
-    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
-    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
     fin = np.isfinite(ref)
     _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
                               with_absdot=True)
-    assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
+    for kind in ("filter", None):
+        note(f"conv fp16 thin special values {sh.describe()} ws={kind}")
+        y = _run(sh, "f16", x, w, kind).astype(np.float64)
+        assert np.array_equal(np.isnan(y), np.isnan(ref))
+        assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+        assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+        assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
 
 
 @pytest.mark.parametrize("t", [(2, 24, 14, 14, 96, 5, 5, 1), (2, 16, 14, 14, 128, 5, 5, 1),
