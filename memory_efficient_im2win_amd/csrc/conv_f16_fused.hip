@@ -647,7 +647,8 @@ int launch_w(const uint16_t* x, const uint16_t* w, const uint4* wpk, float* y,
 // (its own filter layout), then shapes the thin-layer kernel takes (the same
 // slice layout), then shapes the wide-tile kernel takes (this layout); the
 // rest run the kernel above. Without one, thin layers run the thin-layer
-// kernel (gathering its filter) and the rest the kernel above.
+// kernel and wide ones the wide-tile kernel (each gathering its filter), the
+// rest the kernel above.
 size_t f16_filter_pack_bytes(const ConvShape& c)
 {
     if (f16_rows_applies(c)) return f16_rows_filter_bytes(c);
@@ -686,7 +687,7 @@ int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk,
 {
     if (wpk && f16_rows_applies(c)) return launch_conv_f16_rows(x, wpk, y, c, stream);
     if (f16_thin_applies(c)) return launch_conv_f16_thin(x, wpk, w, y, c, stream);
-    if (wpk && f16_wide_applies(c, kCoPad)) return launch_conv_f16_wide(x, wpk, y, c, kCoPad, stream);
+    if (f16_wide_applies(c, kCoPad)) return launch_conv_f16_wide(x, wpk, w, y, c, kCoPad, stream);
     FusedArgs a;
     int wco, wpx, nb;
     if (!plan(c, a, wco, wpx, nb)) return -1;

@@ -58,7 +58,7 @@ struct WideArgs {
     uint32_t stage_bytes;           // filter part + input rows
     uint32_t tab;                   // LDS byte offset of the tap table
     uint32_t lds_bytes;
-    uint32_t xbytes, ybytes, wbytes;
+    uint32_t xbytes, ybytes, wbytes, worig;   // x, y, prepacked filter, filter in w's layout
     FastDiv divWo, divHo, divWi, divHalfW, divS;
 };
 
@@ -85,10 +85,12 @@ __device__ __forceinline__ void dma16w(__amdgpu_buffer_rsrc_t r, uint32_t lds, u
         : "memory");
 }
 
-// NW waves of NB 32-pixel blocks each (NW * NB * 32 = kPW).
-template <int NW, int NB, bool XPAIR>
+// NW waves of NB 32-pixel blocks each (NW * NB * 32 = kPW). WPK: the filter
+// comes prepacked (wpk); otherwise each stage gathers its entries from w.
+template <int NW, int NB, bool XPAIR, bool WPK>
 __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* __restrict__ x,
                                                              const uint4* __restrict__ wpk,
+                                                             const uint16_t* __restrict__ w,
                                                              float* __restrict__ y, WideArgs a)
 {
     static_assert(NW * NB * 32 == kPW, "tile width");
@@ -254,6 +256,41 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
             dma16w(r, dst + (uint32_t)m * 1024,
                    lo + (uint32_t)(m >> 1) * a.Copad * 16 + (uint32_t)(m & 1) * 1024);
     };
+    // Without a prepacked filter: half c of entry (tap j, channel co0 + k) is
+    // w[co0 + k][8g + c][j] (zero past HW, Co, Ci). A thread takes the
+    // (k, c) pairs tid, tid + NT, ... and their taps in chunks, written to
+    // LDS as each chunk arrives.
+    auto gather_w = [&](int g, int sb) {
+        constexpr int NPR = 8 * kCoW / kNTW;   // (k, c) pairs per thread
+        constexpr int JC = 32 / NPR;           // taps per chunk
+        const __amdgpu_buffer_rsrc_t r = wbuf(w, a.worig);
+        unsigned short* F = reinterpret_cast<unsigned short*>(smem + (size_t)sb * a.stage_bytes);
+        uint32_t base[NPR];
+        int dst[NPR];
+#pragma unroll
+        for (int p = 0; p < NPR; ++p) {
+            const int pr = tid + p * kNTW, k = pr >> 3, c = pr & 7;
+            const int co = co0 + k, ch = 8 * g + c;
+            base[p] = co < Co && ch < Ci ? (uint32_t)(((int64_t)co * Ci + ch) * HW * 2) : kMissW;
+            dst[p] = k * 8 + c;
+        }
+        for (int j0 = 0; j0 < a.HWp; j0 += JC) {
+            uint32_t v[NPR][JC];
+#pragma unroll
+            for (int p = 0; p < NPR; ++p)
+#pragma unroll
+                for (int q = 0; q < JC; ++q) {
+                    const int j = j0 + q;
+                    v[p][q] = __builtin_amdgcn_raw_buffer_load_b16(
+                        r, (int)(j < HW && base[p] != kMissW ? base[p] + 2 * j : kMissW), 0, 0);
+                }
+#pragma unroll
+            for (int p = 0; p < NPR; ++p)
+#pragma unroll
+                for (int q = 0; q < JC; ++q)
+                    if (j0 + q < a.HWp) F[(j0 + q) * kCoW * 8 + dst[p]] = (unsigned short)v[p][q];
+        }
+    };
 
     // Window offsets of the taps in filter order j = kh*Wf + kw, from the
     // pixel's tap (0, 0): kh*RS + (kw % sw)*NU + kw / sw. Entries from HW on
@@ -309,7 +346,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
     const bool odd = (HW & 1) != 0;
 
     // Stage 0.
-    dma_w(0, 0);
+    if (WPK) dma_w(0, 0); else gather_w(0, 0);
     load_x(0);
     store_x(0);
     __syncthreads();   // the tap table
@@ -330,7 +367,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
         on1 = t1;
         fetch(f0, 0);
         if (g + 1 < a.CG) {
-            dma_w(g + 1, (g + 1) & 1);
+            if (WPK) dma_w(g + 1, (g + 1) & 1);
             load_x(g + 1);
         }
         int t = 0;
@@ -364,7 +401,10 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
             }
             mma(f0);
         }
-        if (g + 1 < a.CG) store_x((g + 1) & 1);
+        if (g + 1 < a.CG) {
+            store_x((g + 1) & 1);
+            if (!WPK) gather_w(g + 1, (g + 1) & 1);
+        }
     }
 
     // Output: lane holds pixel l32 of each block and channels
@@ -442,7 +482,11 @@ bool plan(const ConvShape& c, WideArgs& a, size_t copad_mult)
     const int64_t xb = (int64_t)c.N * c.Ci * c.Hi * c.Wi * 2;
     const int64_t yb = (int64_t)c.N * c.Co * c.Ho * c.Wo * 4;
     const int64_t wb = (int64_t)a.CG * a.HWp * a.Copad * 16;
-    if (xb >= (int64_t)kMissW || yb >= (int64_t)kMissW || wb >= (int64_t)kMissW) return false;
+    const int64_t wo = (int64_t)c.Co * c.Ci * a.HW * 2;
+    if (xb >= (int64_t)kMissW || yb >= (int64_t)kMissW || wb >= (int64_t)kMissW ||
+        wo >= (int64_t)kMissW)
+        return false;
+    a.worig = (uint32_t)wo;
     a.xbytes = (uint32_t)xb;
     a.ybytes = (uint32_t)yb;
     a.wbytes = (uint32_t)wb;
@@ -454,28 +498,30 @@ bool plan(const ConvShape& c, WideArgs& a, size_t copad_mult)
     return true;
 }
 
-template <int NW, int NB, bool XPAIR>
-int launch_t(const uint16_t* x, const uint4* wpk, float* y, const WideArgs& a, hipStream_t stream)
+template <int NW, int NB, bool XPAIR, bool WPK>
+int launch_t(const uint16_t* x, const uint4* wpk, const uint16_t* w, float* y, const WideArgs& a,
+             hipStream_t stream)
 {
     static bool attr = false;
     if (!attr) {
         // On failure the launch below reports any limit it exceeds.
-        if (hipFuncSetAttribute((const void*)conv_f16_wide_kernel<NW, NB, XPAIR>,
+        if (hipFuncSetAttribute((const void*)conv_f16_wide_kernel<NW, NB, XPAIR, WPK>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds) != hipSuccess)
             (void)hipGetLastError();
         attr = true;
     }
-    hipLaunchKernelGGL((conv_f16_wide_kernel<NW, NB, XPAIR>),
+    hipLaunchKernelGGL((conv_f16_wide_kernel<NW, NB, XPAIR, WPK>),
                        dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(64 * NW), a.lds_bytes,
-                       stream, x, wpk, y, a);
+                       stream, x, wpk, w, y, a);
     return launch_status();
 }
 
-template <int NW, int NB>
-int launch_x(const uint16_t* x, const uint4* wpk, float* y, const WideArgs& a, hipStream_t stream)
+template <int NW, int NB, bool WPK>
+int launch_x(const uint16_t* x, const uint4* wpk, const uint16_t* w, float* y, const WideArgs& a,
+             hipStream_t stream)
 {
-    return a.c.Wi % 2 == 0 ? launch_t<NW, NB, true>(x, wpk, y, a, stream)
-                           : launch_t<NW, NB, false>(x, wpk, y, a, stream);
+    return a.c.Wi % 2 == 0 ? launch_t<NW, NB, true, WPK>(x, wpk, w, y, a, stream)
+                           : launch_t<NW, NB, false, WPK>(x, wpk, w, y, a, stream);
 }
 
 }  // namespace
@@ -486,8 +532,8 @@ bool f16_wide_applies(const ConvShape& c, size_t copad_mult)
     return plan(c, a, copad_mult);
 }
 
-int launch_conv_f16_wide(const uint16_t* x, const void* wpk, float* y, const ConvShape& c,
-                         size_t copad_mult, hipStream_t stream)
+int launch_conv_f16_wide(const uint16_t* x, const void* wpk, const uint16_t* w, float* y,
+                         const ConvShape& c, size_t copad_mult, hipStream_t stream)
 {
     WideArgs a;
     if (copad_mult % kCoW != 0) return -1;
@@ -495,8 +541,11 @@ int launch_conv_f16_wide(const uint16_t* x, const void* wpk, float* y, const Con
     if ((uintptr_t)wpk % 16 != 0) return -1;
     const uint4* w4 = static_cast<const uint4*>(wpk);
     // IM2WIN_F16_WIDE_NW: 4 waves of 4 x 4 blocks or 8 waves of 4 x 2.
-    if (env_int("IM2WIN_F16_WIDE_NW", 8) == 4) return launch_x<4, 4>(x, w4, y, a, stream);
-    return launch_x<8, 2>(x, w4, y, a, stream);
+    const bool nw4 = env_int("IM2WIN_F16_WIDE_NW", 8) == 4;
+    if (w4) return nw4 ? launch_x<4, 4, true>(x, w4, w, y, a, stream)
+                       : launch_x<8, 2, true>(x, w4, w, y, a, stream);
+    return nw4 ? launch_x<4, 4, false>(x, w4, w, y, a, stream)
+               : launch_x<8, 2, false>(x, w4, w, y, a, stream);
 }
 
 }  // namespace im2win

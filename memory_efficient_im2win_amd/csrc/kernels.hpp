@@ -73,14 +73,14 @@ bool f16_thin_applies(const ConvShape& c);
 int launch_conv_f16_thin(const uint16_t* x, const void* wp, const uint16_t* w, float* y,
                          const ConvShape& c, hipStream_t stream);
 
-// fp16 convolution for layers with many output channels (128-channel x
-// 128-pixel register tiles per wave), reading the filter prepacked by
-// launch_f16_filter_pack with its channels padded to a multiple of
-// copad_mult. Used by launch_conv_f16_fused, with a prepacked filter, for the
-// shapes it takes (f16_wide_applies) that the row-staged kernel does not.
+// fp16 convolution for layers with many output channels (128-channel wave
+// tiles), reading the filter prepacked by launch_f16_filter_pack with its
+// channels padded to a multiple of copad_mult (wpk), or gathering it from w
+// when wpk is nullptr. Used by launch_conv_f16_fused for the shapes it takes
+// (f16_wide_applies) that the row-staged and thin-layer kernels do not.
 bool f16_wide_applies(const ConvShape& c, size_t copad_mult);
-int launch_conv_f16_wide(const uint16_t* x, const void* wpk, float* y, const ConvShape& c,
-                         size_t copad_mult, hipStream_t stream);
+int launch_conv_f16_wide(const uint16_t* x, const void* wpk, const uint16_t* w, float* y,
+                         const ConvShape& c, size_t copad_mult, hipStream_t stream);
 
 // im2col + GEMM baseline: elements per im2col row (Ci*Hf*Wf padded to 32
 // bytes); the transform of N images into N*Ho*Wo rows; the GEMM over those

@@ -382,8 +382,9 @@ def _wide_plan(sh):
 @pytest.mark.parametrize("t", WIDE, ids=str)
 def test_conv_f16_wide_tiles(t, nw, orc, monkeypatch):
     """The fp16 kernel with 128-channel wave tiles (8 waves of 4 x 2 blocks or
-    4 waves of 4 x 4) and the filter copied to LDS by direct loads: uniform
-    and integer inputs; switching it off (IM2WIN_F16_WIDE=0) gives the
+    4 waves of 4 x 4), the filter copied to LDS by direct loads from the
+    prepacked copy or gathered from w (no workspace): uniform and integer
+    inputs; switching it off (IM2WIN_F16_WIDE=0) gives the
     channel-interleaved kernel's results."""
     monkeypatch.setenv("IM2WIN_F16_WIDE_NW", nw)
     sh = _shape(t, "f16")
@@ -393,13 +394,17 @@ def test_conv_f16_wide_tiles(t, nw, orc, monkeypatch):
         monkeypatch.setenv("IM2WIN_F16_WIDE", "2")
     x, w = workloads.make_inputs(sh, seed=50)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
-    note(f"conv fp16 wide tiles NW={nw} {sh.describe()} (LDS {lds} B)")
-    assert_within(_run(sh, "f16", x, w, "filter"), ref, absd, TOL["f16"], sh.describe())
     xi, wi = workloads.make_inputs(sh, seed=51, mode="int")
-    yi = _run(sh, "f16", xi, wi, "filter")
-    assert_exact(yi, orc.conv_direct(xi, wi, sh.s), sh.describe())
+    refi = orc.conv_direct(xi, wi, sh.s)
+    yi = {}
+    for kind in ("filter", None):
+        note(f"conv fp16 wide tiles NW={nw} {sh.describe()} ws={kind} (LDS {lds} B)")
+        assert_within(_run(sh, "f16", x, w, kind), ref, absd, TOL["f16"], sh.describe())
+        yi[kind] = _run(sh, "f16", xi, wi, kind)
+        assert_exact(yi[kind], refi, sh.describe())
     monkeypatch.setenv("IM2WIN_F16_WIDE", "0")
-    assert_exact(_run(sh, "f16", xi, wi, "filter"), yi, "channel-interleaved kernel")
+    for kind in ("filter", None):
+        assert_exact(_run(sh, "f16", xi, wi, kind), yi[kind], "channel-interleaved kernel")
 
 
 @pytest.mark.parametrize("t", [(2, 13, 19, 21, 130, 3, 3, 1), (2, 16, 14, 14, 128, 5, 5, 1)],
@@ -417,15 +422,16 @@ def test_conv_f16_wide_special_values(t, orc):
     x[0, 0, 2, 7] = np.inf
     w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
     ref = orc.conv_direct(x, w, sh.s)
-    note(f"conv fp16 wide special values {sh.describe()}")
-    y = _run(sh, "f16", x, w, "filter").astype(np.float64)
-    assert np.array_equal(np.isnan(y), np.isnan(ref))
-    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
-    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
     fin = np.isfinite(ref)
     _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
                               with_absdot=True)
-    assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
+    for kind in ("filter", None):
+        note(f"conv fp16 wide special values {sh.describe()} ws={kind}")
+        y = _run(sh, "f16", x, w, kind).astype(np.float64)
+        assert np.array_equal(np.isnan(y), np.isnan(ref))
+        assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+        assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+        assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
 
 
 @pytest.mark.parametrize("t", [(1, 10, 40, 40, 24, 17, 17, 1), (2, 12, 21, 40, 136, 16, 16, 1),
