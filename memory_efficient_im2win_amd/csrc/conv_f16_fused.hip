@@ -646,9 +646,9 @@ int launch_w(const uint16_t* x, const uint16_t* w, const uint4* wpk, float* y,
 // With a prepacked filter, shapes the row-staged kernel takes run there
 // (its own filter layout), then shapes the thin-layer kernel takes (the same
 // slice layout), then shapes the wide-tile kernel takes (this layout); the
-// rest run the kernel above. Without one, thin layers run the thin-layer
-// kernel and wide ones the wide-tile kernel (each gathering its filter), the
-// rest the kernel above.
+// rest run the kernel above. Without one, the same kernels take the same
+// shapes, each gathering its filter from w, and the rest run the kernel
+// above.
 size_t f16_filter_pack_bytes(const ConvShape& c)
 {
     if (f16_rows_applies(c)) return f16_rows_filter_bytes(c);
@@ -685,7 +685,12 @@ int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, hip
 int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk, float* y,
                           const ConvShape& c, hipStream_t stream)
 {
-    if (wpk && f16_rows_applies(c)) return launch_conv_f16_rows(x, wpk, y, c, stream);
+    if (f16_rows_applies(c)) {
+        // Without a workspace and with x off 16-byte alignment the next
+        // kernels take the call; a prepacked row-layout filter only this one.
+        const int rc = launch_conv_f16_rows(x, wpk, w, y, c, stream);
+        if (rc != -1 || wpk) return rc;
+    }
     if (f16_thin_applies(c)) return launch_conv_f16_thin(x, wpk, w, y, c, stream);
     if (f16_wide_applies(c, kCoPad)) return launch_conv_f16_wide(x, wpk, w, y, c, kCoPad, stream);
     FusedArgs a;

@@ -60,7 +60,7 @@ struct RowsArgs {
     uint32_t stage_bytes;           // (S + NX) KB: filter slices, then rows
     uint32_t dummy;                 // LDS byte offset of the landing kilobyte of unused loads
     uint32_t lds_bytes;
-    uint32_t xbytes, ybytes, wbytes;
+    uint32_t xbytes, ybytes, wbytes, worig;   // x, y, prepacked filter, filter in w's layout
     uint32_t mask[4];               // B dwords: halves kw >= Wf cleared
     bool swz;                       // XCD-grouped tile order
     FastDiv divWo, divHo;
@@ -139,9 +139,14 @@ __global__ __launch_bounds__(256) void f16_rows_filter_pack_kernel(const uint16_
     }
 }
 
-template <int NWV, int DMAX, bool M3>
+// WPK: the filter slices come prepacked (wp) by direct loads; otherwise each
+// stage's slices are gathered from w, two stages ahead, after a stage's
+// MFMAs (its direct-load slots then land in the dummy kilobyte, so every
+// wave still issues DMAX loads per stage).
+template <int NWV, int DMAX, bool M3, bool WPK>
 __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t* __restrict__ x,
                                                                  const uint4* __restrict__ wp,
+                                                                 const uint16_t* __restrict__ w,
                                                                  float* __restrict__ y, RowsArgs a)
 {
     constexpr int NT = 64 * NWV;
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
         const int m = wave + NWV * i;
         uint32_t v = kMiss;
         if (m < a.S) {
-            v = (uint32_t)(((m * a.Copad + co0) + lane) * 16);
+            if (WPK) v = (uint32_t)(((m * a.Copad + co0) + lane) * 16);
         } else if (m < a.S + a.NX) {
             const int e = (m - a.S) * 64 + lane;
             const int row = e / rpc, cc = e - row * rpc;
@@ -242,13 +247,15 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
     auto issue = [&](int s, int sb) {
         const uint32_t fo = (uint32_t)s * a.S * a.Copad * 16;
         const int64_t xo = (int64_t)s * a.Cg * Hi * Wi;
-        const __amdgpu_buffer_rsrc_t ra = rbuf(wp + (int64_t)s * a.S * a.Copad, a.wbytes - fo);
+        const __amdgpu_buffer_rsrc_t ra =
+            rbuf(wp + (int64_t)s * a.S * a.Copad, WPK ? a.wbytes - fo : 0u);
         const __amdgpu_buffer_rsrc_t rx = rbuf(x + xo, a.xbytes - (uint32_t)(xo * 2));
         const uint32_t base = lbase + (uint32_t)sb * a.stage_bytes;
 #pragma unroll
         for (int i = 0; i < DMAX; ++i) {
             const int m = wave + NWV * i;
-            const uint32_t dst = m < a.S + a.NX ? base + (uint32_t)m * 1024 : lbase + a.dummy;
+            const bool real = m < a.S + a.NX && (WPK || m >= a.S);
+            const uint32_t dst = real ? base + (uint32_t)m * 1024 : lbase + a.dummy;
             dma16(m < a.S ? ra : rx, dst, voff[i]);
         }
     };
@@ -315,9 +322,45 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
         }
     };
 
+    // Without a prepacked filter: entry (slice m, channel co0 + j) of stage
+    // sg holds the taps of w[co0 + j][sg*Cg + m/Hf][m%Hf][*] (zeros past Wf
+    // and Co).
+    auto gather = [&](int sg, int sb) {
+        const __amdgpu_buffer_rsrc_t rw = rbuf(w, a.worig);
+        uint4* F = reinterpret_cast<uint4*>(smem + (size_t)sb * a.stage_bytes);
+        const int ne = a.S * 64;
+        for (int e0 = 0; e0 < ne; e0 += 2 * NT) {
+            uint32_t hv[2][8];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int e = e0 + k * NT + tid;
+                const int m = e >> 6, co = co0 + (e & 63);
+                const int c = sg * a.Cg + m / Hf, kh = m - (m / Hf) * Hf;
+                const uint32_t src = e < ne && co < Co
+                                         ? (uint32_t)((((co * Ci + c) * Hf + kh) * a.c.Wf) * 2)
+                                         : kMiss;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    hv[k][q] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rw, (int)(q < a.c.Wf ? src + 2 * q : kMiss), 0, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int e = e0 + k * NT + tid;
+                if (e < ne)
+                    F[e] = make_uint4(hv[k][0] | (hv[k][1] << 16), hv[k][2] | (hv[k][3] << 16),
+                                      hv[k][4] | (hv[k][5] << 16), hv[k][6] | (hv[k][7] << 16));
+            }
+        }
+    };
+
     const int nk = a.S >> 1;   // K steps per stage (S is even)
     issue(0, 0);
     if (a.NS > 1) issue(1, 1); else issue_none();
+    if (!WPK) {
+        gather(0, 0);
+        if (a.NS > 1) gather(1, 1);
+    }
     for (int s = 0; s < a.NS; ++s) {
         wait_loads<DMAX>();   // this wave's loads of stage s have landed
         __syncthreads();      // every wave's; and stage s-1's buffer is free
@@ -346,6 +389,8 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
             __builtin_amdgcn_sched_barrier(0);
         }
         if (t < nk) mma(f0);
+        // Stage s+2's buffer was freed by the barrier above.
+        if (!WPK && s + 2 < a.NS) gather(s + 2, (s + 2) % kBufs);
     }
     wait_loads<0>();   // the last (unused) loads have landed before the workgroup ends
 
@@ -454,7 +499,10 @@ bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax)
     const int64_t xb = (int64_t)c.N * c.Ci * c.Hi * c.Wi * 2;
     const int64_t yb = (int64_t)c.N * c.Co * c.Ho * c.Wo * 4;
     const int64_t wb = (int64_t)c.Ci * c.Hf * a.Copad * 16;
-    if (xb >= 0x7fffffff || yb >= (int64_t)kMiss || wb >= 0x7fffffff) return false;
+    const int64_t wo = (int64_t)c.Co * c.Ci * c.Hf * c.Wf * 2;
+    if (xb >= 0x7fffffff || yb >= (int64_t)kMiss || wb >= 0x7fffffff || wo >= 0x7fffffff)
+        return false;
+    a.worig = (uint32_t)wo;
     a.xbytes = (uint32_t)xb;
     a.ybytes = (uint32_t)yb;
     a.wbytes = (uint32_t)wb;
@@ -470,36 +518,46 @@ bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax)
     return true;
 }
 
-template <int NWV, int DMAX, bool M3>
-int launch_t(const uint16_t* x, const uint4* wp, float* y, const RowsArgs& a, hipStream_t stream)
+template <int NWV, int DMAX, bool M3, bool WPK>
+int launch_t(const uint16_t* x, const uint4* wp, const uint16_t* w, float* y, const RowsArgs& a,
+             hipStream_t stream)
 {
     static bool attr = false;
     if (!attr) {
         // On failure the launch below reports any limit it exceeds.
-        if (hipFuncSetAttribute((const void*)conv_f16_rows_kernel<NWV, DMAX, M3>,
+        if (hipFuncSetAttribute((const void*)conv_f16_rows_kernel<NWV, DMAX, M3, WPK>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kRowsLds) != hipSuccess)
             (void)hipGetLastError();
         attr = true;
     }
-    hipLaunchKernelGGL((conv_f16_rows_kernel<NWV, DMAX, M3>),
+    hipLaunchKernelGGL((conv_f16_rows_kernel<NWV, DMAX, M3, WPK>),
                        dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(64 * NWV), a.lds_bytes,
-                       stream, x, wp, y, a);
+                       stream, x, wp, w, y, a);
     return launch_status();
 }
 
-template <int NWV, bool M3>
-int launch_d(int dmax, const uint16_t* x, const uint4* wp, float* y, const RowsArgs& a,
-             hipStream_t stream)
+template <int NWV, bool M3, bool WPK>
+int launch_d(int dmax, const uint16_t* x, const uint4* wp, const uint16_t* w, float* y,
+             const RowsArgs& a, hipStream_t stream)
 {
     switch (dmax) {
-    case 4: return launch_t<NWV, 4, M3>(x, wp, y, a, stream);
-    case 5: return launch_t<NWV, 5, M3>(x, wp, y, a, stream);
-    case 6: return launch_t<NWV, 6, M3>(x, wp, y, a, stream);
-    case 8: return launch_t<NWV, 8, M3>(x, wp, y, a, stream);
-    case 12: return launch_t<NWV, 12, M3>(x, wp, y, a, stream);
-    case 16: return launch_t<NWV, 16, M3>(x, wp, y, a, stream);
+    case 4: return launch_t<NWV, 4, M3, WPK>(x, wp, w, y, a, stream);
+    case 5: return launch_t<NWV, 5, M3, WPK>(x, wp, w, y, a, stream);
+    case 6: return launch_t<NWV, 6, M3, WPK>(x, wp, w, y, a, stream);
+    case 8: return launch_t<NWV, 8, M3, WPK>(x, wp, w, y, a, stream);
+    case 12: return launch_t<NWV, 12, M3, WPK>(x, wp, w, y, a, stream);
+    case 16: return launch_t<NWV, 16, M3, WPK>(x, wp, w, y, a, stream);
     }
     return -1;
+}
+
+template <bool WPK>
+int launch_p(int nwv, int dmax, const uint16_t* x, const uint4* wp, const uint16_t* w, float* y,
+             const RowsArgs& a, hipStream_t stream)
+{
+    if (nwv == 8 && a.c.Wf >= 6) return launch_d<8, true, WPK>(dmax, x, wp, w, y, a, stream);
+    if (nwv == 8) return launch_d<8, false, WPK>(dmax, x, wp, w, y, a, stream);
+    return launch_d<4, false, WPK>(dmax, x, wp, w, y, a, stream);
 }
 
 }  // namespace
@@ -548,8 +606,8 @@ int launch_f16_slices_filter_pack(const uint16_t* w, void* wp, const ConvShape& 
     return launch_status();
 }
 
-int launch_conv_f16_rows(const uint16_t* x, const void* wp, float* y, const ConvShape& c,
-                         hipStream_t stream)
+int launch_conv_f16_rows(const uint16_t* x, const void* wp, const uint16_t* w, float* y,
+                         const ConvShape& c, hipStream_t stream)
 {
     RowsArgs a;
     int nwv, dmax;
@@ -557,9 +615,8 @@ int launch_conv_f16_rows(const uint16_t* x, const void* wp, float* y, const Conv
     // Rows are fetched in 16-byte chunks from 16-byte boundaries.
     if ((uintptr_t)x % 16 != 0 || (uintptr_t)wp % 16 != 0) return -1;
     const uint4* w4 = static_cast<const uint4*>(wp);
-    if (nwv == 8 && c.Wf >= 6) return launch_d<8, true>(dmax, x, w4, y, a, stream);
-    if (nwv == 8) return launch_d<8, false>(dmax, x, w4, y, a, stream);
-    return launch_d<4, false>(dmax, x, w4, y, a, stream);
+    return w4 ? launch_p<true>(nwv, dmax, x, w4, w, y, a, stream)
+              : launch_p<false>(nwv, dmax, x, w4, w, y, a, stream);
 }
 
 }  // namespace im2win

@@ -49,15 +49,16 @@ size_t f16_filter_pack_bytes(const ConvShape& c);
 int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, hipStream_t stream);
 
 // fp16 convolution with the input rows copied to LDS by direct loads and the
-// filter prepacked by launch_f16_rows_filter_pack (its own layout). Used by
-// the three calls above, with a prepacked filter, for the shapes it takes
-// (f16_rows_applies). -1 if the shape or x's alignment is outside its envelope.
+// filter prepacked by launch_f16_rows_filter_pack (its own layout; wp), or
+// gathered from w when wp is nullptr. Used by the three calls above for the
+// shapes it takes (f16_rows_applies). -1 if the shape or x's alignment is
+// outside its envelope.
 bool f16_rows_applies(const ConvShape& c);
 size_t f16_rows_filter_bytes(const ConvShape& c);
 int launch_f16_rows_filter_pack(const uint16_t* w, void* wp, const ConvShape& c,
                                 hipStream_t stream);
-int launch_conv_f16_rows(const uint16_t* x, const void* wp, float* y, const ConvShape& c,
-                         hipStream_t stream);
+int launch_conv_f16_rows(const uint16_t* x, const void* wp, const uint16_t* w, float* y,
+                         const ConvShape& c, hipStream_t stream);
 // The same filter layout, slices (c, kh) of the 8 taps kw, channels padded
 // to a multiple of 64, for any shape with Wf <= 8 and Hf*Wf <= 256.
 size_t f16_slices_filter_bytes(const ConvShape& c);

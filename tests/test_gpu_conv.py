@@ -295,10 +295,13 @@ def test_conv_f16_row_staged(t, nwv, orc, monkeypatch):
     assert on == sh.Ci * sh.Hf * ((sh.Co + 63) // 64 * 64) * 16 and on != off, (on, off)
     x, w = workloads.make_inputs(sh, seed=40)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
-    note(f"conv fp16 row-staged NWV={nwv} {sh.describe()}")
-    assert_within(_run(sh, "f16", x, w, "filter"), ref, absd, TOL["f16"], sh.describe())
     xi, wi = workloads.make_inputs(sh, seed=41, mode="int")
-    assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
+    refi = orc.conv_direct(xi, wi, sh.s)
+    # With the filter prepacked, and gathered in the kernel (no workspace).
+    for kind in ("filter", None):
+        note(f"conv fp16 row-staged NWV={nwv} {sh.describe()} ws={kind}")
+        assert_within(_run(sh, "f16", x, w, kind), ref, absd, TOL["f16"], sh.describe())
+        assert_exact(_run(sh, "f16", xi, wi, kind), refi, sh.describe())
 
 
 @pytest.mark.parametrize("t", [(2, 4, 14, 16, 40, 3, 5, 2), (2, 4, 15, 24, 40, 3, 7, 2)], ids=str)
@@ -315,15 +318,16 @@ def test_conv_f16_row_staged_special_values(t, orc):
     x[0, 0, 2, 7] = np.inf
     w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
     ref = orc.conv_direct(x, w, sh.s)
-    note(f"conv fp16 row-staged special values {sh.describe()}")
-    y = _run(sh, "f16", x, w, "filter").astype(np.float64)
-    assert np.array_equal(np.isnan(y), np.isnan(ref))
-    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
-    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
     fin = np.isfinite(ref)
     _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
                               with_absdot=True)
-    assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
+    for kind in ("filter", None):
+        note(f"conv fp16 row-staged special values {sh.describe()} ws={kind}")
+        y = _run(sh, "f16", x, w, kind).astype(np.float64)
+        assert np.array_equal(np.isnan(y), np.isnan(ref))
+        assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+        assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+        assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
 
 
 @pytest.mark.parametrize("swz", ["1", "0"])
