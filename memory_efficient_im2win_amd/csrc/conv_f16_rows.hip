@@ -27,7 +27,9 @@
 //    (channel, input row)) are fetched with buffer_load_dwordx4 ... lds: no
 //    registers, no transposition. Three stage buffers rotate; the loads of
 //    stage s+2 are issued as stage s starts, and one barrier per stage both
-//    publishes stage s and frees the buffer of stage s-1.
+//    publishes stage s and frees the buffer of stage s-1. Without a
+//    prepacked filter the slices of stage s+2 are gathered from w after the
+//    MFMAs of stage s instead.
 //  * The loads are issued from inline assembly so that the compiler, which
 //    would otherwise wait for every outstanding LDS load before each LDS
 //    read, leaves the pipelining to the explicit waits here.

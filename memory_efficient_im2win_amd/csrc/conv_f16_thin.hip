@@ -1,6 +1,6 @@
 // fp16 im2win convolution on the CDNA4 matrix cores for thin layers: few
-// input channels, so the whole filter stays in LDS (fp32 accumulate,
-// prepacked filter).
+// input channels, so the whole filter stays in LDS (fp32 accumulate; filter
+// prepacked or gathered).
 //
 // The half-precision path of "Enabling Memory-efficient Im2win Convolution
 // with Multi-precision Support on GPU CUDA and Tensor Cores" (Abstract: half
@@ -18,7 +18,8 @@
 //    16-byte LDS read. Channel-interleaved slices would pad 3 channels to 8;
 //    these pad 7 taps to 8.
 //  * The whole contraction is one stage: a workgroup copies the filter
-//    slices of its 64 output channels (direct global-to-LDS loads) and the
+//    slices of its 64 output channels (direct global-to-LDS loads from the
+//    prepacked filter, or gathered from w without one) and the
 //    input rows of its pixels, for every input channel (through registers,
 //    so rows of any width and alignment are taken), then runs all the MFMAs
 //    and stores. Four waves each hold a 2 x NB tile of 32 x 32 accumulators

@@ -1,5 +1,5 @@
 // fp16 im2win convolution on the CDNA4 matrix cores for layers with many
-// output channels (fp32 accumulate, prepacked filter).
+// output channels (fp32 accumulate; filter prepacked or gathered).
 //
 // The half-precision path of "Enabling Memory-efficient Im2win Convolution
 // with Multi-precision Support on GPU CUDA and Tensor Cores" (Abstract: half
@@ -14,17 +14,19 @@
 //    16-byte entry = 8 channels of one input column, columns stride-phase
 //    major), so every lane's 8-element K slice of A or B is one aligned
 //    16-byte LDS read.
-//  * A workgroup of 4 waves (one per SIMD) owns 128 output channels x 512
-//    pixels; every wave owns all 128 channels x 128 pixels, a 4 x 4 tile of
-//    32 x 32 accumulators (256 registers), so each A read feeds four MFMAs
-//    and each B read four: half a kilobyte of LDS per MFMA.
+//  * A workgroup owns 128 output channels x 512 pixels. By default 8 waves
+//    (two per SIMD) each hold all 128 channels x 64 pixels, a 4 x 2 tile of
+//    32 x 32 accumulators, so each A read feeds two MFMAs and each B read
+//    four (0.75 KB of LDS per MFMA); the alternative is 4 waves of 4 x 4
+//    (256 accumulators, one wave per SIMD, 0.5 KB per MFMA).
 //  * A stage is one channel group: the filter entries (tap, channel) of the
 //    group for the tile's 128 channels, copied from the prepacked filter by
-//    direct global-to-LDS loads (contiguous kilobytes, no registers), and
-//    the tile's input rows of the group, gathered through registers (8
-//    channel planes -> one entry). Two stage buffers alternate: the loads of
-//    group g+1 are issued after the barrier that opens group g and land
-//    while its MFMAs run; one barrier per group.
+//    direct global-to-LDS loads (contiguous kilobytes, no registers) or,
+//    without one, gathered from w after the previous group's MFMAs; and the
+//    tile's input rows of the group, gathered through registers (8 channel
+//    planes -> one entry). Two stage buffers alternate: the loads of group
+//    g+1 are issued after the barrier that opens group g and land while its
+//    MFMAs run; one barrier per group.
 #include <algorithm>
 #include <cstdlib>
 
