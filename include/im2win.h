@@ -11,9 +11,11 @@
  *     y[n][co][ho][wo] = sum over ci, kh, kw of
  *                        x[n][ci][ho*sh + kh][wo*sw + kw] * w[co][ci][kh][kw]
  * (cross-correlation: no filter flip, no padding, no dilation, no bias; the
- * pages' layers are all unpadded). Full precision runs on the vector ALUs,
- * half precision on the matrix cores, as the same page's Abstract splits the
- * work between CUDA cores and tensor cores.
+ * pages' layers are all unpadded). The same page's Abstract splits the work
+ * between general-purpose cores (full precision) and matrix hardware (half
+ * precision). Here full precision keeps fp32 inputs, products and sums and
+ * runs on the fp32 matrix instructions (a vector-ALU kernel on request);
+ * half precision runs on the fp16 matrix instructions with fp32 sums.
  *
  * The im2win transform is the one of "Im2win: Memory Efficient Convolution
  * On SIMD Architectures" (Abstract): each row of dot-product windows is
@@ -102,9 +104,9 @@ int im2win_pack_strided(const void *x, void *ws, int N, int Ci, int Hi, int Wi, 
  * The workspace (optional) is one caller-owned device buffer, 16-byte
  * aligned, laid out as
  *     [ prepacked filter | im2win tensor of a chunk of images ]
- * The prepacked part is the filter re-laid out for the matrix-core kernel
- * (fp16 only; it is 0 bytes for fp32 and for fp16 shapes the fused kernel
- * does not take); it is rounded up to a multiple of 256 bytes.
+ * The prepacked part is the filter re-laid out for the fp16 matrix-core
+ * kernel the shape runs on (fp16 only; it is 0 bytes for fp32 and for fp16
+ * shapes no such kernel takes); it is rounded up to a multiple of 256 bytes.
  *
  *  materialize == 0: bytes for the fused mode with a prepacked filter
  *                    (0 for fp32: the fused fp32 path needs no workspace).
@@ -119,8 +121,10 @@ size_t conv2d_im2win_workspace_bytes_strided(int materialize, int N, int Ci, int
                                              size_t elem_bytes);
 
 /*
- * fp32 convolution on the vector ALUs ("full precision on CUDA cores" in the
- * GPU page's Abstract). x, w fp32; y fp32 (written fully).
+ * fp32 convolution ("full precision" in the GPU page's Abstract): x, w fp32;
+ * fp32 products and sums on the fp32 matrix instructions (the vector-ALU
+ * kernel when the environment sets IM2WIN_F32_PATH=valu, and for shapes
+ * outside the matrix kernel's envelope); y fp32 (written fully).
  *
  * The workspace selects how the im2win rows reach the dot products; with
  * F = the prepacked part (see conv2d_im2win_workspace_bytes, 0 for fp32)
