@@ -504,29 +504,38 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     }
 
     // Output: lane holds pixel l32 of each block and channels
-    // 8*(r/4) + 4*hl + r%4 of each 32-channel block. Byte offset in y =
-    // per-lane part (image, pixel, 4*hl channels) + uniform part (channel).
+    // 8*(r/4) + 4*hl + r%4 of each 32-channel block. Blocks 2p and 2p+1 of a
+    // wave are 64 consecutive pixels: swapping lanes 32-63 of the first with
+    // lanes 0-31 of the second (v_permlane32_swap) gives one register with
+    // channel cu for all 64 pixels and one with channel cu+4, so every store
+    // writes 256 contiguous bytes of one channel plane.
+    static_assert(NB % 2 == 0, "blocks are stored in pairs");
     const int64_t plane = (int64_t)Ho * Wo;
     const __amdgpu_buffer_rsrc_t yb = buf(y, a.ybytes);
     const bool all_co = co0 + COT <= Co;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int64_t q = q0 + (wpx * NB + b) * 32 + l32;
+    for (int p = 0; p < NB / 2; ++p) {
+        const int64_t qa = q0 + (wpx * NB + 2 * p) * 32 + lane;
+        const bool ok = qa < qend;
+        const int64_t q = ok ? qa : qend - 1;
         const int gr = (int)(q / Wo);
         const int wo = (int)(q - (int64_t)gr * Wo);
         const int n = (int)a.divHo.div((uint32_t)gr), ho = gr - n * Ho;
-        const uint32_t voff =
-            (uint32_t)((((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo) * 4);
-        if (q >= qend) continue;
+        const uint32_t voff = (uint32_t)((((int64_t)n * Co) * plane + (int64_t)ho * Wo + wo) * 4);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int cu = co0 + wco * 64 + i * 32 + 8 * (r >> 2) + (r & 3);  // co - 4*hl
-                const float v = acc[i][b][r];
-                if (all_co || cu + 4 * hl < Co)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yb, (int)voff,
-                                                          (int)(cu * plane * 4), 0);
+                const int cu = co0 + wco * 64 + i * 32 + 8 * (r >> 2) + (r & 3);
+                const auto sv = __builtin_amdgcn_permlane32_swap(
+                    __float_as_uint(acc[i][2 * p][r]), __float_as_uint(acc[i][2 * p + 1][r]), false,
+                    false);
+                if (ok && (all_co || cu < Co))
+                    __builtin_amdgcn_raw_buffer_store_b32(sv[0], yb, (int)voff, (int)(cu * plane * 4),
+                                                          0);
+                if (ok && (all_co || cu + 4 < Co))
+                    __builtin_amdgcn_raw_buffer_store_b32(sv[1], yb, (int)voff,
+                                                          (int)((cu + 4) * plane * 4), 0);
             }
     }
 }
