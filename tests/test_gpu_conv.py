@@ -571,3 +571,58 @@ def test_conv_f16_input_at_odd_element_offset(t, orc):
         y = m.conv2d(xv, wt, sh.s, ws=_ws(sh, kind, dev)).cpu().numpy()
         assert_exact(y, ref, f"{sh.describe()} ws={kind}")
     torch.cuda.synchronize()
+
+
+def _random_f16_shapes(count_per_family=12, seed=2024):
+    """Seeded random small shapes aimed at each fp16 kernel family: row-staged
+    (even Ci, Wi % 8 = 0, even column stride, Wf <= 8), thin-layer (Ci < 8,
+    even column stride, Wf <= 8), wide-tile (Co >= 128) and the
+    channel-interleaved kernel (the rest). Strides may differ per axis."""
+    rng = np.random.default_rng(seed)
+    out = []
+
+    def pick(family):
+        for _ in range(1000):
+            N = int(rng.integers(1, 4))
+            Hf, Wf = int(rng.integers(1, 8)), int(rng.integers(1, 9))
+            sh, sw = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+            Hi = int(rng.integers(Hf, Hf + 24))
+            Wi = int(rng.integers(Wf, Wf + 40))
+            if family == "rows":
+                Ci, Co, sw = 2 * int(rng.integers(1, 9)), int(rng.integers(1, 130)), 2 * int(rng.integers(1, 3))
+                Wi = max(8, (Wi + 7) // 8 * 8)
+            elif family == "thin":
+                Ci, Co, sw = int(rng.integers(1, 8)), int(rng.integers(1, 200)), 2 * int(rng.integers(1, 3))
+                if Ci % 2 == 0 and Wi % 8 == 0:
+                    Wi += 1
+            elif family == "wide":
+                Ci, Co = int(rng.integers(8, 40)), int(rng.integers(128, 300))
+                Hf, Wf = min(Hf, 5), min(Wf, 5)
+            else:
+                Ci, Co = int(rng.integers(8, 40)), int(rng.integers(1, 128))
+            if Wi < Wf or Hi < Hf:
+                continue
+            s = sh if sh == sw else (sh, sw)
+            return (N, Ci, Hi, Wi, Co, Hf, Wf, s)
+        raise RuntimeError(family)
+
+    for family in ("rows", "thin", "wide", "interleaved"):
+        for _ in range(count_per_family):
+            out.append((family, pick(family)))
+    return out
+
+
+@pytest.mark.parametrize("family,t", _random_f16_shapes(), ids=lambda v: str(v))
+def test_conv_f16_random_shapes(family, t, orc):
+    """Seeded random shapes for every fp16 kernel family, bit-exact on
+    integer inputs with the filter prepacked and gathered in the kernel (no
+    workspace), and within tolerance on uniform inputs."""
+    sh = _shape(t, "f16")
+    xi, wi = workloads.make_inputs(sh, seed=64, mode="int")
+    refi = orc.conv_direct(xi, wi, sh.s)
+    for kind in ("filter", None):
+        note(f"conv fp16 random {family} {sh.describe()} ws={kind}")
+        assert_exact(_run(sh, "f16", xi, wi, kind), refi, f"{family} {sh.describe()} ws={kind}")
+    x, w = workloads.make_inputs(sh, seed=65)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    assert_within(_run(sh, "f16", x, w, "filter"), ref, absd, TOL["f16"], sh.describe())
