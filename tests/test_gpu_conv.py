@@ -626,3 +626,33 @@ def test_conv_f16_random_shapes(family, t, orc):
     x, w = workloads.make_inputs(sh, seed=65)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
     assert_within(_run(sh, "f16", x, w, "filter"), ref, absd, TOL["f16"], sh.describe())
+
+
+def _random_f32_shapes(count=24, seed=2025):
+    """Seeded random small fp32 shapes: thin and wide channel counts, filters
+    up to 11 x 11, strides up to 4 per axis."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        N = int(rng.integers(1, 4))
+        Ci, Co = int(rng.integers(1, 40)), int(rng.integers(1, 200))
+        Hf, Wf = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        sh, sw = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+        Hi, Wi = int(rng.integers(Hf, Hf + 30)), int(rng.integers(Wf, Wf + 40))
+        out.append((N, Ci, Hi, Wi, Co, Hf, Wf, sh if sh == sw else (sh, sw)))
+    return out
+
+
+@pytest.mark.parametrize("t", _random_f32_shapes(), ids=str)
+def test_conv_f32_random_shapes(t, orc, monkeypatch):
+    """Seeded random fp32 shapes, bit-exact on integer inputs through the
+    matrix-core kernel, the vector-ALU kernel and the materialised mode."""
+    sh = _shape(t, "f32")
+    xi, wi = workloads.make_inputs(sh, seed=66, mode="int")
+    refi = orc.conv_direct(xi, wi, sh.s)
+    for kind in (None, "full"):
+        note(f"conv fp32 random {sh.describe()} ws={kind}")
+        assert_exact(_run(sh, "f32", xi, wi, kind), refi, f"{sh.describe()} ws={kind}")
+    monkeypatch.setenv("IM2WIN_F32_PATH", "valu")
+    note(f"conv fp32 random {sh.describe()} vector ALU")
+    assert_exact(_run(sh, "f32", xi, wi, None), refi, f"{sh.describe()} vector ALU")
