@@ -49,6 +49,7 @@ constexpr int kNB = 4;                    // 32-pixel blocks per wave
 constexpr int kBufs = 3;                  // stage buffers
 constexpr int kSlack = 2048;              // LDS past the last buffer: reads one pair past a stage
 constexpr uint32_t kMiss = 0xFFFFFFF0u;   // vector offset past every accepted buffer
+constexpr int kGL = 16;                   // most dword gather loads per thread and stage
 
 struct RowsArgs {
     ConvShape c;
@@ -64,6 +65,13 @@ struct RowsArgs {
     uint32_t lds_bytes;
     uint32_t xbytes, ybytes, wbytes, worig;   // x, y, prepacked filter, filter in w's layout
     uint32_t mask[4];               // B dwords: halves kw >= Wf cleared
+    // Dword filter gather (no prepacked filter, w 4-byte aligned): gl dword
+    // loads per thread and stage (0: one 16-byte entry per thread and load
+    // round instead); RD dwords of w per output channel and stage, wco bytes
+    // between output channels; a thread's dword index advances by gjs*RD + grs
+    // per load; wfm = ceil(2^16 / Wf).
+    int gl, gjs, grs;
+    uint32_t RD, wco, wfm;
     bool swz;                       // XCD-grouped tile order
     FastDiv divWo, divHo;
 };
@@ -356,10 +364,81 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
         }
     };
 
+    // Dword gather: for its 64 channels a stage's taps are 64 runs of RD
+    // dwords in w (channel co0+j, input channels sg*Cg.., all Hf*Wf taps),
+    // read with consecutive threads on consecutive dwords of a run. Each of
+    // a dword's two halves goes to the entry of its slice (tap t of the run
+    // is slice t / Wf, column t % Wf). The loads of stage s+2 go out with
+    // stage s's direct loads and are written to LDS after its MFMAs.
+    // Channels past Co fall outside w's range and read zeros; halves
+    // kw >= Wf of every entry are zeroed once below and never written again.
+    uint32_t gv[kGL];
+    const int gj0 = tid / (int)a.RD, gq0 = tid - gj0 * (int)a.RD;
+    auto gather_load = [&](int sg) {
+        const __amdgpu_buffer_rsrc_t rw = rbuf(w, a.worig);
+        const uint32_t base = (uint32_t)co0 * a.wco + (uint32_t)sg * a.RD * 4;
+        int j = gj0, r = gq0;
+        // Opaque per call: the offsets do not depend on the stage, and
+        // hoisting them out of the stage loop would cost 3*kGL registers.
+        asm volatile("" : "+v"(j), "+v"(r));
+#pragma unroll
+        for (int i = 0; i < kGL; ++i) {
+            if (i < a.gl) {
+                const uint32_t src = j < 64 ? base + (uint32_t)j * a.wco + (uint32_t)r * 4 : kMiss;
+                gv[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, (int)src, 0, 0);
+            }
+            j += a.gjs;
+            r += a.grs;
+            if (r >= (int)a.RD) {
+                r -= (int)a.RD;
+                ++j;
+            }
+        }
+    };
+    auto gather_store = [&](int sb) {
+        uint16_t* F = reinterpret_cast<uint16_t*>(smem + (size_t)sb * a.stage_bytes);
+        int j = gj0, r = gq0;
+        asm volatile("" : "+v"(j), "+v"(r));
+#pragma unroll
+        for (int i = 0; i < kGL; ++i) {
+            if (i < a.gl && j < 64) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t t = 2 * (uint32_t)r + h;
+                    const uint32_t m = (t * a.wfm) >> 16;
+                    const uint32_t kw = t - m * (uint32_t)a.c.Wf;
+                    F[((m * 64 + j) << 3) + kw] = (uint16_t)(gv[i] >> (16 * h));
+                }
+            }
+            j += a.gjs;
+            r += a.grs;
+            if (r >= (int)a.RD) {
+                r -= (int)a.RD;
+                ++j;
+            }
+        }
+    };
+    const bool coal = !WPK && a.gl > 0;
+    if (coal && a.c.Wf < 8) {
+        for (int e = tid; e < kBufs * a.S * 64; e += NT) {
+            const int b = e / (a.S * 64);
+            uint16_t* F = reinterpret_cast<uint16_t*>(smem + (size_t)b * a.stage_bytes);
+            const int el = e - b * a.S * 64;
+            for (int kw = a.c.Wf; kw < 8; ++kw) F[el * 8 + kw] = 0;
+        }
+    }
+
     const int nk = a.S >> 1;   // K steps per stage (S is even)
     issue(0, 0);
     if (a.NS > 1) issue(1, 1); else issue_none();
-    if (!WPK) {
+    if (coal) {
+        gather_load(0);
+        gather_store(0);
+        if (a.NS > 1) {
+            gather_load(1);
+            gather_store(1);
+        }
+    } else if (!WPK) {
         gather(0, 0);
         if (a.NS > 1) gather(1, 1);
     }
@@ -367,6 +446,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
         wait_loads<DMAX>();   // this wave's loads of stage s have landed
         __syncthreads();      // every wave's; and stage s-1's buffer is free
         if (s + 2 < a.NS) issue(s + 2, (s + 2) % kBufs); else issue_none();
+        if (coal && s + 2 < a.NS) gather_load(s + 2);
 
         const unsigned char* A = smem + (size_t)(s % kBufs) * a.stage_bytes;
         const unsigned char* X = A + (size_t)a.S * 1024;
@@ -392,7 +472,12 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
         }
         if (t < nk) mma(f0);
         // Stage s+2's buffer was freed by the barrier above.
-        if (!WPK && s + 2 < a.NS) gather(s + 2, (s + 2) % kBufs);
+        if (!WPK && s + 2 < a.NS) {
+            if (coal)
+                gather_store((s + 2) % kBufs);
+            else
+                gather(s + 2, (s + 2) % kBufs);
+        }
     }
     wait_loads<0>();   // the last (unused) loads have landed before the workgroup ends
 
@@ -626,6 +711,24 @@ int launch_conv_f16_rows(const uint16_t* x, const void* wp, const uint16_t* w, f
     // Rows are fetched in 16-byte chunks from 16-byte boundaries.
     if ((uintptr_t)x % 16 != 0 || (uintptr_t)wp % 16 != 0) return -1;
     const uint4* w4 = static_cast<const uint4*>(wp);
+    a.gl = a.gjs = a.grs = 0;
+    a.RD = 1;
+    a.wco = a.wfm = 0;
+    if (!w4 && (uintptr_t)w % 4 == 0) {
+        // S is even, so RD is whole; Ci is even, so every run starts on a dword.
+        const int nt = 64 * nwv;
+        const int rd = a.S * c.Wf / 2;
+        const int gl = ceil_div(64 * rd, nt);
+        const int64_t wco = (int64_t)c.Ci * c.Hf * c.Wf * 2;
+        if (gl <= kGL && (int64_t)ceil_div(c.Co, kCoT) * kCoT * wco < (int64_t)kMiss) {
+            a.gl = gl;
+            a.RD = (uint32_t)rd;
+            a.gjs = nt / rd;
+            a.grs = nt % rd;
+            a.wco = (uint32_t)wco;
+            a.wfm = (uint32_t)ceil_div(65536, c.Wf);
+        }
+    }
     return w4 ? launch_p<true>(nwv, dmax, x, w4, w, y, a, stream)
               : launch_p<false>(nwv, dmax, x, w4, w, y, a, stream);
 }

@@ -270,6 +270,7 @@ ROWS = [
     (5, 4, 12, 16, 64, 3, 3, 2),
     (2, 8, 20, 64, 128, 5, 3, (2, 2)),
     (2, 2, 65, 64, 40, 3, 3, 2),      # tiles aligned to images
+    (2, 4, 24, 32, 64, 16, 8, 2),     # 16 dword gather loads per thread (8 waves)
 ]
 
 
@@ -569,6 +570,32 @@ def test_conv_f16_input_at_odd_element_offset(t, orc):
     for kind in (None, "filter", "full"):
         note(f"conv fp16 input at odd offset {sh.describe()} ws={kind}")
         y = m.conv2d(xv, wt, sh.s, ws=_ws(sh, kind, dev)).cpu().numpy()
+        assert_exact(y, ref, f"{sh.describe()} ws={kind}")
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("t", [(2, 24, 14, 14, 96, 5, 5, 1), (2, 16, 14, 14, 128, 5, 5, 1),
+                               (3, 3, 35, 64, 64, 7, 7, 2), (1, 64, 40, 40, 64, 7, 7, 2),
+                               (2, 4, 24, 32, 64, 16, 8, 2), (2, 9, 13, 21, 40, 3, 3, 1)],
+                         ids=str)
+def test_conv_f16_filter_at_odd_element_offset(t, orc):
+    """An fp16 filter that starts 2 bytes past a 4-byte boundary gives the
+    exact results when the kernels gather it themselves (no workspace; the
+    row-staged kernel's dword-wide gather needs a 4-byte-aligned filter and
+    takes its per-entry gather here) and when it is prepacked."""
+    import torch
+    dev = device()
+    sh = _shape(t, "f16")
+    xi, wi = workloads.make_inputs(sh, seed=64, mode="int")
+    ref = orc.conv_direct(xi, wi, sh.s)
+    big = torch.zeros(wi.size + 1, dtype=torch.float16, device=dev)
+    big[1:] = torch.from_numpy(np.ascontiguousarray(wi).reshape(-1)).to(dev)
+    wv = big[1:].view(wi.shape)
+    assert wv.data_ptr() % 4 == 2
+    xt = to_dev(xi, dev)
+    for kind in (None, "filter"):
+        note(f"conv fp16 filter at odd offset {sh.describe()} ws={kind}")
+        y = m.conv2d(xt, wv, sh.s, ws=_ws(sh, kind, dev)).cpu().numpy()
         assert_exact(y, ref, f"{sh.describe()} ws={kind}")
     torch.cuda.synchronize()
 
