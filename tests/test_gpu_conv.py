@@ -261,6 +261,9 @@ def test_conv_f16_fused_tilings(t, env, orc, monkeypatch):
 # Shapes the row-staged fp16 kernel takes with a prepacked filter (even column
 # stride, Wf <= 8, Wi a multiple of 8, Ci even): several tiles and channel
 # tiles, image breaks inside tiles, rectangles, Wf = 8 (no padded taps).
+# Without a workspace, 8 waves gather the filter with dword loads up to 16
+# per thread and stage, past that (and with 4 waves on the 7x7 shapes) one
+# 16-byte entry per thread.
 ROWS = [
     (2, 16, 30, 32, 70, 7, 7, 2),
     (1, 64, 40, 40, 64, 7, 7, 2),
@@ -271,6 +274,7 @@ ROWS = [
     (2, 8, 20, 64, 128, 5, 3, (2, 2)),
     (2, 2, 65, 64, 40, 3, 3, 2),      # tiles aligned to images
     (2, 4, 24, 32, 64, 16, 8, 2),     # 16 dword gather loads per thread (8 waves)
+    (2, 4, 24, 32, 64, 17, 8, 2),     # 17 would be needed: per-entry gather
 ]
 
 
