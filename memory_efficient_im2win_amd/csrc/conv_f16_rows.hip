@@ -28,8 +28,10 @@
 //    registers, no transposition. Three stage buffers rotate; the loads of
 //    stage s+2 are issued as stage s starts, and one barrier per stage both
 //    publishes stage s and frees the buffer of stage s-1. Without a
-//    prepacked filter the slices of stage s+2 are gathered from w after the
-//    MFMAs of stage s instead.
+//    prepacked filter the slices of stage s+2 are gathered from w instead
+//    (loaded as stage s starts, written after its MFMAs); there two buffers
+//    (loads one stage ahead) are used when they let a stage hold twice the
+//    channels, which halves the gather rounds.
 //  * The loads are issued from inline assembly so that the compiler, which
 //    would otherwise wait for every outstanding LDS load before each LDS
 //    read, leaves the pipelining to the explicit waits here.
@@ -46,7 +48,7 @@ namespace {
 constexpr int kRowsLds = 160 * 1024;
 constexpr int kCoT = 64;                  // output channels per tile
 constexpr int kNB = 4;                    // 32-pixel blocks per wave
-constexpr int kBufs = 3;                  // stage buffers
+constexpr int kBufsMax = 3;               // stage buffers (3: loads two stages ahead; 2: one)
 constexpr int kSlack = 2048;              // LDS past the last buffer: reads one pair past a stage
 constexpr uint32_t kMiss = 0xFFFFFFF0u;   // vector offset past every accepted buffer
 constexpr int kGL = 16;                   // most dword gather loads per thread and stage
@@ -61,6 +63,7 @@ struct RowsArgs {
     int Cg, S, NX, NS, Copad;       // channels per stage, slices per stage (Cg*Hf), row kilobytes
                                     // per stage, stages (Ci/Cg), prepacked filter channels
     uint32_t stage_bytes;           // (S + NX) KB: filter slices, then rows
+    int bufs;                       // stage buffers: loads run bufs - 1 stages ahead
     uint32_t dummy;                 // LDS byte offset of the landing kilobyte of unused loads
     uint32_t lds_bytes;
     uint32_t xbytes, ybytes, wbytes, worig;   // x, y, prepacked filter, filter in w's layout
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
     };
     const bool coal = !WPK && a.gl > 0;
     if (coal && a.c.Wf < 8) {
-        for (int e = tid; e < kBufs * a.S * 64; e += NT) {
+        for (int e = tid; e < a.bufs * a.S * 64; e += NT) {
             const int b = e / (a.S * 64);
             uint16_t* F = reinterpret_cast<uint16_t*>(smem + (size_t)b * a.stage_bytes);
             const int el = e - b * a.S * 64;
@@ -429,26 +432,34 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
     }
 
     const int nk = a.S >> 1;   // K steps per stage (S is even)
+    const int D = a.bufs - 1;  // stages the loads run ahead (2 or 1)
     issue(0, 0);
-    if (a.NS > 1) issue(1, 1); else issue_none();
+    if (D == 2) {
+        if (a.NS > 1) issue(1, 1); else issue_none();
+    }
     if (coal) {
         gather_load(0);
         gather_store(0);
-        if (a.NS > 1) {
+        if (D == 2 && a.NS > 1) {
             gather_load(1);
             gather_store(1);
         }
     } else if (!WPK) {
         gather(0, 0);
-        if (a.NS > 1) gather(1, 1);
+        if (D == 2 && a.NS > 1) gather(1, 1);
     }
     for (int s = 0; s < a.NS; ++s) {
-        wait_loads<DMAX>();   // this wave's loads of stage s have landed
+        // This wave's loads of stage s have landed (those of stage s+1 may
+        // still be in flight with three buffers).
+        if (D == 2)
+            wait_loads<DMAX>();
+        else
+            wait_loads<0>();
         __syncthreads();      // every wave's; and stage s-1's buffer is free
-        if (s + 2 < a.NS) issue(s + 2, (s + 2) % kBufs); else issue_none();
-        if (coal && s + 2 < a.NS) gather_load(s + 2);
+        if (s + D < a.NS) issue(s + D, (s + D) % a.bufs); else issue_none();
+        if (coal && s + D < a.NS) gather_load(s + D);
 
-        const unsigned char* A = smem + (size_t)(s % kBufs) * a.stage_bytes;
+        const unsigned char* A = smem + (size_t)(s % a.bufs) * a.stage_bytes;
         const unsigned char* X = A + (size_t)a.S * 1024;
         Frags f0, f1;
         skh = hl < Hf ? hl : hl - Hf;       // slice hl (Hf = 1: channel 1, row 0)
@@ -471,12 +482,12 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
             __builtin_amdgcn_sched_barrier(0);
         }
         if (t < nk) mma(f0);
-        // Stage s+2's buffer was freed by the barrier above.
-        if (!WPK && s + 2 < a.NS) {
+        // Stage s+D's buffer was freed by the barrier above.
+        if (!WPK && s + D < a.NS) {
             if (coal)
-                gather_store((s + 2) % kBufs);
+                gather_store((s + D) % a.bufs);
             else
-                gather(s + 2, (s + 2) % kBufs);
+                gather(s + D, (s + D) % a.bufs);
         }
     }
     wait_loads<0>();   // the last (unused) loads have landed before the workgroup ends
@@ -532,8 +543,10 @@ constexpr int kDmax[] = {4, 5, 6, 8, 12, 16};
 // Ci a multiple of the stage's channel count, tensors addressable with
 // 32-bit buffer offsets. IM2WIN_F16_ROWS=0 turns the kernel off,
 // IM2WIN_F16_ROWS_NWV picks the waves per workgroup and
-// IM2WIN_F16_ROWS_SWIZZLE=0 keeps tiles in launch order (tuning and tests).
-bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax)
+// IM2WIN_F16_ROWS_SWIZZLE=0 keeps tiles in launch order and
+// IM2WIN_F16_ROWS_BUFS=2 or 3 fixes the stage buffers (tuning and tests).
+// bufs: stage buffers to plan for (0: three, or IM2WIN_F16_ROWS_BUFS).
+bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax, int bufs_want = 0)
 {
     if (env_int("IM2WIN_F16_ROWS", 1) == 0) return false;
     if (c.Wf > 8 || c.sw % 2 != 0 || c.Wi % 8 != 0 || c.Hf * c.Wf > 256) return false;
@@ -545,6 +558,8 @@ bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax)
     if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
     const int64_t plane = (int64_t)c.Ho * c.Wo;
     const int env_nwv = env_int("IM2WIN_F16_ROWS_NWV", 0);
+    const int env_bufs = env_int("IM2WIN_F16_ROWS_BUFS", 0);
+    const int bufs = env_bufs == 2 || env_bufs == 3 ? env_bufs : bufs_want == 2 ? 2 : kBufsMax;
     bool found = false;
     for (int v : {8, 4}) {
         if (env_nwv && v != env_nwv) continue;
@@ -570,13 +585,14 @@ bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax)
                 }
             if (!dm) continue;
             const int64_t stage = (int64_t)(S + NX) * 1024;
-            const int64_t lds = kBufs * stage + 1024 + kSlack;
+            const int64_t lds = bufs * stage + 1024 + kSlack;
             if (lds > kRowsLds) continue;
             a.Cg = cg;
             a.S = S;
             a.NX = NX;
             a.stage_bytes = (uint32_t)stage;
-            a.dummy = (uint32_t)(kBufs * stage);
+            a.dummy = (uint32_t)(bufs * stage);
+            a.bufs = bufs;
             a.lds_bytes = (uint32_t)lds;
             nwv = v;
             dmax = dm;
@@ -711,6 +727,17 @@ int launch_conv_f16_rows(const uint16_t* x, const void* wp, const uint16_t* w, f
     // Rows are fetched in 16-byte chunks from 16-byte boundaries.
     if ((uintptr_t)x % 16 != 0 || (uintptr_t)wp % 16 != 0) return -1;
     const uint4* w4 = static_cast<const uint4*>(wp);
+    if (!w4) {
+        // Gathering the filter costs a round of loads per stage: with two
+        // buffers a stage may hold twice the channels (half the stages).
+        RowsArgs a2;
+        int nwv2, dmax2;
+        if (plan(c, a2, nwv2, dmax2, 2) && a2.Cg > a.Cg) {
+            a = a2;
+            nwv = nwv2;
+            dmax = dmax2;
+        }
+    }
     a.gl = a.gjs = a.grs = 0;
     a.RD = 1;
     a.wco = a.wfm = 0;

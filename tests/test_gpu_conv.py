@@ -309,6 +309,22 @@ def test_conv_f16_row_staged(t, nwv, orc, monkeypatch):
         assert_exact(_run(sh, "f16", xi, wi, kind), refi, sh.describe())
 
 
+@pytest.mark.parametrize("bufs", ["2", "3"])
+@pytest.mark.parametrize("t", ROWS, ids=str)
+def test_conv_f16_row_staged_buffers(t, bufs, orc, monkeypatch):
+    """Two stage buffers (loads one stage ahead; without a workspace the
+    kernel picks them when a stage can then hold twice the channels) and
+    three (two stages ahead), with the filter prepacked and gathered: exact
+    on integer inputs."""
+    monkeypatch.setenv("IM2WIN_F16_ROWS_BUFS", bufs)
+    sh = _shape(t, "f16")
+    xi, wi = workloads.make_inputs(sh, seed=44, mode="int")
+    refi = orc.conv_direct(xi, wi, sh.s)
+    for kind in ("filter", None):
+        note(f"conv fp16 row-staged buffers={bufs} {sh.describe()} ws={kind}")
+        assert_exact(_run(sh, "f16", xi, wi, kind), refi, sh.describe())
+
+
 @pytest.mark.parametrize("t", [(2, 4, 14, 16, 40, 3, 5, 2), (2, 4, 15, 24, 40, 3, 7, 2)], ids=str)
 def test_conv_f16_row_staged_special_values(t, orc):
     """Infinities and NaN in the input reach exactly the outputs whose windows
