@@ -49,6 +49,7 @@ constexpr int kMaxSlices = 64;            // filter slices (c, kh) held in LDS
 constexpr int kBatch = 8;                 // row chunks a thread has in flight
 constexpr int kSlackT = 2048;             // A reads run one pair past the filter
 constexpr uint32_t kMissT = 0xFFFFFFF0u;  // vector offset past every accepted buffer
+constexpr int kGT = 16;                   // dword gather loads in flight per thread
 
 struct ThinArgs {
     ConvShape c;
@@ -66,6 +67,12 @@ struct ThinArgs {
     uint32_t xbytes, ybytes, wbytes, worig;   // x, y, prepacked filter, filter in w's layout
     uint32_t mask[4];               // B dwords: halves kw >= Wf cleared
     FastDiv divWo, divHo, divCH, divRIN;
+    // Dword filter gather (no prepacked filter, w 4-byte aligned, Ci*Hf*Wf
+    // and Wf at least 2): the tile's filter is one run of 64*chw halves
+    // (chw = Ci*Hf*Wf per channel); chwm = ceil(2^32 / chw), wfm =
+    // ceil(2^32 / Wf). gd = 0: one 16-byte entry per thread and load round.
+    int gd;
+    uint32_t chw, chwm, wfm;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tbuf(const void* base, uint32_t bytes)
@@ -174,6 +181,46 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
         const __amdgpu_buffer_rsrc_t r = tbuf(wp, a.wbytes);
         for (int m = wave; m < a.S; m += kNW)
             dma16t(r, lbase + (uint32_t)m * 1024, (uint32_t)((m * a.Copad + co0 + lane) * 16));
+    } else if (a.gd) {
+        // The tile's 64 channels' taps are one run of w: consecutive
+        // threads read consecutive dwords of it, and each half goes to its
+        // entry (channel j = f / chw of the tile, slice t / Wf, column
+        // t % Wf, t = f % chw). Channels past Co fall outside w's range and
+        // read zeros; the halves kw >= Wf of every entry are zeroed here too.
+        const __amdgpu_buffer_rsrc_t r = tbuf(w, a.worig);
+        unsigned short* F = reinterpret_cast<unsigned short*>(smem);
+        const uint32_t base = (uint32_t)co0 * a.chw * 2;
+        const int nd = 32 * (int)a.chw;
+        for (int d0 = 0; d0 < nd; d0 += kGT * kNT) {
+            int dd = d0 + tid;
+            // Opaque: keeps the per-round index math inside the round.
+            asm volatile("" : "+v"(dd));
+            uint32_t v[kGT];
+#pragma unroll
+            for (int k = 0; k < kGT; ++k) {
+                const int d = dd + k * kNT;
+                v[k] = __builtin_amdgcn_raw_buffer_load_b32(
+                    r, (int)(d < nd ? base + 4 * (uint32_t)d : kMissT), 0, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < kGT; ++k) {
+                const int d = dd + k * kNT;
+                if (d < nd) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const uint32_t f = 2 * (uint32_t)d + e;
+                        const uint32_t j = __umulhi(f, a.chwm);
+                        const uint32_t t = f - j * a.chw;
+                        const uint32_t m = __umulhi(t, a.wfm);
+                        const uint32_t kw = t - m * (uint32_t)a.c.Wf;
+                        F[(m * 64 + j) * 8 + kw] = (unsigned short)(v[k] >> (16 * e));
+                    }
+                }
+            }
+        }
+        if (a.c.Wf < 8)
+            for (int e = tid; e < a.S * 64; e += kNT)
+                for (int kw = a.c.Wf; kw < 8; ++kw) F[e * 8 + kw] = 0;
     } else {
         const __amdgpu_buffer_rsrc_t r = tbuf(w, a.worig);
         uint4* F = reinterpret_cast<uint4*>(smem);
@@ -488,6 +535,21 @@ int launch_conv_f16_thin(const uint16_t* x, const void* wp, const uint16_t* w, f
     const uint4* w4 = static_cast<const uint4*>(wp);
     const bool xvec = c.Wi % 8 == 0 && (uintptr_t)x % 16 == 0;
     const bool nb2 = a.P == 32 * kNW * 2;
+    a.gd = 0;
+    a.chw = (uint32_t)(c.Ci * c.Hf * c.Wf);
+    a.chwm = a.wfm = 0;
+    // The run of a tile starts at co0*chw halves, co0 a multiple of 64:
+    // on a dword when w is. Co*chw even: w ends on a dword, so no dword
+    // holds both a last tap and bytes past w (a range check zeroes such a
+    // dword whole). Offsets up to the last tile's end must stay below the
+    // miss offset.
+    if (!w4 && (uintptr_t)w % 4 == 0 && a.chw >= 2 && c.Wf >= 2 &&
+        ((int64_t)c.Co * a.chw) % 2 == 0 &&
+        (int64_t)a.co_tiles * 64 * a.chw * 2 < (int64_t)kMissT) {
+        a.gd = 1;
+        a.chwm = (uint32_t)(((uint64_t)1 << 32) / a.chw + 1);
+        a.wfm = (uint32_t)(((uint64_t)1 << 32) / (uint64_t)c.Wf + 1);
+    }
     if (w4) return nb2 ? launch_nb<2, true>(x, w4, w, y, a, xvec, stream)
                        : launch_nb<4, true>(x, w4, w, y, a, xvec, stream);
     return nb2 ? launch_nb<2, false>(x, w4, w, y, a, xvec, stream)

@@ -478,7 +478,7 @@ def test_conv_f16_filter_pack_tap_counts(t, orc):
 # widths that are multiples of 8 (16-byte row loads), several channel tiles,
 # row strides below and above the filter height, a 1x1 filter, cv3 images.
 THIN = [
-    (2, 3, 47, 45, 37, 7, 7, 2),
+    (2, 3, 47, 45, 37, 7, 7, 2),      # odd filter length: per-entry gather without a workspace
     (3, 3, 35, 64, 64, 7, 7, 2),
     (2, 1, 30, 31, 70, 5, 3, (1, 2)),
     (2, 5, 20, 40, 130, 3, 8, 2),
