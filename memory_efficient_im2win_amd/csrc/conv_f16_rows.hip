@@ -371,8 +371,9 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
     // dwords in w (channel co0+j, input channels sg*Cg.., all Hf*Wf taps),
     // read with consecutive threads on consecutive dwords of a run. Each of
     // a dword's two halves goes to the entry of its slice (tap t of the run
-    // is slice t / Wf, column t % Wf). The loads of stage s+2 go out with
-    // stage s's direct loads and are written to LDS after its MFMAs.
+    // is slice t / Wf, column t % Wf). The loads of stage s+D (D: stages the
+    // loads run ahead) go out with stage s's direct loads and are written to
+    // LDS after its MFMAs.
     // Channels past Co fall outside w's range and read zeros; halves
     // kw >= Wf of every entry are zeroed once below and never written again.
     uint32_t gv[kGL];
