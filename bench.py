@@ -339,6 +339,37 @@ def ablation(keys, steps):
         print(f"| {key} | {label} | {tf:.1f} | {us:.1f} | {fr:.3f} | {wsb:,} |")
 
 
+def fill_rate(key, sh, steps, warmup):
+    """torch's fill_ and copy_ over the fp32 output size of sh, timed with HIP
+    events: the write (and read + write) rates that plain streaming kernels
+    reach, beside which an output-bound convolution is read."""
+    import torch
+    dev = torch.device("cuda:0")
+    import memory_efficient_im2win_amd as m
+    Ho, Wo = m.output_dims(sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s)
+    n = sh.N * sh.Co * Ho * Wo
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    z = torch.empty(n, dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        y.fill_(1.0)
+        z.copy_(y)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(steps):
+        y.fill_(1.0)
+    ev[1].record()
+    for _ in range(steps):
+        z.copy_(y)
+    ev[2].record()
+    torch.cuda.synchronize()
+    f_us = ev[0].elapsed_time(ev[1]) / steps * 1e3
+    c_us = ev[1].elapsed_time(ev[2]) / steps * 1e3
+    return {"workload": key, "bytes": n * 4, "steps": steps, "fill_us": round(f_us, 2),
+            "fill_TBps": round(n * 4 / f_us / 1e6, 3), "copy_us": round(c_us, 2),
+            "copy_TBps_read_plus_write": round(2 * n * 4 / c_us / 1e6, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -359,6 +390,10 @@ def main():
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of this bench into "
                          "profiles/traffic.json for the current kernel sources, then exit")
+    ap.add_argument("--fill-rate", action="store_true",
+                    help="time a plain fill and a device copy of the workload's fp32 output "
+                         "size (the write rate an HBM-bound kernel can reach), print one "
+                         "JSON line and exit")
     ap.add_argument("--ablation", action="store_true",
                     help="time every layer under the library's variant switches and print a "
                          "Markdown table instead of the JSON line")
@@ -404,6 +439,12 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+
+    if args.fill_rate:
+        print(json.dumps(fill_rate(args.workload, workloads.BY_KEY[args.workload], args.steps,
+                                   args.warmup)),
+              flush=True)
+        return
 
     sh = workloads.BY_KEY[args.workload]
     log(f"[bench] headline {sh.describe()} mode={args.mode} steps={args.steps} warmup={args.warmup}")
