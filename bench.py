@@ -8,8 +8,10 @@ Memory-efficient Im2win Convolution with Multi-precision Support on GPU CUDA
 and Tensor Cores"): N=32, 3x227x227 input, 96 11x11 filters, stride 4, fp32
 inputs, products and accumulation (on the fp32 matrix instructions by
 default; mode fused_valu forces the vector-ALU kernel). The other Table I
-layers (cv5 fp32 N=1; cv5, cv3, cv4 fp16 on the matrix cores) are timed the
-same way and reported under "layers".
+layers (cv5 fp32 N=1; cv5, cv3, cv4 fp16 on the matrix cores; cv2 fp32) are
+timed the same way and reported under "layers", each with the roofline of
+its kernel, the im2win transform timed on its own, and the CPU oracle timed
+on a bounded sample of it.
 
 Prints ONE JSON line on stdout (rank 0); progress goes to stderr.
 """
@@ -43,9 +45,12 @@ KERNEL_SOURCES = ["conv_f32_mfma.hip", "conv_f32.hip", "conv_f16_fused.hip", "co
                   "conv_f16.hip", "conv_generic.hip", "pack.hip", "im2col.hip", "nhwc.hip",
                   "api.hip", "common.hpp", "kernels.hpp"]
 # Modes: fused (no workspace), fused_valu (fp32 on the vector-ALU kernel),
-# prepacked (fp16 filter prepacked into a small workspace), materialized
-# (im2win tensor in HBM).
+# prepacked (fp16 fused with the filter prepacked per call into a small
+# workspace, conv2d_fused), materialized (the im2win tensor of the whole batch
+# in HBM: a workspace of exactly workspace_bytes(N)).
 MODES = ["fused", "fused_valu", "prepacked", "materialized"]
+# Timed calls per layer (median and min reported): 50, and 20 for cv4.
+LAYER_STEPS = {"cv4_f16_n64": 20}
 
 
 CONV_KERNELS = ("conv_f32_mfma_kernel", "conv_f32_kernel", "conv_f16_fused_kernel",
@@ -69,18 +74,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def _knobs_of(mode):
+    return {"f32_valu": 1} if mode == "fused_valu" else {}
+
+
 def time_layer(sh, mode, steps, warmup):
-    """Returns dict with per-launch-averaged ms and workspace bytes."""
-    if mode == "fused_valu":
-        old = os.environ.get("IM2WIN_F32_PATH")
-        os.environ["IM2WIN_F32_PATH"] = "valu"
-        try:
-            return time_layer(sh, "fused", steps, warmup)
-        finally:
-            if old is None:
-                os.environ.pop("IM2WIN_F32_PATH", None)
-            else:
-                os.environ["IM2WIN_F32_PATH"] = old
+    """Times `steps` calls of one mode on layer sh (inputs resident in HBM,
+    warm caches) with HIP events around each call on the stream the library
+    launches on. Returns per-call mean, median and min, and the step rate."""
+    import torch
+    import memory_efficient_im2win_amd as m
+    with m.knobs(**_knobs_of(mode)):
+        return _time_layer(sh, mode, steps, warmup)
+
+
+def _time_layer(sh, mode, steps, warmup):
     import torch
     import memory_efficient_im2win_amd as m
     dev = torch.device("cuda:0")
@@ -97,15 +105,15 @@ def time_layer(sh, mode, steps, warmup):
         y = torch.empty((sh.N, Ho, Wo, sh.Co), dtype=torch.float32, device=dev)
         wsb = m.nhwc_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
                                      sh.elem_bytes)
-        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     elif mode == "im2col":
         wsb = m.im2col_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
                                        sh.elem_bytes)
+    elif mode == "materialized":
+        wsb = m.workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
+    elif mode == "prepacked" and sh.dtype == "f16":
+        wsb = m.fused_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s)
+    if wsb:
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    elif mode != "fused" and mode != "direct":
-        wsb = m.conv_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
-                                     sh.elem_bytes, mode == "materialized")
-        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
 
     def call():
         if mode == "nhwc_materialized":
@@ -114,8 +122,28 @@ def time_layer(sh, mode, steps, warmup):
             m.conv2d_im2col(xt, wt, sh.s, ws=ws, out=y)
         elif mode == "direct":
             m.conv2d_direct(xt, wt, sh.s, out=y)
+        elif mode == "prepacked" and sh.dtype == "f16":
+            m.conv2d_fused(xt, wt, sh.s, fws=ws, out=y)
         else:
             m.conv2d(xt, wt, sh.s, ws=ws, out=y)
+    res = _time_calls(call, steps, warmup)
+    f = flops(sh, Ho, Wo)
+    res.update({
+        "tflops": f / (res["ms_per_step"]) / 1e9,
+        "tflops_median": f / res["ms_per_launch_median"] / 1e9,
+        "flops": f,
+        "workspace_bytes": wsb,
+        "Ho": Ho, "Wo": Wo,
+    })
+    del ws, y, xt, wt
+    torch.cuda.empty_cache()
+    return res
+
+
+def _time_calls(call, steps, warmup):
+    """HIP events around each of `steps` calls and around all of them, on
+    torch's current stream (the stream the binding passes to the library)."""
+    import torch
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -133,26 +161,52 @@ def time_layer(sh, mode, steps, warmup):
     torch.cuda.synchronize()
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     total_ms = t_all0.elapsed_time(t_all1)
-    f = flops(sh, Ho, Wo)
-    res = {
+    return {
         "ms_per_step": total_ms / steps,
         "ms_per_launch_avg": float(np.mean(per)),
+        "ms_per_launch_median": float(np.median(per)),
         "ms_per_launch_min": float(np.min(per)),
-        "tflops": f / (total_ms / steps) / 1e9,
-        "flops": f,
-        "workspace_bytes": wsb,
-        "Ho": Ho, "Wo": Wo,
     }
-    del ws, y, xt, wt
+
+
+def time_pack(sh, steps, warmup):
+    """The im2win transform alone (im2win_pack of the whole batch): per-call
+    median and min, and the rate of its algorithmic bytes (x read + the
+    im2win tensor written) against the HBM peak."""
+    import torch
+    import memory_efficient_im2win_amd as m
+    dev = torch.device("cuda:0")
+    x, _ = workloads.make_inputs(sh, seed=0)
+    xt = torch.from_numpy(x).to(dev)
+    Ho, _ = m.output_dims(sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s)
+    out = torch.empty((sh.N, sh.Ci, Ho, sh.Wi * sh.Hf), dtype=xt.dtype, device=dev)
+    r = _time_calls(lambda: m.pack(xt, sh.Hf, sh.Wf, sh.s, out=out), steps, warmup)
+    nbytes = (xt.numel() + out.numel()) * xt.element_size()
+    del xt, out
     torch.cuda.empty_cache()
-    return res
+    gbs = nbytes / (r["ms_per_launch_median"] * 1e-3) / 1e9
+    return {"kernel": "pack_kernel", "us_median": round(r["ms_per_launch_median"] * 1e3, 2),
+            "us_min": round(r["ms_per_launch_min"] * 1e3, 2), "bytes": nbytes,
+            "GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(sh, budget_s=12.0):
     """The oracle (plain C loops, fp64 accumulation) on the host cores, on a
     bounded sample of the workload: as many images as fit the time budget,
     and when the whole batch takes less than that, the whole batch repeated
-    until the budget is used. Scaled to TFLOPS."""
+    until the budget is used. Scaled to TFLOPS. The oracle's im2win transform
+    of the same sample is timed beside it."""
     import oracle
     O = oracle.default()
     x, w = workloads.make_inputs(sh, seed=0)
@@ -167,6 +221,10 @@ def cpu_baseline(sh, budget_s=12.0):
         O.conv_direct(x[:n], w, sh.s)
         dt += time.perf_counter() - t0
         reps += 1
+    t0 = time.perf_counter()
+    pk = O.im2win_pack(x[:n], sh.Hf, sh.Wf, sh.s)
+    tp = time.perf_counter() - t0
+    pbytes = (x[:n].nbytes + pk.nbytes)
     f = 2 * n * reps * sh.Co * Ho * Wo * sh.Ci * sh.Hf * sh.Wf
     what = f"{n} of {sh.N} images" + (f", {reps} times" if reps > 1 else "")
     return {
@@ -174,7 +232,10 @@ def cpu_baseline(sh, budget_s=12.0):
         "unit": "TFLOP/s",
         "cores": O.num_threads(),
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"{what}, of {sh.name} ({sh.dtype} inputs, fp64 accumulation), {dt:.2f} s",
+        "pack_s": round(tp, 4),
+        "pack_GBps": round(pbytes / tp / 1e9, 3),
     }
 
 
@@ -218,7 +279,8 @@ def baselines(sh, entry):
     peak = PEAK_FP32_MFMA_TFLOPS if sh.dtype == "f32" else PEAK_FP16_MFMA_TFLOPS
     for mode in ("im2col", "direct", "nhwc_materialized"):
         r = time_layer(sh, mode, 3, 1)
-        entry[mode] = {"tflops": round(r["tflops"], 3), "us_per_call": round(r["ms_per_step"] * 1e3, 2),
+        entry[mode] = {"tflops": round(r["tflops_median"], 3),
+                       "us_per_call": round(r["ms_per_launch_median"] * 1e3, 2),
                        "frac_of_peak": round(r["tflops"] / peak, 4),
                        "workspace_bytes": r["workspace_bytes"]}
         log(f"[bench] {sh.name} {mode}: {r['tflops']:.2f} TFLOP/s "
@@ -279,32 +341,29 @@ def ingest_pmc(fetch_csv, write_csv, copy_bytes=1 << 30):
     return out
 
 
-# Variants timed by --ablation: (label, mode, environment) per precision. The
-# environment switches are the library's own planner overrides.
+# Variants timed by --ablation: (label, mode, knobs) per precision. The knobs
+# are the library's own planner overrides (im2win_set_knob).
 ABLATION = {
     "f32": [("matrix cores, planner's choice", "fused", {}),
-            ("matrix cores, 4 waves/workgroup", "fused", {"IM2WIN_F32_NW": "4"}),
-            ("matrix cores, 8 waves/workgroup", "fused", {"IM2WIN_F32_NW": "8"}),
-            ("matrix cores, 12 waves/workgroup", "fused", {"IM2WIN_F32_NW": "12"}),
-            ("vector ALU", "fused", {"IM2WIN_F32_PATH": "valu"}),
+            ("matrix cores, 4 waves/workgroup", "fused", {"f32_nw": 4, "f32_ksplit": 1}),
+            ("matrix cores, 8 waves/workgroup", "fused", {"f32_nw": 8, "f32_ksplit": 1}),
+            ("matrix cores, 12 waves/workgroup", "fused", {"f32_nw": 12, "f32_ksplit": 1}),
+            ("matrix cores, K shared by 8 waves", "fused", {"f32_ksplit": 8}),
+            ("vector ALU", "fused", {"f32_valu": 1}),
             ("materialised im2win tensor", "materialized", {})],
-    "f16": [("fused, filter gathered in-kernel", "fused", {}),
-            ("fused, filter prepacked (planner's kernel)", "prepacked", {}),
-            ("prepacked, row-staged kernel with 4 waves", "prepacked", {"IM2WIN_F16_ROWS_NWV": "4"}),
-            ("prepacked, row-staged, tiles in launch order", "prepacked",
-             {"IM2WIN_F16_ROWS_SWIZZLE": "0"}),
-            ("prepacked, thin-layer kernel with 512-pixel tiles", "prepacked",
-             {"IM2WIN_F16_THIN_NB": "4"}),
+    "f16": [("fused, filter gathered in-kernel (planner's kernel)", "fused", {}),
+            ("fused, filter prepacked per call", "prepacked", {}),
+            ("prepacked, row-staged kernel with 4 waves", "prepacked", {"f16_rows_nwv": 4}),
+            ("prepacked, row-staged, tiles in launch order", "prepacked", {"tile_order": 1}),
+            ("prepacked, thin-layer kernel with 512-pixel tiles", "prepacked", {"f16_thin_nb": 4}),
             ("prepacked, wide-tile kernel with 4 waves of 4 x 4 blocks", "prepacked",
-             {"IM2WIN_F16_WIDE_NW": "4"}),
+             {"f16_wide_nw": 4}),
             ("prepacked, channel-interleaved kernel", "prepacked",
-             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_THIN": "0", "IM2WIN_F16_WIDE": "0"}),
+             {"f16_rows": -1, "f16_thin": -1, "f16_wide": -1}),
             ("channel-interleaved, 8 waves along pixels", "prepacked",
-             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_THIN": "0", "IM2WIN_F16_WIDE": "0",
-              "IM2WIN_F16_WPX": "8"}),
+             {"f16_rows": -1, "f16_thin": -1, "f16_wide": -1, "f16_wpx": 8}),
             ("channel-interleaved, >= 2 filter parts per group", "prepacked",
-             {"IM2WIN_F16_ROWS": "0", "IM2WIN_F16_THIN": "0", "IM2WIN_F16_WIDE": "0",
-              "IM2WIN_F16_NWH": "2"}),
+             {"f16_rows": -1, "f16_thin": -1, "f16_wide": -1, "f16_nwh": 2}),
             ("materialised im2win tensor", "materialized", {})],
 }
 
@@ -317,23 +376,15 @@ def ablation(keys, steps):
     rows = []
     for key in keys:
         sh = workloads.BY_KEY[key]
-        for label, mode, env in ABLATION[sh.dtype]:
-            saved = {k: os.environ.get(k) for k in env}
-            os.environ.update(env)
-            try:
+        for label, mode, kn in ABLATION[sh.dtype]:
+            with m.knobs(**kn):
                 r = time_layer(sh, mode, steps, 3)
-            finally:
-                for k, v in saved.items():
-                    if v is None:
-                        os.environ.pop(k, None)
-                    else:
-                        os.environ[k] = v
             peak = PEAK_FP32_MFMA_TFLOPS if sh.dtype == "f32" else PEAK_FP16_MFMA_TFLOPS
-            rows.append((key, label, r["tflops"], r["ms_per_launch_avg"] * 1e3, r["tflops"] / peak,
-                         r["workspace_bytes"]))
-            log(f"[ablation] {key} {label}: {r['tflops']:.1f} TFLOP/s")
+            rows.append((key, label, r["tflops_median"], r["ms_per_launch_median"] * 1e3,
+                         r["tflops_median"] / peak, r["workspace_bytes"]))
+            log(f"[ablation] {key} {label}: {r['tflops_median']:.1f} TFLOP/s")
     torch.cuda.synchronize()
-    print("| layer | variant | TFLOP/s | us per call | fraction of peak | workspace bytes |")
+    print("| layer | variant | TFLOP/s | us per call (median) | fraction of peak | workspace bytes |")
     print("|---|---|---|---|---|---|")
     for key, label, tf, us, fr, wsb in rows:
         print(f"| {key} | {label} | {tf:.1f} | {us:.1f} | {fr:.3f} | {wsb:,} |")
@@ -368,6 +419,81 @@ def fill_rate(key, sh, steps, warmup):
     return {"workload": key, "bytes": n * 4, "steps": steps, "fill_us": round(f_us, 2),
             "fill_TBps": round(n * 4 / f_us / 1e6, 3), "copy_us": round(c_us, 2),
             "copy_TBps_read_plus_write": round(2 * n * 4 / c_us / 1e6, 3)}
+
+
+def peak_of(sh, mode):
+    """(bound, peak TFLOP/s) of a layer's convolution kernel in a mode."""
+    if sh.dtype == "f16":
+        return "mfma", PEAK_FP16_MFMA_TFLOPS
+    if mode == "fused_valu" or mode == "materialized":
+        return "alu", PEAK_FP32_VECTOR_TFLOPS
+    return "mfma", PEAK_FP32_MFMA_TFLOPS
+
+
+def kernel_of(sh, mode):
+    import memory_efficient_im2win_amd as m
+    kmode = {"fused": "fused", "fused_valu": "fused", "prepacked": "prepacked",
+             "materialized": "materialized"}[mode]
+    with m.knobs(**_knobs_of(mode)):
+        return m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
+                                  sh.elem_bytes, kmode)
+
+
+def roofline_of(key, sh, mode, r):
+    """Roofline of a layer's dominant kernel. In the fused modes one call is
+    one kernel launch, so the per-call event time on the stream the library
+    launches on is that kernel's time (average over the timed calls). In the
+    prepacked mode a call is the filter prepack plus the convolution kernel,
+    and in the materialised mode the im2win transform plus the convolution
+    kernel; their per-call time includes those launches."""
+    bound, peak = peak_of(sh, mode)
+    achieved = r["flops"] / (r["ms_per_launch_avg"] * 1e-3) / 1e12
+    return {
+        "bound": bound,
+        "achieved": round(achieved, 3),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": load_traffic(key, mode),
+        "kernel": kernel_of(sh, mode),
+        "launches_per_call": 1 if mode in ("fused", "fused_valu") else 2,
+        "launch_avg_us": round(r["ms_per_launch_avg"] * 1e3, 2),
+        "launch_median_us": round(r["ms_per_launch_median"] * 1e3, 2),
+        "launch_min_us": round(r["ms_per_launch_min"] * 1e3, 2),
+    }
+
+
+def layer_entry(key, args):
+    """Every mode of one layer: per-call median, min and mean, TFLOP/s (on the
+    median), the kernel and its roofline; the im2win transform alone; the
+    baselines; the CPU oracle on a bounded sample."""
+    lsh = workloads.BY_KEY[key]
+    steps = LAYER_STEPS.get(key, 50)
+    entry = {}
+    modes = ("fused", "fused_valu", "materialized") if lsh.dtype == "f32" else \
+        ("fused", "prepacked", "materialized")
+    for mode in modes:
+        r = time_layer(lsh, mode, steps, 5)
+        _, peak = peak_of(lsh, mode)
+        entry[mode] = {"tflops": round(r["tflops_median"], 3),
+                       "us_per_call": round(r["ms_per_launch_median"] * 1e3, 2),
+                       "us_min": round(r["ms_per_launch_min"] * 1e3, 2),
+                       "us_mean": round(r["ms_per_launch_avg"] * 1e3, 2),
+                       "frac_of_peak": round(r["tflops_median"] / peak, 4),
+                       "workspace_bytes": r["workspace_bytes"],
+                       "roofline": roofline_of(key, lsh, mode, r)}
+        log(f"[bench] {key} {mode}: {r['tflops_median']:.2f} TFLOP/s "
+            f"({r['ms_per_launch_median']*1e3:.1f} us/call median, "
+            f"{r['ms_per_launch_min']*1e3:.1f} min, ws {r['workspace_bytes']} B, "
+            f"{entry[mode]['roofline']['kernel']})")
+    entry["pack"] = time_pack(lsh, steps, 5)
+    log(f"[bench] {key} pack: {entry['pack']['us_median']} us, {entry['pack']['GBps']} GB/s")
+    if not args.no_baselines:
+        baselines(lsh, entry)
+    if not args.no_cpu:
+        entry["cpu_oracle"] = cpu_baseline(lsh, budget_s=2.5)
+        log(f"[bench] {key} cpu oracle {entry['cpu_oracle']['value']*1e3:.2f} GFLOP/s")
+    return entry
 
 
 def main():
@@ -454,61 +580,16 @@ def main():
     layers = {}
     if not args.no_layers:
         for key in LAYER_KEYS:
-            lsh = workloads.BY_KEY[key]
-            entry = {}
-            modes = ("fused", "fused_valu", "materialized") if lsh.dtype == "f32" else \
-                ("fused", "prepacked", "materialized")
-            for mode in modes:
-                r = time_layer(lsh, mode, max(5, args.steps // 2), 3)
-                peak = PEAK_FP32_MFMA_TFLOPS if lsh.dtype == "f32" else PEAK_FP16_MFMA_TFLOPS
-                entry[mode] = {"tflops": round(r["tflops"], 3), "us_per_call": round(r["ms_per_step"] * 1e3, 2),
-                               "frac_of_peak": round(r["tflops"] / peak, 4),
-                               "workspace_bytes": r["workspace_bytes"]}
-                log(f"[bench] {key} {mode}: {r['tflops']:.2f} TFLOP/s "
-                    f"({r['ms_per_step']*1e3:.1f} us/call, ws {r['workspace_bytes']} B)")
-            if not args.no_baselines:
-                baselines(lsh, entry)
-            layers[key] = entry
+            layers[key] = layer_entry(key, args)
 
-    # Roofline of the dominant kernel. For the headline (cv1, fused) one call
-    # is exactly one kernel launch, so the per-launch event time, taken on the
-    # stream the library launches on, is that kernel's time.
-    is_f32 = sh.dtype == "f32"
-    valu = args.mode == "fused_valu"
-    achieved = head["flops"] / (head["ms_per_launch_avg"] * 1e-3) / 1e12
-    peak = (PEAK_FP32_VECTOR_TFLOPS if valu else PEAK_FP32_MFMA_TFLOPS) if is_f32 \
-        else PEAK_FP16_MFMA_TFLOPS
-    # With a prepacked filter the library runs the row-staged fp16 kernel on
-    # shapes with an even column stride, Wf <= 8, Wi % 8 == 0 and even Ci.
-    sw = sh.s[1] if isinstance(sh.s, tuple) else sh.s
-    rows = (args.mode == "prepacked" and sh.Wf <= 8 and sw % 2 == 0 and sh.Wi % 8 == 0
-            and sh.Ci % 2 == 0)
-    # Otherwise, with a prepacked filter, layers with fewer than 8 input
-    # channels run the thin-layer kernel and layers with at least 128 output
-    # channels the wide-tile kernel (when their tiles fit LDS).
-    thin = (args.mode == "prepacked" and not rows and sh.Ci < 8 and sh.Wf <= 8 and sw % 2 == 0
-            and sh.Ci * sh.Hf <= 64)
-    wide = args.mode == "prepacked" and not rows and not thin and sh.Co >= 128
-    kernel = ("conv_f32_kernel" if valu else "conv_f32_mfma_kernel") if is_f32 else \
-        ("conv_f16_kernel" if args.mode == "materialized" else
-         "conv_f16_rows_kernel" if rows else "conv_f16_thin_kernel" if thin else
-         "conv_f16_wide_kernel" if wide else "conv_f16_fused_kernel")
-    roofline = {
-        "bound": "alu" if valu else "mfma",
-        "achieved": round(achieved, 3),
-        "peak": peak,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / peak, 4),
-        "traffic": load_traffic(args.workload, args.mode),
-        "kernel": kernel,
-        "launch_avg_us": round(head["ms_per_launch_avg"] * 1e3, 2),
-    }
+    roofline = roofline_of(args.workload, sh, args.mode, head)
 
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(sh)
         log(f"[bench] cpu oracle {cpu['value']*1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+    is_f32 = sh.dtype == "f32"
 
     out = {
         "metric": "conv TFLOPS (fp32 VALU, fp16 MFMA) + workspace bytes on cv1-cv5 shapes",

@@ -39,8 +39,11 @@
  *    exactly and accumulates in fp32.
  *  - `stream` is a hipStream_t (NULL: the legacy default stream). Work is
  *    enqueued and the call returns without synchronising. The library
- *    allocates no memory and keeps no state between calls; concurrent calls
- *    on different streams are safe when their output buffers differ.
+ *    allocates no device memory. Its only state is process-wide: the tuning
+ *    knobs (im2win_set_knob; default 0 everywhere), per-device kernel
+ *    attributes and the fp32 planner's occupancy cache, set up on first use
+ *    under a lock. Concurrent calls on different streams are safe when their
+ *    output and workspace buffers differ and no knob changes meanwhile.
  *  - Shape limits: every dimension >= 1, Hf <= Hi, Wf <= Wi, strides >= 1, and the
  *    per-image element counts Ci*Hi*Wi, Co*Ho*Wo, Ci*Ho*Wi*Hf and the filter
  *    size Co*Ci*Hf*Wf each below 2^31.
@@ -61,7 +64,7 @@ extern "C" {
 typedef enum {
     IM2WIN_OK = 0,
     IM2WIN_EINVAL = -1,     /* bad shape, stride, element size or NULL pointer */
-    IM2WIN_EWORKSPACE = -2, /* workspace given but smaller than one image's im2win rows */
+    IM2WIN_EWORKSPACE = -2, /* workspace too small for the mode (or a size with no buffer) */
     IM2WIN_ELAUNCH = -3     /* a kernel launch failed (message: im2win_last_error) */
 } im2win_status;
 
@@ -99,48 +102,26 @@ int im2win_pack_strided(const void *x, void *ws, int N, int Ci, int Hi, int Wi, 
                         int sh, int sw, size_t elem_bytes, void *stream);
 
 /*
- * Workspace of the two convolution entry points, in bytes.
- *
- * The workspace (optional) is one caller-owned device buffer, 16-byte
- * aligned, laid out as
- *     [ prepacked filter | im2win tensor of a chunk of images ]
- * The prepacked part is the filter re-laid out for the fp16 matrix-core
- * kernel the shape runs on (fp16 only; it is 0 bytes for fp32 and for fp16
- * shapes no such kernel takes); it is rounded up to a multiple of 256 bytes.
- *
- *  materialize == 0: bytes for the fused mode with a prepacked filter
- *                    (0 for fp32: the fused fp32 path needs no workspace).
- *  materialize != 0: bytes for the materialised mode over the whole batch:
- *                    the prepacked part + N * one image's im2win bytes.
- * Returns 0 for an invalid shape or elem_bytes not in {2, 4}. Host only.
- */
-size_t conv2d_im2win_workspace_bytes(int materialize, int N, int Ci, int Hi, int Wi, int Co,
-                                     int Hf, int Wf, int s, size_t elem_bytes);
-size_t conv2d_im2win_workspace_bytes_strided(int materialize, int N, int Ci, int Hi, int Wi,
-                                             int Co, int Hf, int Wf, int sh, int sw,
-                                             size_t elem_bytes);
-
-/*
  * fp32 convolution ("full precision" in the GPU page's Abstract): x, w fp32;
  * fp32 products and sums on the fp32 matrix instructions (the vector-ALU
- * kernel when the environment sets IM2WIN_F32_PATH=valu, and for shapes
- * outside the matrix kernel's envelope); y fp32 (written fully).
+ * kernel with knob "f32_valu" = 1, and for shapes outside the matrix
+ * kernel's envelope); y fp32 (written fully).
  *
- * The workspace selects how the im2win rows reach the dot products; with
- * F = the prepacked part (see conv2d_im2win_workspace_bytes, 0 for fp32)
- * and I = one image's im2win bytes (im2win_workspace_bytes with N = 1):
+ * The workspace selects how the im2win rows reach the dot products. With
+ * I = one image's im2win bytes (im2win_workspace_bytes with N = 1):
  *  - ws == NULL and ws_bytes == 0: fused. Each workgroup builds the im2win
  *    rows it needs in LDS straight from x; no HBM workspace.
- *  - F <= ws_bytes < F + I (fp16 only, F > 0): fused, the filter prepacked
- *    once per call into the workspace.
- *  - ws_bytes >= F + I: materialised. The im2win tensor of
- *    floor((ws_bytes - F) / I) images at a time (at most N) is packed into
- *    the workspace after F (im2win_pack layout) and convolved from there,
- *    chunk by chunk in stream order.
- *  - anything else (ws == NULL with ws_bytes != 0, or too small): returns
+ *  - ws_bytes >= I: materialised (the pages' own formulation). The im2win
+ *    tensor of floor(ws_bytes / I) images at a time (at most N; the whole
+ *    batch when ws_bytes >= im2win_workspace_bytes(N, ...)) is packed into
+ *    the start of the workspace (im2win_pack layout) and convolved from
+ *    there, chunk by chunk in stream order. The workspace never needs more
+ *    than N * Ci * Ho * Wi * Hf elements.
+ *  - anything else (ws == NULL with ws_bytes != 0, or 0 < ws_bytes < I):
  *    IM2WIN_EWORKSPACE; ws not 16-byte aligned: IM2WIN_EINVAL.
  * All modes compute the same windowed dot products; only their fp32
- * summation order may differ.
+ * summation order may differ. Results of one mode on one shape are the
+ * same bits on every call (no atomics, fixed summation order).
  */
 int conv2d_im2win_fp32(const float *x, const float *w, float *y, void *ws, size_t ws_bytes,
                        int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int s,
@@ -153,7 +134,7 @@ int conv2d_im2win_fp32_strided(const float *x, const float *w, float *y, void *w
  * fp16-input convolution on the matrix cores ("half precision on tensor
  * cores", same Abstract): x, w binary16; products exact, fp32 accumulation;
  * y fp32 (written fully). Workspace rules as for conv2d_im2win_fp32, with
- * elem_bytes = 2.
+ * elem_bytes = 2; in the fused mode the kernels gather the filter from w.
  */
 int conv2d_im2win_fp16(const uint16_t *x, const uint16_t *w, float *y, void *ws,
                        size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf,
@@ -161,6 +142,26 @@ int conv2d_im2win_fp16(const uint16_t *x, const uint16_t *w, float *y, void *ws,
 int conv2d_im2win_fp16_strided(const uint16_t *x, const uint16_t *w, float *y, void *ws,
                                size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf,
                                int Wf, int sh, int sw, void *stream);
+
+/*
+ * The fused fp16 convolution with its filter staging split out: the filter is
+ * first re-laid out ("prepacked") into fws in the order of the K slices of
+ * the matrix-core kernel the shape runs on, then that kernel copies its
+ * slices straight from fws instead of gathering them from w. Same results as
+ * conv2d_im2win_fp16 without a workspace (same kernel, same summation order).
+ * Strides per axis, as the *_strided calls.
+ *  - conv2d_im2win_fp16_fused_workspace_bytes: bytes fws needs for the shape
+ *    (a multiple of 256; depends on the shape only); 0 for an invalid shape.
+ *  - conv2d_im2win_fp16_fused: fws (16-byte aligned, caller-owned, at least
+ *    that many bytes, overwritten) holds the prepacked filter during the
+ *    call; fws == NULL with fws_bytes == 0 gathers the filter in the kernel.
+ *    A smaller fws, or a size without a buffer: IM2WIN_EWORKSPACE.
+ */
+size_t conv2d_im2win_fp16_fused_workspace_bytes(int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                                                int Wf, int sh, int sw);
+int conv2d_im2win_fp16_fused(const uint16_t *x, const uint16_t *w, float *y, void *fws,
+                             size_t fws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                             int Wf, int sh, int sw, void *stream);
 
 /*
  * Baselines the pages compare im2win against, built here on the same
@@ -232,6 +233,32 @@ int conv2d_im2win_nhwc_fp32(const float *x, const float *w, float *y, void *ws, 
 int conv2d_im2win_nhwc_fp16(const uint16_t *x, const uint16_t *w, float *y, void *ws,
                             size_t ws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf,
                             int sh, int sw, void *stream);
+
+/*
+ * Tuning knobs of the kernel planners, for tests and the ablation study
+ * (the pages' variant study, Table II and Fig. 4 of "Enabling
+ * Memory-efficient Im2win Convolution ..."). Knob k is named by
+ * im2win_knob_name(k) (NULL past the last one); every knob is 0 by default,
+ * meaning the planner's choice. A knob selects which kernel, tiling, tile
+ * order or staging runs; it never changes a workspace size or any result
+ * beyond the fp32 summation order. Process-wide; set them only while no call
+ * runs. im2win_set_knob returns IM2WIN_OK, or IM2WIN_EINVAL for an unknown
+ * knob; im2win_get_knob returns the value (0 for an unknown knob).
+ */
+int im2win_set_knob(int knob, int value);
+int im2win_get_knob(int knob);
+const char *im2win_knob_name(int knob);
+
+/*
+ * Name of the main kernel a convolution call with this shape runs under the
+ * current knobs (for profiles and reports), assuming x 16-byte aligned.
+ * elem_bytes 4 (conv2d_im2win_fp32) or 2 (the fp16 calls); mode 0: fused (no
+ * workspace), 1: conv2d_im2win_fp16_fused with a filter workspace, 2:
+ * materialised (the im2win_pack launches come first). Static string; NULL
+ * for an invalid shape or mode. Host only.
+ */
+const char *im2win_conv_kernel_name(int elem_bytes, int mode, int N, int Ci, int Hi, int Wi,
+                                   int Co, int Hf, int Wf, int sh, int sw);
 
 /* Static, human-readable text for a status code. */
 const char *im2win_status_string(int status);

@@ -7,7 +7,9 @@ in the library's HIP kernels.
 
     y = conv2d(x, w, stride)                 # fused: im2win rows built in LDS
     y = conv2d(x, w, stride, ws=workspace)   # materialised im2win tensor
+    y = conv2d_fused(x, w, stride, fws=f)    # fp16 fused, filter prepacked into f
     ws = pack(x, Hf, Wf, stride)             # the im2win transform itself
+    with knobs(f16_rows=-1): ...             # planner overrides (tests, ablation)
 
 A stride is one int (both axes) or a pair (sh, sw): row stride, then column
 stride. Equal strides go through the single-stride entry points of the C ABI,
@@ -20,7 +22,9 @@ import ctypes
 from . import _lib
 from ._lib import Im2winError, status_string  # noqa: F401
 
-__all__ = ["conv2d", "pack", "workspace_bytes", "conv_workspace_bytes", "output_dims", "strides",
+__all__ = ["conv2d", "conv2d_fused", "pack", "workspace_bytes", "fused_workspace_bytes",
+           "output_dims", "strides", "knob_names", "set_knob", "get_knob", "knobs",
+           "conv_kernel_name",
            "im2col", "im2col_workspace_bytes", "conv2d_im2col", "conv2d_direct",
            "pack_nhwc", "conv2d_nhwc", "nhwc_workspace_bytes",
            "Im2winError", "status_string", "load_library"]
@@ -62,12 +66,73 @@ def workspace_bytes(N, Ci, Hi, Wi, Hf, Wf, s, elem_bytes) -> int:
     return fn(N, Ci, Hi, Wi, Hf, Wf, *st, elem_bytes)
 
 
-def conv_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s, elem_bytes, materialize: bool) -> int:
-    """Workspace bytes of a convolution call: the fused mode with a prepacked
-    filter (materialize=False; 0 for fp32) or the materialised mode over the
-    whole batch (materialize=True). 0 for an invalid shape."""
-    fn, st = _entry("conv2d_im2win_workspace_bytes", s)
-    return fn(1 if materialize else 0, N, Ci, Hi, Wi, Co, Hf, Wf, *st, elem_bytes)
+def fused_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s) -> int:
+    """Bytes conv2d_fused needs for its prepacked fp16 filter (0 for an
+    invalid shape)."""
+    sh, sw = strides(s)
+    return _lib.load().conv2d_im2win_fp16_fused_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw)
+
+
+def conv_kernel_name(N, Ci, Hi, Wi, Co, Hf, Wf, s, elem_bytes, mode: str = "fused") -> str:
+    """Name of the main kernel a call runs (mode "fused", "prepacked" for
+    conv2d_fused with a filter workspace, or "materialized")."""
+    sh, sw = strides(s)
+    code = {"fused": 0, "prepacked": 1, "materialized": 2}[mode]
+    if code == 1 and elem_bytes == 4:
+        code = 0
+    r = _lib.load().im2win_conv_kernel_name(elem_bytes, code, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw)
+    if r is None:
+        raise ValueError("invalid shape or mode")
+    return r.decode()
+
+
+# ---- tuning knobs ------------------------------------------------------------
+def knob_names():
+    """Names of the library's tuning knobs, in the order of their ids."""
+    L = _lib.load()
+    out = []
+    while True:
+        n = L.im2win_knob_name(len(out))
+        if n is None:
+            return out
+        out.append(n.decode())
+
+
+def _knob_id(name: str) -> int:
+    names = knob_names()
+    if name not in names:
+        raise ValueError(f"unknown knob {name!r}; known: {names}")
+    return names.index(name)
+
+
+def set_knob(name: str, value: int) -> None:
+    """Sets a planner knob (0: the planner's choice). Process-wide; change
+    knobs only while no call is running."""
+    _lib.check(_lib.load().im2win_set_knob(_knob_id(name), int(value)), f"set_knob({name})")
+
+
+def get_knob(name: str) -> int:
+    return _lib.load().im2win_get_knob(_knob_id(name))
+
+
+class knobs:
+    """Context manager: ``with knobs(f16_rows=-1, tile_order=1): ...`` sets
+    the given knobs and restores their previous values on exit."""
+
+    def __init__(self, **values):
+        self.values = values
+        self.saved = {}
+
+    def __enter__(self):
+        for k, v in self.values.items():
+            self.saved[k] = get_knob(k)
+            set_knob(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            set_knob(k, v)
+        return False
 
 
 def _torch():
@@ -113,18 +178,35 @@ def pack(x, Hf: int, Wf: int, s, out=None):
     return out
 
 
+def _ws_arg(ws, ws_bytes, x, name):
+    """(pointer, byte count) of an optional workspace tensor on x's device;
+    ws_bytes may name a prefix of it, never more."""
+    if ws is None:
+        if ws_bytes:
+            raise ValueError(f"{name}_bytes given without {name}")
+        return None, 0
+    if not getattr(ws, "is_cuda", False) or not ws.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if ws.device != x.device:
+        raise ValueError(f"{name} must be on x's device")
+    size = ws.numel() * ws.element_size()
+    nbytes = size if ws_bytes is None else int(ws_bytes)
+    if nbytes < 0 or nbytes > size:
+        raise ValueError(f"{name}_bytes={nbytes} is outside the {size}-byte {name} tensor")
+    return ctypes.c_void_p(ws.data_ptr()), nbytes
+
+
 def conv2d(x, w, stride=1, ws=None, ws_bytes: int | None = None, out=None):
     """Forward convolution (cross-correlation, no padding) of x (N,Ci,Hi,Wi)
     with w (Co,Ci,Hf,Wf); fp32 output (N,Co,Ho,Wo).
 
     float32 inputs run on the fp32 matrix instructions (the vector-ALU kernel
-    with IM2WIN_F32_PATH=valu), float16 inputs on the fp16 matrix
-    instructions with fp32 accumulation. Without ``ws`` the im2win rows are
-    built in LDS
-    (fused). With ``ws`` (a device tensor; see conv_workspace_bytes) the
-    fp16 filter is prepacked into its head, and if the rest holds at least
-    one image's im2win tensor that tensor is materialised, in chunks of as
-    many images as fit.
+    with knob f32_valu=1), float16 inputs on the fp16 matrix instructions
+    with fp32 accumulation. Without ``ws`` the im2win rows are built in LDS
+    (fused). With ``ws`` (a device tensor of at least one image's im2win
+    bytes; ``workspace_bytes(N, ...)`` for the whole batch) the im2win tensor
+    is materialised in it, in chunks of as many images as fit. ``ws_bytes``
+    may restrict the call to a prefix of ``ws``.
     """
     torch = _torch()
     _check_tensor(x, "x", (torch.float32, torch.float16), 4)
@@ -141,18 +223,29 @@ def conv2d(x, w, stride=1, ws=None, ws_bytes: int | None = None, out=None):
     elif (tuple(out.shape) != (N, Co, Ho, Wo) or out.dtype != torch.float32
           or not out.is_contiguous() or out.device != x.device):
         raise ValueError("out has the wrong shape, dtype, device or layout")
-    if ws is None:
-        ws_ptr, nbytes = None, 0
-    else:
-        if not ws.is_cuda or not ws.is_contiguous():
-            raise ValueError("ws must be a contiguous GPU tensor")
-        ws_ptr = ctypes.c_void_p(ws.data_ptr())
-        nbytes = ws.numel() * ws.element_size() if ws_bytes is None else int(ws_bytes)
+    ws_ptr, nbytes = _ws_arg(ws, ws_bytes, x, "ws")
     fn, st = _entry("conv2d_im2win_fp32" if x.dtype == torch.float32 else "conv2d_im2win_fp16",
                     stride)
     _lib.check(fn(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
                   ctypes.c_void_p(out.data_ptr()), ws_ptr, nbytes,
                   N, Ci, Hi, Wi, Co, Hf, Wf, *st, _stream_handle(x)), fn.__name__)
+    return out
+
+
+def conv2d_fused(x, w, stride=1, fws=None, fws_bytes: int | None = None, out=None):
+    """fp16 fused convolution with the filter prepacked per call into ``fws``
+    (a device tensor of at least fused_workspace_bytes(...) bytes), then
+    copied from there by the matrix-core kernel. Without ``fws`` the kernel
+    gathers the filter from w, as conv2d does without a workspace."""
+    torch = _torch()
+    dims, out = _conv_args(x, w, stride, out)
+    if x.dtype != torch.float16:
+        raise TypeError("conv2d_fused takes float16 inputs")
+    ptr, nbytes = _ws_arg(fws, fws_bytes, x, "fws")
+    L = _lib.load()
+    _lib.check(L.conv2d_im2win_fp16_fused(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                                          ctypes.c_void_p(out.data_ptr()), ptr, nbytes, *dims,
+                                          _stream_handle(x)), "conv2d_im2win_fp16_fused")
     return out
 
 

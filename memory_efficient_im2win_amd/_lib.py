@@ -26,13 +26,17 @@ EXPORTS = {
     "im2win_pack": ([_p, _p] + [_i] * 7 + [_sz, _p], _i),
     "conv2d_im2win_fp32": ([_p, _p, _p, _p, _sz] + [_i] * 8 + [_p], _i),
     "conv2d_im2win_fp16": ([_p, _p, _p, _p, _sz] + [_i] * 8 + [_p], _i),
-    "conv2d_im2win_workspace_bytes": ([_i] * 9 + [_sz], _sz),
     "im2win_workspace_bytes_strided": ([_i] * 8 + [_sz], _sz),
     "im2win_output_dims_strided": ([_i] * 6 + [ctypes.POINTER(_i), ctypes.POINTER(_i)], _i),
     "im2win_pack_strided": ([_p, _p] + [_i] * 8 + [_sz, _p], _i),
     "conv2d_im2win_fp32_strided": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
     "conv2d_im2win_fp16_strided": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
-    "conv2d_im2win_workspace_bytes_strided": ([_i] * 10 + [_sz], _sz),
+    "conv2d_im2win_fp16_fused_workspace_bytes": ([_i] * 9, _sz),
+    "conv2d_im2win_fp16_fused": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
+    "im2win_set_knob": ([_i, _i], _i),
+    "im2win_get_knob": ([_i], _i),
+    "im2win_knob_name": ([_i], ctypes.c_char_p),
+    "im2win_conv_kernel_name": ([_i] * 11, ctypes.c_char_p),
     "im2win_status_string": ([_i], ctypes.c_char_p),
     "im2win_last_error": ([], ctypes.c_char_p),
     "conv2d_im2col_workspace_bytes": ([_i] * 9 + [_sz], _sz),

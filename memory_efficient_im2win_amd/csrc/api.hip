@@ -1,12 +1,14 @@
 // C ABI of the im2win library: argument checks, workspace/mode selection and
 // kernel dispatch. Declarations and the contract are in include/im2win.h.
 #include <algorithm>
-#include <cstdlib>
-#include <cstring>
+#include <map>
+#include <mutex>
 #include <stdint.h>
+#include <utility>
 
 #include "im2win.h"
 #include "kernels.hpp"
+#include "knobs.hpp"
 
 namespace {
 
@@ -46,38 +48,27 @@ thread_local hipError_t g_last_error = hipSuccess;
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace layout: [prepacked filter, rounded up to 256 bytes | im2win chunk].
-// The prepacked part is empty where the fused kernel does not use one (fp32,
-// or shapes outside its envelope).
-struct WsPlan {
-    size_t fbytes;     // prepacked filter bytes (aligned), 0 if none
-    size_t per_image;  // im2win bytes of one image
-};
-
-WsPlan ws_plan(const ConvShape& c, size_t elem)
+// Bytes of one image's im2win rows (the unit of the materialised mode).
+size_t im2win_image_bytes(const ConvShape& c, size_t elem)
 {
-    WsPlan p;
-    p.fbytes = elem == 2 ? align_up(im2win::f16_filter_pack_bytes(c)) : 0;
-    p.per_image = (size_t)c.Ci * c.Ho * c.Wi * c.Hf * elem;
-    return p;
+    return (size_t)c.Ci * c.Ho * c.Wi * c.Hf * elem;
 }
 
-// Shared driver of both precisions. T is the element type of x, w and ws.
+// Shared driver of both precisions (the workspace contract of
+// conv2d_im2win_fp32 / _fp16). T is the element type of x, w and ws.
 template <typename T>
 int conv_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int N, int Ci, int Hi,
                 int Wi, int Co, int Hf, int Wf, int sh, int sw, hipStream_t stream,
                 int (*fused)(const T*, const T*, const void*, float*, const ConvShape&, hipStream_t),
                 int (*from_ws)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t),
-                int (*generic)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t),
-                int (*filter_pack)(const T*, void*, const ConvShape&, hipStream_t))
+                int (*generic)(const T*, const T*, const T*, float*, const ConvShape&, hipStream_t))
 {
     int Ho, Wo;
     if (!x || !w || !y) return IM2WIN_EINVAL;
     if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return IM2WIN_EINVAL;
     if (!aligned(x, sizeof(T)) || !aligned(w, sizeof(T)) || !aligned(y, sizeof(float)))
         return IM2WIN_EINVAL;
-    ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo};
-    const WsPlan p = ws_plan(c, sizeof(T));
+    const ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo};
     if (ws == nullptr) {
         if (ws_bytes != 0) return IM2WIN_EWORKSPACE;
         int rc = fused(x, w, nullptr, y, c, stream);
@@ -85,24 +76,16 @@ int conv_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int
         return status_of(rc);
     }
     if (!aligned(ws, 16)) return IM2WIN_EINVAL;
-    if (ws_bytes < p.fbytes + (p.fbytes ? 0 : p.per_image)) return IM2WIN_EWORKSPACE;
-    unsigned char* wsb = static_cast<unsigned char*>(ws);
-    const size_t rest = ws_bytes - p.fbytes;
-    if (rest < p.per_image) {
-        // Fused, with the filter prepacked once into the workspace.
-        int rc = filter_pack(w, wsb, c, stream);
-        if (rc != 0) return status_of(rc);
-        rc = fused(x, w, wsb, y, c, stream);
-        if (rc == -1) rc = generic(x, nullptr, w, y, c, stream);
-        return status_of(rc);
-    }
-    // Materialised: the im2win tensor of as many images as fit, chunk by chunk.
-    const T* ims = reinterpret_cast<const T*>(wsb + p.fbytes);
-    const int chunk = (int)std::min<size_t>((size_t)N, rest / p.per_image);
+    // Materialised: the im2win tensor of as many images as fit, chunk by
+    // chunk, at the start of the workspace.
+    const size_t per_image = im2win_image_bytes(c, sizeof(T));
+    if (ws_bytes < per_image) return IM2WIN_EWORKSPACE;
+    const T* ims = static_cast<const T*>(ws);
+    const int chunk = (int)std::min<size_t>((size_t)N, ws_bytes / per_image);
     const int64_t x_img = (int64_t)Ci * Hi * Wi, y_img = (int64_t)Co * Ho * Wo;
     for (int n0 = 0; n0 < N; n0 += chunk) {
         const int nc = std::min(chunk, N - n0);
-        int rc = im2win::launch_pack(x + n0 * x_img, wsb + p.fbytes, nc, Ci, Hi, Wi, Hf, sh, Ho,
+        int rc = im2win::launch_pack(x + n0 * x_img, ws, nc, Ci, Hi, Wi, Hf, sh, Ho,
                                      (int)sizeof(T), stream);
         if (rc != 0) return status_of(rc);
         ConvShape cc = c;
@@ -116,16 +99,11 @@ int conv_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int
 
 // Adapters to the driver's signatures.
 // fp32 fused: the matrix-core kernel where the shape fits its envelope,
-// else the vector-ALU kernel. IM2WIN_F32_PATH=valu selects the latter always.
-bool f32_valu_only()
-{
-    const char* v = std::getenv("IM2WIN_F32_PATH");
-    return v && std::strcmp(v, "valu") == 0;
-}
+// else the vector-ALU kernel. KNOB_F32_VALU = 1 selects the latter always.
 int f32_fused(const float* x, const float* w, const void*, float* y, const ConvShape& c,
               hipStream_t st)
 {
-    if (!f32_valu_only()) {
+    if (im2win::knob(im2win::KNOB_F32_VALU) != 1) {
         const int rc = im2win::launch_conv_f32_mfma(x, w, y, c, st);
         if (rc != -1) return rc;
     }
@@ -141,7 +119,6 @@ int f32_generic(const float* x, const float* ws, const float* w, float* y, const
 {
     return im2win::launch_conv_generic_f32(x, ws, w, y, c, st);
 }
-int f32_no_pack(const float*, void*, const ConvShape&, hipStream_t) { return -1; }
 int f16_from_ws(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float* y,
                 const ConvShape& c, hipStream_t st)
 {
@@ -151,6 +128,33 @@ int f16_generic(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float*
                 const ConvShape& c, hipStream_t st)
 {
     return im2win::launch_conv_generic_f16(x, ws, w, y, c, st);
+}
+
+// fp16 fused with the filter prepacked per call into fws (fws_bytes >=
+// im2win::f16_filter_pack_bytes), or gathered in the kernel (fws NULL).
+int f16_fused_driver(const uint16_t* x, const uint16_t* w, float* y, void* fws, size_t fws_bytes,
+                     int N, int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw,
+                     hipStream_t stream)
+{
+    int Ho, Wo;
+    if (!x || !w || !y) return IM2WIN_EINVAL;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return IM2WIN_EINVAL;
+    if (!aligned(x, 2) || !aligned(w, 2) || !aligned(y, 4)) return IM2WIN_EINVAL;
+    const ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo};
+    if (fws == nullptr) {
+        if (fws_bytes != 0) return IM2WIN_EWORKSPACE;
+        int rc = im2win::launch_conv_f16_fused(x, w, nullptr, y, c, stream);
+        if (rc == -1) rc = f16_generic(x, nullptr, w, y, c, stream);
+        return status_of(rc);
+    }
+    if (!aligned(fws, 16)) return IM2WIN_EINVAL;
+    if (fws_bytes < im2win::f16_filter_pack_bytes(c)) return IM2WIN_EWORKSPACE;
+    int rc = im2win::launch_f16_filter_pack(w, fws, c, x, stream);
+    if (rc == -1) return status_of(f16_generic(x, nullptr, w, y, c, stream));
+    if (rc != 0) return status_of(rc);
+    rc = im2win::launch_conv_f16_fused(x, w, fws, y, c, stream);
+    if (rc == -1) rc = f16_generic(x, nullptr, w, y, c, stream);
+    return status_of(rc);
 }
 
 // im2col baseline workspace: [padded filter, rounded up to 256 bytes | im2col
@@ -274,6 +278,31 @@ int launch_status(hipError_t e)
     g_last_error = e;
     return -3;
 }
+
+void ensure_lds_limit(const void* f, int bytes)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();   // left for the launch to report
+        return;
+    }
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, int> done;
+    std::lock_guard<std::mutex> lk(mu);
+    int& have = done[std::make_pair(f, dev)];
+    if (have >= bytes) return;
+    if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+        (void)hipGetLastError();   // the launch reports any limit it exceeds
+    else
+        have = bytes;
+}
+
+const char* const kKnobNames[KNOB_COUNT] = {
+    "f32_valu", "f32_nw", "f32_wco", "f32_cb", "f32_ksplit", "f32_occ",
+    "f16_rows", "f16_rows_nwv", "f16_rows_bufs", "f16_thin", "f16_thin_nb", "f16_wide",
+    "f16_wide_nw", "f16_wpx", "f16_nwh", "tile_order"};
+
+std::atomic<int> g_knobs[KNOB_COUNT];
 }  // namespace im2win
 
 extern "C" {
@@ -321,22 +350,20 @@ int im2win_pack(const void* x, void* ws, int N, int Ci, int Hi, int Wi, int Hf, 
     return im2win_pack_strided(x, ws, N, Ci, Hi, Wi, Hf, Wf, s, s, elem_bytes, stream);
 }
 
-size_t conv2d_im2win_workspace_bytes_strided(int materialize, int N, int Ci, int Hi, int Wi,
-                                             int Co, int Hf, int Wf, int sh, int sw,
-                                             size_t elem_bytes)
+size_t conv2d_im2win_fp16_fused_workspace_bytes(int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                                                int Wf, int sh, int sw)
 {
     int Ho, Wo;
-    if (elem_bytes != 2 && elem_bytes != 4) return 0;
     if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return 0;
-    const WsPlan p = ws_plan(ConvShape{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo}, elem_bytes);
-    return p.fbytes + (materialize ? (size_t)N * p.per_image : 0);
+    return align_up(im2win::f16_filter_pack_bytes(ConvShape{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo}));
 }
 
-size_t conv2d_im2win_workspace_bytes(int materialize, int N, int Ci, int Hi, int Wi, int Co,
-                                     int Hf, int Wf, int s, size_t elem_bytes)
+int conv2d_im2win_fp16_fused(const uint16_t* x, const uint16_t* w, float* y, void* fws,
+                             size_t fws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                             int Wf, int sh, int sw, void* stream)
 {
-    return conv2d_im2win_workspace_bytes_strided(materialize, N, Ci, Hi, Wi, Co, Hf, Wf, s, s,
-                                                 elem_bytes);
+    return f16_fused_driver(x, w, y, fws, fws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
+                            static_cast<hipStream_t>(stream));
 }
 
 int conv2d_im2win_fp32_strided(const float* x, const float* w, float* y, void* ws,
@@ -345,7 +372,7 @@ int conv2d_im2win_fp32_strided(const float* x, const float* w, float* y, void* w
 {
     return conv_driver<float>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
                               static_cast<hipStream_t>(stream), f32_fused, f32_from_ws,
-                              f32_generic, f32_no_pack);
+                              f32_generic);
 }
 
 int conv2d_im2win_fp32(const float* x, const float* w, float* y, void* ws, size_t ws_bytes, int N,
@@ -361,7 +388,7 @@ int conv2d_im2win_fp16_strided(const uint16_t* x, const uint16_t* w, float* y, v
 {
     return conv_driver<uint16_t>(x, w, y, ws, ws_bytes, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw,
                                  static_cast<hipStream_t>(stream), im2win::launch_conv_f16_fused,
-                                 f16_from_ws, f16_generic, im2win::launch_f16_filter_pack);
+                                 f16_from_ws, f16_generic);
 }
 
 int conv2d_im2win_fp16(const uint16_t* x, const uint16_t* w, float* y, void* ws, size_t ws_bytes,
@@ -462,6 +489,42 @@ int conv2d_im2win_nhwc_fp16(const uint16_t* x, const uint16_t* w, float* y, void
                                  static_cast<hipStream_t>(stream));
 }
 
+const char* im2win_conv_kernel_name(int elem_bytes, int mode, int N, int Ci, int Hi, int Wi,
+                                   int Co, int Hf, int Wf, int sh, int sw)
+{
+    int Ho, Wo;
+    if (elem_bytes != 2 && elem_bytes != 4) return nullptr;
+    if (mode < 0 || mode > 2 || (mode == 1 && elem_bytes != 2)) return nullptr;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return nullptr;
+    const ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo};
+    if (elem_bytes == 4) {
+        if (mode == 2) return "conv_f32_kernel";
+        const bool mfma = im2win::knob(im2win::KNOB_F32_VALU) != 1 && im2win::f32_mfma_applies(c);
+        return mfma ? "conv_f32_mfma_kernel" : "conv_f32_kernel";
+    }
+    if (mode == 2) return "conv_f16_kernel";
+    return im2win::f16_fused_kernel_name(c, reinterpret_cast<const void*>(uintptr_t(256)));
+}
+
+int im2win_set_knob(int knob, int value)
+{
+    if (knob < 0 || knob >= im2win::KNOB_COUNT) return IM2WIN_EINVAL;
+    im2win::g_knobs[knob].store(value, std::memory_order_relaxed);
+    return IM2WIN_OK;
+}
+
+int im2win_get_knob(int knob)
+{
+    if (knob < 0 || knob >= im2win::KNOB_COUNT) return 0;
+    return im2win::g_knobs[knob].load(std::memory_order_relaxed);
+}
+
+const char* im2win_knob_name(int knob)
+{
+    if (knob < 0 || knob >= im2win::KNOB_COUNT) return nullptr;
+    return im2win::kKnobNames[knob];
+}
+
 const char* im2win_last_error(void)
 {
     return g_last_error == hipSuccess ? "no error" : hipGetErrorString(g_last_error);
@@ -472,7 +535,7 @@ const char* im2win_status_string(int status)
     switch (status) {
     case IM2WIN_OK: return "ok";
     case IM2WIN_EINVAL: return "invalid argument (shape, stride, element size, alignment or NULL pointer)";
-    case IM2WIN_EWORKSPACE: return "workspace smaller than one image's im2win rows";
+    case IM2WIN_EWORKSPACE: return "workspace too small for the requested mode (or size without a buffer)";
     case IM2WIN_ELAUNCH: return "kernel launch failed";
     default: return "unknown status";
     }

@@ -243,16 +243,9 @@ int launch_conv_f16(const uint16_t* x, const uint16_t* ws, const uint16_t* w, fl
     a.tpr_shift = log2_ceil_pow2(ws ? a.LW * c.Hf : a.LW, kThreads);
     const int64_t blocks = (int64_t)c.N * a.tiles_h * a.tiles_w * a.co_tiles;
     if (blocks <= 0 || blocks > 0x7fffffff) return -1;
-    // Allow the full 160 KiB of gfx950 LDS (set once per kernel).
-    static bool lds_attr_set[2] = {false, false};
-    if (!lds_attr_set[ws != nullptr]) {
-        // On failure the launch below reports any limit it exceeds.
-        const void* f = ws ? (const void*)conv_f16_kernel<true> : (const void*)conv_f16_kernel<false>;
-        if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds) !=
-            hipSuccess)
-            (void)hipGetLastError();
-        lds_attr_set[ws != nullptr] = true;
-    }
+    // Allow the full 160 KiB of gfx950 LDS.
+    ensure_lds_limit(ws ? (const void*)conv_f16_kernel<true> : (const void*)conv_f16_kernel<false>,
+                     kMaxLds);
     if (ws)
         hipLaunchKernelGGL(conv_f16_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), lds,
                            stream, x, ws, w, y, a);

@@ -30,10 +30,10 @@
 //    odd tap count gets a zero filter entry and a zeroed B slice, so an
 //    infinity next to a window never turns into NaN.
 #include <algorithm>
-#include <cstdlib>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "knobs.hpp"
 
 namespace im2win {
 
@@ -540,15 +540,10 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     }
 }
 
-int env_int(const char* name, int dflt)
-{
-    const char* v = std::getenv(name);
-    return v && *v ? std::atoi(v) : dflt;
-}
-
 // Plans the fused launch; returns false if the shape is outside its envelope.
-// IM2WIN_F16_WPX / IM2WIN_F16_NWH override the waves along pixels and the
-// filter stages per channel group (tuning and tests only).
+// KNOB_F16_WPX / KNOB_F16_NWH override the waves along pixels and the filter
+// stages per channel group (tuning and tests only). One 64-channel column of
+// waves (WCO = 1).
 bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
 {
     a.c = c;
@@ -561,7 +556,7 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
     a.dup = std::max(0, c.Hf - c.sh);
     if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
     nb = 2;
-    wco = std::max(1, std::min(2, env_int("IM2WIN_F16_WCO", 1)));
+    wco = 1;
     a.xpair = c.Wi % 2 == 0;
     a.NU = ceil_div(c.Wi, c.sw);
     a.RS = c.sw * a.NU;
@@ -570,7 +565,7 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
     // Smallest workgroup LDS first: two workgroups of four waves per CU let one
     // stage its next channel group while the other runs MFMAs.
     bool found = false;
-    const int env_wpx = env_int("IM2WIN_F16_WPX", 0), env_nwh = env_int("IM2WIN_F16_NWH", 0);
+    const int env_wpx = knob(KNOB_F16_WPX), env_nwh = knob(KNOB_F16_NWH);
     for (int budget : {80 * 1024, kMaxLds}) {
         for (wpx = 8; wpx >= 1; wpx /= 2) {
             if (env_wpx ? wpx != env_wpx : wpx == 8) continue;
@@ -624,14 +619,7 @@ template <int WCO, int WPX, int NB, bool XVEC, bool WPK>
 int launch_t(const uint16_t* x, const uint16_t* w, const uint4* wpk, float* y,
              const FusedArgs& a, hipStream_t stream)
 {
-    static bool attr = false;
-    if (!attr) {
-        // On failure the launch below reports any limit it exceeds.
-        if (hipFuncSetAttribute((const void*)conv_f16_fused_kernel<WCO, WPX, NB, XVEC, WPK>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds) != hipSuccess)
-            (void)hipGetLastError();
-        attr = true;
-    }
+    ensure_lds_limit((const void*)conv_f16_fused_kernel<WCO, WPX, NB, XVEC, WPK>, kMaxLds);
     const size_t lds = fused_lds_bytes(a.xentries, a.HPH, a.co_tile, a.KT);
     hipLaunchKernelGGL((conv_f16_fused_kernel<WCO, WPX, NB, XVEC, WPK>),
                        dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(64 * WCO * WPX), lds,
@@ -652,26 +640,52 @@ int launch_w(const uint16_t* x, const uint16_t* w, const uint4* wpk, float* y,
 
 }  // namespace
 
-// With a prepacked filter, shapes the row-staged kernel takes run there
-// (its own filter layout), then shapes the thin-layer kernel takes (the same
-// slice layout), then shapes the wide-tile kernel takes (this layout); the
-// rest run the kernel above. Without one, the same kernels take the same
-// shapes, each gathering its filter from w, and the rest run the kernel
-// above.
-size_t f16_filter_pack_bytes(const ConvShape& c)
+// Which kernel a fused fp16 call runs on: the row-staged kernel for the
+// shapes it takes (x 16-byte aligned), then the thin-layer kernel, then the
+// wide-tile kernel, then the channel-interleaved kernel above; 0 if none
+// takes the shape. The filter, prepacked or gathered, follows the kernel's
+// layout.
+enum F16Route { kRouteNone = 0, kRouteRows, kRouteThin, kRouteWide, kRouteFused };
+
+F16Route f16_route(const ConvShape& c, const void* x)
 {
-    if (f16_rows_applies(c)) return f16_rows_filter_bytes(c);
-    if (f16_thin_applies(c)) return f16_slices_filter_bytes(c);
+    if (f16_rows_applies(c) && (uintptr_t)x % 16 == 0) return kRouteRows;
+    if (f16_thin_applies(c)) return kRouteThin;
+    if (f16_wide_applies(c, kCoPad)) return kRouteWide;
     FusedArgs a;
     int wco, wpx, nb;
-    if (!plan(c, a, wco, wpx, nb)) return 0;
-    return (size_t)a.CG * a.HWp * a.Copad * 16;
+    return plan(c, a, wco, wpx, nb) ? kRouteFused : kRouteNone;
 }
 
-int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, hipStream_t stream)
+size_t f16_filter_pack_bytes(const ConvShape& c)
 {
-    if (f16_rows_applies(c)) return launch_f16_rows_filter_pack(w, wpk, c, stream);
-    if (f16_thin_applies(c)) return launch_f16_slices_filter_pack(w, wpk, c, stream);
+    // Enough for whichever layout the planners pick, whatever the knobs: the
+    // channel-interleaved entries of this kernel and the wide-tile one, or
+    // the (channel, filter row) slices of the row-staged and thin-layer ones.
+    size_t b = (size_t)ceil_div(c.Ci, 8) * (size_t)((c.Hf * c.Wf + 1) & ~1) *
+               (size_t)(ceil_div(c.Co, kCoPad) * kCoPad) * 16;
+    if (c.Wf <= 8 && c.Hf * c.Wf <= 256) b = std::max(b, f16_slices_filter_bytes(c));
+    return b;
+}
+
+const char* f16_fused_kernel_name(const ConvShape& c, const void* x)
+{
+    switch (f16_route(c, x)) {
+    case kRouteRows: return "conv_f16_rows_kernel";
+    case kRouteThin: return "conv_f16_thin_kernel";
+    case kRouteWide: return "conv_f16_wide_kernel";
+    case kRouteFused: return "conv_f16_fused_kernel";
+    default: return "conv_generic_kernel";
+    }
+}
+
+int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, const void* x,
+                           hipStream_t stream)
+{
+    const F16Route r = f16_route(c, x);
+    if (r == kRouteNone) return -1;
+    if (r == kRouteRows) return launch_f16_rows_filter_pack(w, wpk, c, stream);
+    if (r == kRouteThin) return launch_f16_slices_filter_pack(w, wpk, c, stream);
     FusedArgs a;
     int wco, wpx, nb;
     if (!plan(c, a, wco, wpx, nb)) return -1;
@@ -694,14 +708,11 @@ int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, hip
 int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk, float* y,
                           const ConvShape& c, hipStream_t stream)
 {
-    if (f16_rows_applies(c)) {
-        // Without a workspace and with x off 16-byte alignment the next
-        // kernels take the call; a prepacked row-layout filter only this one.
-        const int rc = launch_conv_f16_rows(x, wpk, w, y, c, stream);
-        if (rc != -1 || wpk) return rc;
-    }
-    if (f16_thin_applies(c)) return launch_conv_f16_thin(x, wpk, w, y, c, stream);
-    if (f16_wide_applies(c, kCoPad)) return launch_conv_f16_wide(x, wpk, w, y, c, kCoPad, stream);
+    const F16Route r = f16_route(c, x);
+    if (r == kRouteNone) return -1;
+    if (r == kRouteRows) return launch_conv_f16_rows(x, wpk, w, y, c, stream);
+    if (r == kRouteThin) return launch_conv_f16_thin(x, wpk, w, y, c, stream);
+    if (r == kRouteWide) return launch_conv_f16_wide(x, wpk, w, y, c, kCoPad, stream);
     FusedArgs a;
     int wco, wpx, nb;
     if (!plan(c, a, wco, wpx, nb)) return -1;
@@ -710,9 +721,6 @@ int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk,
     if (wco == 1 && wpx == 4) return launch_w<1, 4>(x, w, wp, y, a, stream);
     if (wco == 1 && wpx == 2) return launch_w<1, 2>(x, w, wp, y, a, stream);
     if (wco == 1 && wpx == 1) return launch_w<1, 1>(x, w, wp, y, a, stream);
-    if (wco == 2 && wpx == 4) return launch_w<2, 4>(x, w, wp, y, a, stream);
-    if (wco == 2 && wpx == 2) return launch_w<2, 2>(x, w, wp, y, a, stream);
-    if (wco == 2 && wpx == 1) return launch_w<2, 1>(x, w, wp, y, a, stream);
     return -1;
 }
 

@@ -36,10 +36,10 @@
 //    would otherwise wait for every outstanding LDS load before each LDS
 //    read, leaves the pipelining to the explicit waits here.
 #include <algorithm>
-#include <cstdlib>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "knobs.hpp"
 
 namespace im2win {
 
@@ -529,12 +529,6 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_rows_kernel(const uint16_t*
     }
 }
 
-int env_int(const char* name, int dflt)
-{
-    const char* v = std::getenv(name);
-    return v && *v ? std::atoi(v) : dflt;
-}
-
 // Load instructions per wave and stage the kernel is built for.
 constexpr int kDmax[] = {4, 5, 6, 8, 12, 16};
 
@@ -542,14 +536,14 @@ constexpr int kDmax[] = {4, 5, 6, 8, 12, 16};
 // even column stride, Wf <= 8, Hf*Wf <= 256 (the filter pack's LDS), Wi a
 // multiple of 8 (16-byte row chunks),
 // Ci a multiple of the stage's channel count, tensors addressable with
-// 32-bit buffer offsets. IM2WIN_F16_ROWS=0 turns the kernel off,
-// IM2WIN_F16_ROWS_NWV picks the waves per workgroup and
-// IM2WIN_F16_ROWS_SWIZZLE=0 keeps tiles in launch order and
-// IM2WIN_F16_ROWS_BUFS=2 or 3 fixes the stage buffers (tuning and tests).
-// bufs: stage buffers to plan for (0: three, or IM2WIN_F16_ROWS_BUFS).
+// 32-bit buffer offsets. Knobs (tuning and tests): KNOB_F16_ROWS < 0 turns
+// the kernel off, KNOB_F16_ROWS_NWV picks the waves per workgroup,
+// KNOB_TILE_ORDER = 1 keeps tiles in launch order and KNOB_F16_ROWS_BUFS =
+// 2 or 3 fixes the stage buffers. bufs_want: stage buffers to plan for (0:
+// three, or the knob).
 bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax, int bufs_want = 0)
 {
-    if (env_int("IM2WIN_F16_ROWS", 1) == 0) return false;
+    if (knob(KNOB_F16_ROWS) < 0) return false;
     if (c.Wf > 8 || c.sw % 2 != 0 || c.Wi % 8 != 0 || c.Hf * c.Wf > 256) return false;
     a.c = c;
     a.total = (int64_t)c.N * c.Ho * c.Wo;
@@ -558,8 +552,8 @@ bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax, int bufs_want = 
     a.Copad = ceil_div(c.Co, kCoT) * kCoT;
     if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
     const int64_t plane = (int64_t)c.Ho * c.Wo;
-    const int env_nwv = env_int("IM2WIN_F16_ROWS_NWV", 0);
-    const int env_bufs = env_int("IM2WIN_F16_ROWS_BUFS", 0);
+    const int env_nwv = knob(KNOB_F16_ROWS_NWV);
+    const int env_bufs = knob(KNOB_F16_ROWS_BUFS);
     const int bufs = env_bufs == 2 || env_bufs == 3 ? env_bufs : bufs_want == 2 ? 2 : kBufsMax;
     bool found = false;
     for (int v : {8, 4}) {
@@ -627,7 +621,7 @@ bool plan(const ConvShape& c, RowsArgs& a, int& nwv, int& dmax, int bufs_want = 
     }
     a.divWo = FastDiv((uint32_t)c.Wo);
     a.divHo = FastDiv((uint32_t)c.Ho);
-    a.swz = env_int("IM2WIN_F16_ROWS_SWIZZLE", 1) != 0;
+    a.swz = knob(KNOB_TILE_ORDER) != 1;
     return true;
 }
 
@@ -635,14 +629,7 @@ template <int NWV, int DMAX, bool M3, bool WPK>
 int launch_t(const uint16_t* x, const uint4* wp, const uint16_t* w, float* y, const RowsArgs& a,
              hipStream_t stream)
 {
-    static bool attr = false;
-    if (!attr) {
-        // On failure the launch below reports any limit it exceeds.
-        if (hipFuncSetAttribute((const void*)conv_f16_rows_kernel<NWV, DMAX, M3, WPK>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kRowsLds) != hipSuccess)
-            (void)hipGetLastError();
-        attr = true;
-    }
+    ensure_lds_limit((const void*)conv_f16_rows_kernel<NWV, DMAX, M3, WPK>, kRowsLds);
     hipLaunchKernelGGL((conv_f16_rows_kernel<NWV, DMAX, M3, WPK>),
                        dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(64 * NWV), a.lds_bytes,
                        stream, x, wp, w, y, a);

@@ -32,10 +32,10 @@
 //    are zero in the filter and masked in B, so an infinity next to a window
 //    never turns into NaN.
 #include <algorithm>
-#include <cstdlib>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "knobs.hpp"
 
 namespace im2win {
 
@@ -421,20 +421,14 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
     }
 }
 
-int env_int(const char* name, int dflt)
-{
-    const char* v = std::getenv(name);
-    return v && *v ? std::atoi(v) : dflt;
-}
-
 // Plans a launch; false if the shape is outside the kernel's envelope:
 // fewer than 8 input channels, Ci*Hf <= 64 filter slices, Wf <= 8, an even
 // column stride, LDS for the tile, tensors addressable with 32-bit buffer
-// offsets. IM2WIN_F16_THIN=0 turns the kernel off and IM2WIN_F16_THIN_NB
-// picks 2 or 4 pixel blocks per wave (tuning and tests).
+// offsets. Knobs (tuning and tests): KNOB_F16_THIN < 0 turns the kernel
+// off and KNOB_F16_THIN_NB picks 2 or 4 pixel blocks per wave.
 bool plan(const ConvShape& c, ThinArgs& a)
 {
-    if (env_int("IM2WIN_F16_THIN", 1) == 0) return false;
+    if (knob(KNOB_F16_THIN) < 0) return false;
     if (c.Ci >= 8 || c.Wf > 8 || c.sw % 2 != 0 || c.Hf * c.Wf > 256) return false;
     a.c = c;
     a.S = c.Ci * c.Hf;
@@ -444,7 +438,7 @@ bool plan(const ConvShape& c, ThinArgs& a)
     a.dup = std::max(0, c.Hf - c.sh);
     if ((int64_t)c.N * c.Ho > 0x7fffffff) return false;
     const int64_t plane = (int64_t)c.Ho * c.Wo;
-    const int kP = a.P = 32 * kNW * (env_int("IM2WIN_F16_THIN_NB", 2) == 4 ? 4 : 2);
+    const int kP = a.P = 32 * kNW * (knob(KNOB_F16_THIN_NB) == 4 ? 4 : 2);
     a.rows_max = (int)std::min<int64_t>((kP - 1) / c.Wo + 2, (int64_t)c.N * c.Ho);
     a.tiles_per_image = (plane + kP - 1) / kP;
     a.aligned = (double)(a.tiles_per_image * kP) <= 1.05 * (double)plane;
@@ -493,14 +487,7 @@ template <int NB, bool XVEC, bool M3, bool WPK>
 int launch_t(const uint16_t* x, const uint4* wp, const uint16_t* w, float* y, const ThinArgs& a,
              hipStream_t stream)
 {
-    static bool attr = false;
-    if (!attr) {
-        // On failure the launch below reports any limit it exceeds.
-        if (hipFuncSetAttribute((const void*)conv_f16_thin_kernel<NB, XVEC, M3, WPK>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kThinLds) != hipSuccess)
-            (void)hipGetLastError();
-        attr = true;
-    }
+    ensure_lds_limit((const void*)conv_f16_thin_kernel<NB, XVEC, M3, WPK>, kThinLds);
     hipLaunchKernelGGL((conv_f16_thin_kernel<NB, XVEC, M3, WPK>),
                        dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(kNT), a.lds_bytes, stream, x,
                        wp, w, y, a);

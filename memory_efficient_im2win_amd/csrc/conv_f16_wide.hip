@@ -28,10 +28,10 @@
 //    g+1 are issued after the barrier that opens group g and land while its
 //    MFMAs run; one barrier per group.
 #include <algorithm>
-#include <cstdlib>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "knobs.hpp"
 
 namespace im2win {
 
@@ -445,22 +445,16 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
     }
 }
 
-int env_int(const char* name, int dflt)
-{
-    const char* v = std::getenv(name);
-    return v && *v ? std::atoi(v) : dflt;
-}
-
 // Plans a launch; false if the shape is outside the kernel's envelope:
 // Co >= 128 (a tile's 128 channels are mostly real), the stage fits LDS
 // twice over, the input rows fit the per-thread staging capacity, tensors
-// addressable with 32-bit buffer offsets. IM2WIN_F16_WIDE=0 turns the
-// kernel off and =2 lets it take Co < 128 too (tuning and tests).
+// addressable with 32-bit buffer offsets. Knobs (tuning and tests):
+// KNOB_F16_WIDE < 0 turns the kernel off, > 0 lets it take Co < 128 too.
 bool plan(const ConvShape& c, WideArgs& a, size_t copad_mult)
 {
-    const int sw_env = env_int("IM2WIN_F16_WIDE", 1);
-    if (sw_env == 0) return false;
-    if (c.Co < kCoW && sw_env != 2) return false;
+    const int sw_knob = knob(KNOB_F16_WIDE);
+    if (sw_knob < 0) return false;
+    if (c.Co < kCoW && sw_knob <= 0) return false;
     a.c = c;
     a.HW = c.Hf * c.Wf;
     a.HWp = (a.HW + 1) & ~1;
@@ -514,14 +508,7 @@ template <int NW, int NB, bool XPAIR, bool WPK>
 int launch_t(const uint16_t* x, const uint4* wpk, const uint16_t* w, float* y, const WideArgs& a,
              hipStream_t stream)
 {
-    static bool attr = false;
-    if (!attr) {
-        // On failure the launch below reports any limit it exceeds.
-        if (hipFuncSetAttribute((const void*)conv_f16_wide_kernel<NW, NB, XPAIR, WPK>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds) != hipSuccess)
-            (void)hipGetLastError();
-        attr = true;
-    }
+    ensure_lds_limit((const void*)conv_f16_wide_kernel<NW, NB, XPAIR, WPK>, kWideLds);
     hipLaunchKernelGGL((conv_f16_wide_kernel<NW, NB, XPAIR, WPK>),
                        dim3((unsigned)(a.px_tiles * a.co_tiles)), dim3(64 * NW), a.lds_bytes,
                        stream, x, wpk, w, y, a);
@@ -552,8 +539,8 @@ int launch_conv_f16_wide(const uint16_t* x, const void* wpk, const uint16_t* w, 
     if (!plan(c, a, copad_mult)) return -1;
     if ((uintptr_t)wpk % 16 != 0) return -1;
     const uint4* w4 = static_cast<const uint4*>(wpk);
-    // IM2WIN_F16_WIDE_NW: 4 waves of 4 x 4 blocks or 8 waves of 4 x 2.
-    const bool nw4 = env_int("IM2WIN_F16_WIDE_NW", 8) == 4;
+    // KNOB_F16_WIDE_NW: 4 waves of 4 x 4 blocks, or (default) 8 waves of 4 x 2.
+    const bool nw4 = knob(KNOB_F16_WIDE_NW) == 4;
     if (w4) return nw4 ? launch_x<4, 4, true>(x, w4, w, y, a, stream)
                        : launch_x<8, 2, true>(x, w4, w, y, a, stream);
     return nw4 ? launch_x<4, 4, false>(x, w4, w, y, a, stream)

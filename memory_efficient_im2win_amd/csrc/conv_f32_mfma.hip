@@ -1,17 +1,19 @@
 // fp32 im2win convolution on the CDNA4 matrix cores (v_mfma_f32_32x32x2_f32).
 //
 // The single-precision path of "Enabling Memory-efficient Im2win Convolution
-// with Multi-precision Support on GPU CUDA and Tensor Cores" (Section III:
-// the convolution as dot products of filter rows with im2win windows) for
-// one MI355X. fp32 products and fp32 accumulation, as on the vector ALUs, but
-// at the matrix-core rate (twice the unpacked vector FMA rate):
+// with Multi-precision Support on GPU CUDA and Tensor Cores" (Abstract: full
+// precision; Fig. 1: the convolution as dot products of filters with im2win
+// windows) for one MI355X. fp32 products and fp32 accumulation, as on the
+// vector ALUs, but at the matrix-core rate (twice the unpacked vector FMA
+// rate):
 //
 //  * GEMM view: rows = output channels (A = filters), columns = output
 //    pixels (B = windows), K = (input channel, kh, kw) in the filter's own
 //    memory order. Pixels are numbered over the whole batch,
-//    q = (n*Ho + ho)*Wo + wo. A workgroup of four waves owns 32*WCO channels
-//    and 128 consecutive pixels; wave v owns pixels 32v..32v+31 of the tile
-//    and all 32*WCO channels (WCO MFMA tiles, AGPR accumulators).
+//    q = (n*Ho + ho)*Wo + wo. A workgroup of NW waves owns 32*WCO channels
+//    and 32*NW/KSW consecutive pixels; wave v owns the 32-pixel block
+//    v % (NW/KSW) of the tile and all 32*WCO channels (WCO MFMA tiles,
+//    AGPR accumulators).
 //  * A stage is CB input channels. Per stage the workgroup stages in LDS the
 //    input rows its pixels' windows cover (one fp32 per entry, columns
 //    stride-phase major so the 32 pixels of a block read 32 consecutive
@@ -24,17 +26,19 @@
 //    into NaN.
 //  * The next stage's global loads are issued into registers before the
 //    MFMAs of the current stage and written to LDS after them.
-//  * Small problems split K over workgroups and add their partial sums into
-//    the zero-filled output with hardware float atomics.
+//  * Small problems (too few tiles to fill the chip) split K inside the
+//    workgroup: KSW waves share each pixel block, each taking a contiguous
+//    range of every stage's K pairs, and their partial sums are added
+//    through LDS in a fixed order (wave share 0 + 1 + ... + KSW-1) before
+//    the store, so results do not depend on timing.
 #include <algorithm>
-#include <cstdlib>
 #include <map>
 #include <mutex>
-#include <set>
 #include <utility>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "knobs.hpp"
 
 namespace im2win {
 
@@ -47,7 +51,7 @@ constexpr uint32_t kMaxBuf = 0xFFFFFFF0u;   // buffer ranges are 32-bit
 
 struct MArgs {
     ConvShape c;
-    int co_tiles, ksplit, spk;        // channel tiles; K splits; stages per split
+    int co_tiles;                     // channel tiles
     int64_t px_tiles, total, tiles_per_image;
     bool aligned;                     // tiles never cross images
     int rows_max, kmax, dup, RIN;     // output rows per tile, image breaks, sh<Hf overlap, LDS rows
@@ -68,12 +72,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void* base, uint32_t
                                              0x00020000);
 }
 
-template <int NW, int WCO, int XCH, int WCH>
+template <int NW, int KSW, int WCO, int XCH, int WCH>
 __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
     const float* __restrict__ x, const float* __restrict__ w, float* __restrict__ y, MArgs a)
 {
     constexpr int NT = 64 * NW;
-    constexpr int P = 32 * NW;                    // pixels per tile
+    constexpr int NPB = NW / KSW;                 // 32-pixel blocks per tile
+    constexpr int P = 32 * NPB;                   // pixels per tile
     constexpr int COT = 32 * WCO;
     constexpr int RPW = rows_per_wave(NW);        // input rows per wave and stage
     constexpr int WRW = (COT + NW - 1) / NW;      // filter rows per wave and stage
@@ -94,25 +99,24 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
     const int lane = tid & 63;
     const int hl = lane >> 5, l32 = lane & 31;
     const int wave = uniform(tid >> 6);
+    const int pbk = wave % NPB;    // this wave's pixel block
+    const int kgr = wave / NPB;    // this wave's share of each stage's K pairs
 
-    // Work items (channel tile, K split, pixel tile), item =
-    // (pixel tile * ksplit + split) * co_tiles + channel tile. A workgroup
-    // takes items blockIdx.x, blockIdx.x + gridDim.x, ... and streams their
-    // stages back to back, so the next item's first stage is fetched while
-    // the current item's last stage runs.
-    const int64_t items = a.px_tiles * a.co_tiles * a.ksplit;
+    // Work items (channel tile, pixel tile), item = pixel tile * co_tiles +
+    // channel tile. A workgroup takes items blockIdx.x, blockIdx.x +
+    // gridDim.x, ... and streams their stages back to back, so the next
+    // item's first stage is fetched while the current item's last stage runs.
+    const int64_t items = a.px_tiles * a.co_tiles;
     struct Item {
         int co0, st0, st1, gr0, grl, n0;
         int64_t q0, qend;
     };
     auto item_of = [&](int64_t it, Item& m) {
         const int co_t = (int)(it % a.co_tiles);
-        const int64_t rest = it / a.co_tiles;
-        const int ksi = (int)(rest % a.ksplit);
-        const int64_t pt = rest / a.ksplit;
+        const int64_t pt = it / a.co_tiles;
         m.co0 = co_t * COT;
-        m.st0 = ksi * a.spk;
-        m.st1 = min(a.nstages, m.st0 + a.spk);
+        m.st0 = 0;
+        m.st1 = a.nstages;
         if (a.aligned) {   // pixel tile = (image, tile within the image)
             const int64_t img = pt / a.tiles_per_image;
             m.q0 = img * plane + (pt - img * a.tiles_per_image) * P;
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
     Item C;
     int xb = 0;
     auto setup_compute = [&]() {
-        int64_t q = C.q0 + wave * 32 + l32;
+        int64_t q = C.q0 + pbk * 32 + l32;
         if (q >= C.qend) q = C.qend - 1;
         const int gr = (int)a.divWo.div((uint32_t)(q - (int64_t)C.gr0 * Wo)) + C.gr0;
         const int wo = (int)(q - (int64_t)gr * Wo);
@@ -297,16 +301,28 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
     };
     auto compute_stage = [&](int st) {
         const int ks = min(CB, Ci - st * CB) * HW;
-        const int nfull = ks >> 1;   // pairs with two real K indices
+        // This wave's pairs [t0, t1) of the stage's (ks + 1) / 2; with ks
+        // odd the stage's last pair is half empty (odd_last: this wave has
+        // it) and nfull ends the pairs with two real K indices.
+        const int np = (ks + 1) >> 1;
+        int t0 = 0, t1 = np;
+        if (KSW > 1) {
+            const int per = (np + KSW - 1) / KSW;
+            t0 = min(np, kgr * per);
+            t1 = min(np, t0 + per);
+        }
+        const bool odd_last = (ks & 1) && t1 == np && t0 < t1;
+        const int nfull = odd_last ? t1 - 1 : t1;
+        if (t0 >= t1) return;
         // Pair t+1 is read from LDS while the MFMAs of pair t run. The loop
         // body fetches unconditionally (one pair past the end at most: an
         // in-allocation read that is never used), so every path into an
         // MFMA has the same reads outstanding and the waits stay exact.
         Frags f0, f1;
-        on0 = T[hl];
-        on1 = T[2 + hl];
-        fetch(f0, 0);
-        int t = 0;
+        on0 = T[2 * t0 + hl];
+        on1 = T[2 * t0 + 2 + hl];
+        fetch(f0, t0);
+        int t = t0;
         for (; t + 2 <= nfull; t += 2) {
             fetch(f1, t + 1);
             __builtin_amdgcn_sched_barrier(0);
@@ -317,24 +333,55 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
             mma(f1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // Left: f0 = pair t. Pair nfull, if ks is odd, is the last K index
+        // Left: f0 = pair t. Pair nfull, if odd_last, is the last K index
         // with a zero partner: filter entry ks is zero and lanes 32-63 zero
         // their window value.
         if (t < nfull) {
             mma(f0);
-            if (ks & 1) fetch(f0, nfull);
+            if (odd_last) fetch(f0, nfull);
             ++t;
         }
-        if (ks & 1) {
+        if (odd_last) {
             f0.b = hl ? 0.f : f0.b;
             mma(f0);
+        }
+    };
+
+    // Partial sums of the K shares (KSW > 1): shares 1 .. KSW-1 leave theirs
+    // in LDS past the offset table (one 4 KB block per share, pixel block
+    // and channel block: register r of lane l at float r*64 + l), and share
+    // 0 adds them in share order before the store. Every wave takes part in
+    // the barrier; the loop's next barrier keeps the area from being
+    // rewritten before share 0 has read it.
+    auto reduce_shares = [&]() {
+        float* R = reinterpret_cast<float*>(T + a.KT);
+        if (kgr > 0) {
+            float* d = R + (((kgr - 1) * NPB + pbk) * WCO) * 1024 + lane;
+#pragma unroll
+            for (int i = 0; i < WCO; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) d[(i * 16 + r) * 64] = acc[i][r];
+        }
+        __syncthreads();
+        if (kgr == 0) {
+            for (int g = 1; g < KSW; ++g) {
+                const float* s = R + (((g - 1) * NPB + pbk) * WCO) * 1024 + lane;
+#pragma unroll
+                for (int i = 0; i < WCO; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][r] += s[(i * 16 + r) * 64];
+            }
         }
     };
 
     // Output of item C: lane holds pixel l32 of its block and channels
     // 8*(r/4) + 4*hl + r%4 of each 32-channel block.
     auto epilogue = [&]() {
-        const int64_t qme = C.q0 + wave * 32 + l32;
+        if (KSW > 1) {
+            reduce_shares();
+            if (kgr > 0) return;
+        }
+        const int64_t qme = C.q0 + pbk * 32 + l32;
         const bool qok = qme < C.qend;
         const int64_t q = qok ? qme : C.qend - 1;
         const int gr = (int)(q / Wo);
@@ -342,34 +389,21 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
         const int n = (int)a.divHo.div((uint32_t)gr), ho = gr - n * Ho;
         const int co0 = C.co0;
         const bool all_co = co0 + COT <= Co;
-        if (a.ksplit == 1) {
-            // Byte offset = per-lane part (image, pixel, 4*hl channels) +
-            // uniform part (channel block row).
-            const __amdgpu_buffer_rsrc_t yb = buf(y, a.ybytes);
-            const uint32_t voff =
-                (uint32_t)((((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo) * 4);
-            if (qok) {
-#pragma unroll
-                for (int i = 0; i < WCO; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int cu = co0 + i * 32 + 8 * (r >> 2) + (r & 3);   // channel - 4*hl
-                        const float v = acc[i][r];
-                        if (all_co || cu + 4 * hl < Co)
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yb,
-                                                                  (int)voff,
-                                                                  (int)(cu * plane * 4), 0);
-                    }
-            }
-        } else {
-            float* yp = y + (((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo);
+        // Byte offset = per-lane part (image, pixel, 4*hl channels) +
+        // uniform part (channel block row).
+        const __amdgpu_buffer_rsrc_t yb = buf(y, a.ybytes);
+        const uint32_t voff =
+            (uint32_t)((((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo) * 4);
+        if (qok) {
 #pragma unroll
             for (int i = 0; i < WCO; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int cu = co0 + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (qok && (all_co || cu + 4 * hl < Co))
-                        unsafeAtomicAdd(yp + (int64_t)cu * plane, acc[i][r]);
+                    const int cu = co0 + i * 32 + 8 * (r >> 2) + (r & 3);   // channel - 4*hl
+                    const float v = acc[i][r];
+                    if (all_co || cu + 4 * hl < Co)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yb, (int)voff,
+                                                              (int)(cu * plane * 4), 0);
                 }
         }
     };
@@ -420,22 +454,10 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
     }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ y, int64_t n)
-{
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) y[i] = 0.f;
-}
-
-int env_int(const char* name, int dflt)
-{
-    const char* v = std::getenv(name);
-    return v && *v ? std::atoi(v) : dflt;
-}
-
-// Geometry of a launch with NW waves (32*NW pixels per tile) and 32*WCO
-// channels per tile, without K split; false if the shape is outside the
-// kernel's envelope.
-bool plan(const ConvShape& c, int nw, int wco, MArgs& a, int& xch, int& wch)
+// Geometry of a launch with NW waves, KSW of them sharing each pixel block
+// (32*NW/KSW pixels per tile), and 32*WCO channels per tile; false if the
+// shape is outside the kernel's envelope.
+bool plan(const ConvShape& c, int nw, int ksw, int wco, MArgs& a, int& xch, int& wch)
 {
     a.c = c;
     a.HW = c.Hf * c.Wf;
@@ -445,7 +467,8 @@ bool plan(const ConvShape& c, int nw, int wco, MArgs& a, int& xch, int& wch)
     xch = ceil_div(c.Wi, 64);
     if (xch == 3) xch = 4;
     if (xch > 4 || a.HW > 254) return false;
-    const int P = 32 * nw, cot = 32 * wco, rows_cap = nw * rows_per_wave(nw);
+    const int P = 32 * (nw / ksw), cot = 32 * wco, rows_cap = nw * rows_per_wave(nw);
+    const int64_t red = (int64_t)(ksw - 1) * (nw / ksw) * wco * 4096;   // K-share partial sums
     const int wrows = (cot + nw - 1) / nw * nw;   // filter rows staged (>= cot)
 
     // Entries per stride phase: every lane column (64*xch of them) has one.
@@ -469,14 +492,14 @@ bool plan(const ConvShape& c, int nw, int wco, MArgs& a, int& xch, int& wch)
     auto wregs = [&](int cb) { return wrows / nw * wch_of(cb); };
     auto lds_of = [&](int cb) {
         return (((int64_t)cb * a.RIN + 1) * a.RS + (int64_t)wrows * (64 * wch_of(cb) + 1) +
-                cb * a.HW + 12) * 4;
+                cb * a.HW + 12) * 4 + red;
     };
     auto fits = [&](int cb, int64_t budget) {
         return wch_of(cb) <= 2 && wregs(cb) <= 48 && lds_of(cb) <= budget;
     };
     int cb = std::min(c.Ci, rows_cap / a.RIN);
     while (cb > 1 && !fits(cb, 80 * 1024)) --cb;
-    cb = std::max(1, std::min(cb, env_int("IM2WIN_F32_CB", cb)));
+    if (knob(KNOB_F32_CB) > 0) cb = std::min(cb, knob(KNOB_F32_CB));
     if (!fits(cb, kMaxLds)) return false;
     wch = wch_of(cb);
     a.CB = cb;
@@ -486,8 +509,6 @@ bool plan(const ConvShape& c, int nw, int wco, MArgs& a, int& xch, int& wch)
     a.nstages = ceil_div(c.Ci, cb);
     a.co_tiles = ceil_div(c.Co, cot);
     a.px_tiles = a.aligned ? (int64_t)c.N * a.tiles_per_image : (a.total + P - 1) / P;
-    a.ksplit = 1;
-    a.spk = a.nstages;
     if (a.px_tiles * a.co_tiles > 0x7fffffff) return false;
 
     // Scalar offsets and buffer ranges are 32-bit; a row with no source uses
@@ -506,27 +527,28 @@ bool plan(const ConvShape& c, int nw, int wco, MArgs& a, int& xch, int& wch)
     return true;
 }
 
-size_t lds_bytes(const MArgs& a, int nw, int wco)
+size_t lds_bytes(const MArgs& a, int nw, int ksw, int wco)
 {
     const int wrows = (32 * wco + nw - 1) / nw * nw;
-    return ((size_t)a.xent + (size_t)wrows * a.KSP + a.KT) * 4;
+    return ((size_t)a.xent + (size_t)wrows * a.KSP + a.KT) * 4 +
+           (size_t)(ksw - 1) * (nw / ksw) * wco * 4096;
 }
 
-template <int NW, int WCO, int XCH>
+template <int NW, int KSW, int WCO, int XCH>
 const void* kernel_w(int wch)
 {
-    if (wch == 1) return (const void*)conv_f32_mfma_kernel<NW, WCO, XCH, 1>;
-    if (wch == 2) return (const void*)conv_f32_mfma_kernel<NW, WCO, XCH, 2>;
+    if (wch == 1) return (const void*)conv_f32_mfma_kernel<NW, KSW, WCO, XCH, 1>;
+    if (wch == 2) return (const void*)conv_f32_mfma_kernel<NW, KSW, WCO, XCH, 2>;
     return nullptr;
 }
 
-template <int NW, int WCO>
+template <int NW, int KSW, int WCO>
 const void* kernel_x(int xch, int wch)
 {
     switch (xch) {
-    case 1: return kernel_w<NW, WCO, 1>(wch);
-    case 2: return kernel_w<NW, WCO, 2>(wch);
-    case 4: return kernel_w<NW, WCO, 4>(wch);
+    case 1: return kernel_w<NW, KSW, WCO, 1>(wch);
+    case 2: return kernel_w<NW, KSW, WCO, 2>(wch);
+    case 4: return kernel_w<NW, KSW, WCO, 4>(wch);
     }
     return nullptr;
 }
@@ -535,20 +557,31 @@ template <int NW>
 const void* kernel_c(int wco, int xch, int wch)
 {
     switch (wco) {
-    case 1: return kernel_x<NW, 1>(xch, wch);
-    case 2: return kernel_x<NW, 2>(xch, wch);
-    case 3: return kernel_x<NW, 3>(xch, wch);
-    case 4: return kernel_x<NW, 4>(xch, wch);
+    case 1: return kernel_x<NW, 1, 1>(xch, wch);
+    case 2: return kernel_x<NW, 1, 2>(xch, wch);
+    case 3: return kernel_x<NW, 1, 3>(xch, wch);
+    case 4: return kernel_x<NW, 1, 4>(xch, wch);
     }
     return nullptr;
 }
 
-const void* kernel_of(int nw, int wco, int xch, int wch)
+// Kernels: K shares ksw of 1 (any channel tile) or NW (one pixel block and
+// one 32-channel block per tile).
+const void* kernel_of(int nw, int ksw, int wco, int xch, int wch)
 {
+    if (ksw == 1) {
+        switch (nw) {
+        case 4: return kernel_c<4>(wco, xch, wch);
+        case 8: return kernel_c<8>(wco, xch, wch);
+        case 12: return kernel_c<12>(wco, xch, wch);
+        }
+        return nullptr;
+    }
+    if (wco != 1 || ksw != nw) return nullptr;
     switch (nw) {
-    case 4: return kernel_c<4>(wco, xch, wch);
-    case 8: return kernel_c<8>(wco, xch, wch);
-    case 12: return kernel_c<12>(wco, xch, wch);
+    case 4: return kernel_x<4, 4, 1>(xch, wch);
+    case 8: return kernel_x<8, 8, 1>(xch, wch);
+    case 12: return kernel_x<12, 12, 1>(xch, wch);
     }
     return nullptr;
 }
@@ -556,22 +589,28 @@ const void* kernel_of(int nw, int wco, int xch, int wch)
 std::mutex g_mu;
 
 // Workgroups of kernel f that fit on one CU (registers and LDS), with the
-// LDS limit raised to the CU's full 160 KB once per kernel.
+// LDS limit raised to the CU's full 160 KB once per kernel. Results are
+// cached per (kernel, LDS bytes, device) under a lock.
 int blocks_per_cu(const void* f, int nt, size_t lds)
 {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();   // handled: no device, the kernel is not used
+        return 0;
+    }
     std::lock_guard<std::mutex> lk(g_mu);
-    static std::set<const void*> raised;
-    static std::map<std::pair<const void*, size_t>, int> cache;
-    const auto key = std::make_pair(f, lds);
+    static std::map<std::pair<const void*, int>, bool> raised;
+    static std::map<std::pair<std::pair<const void*, size_t>, int>, int> cache;
+    const auto key = std::make_pair(std::make_pair(f, lds), dev);
     const auto it = cache.find(key);
     if (it != cache.end()) return it->second;
-    if (!raised.count(f)) {
+    if (!raised.count(std::make_pair(f, dev))) {
         if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds) !=
             hipSuccess) {
             (void)hipGetLastError();   // handled: this kernel is not used
             return 0;
         }
-        raised.insert(f);
+        raised[std::make_pair(f, dev)] = true;
     }
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, nt, lds) != hipSuccess) {
@@ -595,7 +634,7 @@ int cu_count()
 
 struct Choice {
     MArgs a;
-    int nw, wco, xch, wch;
+    int nw, ksw, wco, xch, wch;
     const void* f;
     size_t lds;
     int occ;          // workgroups that fit on a CU
@@ -604,23 +643,23 @@ struct Choice {
     int wps;          // waves per SIMD
 };
 
-// Persistent grid for `items` work items: G = CUs*o workgroups (o <= occ),
-// each taking ceil(items/G) items in turn. A wave's work per item is the same
-// for every NW (32 pixels x the channel tile x K), and a SIMD's matrix core
-// is shared by its waves, so the time is ~ items per workgroup x waves per
-// SIMD; ties go to more waves per SIMD (more latency hiding).
+// Persistent grid for the work items: G = CUs*o workgroups (o <= occ), each
+// taking ceil(items/G) items in turn. A wave's work per item is 32 pixels x
+// the channel tile (32*WCO) x K / KSW, and a SIMD's matrix core is shared by
+// its waves, so the time is ~ items per workgroup x waves per SIMD x WCO /
+// KSW; ties go to more waves per SIMD (more latency hiding).
 void size_grid(Choice& t, int ncu)
 {
-    const int64_t items = t.a.px_tiles * t.a.co_tiles * t.a.ksplit;
-    const int force = env_int("IM2WIN_F32_OCC", 0);
+    const int64_t items = t.a.px_tiles * t.a.co_tiles;
+    const int force = knob(KNOB_F32_OCC);
     t.cost = 1e300;
     t.wps = 0;
     for (int o = 1; o <= t.occ; ++o) {
-        if (force && o != force) continue;
+        if (force > 0 && o != force) continue;
         const int64_t G = std::min<int64_t>(items, (int64_t)ncu * o);
         const int64_t per = (items + G - 1) / G;
         const int wps = (t.nw * o + 3) / 4;
-        const double c = (double)per * wps;
+        const double c = (double)per * wps * t.wco / t.ksw;
         if (c < t.cost * (1 - 1e-9) || (c < t.cost * (1 + 1e-9) && wps > t.wps)) {
             t.cost = c;
             t.wps = wps;
@@ -629,7 +668,7 @@ void size_grid(Choice& t, int ncu)
     }
 }
 
-// Picks waves per workgroup, channel tile, K split and grid.
+// Picks waves per workgroup, K shares, channel tile and grid.
 bool choose(const ConvShape& c, Choice& ch)
 {
     const int ncu = cu_count();
@@ -641,74 +680,72 @@ bool choose(const ConvShape& c, Choice& ch)
             wco0 = cand;
         }
     }
-    const int env_wco = env_int("IM2WIN_F32_WCO", 0), env_nw = env_int("IM2WIN_F32_NW", 0);
-    if (env_wco) wco0 = env_wco;
+    const int k_wco = knob(KNOB_F32_WCO), k_nw = knob(KNOB_F32_NW), k_ks = knob(KNOB_F32_KSPLIT);
+    if (k_wco >= 1 && k_wco <= 4) wco0 = k_wco;
 
-    auto make = [&](int nw, int wc, Choice& t) -> bool {
+    auto make = [&](int nw, int ksw, int wc, Choice& t) -> bool {
         t.nw = nw;
+        t.ksw = ksw;
         t.wco = wc;
-        if (!plan(c, nw, wc, t.a, t.xch, t.wch)) return false;
-        t.f = kernel_of(nw, wc, t.xch, t.wch);
+        if (!plan(c, nw, ksw, wc, t.a, t.xch, t.wch)) return false;
+        t.f = kernel_of(nw, ksw, wc, t.xch, t.wch);
         if (!t.f) return false;
-        t.lds = lds_bytes(t.a, nw, wc);
+        t.lds = lds_bytes(t.a, nw, ksw, wc);
         t.occ = blocks_per_cu(t.f, 64 * nw, t.lds);
-        return t.occ >= 1;
+        if (t.occ < 1) return false;
+        size_grid(t, ncu);
+        return true;
     };
-    // Too few tiles to fill the chip: narrow channel tiles and split K over
-    // work items (about 2.5 per CU).
-    auto split = [&](Choice& t) {
-        if (t.a.px_tiles * t.a.co_tiles < ncu && t.a.nstages > 1 && !env_wco && t.wco > 1) {
-            Choice u;
-            if (make(t.nw, 1, u)) t = u;
-        }
-        MArgs& a = t.a;
-        const int64_t b = a.px_tiles * a.co_tiles;
-        a.ksplit = 1;
-        if (b < ncu && a.nstages > 1)
-            a.ksplit = (int)std::min<int64_t>(a.nstages, (5 * (int64_t)ncu / 2 + b - 1) / b);
-        const int ks = env_int("IM2WIN_F32_KSPLIT", 0);
-        if (ks > 0) a.ksplit = std::min(a.nstages, ks);
-        a.spk = ceil_div(a.nstages, a.ksplit);
-        a.ksplit = ceil_div(a.nstages, a.spk);
+    auto better = [&](const Choice& t) {
+        return t.cost < ch.cost * (1 - 1e-9) || (t.cost < ch.cost * (1 + 1e-9) && t.wps > ch.wps);
     };
 
     bool found = false;
     for (int wco = wco0; wco >= 1 && !found; --wco) {
         for (int nw : {12, 8, 4}) {
-            if (env_nw && nw != env_nw) continue;
+            if (k_nw && nw != k_nw) continue;
             Choice t;
-            if (!make(nw, wco, t)) continue;
-            split(t);
-            if (t.a.px_tiles * t.a.co_tiles * t.a.ksplit > 0x7fffffff) continue;
-            size_grid(t, ncu);
-            if (!found || t.cost < ch.cost * (1 - 1e-9) ||
-                (t.cost < ch.cost * (1 + 1e-9) && t.wps > ch.wps)) {
+            if (k_ks > 1 || !make(nw, 1, wco, t)) continue;
+            if (!found || better(t)) {
                 ch = t;
                 found = true;
             }
         }
-        if (env_wco) break;
+        if (k_wco) break;
+    }
+    // Too few tiles to fill the chip: one 32-channel block and one pixel
+    // block per tile, K shared by the workgroup's waves.
+    const bool small = !found || ch.a.px_tiles * ch.a.co_tiles < ncu;
+    if ((small && k_ks != 1 && !k_wco) || k_ks > 1) {
+        for (int nw : {12, 8, 4}) {
+            if (k_nw && nw != k_nw) continue;
+            if (k_ks > 1 && nw != k_ks) continue;
+            Choice t;
+            if (!make(nw, nw, 1, t)) continue;
+            if (!found || k_ks > 1 || better(t)) {
+                ch = t;
+                found = true;
+                if (k_ks > 1) break;
+            }
+        }
     }
     return found;
 }
 
 }  // namespace
 
+bool f32_mfma_applies(const ConvShape& c)
+{
+    Choice ch;
+    return choose(c, ch);
+}
+
 int launch_conv_f32_mfma(const float* x, const float* w, float* y, const ConvShape& c,
                          hipStream_t stream)
 {
     Choice ch;
     if (!choose(c, ch)) return -1;
-    const MArgs& a = ch.a;
-    if (a.ksplit > 1) {
-        // Partial sums are added into y: clear it first (a kernel, not a
-        // memset node, so the call stays capturable).
-        const int64_t n = (int64_t)c.N * c.Co * c.Ho * c.Wo;
-        const int64_t blocks = (n + 255) / 256;
-        if (blocks > 0x7fffffff) return -1;
-        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y, n);
-    }
-    MArgs args = a;
+    MArgs args = ch.a;
     void* params[] = {(void*)&x, (void*)&w, (void*)&y, (void*)&args};
     const dim3 grid((unsigned)ch.grid), block(64 * ch.nw);
     const hipError_t e = hipLaunchKernel(ch.f, grid, block, params, ch.lds, stream);

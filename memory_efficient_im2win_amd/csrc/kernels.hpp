@@ -31,22 +31,34 @@ int launch_conv_f32(const float* x, const float* ws, const float* w, float* y,
 
 // fp32 convolution on the matrix cores (v_mfma_f32_32x32x2_f32), window
 // tiles built in LDS from x. -1 if the shape is outside its envelope. Small
-// problems split K and clear y first (atomics add the partial sums).
+// problems split K over the waves of a workgroup (fixed-order sums).
 int launch_conv_f32_mfma(const float* x, const float* w, float* y, const ConvShape& c,
                          hipStream_t stream);
+bool f32_mfma_applies(const ConvShape& c);
 
 // fp16 x fp16 -> fp32 convolution on the matrix cores; ws as above.
 int launch_conv_f16(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float* y,
                     const ConvShape& c, hipStream_t stream);
 
 // Fused fp16 convolution (im2win window tiles built in LDS). wpk is the
-// filter prepacked by launch_f16_filter_pack, or nullptr to gather the
-// filters from w inside the kernel. -1 if the shape is outside its envelope.
+// filter prepacked by launch_f16_filter_pack for the same shape and x, or
+// nullptr to gather the filters from w inside the kernel. -1 if the shape is
+// outside every tiled kernel's envelope.
 int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk, float* y,
                           const ConvShape& c, hipStream_t stream);
-// Bytes of the prepacked fp16 filter for the fused kernel (0: not used).
+// Bytes that hold the prepacked fp16 filter in the layout of any fused
+// kernel (depends on the shape only). The pack writes the layout of the
+// kernel the call with this shape and x runs on (-1: none of them takes it).
 size_t f16_filter_pack_bytes(const ConvShape& c);
-int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, hipStream_t stream);
+int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, const void* x,
+                           hipStream_t stream);
+// Name of the kernel launch_conv_f16_fused runs for this shape and x.
+const char* f16_fused_kernel_name(const ConvShape& c, const void* x);
+
+// Raises kernel f's dynamic LDS limit to `bytes` on the current device, once
+// per (kernel, device); thread-safe. A failure is left for the launch to
+// report.
+void ensure_lds_limit(const void* f, int bytes);
 
 // fp16 convolution with the input rows copied to LDS by direct loads and the
 // filter prepacked by launch_f16_rows_filter_pack (its own layout; wp), or

@@ -19,6 +19,23 @@ def orc():
     return oracle.default()
 
 
+@pytest.fixture
+def knob():
+    """knob(name, value) sets a planner knob of the library for the test and
+    restores the previous values afterwards."""
+    import memory_efficient_im2win_amd as m
+    saved = {}
+
+    def set_(name, value):
+        if name not in saved:
+            saved[name] = m.get_knob(name)
+        m.set_knob(name, int(value))
+
+    yield set_
+    for k, v in saved.items():
+        m.set_knob(k, v)
+
+
 def pytest_sessionstart(session):
     # Load what is built; build (CPU cross-compile) only if nothing is.
     lib = os.path.join(ROOT, "memory_efficient_im2win_amd", "libim2win.so")

@@ -46,3 +46,36 @@ def assert_exact(y, ref, what):
         detail = ", ".join(f"{tuple(int(v) for v in i)}: gpu={y[tuple(i)]} ref={r[tuple(i)]}"
                            for i in bad)
         raise AssertionError(f"{what}: {int((y != r).sum())} outputs differ; {detail}")
+
+
+# Workspace modes of a convolution call: None (fused, no workspace),
+# "filter" (fp16 fused with its filter prepacked into a workspace by
+# conv2d_fused; the same as None for fp32), "full" (materialised over the
+# whole batch: exactly workspace_bytes(N)) and "one" (materialised one image
+# at a time: workspace_bytes(1)).
+WS_KINDS = [None, "filter", "full", "one"]
+
+
+def workspace(sh, kind, dev):
+    """The workspace tensor for mode `kind` of shape sh, or None."""
+    import torch
+    import memory_efficient_im2win_amd as m
+    if kind is None or (kind == "filter" and sh.dtype == "f32"):
+        return None
+    if kind == "filter":
+        nb = m.fused_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s)
+    else:
+        n = sh.N if kind == "full" else 1
+        nb = m.workspace_bytes(n, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
+    return torch.empty(nb, dtype=torch.uint8, device=dev)
+
+
+def call(sh, xt, wt, kind, dev, out=None, ws=None):
+    """One convolution call through the binding in workspace mode `kind`
+    (ws: a workspace tensor to use instead of a fresh one)."""
+    import memory_efficient_im2win_amd as m
+    if ws is None:
+        ws = workspace(sh, kind, dev)
+    if kind == "filter" and sh.dtype == "f16":
+        return m.conv2d_fused(xt, wt, sh.s, fws=ws, out=out)
+    return m.conv2d(xt, wt, sh.s, ws=ws, out=out)

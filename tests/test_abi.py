@@ -21,9 +21,11 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     single = ["im2win_workspace_bytes", "im2win_output_dims", "im2win_pack",
-              "conv2d_im2win_fp32", "conv2d_im2win_fp16", "conv2d_im2win_workspace_bytes"]
+              "conv2d_im2win_fp32", "conv2d_im2win_fp16"]
     assert declared_functions() == sorted(
         single + [f + "_strided" for f in single] + ["im2win_status_string", "im2win_last_error"] +
+        ["conv2d_im2win_fp16_fused_workspace_bytes", "conv2d_im2win_fp16_fused",
+         "im2win_set_knob", "im2win_get_knob", "im2win_knob_name", "im2win_conv_kernel_name"] +
         ["conv2d_im2col_workspace_bytes", "im2col_pack", "conv2d_im2col_fp32", "conv2d_im2col_fp16",
          "conv2d_direct_fp32", "conv2d_direct_fp16", "conv2d_im2win_nhwc_workspace_bytes",
          "im2win_pack_nhwc", "conv2d_im2win_nhwc_fp32", "conv2d_im2win_nhwc_fp16"])
@@ -84,9 +86,6 @@ def test_single_stride_entry_points_equal_their_strided_twins():
         for e in (2, 4):
             assert L.im2win_workspace_bytes(3, 5, Hi, Wi, Hf, Wf, s, e) == \
                 L.im2win_workspace_bytes_strided(3, 5, Hi, Wi, Hf, Wf, s, s, e)
-            for mat in (0, 1):
-                assert L.conv2d_im2win_workspace_bytes(mat, 3, 5, Hi, Wi, 64, Hf, Wf, s, e) == \
-                    L.conv2d_im2win_workspace_bytes_strided(mat, 3, 5, Hi, Wi, 64, Hf, Wf, s, s, e)
 
 
 def test_unequal_strides_axes():
@@ -116,7 +115,7 @@ def test_workspace_bytes_invalid(args):
 def test_strided_rejects_a_zero_or_negative_stride(sh, sw):
     L = m.load_library()
     assert L.im2win_workspace_bytes_strided(1, 1, 8, 8, 2, 2, sh, sw, 4) == 0
-    assert L.conv2d_im2win_workspace_bytes_strided(1, 1, 1, 8, 8, 1, 2, 2, sh, sw, 4) == 0
+    assert L.conv2d_im2win_fp16_fused_workspace_bytes(1, 1, 8, 8, 1, 2, 2, sh, sw) == 0
     assert L.im2win_output_dims_strided(8, 8, 2, 2, sh, sw, None, None) == _lib.IM2WIN_EINVAL
     assert L.im2win_pack_strided(FAKE, FAKE, 1, 1, 8, 8, 2, 2, sh, sw, 4, None) == \
         _lib.IM2WIN_EINVAL
@@ -157,11 +156,9 @@ def test_conv_rejects_bad_arguments_before_launch(fn):
     # misaligned tensors
     odd = ctypes.c_void_p(0x10001)
     assert f(odd, FAKE, FAKE, None, 0, *ok, None) == _lib.IM2WIN_EINVAL
-    # workspace: NULL with a size, or smaller than its smallest valid size
+    # workspace: NULL with a size, or smaller than one image's im2win rows
     e = 4 if fn.endswith("32") else 2
-    F = m.conv_workspace_bytes(1, 3, 8, 8, 4, 3, 3, 1, e, False)
-    I = m.workspace_bytes(1, 3, 8, 8, 3, 3, 1, e)
-    smallest = F if F else I
+    smallest = m.workspace_bytes(1, 3, 8, 8, 3, 3, 1, e)
     assert f(FAKE, FAKE, FAKE, None, 64, *ok, None) == _lib.IM2WIN_EWORKSPACE
     assert f(FAKE, FAKE, FAKE, FAKE, smallest - 1, *ok, None) == _lib.IM2WIN_EWORKSPACE
     assert f(FAKE, FAKE, FAKE, FAKE, 0, *ok, None) == _lib.IM2WIN_EWORKSPACE
@@ -169,20 +166,48 @@ def test_conv_rejects_bad_arguments_before_launch(fn):
     assert f(FAKE, FAKE, FAKE, ctypes.c_void_p(0x10008), smallest, *ok, None) == _lib.IM2WIN_EINVAL
 
 
-def test_conv_workspace_query():
-    # fp32: the fused path needs nothing; materialised = the im2win tensor.
-    assert m.conv_workspace_bytes(32, 3, 227, 227, 96, 11, 11, 4, 4, False) == 0
-    assert m.conv_workspace_bytes(32, 3, 227, 227, 96, 11, 11, 4, 4, True) == 52_736_640
-    # fp16: a prepacked filter (256-byte multiple, at least the filter) ahead of the im2win part.
+def test_fused_workspace_query():
+    """The fp16 filter scratch holds either prepacked layout (slices of 8 taps
+    for 64-channel tiles, or 16-byte entries of 8 input channels for
+    128-channel tiles; worked out here independently), rounded up to 256
+    bytes, and depends on the shape only (no knob changes it)."""
     for (N, Ci, Hi, Wi, Co, Hf, Wf, s) in [(64, 64, 224, 224, 64, 7, 7, 2),
                                            (128, 96, 24, 24, 256, 5, 5, 1),
-                                           (64, 3, 227, 227, 64, 7, 7, 2)]:
-        F = m.conv_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s, 2, False)
-        assert F % 256 == 0 and F >= Co * Ci * Hf * Wf * 2
-        assert m.conv_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s, 2, True) == \
-            F + m.workspace_bytes(N, Ci, Hi, Wi, Hf, Wf, s, 2)
-    assert m.conv_workspace_bytes(1, 3, 4, 4, 2, 5, 5, 1, 2, False) == 0   # invalid shape
-    assert m.conv_workspace_bytes(1, 3, 8, 8, 2, 3, 3, 1, 3, False) == 0   # element size
+                                           (64, 3, 227, 227, 64, 7, 7, 2),
+                                           (1, 10, 40, 40, 24, 17, 17, 1)]:
+        slices = Ci * Hf * (-(-Co // 64) * 64) * 16 if Wf <= 8 and Hf * Wf <= 256 else 0
+        inter = -(-Ci // 8) * ((Hf * Wf + 1) & ~1) * (-(-Co // 128) * 128) * 16
+        F = m.fused_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s)
+        assert F == -(-max(slices, inter) // 256) * 256, (F, slices, inter)
+        with m.knobs(f16_rows=-1, f16_thin=-1, f16_wide=-1):
+            assert m.fused_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s) == F
+    assert m.fused_workspace_bytes(1, 3, 4, 4, 2, 5, 5, 1) == 0   # invalid shape
+
+
+def test_fused_rejects_bad_arguments_before_launch():
+    L = m.load_library()
+    f = L.conv2d_im2win_fp16_fused
+    ok = (1, 3, 8, 8, 4, 3, 3, 1, 1)
+    F = L.conv2d_im2win_fp16_fused_workspace_bytes(*ok)
+    assert f(None, FAKE, FAKE, None, 0, *ok, None) == _lib.IM2WIN_EINVAL
+    assert f(FAKE, FAKE, FAKE, None, 0, 1, 3, 8, 8, 4, 9, 3, 1, 1, None) == _lib.IM2WIN_EINVAL
+    assert f(FAKE, FAKE, FAKE, None, 64, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, F - 1, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    assert f(FAKE, FAKE, FAKE, ctypes.c_void_p(0x10008), F, *ok, None) == _lib.IM2WIN_EINVAL
+
+
+def test_knobs():
+    names = m.knob_names()
+    assert len(names) == len(set(names)) and "f32_valu" in names and "tile_order" in names
+    L = m.load_library()
+    assert L.im2win_knob_name(len(names)) is None and L.im2win_knob_name(-1) is None
+    assert L.im2win_set_knob(len(names), 1) == _lib.IM2WIN_EINVAL
+    assert all(m.get_knob(n) == 0 for n in names)
+    with m.knobs(f32_nw=8, tile_order=1):
+        assert m.get_knob("f32_nw") == 8 and m.get_knob("tile_order") == 1
+    assert m.get_knob("f32_nw") == 0 and m.get_knob("tile_order") == 0
+    with pytest.raises(ValueError):
+        m.set_knob("no_such_knob", 1)
 
 
 def test_pack_rejects_bad_arguments_before_launch():
@@ -272,3 +297,60 @@ def test_nhwc_conv_rejects_bad_arguments(fn):
     assert f(FAKE, FAKE, FAKE, FAKE, 64, *ok, None) == _lib.IM2WIN_EWORKSPACE
     assert f(FAKE, FAKE, FAKE, None, 0, 1, 16, 8, 8, 4, 3, 3, 1, 0, None) == _lib.IM2WIN_EINVAL
     assert L.im2win_pack_nhwc(FAKE, None, 1, 1, 4, 4, 2, 2, 1, 1, 4, None) == _lib.IM2WIN_EINVAL
+
+
+def test_binding_checks_workspace_extent():
+    """A workspace byte count past the tensor, or a tensor on another device,
+    is refused before the library is called (stand-in tensor objects; no GPU
+    needed)."""
+    from memory_efficient_im2win_amd import _ws_arg
+
+    class Dev:
+        def __init__(self, i):
+            self.i = i
+
+        def __eq__(self, o):
+            return self.i == o.i
+
+    class T:
+        is_cuda = True
+
+        def __init__(self, n, dev=0):
+            self.n, self.device = n, Dev(dev)
+
+        def is_contiguous(self):
+            return True
+
+        def numel(self):
+            return self.n
+
+        def element_size(self):
+            return 1
+
+        def data_ptr(self):
+            return 0x10000
+
+    x = T(1)
+    assert _ws_arg(T(100), None, x, "ws")[1] == 100
+    assert _ws_arg(T(100), 60, x, "ws")[1] == 60
+    with pytest.raises(ValueError):
+        _ws_arg(T(100), 101, x, "ws")
+    with pytest.raises(ValueError):
+        _ws_arg(T(100, dev=1), None, x, "ws")
+    with pytest.raises(ValueError):
+        _ws_arg(None, 64, x, "ws")
+
+
+def test_conv_kernel_name():
+    """The fp16 kernel a call runs, as the planners pick it (no GPU needed;
+    the fp32 planner asks the device for occupancy, so its names are checked
+    on the GPU)."""
+    assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2) == "conv_f16_rows_kernel"
+    assert m.conv_kernel_name(64, 3, 227, 227, 64, 7, 7, 2, 2) == "conv_f16_thin_kernel"
+    assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2) == "conv_f16_wide_kernel"
+    with m.knobs(f16_rows=-1, f16_thin=-1, f16_wide=-1):
+        assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2, "prepacked") == \
+            "conv_f16_fused_kernel"
+    assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2, "materialized") == "conv_f16_kernel"
+    with pytest.raises(ValueError):
+        m.conv_kernel_name(1, 3, 4, 4, 2, 5, 5, 1, 2)

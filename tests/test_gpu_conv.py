@@ -10,7 +10,8 @@ import pytest
 
 import memory_efficient_im2win_amd as m
 import workloads
-from parity import TOL, assert_exact, assert_within, device, note, to_dev
+from parity import (TOL, WS_KINDS, assert_exact, assert_within, call, device, note, to_dev,
+                    workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,34 +34,15 @@ SMALL = [
 ]
 
 
-WS_KINDS = [None, "filter", "full", "one"]
-
-
 def _ws(sh, kind, dev):
-    """Workspace tensor for a call: None (fused, no workspace), "filter" (fused
-    with the fp16 filter prepacked; same as None for fp32), "full" (materialised
-    over the whole batch) or "one" (materialised one image at a time)."""
-    import torch
-    if kind is None:
-        return None
-    args = (sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
-    F = m.conv_workspace_bytes(*args, False)
-    if kind == "filter":
-        nb = F
-    elif kind == "full":
-        nb = m.conv_workspace_bytes(*args, True)
-    else:
-        nb = F + m.workspace_bytes(1, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
-    if nb == 0:
-        return None
-    return torch.empty(nb, dtype=torch.uint8, device=dev)
+    return workspace(sh, kind, dev)
 
 
 def _run(sh, mode, x, w, ws_kind=None):
     import torch
     dev = device()
     xt, wt = to_dev(x, dev), to_dev(w, dev)
-    y = m.conv2d(xt, wt, sh.s, ws=_ws(sh, ws_kind, dev))
+    y = call(sh, xt, wt, ws_kind, dev)
     out = y.cpu().numpy()
     torch.cuda.synchronize()
     return out
@@ -94,9 +76,9 @@ def test_conv_small_integer_exact(t, dt, orc):
 
 
 @pytest.mark.parametrize("t", SMALL, ids=str)
-def test_conv_f32_vector_alu_path(t, orc, monkeypatch):
+def test_conv_f32_vector_alu_path(t, orc, knob):
     """fp32 on the vector-ALU kernel (the fallback of the matrix-core one)."""
-    monkeypatch.setenv("IM2WIN_F32_PATH", "valu")
+    knob("f32_valu", 1)
     sh = _shape(t, "f32")
     x, w = workloads.make_inputs(sh, seed=16)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
@@ -108,13 +90,15 @@ def test_conv_f32_vector_alu_path(t, orc, monkeypatch):
     assert_exact(_run(sh, "f32", xi, wi), orc.conv_direct(xi, wi, sh.s), sh.describe())
 
 
-@pytest.mark.parametrize("ksplit", [1, 3])
+@pytest.mark.parametrize("ksplit", [1, 4, 8, 12])
 @pytest.mark.parametrize("t", [(1, 96, 12, 12, 256, 5, 5, 1), (2, 16, 20, 20, 40, 3, 3, 1),
-                               (3, 7, 26, 26, 33, 5, 5, 1)], ids=str)
-def test_conv_f32_k_split(t, ksplit, orc, monkeypatch):
-    """The matrix-core fp32 kernel with K split over workgroups (partial sums
-    added into the cleared output) and without."""
-    monkeypatch.setenv("IM2WIN_F32_KSPLIT", str(ksplit))
+                               (3, 7, 26, 26, 33, 5, 5, 1), (1, 3, 40, 40, 20, 11, 11, 4),
+                               (1, 5, 9, 9, 7, 3, 3, 2)], ids=str)
+def test_conv_f32_k_split(t, ksplit, orc, knob):
+    """The matrix-core fp32 kernel with K shared by 4, 8 or 12 waves of a
+    workgroup (partial sums added through LDS in a fixed order; stages with
+    fewer K pairs than waves included) and without a K split."""
+    knob("f32_ksplit", ksplit)
     sh = _shape(t, "f32")
     x, w = workloads.make_inputs(sh, seed=18)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
@@ -161,6 +145,8 @@ def test_conv_special_values(dt, orc):
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_conv_writes_only_its_output(dt, orc):
+    """Outputs and workspaces sit between NaN / 0x7F guard bands that no
+    call may touch, in every workspace mode."""
     import torch
     dev = device()
     sh = _shape((2, 12, 17, 15, 41, 3, 5, 2), dt)
@@ -168,17 +154,21 @@ def test_conv_writes_only_its_output(dt, orc):
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
     n = ref.size
     note(f"conv guard bands {sh.describe()}")
+    xt, wt = to_dev(x, dev), to_dev(w, dev)
     for kind in WS_KINDS:
         big = torch.full((n + 2 * 129,), float("nan"), dtype=torch.float32, device=dev)
         out = big[129:129 + n].view(ref.shape)
         ws = _ws(sh, kind, dev)
         wsbig = None
-        kw = {}
-        if ws is not None:
+        if ws is None:
+            m.conv2d(xt, wt, sh.s, out=out)
+        else:
             nb = ws.numel()
             wsbig = torch.full((nb + 4096,), 0x7F, dtype=torch.uint8, device=dev)
-            kw = dict(ws=wsbig, ws_bytes=nb)
-        m.conv2d(to_dev(x, dev), to_dev(w, dev), sh.s, out=out, **kw)
+            if kind == "filter":
+                m.conv2d_fused(xt, wt, sh.s, fws=wsbig, fws_bytes=nb, out=out)
+            else:
+                m.conv2d(xt, wt, sh.s, ws=wsbig, ws_bytes=nb, out=out)
         b = big.cpu().numpy()
         assert np.isnan(b[:129]).all() and np.isnan(b[129 + n:]).all()
         assert_within(b[129:129 + n].reshape(ref.shape), ref, absd, TOL[dt], f"guarded output {kind}")
@@ -186,46 +176,15 @@ def test_conv_writes_only_its_output(dt, orc):
             assert (wsbig[nb:].cpu().numpy() == 0x7F).all()
 
 
-@pytest.mark.slow
-@pytest.mark.parametrize("key", ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64",
-                                 "cv4_f16_n64", "cv2_f32_n32"])
-@pytest.mark.parametrize("mode", ["uniform", "int"])
-def test_conv_full_size_sampled(key, mode, orc):
-    """The benchmark layers at full size in every launch configuration the
-    benchmark times (fused; fused with a prepacked fp16 filter; materialised),
-    checked at ~3000 outputs the oracle computes one by one (corners
-    included)."""
-    import torch
-    dev = device()
-    sh = workloads.BY_KEY[key]
-    x, w = workloads.make_inputs(sh, seed=0 if mode == "uniform" else 1, mode=mode)
-    Ho, Wo = m.output_dims(sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s)
-    idx = workloads.sample_output_indices(sh, Ho, Wo, 3000)
-    ref, absd = orc.conv_points(x, w, sh.s, idx)
-    xt, wt = to_dev(x, dev), to_dev(w, dev)
-    for kind in (None, "filter", "full"):
-        if kind == "filter" and sh.dtype == "f32":
-            continue
-        note(f"conv full {sh.describe()} {mode} ws={kind}")
-        y = m.conv2d(xt, wt, sh.s, ws=_ws(sh, kind, dev)).reshape(-1)
-        got = y[torch.from_numpy(idx).to(dev)].cpu().numpy()
-        assert bool(torch.isfinite(y).all())
-        if mode == "int":
-            assert_exact(got, ref, sh.describe())
-        else:
-            assert_within(got, ref, absd, TOL[sh.dtype], sh.describe())
-        del y
-    torch.cuda.synchronize()
-
-
 @pytest.mark.parametrize("nw", [4, 8, 12])
 @pytest.mark.parametrize("t", [(2, 3, 227, 227, 96, 11, 11, 4), (1, 16, 30, 30, 64, 7, 7, 2),
                                (3, 7, 26, 26, 33, 5, 5, 1), (2, 10, 19, 37, 130, 3, 3, 2),
                                (2, 5, 31, 40, 48, 3, 7, 2), (1, 8, 20, 33, 40, 7, 3, 3)], ids=str)
-def test_conv_f32_matrix_waves(t, nw, orc, monkeypatch):
+def test_conv_f32_matrix_waves(t, nw, orc, knob):
     """The fp32 matrix-core kernel forced to 4, 8 and 12 waves per workgroup
     (32*NW-pixel tiles: different tilings, row counts and item streams)."""
-    monkeypatch.setenv("IM2WIN_F32_NW", str(nw))
+    knob("f32_ksplit", 1)
+    knob("f32_nw", nw)
     sh = _shape(t, "f32")
     x, w = workloads.make_inputs(sh, seed=20)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
@@ -235,19 +194,18 @@ def test_conv_f32_matrix_waves(t, nw, orc, monkeypatch):
     assert_exact(_run(sh, "f32", xi, wi), orc.conv_direct(xi, wi, sh.s), sh.describe())
 
 
-@pytest.mark.parametrize("env", [{"IM2WIN_F16_WPX": "8"}, {"IM2WIN_F16_WPX": "1"},
-                                 {"IM2WIN_F16_NWH": "3"}], ids=str)
+@pytest.mark.parametrize("env", [{"f16_wpx": 8}, {"f16_wpx": 1}, {"f16_nwh": 3}], ids=str)
 @pytest.mark.parametrize("t", [(1, 64, 30, 30, 64, 7, 7, 2), (2, 24, 14, 14, 96, 5, 5, 1),
                                (2, 3, 47, 45, 37, 7, 7, 2), (2, 12, 26, 40, 70, 3, 7, 2),
                                (1, 16, 22, 19, 40, 5, 2, 1)], ids=str)
-def test_conv_f16_fused_tilings(t, env, orc, monkeypatch):
+def test_conv_f16_fused_tilings(t, env, orc, knob):
     """The fused fp16 kernel with forced waves along pixels and filter stages
     per channel group, with and without the prepacked filter (the thin-layer
     and wide-tile kernels switched off, so the prepacked calls reach it)."""
     for k, v in env.items():
-        monkeypatch.setenv(k, v)
-    monkeypatch.setenv("IM2WIN_F16_THIN", "0")
-    monkeypatch.setenv("IM2WIN_F16_WIDE", "0")
+        knob(k, v)
+    knob("f16_thin", -1)
+    knob("f16_wide", -1)
     sh = _shape(t, "f16")
     x, w = workloads.make_inputs(sh, seed=22)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
@@ -279,25 +237,35 @@ ROWS = [
 
 
 def _filter_bytes(sh):
-    return m.conv_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 2, False)
+    return m.fused_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s)
 
 
-@pytest.mark.parametrize("nwv", ["8", "4"])
+def _layout_bytes(sh):
+    """The two prepacked fp16 filter layouts, worked out independently of the
+    library: (channel, filter row) slices of 8 taps for 64-channel tiles, and
+    channel-interleaved 16-byte entries (8 input channels of a tap, taps
+    rounded up to even) for 128-channel tiles."""
+    slices = sh.Ci * sh.Hf * ((sh.Co + 63) // 64 * 64) * 16
+    inter = -(-sh.Ci // 8) * ((sh.Hf * sh.Wf + 1) & ~1) * ((sh.Co + 127) // 128 * 128) * 16
+    return slices, inter
+
+
+@pytest.mark.parametrize("nwv", [8, 4])
 @pytest.mark.parametrize("t", ROWS, ids=str)
-def test_conv_f16_row_staged(t, nwv, orc, monkeypatch):
+def test_conv_f16_row_staged(t, nwv, orc, knob):
     """The fp16 kernel that copies input rows to LDS with direct loads (used
-    with a prepacked filter): uniform and integer inputs, 8 and 4 waves."""
-    monkeypatch.setenv("IM2WIN_F16_ROWS_NWV", nwv)
+    with a prepacked filter): uniform and integer inputs, 8 and 4 waves. The
+    filter workspace holds either layout, whatever the knobs."""
+    knob("f16_rows_nwv", nwv)
     sh = _shape(t, "f16")
     on = _filter_bytes(sh)
-    # Off, thin layers would take the thin-layer kernel, which packs the
-    # filter the same way; with both off the layout differs.
-    monkeypatch.setenv("IM2WIN_F16_ROWS", "0")
-    monkeypatch.setenv("IM2WIN_F16_THIN", "0")
+    knob("f16_rows", -1)
+    knob("f16_thin", -1)
     off = _filter_bytes(sh)
-    monkeypatch.setenv("IM2WIN_F16_ROWS", "1")
-    monkeypatch.delenv("IM2WIN_F16_THIN")
-    assert on == sh.Ci * sh.Hf * ((sh.Co + 63) // 64 * 64) * 16 and on != off, (on, off)
+    knob("f16_rows", 0)
+    knob("f16_thin", 0)
+    need = max(_layout_bytes(sh))
+    assert on == off == -(-need // 256) * 256, (on, off, need)
     x, w = workloads.make_inputs(sh, seed=40)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
     xi, wi = workloads.make_inputs(sh, seed=41, mode="int")
@@ -309,14 +277,14 @@ def test_conv_f16_row_staged(t, nwv, orc, monkeypatch):
         assert_exact(_run(sh, "f16", xi, wi, kind), refi, sh.describe())
 
 
-@pytest.mark.parametrize("bufs", ["2", "3"])
+@pytest.mark.parametrize("bufs", [2, 3])
 @pytest.mark.parametrize("t", ROWS, ids=str)
-def test_conv_f16_row_staged_buffers(t, bufs, orc, monkeypatch):
+def test_conv_f16_row_staged_buffers(t, bufs, orc, knob):
     """Two stage buffers (loads one stage ahead; without a workspace the
     kernel picks them when a stage can then hold twice the channels) and
     three (two stages ahead), with the filter prepacked and gathered: exact
     on integer inputs."""
-    monkeypatch.setenv("IM2WIN_F16_ROWS_BUFS", bufs)
+    knob("f16_rows_bufs", bufs)
     sh = _shape(t, "f16")
     xi, wi = workloads.make_inputs(sh, seed=44, mode="int")
     refi = orc.conv_direct(xi, wi, sh.s)
@@ -351,20 +319,20 @@ def test_conv_f16_row_staged_special_values(t, orc):
         assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
 
 
-@pytest.mark.parametrize("swz", ["1", "0"])
+@pytest.mark.parametrize("order", [0, 1])
 @pytest.mark.parametrize("t", [(11, 2, 65, 64, 40, 3, 3, 2), (40, 4, 21, 32, 70, 5, 5, 2)], ids=str)
-def test_conv_f16_row_staged_tile_order(t, swz, orc, monkeypatch):
+def test_conv_f16_row_staged_tile_order(t, order, orc, knob):
     """XCD-grouped and launch-order tiling give the same (exact) results,
     with grids that are not a multiple of the 8 XCDs (partial last round)."""
-    monkeypatch.setenv("IM2WIN_F16_ROWS_SWIZZLE", swz)
+    knob("tile_order", order)
     sh = _shape(t, "f16")
     xi, wi = workloads.make_inputs(sh, seed=43, mode="int")
-    note(f"conv fp16 row-staged swizzle={swz} {sh.describe()}")
+    note(f"conv fp16 row-staged tile order={order} {sh.describe()}")
     assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
 
 
 # Shapes the wide-tile fp16 kernel takes with a prepacked filter (Co >= 128,
-# or any Co with IM2WIN_F16_WIDE=2; not taken by the row-staged kernel):
+# or any Co with knob f16_wide=1; not taken by the row-staged kernel):
 # tiles crossing images, Ci and Co off the multiples of 8 and 128, odd Wi
 # (single-column staging), column strides 2 and 3, unequal strides, tiles
 # aligned to images, a 1x1 filter, odd and even tap counts.
@@ -403,20 +371,20 @@ def _wide_plan(sh):
     return units <= cap and lds <= 160 * 1024, lds, units
 
 
-@pytest.mark.parametrize("nw", ["8", "4"])
+@pytest.mark.parametrize("nw", [8, 4])
 @pytest.mark.parametrize("t", WIDE, ids=str)
-def test_conv_f16_wide_tiles(t, nw, orc, monkeypatch):
+def test_conv_f16_wide_tiles(t, nw, orc, knob):
     """The fp16 kernel with 128-channel wave tiles (8 waves of 4 x 2 blocks or
     4 waves of 4 x 4), the filter copied to LDS by direct loads from the
     prepacked copy or gathered from w (no workspace): uniform and integer
-    inputs; switching it off (IM2WIN_F16_WIDE=0) gives the
+    inputs; switching it off (knob f16_wide=-1) gives the
     channel-interleaved kernel's results."""
-    monkeypatch.setenv("IM2WIN_F16_WIDE_NW", nw)
+    knob("f16_wide_nw", nw)
     sh = _shape(t, "f16")
     ok, lds, units = _wide_plan(sh)
     assert ok, (lds, units)
     if sh.Co < 128:
-        monkeypatch.setenv("IM2WIN_F16_WIDE", "2")
+        knob("f16_wide", 1)
     x, w = workloads.make_inputs(sh, seed=50)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
     xi, wi = workloads.make_inputs(sh, seed=51, mode="int")
@@ -427,7 +395,7 @@ def test_conv_f16_wide_tiles(t, nw, orc, monkeypatch):
         assert_within(_run(sh, "f16", x, w, kind), ref, absd, TOL["f16"], sh.describe())
         yi[kind] = _run(sh, "f16", xi, wi, kind)
         assert_exact(yi[kind], refi, sh.describe())
-    monkeypatch.setenv("IM2WIN_F16_WIDE", "0")
+    knob("f16_wide", -1)
     for kind in ("filter", None):
         assert_exact(_run(sh, "f16", xi, wi, kind), yi[kind], "channel-interleaved kernel")
 
@@ -511,20 +479,20 @@ def _thin_plan(sh, P=512):
     return lds <= 160 * 1024, lds
 
 
-@pytest.mark.parametrize("nb", ["4", "2"])
+@pytest.mark.parametrize("nb", [4, 2])
 @pytest.mark.parametrize("t", THIN, ids=str)
-def test_conv_f16_thin_layers(t, nb, orc, monkeypatch):
+def test_conv_f16_thin_layers(t, nb, orc, knob):
     """The fp16 kernel that keeps a thin layer's whole filter in LDS as
     (channel, filter row) slices, with 4 and 2 pixel blocks per wave, the
     filter prepacked or gathered in the kernel (no workspace): uniform and
     integer inputs, and the same exact results as the kernels it replaces
-    (IM2WIN_F16_THIN=0)."""
-    monkeypatch.setenv("IM2WIN_F16_THIN_NB", nb)
+    (knob f16_thin=-1)."""
+    knob("f16_thin_nb", nb)
     sh = _shape(t, "f16")
     ok, lds = _thin_plan(sh, 32 * 4 * int(nb))
     assert ok, lds
     on = _filter_bytes(sh)
-    assert on == sh.Ci * sh.Hf * ((sh.Co + 63) // 64 * 64) * 16, on
+    assert on == -(-max(_layout_bytes(sh)) // 256) * 256, on
     x, w = workloads.make_inputs(sh, seed=60)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
     xi, wi = workloads.make_inputs(sh, seed=61, mode="int")
@@ -535,8 +503,8 @@ def test_conv_f16_thin_layers(t, nb, orc, monkeypatch):
         assert_within(_run(sh, "f16", x, w, kind), ref, absd, TOL["f16"], sh.describe())
         yi[kind] = _run(sh, "f16", xi, wi, kind)
         assert_exact(yi[kind], refi, sh.describe())
-    monkeypatch.setenv("IM2WIN_F16_THIN", "0")
-    assert _filter_bytes(sh) != on
+    knob("f16_thin", -1)
+    assert _filter_bytes(sh) == on
     for kind in ("filter", None):
         assert_exact(_run(sh, "f16", xi, wi, kind), yi[kind], "kernels without the thin path")
 
@@ -589,7 +557,7 @@ def test_conv_f16_input_at_odd_element_offset(t, orc):
     wt = to_dev(wi, dev)
     for kind in (None, "filter", "full"):
         note(f"conv fp16 input at odd offset {sh.describe()} ws={kind}")
-        y = m.conv2d(xv, wt, sh.s, ws=_ws(sh, kind, dev)).cpu().numpy()
+        y = call(sh, xv, wt, kind, dev).cpu().numpy()
         assert_exact(y, ref, f"{sh.describe()} ws={kind}")
     torch.cuda.synchronize()
 
@@ -615,7 +583,7 @@ def test_conv_f16_filter_at_odd_element_offset(t, orc):
     xt = to_dev(xi, dev)
     for kind in (None, "filter"):
         note(f"conv fp16 filter at odd offset {sh.describe()} ws={kind}")
-        y = m.conv2d(xt, wv, sh.s, ws=_ws(sh, kind, dev)).cpu().numpy()
+        y = call(sh, xt, wv, kind, dev).cpu().numpy()
         assert_exact(y, ref, f"{sh.describe()} ws={kind}")
     torch.cuda.synchronize()
 
@@ -691,7 +659,7 @@ def _random_f32_shapes(count=24, seed=2025):
 
 
 @pytest.mark.parametrize("t", _random_f32_shapes(), ids=str)
-def test_conv_f32_random_shapes(t, orc, monkeypatch):
+def test_conv_f32_random_shapes(t, orc, knob):
     """Seeded random fp32 shapes, bit-exact on integer inputs through the
     matrix-core kernel, the vector-ALU kernel and the materialised mode."""
     sh = _shape(t, "f32")
@@ -700,6 +668,6 @@ def test_conv_f32_random_shapes(t, orc, monkeypatch):
     for kind in (None, "full"):
         note(f"conv fp32 random {sh.describe()} ws={kind}")
         assert_exact(_run(sh, "f32", xi, wi, kind), refi, f"{sh.describe()} ws={kind}")
-    monkeypatch.setenv("IM2WIN_F32_PATH", "valu")
+    knob("f32_valu", 1)
     note(f"conv fp32 random {sh.describe()} vector ALU")
     assert_exact(_run(sh, "f32", xi, wi, None), refi, f"{sh.describe()} vector ALU")

@@ -16,7 +16,7 @@ import pytest
 
 import memory_efficient_im2win_amd as m
 import workloads
-from parity import TOL, assert_exact, assert_within, device, note, to_dev
+from parity import WS_KINDS, TOL, assert_exact, assert_within, call, device, note, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -38,32 +38,14 @@ STRIDED = [
     (2, 8, 12, 40, 64, 1, 1, (2, 3)),
 ]
 
-WS_KINDS = [None, "filter", "full", "one"]
-
-
 def _shape(t, dt):
     return workloads.ConvShape("strided", *t, dt)
-
-
-def _ws(sh, kind, dev):
-    import torch
-    if kind is None:
-        return None
-    args = (sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
-    F = m.conv_workspace_bytes(*args, False)
-    if kind == "filter":
-        nb = F
-    elif kind == "full":
-        nb = m.conv_workspace_bytes(*args, True)
-    else:
-        nb = F + m.workspace_bytes(1, sh.Ci, sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
-    return torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
 
 
 def _run(sh, x, w, kind=None):
     import torch
     dev = device()
-    y = m.conv2d(to_dev(x, dev), to_dev(w, dev), sh.s, ws=_ws(sh, kind, dev)).cpu().numpy()
+    y = call(sh, to_dev(x, dev), to_dev(w, dev), kind, dev).cpu().numpy()
     torch.cuda.synchronize()
     return y
 
@@ -84,8 +66,8 @@ def test_conv_strided(t, dt, orc):
 
 
 @pytest.mark.parametrize("t", STRIDED, ids=str)
-def test_conv_strided_f32_vector_alu(t, orc, monkeypatch):
-    monkeypatch.setenv("IM2WIN_F32_PATH", "valu")
+def test_conv_strided_f32_vector_alu(t, orc, knob):
+    knob("f32_valu", 1)
     sh = _shape(t, "f32")
     x, w = workloads.make_inputs(sh, seed=33)
     ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
@@ -97,22 +79,23 @@ def test_conv_strided_f32_vector_alu(t, orc, monkeypatch):
 
 @pytest.mark.parametrize("nw", [4, 8, 12])
 @pytest.mark.parametrize("t", [STRIDED[1], STRIDED[3], STRIDED[6], STRIDED[9]], ids=str)
-def test_conv_strided_f32_matrix_waves(t, nw, orc, monkeypatch):
-    monkeypatch.setenv("IM2WIN_F32_NW", str(nw))
+def test_conv_strided_f32_matrix_waves(t, nw, orc, knob):
+    knob("f32_ksplit", 1)
+    knob("f32_nw", nw)
     sh = _shape(t, "f32")
     xi, wi = workloads.make_inputs(sh, seed=35, mode="int")
     note(f"conv strided fp32 NW={nw} {sh.describe()}")
     assert_exact(_run(sh, xi, wi), orc.conv_direct(xi, wi, sh.s), sh.describe())
 
 
-@pytest.mark.parametrize("env", [{"IM2WIN_F16_WPX": "1"}, {"IM2WIN_F16_NWH": "3"}], ids=str)
+@pytest.mark.parametrize("env", [{"f16_wpx": 1}, {"f16_nwh": 3}], ids=str)
 @pytest.mark.parametrize("t", [STRIDED[0], STRIDED[3], STRIDED[8], STRIDED[9]], ids=str)
-def test_conv_strided_f16_fused_tilings(t, env, orc, monkeypatch):
+def test_conv_strided_f16_fused_tilings(t, env, orc, knob):
     for k, v in env.items():
-        monkeypatch.setenv(k, v)
+        knob(k, v)
     # The prepacked calls reach the channel-interleaved kernel.
-    monkeypatch.setenv("IM2WIN_F16_THIN", "0")
-    monkeypatch.setenv("IM2WIN_F16_WIDE", "0")
+    knob("f16_thin", -1)
+    knob("f16_wide", -1)
     sh = _shape(t, "f16")
     xi, wi = workloads.make_inputs(sh, seed=36, mode="int")
     refi = orc.conv_direct(xi, wi, sh.s)
