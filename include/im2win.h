@@ -164,6 +164,23 @@ int conv2d_im2win_fp16_fused(const uint16_t *x, const uint16_t *w, float *y, voi
                              int Wf, int sh, int sw, void *stream);
 
 /*
+ * conv2d_im2win_fp16_fused for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the prepacked filter goes to a fixed 4 MiB array in each
+ * device's global memory that the library holds until the process ends,
+ * instead of a caller workspace. The call itself allocates nothing. Same
+ * results as conv2d_im2win_fp16_fused (same kernels). A shape whose
+ * conv2d_im2win_fp16_fused_workspace_bytes exceeds 4 MiB (4194304) returns
+ * IM2WIN_EWORKSPACE before anything is enqueued; an invalid shape or pointer
+ * IM2WIN_EINVAL. Every call on one device uses that device's array: calls
+ * that overlap on one device (other streams or threads) race and must be
+ * serialised by the caller.
+ */
+int conv2d_im2win_fp16_fused_noalloc(const uint16_t *x, const uint16_t *w, float *y, int N,
+                                     int Ci, int Hi, int Wi, int Co, int Hf, int Wf, int sh, int sw,
+                                     void *stream);
+
+/*
  * Baselines the pages compare im2win against, built here on the same
  * hardware paths (they carry the row and column strides directly):
  *

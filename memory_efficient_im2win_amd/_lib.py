@@ -33,6 +33,7 @@ EXPORTS = {
     "conv2d_im2win_fp16_strided": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
     "conv2d_im2win_fp16_fused_workspace_bytes": ([_i] * 9, _sz),
     "conv2d_im2win_fp16_fused": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
+    "conv2d_im2win_fp16_fused_noalloc": ([_p, _p, _p] + [_i] * 9 + [_p], _i),
     "im2win_set_knob": ([_i, _i], _i),
     "im2win_get_knob": ([_i], _i),
     "im2win_knob_name": ([_i], ctypes.c_char_p),

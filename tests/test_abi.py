@@ -25,6 +25,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         single + [f + "_strided" for f in single] + ["im2win_status_string", "im2win_last_error"] +
         ["conv2d_im2win_fp16_fused_workspace_bytes", "conv2d_im2win_fp16_fused",
+         "conv2d_im2win_fp16_fused_noalloc",
          "im2win_set_knob", "im2win_get_knob", "im2win_knob_name", "im2win_conv_kernel_name"] +
         ["conv2d_im2col_workspace_bytes", "im2col_pack", "conv2d_im2col_fp32", "conv2d_im2col_fp16",
          "conv2d_direct_fp32", "conv2d_direct_fp16", "conv2d_im2win_nhwc_workspace_bytes",
@@ -354,3 +355,17 @@ def test_conv_kernel_name():
     assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2, "materialized") == "conv_f16_kernel"
     with pytest.raises(ValueError):
         m.conv_kernel_name(1, 3, 4, 4, 2, 5, 5, 1, 2)
+
+
+def test_noalloc_rejects_before_launch():
+    """The entry point without allocation refuses bad arguments and shapes
+    whose filter scratch exceeds its 4 MiB before touching the GPU."""
+    L = m.load_library()
+    f = L.conv2d_im2win_fp16_fused_noalloc
+    ok = (1, 3, 8, 8, 4, 3, 3, 1, 1)
+    assert f(None, FAKE, FAKE, *ok, None) == _lib.IM2WIN_EINVAL
+    assert f(FAKE, FAKE, FAKE, 1, 3, 8, 8, 4, 9, 3, 1, 1, None) == _lib.IM2WIN_EINVAL
+    assert f(ctypes.c_void_p(0x10001), FAKE, FAKE, *ok, None) == _lib.IM2WIN_EINVAL
+    big = (1, 512, 16, 16, 512, 7, 7, 1, 1)   # filter scratch > 4 MiB
+    assert L.conv2d_im2win_fp16_fused_workspace_bytes(*big) > 4 << 20
+    assert f(FAKE, FAKE, FAKE, *big, None) == _lib.IM2WIN_EWORKSPACE
