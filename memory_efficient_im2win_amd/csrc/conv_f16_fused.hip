@@ -645,10 +645,11 @@ int launch_w(const uint16_t* x, const uint16_t* w, const uint4* wpk, float* y,
 // wide-tile kernel, then the channel-interleaved kernel above; 0 if none
 // takes the shape. The filter, prepacked or gathered, follows the kernel's
 // layout.
-enum F16Route { kRouteNone = 0, kRouteRows, kRouteThin, kRouteWide, kRouteFused };
+enum F16Route { kRouteNone = 0, kRouteReuse, kRouteRows, kRouteThin, kRouteWide, kRouteFused };
 
 F16Route f16_route(const ConvShape& c, const void* x)
 {
+    if (f16_reuse_applies(c) && (uintptr_t)x % 16 == 0) return kRouteReuse;
     if (f16_rows_applies(c) && (uintptr_t)x % 16 == 0) return kRouteRows;
     if (f16_thin_applies(c)) return kRouteThin;
     if (f16_wide_applies(c, kCoPad)) return kRouteWide;
@@ -671,6 +672,7 @@ size_t f16_filter_pack_bytes(const ConvShape& c)
 const char* f16_fused_kernel_name(const ConvShape& c, const void* x)
 {
     switch (f16_route(c, x)) {
+    case kRouteReuse: return "conv_f16_reuse_kernel";
     case kRouteRows: return "conv_f16_rows_kernel";
     case kRouteThin: return "conv_f16_thin_kernel";
     case kRouteWide: return "conv_f16_wide_kernel";
@@ -684,7 +686,7 @@ int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, con
 {
     const F16Route r = f16_route(c, x);
     if (r == kRouteNone) return -1;
-    if (r == kRouteRows) return launch_f16_rows_filter_pack(w, wpk, c, stream);
+    if (r == kRouteRows || r == kRouteReuse) return launch_f16_rows_filter_pack(w, wpk, c, stream);
     if (r == kRouteThin) return launch_f16_slices_filter_pack(w, wpk, c, stream);
     FusedArgs a;
     int wco, wpx, nb;
@@ -710,6 +712,7 @@ int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk,
 {
     const F16Route r = f16_route(c, x);
     if (r == kRouteNone) return -1;
+    if (r == kRouteReuse) return launch_conv_f16_reuse(x, wpk, w, y, c, stream);
     if (r == kRouteRows) return launch_conv_f16_rows(x, wpk, w, y, c, stream);
     if (r == kRouteThin) return launch_conv_f16_thin(x, wpk, w, y, c, stream);
     if (r == kRouteWide) return launch_conv_f16_wide(x, wpk, w, y, c, kCoPad, stream);

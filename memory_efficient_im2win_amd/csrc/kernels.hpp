@@ -77,6 +77,14 @@ size_t f16_slices_filter_bytes(const ConvShape& c);
 int launch_f16_slices_filter_pack(const uint16_t* w, void* wp, const ConvShape& c,
                                   hipStream_t stream);
 
+// fp16 convolution of the row-staged kernel's shapes (its filter layout)
+// with each staged input row reused across the output rows that share it
+// and the filter held in registers (f16_reuse_applies). -1 if the shape or
+// x's alignment is outside its envelope.
+bool f16_reuse_applies(const ConvShape& c);
+int launch_conv_f16_reuse(const uint16_t* x, const void* wp, const uint16_t* w, float* y,
+                          const ConvShape& c, hipStream_t stream);
+
 // fp16 convolution for thin layers (few input channels: the whole filter
 // stays in LDS as slices (c, kh) of 8 taps), reading the filter packed by
 // launch_f16_slices_filter_pack (wp), or gathering it from w when wp is

@@ -255,7 +255,9 @@ def _layout_bytes(sh):
 def test_conv_f16_row_staged(t, nwv, orc, knob):
     """The fp16 kernel that copies input rows to LDS with direct loads (used
     with a prepacked filter): uniform and integer inputs, 8 and 4 waves. The
-    filter workspace holds either layout, whatever the knobs."""
+    filter workspace holds either layout, whatever the knobs. (The row-reuse
+    kernel, which takes most of these shapes by default, is switched off.)"""
+    knob("f16_reuse", -1)
     knob("f16_rows_nwv", nwv)
     sh = _shape(t, "f16")
     on = _filter_bytes(sh)
@@ -284,6 +286,7 @@ def test_conv_f16_row_staged_buffers(t, bufs, orc, knob):
     kernel picks them when a stage can then hold twice the channels) and
     three (two stages ahead), with the filter prepacked and gathered: exact
     on integer inputs."""
+    knob("f16_reuse", -1)
     knob("f16_rows_bufs", bufs)
     sh = _shape(t, "f16")
     xi, wi = workloads.make_inputs(sh, seed=44, mode="int")
@@ -294,10 +297,11 @@ def test_conv_f16_row_staged_buffers(t, bufs, orc, knob):
 
 
 @pytest.mark.parametrize("t", [(2, 4, 14, 16, 40, 3, 5, 2), (2, 4, 15, 24, 40, 3, 7, 2)], ids=str)
-def test_conv_f16_row_staged_special_values(t, orc):
+def test_conv_f16_row_staged_special_values(t, orc, knob):
     """Infinities and NaN in the input reach exactly the outputs whose windows
     hold them: the padded taps kw >= Wf never multiply a neighbour's Inf
     (Wf = 5 masks three dwords of each slice, Wf = 7 only the last)."""
+    knob("f16_reuse", -1)
     sh = _shape(t, "f16")
     x, w = workloads.make_inputs(sh, seed=42)
     x[0, 1, 4, 5] = np.inf
@@ -327,8 +331,93 @@ def test_conv_f16_row_staged_tile_order(t, order, orc, knob):
     knob("tile_order", order)
     sh = _shape(t, "f16")
     xi, wi = workloads.make_inputs(sh, seed=43, mode="int")
+    for reuse in (-1, 0):
+        knob("f16_reuse", reuse)
+        note(f"conv fp16 row-staged tile order={order} reuse={reuse} {sh.describe()}")
+        assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
     note(f"conv fp16 row-staged tile order={order} {sh.describe()}")
     assert_exact(_run(sh, "f16", xi, wi, "filter"), orc.conv_direct(xi, wi, sh.s), sh.describe())
+
+
+# Shapes the row-reuse fp16 kernel takes (even column stride, Wf <= 8, Wi a
+# multiple of 8, even Ci, a built (filter height, row stride) pair): every
+# built pair; output heights not a multiple of the 4-row groups (partial last
+# group); tiles crossing images (including several images per tile); one row
+# group per image; Wf = 8 (no padded taps) and Wf = 1; column strides 2 and
+# 4; channel counts that give stages of 4 and of 2 channels; Co off 64.
+REUSE = [
+    (2, 64, 40, 40, 64, 7, 7, 2),       # cv4-like
+    (3, 6, 23, 24, 33, 3, 5, (1, 2)),
+    (2, 16, 30, 32, 70, 7, 7, 2),
+    (5, 4, 12, 16, 64, 3, 3, 2),
+    (2, 8, 20, 64, 128, 5, 3, 2),
+    (11, 2, 65, 64, 40, 3, 3, 2),
+    (40, 4, 21, 32, 70, 5, 5, 2),       # several images per tile
+    (7, 2, 7, 8, 5, 7, 3, (1, 2)),      # one output row per image
+    (3, 2, 10, 8, 8, 3, 3, (1, 4)),
+    (2, 6, 19, 24, 65, 5, 8, (1, 2)),   # Wf = 8
+    (3, 10, 26, 16, 40, 7, 1, (1, 2)),  # Wf = 1, Hf 7 at row stride 1
+    (1, 12, 33, 48, 130, 5, 5, 2),      # three channel tiles
+]
+
+
+@pytest.mark.parametrize("t", REUSE, ids=str)
+def test_conv_f16_row_reuse(t, orc, knob):
+    """The fp16 kernel that reuses each staged input row across the output
+    rows sharing it, with the filter prepacked and gathered in the kernel
+    (dword and, with w at an odd element offset, per-entry gathers): within
+    tolerance on uniform inputs, exact on integer inputs, and the same bits
+    as the row-staged kernel it replaces (knob f16_reuse=-1)."""
+    import torch
+    sh = _shape(t, "f16")
+    assert m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 2) == \
+        "conv_f16_reuse_kernel"
+    x, w = workloads.make_inputs(sh, seed=45)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    xi, wi = workloads.make_inputs(sh, seed=46, mode="int")
+    refi = orc.conv_direct(xi, wi, sh.s)
+    got = {}
+    for kind in ("filter", None):
+        note(f"conv fp16 row reuse {sh.describe()} ws={kind}")
+        assert_within(_run(sh, "f16", x, w, kind), ref, absd, TOL["f16"], sh.describe())
+        got[kind] = _run(sh, "f16", xi, wi, kind)
+        assert_exact(got[kind], refi, f"{sh.describe()} ws={kind}")
+    dev = device()
+    big = torch.zeros(wi.size + 1, dtype=torch.float16, device=dev)
+    big[1:] = torch.from_numpy(np.ascontiguousarray(wi).reshape(-1)).to(dev)
+    note(f"conv fp16 row reuse {sh.describe()} filter at an odd offset")
+    y = m.conv2d(to_dev(xi, dev), big[1:].view(wi.shape), sh.s).cpu().numpy()
+    assert_exact(y, refi, f"{sh.describe()} odd filter offset")
+    knob("f16_reuse", -1)
+    for kind in ("filter", None):
+        assert_exact(_run(sh, "f16", xi, wi, kind), got[kind], "row-staged kernel")
+
+
+@pytest.mark.parametrize("t", [(2, 4, 14, 16, 40, 3, 5, 2), (2, 4, 19, 24, 40, 7, 7, 2),
+                               (2, 2, 12, 16, 40, 5, 6, (1, 2))], ids=str)
+def test_conv_f16_row_reuse_special_values(t, orc):
+    """Infinities and NaN reach exactly the outputs whose windows hold them
+    (padded taps are cleared in B, the rows of a partial row group past the
+    image are zeros)."""
+    sh = _shape(t, "f16")
+    x, w = workloads.make_inputs(sh, seed=47)
+    x[0, 1, 4, 5] = np.inf
+    x[0, 2 % sh.Ci, 7, 13] = -np.inf
+    x[1, 3 % sh.Ci, 0, 6] = np.nan
+    x[1, 0, sh.Hi - 1, sh.Wi - 1] = np.inf
+    x[0, 0, 2, 7] = np.inf
+    w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
+    ref = orc.conv_direct(x, w, sh.s)
+    fin = np.isfinite(ref)
+    _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
+                              with_absdot=True)
+    for kind in ("filter", None):
+        note(f"conv fp16 row reuse special values {sh.describe()} ws={kind}")
+        y = _run(sh, "f16", x, w, kind).astype(np.float64)
+        assert np.array_equal(np.isnan(y), np.isnan(ref))
+        assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+        assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+        assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
 
 
 # Shapes the wide-tile fp16 kernel takes with a prepacked filter (Co >= 128,
