@@ -346,7 +346,9 @@ def test_conv_kernel_name():
     """The fp16 kernel a call runs, as the planners pick it (no GPU needed;
     the fp32 planner asks the device for occupancy, so its names are checked
     on the GPU)."""
-    assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2) == "conv_f16_rows_kernel"
+    assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2) == "conv_f16_reuse_kernel"
+    with m.knobs(f16_reuse=-1):
+        assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2) == "conv_f16_rows_kernel"
     assert m.conv_kernel_name(64, 3, 227, 227, 64, 7, 7, 2, 2) == "conv_f16_thin_kernel"
     assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2) == "conv_f16_wide_kernel"
     with m.knobs(f16_rows=-1, f16_thin=-1, f16_wide=-1):
