@@ -122,6 +122,8 @@ int f32_generic(const float* x, const float* ws, const float* w, float* y, const
 int f16_from_ws(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float* y,
                 const ConvShape& c, hipStream_t st)
 {
+    const int rc = im2win::launch_conv_f16_ws(ws, w, y, c, st);
+    if (rc != -1) return rc;
     return im2win::launch_conv_f16(x, ws, w, y, c, st);
 }
 int f16_generic(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float* y,
@@ -300,7 +302,7 @@ void ensure_lds_limit(const void* f, int bytes)
 const char* const kKnobNames[KNOB_COUNT] = {
     "f32_valu", "f32_nw", "f32_wco", "f32_cb", "f32_ksplit", "f32_occ",
     "f16_rows", "f16_rows_nwv", "f16_rows_bufs", "f16_thin", "f16_thin_nb", "f16_wide",
-    "f16_wide_nw", "f16_wpx", "f16_nwh", "tile_order", "f16_reuse"};
+    "f16_wide_nw", "f16_wpx", "f16_nwh", "tile_order", "f16_reuse", "f16_ws"};
 
 std::atomic<int> g_knobs[KNOB_COUNT];
 }  // namespace im2win
@@ -502,7 +504,7 @@ const char* im2win_conv_kernel_name(int elem_bytes, int mode, int N, int Ci, int
         const bool mfma = im2win::knob(im2win::KNOB_F32_VALU) != 1 && im2win::f32_mfma_applies(c);
         return mfma ? "conv_f32_mfma_kernel" : "conv_f32_kernel";
     }
-    if (mode == 2) return "conv_f16_kernel";
+    if (mode == 2) return im2win::f16_ws_applies(c) ? "conv_f16_ws_kernel" : "conv_f16_kernel";
     return im2win::f16_fused_kernel_name(c, reinterpret_cast<const void*>(uintptr_t(256)));
 }
 

@@ -36,6 +36,13 @@ int launch_conv_f32_mfma(const float* x, const float* w, float* y, const ConvSha
                          hipStream_t stream);
 bool f32_mfma_applies(const ConvShape& c);
 
+// fp16 convolution from the materialised tensor ws (N images) with each
+// channel's window stretch copied into LDS by direct loads (f16_ws_applies);
+// -1 if the shape or ws's alignment is outside its envelope.
+bool f16_ws_applies(const ConvShape& c);
+int launch_conv_f16_ws(const uint16_t* ws, const uint16_t* w, float* y, const ConvShape& c,
+                       hipStream_t stream);
+
 // fp16 x fp16 -> fp32 convolution on the matrix cores; ws as above.
 int launch_conv_f16(const uint16_t* x, const uint16_t* ws, const uint16_t* w, float* y,
                     const ConvShape& c, hipStream_t stream);

@@ -28,6 +28,7 @@ enum Knob : int {
     KNOB_F16_NWH,            // >= 1: filter stages per channel group, channel-interleaved kernel
     KNOB_TILE_ORDER,         // 1: tiles in launch order (default: XCD-grouped where a kernel has it)
     KNOB_F16_REUSE,          // -1: row-reuse fp16 kernel off (the row-staged kernel takes its shapes)
+    KNOB_F16_WS,             // -1: staged fp16 kernel over the materialised tensor off
     KNOB_COUNT
 };
 

@@ -354,7 +354,12 @@ def test_conv_kernel_name():
     with m.knobs(f16_rows=-1, f16_thin=-1, f16_wide=-1):
         assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2, "prepacked") == \
             "conv_f16_fused_kernel"
-    assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2, "materialized") == "conv_f16_kernel"
+    assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2, "materialized") == \
+        "conv_f16_ws_kernel"
+    assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2, "materialized") == "conv_f16_kernel"
+    with m.knobs(f16_ws=-1):
+        assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2, "materialized") == \
+            "conv_f16_kernel"
     with pytest.raises(ValueError):
         m.conv_kernel_name(1, 3, 4, 4, 2, 5, 5, 1, 2)
 

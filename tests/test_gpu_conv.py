@@ -420,6 +420,73 @@ def test_conv_f16_row_reuse_special_values(t, orc):
         assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
 
 
+# Shapes the fp16 kernel over the materialised tensor takes (sw*Hf even,
+# packed rows a multiple of 8 elements): several slices per channel (Wf*Hf
+# from 8 to 49, the last slice partly padding), stages of 4 and 2 channels,
+# tiles crossing images, Co off 64 and above it, unequal strides.
+WS = [
+    (2, 16, 30, 32, 70, 7, 7, 2),
+    (2, 64, 40, 40, 64, 7, 7, 2),
+    (3, 6, 23, 24, 33, 3, 5, (1, 2)),
+    (4, 8, 20, 16, 40, 2, 4, 2),
+    (3, 4, 26, 32, 130, 4, 4, (3, 2)),
+    (2, 12, 33, 48, 64, 5, 6, (2, 2)),
+    (2, 8, 15, 24, 20, 1, 8, 2),
+    (1, 10, 40, 64, 96, 3, 6, (2, 4)),
+    (2, 16, 24, 40, 64, 7, 2, (1, 2)),
+]
+
+
+@pytest.mark.parametrize("t", WS, ids=str)
+def test_conv_f16_materialised_staged(t, orc, knob):
+    """The fp16 kernel that copies each channel's window stretch of the
+    materialised im2win tensor into LDS with direct loads, over the whole
+    batch and one image at a time: within tolerance on uniform inputs, exact
+    on integer inputs, and the same bits as the per-entry kernel it replaces
+    (knob f16_ws=-1)."""
+    sh = _shape(t, "f16")
+    assert m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 2,
+                              "materialized") == "conv_f16_ws_kernel"
+    x, w = workloads.make_inputs(sh, seed=48)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    xi, wi = workloads.make_inputs(sh, seed=49, mode="int")
+    refi = orc.conv_direct(xi, wi, sh.s)
+    got = {}
+    for kind in ("full", "one"):
+        note(f"conv fp16 materialised staged {sh.describe()} ws={kind}")
+        assert_within(_run(sh, "f16", x, w, kind), ref, absd, TOL["f16"], sh.describe())
+        got[kind] = _run(sh, "f16", xi, wi, kind)
+        assert_exact(got[kind], refi, f"{sh.describe()} ws={kind}")
+    knob("f16_ws", -1)
+    assert_exact(_run(sh, "f16", xi, wi, "full"), got["full"], "per-entry kernel")
+
+
+@pytest.mark.parametrize("t", [(2, 4, 19, 24, 40, 7, 7, 2), (2, 3, 14, 16, 40, 3, 4, (1, 2))],
+                         ids=str)
+def test_conv_f16_materialised_staged_special_values(t, orc):
+    """Infinities and NaN in the input reach exactly the outputs whose windows
+    hold them: the padding of a channel's last slice (the next window's
+    elements in the packed row) is masked."""
+    sh = _shape(t, "f16")
+    x, w = workloads.make_inputs(sh, seed=57)
+    x[0, 1, 4, 5] = np.inf
+    x[0, 2 % sh.Ci, 7, 13] = -np.inf
+    x[1, 0, 0, 6] = np.nan
+    x[1, 0, sh.Hi - 1, sh.Wi - 1] = np.inf
+    x[0, 0, 2, 7] = np.inf
+    w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
+    ref = orc.conv_direct(x, w, sh.s)
+    fin = np.isfinite(ref)
+    _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
+                              with_absdot=True)
+    note(f"conv fp16 materialised staged special values {sh.describe()}")
+    y = _run(sh, "f16", x, w, "full").astype(np.float64)
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+    assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
+
+
 # Shapes the wide-tile fp16 kernel takes with a prepacked filter (Co >= 128,
 # or any Co with knob f16_wide=1; not taken by the row-staged kernel):
 # tiles crossing images, Ci and Co off the multiples of 8 and 128, odd Wi
