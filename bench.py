@@ -90,6 +90,48 @@ def time_layer(sh, mode, steps, warmup):
 
 def _time_layer(sh, mode, steps, warmup):
     import torch
+    call, info, hold = _layer_call(sh, mode)
+    res = _time_calls(call, steps, warmup)
+    f = info["flops"]
+    res.update({
+        "tflops": f / (res["ms_per_step"]) / 1e9,
+        "tflops_median": f / res["ms_per_launch_median"] / 1e9,
+        **info,
+    })
+    del call, hold
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_variants(sh, mode, variants, steps, rounds=4):
+    """Times knob variants of one mode on layer sh over the same resident
+    inputs, interleaved: `rounds` rounds, each timing steps // rounds calls
+    of every variant in turn, so slow drifts of the clock (the chip's power
+    management) fall on every variant alike. Per variant: the median call."""
+    import torch
+    import memory_efficient_im2win_amd as m
+    with m.knobs(**_knobs_of(mode)):
+        call, info, hold = _layer_call(sh, mode)
+        per = {label: [] for label, _ in variants}
+        for _ in range(rounds):
+            for label, kn in variants:
+                with m.knobs(**kn):
+                    per[label] += _time_calls(call, max(1, steps // rounds), 2, raw=True)["per"]
+    del call, hold
+    torch.cuda.empty_cache()
+    out = {}
+    for label, _ in variants:
+        med = float(np.median(per[label]))
+        out[label] = {"ms_per_launch_median": med, "tflops_median": info["flops"] / med / 1e9,
+                      "calls": len(per[label]), **info}
+    return out
+
+
+def _layer_call(sh, mode):
+    """One mode on layer sh with seeded inputs, output and workspace resident
+    on the GPU: the call, its flops and workspace bytes, and the tensors it
+    holds."""
+    import torch
     import memory_efficient_im2win_amd as m
     dev = torch.device("cuda:0")
     x, w = workloads.make_inputs(sh, seed=0)
@@ -126,21 +168,11 @@ def _time_layer(sh, mode, steps, warmup):
             m.conv2d_fused(xt, wt, sh.s, fws=ws, out=y)
         else:
             m.conv2d(xt, wt, sh.s, ws=ws, out=y)
-    res = _time_calls(call, steps, warmup)
-    f = flops(sh, Ho, Wo)
-    res.update({
-        "tflops": f / (res["ms_per_step"]) / 1e9,
-        "tflops_median": f / res["ms_per_launch_median"] / 1e9,
-        "flops": f,
-        "workspace_bytes": wsb,
-        "Ho": Ho, "Wo": Wo,
-    })
-    del ws, y, xt, wt
-    torch.cuda.empty_cache()
-    return res
+    info = {"flops": flops(sh, Ho, Wo), "workspace_bytes": wsb, "Ho": Ho, "Wo": Wo}
+    return call, info, (xt, wt, y, ws)
 
 
-def _time_calls(call, steps, warmup):
+def _time_calls(call, steps, warmup, raw=False):
     """HIP events around each of `steps` calls and around all of them, on
     torch's current stream (the stream the binding passes to the library)."""
     import torch
@@ -161,12 +193,15 @@ def _time_calls(call, steps, warmup):
     torch.cuda.synchronize()
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     total_ms = t_all0.elapsed_time(t_all1)
-    return {
+    res = {
         "ms_per_step": total_ms / steps,
         "ms_per_launch_avg": float(np.mean(per)),
         "ms_per_launch_median": float(np.median(per)),
         "ms_per_launch_min": float(np.min(per)),
     }
+    if raw:
+        res["per"] = per
+    return res
 
 
 def time_pack(sh, steps, warmup):
@@ -341,53 +376,106 @@ def ingest_pmc(fetch_csv, write_csv, copy_bytes=1 << 30):
     return out
 
 
-# Variants timed by --ablation: (label, mode, knobs) per precision. The knobs
-# are the library's own planner overrides (im2win_set_knob).
+# Variants timed by --ablation: (label, mode, knobs, kernel) per precision.
+# The knobs are the library's own planner overrides (im2win_set_knob); a row
+# is timed only on layers where the knobs route the call to `kernel` (None:
+# whatever the planner picks), so every row names the kernel it measured.
+_ALL_F16_OFF = {"f16_reuse": -1, "f16_rows": -1, "f16_thin": -1, "f16_wide": -1}
 ABLATION = {
-    "f32": [("matrix cores, planner's choice", "fused", {}),
-            ("matrix cores, 4 waves/workgroup", "fused", {"f32_nw": 4, "f32_ksplit": 1}),
-            ("matrix cores, 8 waves/workgroup", "fused", {"f32_nw": 8, "f32_ksplit": 1}),
-            ("matrix cores, 12 waves/workgroup", "fused", {"f32_nw": 12, "f32_ksplit": 1}),
-            ("matrix cores, K shared by 8 waves", "fused", {"f32_ksplit": 8}),
-            ("vector ALU", "fused", {"f32_valu": 1}),
-            ("materialised im2win tensor", "materialized", {})],
-    "f16": [("fused, filter gathered in-kernel (planner's kernel)", "fused", {}),
-            ("fused, filter prepacked per call", "prepacked", {}),
-            ("prepacked, row-staged kernel with 4 waves", "prepacked", {"f16_rows_nwv": 4}),
-            ("prepacked, row-staged, tiles in launch order", "prepacked", {"tile_order": 1}),
-            ("prepacked, thin-layer kernel with 512-pixel tiles", "prepacked", {"f16_thin_nb": 4}),
-            ("prepacked, wide-tile kernel with 4 waves of 4 x 4 blocks", "prepacked",
-             {"f16_wide_nw": 4}),
-            ("prepacked, channel-interleaved kernel", "prepacked",
-             {"f16_rows": -1, "f16_thin": -1, "f16_wide": -1}),
+    "f32": [("matrix cores, planner's choice", "fused", {}, None),
+            ("matrix cores, 4 waves/workgroup", "fused", {"f32_nw": 4, "f32_ksplit": 1}, None),
+            ("matrix cores, 8 waves/workgroup", "fused", {"f32_nw": 8, "f32_ksplit": 1}, None),
+            ("matrix cores, 12 waves/workgroup", "fused", {"f32_nw": 12, "f32_ksplit": 1}, None),
+            ("matrix cores, K shared by 8 waves", "fused", {"f32_ksplit": 8}, None),
+            ("vector ALU", "fused", {"f32_valu": 1}, None),
+            ("materialised im2win tensor", "materialized", {}, None)],
+    "f16": [("fused, filter gathered in-kernel (planner's kernel)", "fused", {}, None),
+            ("fused, filter prepacked per call (planner's kernel)", "prepacked", {}, None),
+            ("row-staged kernel (row reuse off)", "prepacked", {"f16_reuse": -1},
+             "conv_f16_rows_kernel"),
+            ("row-staged kernel, 4 waves", "prepacked", {"f16_reuse": -1, "f16_rows_nwv": 4},
+             "conv_f16_rows_kernel"),
+            ("row-staged kernel, 2 stage buffers", "prepacked",
+             {"f16_reuse": -1, "f16_rows_bufs": 2}, "conv_f16_rows_kernel"),
+            ("thin-layer kernel, 512-pixel tiles", "prepacked", {"f16_thin_nb": 4},
+             "conv_f16_thin_kernel"),
+            ("wide-tile kernel, 4 waves of 4 x 4 blocks", "prepacked", {"f16_wide_nw": 4},
+             "conv_f16_wide_kernel"),
+            ("channel-interleaved kernel", "prepacked", dict(_ALL_F16_OFF),
+             "conv_f16_fused_kernel"),
             ("channel-interleaved, 8 waves along pixels", "prepacked",
-             {"f16_rows": -1, "f16_thin": -1, "f16_wide": -1, "f16_wpx": 8}),
+             dict(_ALL_F16_OFF, f16_wpx=8), "conv_f16_fused_kernel"),
             ("channel-interleaved, >= 2 filter parts per group", "prepacked",
-             {"f16_rows": -1, "f16_thin": -1, "f16_wide": -1, "f16_nwh": 2}),
-            ("materialised im2win tensor", "materialized", {})],
+             dict(_ALL_F16_OFF, f16_nwh=2), "conv_f16_fused_kernel"),
+            ("materialised im2win tensor", "materialized", {}, None),
+            ("materialised, tiled kernel (staged kernel off)", "materialized", {"f16_ws": -1},
+             "conv_f16_kernel")],
 }
 
 
+# The two switches every staged matrix-core kernel has, timed per layer and
+# call mode: tiles in launch order instead of XCD-grouped (tile_order=1), and
+# stages copied through registers and waited for before their MFMAs instead
+# of loaded ahead while the previous stage computes (sync_staging=1).
+SWITCHES = [("default", {}), ("tiles in launch order", {"tile_order": 1}),
+            ("synchronous staging", {"sync_staging": 1}),
+            ("launch order + synchronous staging", {"tile_order": 1, "sync_staging": 1})]
+SWITCH_MODES = {"f32": ["fused"], "f16": ["fused", "prepacked", "materialized"]}
+SWITCH_KERNELS = ("conv_f32_mfma_kernel", "conv_f16_reuse_kernel", "conv_f16_rows_kernel",
+                  "conv_f16_thin_kernel", "conv_f16_wide_kernel", "conv_f16_fused_kernel",
+                  "conv_f16_ws_kernel")
+
+
 def ablation(keys, steps):
-    """Times every layer under the ABLATION variants; prints a Markdown table."""
+    """Times every layer under the two switches (per call mode) and under the
+    ABLATION variants; prints two Markdown tables."""
     import torch
     import memory_efficient_im2win_amd as m
     m.load_library()
-    rows = []
+    sw_rows, rows = [], []
     for key in keys:
         sh = workloads.BY_KEY[key]
-        for label, mode, kn in ABLATION[sh.dtype]:
+        peak = PEAK_FP32_MFMA_TFLOPS if sh.dtype == "f32" else PEAK_FP16_MFMA_TFLOPS
+        for mode in SWITCH_MODES[sh.dtype]:
+            kern = m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
+                                      sh.elem_bytes, mode)
+            variants = SWITCHES if kern in SWITCH_KERNELS else SWITCHES[:1]
+            res = time_variants(sh, mode, variants, steps)
+            base = res[variants[0][0]]["ms_per_launch_median"]
+            for label, _ in variants:
+                r = res[label]
+                us = r["ms_per_launch_median"] * 1e3
+                sw_rows.append((key, mode, kern, label, r["tflops_median"], us,
+                                r["ms_per_launch_median"] / base, r["tflops_median"] / peak))
+                log(f"[ablation] {key} {mode} {kern} {label}: {us:.1f} us")
+        todo = []
+        for label, mode, kn, target in ABLATION[sh.dtype]:
             with m.knobs(**kn):
-                r = time_layer(sh, mode, steps, 3)
-            peak = PEAK_FP32_MFMA_TFLOPS if sh.dtype == "f32" else PEAK_FP16_MFMA_TFLOPS
-            rows.append((key, label, r["tflops_median"], r["ms_per_launch_median"] * 1e3,
+                kern = m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
+                                          sh.elem_bytes, mode)
+            if target is None or kern == target:
+                todo.append((label, mode, kn, kern))
+        res = {}
+        for mode in dict.fromkeys(md for _, md, _, _ in todo):
+            res.update(time_variants(sh, mode, [(lb, kn) for lb, md, kn, _ in todo
+                                                if md == mode], steps))
+        for label, _, _, kern in todo:
+            r = res[label]
+            rows.append((key, label, kern, r["tflops_median"], r["ms_per_launch_median"] * 1e3,
                          r["tflops_median"] / peak, r["workspace_bytes"]))
             log(f"[ablation] {key} {label}: {r['tflops_median']:.1f} TFLOP/s")
     torch.cuda.synchronize()
-    print("| layer | variant | TFLOP/s | us per call (median) | fraction of peak | workspace bytes |")
-    print("|---|---|---|---|---|---|")
-    for key, label, tf, us, fr, wsb in rows:
-        print(f"| {key} | {label} | {tf:.1f} | {us:.1f} | {fr:.3f} | {wsb:,} |")
+    print("| layer | mode | kernel | variant | TFLOP/s | us per call (median) "
+          "| time / default | fraction of peak |")
+    print("|---|---|---|---|---|---|---|---|")
+    for key, mode, kern, label, tf, us, rel, fr in sw_rows:
+        print(f"| {key} | {mode} | {kern} | {label} | {tf:.1f} | {us:.1f} | {rel:.3f} | {fr:.3f} |")
+    print()
+    print("| layer | variant | kernel | TFLOP/s | us per call (median) | fraction of peak "
+          "| workspace bytes |")
+    print("|---|---|---|---|---|---|---|")
+    for key, label, kern, tf, us, fr, wsb in rows:
+        print(f"| {key} | {label} | {kern} | {tf:.1f} | {us:.1f} | {fr:.3f} | {wsb:,} |")
 
 
 def fill_rate(key, sh, steps, warmup):
@@ -526,7 +614,7 @@ def main():
     args = ap.parse_args()
 
     if args.ablation:
-        ablation(LAYER_KEYS, max(5, args.steps // 2))
+        ablation(LAYER_KEYS, max(8, args.steps))
         return
 
     if args.ingest_pmc:

@@ -302,7 +302,7 @@ void ensure_lds_limit(const void* f, int bytes)
 const char* const kKnobNames[KNOB_COUNT] = {
     "f32_valu", "f32_nw", "f32_wco", "f32_cb", "f32_ksplit", "f32_occ",
     "f16_rows", "f16_rows_nwv", "f16_rows_bufs", "f16_thin", "f16_thin_nb", "f16_wide",
-    "f16_wide_nw", "f16_wpx", "f16_nwh", "tile_order", "f16_reuse", "f16_ws"};
+    "f16_wide_nw", "f16_wpx", "f16_nwh", "tile_order", "f16_reuse", "f16_ws", "sync_staging"};
 
 std::atomic<int> g_knobs[KNOB_COUNT];
 }  // namespace im2win

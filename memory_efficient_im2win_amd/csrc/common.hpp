@@ -33,4 +33,16 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 // Wave-uniform value in an SGPR (the argument must already be uniform).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Tile of workgroup b of a grid of `grid`. Workgroups are handed to the 8
+// XCDs in turn (b on XCD b % 8). grouped: XCD x takes the contiguous tiles
+// [x*G8, (x+1)*G8) of the first 8*G8 (G8 = grid / 8), so neighbouring tiles,
+// which share input rows, share that XCD's L2; the last partial round keeps
+// launch order. Otherwise tile = b (launch order).
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t grid, bool grouped)
+{
+    if (!grouped) return b;
+    const int64_t G8 = grid / 8;
+    return b < 8 * G8 ? (b % 8) * G8 + b / 8 : b;
+}
+
 }  // namespace im2win

@@ -58,6 +58,8 @@ struct FusedArgs {
     int KT;                         // entries of the tap offset table
     uint32_t xbytes, ybytes;        // sizes of x and y (each below 4 GiB: buffer addressing)
     FastDiv divWo, divHo, divWi, divHalfW, divS;
+    bool swz;                       // XCD-grouped tile order
+    bool sync;                      // next stage loaded after this one's MFMAs
 };
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi)
@@ -178,8 +180,10 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     const int Ho = a.c.Ho, Wo = a.c.Wo, Hf = a.c.Hf, Wf = a.c.Wf;
     const int HW = a.HW, HWp = a.HWp, RS = a.RS, NU = a.NU;
 
-    const int co_t = (int)(blockIdx.x % a.co_tiles);
-    const int64_t pt = blockIdx.x / a.co_tiles;
+    // XCD-grouped tile order unless the tile_order knob asks for launch order.
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, a.swz);
+    const int co_t = (int)(bid % a.co_tiles);
+    const int64_t pt = bid / a.co_tiles;
     const int co0 = co_t * COT;
     int64_t q0, qend;
     if (a.aligned) {   // tile pt = (image, tile within the image)
@@ -451,7 +455,9 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     for (int st = 0; st < nstages; ++st) {
         const int g = st / a.NWH, h = st % a.NWH;
         const bool xnext = a.NWH >= 2 ? h == 0 && g + 1 < a.CG : st + 1 < nstages;
-        if (st + 1 < nstages) load_stage(st + 1, xnext, g + 1);
+        // sync: the next stage's loads wait until this stage's MFMAs are
+        // issued, so no copy is in flight while they run.
+        if (!a.sync && st + 1 < nstages) load_stage(st + 1, xnext, g + 1);
 
         // Pairs [t0, t1) of this stage; the fragments of pair t+1 are read
         // from LDS while the MFMAs of pair t run. The loop body fetches
@@ -498,6 +504,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
 
         if (st + 1 < nstages) {
             __syncthreads();
+            if (a.sync) load_stage(st + 1, xnext, g + 1);
             store_stage((st + 1) % a.NWH == 0);
             __syncthreads();
         }
@@ -612,6 +619,8 @@ bool plan(const ConvShape& c, FusedArgs& a, int& wco, int& wpx, int& nb)
     a.divWi = FastDiv((uint32_t)c.Wi);
     a.divHalfW = FastDiv((uint32_t)std::max(1, c.Wi / 2));
     a.divS = FastDiv((uint32_t)c.sw);
+    a.swz = knob(KNOB_TILE_ORDER) != 1;
+    a.sync = knob(KNOB_SYNC_STAGING) == 1;
     return true;
 }
 

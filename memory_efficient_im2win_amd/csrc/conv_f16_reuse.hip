@@ -74,6 +74,7 @@ struct ReuseArgs {
     int gl, gjs, grs;
     uint32_t RD, wco, wfm;
     bool swz;                       // XCD-grouped tile order
+    bool sync;                      // stages copied through registers, one buffer
     FastDiv divWo, divG;
 };
 
@@ -124,15 +125,8 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
     const int Ho = a.c.Ho, Wo = a.c.Wo;
     const int G = a.G;
 
-    // Workgroups are handed to the 8 XCDs in turn (block b on XCD b % 8).
-    // With swz, XCD x takes the contiguous tiles [x*G8, (x+1)*G8), so tiles
-    // that share input rows share that XCD's L2; the last partial round
-    // keeps launch order.
-    int64_t bid = blockIdx.x;
-    if (a.swz) {
-        const int64_t G8 = (int64_t)gridDim.x / 8;
-        if (bid < 8 * G8) bid = (bid % 8) * G8 + bid / 8;
-    }
+    // XCD-grouped tile order unless the tile_order knob asks for launch order.
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, a.swz);
     const int co_t = (int)(bid % a.co_tiles);
     const int64_t pt = bid / a.co_tiles;
     const int co0 = co_t * kCoT;
@@ -242,6 +236,35 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
         const __amdgpu_buffer_rsrc_t rx = rbuf(x, a.xbytes);
 #pragma unroll
         for (int i = 0; i < DMAX; ++i) dma16(rx, lbase + a.dummy, kMiss);
+    };
+    // Without direct loads (sync): the same slots copied through registers
+    // into buffer sb, four slots at a time, each wave waiting for its loads.
+    auto copy_stage = [&](int s, int sb) {
+        const uint32_t fo = (uint32_t)s * a.S * a.Copad * 16;
+        const int64_t xo = (int64_t)s * a.Cg * Hi * Wi;
+        const __amdgpu_buffer_rsrc_t ra =
+            rbuf(wp + (int64_t)s * a.S * a.Copad, WPK ? a.wbytes - fo : 0u);
+        const __amdgpu_buffer_rsrc_t rx = rbuf(x + xo, a.xbytes - (uint32_t)(xo * 2));
+        unsigned char* base = smem + (size_t)sb * a.stage_bytes;
+#pragma unroll
+        for (int i0 = 0; i0 < DMAX; i0 += 4) {
+            uint4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int m = wave + NWV * (i0 + k);
+                if (i0 + k < DMAX) {
+                    const auto r = __builtin_amdgcn_raw_buffer_load_b128(m < a.S ? ra : rx,
+                                                                         (int)voff[i0 + k], 0, 0);
+                    v[k] = make_uint4(r[0], r[1], r[2], r[3]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int m = wave + NWV * (i0 + k);
+                if (i0 + k < DMAX && m < a.S + a.NX && (WPK || m >= a.S))
+                    *reinterpret_cast<uint4*>(base + (size_t)m * 1024 + 16 * lane) = v[k];
+            }
+        }
     };
 
     floatx16_t acc[2][kJ];
@@ -421,32 +444,50 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
         }
     }
 
-    issue(0, 0);
-    if (a.NS > 1) issue(1, 1); else issue_none();
-    if (coal) {
-        gather_load(0);
-        gather_store(0);
-        if (a.NS > 1) {
-            gather_load(1);
-            gather_store(1);
+    // sync: one buffer, each stage copied through registers after every
+    // wave is done with the one before, and computed once it has landed (no
+    // copy in flight during the MFMAs).
+    const bool sync = a.sync;
+    if (!sync) {
+        issue(0, 0);
+        if (a.NS > 1) issue(1, 1); else issue_none();
+        if (coal) {
+            gather_load(0);
+            gather_store(0);
+            if (a.NS > 1) {
+                gather_load(1);
+                gather_store(1);
+            }
+        } else if (!WPK) {
+            gather(0, 0);
+            if (a.NS > 1) gather(1, 1);
         }
-    } else if (!WPK) {
-        gather(0, 0);
-        if (a.NS > 1) gather(1, 1);
     }
     const int npairs = a.Cg >> 1;
     for (int s = 0; s < a.NS; ++s) {
-        // This wave's loads of stage s have landed (those of stage s+1 may
-        // still be in flight).
-        wait_loads<DMAX>();
-        __syncthreads();      // every wave's; and stage s-1's buffer is free
-        if (s + 2 < a.NS) issue(s + 2, (s + 2) % kBufs); else issue_none();
-        if (coal && s + 2 < a.NS) gather_load(s + 2);
-        const unsigned char* A = smem + (size_t)(s % kBufs) * a.stage_bytes;
+        if (sync) {
+            __syncthreads();   // every wave is done with the previous stage
+            copy_stage(s, 0);
+            if (coal) {
+                gather_load(s);
+                gather_store(0);
+            } else if (!WPK) {
+                gather(s, 0);
+            }
+            __syncthreads();
+        } else {
+            // This wave's loads of stage s have landed (those of stage s+1
+            // may still be in flight).
+            wait_loads<DMAX>();
+            __syncthreads();      // every wave's; and stage s-1's buffer is free
+            if (s + 2 < a.NS) issue(s + 2, (s + 2) % kBufs); else issue_none();
+            if (coal && s + 2 < a.NS) gather_load(s + 2);
+        }
+        const unsigned char* A = smem + (size_t)(sync ? 0 : s % kBufs) * a.stage_bytes;
         const unsigned char* X = A + (size_t)a.S * 1024;
         for (int cp = 0; cp < npairs; ++cp) pair_mmas(A, X, cp);
         // Stage s+2's buffer was freed by the barrier above.
-        if (!WPK && s + 2 < a.NS) {
+        if (!sync && !WPK && s + 2 < a.NS) {
             if (coal)
                 gather_store((s + 2) % kBufs);
             else
@@ -570,6 +611,7 @@ bool plan(const ConvShape& c, ReuseArgs& a, int& nwv, int& dmax)
     a.divWo = FastDiv((uint32_t)c.Wo);
     a.divG = FastDiv((uint32_t)a.G);
     a.swz = knob(KNOB_TILE_ORDER) != 1;
+    a.sync = knob(KNOB_SYNC_STAGING) == 1;
     return true;
 }
 

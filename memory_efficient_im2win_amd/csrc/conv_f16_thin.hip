@@ -73,6 +73,8 @@ struct ThinArgs {
     // ceil(2^32 / Wf). gd = 0: one 16-byte entry per thread and load round.
     int gd;
     uint32_t chw, chwm, wfm;
+    bool swz;                       // XCD-grouped tile order
+    bool sync;                      // filter copied through registers
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tbuf(const void* base, uint32_t bytes)
@@ -117,8 +119,10 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
     const int sh = a.c.sh, sw = a.c.sw;
     const int Ho = a.c.Ho, Wo = a.c.Wo, Hf = a.c.Hf;
 
-    const int co_t = (int)(blockIdx.x % a.co_tiles);
-    const int64_t pt = blockIdx.x / a.co_tiles;
+    // XCD-grouped tile order unless the tile_order knob asks for launch order.
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, a.swz);
+    const int co_t = (int)(bid % a.co_tiles);
+    const int64_t pt = bid / a.co_tiles;
     const int co0 = co_t * kCoT;
     int64_t q0, qend;
     if (a.aligned) {   // tile pt = (image, tile within the image)
@@ -177,7 +181,19 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
     // and Co): from the prepacked filter, entries m*Copad + co0 + j, or
     // gathered from w, whose taps of slice m of channel co start at element
     // (co*Ci*Hf + m)*Wf.
-    if (WPK) {
+    // The whole tile is one stage, so no copy overlaps an MFMA either way;
+    // sync copies the filter through registers instead of loading it
+    // straight into LDS.
+    if (WPK && a.sync) {
+        const __amdgpu_buffer_rsrc_t r = tbuf(wp, a.wbytes);
+#pragma unroll 4
+        for (int m = wave; m < a.S; m += kNW) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                r, (int)((m * a.Copad + co0 + lane) * 16), 0, 0);
+            *reinterpret_cast<uint4*>(smem + (size_t)m * 1024 + 16 * lane) =
+                make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    } else if (WPK) {
         const __amdgpu_buffer_rsrc_t r = tbuf(wp, a.wbytes);
         for (int m = wave; m < a.S; m += kNW)
             dma16t(r, lbase + (uint32_t)m * 1024, (uint32_t)((m * a.Copad + co0 + lane) * 16));
@@ -480,6 +496,8 @@ bool plan(const ConvShape& c, ThinArgs& a)
     a.divHo = FastDiv((uint32_t)c.Ho);
     a.divCH = FastDiv((uint32_t)a.CH);
     a.divRIN = FastDiv((uint32_t)a.RIN);
+    a.swz = knob(KNOB_TILE_ORDER) != 1;
+    a.sync = knob(KNOB_SYNC_STAGING) == 1;
     return true;
 }
 

@@ -62,6 +62,8 @@ struct WideArgs {
     uint32_t lds_bytes;
     uint32_t xbytes, ybytes, wbytes, worig;   // x, y, prepacked filter, filter in w's layout
     FastDiv divWo, divHo, divWi, divHalfW, divS;
+    bool swz;                       // XCD-grouped tile order
+    bool sync;                      // groups copied through registers, one buffer
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t wbuf(const void* base, uint32_t bytes)
@@ -106,8 +108,10 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
     const int Ho = a.c.Ho, Wo = a.c.Wo, Hf = a.c.Hf, Wf = a.c.Wf;
     const int HW = a.HW, RS = a.RS, NU = a.NU;
 
-    const int co_t = (int)(blockIdx.x % a.co_tiles);
-    const int64_t pt = blockIdx.x / a.co_tiles;
+    // XCD-grouped tile order unless the tile_order knob asks for launch order.
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, a.swz);
+    const int co_t = (int)(bid % a.co_tiles);
+    const int64_t pt = bid / a.co_tiles;
     const int co0 = co_t * kCoW;
     int64_t q0, qend;
     if (a.aligned) {   // tile pt = (image, tile within the image)
@@ -258,6 +262,19 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
             dma16w(r, dst + (uint32_t)m * 1024,
                    lo + (uint32_t)(m >> 1) * a.Copad * 16 + (uint32_t)(m & 1) * 1024);
     };
+    // The same kilobytes copied through registers (synchronous staging).
+    auto copy_w = [&](int g, int sb) {
+        const uint32_t go = (uint32_t)g * a.HWp * a.Copad * 16;
+        const __amdgpu_buffer_rsrc_t r = wbuf(wpk + (int64_t)g * a.HWp * a.Copad, a.wbytes - go);
+        unsigned char* dst = smem + (size_t)sb * a.stage_bytes + 16 * lane;
+        const uint32_t lo = (uint32_t)(co0 + lane) * 16;
+#pragma unroll 4
+        for (int m = wave; m < a.S; m += kWavesW) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                r, (int)(lo + (uint32_t)(m >> 1) * a.Copad * 16 + (uint32_t)(m & 1) * 1024), 0, 0);
+            *reinterpret_cast<uint4*>(dst + (size_t)m * 1024) = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    };
     // Without a prepacked filter: half c of entry (tap j, channel co0 + k) is
     // w[co0 + k][8g + c][j] (zero past HW, Co, Ci). A thread takes the
     // (k, c) pairs tid, tid + NT, ... and their taps in chunks, written to
@@ -347,18 +364,33 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
     const int nfull = HW >> 1;          // tap pairs with two real taps
     const bool odd = (HW & 1) != 0;
 
+    // sync: one buffer; group g's filter and rows are copied through
+    // registers after every wave is done with group g-1, and its MFMAs start
+    // once they have landed (no copy in flight during the MFMAs).
+    const bool sync = a.sync;
     // Stage 0.
-    if (WPK) dma_w(0, 0); else gather_w(0, 0);
+    if (WPK) {
+        if (sync) copy_w(0, 0); else dma_w(0, 0);
+    } else {
+        gather_w(0, 0);
+    }
     load_x(0);
     store_x(0);
     __syncthreads();   // the tap table
     // Window offsets of the first two pairs, the same in every group.
     const int t0 = T[hl], t1 = T[2 + hl];
     for (int g = 0; g < a.CG; ++g) {
+        if (sync && g > 0) {
+            __syncthreads();   // every wave is done with group g-1
+            if (WPK) copy_w(g, 0); else gather_w(g, 0);
+            load_x(g);
+            store_x(0);
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's filter loads of group g
         __syncthreads();   // every wave's loads and input rows; buffer (g+1)%2 is free
-        A = reinterpret_cast<const uint4*>(smem + (size_t)(g & 1) * a.stage_bytes);
-        X = reinterpret_cast<const uint4*>(smem + (size_t)(g & 1) * a.stage_bytes + a.fbytes);
+        const size_t sb = sync ? 0 : (size_t)(g & 1);
+        A = reinterpret_cast<const uint4*>(smem + sb * a.stage_bytes);
+        X = reinterpret_cast<const uint4*>(smem + sb * a.stage_bytes + a.fbytes);
 
         // The fragments of pair t+1 are read while the MFMAs of pair t run;
         // reads run at most two pairs past the group (inside the allocation,
@@ -368,7 +400,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
         on0 = t0;
         on1 = t1;
         fetch(f0, 0);
-        if (g + 1 < a.CG) {
+        if (!sync && g + 1 < a.CG) {
             if (WPK) dma_w(g + 1, (g + 1) & 1);
             load_x(g + 1);
         }
@@ -403,7 +435,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
             }
             mma(f0);
         }
-        if (g + 1 < a.CG) {
+        if (!sync && g + 1 < a.CG) {
             store_x((g + 1) & 1);
             if (!WPK) gather_w(g + 1, (g + 1) & 1);
         }
@@ -501,6 +533,8 @@ bool plan(const ConvShape& c, WideArgs& a, size_t copad_mult)
     a.divWi = FastDiv((uint32_t)c.Wi);
     a.divHalfW = FastDiv((uint32_t)std::max(1, c.Wi / 2));
     a.divS = FastDiv((uint32_t)c.sw);
+    a.swz = knob(KNOB_TILE_ORDER) != 1;
+    a.sync = knob(KNOB_SYNC_STAGING) == 1;
     return true;
 }
 

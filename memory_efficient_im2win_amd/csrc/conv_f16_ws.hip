@@ -64,6 +64,7 @@ struct WsArgs {
     uint32_t wsbytes, ybytes, worig;
     uint32_t lastmask[4];           // B dwords of a channel's last slice: positions past Wf*Hf cleared
     bool swz;                       // XCD-grouped tile order
+    bool sync;                      // stages copied through registers, one buffer
     FastDiv divWo, divHo, divPlane;
 };
 
@@ -110,11 +111,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
     const int HW = Hf * Wf, M = a.M, L = a.L, step = a.step;
     const int64_t plane = (int64_t)Ho * Wo;
 
-    int64_t bid = blockIdx.x;
-    if (a.swz) {
-        const int64_t G8 = (int64_t)gridDim.x / 8;
-        if (bid < 8 * G8) bid = (bid % 8) * G8 + bid / 8;
-    }
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, a.swz);
     const int co_t = (int)(bid % a.co_tiles);
     const int64_t pt = bid / a.co_tiles;
     const int co0 = co_t * kCoT;
@@ -210,6 +207,29 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
 #pragma unroll
         for (int i = 0; i < DMAX; ++i) dma16(rx, lbase + a.dummy, kMiss);
     };
+    // Without direct loads (sync): the same row kilobytes copied through
+    // registers into buffer sb, four at a time.
+    auto copy_stage = [&](int s, int sb) {
+        const int64_t xo = (int64_t)s * a.Cg * Ho * L;
+        const __amdgpu_buffer_rsrc_t rx = rbuf(ws + xo, a.wsbytes - (uint32_t)(xo * 2));
+        unsigned char* base = smem + (size_t)sb * a.stage_bytes + (size_t)a.S * 1024 + 16 * lane;
+#pragma unroll
+        for (int i0 = 0; i0 < DMAX; i0 += 4) {
+            uint4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (i0 + k < DMAX) {
+                    const auto r = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)voff[i0 + k], 0, 0);
+                    v[k] = make_uint4(r[0], r[1], r[2], r[3]);
+                }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int m = wave + NWV * (i0 + k);
+                if (i0 + k < DMAX && m < a.NX)
+                    *reinterpret_cast<uint4*>(base + (size_t)m * 1024) = v[k];
+            }
+        }
+    };
 
     // Filter slices of stage sg in window order: entry (slice m, channel
     // co0 + e) holds w[co0 + e][sg*Cg + m/M][kh][kw] at position p of the
@@ -304,16 +324,28 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
     };
 
     const int nk = a.S >> 1;   // K steps per stage (S is even)
-    issue(0, 0);
-    gather(0, 0);
+    // sync: one buffer, each stage copied through registers after every wave
+    // is done with the one before (no copy in flight during the MFMAs).
+    const bool sync = a.sync;
+    if (!sync) {
+        issue(0, 0);
+        gather(0, 0);
+    }
     for (int s = 0; s < a.NS; ++s) {
-        // This wave's loads of stage s have landed, and (barrier) every
-        // wave's, and every wave is done with stage s-1's buffer.
-        wait_loads<0>();
-        __syncthreads();
-        if (s + 1 < a.NS) issue(s + 1, (s + 1) % kBufs); else issue_none();
+        if (sync) {
+            __syncthreads();   // every wave is done with the previous stage
+            copy_stage(s, 0);
+            gather(s, 0);
+            __syncthreads();
+        } else {
+            // This wave's loads of stage s have landed, and (barrier) every
+            // wave's, and every wave is done with stage s-1's buffer.
+            wait_loads<0>();
+            __syncthreads();
+            if (s + 1 < a.NS) issue(s + 1, (s + 1) % kBufs); else issue_none();
+        }
 
-        const unsigned char* A = smem + (size_t)(s % kBufs) * a.stage_bytes;
+        const unsigned char* A = smem + (size_t)(sync ? 0 : s % kBufs) * a.stage_bytes;
         const unsigned char* X = A + (size_t)a.S * 1024;
         Frags f0, f1;
         sms = hl < M ? hl : hl - M;
@@ -332,7 +364,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
         }
         if (t < nk) mma(f0);
         // The next stage's filter goes to the buffer freed by the barrier.
-        if (s + 1 < a.NS) gather(s + 1, (s + 1) % kBufs);
+        if (!sync && s + 1 < a.NS) gather(s + 1, (s + 1) % kBufs);
     }
     wait_loads<0>();
 
@@ -449,6 +481,7 @@ bool plan(const ConvShape& c, WsArgs& a, int& nwv, int& dmax)
     a.divHo = FastDiv((uint32_t)c.Ho);
     a.divPlane = FastDiv((uint32_t)plane);
     a.swz = knob(KNOB_TILE_ORDER) != 1;
+    a.sync = knob(KNOB_SYNC_STAGING) == 1;
     return true;
 }
 

@@ -59,6 +59,8 @@ struct MArgs {
                                       // K offset table entries
     int NU, RS, CSX, xent;            // entries per phase, per row (sw*NU), per channel; total
     uint32_t xbytes, wbytes, ybytes;
+    bool swz;                         // XCD-grouped item order
+    bool sync;                        // next stage loaded after this one's MFMAs
     FastDiv divWo, divHo, divS;
 };
 
@@ -409,7 +411,10 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
     };
 
     // ---- the step stream ------------------------------------------------------
-    int64_t it = blockIdx.x;
+    // Workgroups of one XCD take neighbouring items (XCD-grouped order)
+    // unless the tile_order knob asks for launch order; either way the
+    // first items are a permutation of 0 .. gridDim.x - 1.
+    int64_t it = xcd_tile(blockIdx.x, gridDim.x, a.swz);
     if (it >= items) return;
     item_of(it, L);
     setup_load(L);
@@ -435,7 +440,9 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
                 nst = L.st0;
             }
         }
-        if (more) load_stage(nst);
+        // sync: the next stage's loads wait until this stage's MFMAs are
+        // issued, so no copy is in flight while they run.
+        if (more && !a.sync) load_stage(nst);
         compute_stage(st);
         if (last) {
             epilogue();
@@ -443,6 +450,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
         }
         if (!more) break;
         __syncthreads();
+        if (a.sync) load_stage(nst);
         store_stage(nst);
         __syncthreads();
         if (last) {
@@ -746,6 +754,8 @@ int launch_conv_f32_mfma(const float* x, const float* w, float* y, const ConvSha
     Choice ch;
     if (!choose(c, ch)) return -1;
     MArgs args = ch.a;
+    args.swz = knob(KNOB_TILE_ORDER) != 1;
+    args.sync = knob(KNOB_SYNC_STAGING) == 1;
     void* params[] = {(void*)&x, (void*)&w, (void*)&y, (void*)&args};
     const dim3 grid((unsigned)ch.grid), block(64 * ch.nw);
     const hipError_t e = hipLaunchKernel(ch.f, grid, block, params, ch.lds, stream);

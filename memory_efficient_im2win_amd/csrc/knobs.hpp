@@ -29,6 +29,8 @@ enum Knob : int {
     KNOB_TILE_ORDER,         // 1: tiles in launch order (default: XCD-grouped where a kernel has it)
     KNOB_F16_REUSE,          // -1: row-reuse fp16 kernel off (the row-staged kernel takes its shapes)
     KNOB_F16_WS,             // -1: staged fp16 kernel over the materialised tensor off
+    KNOB_SYNC_STAGING,       // 1: each stage copied through registers and waited for before its
+                             //    MFMAs (no copy in flight during them; no direct global-to-LDS loads)
     KNOB_COUNT
 };
 

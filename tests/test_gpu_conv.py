@@ -827,3 +827,66 @@ def test_conv_f32_random_shapes(t, orc, knob):
     knob("f32_valu", 1)
     note(f"conv fp32 random {sh.describe()} vector ALU")
     assert_exact(_run(sh, "f32", xi, wi, None), refi, f"{sh.describe()} vector ALU")
+
+
+# One case per kernel that has the ablation switches (tile_order=1: tiles in
+# launch order instead of XCD-grouped; sync_staging=1: each stage copied
+# through registers and waited for before its MFMAs), with the knobs that
+# route the shape to it: (shape, dtype, workspace kind, knobs, kernel).
+SWITCH_CASES = [
+    ((2, 64, 40, 40, 64, 7, 7, 2), "f16", "filter", {}, "conv_f16_reuse_kernel"),
+    ((40, 4, 21, 32, 70, 5, 5, 2), "f16", None, {}, "conv_f16_reuse_kernel"),
+    ((2, 64, 40, 40, 64, 7, 7, 2), "f16", "filter", {"f16_reuse": -1}, "conv_f16_rows_kernel"),
+    ((40, 4, 21, 32, 70, 5, 5, 2), "f16", None, {"f16_reuse": -1, "f16_rows_bufs": 2},
+     "conv_f16_rows_kernel"),
+    ((3, 3, 35, 64, 64, 7, 7, 2), "f16", "filter", {}, "conv_f16_thin_kernel"),
+    ((2, 3, 47, 45, 37, 7, 7, 2), "f16", None, {}, "conv_f16_thin_kernel"),
+    ((2, 96, 24, 24, 256, 5, 5, 1), "f16", "filter", {}, "conv_f16_wide_kernel"),
+    ((3, 13, 19, 21, 130, 3, 3, 1), "f16", None, {}, "conv_f16_wide_kernel"),
+    ((1, 64, 30, 30, 64, 7, 7, 2), "f16", "filter", {}, "conv_f16_fused_kernel"),
+    ((2, 24, 14, 14, 96, 5, 5, 1), "f16", None, {"f16_nwh": 3}, "conv_f16_fused_kernel"),
+    ((2, 16, 30, 32, 70, 7, 7, 2), "f16", "full", {}, "conv_f16_ws_kernel"),
+    ((3, 6, 23, 24, 33, 3, 5, (1, 2)), "f16", "one", {}, "conv_f16_ws_kernel"),
+    ((2, 3, 99, 99, 96, 11, 11, 4), "f32", None, {}, "conv_f32_mfma_kernel"),
+    ((1, 96, 12, 12, 256, 5, 5, 1), "f32", None, {"f32_ksplit": 4}, "conv_f32_mfma_kernel"),
+    # 271 items on a grid of at most 256 workgroups: items in turn
+    ((24, 4, 40, 40, 32, 3, 3, 1), "f32", None, {"f32_nw": 4, "f32_occ": 1},
+     "conv_f32_mfma_kernel"),
+]
+_MODE_OF_KIND = {None: "fused", "filter": "prepacked", "full": "materialized",
+                 "one": "materialized"}
+
+
+@pytest.mark.parametrize("case", SWITCH_CASES, ids=lambda c: f"{c[4]}-{c[0]}-{c[2]}")
+def test_ablation_switches_keep_results(case, orc, knob):
+    """The two ablation switches change how a kernel stages its operands and
+    orders its tiles, never what it sums or in which order: every switch
+    setting runs the same kernel, exact on integer inputs, and gives the same
+    bits as the default on uniform inputs."""
+    import torch
+    t, dt, kind, kn, kernel = case
+    sh = _shape(t, dt)
+    for k, v in kn.items():
+        knob(k, v)
+    name = m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
+                              sh.elem_bytes, _MODE_OF_KIND[kind])
+    assert name == kernel
+    dev = device()
+    x, w = workloads.make_inputs(sh, seed=61)
+    xi, wi = workloads.make_inputs(sh, seed=62, mode="int")
+    refi = orc.conv_direct(xi, wi, sh.s)
+    xt, wt, xit, wit = to_dev(x, dev), to_dev(w, dev), to_dev(xi, dev), to_dev(wi, dev)
+    note(f"ablation switches {kernel} {sh.describe()} ws={kind}: default")
+    base = call(sh, xt, wt, kind, dev).cpu()
+    for order, sync in ((1, 0), (0, 1), (1, 1)):
+        knob("tile_order", order)
+        knob("sync_staging", sync)
+        note(f"ablation switches {kernel} {sh.describe()} ws={kind} tile_order={order} "
+             f"sync_staging={sync}")
+        assert m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
+                                  sh.elem_bytes, _MODE_OF_KIND[kind]) == kernel
+        assert_exact(call(sh, xit, wit, kind, dev).cpu().numpy(), refi,
+                     f"{sh.describe()} order={order} sync={sync}")
+        got = call(sh, xt, wt, kind, dev).cpu()
+        assert torch.equal(got, base), f"{sh.describe()} order={order} sync={sync}"
+    torch.cuda.synchronize()
