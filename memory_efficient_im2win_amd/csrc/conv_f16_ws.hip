@@ -96,7 +96,7 @@ __device__ __forceinline__ void wait_loads()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int NWV, int DMAX>
+template <int NWV, int DMAX, bool ODD>
 __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* __restrict__ ws,
                                                                const uint16_t* __restrict__ w,
                                                                float* __restrict__ y, WsArgs a)
@@ -166,6 +166,15 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
                 s = sa[kk];
             }
         pbo[b] = (o + ho * L + wo * step - s) * 2;
+    }
+    // Odd sw*Hf: a window may start on an odd element (two bytes past a
+    // dword). Its 16 bytes are then read as the five dwords around them and
+    // shifted down by psh bits (0 or 16) per dword pair.
+    int psh[kNB];
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+        psh[b] = ODD ? (pbo[b] & 2) * 8 : 0;
+        if (ODD) pbo[b] &= ~3;
     }
 
     // Load slots of a stage: slot j < NX is kilobyte j of the stage's
@@ -287,9 +296,13 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
     // This lane's slice 2t + hl = (channel cl, slice ms) sits at byte
     // cl*XC*2 + 16*ms from a pixel's window start; it advances by two slices
     // per pair, carrying ms into cl.
+    // The loop below reads one pair past a stage (never used); such a read,
+    // a channel region past the stage's last, is sent back to offset 0 so
+    // that every LDS read stays inside the stage's regions.
+    const int oend = a.Cg * xc2;
     int sms = 0, soff = 0;
     auto fetch = [&](Frags& f, const unsigned char* A, const unsigned char* X, int t) {
-        const int o = soff;
+        const int o = soff < oend ? soff : 0;
         f.last = sms == M - 1;
         sms += 2;
         soff += 32;
@@ -298,12 +311,21 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             __builtin_memcpy(&f.a[i], A + (size_t)(abase + 2 * t * kCoT + i * 32) * 16, 16);
-        // B addresses are 4-byte aligned (sw*Hf even, regions start on
+        // B addresses are 4-byte aligned (pbo is, and regions start on
         // 16-byte boundaries); stated so, the reads become aligned dword
         // reads instead of the much slower unaligned 16-byte form.
 #pragma unroll
-        for (int b = 0; b < kNB; ++b)
-            __builtin_memcpy(&f.b[b], __builtin_assume_aligned(X + pbo[b] + o, 4), 16);
+        for (int b = 0; b < kNB; ++b) {
+            if (ODD) {
+                uint32_t d[5], r[4];
+                __builtin_memcpy(d, __builtin_assume_aligned(X + pbo[b] + o, 4), 20);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], psh[b]);
+                __builtin_memcpy(&f.b[b], r, 16);
+            } else {
+                __builtin_memcpy(&f.b[b], __builtin_assume_aligned(X + pbo[b] + o, 4), 16);
+            }
+        }
     };
     auto mma = [&](Frags& f) {
         const uint32_t k0 = f.last ? lm0 : ~0u, k1 = f.last ? lm1 : ~0u, k2 = f.last ? lm2 : ~0u,
@@ -403,8 +425,8 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
 
 constexpr int kDmax[] = {4, 6, 8, 10, 12, 16};
 
-// Plans a launch; false if the shape is outside the kernel's envelope: sw*Hf
-// even (4-byte aligned window reads), packed rows a multiple of 8 elements
+// Plans a launch; false if the shape is outside the kernel's envelope: packed
+// rows a multiple of 8 elements
 // (16-byte aligned regions), a stage of two channels in LDS, tiles touching
 // at most kMaxSeg images, tensors addressable with 32-bit buffer offsets.
 bool plan(const ConvShape& c, WsArgs& a, int& nwv, int& dmax)
@@ -412,7 +434,7 @@ bool plan(const ConvShape& c, WsArgs& a, int& nwv, int& dmax)
     a.c = c;
     a.L = c.Wi * c.Hf;
     a.step = c.sw * c.Hf;
-    if (a.step % 2 != 0 || a.L % 8 != 0) return false;
+    if (a.L % 8 != 0) return false;
     a.M = ceil_div(c.Hf * c.Wf, 8);
     a.total = (int64_t)c.N * c.Ho * c.Wo;
     const int64_t plane = (int64_t)c.Ho * c.Wo;
@@ -443,7 +465,7 @@ bool plan(const ConvShape& c, WsArgs& a, int& nwv, int& dmax)
                 }
             if (!dm) continue;
             const int64_t stage = (int64_t)(S + NX) * 1024;
-            const int64_t lds = kBufs * stage + 1024 + kSlack;
+            const int64_t lds = kBufs * stage + 1024 + kSlack;   // slack: reads past a stage
             if (lds > kWsLds) continue;
             a.Cg = cg;
             a.S = S;
@@ -488,9 +510,16 @@ bool plan(const ConvShape& c, WsArgs& a, int& nwv, int& dmax)
 template <int NWV, int DMAX>
 int launch_t(const uint16_t* ws, const uint16_t* w, float* y, const WsArgs& a, hipStream_t stream)
 {
-    ensure_lds_limit((const void*)conv_f16_ws_kernel<NWV, DMAX>, kWsLds);
-    hipLaunchKernelGGL((conv_f16_ws_kernel<NWV, DMAX>), dim3((unsigned)(a.px_tiles * a.co_tiles)),
-                       dim3(64 * NWV), a.lds_bytes, stream, ws, w, y, a);
+    const dim3 grid((unsigned)(a.px_tiles * a.co_tiles)), block(64 * NWV);
+    if (a.step % 2) {
+        ensure_lds_limit((const void*)conv_f16_ws_kernel<NWV, DMAX, true>, kWsLds);
+        hipLaunchKernelGGL((conv_f16_ws_kernel<NWV, DMAX, true>), grid, block, a.lds_bytes, stream,
+                           ws, w, y, a);
+    } else {
+        ensure_lds_limit((const void*)conv_f16_ws_kernel<NWV, DMAX, false>, kWsLds);
+        hipLaunchKernelGGL((conv_f16_ws_kernel<NWV, DMAX, false>), grid, block, a.lds_bytes, stream,
+                           ws, w, y, a);
+    }
     return launch_status();
 }
 

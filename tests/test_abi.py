@@ -356,7 +356,9 @@ def test_conv_kernel_name():
             "conv_f16_fused_kernel"
     assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2, "materialized") == \
         "conv_f16_ws_kernel"
-    assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2, "materialized") == "conv_f16_kernel"
+    assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2, "materialized") == \
+        "conv_f16_ws_kernel"
+    assert m.conv_kernel_name(64, 3, 227, 227, 64, 7, 7, 2, 2, "materialized") == "conv_f16_kernel"
     with m.knobs(f16_ws=-1):
         assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2, "materialized") == \
             "conv_f16_kernel"

@@ -434,6 +434,12 @@ WS = [
     (2, 8, 15, 24, 20, 1, 8, 2),
     (1, 10, 40, 64, 96, 3, 6, (2, 4)),
     (2, 16, 24, 40, 64, 7, 2, (1, 2)),
+    # odd window steps sw*Hf (windows starting on odd elements)
+    (2, 96, 24, 24, 256, 5, 5, 1),      # cv5 images: tiles across four images
+    (2, 16, 14, 16, 70, 5, 5, 1),
+    (3, 8, 12, 24, 40, 3, 3, 1),
+    (2, 6, 20, 8, 33, 7, 3, 1),
+    (3, 4, 15, 16, 64, 3, 3, (2, 3)),
 ]
 
 
@@ -461,8 +467,8 @@ def test_conv_f16_materialised_staged(t, orc, knob):
     assert_exact(_run(sh, "f16", xi, wi, "full"), got["full"], "per-entry kernel")
 
 
-@pytest.mark.parametrize("t", [(2, 4, 19, 24, 40, 7, 7, 2), (2, 3, 14, 16, 40, 3, 4, (1, 2))],
-                         ids=str)
+@pytest.mark.parametrize("t", [(2, 4, 19, 24, 40, 7, 7, 2), (2, 3, 14, 16, 40, 3, 4, (1, 2)),
+                               (2, 4, 14, 16, 40, 5, 5, 1)], ids=str)
 def test_conv_f16_materialised_staged_special_values(t, orc):
     """Infinities and NaN in the input reach exactly the outputs whose windows
     hold them: the padding of a channel's last slice (the next window's
