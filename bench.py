@@ -53,8 +53,9 @@ MODES = ["fused", "fused_valu", "prepacked", "materialized"]
 LAYER_STEPS = {"cv4_f16_n64": 20}
 
 
-CONV_KERNELS = ("conv_f32_mfma_kernel", "conv_f32_kernel", "conv_f16_fused_kernel",
-                "conv_f16_rows_kernel", "conv_f16_thin_kernel", "conv_f16_wide_kernel",
+CONV_KERNELS = ("conv_f32_mfma_kernel", "conv_f32_small_kernel", "conv_f32_kernel",
+                "conv_f16_fused_kernel", "conv_f16_rows_kernel", "conv_f16_reuse_kernel",
+                "conv_f16_thin_kernel", "conv_f16_wide_kernel", "conv_f16_ws_kernel",
                 "conv_f16_kernel")
 
 
@@ -421,9 +422,12 @@ SWITCHES = [("default", {}), ("tiles in launch order", {"tile_order": 1}),
             ("synchronous staging", {"sync_staging": 1}),
             ("launch order + synchronous staging", {"tile_order": 1, "sync_staging": 1})]
 SWITCH_MODES = {"f32": ["fused"], "f16": ["fused", "prepacked", "materialized"]}
+# Kernels with both switches; the small-problem fp32 kernel stages once (no
+# copy can overlap its MFMAs) and has only the tile order.
 SWITCH_KERNELS = ("conv_f32_mfma_kernel", "conv_f16_reuse_kernel", "conv_f16_rows_kernel",
                   "conv_f16_thin_kernel", "conv_f16_wide_kernel", "conv_f16_fused_kernel",
                   "conv_f16_ws_kernel")
+ORDER_ONLY_KERNELS = ("conv_f32_small_kernel",)
 
 
 def ablation(keys, steps):
@@ -439,7 +443,8 @@ def ablation(keys, steps):
         for mode in SWITCH_MODES[sh.dtype]:
             kern = m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
                                       sh.elem_bytes, mode)
-            variants = SWITCHES if kern in SWITCH_KERNELS else SWITCHES[:1]
+            variants = SWITCHES if kern in SWITCH_KERNELS else \
+                SWITCHES[:2] if kern in ORDER_ONLY_KERNELS else SWITCHES[:1]
             res = time_variants(sh, mode, variants, steps)
             base = res[variants[0][0]]["ms_per_launch_median"]
             for label, _ in variants:

@@ -302,7 +302,8 @@ void ensure_lds_limit(const void* f, int bytes)
 const char* const kKnobNames[KNOB_COUNT] = {
     "f32_valu", "f32_nw", "f32_wco", "f32_cb", "f32_ksplit", "f32_occ",
     "f16_rows", "f16_rows_nwv", "f16_rows_bufs", "f16_thin", "f16_thin_nb", "f16_wide",
-    "f16_wide_nw", "f16_wpx", "f16_nwh", "tile_order", "f16_reuse", "f16_ws", "sync_staging"};
+    "f16_wide_nw", "f16_wpx", "f16_nwh", "tile_order", "f16_reuse", "f16_ws", "sync_staging",
+    "f32_small"};
 
 std::atomic<int> g_knobs[KNOB_COUNT];
 }  // namespace im2win
@@ -501,8 +502,9 @@ const char* im2win_conv_kernel_name(int elem_bytes, int mode, int N, int Ci, int
     const ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo};
     if (elem_bytes == 4) {
         if (mode == 2) return "conv_f32_kernel";
-        const bool mfma = im2win::knob(im2win::KNOB_F32_VALU) != 1 && im2win::f32_mfma_applies(c);
-        return mfma ? "conv_f32_mfma_kernel" : "conv_f32_kernel";
+        const char* mfma =
+            im2win::knob(im2win::KNOB_F32_VALU) != 1 ? im2win::f32_mfma_kernel_name(c) : nullptr;
+        return mfma ? mfma : "conv_f32_kernel";
     }
     if (mode == 2) return im2win::f16_ws_applies(c) ? "conv_f16_ws_kernel" : "conv_f16_kernel";
     return im2win::f16_fused_kernel_name(c, reinterpret_cast<const void*>(uintptr_t(256)));

@@ -740,6 +740,14 @@ bool choose(const ConvShape& c, Choice& ch)
     return found;
 }
 
+// A problem too small to fill the chip (the planner splits K inside the
+// workgroup) runs on the one-stage small-problem kernel when that kernel
+// takes the shape, unless a K split is forced.
+bool use_small(const ConvShape& c, const Choice& ch)
+{
+    return ch.ksw > 1 && knob(KNOB_F32_KSPLIT) <= 0 && f32_small_applies(c);
+}
+
 }  // namespace
 
 bool f32_mfma_applies(const ConvShape& c)
@@ -748,11 +756,22 @@ bool f32_mfma_applies(const ConvShape& c)
     return choose(c, ch);
 }
 
+const char* f32_mfma_kernel_name(const ConvShape& c)
+{
+    Choice ch;
+    if (!choose(c, ch)) return nullptr;
+    return use_small(c, ch) ? "conv_f32_small_kernel" : "conv_f32_mfma_kernel";
+}
+
 int launch_conv_f32_mfma(const float* x, const float* w, float* y, const ConvShape& c,
                          hipStream_t stream)
 {
     Choice ch;
     if (!choose(c, ch)) return -1;
+    if (use_small(c, ch)) {
+        const int rc = launch_conv_f32_small(x, w, y, c, stream);
+        if (rc != -1) return rc;
+    }
     MArgs args = ch.a;
     args.swz = knob(KNOB_TILE_ORDER) != 1;
     args.sync = knob(KNOB_SYNC_STAGING) == 1;

@@ -35,6 +35,16 @@ int launch_conv_f32(const float* x, const float* ws, const float* w, float* y,
 int launch_conv_f32_mfma(const float* x, const float* w, float* y, const ConvShape& c,
                          hipStream_t stream);
 bool f32_mfma_applies(const ConvShape& c);
+// The fp32 matrix-core kernel the planner runs for shape c:
+// "conv_f32_mfma_kernel" or "conv_f32_small_kernel" (nullptr: neither).
+const char* f32_mfma_kernel_name(const ConvShape& c);
+
+// fp32 convolution for problems whose output tiles cannot fill the chip
+// (v_mfma_f32_16x16x4_f32, one stage, K split over a workgroup's waves);
+// -1 if the shape is outside its envelope.
+bool f32_small_applies(const ConvShape& c);
+int launch_conv_f32_small(const float* x, const float* w, float* y, const ConvShape& c,
+                          hipStream_t stream);
 
 // fp16 convolution from the materialised tensor ws (N images) with each
 // channel's window stretch copied into LDS by direct loads (f16_ws_applies);

@@ -31,6 +31,7 @@ enum Knob : int {
     KNOB_F16_WS,             // -1: staged fp16 kernel over the materialised tensor off
     KNOB_SYNC_STAGING,       // 1: each stage copied through registers and waited for before its
                              //    MFMAs (no copy in flight during them; no direct global-to-LDS loads)
+    KNOB_F32_SMALL,          // -1: small-problem fp32 kernel off (K split across a workgroup instead)
     KNOB_COUNT
 };
 

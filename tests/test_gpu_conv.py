@@ -853,8 +853,9 @@ SWITCH_CASES = [
     ((2, 24, 14, 14, 96, 5, 5, 1), "f16", None, {"f16_nwh": 3}, "conv_f16_fused_kernel"),
     ((2, 16, 30, 32, 70, 7, 7, 2), "f16", "full", {}, "conv_f16_ws_kernel"),
     ((3, 6, 23, 24, 33, 3, 5, (1, 2)), "f16", "one", {}, "conv_f16_ws_kernel"),
-    ((2, 3, 99, 99, 96, 11, 11, 4), "f32", None, {}, "conv_f32_mfma_kernel"),
+    ((2, 3, 99, 99, 96, 11, 11, 4), "f32", None, {"f32_small": -1}, "conv_f32_mfma_kernel"),
     ((1, 96, 12, 12, 256, 5, 5, 1), "f32", None, {"f32_ksplit": 4}, "conv_f32_mfma_kernel"),
+    ((1, 96, 24, 24, 256, 5, 5, 1), "f32", None, {}, "conv_f32_small_kernel"),
     # 271 items on a grid of at most 256 workgroups: items in turn
     ((24, 4, 40, 40, 32, 3, 3, 1), "f32", None, {"f32_nw": 4, "f32_occ": 1},
      "conv_f32_mfma_kernel"),
@@ -896,3 +897,75 @@ def test_ablation_switches_keep_results(case, orc, knob):
         got = call(sh, xt, wt, kind, dev).cpu()
         assert torch.equal(got, base), f"{sh.describe()} order={order} sync={sync}"
     torch.cuda.synchronize()
+
+
+# Shapes too small to fill the chip with 32 x 32 fp32 tiles, which the
+# one-stage small-problem kernel takes: the 5x5 layer at N=1; K a multiple of
+# 4 and not (16-byte and 4-byte filter loads); Wi a multiple of 4 and not;
+# unequal strides; Co off 16; planes off 32 pixels; several images; K at the
+# 8 x 24-chunk limit.
+SMALL_F32 = [
+    (1, 96, 24, 24, 256, 5, 5, 1),
+    (1, 16, 20, 20, 40, 3, 3, 1),
+    (2, 7, 19, 23, 33, 3, 5, (2, 1)),
+    (1, 3, 30, 30, 20, 7, 7, 2),
+    (3, 5, 9, 10, 17, 4, 2, (1, 3)),
+    (1, 128, 12, 12, 64, 3, 3, 1),
+    (1, 120, 10, 10, 32, 5, 5, 1),
+]
+
+
+@pytest.mark.parametrize("t", SMALL_F32, ids=str)
+def test_conv_f32_small_problem_kernel(t, orc, knob):
+    """The small-problem fp32 kernel: exact on integer inputs, within
+    tolerance on uniform inputs, the same bits on repeated calls, and the
+    same (exact) integer results as the K split it replaces (knob
+    f32_small=-1)."""
+    import torch
+    sh = _shape(t, "f32")
+    dev = device()
+    assert m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 4) == \
+        "conv_f32_small_kernel"
+    x, w = workloads.make_inputs(sh, seed=81)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    xi, wi = workloads.make_inputs(sh, seed=82, mode="int")
+    refi = orc.conv_direct(xi, wi, sh.s)
+    note(f"conv fp32 small problem {sh.describe()}")
+    xt, wt = to_dev(x, dev), to_dev(w, dev)
+    a = m.conv2d(xt, wt, sh.s)
+    assert_within(a.cpu().numpy(), ref, absd, TOL["f32"], sh.describe())
+    for _ in range(3):
+        assert torch.equal(m.conv2d(xt, wt, sh.s), a)
+    yi = _run(sh, "f32", xi, wi)
+    assert_exact(yi, refi, sh.describe())
+    knob("f32_small", -1)
+    assert m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 4) == \
+        "conv_f32_mfma_kernel"
+    assert_exact(_run(sh, "f32", xi, wi), refi, f"{sh.describe()} K split")
+
+
+@pytest.mark.parametrize("t", [(1, 12, 14, 15, 40, 3, 5, 1), (1, 16, 12, 12, 64, 5, 5, 1)],
+                         ids=str)
+def test_conv_f32_small_problem_special_values(t, orc):
+    """Infinities and NaN in the input reach exactly the outputs whose windows
+    hold them (taps past K read a zero entry with a zero filter value)."""
+    sh = _shape(t, "f32")
+    device()
+    assert m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 4) == \
+        "conv_f32_small_kernel"
+    x, w = workloads.make_inputs(sh, seed=83)
+    x[0, 1, 4, 5] = np.inf
+    x[0, 2, 7, 10] = -np.inf
+    x[0, 0, 0, 6] = np.nan
+    x[0, sh.Ci - 1, sh.Hi - 1, sh.Wi - 1] = np.inf
+    w = np.abs(w) + np.float32(0.25)
+    ref = orc.conv_direct(x, w, sh.s)
+    fin = np.isfinite(ref)
+    _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
+                              with_absdot=True)
+    note(f"conv fp32 small problem special values {sh.describe()}")
+    y = _run(sh, "f32", x, w).astype(np.float64)
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+    assert_within(y[fin], ref[fin], absd[fin], TOL["f32"], "finite outputs")

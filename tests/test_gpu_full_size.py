@@ -125,7 +125,10 @@ def test_fp32_kernel_names(knob):
     the device for occupancy)."""
     device()
     assert m.conv_kernel_name(32, 3, 227, 227, 96, 11, 11, 4, 4) == "conv_f32_mfma_kernel"
+    assert m.conv_kernel_name(1, 96, 24, 24, 256, 5, 5, 1, 4) == "conv_f32_small_kernel"
+    knob("f32_small", -1)
     assert m.conv_kernel_name(1, 96, 24, 24, 256, 5, 5, 1, 4) == "conv_f32_mfma_kernel"
+    knob("f32_small", 0)
     assert m.conv_kernel_name(32, 3, 227, 227, 96, 11, 11, 4, 4, "materialized") == \
         "conv_f32_kernel"
     knob("f32_valu", 1)
