@@ -45,4 +45,36 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t grid, bool groupe
     return b < 8 * G8 ? (b % 8) * G8 + b / 8 : b;
 }
 
+// Raw buffer resource over [base, base + bytes): a load at a byte offset
+// (vector + scalar) at or past `bytes` returns zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16 bytes per lane from buffer r at vector offset voff straight into LDS at
+// byte lds + 16*lane (buffer_load_dwordx4 ... lds; lds wave-uniform, M0
+// saved and restored around the load). An out-of-range lane writes zeros.
+// The load counts in vmcnt like any other vector load.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff)
+{
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
+}
+
+// Waits until at most N of this wave's vector loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace im2win

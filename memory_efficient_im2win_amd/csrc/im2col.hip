@@ -10,13 +10,21 @@
 //        col[q][(ci*Hf + kh)*Wf + kw] = x[n][ci][ho*sh + kh][wo*sw + kw].
 //    That is the transpose of the usual K x P layout, with the same size; it
 //    makes each MFMA operand slice one contiguous 16-byte load.
+//    A workgroup writes the rows of 32 consecutive pixels of one output row
+//    from their input rows staged in LDS; shapes whose rows do not fit fall
+//    back to 128-byte column tiles of 32 rows, one 16-byte piece per thread.
 //  * filter_pad_kernel copies the filters into rows of KP (zero tail).
-//  * gemm_nt_kernel computes y[n][co][p] = sum_k w[co][k] * col[q][k] on the
-//    matrix cores with the same instructions as the im2win kernels
-//    (v_mfma_f32_32x32x16_f16, v_mfma_f32_32x32x2_f32): a wave owns 64
-//    output channels x 64 pixels (2 x 2 tiles of 32 x 32), operands come
-//    straight from memory (16 bytes per lane per slice), the next slice is
-//    loaded while the current one is multiplied.
+//  * gemm_tiled_kernel computes y[n][co][p] = sum_k w[co][k] * col[q][k] on
+//    the matrix cores with the same instructions and operand layouts as the
+//    im2win kernels (v_mfma_f32_32x32x16_f16, v_mfma_f32_32x32x2_f32). A
+//    workgroup owns 64 output channels x 256 pixels, each of its 4 waves 64
+//    x 64 (2 x 2 tiles of 32 x 32). A stage is 128 bytes of K of every row
+//    of both operands (64 filter rows + 256 im2col rows = 40 KB), copied
+//    into LDS with buffer_load_dwordx4 ... lds, eight lanes per row (whole
+//    128-byte lines of the im2col matrix); three stage buffers, loads two
+//    stages ahead, one barrier per stage. The 16-byte pieces of a row are
+//    stored XOR-swizzled by the row's low 3 bits, so the 8 lanes of a read
+//    group (8 rows, one piece) hit all banks.
 #include <algorithm>
 
 #include "common.hpp"
@@ -26,7 +34,6 @@ namespace im2win {
 
 namespace {
 
-constexpr int kGemmThreads = 256;   // 4 waves: 64 channels x 256 pixels per workgroup
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t gbuf(const void* base, uint64_t bytes)
 {
@@ -63,6 +70,147 @@ __global__ __launch_bounds__(256) void im2col_kernel(const T* __restrict__ x, T*
     col[e] = v;
 }
 
+struct ColVArgs {
+    ConvShape c;
+    int K, KP, cpr;           // taps, padded row, 16-byte pieces per row
+    int ptiles;               // 8-piece (128-byte) column tiles per row
+    uint32_t rows;            // N*Ho*Wo
+    FastDiv divPlane, divWo, divHW, divWf;
+};
+
+// A workgroup writes the 128-byte column tile kt of 32 consecutive rows:
+// thread t takes row q0 + t%32 and its 16-byte piece 8*kt + t/32, so the 32
+// lanes of a half-wave read one tap of 32 neighbouring windows (nearby
+// addresses) and the 8 pieces of every row's 128 bytes are written by one
+// workgroup. A piece's first tap is decomposed once; later taps step
+// (kw, kh, ci) along.
+template <typename T>
+__global__ __launch_bounds__(256) void im2col_vec_kernel(const T* __restrict__ x,
+                                                         T* __restrict__ col, ColVArgs a)
+{
+    constexpr int V = 16 / sizeof(T);
+    const uint32_t kt = blockIdx.x % (uint32_t)a.ptiles;
+    const uint32_t q = (blockIdx.x / (uint32_t)a.ptiles) * 32 + (threadIdx.x & 31);
+    const int piece = (int)kt * 8 + (int)(threadIdx.x >> 5);
+    if (q >= a.rows || piece >= a.cpr) return;
+    const int k0 = piece * V;
+    const uint32_t n = a.divPlane.div(q);
+    const int pix = (int)(q - n * (uint32_t)(a.c.Ho * a.c.Wo));
+    const int ho = (int)a.divWo.div((uint32_t)pix), wo = pix - ho * a.c.Wo;
+    const int ci = (int)a.divHW.div((uint32_t)k0);
+    const int r = k0 - ci * a.c.Hf * a.c.Wf;
+    int kh = (int)a.divWf.div((uint32_t)r), kw = r - kh * a.c.Wf;
+    // Offsets within the image (below 2^31 elements): the window corner,
+    // then tap (ci, kh, kw) relative to it, stepped along the taps.
+    const T* xw = x + (int64_t)n * a.c.Ci * a.c.Hi * a.c.Wi +
+                  ((int64_t)ho * a.c.sh) * a.c.Wi + (int64_t)wo * a.c.sw;
+    int off = (ci * a.c.Hi + kh) * a.c.Wi + kw;
+    const int row_skip = a.c.Wi - a.c.Wf, chan_skip = (a.c.Hi - a.c.Hf) * a.c.Wi;
+    T v[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        v[u] = k0 + u < a.K ? xw[off] : T(0);
+        ++off;
+        if (++kw == a.c.Wf) {
+            kw = 0;
+            off += row_skip;
+            if (++kh == a.c.Hf) {
+                kh = 0;
+                off += chan_skip;
+            }
+        }
+    }
+    uint4 o;
+    __builtin_memcpy(&o, v, 16);
+    reinterpret_cast<uint4*>(col)[(int64_t)q * a.cpr + piece] = o;
+}
+
+struct ColRArgs {
+    ConvShape c;
+    int K, KP, cpr;           // taps, padded row, 16-byte pieces per row
+    int cols;                 // LDS row pitch: 31*sw + Wf rounded up to whole dwords
+    int wtiles;               // 32-pixel segments per output row
+    int units;                // dwords per LDS row (cols * sizeof(T) / 4)
+    FastDiv divCpr, divHW, divWf, divUnits;
+};
+
+// A workgroup writes the im2col rows of 32 consecutive pixels of one output
+// row (npx <= 32 rows, contiguous in col): it first copies the input rows
+// their windows cover, every channel, columns c0 .. c0 + cols - 1, into LDS
+// ([ci][kh][col]); then consecutive threads build consecutive 16-byte
+// pieces of those rows from LDS, so every store instruction writes 1 KB of
+// consecutive bytes.
+template <typename T>
+__global__ __launch_bounds__(256) void im2col_rows_kernel(const T* __restrict__ x,
+                                                          T* __restrict__ col, ColRArgs a)
+{
+    constexpr int V = 16 / sizeof(T);
+    extern __shared__ __align__(16) unsigned char smem_c[];
+    T* Xs = reinterpret_cast<T*>(smem_c);
+    const int Ci = a.c.Ci, Hi = a.c.Hi, Wi = a.c.Wi, Hf = a.c.Hf, Wf = a.c.Wf;
+    const int Ho = a.c.Ho, Wo = a.c.Wo, sw = a.c.sw;
+    const int wt = (int)(blockIdx.x % (uint32_t)a.wtiles);
+    const int rest = (int)(blockIdx.x / (uint32_t)a.wtiles);
+    const int ho = rest % Ho, n = rest / Ho;
+    const int w0 = wt * 32;
+    const int npx = min(32, Wo - w0);
+    const int c0 = w0 * sw;
+    const int ncol = min(a.cols, Wi - c0);
+
+    // Input rows (ci, ho*sh + kh), columns c0 .. c0 + ncol - 1, copied a
+    // dword at a time (Wi*sizeof(T) and c0*sizeof(T) are multiples of 4),
+    // eight loads in flight per thread. LDS row r = ci*Hf + kh.
+    const uint32_t* xr = reinterpret_cast<const uint32_t*>(
+        x + (((int64_t)n * Ci) * Hi + (int64_t)ho * a.c.sh) * Wi + c0);
+    uint32_t* Xu = reinterpret_cast<uint32_t*>(smem_c);
+    constexpr int EPU = 4 / sizeof(T);
+    const int uw = (ncol + EPU - 1) / EPU;      // dwords of a row to copy
+    const int wu = Wi / EPU;                    // dwords per input row
+    const int total_u = Ci * Hf * a.units;
+    for (int e0 = threadIdx.x; e0 < total_u; e0 += 8 * 256) {
+        uint32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + 256 * u;
+            const int r = (int)a.divUnits.div((uint32_t)e), j = e - r * a.units;
+            const int ci = r / Hf, kh = r - ci * Hf;
+            v[u] = e < total_u && j < uw ? xr[((int64_t)ci * Hi + kh) * wu + j] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (e0 + 256 * u < total_u) Xu[e0 + 256 * u] = v[u];
+    }
+    __syncthreads();
+
+    // Pieces of rows q0 .. q0 + npx - 1: piece e = (pixel e / cpr, piece e % cpr).
+    T* out = col + (((int64_t)n * Ho + ho) * Wo + w0) * a.KP;
+    const int total = npx * a.cpr;
+    for (int e = threadIdx.x; e < total; e += 256) {
+        const int qi = (int)a.divCpr.div((uint32_t)e);
+        const int pc = e - qi * a.cpr;
+        const int k0 = pc * V;
+        const int ci = (int)a.divHW.div((uint32_t)k0);
+        const int rr = k0 - ci * Hf * Wf;
+        const int kh = (int)a.divWf.div((uint32_t)rr);
+        int kw = rr - kh * Wf;
+        // LDS row index ci*Hf + kh steps by one when kw wraps.
+        int off = (ci * Hf + kh) * a.cols + qi * sw + kw;
+        T v[V];
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            v[u] = k0 + u < a.K ? Xs[off] : T(0);
+            ++off;
+            if (++kw == Wf) {
+                kw = 0;
+                off += a.cols - Wf;
+            }
+        }
+        uint4 o;
+        __builtin_memcpy(&o, v, 16);
+        reinterpret_cast<uint4*>(out)[e] = o;
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void filter_pad_kernel(const T* __restrict__ w, T* __restrict__ wp,
                                                          int Co, int K, int KP)
@@ -83,42 +231,85 @@ struct GemmArgs {
     int Ho, Wo, Wi, sw, HfC;
 };
 
-// One MFMA slice: fp16 16 K values (lanes 0-31 the first 8, 32-63 the next 8),
-// fp32 8 K values over four 32x32x2 steps (lane half hl holds k0 + 4*hl + j
-// for step j). A and B use the same mapping, so the sum covers each k once.
+constexpr int kTM = 64;                    // output channels per tile
+constexpr int kTN = 256;                   // pixels per tile
+constexpr int kSB = 128;                   // bytes of K per row and stage
+constexpr int kTBufs = 3;                  // stage buffers: loads two stages ahead
+constexpr int kTStage = (kTM + kTN) * kSB;           // 40 KB
+constexpr int kTSlots = kTStage / 1024 / 4;          // 1-KB loads per wave and stage (10)
+constexpr int kTLds = kTBufs * kTStage + 1024;       // + the landing kilobyte of unused loads
+constexpr uint32_t kTMiss = 0xFFFFFFF0u;
+
+// Byte offset of row `row`'s 16-byte piece c in a stage region (pieces
+// XOR-swizzled by the row's low 3 bits).
+__device__ __forceinline__ uint32_t tpos(int row, int c) { return row * kSB + ((c ^ (row & 7)) << 4); }
+
 template <bool F16>
-__global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(const void* __restrict__ colv,
-                                                               const void* __restrict__ wv,
-                                                               float* __restrict__ y, GemmArgs a)
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(const void* __restrict__ colv,
+                                                         const void* __restrict__ wv,
+                                                         float* __restrict__ y, GemmArgs a)
 {
-    constexpr int E = F16 ? 2 : 4;             // element bytes
-    constexpr int SK = F16 ? 16 : 8;           // K values per slice
+    constexpr int E = F16 ? 2 : 4;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const uint32_t lbase =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     const int lane = threadIdx.x & 63, hl = lane >> 5, l32 = lane & 31;
     const int wave = uniform(threadIdx.x >> 6);
-    const int co_tiles = (a.Co + 63) / 64;
-    const int co0 = (int)(blockIdx.x % co_tiles) * 64;
-    const int64_t q0 = (int64_t)(blockIdx.x / co_tiles) * 256 + wave * 64;
+    const int co_tiles = (a.Co + kTM - 1) / kTM;
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, true);
+    const int co0 = (int)(bid % co_tiles) * kTM;
+    const int64_t q0 = (bid / co_tiles) * kTN;
 
-    const __amdgpu_buffer_rsrc_t rc = gbuf(colv, a.colbytes);
-    const __amdgpu_buffer_rsrc_t rw = gbuf(wv, a.wbytes);
-    const uint32_t kMissOff = 0xFFFFFFF0u;
-    // Byte offsets of this lane's operand rows (missing rows read zeros).
-    uint32_t ao[2], bo[2];
+    // Load slots: slot m of a stage is LDS kilobyte m = rows 8m .. 8m+7 of
+    // the stage region (filter rows 0-63 in kilobytes 0-7, im2col rows 0-255
+    // in kilobytes 8-39); wave v issues slots v, v+4, ... Lane l loads row
+    // 8m + l/8, its piece (l%8) ^ (l/8) to land at piece l%8 of the swizzle.
+    uint32_t voff[kTSlots];
+    bool isw[kTSlots];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int co = co0 + i * 32 + l32;
-        ao[i] = co < a.Co ? (uint32_t)(((int64_t)co * a.KP + (SK / 2) * hl) * E) : kMissOff;
-        const int64_t q = q0 + i * 32 + l32;
-        int64_t row = q * a.KP;
-        if (a.win_rows) {
-            const int64_t n = q / a.P;
-            const int pix = (int)(q - n * a.P);
-            const int ho = pix / a.Wo, wo = pix - ho * a.Wo;
-            row = ((n * a.Ho + ho) * a.Wi + (int64_t)wo * a.sw) * a.HfC;
+    for (int i = 0; i < kTSlots; ++i) {
+        const int m = wave + 4 * i;
+        const int row = 8 * m + (lane >> 3);
+        const int pc = (lane & 7) ^ (lane >> 3);
+        uint32_t v = kTMiss;
+        isw[i] = m < kTM / 8;
+        if (isw[i]) {
+            const int co = co0 + row;
+            if (co < a.Co) v = (uint32_t)((int64_t)co * a.KP * E) + pc * 16;
+        } else {
+            const int64_t q = q0 + (row - kTM);
+            if (q < a.rows) {
+                int64_t r = q * a.KP;
+                if (a.win_rows) {
+                    const int64_t n = q / a.P;
+                    const int pix = (int)(q - n * a.P);
+                    const int ho = pix / a.Wo, wo = pix - ho * a.Wo;
+                    r = ((n * a.Ho + ho) * a.Wi + (int64_t)wo * a.sw) * a.HfC;
+                }
+                const uint64_t b = (uint64_t)r * E + pc * 16;
+                if (b < kTMiss) v = (uint32_t)b;
+            }
         }
-        const uint64_t b = (uint64_t)(row + (SK / 2) * hl) * E;
-        bo[i] = q < a.rows && b < 0xFFFFFFF0ull ? (uint32_t)b : kMissOff;
+        voff[i] = v;
     }
+    const int nbytes = a.KP * E;                // bytes of K per row
+    const int NS = (nbytes + kSB - 1) / kSB;    // stages
+    auto issue = [&](int s, int sb) {
+        const uint32_t ko = (uint32_t)s * kSB;
+        const __amdgpu_buffer_rsrc_t rw =
+            raw_rsrc((const unsigned char*)wv + ko, (uint32_t)(a.wbytes - ko));
+        const __amdgpu_buffer_rsrc_t rc =
+            raw_rsrc((const unsigned char*)colv + ko, (uint32_t)(a.colbytes - ko));
+        const uint32_t base = lbase + (uint32_t)sb * kTStage;
+#pragma unroll
+        for (int i = 0; i < kTSlots; ++i)
+            lds_dma16(isw[i] ? rw : rc, base + (uint32_t)(wave + 4 * i) * 1024, voff[i]);
+    };
+    auto issue_none = [&]() {
+        const __amdgpu_buffer_rsrc_t rc = raw_rsrc(colv, 0u);
+#pragma unroll
+        for (int i = 0; i < kTSlots; ++i) lds_dma16(rc, lbase + kTBufs * kTStage, kTMiss);
+    };
 
     floatx16_t acc[2][2];
 #pragma unroll
@@ -128,24 +319,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(const void* __res
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    uint4 A[2], B[2], An[2], Bn[2];
-    auto load = [&](uint4* Ad, uint4* Bd, int k0) {
-        const uint32_t ko = (uint32_t)k0 * E;
+    // A: filter rows i*32 + l32; B: im2col rows kTM + 64*wave + 32*j + l32.
+    // Slice t (32 bytes of K) of a stage: lane half hl reads piece 2t + hl.
+    auto slice = [&](const unsigned char* S, int t) {
+        uint4 A[2], B[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const auto va = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(ao[i] == kMissOff ? kMissOff : ao[i] + ko), 0, 0);
-            const auto vb = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(bo[i] == kMissOff ? kMissOff : bo[i] + ko), 0, 0);
-            Ad[i] = make_uint4(va[0], va[1], va[2], va[3]);
-            Bd[i] = make_uint4(vb[0], vb[1], vb[2], vb[3]);
+            __builtin_memcpy(&A[i], S + tpos(i * 32 + l32, 2 * t + hl), 16);
+            __builtin_memcpy(&B[i], S + tpos(kTM + 64 * wave + 32 * i + l32, 2 * t + hl), 16);
         }
-    };
-    auto mma = [&](const uint4* Ad, const uint4* Bd) {
         if constexpr (F16) {
             half8_t ah[2], bh[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                __builtin_memcpy(&ah[i], &Ad[i], 16);
-                __builtin_memcpy(&bh[i], &Bd[i], 16);
+                __builtin_memcpy(&ah[i], &A[i], 16);
+                __builtin_memcpy(&bh[i], &B[i], 16);
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j)
@@ -153,13 +341,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(const void* __res
                 for (int i = 0; i < 2; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[j], acc[i][j], 0, 0, 0);
         } else {
+            // Lane half hl holds K values k0 + 4*hl + u for step u.
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int u = 0; u < 4; ++u) {
                 float af[2], bf[2];
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const uint32_t ua = s == 0 ? Ad[i].x : s == 1 ? Ad[i].y : s == 2 ? Ad[i].z : Ad[i].w;
-                    const uint32_t ub = s == 0 ? Bd[i].x : s == 1 ? Bd[i].y : s == 2 ? Bd[i].z : Bd[i].w;
+                    uint32_t ua, ub;
+                    __builtin_memcpy(&ua, reinterpret_cast<const uint32_t*>(&A[i]) + u, 4);
+                    __builtin_memcpy(&ub, reinterpret_cast<const uint32_t*>(&B[i]) + u, 4);
                     af[i] = __uint_as_float(ua);
                     bf[i] = __uint_as_float(ub);
                 }
@@ -172,24 +362,29 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(const void* __res
         }
     };
 
-    const int nsl = a.KP / SK;   // KP is a multiple of SK
-    load(A, B, 0);
-    for (int t = 0; t < nsl; ++t) {
-        if (t + 1 < nsl) load(An, Bn, (t + 1) * SK);
-        mma(A, B);
+    issue(0, 0);
+    if (NS > 1) issue(1, 1); else issue_none();
+    for (int s = 0; s < NS; ++s) {
+        wait_vm<kTSlots>();   // this wave's loads of stage s have landed
+        __syncthreads();      // every wave's; and stage s-1's buffer is free
+        if (s + 2 < NS) issue(s + 2, (s + 2) % kTBufs); else issue_none();
+        const unsigned char* S = smem + (size_t)(s % kTBufs) * kTStage;
+        const int ns = min(kSB, nbytes - s * kSB) / 32;   // 32-byte slices in this stage
+        if (ns == kSB / 32) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            A[i] = An[i];
-            B[i] = Bn[i];
+            for (int t = 0; t < kSB / 32; ++t) slice(S, t);
+        } else {
+            for (int t = 0; t < ns; ++t) slice(S, t);
         }
     }
+    wait_vm<0>();
 
     // Output: lane holds pixel l32 of each block and channels
     // 8*(r/4) + 4*hl + r%4 of each 32-channel block.
     const __amdgpu_buffer_rsrc_t ry = gbuf(y, a.ybytes);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int64_t q = q0 + j * 32 + l32;
+        const int64_t q = q0 + 64 * wave + j * 32 + l32;
         if (q >= a.rows) continue;
         const int64_t n = q / a.P;
         const int p = (int)(q - n * a.P);
@@ -212,14 +407,17 @@ int launch_gemm(const void* b, const void* a, float* y, const GemmArgs& g, int C
     // 32-bit buffer offsets: the chunk's matrix and output below 4 GiB.
     if (g.colbytes >= 0xFFFFFFF0ull || g.ybytes >= 0xFFFFFFF0ull || g.wbytes >= 0xFFFFFFF0ull)
         return -1;
-    const int64_t blocks = ((g.rows + 255) / 256) * ((Co + 63) / 64);
+    const int64_t blocks = ((g.rows + kTN - 1) / kTN) * ((Co + kTM - 1) / kTM);
     if (blocks <= 0 || blocks > 0x7fffffff) return -1;
-    if (elem == 2)
-        hipLaunchKernelGGL(gemm_nt_kernel<true>, dim3((unsigned)blocks), dim3(kGemmThreads), 0,
+    if (elem == 2) {
+        ensure_lds_limit((const void*)gemm_tiled_kernel<true>, kTLds);
+        hipLaunchKernelGGL(gemm_tiled_kernel<true>, dim3((unsigned)blocks), dim3(256), kTLds,
                            stream, b, a, y, g);
-    else
-        hipLaunchKernelGGL(gemm_nt_kernel<false>, dim3((unsigned)blocks), dim3(kGemmThreads), 0,
+    } else {
+        ensure_lds_limit((const void*)gemm_tiled_kernel<false>, kTLds);
+        hipLaunchKernelGGL(gemm_tiled_kernel<false>, dim3((unsigned)blocks), dim3(256), kTLds,
                            stream, b, a, y, g);
+    }
     return launch_status();
 }
 
@@ -244,6 +442,60 @@ int launch_im2col(const void* x, void* col, const ConvShape& c, int elem, hipStr
     const int64_t total = a.rows * a.KP;
     const int64_t blocks = (total + 255) / 256;
     if (blocks <= 0 || blocks > 0x7fffffff) return -1;
+    const int cpr = a.KP * elem / 16;   // KP*elem is a multiple of 32 bytes
+    {
+        // Row-segment kernel when a segment's input rows fit in 80 KB of LDS.
+        ColRArgs r;
+        r.c = c;
+        r.K = a.K;
+        r.KP = a.KP;
+        r.cpr = cpr;
+        const int epu = 4 / elem;
+        r.cols = (std::min(31 * c.sw + c.Wf, c.Wi) + epu - 1) / epu * epu;
+        r.units = r.cols / epu;
+        r.wtiles = (c.Wo + 31) / 32;
+        const int64_t lds = (int64_t)c.Ci * c.Hf * r.cols * elem;
+        const int64_t rblocks = (int64_t)c.N * c.Ho * r.wtiles;
+        if (lds <= 80 * 1024 && rblocks < 0x7fffffff && (uintptr_t)col % 16 == 0 &&
+            c.Wi % epu == 0 && (uintptr_t)x % 4 == 0) {
+            r.divUnits = FastDiv((uint32_t)r.units);
+            r.divCpr = FastDiv((uint32_t)cpr);
+            r.divHW = FastDiv((uint32_t)(c.Hf * c.Wf));
+            r.divWf = FastDiv((uint32_t)c.Wf);
+            if (elem == 2) {
+                ensure_lds_limit((const void*)im2col_rows_kernel<uint16_t>, 80 * 1024);
+                hipLaunchKernelGGL(im2col_rows_kernel<uint16_t>, dim3((unsigned)rblocks), dim3(256),
+                                   (unsigned)lds, stream, (const uint16_t*)x, (uint16_t*)col, r);
+            } else {
+                ensure_lds_limit((const void*)im2col_rows_kernel<uint32_t>, 80 * 1024);
+                hipLaunchKernelGGL(im2col_rows_kernel<uint32_t>, dim3((unsigned)rblocks), dim3(256),
+                                   (unsigned)lds, stream, (const uint32_t*)x, (uint32_t*)col, r);
+            }
+            return launch_status();
+        }
+    }
+    const int ptiles = (cpr + 7) / 8;
+    const int64_t vblocks = (a.rows + 31) / 32 * ptiles;
+    if (a.rows < 0x7fffffff && vblocks < 0x7fffffff && (uintptr_t)col % 16 == 0) {
+        ColVArgs v;
+        v.c = c;
+        v.K = a.K;
+        v.KP = a.KP;
+        v.cpr = cpr;
+        v.ptiles = ptiles;
+        v.rows = (uint32_t)a.rows;
+        v.divPlane = FastDiv((uint32_t)(c.Ho * c.Wo));
+        v.divWo = FastDiv((uint32_t)c.Wo);
+        v.divHW = FastDiv((uint32_t)(c.Hf * c.Wf));
+        v.divWf = FastDiv((uint32_t)c.Wf);
+        if (elem == 2)
+            hipLaunchKernelGGL(im2col_vec_kernel<uint16_t>, dim3((unsigned)vblocks), dim3(256), 0,
+                               stream, (const uint16_t*)x, (uint16_t*)col, v);
+        else
+            hipLaunchKernelGGL(im2col_vec_kernel<uint32_t>, dim3((unsigned)vblocks), dim3(256), 0,
+                               stream, (const uint32_t*)x, (uint32_t*)col, v);
+        return launch_status();
+    }
     if (elem == 2)
         hipLaunchKernelGGL(im2col_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
                            (const uint16_t*)x, (uint16_t*)col, a);

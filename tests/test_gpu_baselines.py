@@ -18,6 +18,8 @@ SHAPES = [
     (1, 3, 47, 45, 37, 11, 11, 4),
     (3, 6, 23, 11, 33, 4, 6, (3, 1)),
     (2, 8, 12, 40, 130, 1, 1, 1),
+    (3, 2, 7, 9, 200, 3, 3, 1),         # K below one stage of the GEMM
+    (2, 24, 20, 20, 64, 5, 5, 1),       # K across several stages and a partial last one
 ]
 
 
@@ -98,25 +100,25 @@ def test_conv_direct(t, dt, orc):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("key", ["cv1_f32_n32", "cv5_f16_n128", "cv4_f16_n64"])
-def test_baselines_full_size_sampled(key, orc):
+def test_baselines_full_size(key, orc):
     """The benchmark layers through im2col + GEMM (cv4: 4.8 GB of im2col
-    rows, in chunks below 4 GiB) and, for cv1 and cv5, direct convolution,
-    at ~2000 outputs the oracle computes one by one."""
+    rows, in chunks below 4 GiB) and, for cv1 and cv5, direct convolution:
+    every output against the oracle on small-integer inputs (exact), into an
+    output pre-filled with NaN."""
     import torch
     dev = device()
     sh = workloads.BY_KEY[key]
     x, w = workloads.make_inputs(sh, seed=1, mode="int")
-    Ho, Wo = m.output_dims(sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s)
-    idx = workloads.sample_output_indices(sh, Ho, Wo, 2000)
-    ref, _ = orc.conv_points(x, w, sh.s, idx)
+    note(f"baselines full size {sh.describe()}: oracle")
+    ref = orc.conv_direct(x, w, sh.s)
     xt, wt = to_dev(x, dev), to_dev(w, dev)
-    sel = torch.from_numpy(idx).to(dev)
+    y = torch.full(ref.shape, float("nan"), dtype=torch.float32, device=dev)
     note(f"conv im2col+GEMM full {sh.describe()}")
-    y = m.conv2d_im2col(xt, wt, sh.s).reshape(-1)
-    assert_exact(y[sel].cpu().numpy(), ref, sh.describe())
-    del y
+    m.conv2d_im2col(xt, wt, sh.s, out=y)
+    assert_exact(y.cpu().numpy(), ref, f"{sh.describe()} im2col")
     if key != "cv4_f16_n64":
         note(f"conv direct full {sh.describe()}")
-        y = m.conv2d_direct(xt, wt, sh.s).reshape(-1)
-        assert_exact(y[sel].cpu().numpy(), ref, sh.describe())
+        y.fill_(float("nan"))
+        m.conv2d_direct(xt, wt, sh.s, out=y)
+        assert_exact(y.cpu().numpy(), ref, f"{sh.describe()} direct")
     torch.cuda.synchronize()
