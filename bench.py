@@ -40,10 +40,17 @@ PEAK_HBM_GBS = 8000.0
 HEADLINE = "cv1_f32_n32"
 LAYER_KEYS = ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64", "cv4_f16_n64",
               "cv2_f32_n32"]
-KERNEL_SOURCES = ["conv_f32_mfma.hip", "conv_f32.hip", "conv_f16_fused.hip", "conv_f16_rows.hip",
-                  "conv_f16_wide.hip", "conv_f16_thin.hip",
-                  "conv_f16.hip", "conv_generic.hip", "pack.hip", "im2col.hip", "nhwc.hip",
-                  "api.hip", "common.hpp", "kernels.hpp"]
+# The source file of each convolution kernel: its counter measurements in
+# profiles/traffic.json stay valid while that file and common.hpp do not
+# change.
+KERNEL_FILE = {"conv_f32_mfma_kernel": "conv_f32_mfma.hip",
+               "conv_f32_small_kernel": "conv_f32_small.hip", "conv_f32_kernel": "conv_f32.hip",
+               "conv_f16_fused_kernel": "conv_f16_fused.hip",
+               "conv_f16_rows_kernel": "conv_f16_rows.hip",
+               "conv_f16_reuse_kernel": "conv_f16_reuse.hip",
+               "conv_f16_thin_kernel": "conv_f16_thin.hip",
+               "conv_f16_wide_kernel": "conv_f16_wide.hip", "conv_f16_ws_kernel": "conv_f16_ws.hip",
+               "conv_f16_kernel": "conv_f16.hip"}
 # Modes: fused (no workspace), fused_valu (fp32 on the vector-ALU kernel),
 # prepacked (fp16 fused with the filter prepacked per call into a small
 # workspace, conv2d_fused), materialized (the im2win tensor of the whole batch
@@ -67,10 +74,17 @@ def flops(sh, Ho, Wo) -> int:
     return 2 * sh.N * sh.Co * Ho * Wo * sh.Ci * sh.Hf * sh.Wf
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources of one convolution kernel (its file and
+    common.hpp); of every library source for a name not in KERNEL_FILE."""
+    csrc = os.path.join(ROOT, "memory_efficient_im2win_amd", "csrc")
+    if kernel in KERNEL_FILE:
+        files = [KERNEL_FILE[kernel], "common.hpp"]
+    else:
+        files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "memory_efficient_im2win_amd", "csrc", f), "rb") as fh:
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -275,16 +289,18 @@ def cpu_baseline(sh, budget_s=12.0):
     }
 
 
-def load_traffic(key, mode):
-    """HBM traffic measured with rocprofv3 counters for the current kernel
-    sources, or None (no measurement, or the kernels changed since)."""
+def load_traffic(key, mode, kernel):
+    """HBM bytes per launch of `kernel` measured with rocprofv3 counters for
+    its current sources, or None (no measurement, another kernel, or its
+    sources changed since)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
     ent = d.get(f"{key}:{mode}")
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("conv_kernel") != kernel or \
+            ent.get("source_hash") != kernel_source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -541,14 +557,15 @@ def roofline_of(key, sh, mode, r):
     kernel; their per-call time includes those launches."""
     bound, peak = peak_of(sh, mode)
     achieved = r["flops"] / (r["ms_per_launch_avg"] * 1e-3) / 1e12
+    kern = kernel_of(sh, mode)
     return {
         "bound": bound,
         "achieved": round(achieved, 3),
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": load_traffic(key, mode),
-        "kernel": kernel_of(sh, mode),
+        "traffic": load_traffic(key, mode, kern),
+        "kernel": kern,
         "launches_per_call": 1 if mode in ("fused", "fused_valu") else 2,
         "launch_avg_us": round(r["ms_per_launch_avg"] * 1e3, 2),
         "launch_median_us": round(r["ms_per_launch_median"] * 1e3, 2),
@@ -630,8 +647,14 @@ def main():
         path = os.path.join(ROOT, "profiles", "traffic.json")
         d = json.load(open(path)) if os.path.exists(path) else {}
         kb = t["kernels"][kern[0]]
+        import memory_efficient_im2win_amd as m
+        m.load_library()
+        name = kernel_of(workloads.BY_KEY[args.workload], args.mode)
+        if name not in kern[0]:
+            raise SystemExit(f"the counters are of {kern[0]}, the planner runs {name}")
         d[f"{args.workload}:{args.mode}"] = {
-            "source_hash": kernel_source_hash(),
+            "conv_kernel": name,
+            "source_hash": kernel_source_hash(name),
             "kernel": kern[0][:120],
             "bytes_per_launch": round(kb["fetch_bytes"] + kb["write_bytes"]),
             "fetch_bytes": round(kb["fetch_bytes"]), "write_bytes": round(kb["write_bytes"]),

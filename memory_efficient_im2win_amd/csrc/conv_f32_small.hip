@@ -59,7 +59,7 @@ struct SArgs {
     uint32_t lds_bytes;
     uint32_t xbytes, wbytes, ybytes;
     bool swz;                 // XCD-grouped tile order
-    FastDiv divWo, divWi, divWq, divRIN;
+    FastDiv divWo, divWi, divWq, divRIN, divHW, divWf;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t sbuf(const void* base, uint32_t bytes)
@@ -85,9 +85,13 @@ __global__ __launch_bounds__(kNT) void conv_f32_small_kernel(const float* __rest
     const int K = a.K, RIN = a.RIN;
     const int plane = Ho * Wo;
 
+    // Tiles numbered pixel tile fastest, so the workgroups one XCD takes
+    // (XCD-grouped order) share a few channel tiles: each XCD's L2 then holds
+    // a slice of the filter instead of all of it.
     const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, a.swz);
-    const int co_t = (int)(bid % a.co_tiles);
-    const int rest = (int)(bid / a.co_tiles);
+    const int pts = a.c.N * a.pt_img;
+    const int co_t = (int)(bid / pts);
+    const int rest = (int)(bid - (int64_t)co_t * pts);
     const int n = rest / a.pt_img;
     const int pt = rest - n * a.pt_img;
     const int co0 = co_t * kCoT;
@@ -185,8 +189,8 @@ __global__ __launch_bounds__(kNT) void conv_f32_small_kernel(const float* __rest
         for (int k = tid; k < 16 * a.KC; k += kNT) {
             int t = a.xent;
             if (k < K) {
-                const int c = k / HW, rem = k - c * HW;
-                const int kh = rem / Wf, kw = rem - kh * Wf;
+                const int c = (int)a.divHW.div((uint32_t)k), rem = k - c * HW;
+                const int kh = (int)a.divWf.div((uint32_t)rem), kw = rem - kh * Wf;
                 t = (c * RIN + kh) * Wi + kw;
             }
             Tw[k] = t;
@@ -290,6 +294,8 @@ bool plan(const ConvShape& c, SArgs& a, int& cpw)
     a.divWi = FastDiv((uint32_t)c.Wi);
     a.divWq = FastDiv((uint32_t)std::max(1, c.Wi / 4));
     a.divRIN = FastDiv((uint32_t)a.RIN);
+    a.divHW = FastDiv((uint32_t)(c.Hf * c.Wf));
+    a.divWf = FastDiv((uint32_t)c.Wf);
     a.swz = knob(KNOB_TILE_ORDER) != 1;
     return true;
 }
