@@ -646,7 +646,7 @@ struct Choice {
     const void* f;
     size_t lds;
     int occ;          // workgroups that fit on a CU
-    int64_t grid;     // persistent workgroups
+    int64_t grid = 0; // persistent workgroups
     double cost;
     int wps;          // waves per SIMD
 };
@@ -702,7 +702,7 @@ bool choose(const ConvShape& c, Choice& ch)
         t.occ = blocks_per_cu(t.f, 64 * nw, t.lds);
         if (t.occ < 1) return false;
         size_grid(t, ncu);
-        return true;
+        return t.wps > 0;   // false if a forced occupancy does not fit
     };
     auto better = [&](const Choice& t) {
         return t.cost < ch.cost * (1 - 1e-9) || (t.cost < ch.cost * (1 + 1e-9) && t.wps > ch.wps);
@@ -772,6 +772,7 @@ int launch_conv_f32_mfma(const float* x, const float* w, float* y, const ConvSha
         const int rc = launch_conv_f32_small(x, w, y, c, stream);
         if (rc != -1) return rc;
     }
+    if (ch.grid < 1 || ch.grid > 0x7fffffff) return -1;
     MArgs args = ch.a;
     args.swz = knob(KNOB_TILE_ORDER) != 1;
     args.sync = knob(KNOB_SYNC_STAGING) == 1;

@@ -194,6 +194,29 @@ def test_conv_f32_matrix_waves(t, nw, orc, knob):
     assert_exact(_run(sh, "f32", xi, wi), orc.conv_direct(xi, wi, sh.s), sh.describe())
 
 
+@pytest.mark.parametrize("kn", [{"f32_wco": 1}, {"f32_wco": 2}, {"f32_wco": 3}, {"f32_wco": 4},
+                                {"f32_cb": 1}, {"f32_cb": 3}, {"f32_occ": 2}], ids=str)
+@pytest.mark.parametrize("t", [(2, 3, 227, 227, 96, 11, 11, 4), (2, 16, 30, 30, 130, 5, 5, (2, 1))],
+                         ids=str)
+def test_conv_f32_matrix_tilings(t, kn, orc, knob):
+    """The fp32 matrix-core kernel with its channel tile (32*WCO channels),
+    channels per stage and workgroups per CU forced (the small-problem kernel
+    off, so the tiled kernel runs)."""
+    knob("f32_small", -1)
+    for k, v in kn.items():
+        knob(k, v)
+    sh = _shape(t, "f32")
+    device()
+    assert m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 4) == \
+        "conv_f32_mfma_kernel"
+    x, w = workloads.make_inputs(sh, seed=22)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    note(f"conv fp32 matrix tiling {kn} {sh.describe()}")
+    assert_within(_run(sh, "f32", x, w), ref, absd, TOL["f32"], sh.describe())
+    xi, wi = workloads.make_inputs(sh, seed=23, mode="int")
+    assert_exact(_run(sh, "f32", xi, wi), orc.conv_direct(xi, wi, sh.s), sh.describe())
+
+
 @pytest.mark.parametrize("env", [{"f16_wpx": 8}, {"f16_wpx": 1}, {"f16_nwh": 3}], ids=str)
 @pytest.mark.parametrize("t", [(1, 64, 30, 30, 64, 7, 7, 2), (2, 24, 14, 14, 96, 5, 5, 1),
                                (2, 3, 47, 45, 37, 7, 7, 2), (2, 12, 26, 40, 70, 3, 7, 2),
