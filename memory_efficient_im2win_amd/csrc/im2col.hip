@@ -10,8 +10,8 @@
 //        col[q][(ci*Hf + kh)*Wf + kw] = x[n][ci][ho*sh + kh][wo*sw + kw].
 //    That is the transpose of the usual K x P layout, with the same size; it
 //    makes each MFMA operand slice one contiguous 16-byte load.
-//    A workgroup writes the rows of 32 consecutive pixels of one output row
-//    from their input rows staged in LDS; shapes whose rows do not fit fall
+//    A workgroup writes the rows of up to 32 consecutive pixels of one
+//    output row from their input rows staged in LDS; shapes whose rows do not fit fall
 //    back to 128-byte column tiles of 32 rows, one 16-byte piece per thread.
 //  * filter_pad_kernel copies the filters into rows of KP (zero tail).
 //  * gemm_tiled_kernel computes y[n][co][p] = sum_k w[co][k] * col[q][k] on
@@ -125,17 +125,21 @@ __global__ __launch_bounds__(256) void im2col_vec_kernel(const T* __restrict__ x
     reinterpret_cast<uint4*>(col)[(int64_t)q * a.cpr + piece] = o;
 }
 
+constexpr int64_t kColLds = 40 * 1024;
+
 struct ColRArgs {
     ConvShape c;
     int K, KP, cpr;           // taps, padded row, 16-byte pieces per row
-    int cols;                 // LDS row pitch: 31*sw + Wf rounded up to whole dwords
-    int wtiles;               // 32-pixel segments per output row
+    int cols;                 // LDS row pitch: (seg-1)*sw + Wf rounded up to whole dwords
+    int seg;                  // pixels per row segment
+    int wtiles;               // segments per output row
     int units;                // dwords per LDS row (cols * sizeof(T) / 4)
     FastDiv divCpr, divHW, divWf, divUnits;
 };
 
-// A workgroup writes the im2col rows of 32 consecutive pixels of one output
-// row (npx <= 32 rows, contiguous in col): it first copies the input rows
+// A workgroup writes the im2col rows of a segment of seg (32, 16 or 8)
+// consecutive pixels of one output row (npx <= seg rows, contiguous in
+// col): it first copies the input rows
 // their windows cover, every channel, columns c0 .. c0 + cols - 1, into LDS
 // ([ci][kh][col]); then consecutive threads build consecutive 16-byte
 // pieces of those rows from LDS, so every store instruction writes 1 KB of
@@ -152,8 +156,8 @@ __global__ __launch_bounds__(256) void im2col_rows_kernel(const T* __restrict__ 
     const int wt = (int)(blockIdx.x % (uint32_t)a.wtiles);
     const int rest = (int)(blockIdx.x / (uint32_t)a.wtiles);
     const int ho = rest % Ho, n = rest / Ho;
-    const int w0 = wt * 32;
-    const int npx = min(32, Wo - w0);
+    const int w0 = wt * a.seg;
+    const int npx = min(a.seg, Wo - w0);
     const int c0 = w0 * sw;
     const int ncol = min(a.cols, Wi - c0);
 
@@ -451,10 +455,17 @@ int launch_im2col(const void* x, void* col, const ConvShape& c, int elem, hipStr
         r.KP = a.KP;
         r.cpr = cpr;
         const int epu = 4 / elem;
-        r.cols = (std::min(31 * c.sw + c.Wf, c.Wi) + epu - 1) / epu * epu;
+        // The longest segment (32, 16 or 8 pixels) whose rows take at most
+        // 40 KB of LDS, so that four workgroups share a CU.
+        int64_t lds = 0;
+        for (int seg : {32, 16, 8}) {
+            r.seg = seg;
+            r.cols = (std::min((seg - 1) * c.sw + c.Wf, c.Wi) + epu - 1) / epu * epu;
+            lds = (int64_t)c.Ci * c.Hf * r.cols * elem;
+            if (lds <= kColLds) break;
+        }
         r.units = r.cols / epu;
-        r.wtiles = (c.Wo + 31) / 32;
-        const int64_t lds = (int64_t)c.Ci * c.Hf * r.cols * elem;
+        r.wtiles = (c.Wo + r.seg - 1) / r.seg;
         const int64_t rblocks = (int64_t)c.N * c.Ho * r.wtiles;
         if (lds <= 80 * 1024 && rblocks < 0x7fffffff && (uintptr_t)col % 16 == 0 &&
             c.Wi % epu == 0 && (uintptr_t)x % 4 == 0) {
