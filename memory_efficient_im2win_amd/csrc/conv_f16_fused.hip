@@ -67,16 +67,11 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi)
     return (uint32_t)lo | ((uint32_t)hi << 16);
 }
 
-// Raw buffer resource over [base, base + bytes) (gfx9-family descriptor).
-// Loads at soffset + voffset >= bytes return 0, which the kernel uses instead
+// Buffer resources (raw_rsrc) cover [base, base + bytes): loads at
+// soffset + voffset >= bytes return 0, which the kernel uses instead
 // of per-lane branches; every load that can miss has soffset 0 and voffset
 // kNoOff, which is out of range for any buffer the planner accepts.
 constexpr uint32_t kNoOff = 0xFFFFFFF0u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
 
 // Filters of channel group g as 16-byte entries (tap j, channel co):
 // wpk[(g*HWp + j)*Copad + co] = w[co][8g..8g+7][j], zero beyond Co, Ci, HW.
@@ -314,8 +309,8 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int64_t first = (int64_t)(cbx + q) * cstride * 2;
-                pl[q] = buf(x + (int64_t)(cbx + q < Ci ? cbx + q : 0) * cstride,
-                            cbx + q < Ci ? (uint32_t)(a.xbytes - first) : 0u);
+                pl[q] = raw_rsrc(x + (int64_t)(cbx + q < Ci ? cbx + q : 0) * cstride,
+                                 cbx + q < Ci ? (uint32_t)(a.xbytes - first) : 0u);
             }
 #pragma unroll
             for (int u = 0; u < NXU; ++u) {
@@ -339,7 +334,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
         if (WPK) {
             // Taps j0 .. HWp-1 of group g; entries past HWp read as zero.
             const __amdgpu_buffer_rsrc_t wb =
-                buf(wpk + ((int64_t)g * HWp + j0) * a.Copad, (uint32_t)((HWp - j0) * a.Copad * 16));
+                raw_rsrc(wpk + ((int64_t)g * HWp + j0) * a.Copad, (uint32_t)((HWp - j0) * a.Copad * 16));
 #pragma unroll
             for (int u = 0; u < kWEnt; ++u) {
                 const auto v = __builtin_amdgcn_raw_buffer_load_b128(wb, (int)woff[u], 0, 0);
@@ -349,7 +344,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
             // Gather from w: tap j0 + jj of channel cb + q is (q*HW + j0)*2 bytes
             // past the entry's offset; missing taps and channels read as zero.
             const __amdgpu_buffer_rsrc_t wb =
-                buf(w, (uint32_t)((int64_t)Co * Ci * HW * 2));
+                raw_rsrc(w, (uint32_t)((int64_t)Co * Ci * HW * 2));
 #pragma unroll
             for (int u = 0; u < kWEnt; ++u) {
                 const int jj = (tid + u * NT) / COT;
@@ -518,7 +513,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_f16_fused_kernel(
     // writes 256 contiguous bytes of one channel plane.
     static_assert(NB % 2 == 0, "blocks are stored in pairs");
     const int64_t plane = (int64_t)Ho * Wo;
-    const __amdgpu_buffer_rsrc_t yb = buf(y, a.ybytes);
+    const __amdgpu_buffer_rsrc_t yb = raw_rsrc(y, a.ybytes);
     const bool all_co = co0 + COT <= Co;
 #pragma unroll
     for (int p = 0; p < NB / 2; ++p) {

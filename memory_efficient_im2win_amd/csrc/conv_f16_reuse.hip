@@ -78,34 +78,8 @@ struct ReuseArgs {
     FastDiv divWo, divG;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rbuf(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
 
-// 16 bytes per lane from buffer r at vector offset voff into LDS at byte
-// lds + 16*lane (lds wave-uniform); an out-of-range lane writes zeros. M0 is
-// saved and restored around the load, which waits for nothing (the waits
-// below are explicit).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff)
-{
-    uint32_t save;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save)
-        : "s"(lds), "v"(voff), "s"(r)
-        : "memory");
-}
 
-template <int N>
-__device__ __forceinline__ void wait_loads()
-{
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 template <int NWV, int DMAX, int HF, int SH, bool WPK>
 __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t* __restrict__ x,
@@ -221,21 +195,21 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
         const uint32_t fo = (uint32_t)s * a.S * a.Copad * 16;
         const int64_t xo = (int64_t)s * a.Cg * Hi * Wi;
         const __amdgpu_buffer_rsrc_t ra =
-            rbuf(wp + (int64_t)s * a.S * a.Copad, WPK ? a.wbytes - fo : 0u);
-        const __amdgpu_buffer_rsrc_t rx = rbuf(x + xo, a.xbytes - (uint32_t)(xo * 2));
+            raw_rsrc(wp + (int64_t)s * a.S * a.Copad, WPK ? a.wbytes - fo : 0u);
+        const __amdgpu_buffer_rsrc_t rx = raw_rsrc(x + xo, a.xbytes - (uint32_t)(xo * 2));
         const uint32_t base = lbase + (uint32_t)sb * a.stage_bytes;
 #pragma unroll
         for (int i = 0; i < DMAX; ++i) {
             const int m = wave + NWV * i;
             const bool real = m < a.S + a.NX && (WPK || m >= a.S);
             const uint32_t dst = real ? base + (uint32_t)m * 1024 : lbase + a.dummy;
-            dma16(m < a.S ? ra : rx, dst, voff[i]);
+            lds_dma16(m < a.S ? ra : rx, dst, voff[i]);
         }
     };
     auto issue_none = [&]() {
-        const __amdgpu_buffer_rsrc_t rx = rbuf(x, a.xbytes);
+        const __amdgpu_buffer_rsrc_t rx = raw_rsrc(x, a.xbytes);
 #pragma unroll
-        for (int i = 0; i < DMAX; ++i) dma16(rx, lbase + a.dummy, kMiss);
+        for (int i = 0; i < DMAX; ++i) lds_dma16(rx, lbase + a.dummy, kMiss);
     };
     // Without direct loads (sync): the same slots copied through registers
     // into buffer sb, four slots at a time, each wave waiting for its loads.
@@ -243,8 +217,8 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
         const uint32_t fo = (uint32_t)s * a.S * a.Copad * 16;
         const int64_t xo = (int64_t)s * a.Cg * Hi * Wi;
         const __amdgpu_buffer_rsrc_t ra =
-            rbuf(wp + (int64_t)s * a.S * a.Copad, WPK ? a.wbytes - fo : 0u);
-        const __amdgpu_buffer_rsrc_t rx = rbuf(x + xo, a.xbytes - (uint32_t)(xo * 2));
+            raw_rsrc(wp + (int64_t)s * a.S * a.Copad, WPK ? a.wbytes - fo : 0u);
+        const __amdgpu_buffer_rsrc_t rx = raw_rsrc(x + xo, a.xbytes - (uint32_t)(xo * 2));
         unsigned char* base = smem + (size_t)sb * a.stage_bytes;
 #pragma unroll
         for (int i0 = 0; i0 < DMAX; i0 += 4) {
@@ -357,7 +331,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
     // sg holds the taps of w[co0 + j][sg*Cg + m/HF][m%HF][*] (zeros past Wf
     // and Co).
     auto gather = [&](int sg, int sb) {
-        const __amdgpu_buffer_rsrc_t rw = rbuf(w, a.worig);
+        const __amdgpu_buffer_rsrc_t rw = raw_rsrc(w, a.worig);
         uint4* F = reinterpret_cast<uint4*>(smem + (size_t)sb * a.stage_bytes);
         const int ne = a.S * 64;
         for (int e0 = 0; e0 < ne; e0 += 2 * NT) {
@@ -393,7 +367,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
     uint32_t gv[kGL];
     const int gj0 = tid / (int)a.RD, gq0 = tid - gj0 * (int)a.RD;
     auto gather_load = [&](int sg) {
-        const __amdgpu_buffer_rsrc_t rw = rbuf(w, a.worig);
+        const __amdgpu_buffer_rsrc_t rw = raw_rsrc(w, a.worig);
         const uint32_t base = (uint32_t)co0 * a.wco + (uint32_t)sg * a.RD * 4;
         int j = gj0, r = gq0;
         asm volatile("" : "+v"(j), "+v"(r));
@@ -478,7 +452,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
         } else {
             // This wave's loads of stage s have landed (those of stage s+1
             // may still be in flight).
-            wait_loads<DMAX>();
+            wait_vm<DMAX>();
             __syncthreads();      // every wave's; and stage s-1's buffer is free
             if (s + 2 < a.NS) issue(s + 2, (s + 2) % kBufs); else issue_none();
             if (coal && s + 2 < a.NS) gather_load(s + 2);
@@ -494,14 +468,14 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
                 gather(s + 2, (s + 2) % kBufs);
         }
     }
-    wait_loads<0>();   // the last (unused) loads have landed before the workgroup ends
+    wait_vm<0>();   // the last (unused) loads have landed before the workgroup ends
 
     // Output: lane holds, for each of its J pixels (n, g*J + j, wo), channels
     // 8*(r/4) + 4*hl + r%4 of each 32-channel block; every store writes 32
     // consecutive pixels of one output row into each of two channel planes.
     if (!pok) return;
     const int64_t plane = (int64_t)Ho * Wo;
-    const __amdgpu_buffer_rsrc_t yb = rbuf(y, a.ybytes);
+    const __amdgpu_buffer_rsrc_t yb = raw_rsrc(y, a.ybytes);
     const bool all_co = co0 + kCoT <= Co;
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {

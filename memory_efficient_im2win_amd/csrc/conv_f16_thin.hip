@@ -77,26 +77,7 @@ struct ThinArgs {
     bool sync;                      // filter copied through registers
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tbuf(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
 
-// 16 bytes per lane from buffer r at vector offset voff into LDS at byte
-// lds + 16*lane (lds wave-uniform); M0 is saved and restored around it.
-__device__ __forceinline__ void dma16t(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff)
-{
-    uint32_t save;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save)
-        : "s"(lds), "v"(voff), "s"(r)
-        : "memory");
-}
 
 // NB: 32-pixel blocks per wave (2 x NB register tiles; NB = 2 leaves room
 // for four workgroups per CU, NB = 4 for two). XVEC: Wi % 8 == 0 and x
@@ -185,7 +166,7 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
     // sync copies the filter through registers instead of loading it
     // straight into LDS.
     if (WPK && a.sync) {
-        const __amdgpu_buffer_rsrc_t r = tbuf(wp, a.wbytes);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(wp, a.wbytes);
 #pragma unroll 4
         for (int m = wave; m < a.S; m += kNW) {
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(
@@ -194,16 +175,16 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
                 make_uint4(v[0], v[1], v[2], v[3]);
         }
     } else if (WPK) {
-        const __amdgpu_buffer_rsrc_t r = tbuf(wp, a.wbytes);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(wp, a.wbytes);
         for (int m = wave; m < a.S; m += kNW)
-            dma16t(r, lbase + (uint32_t)m * 1024, (uint32_t)((m * a.Copad + co0 + lane) * 16));
+            lds_dma16(r, lbase + (uint32_t)m * 1024, (uint32_t)((m * a.Copad + co0 + lane) * 16));
     } else if (a.gd) {
         // The tile's 64 channels' taps are one run of w: consecutive
         // threads read consecutive dwords of it, and each half goes to its
         // entry (channel j = f / chw of the tile, slice t / Wf, column
         // t % Wf, t = f % chw). Channels past Co fall outside w's range and
         // read zeros; the halves kw >= Wf of every entry are zeroed here too.
-        const __amdgpu_buffer_rsrc_t r = tbuf(w, a.worig);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(w, a.worig);
         unsigned short* F = reinterpret_cast<unsigned short*>(smem);
         const uint32_t base = (uint32_t)co0 * a.chw * 2;
         const int nd = 32 * (int)a.chw;
@@ -238,7 +219,7 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
             for (int e = tid; e < a.S * 64; e += kNT)
                 for (int kw = a.c.Wf; kw < 8; ++kw) F[e * 8 + kw] = 0;
     } else {
-        const __amdgpu_buffer_rsrc_t r = tbuf(w, a.worig);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(w, a.worig);
         uint4* F = reinterpret_cast<uint4*>(smem);
         const int ne = a.S * 64;
         for (int e0 = 0; e0 < ne; e0 += 4 * kNT) {
@@ -281,7 +262,7 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
     // row i of channel cl (zeros past Wi and where no input row maps).
     {
         uint4* X = reinterpret_cast<uint4*>(smem + a.xoff);
-        const __amdgpu_buffer_rsrc_t rx = tbuf(x, a.xbytes);
+        const __amdgpu_buffer_rsrc_t rx = raw_rsrc(x, a.xbytes);
         for (int e0 = 0; e0 < a.chunks; e0 += kBatch * kNT) {
             uint4 v[kBatch];
 #pragma unroll
@@ -409,7 +390,7 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
     // writes 256 contiguous bytes of one channel plane (32-pixel stores into
     // two planes made the HBM writes about 1.3x the output).
     const int64_t plane = (int64_t)Ho * Wo;
-    const __amdgpu_buffer_rsrc_t yb = tbuf(y, a.ybytes);
+    const __amdgpu_buffer_rsrc_t yb = raw_rsrc(y, a.ybytes);
     const bool all_co = co0 + kCoT <= Co;
 #pragma unroll
     for (int p = 0; p < kNB / 2; ++p) {

@@ -66,28 +66,7 @@ struct WideArgs {
     bool sync;                      // groups copied through registers, one buffer
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t wbuf(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
 
-// 16 bytes per lane from buffer r at vector offset voff into LDS at byte
-// lds + 16*lane (lds wave-uniform). Issued from inline assembly so that the
-// compiler does not wait for it before unrelated LDS reads; M0 is saved and
-// restored around it.
-__device__ __forceinline__ void dma16w(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff)
-{
-    uint32_t save;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save)
-        : "s"(lds), "v"(voff), "s"(r)
-        : "memory");
-}
 
 // NW waves of NB 32-pixel blocks each (NW * NB * 32 = kPW). WPK: the filter
 // comes prepacked (wpk); otherwise each stage gathers its entries from w.
@@ -207,7 +186,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int64_t first = (int64_t)(cb + q) * cstride * 2;
-            pl[q] = wbuf(x + (int64_t)(cb + q < Ci ? cb + q : 0) * cstride,
+            pl[q] = raw_rsrc(x + (int64_t)(cb + q < Ci ? cb + q : 0) * cstride,
                          cb + q < Ci ? (uint32_t)(a.xbytes - first) : 0u);
         }
 #pragma unroll
@@ -255,17 +234,17 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
     // + lane of the prepacked filter. Wave v issues kilobytes v, v+4, ...
     auto dma_w = [&](int g, int sb) {
         const uint32_t go = (uint32_t)g * a.HWp * a.Copad * 16;
-        const __amdgpu_buffer_rsrc_t r = wbuf(wpk + (int64_t)g * a.HWp * a.Copad, a.wbytes - go);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(wpk + (int64_t)g * a.HWp * a.Copad, a.wbytes - go);
         const uint32_t dst = lbase + (uint32_t)sb * a.stage_bytes;
         const uint32_t lo = (uint32_t)(co0 + lane) * 16;
         for (int m = wave; m < a.S; m += kWavesW)
-            dma16w(r, dst + (uint32_t)m * 1024,
+            lds_dma16(r, dst + (uint32_t)m * 1024,
                    lo + (uint32_t)(m >> 1) * a.Copad * 16 + (uint32_t)(m & 1) * 1024);
     };
     // The same kilobytes copied through registers (synchronous staging).
     auto copy_w = [&](int g, int sb) {
         const uint32_t go = (uint32_t)g * a.HWp * a.Copad * 16;
-        const __amdgpu_buffer_rsrc_t r = wbuf(wpk + (int64_t)g * a.HWp * a.Copad, a.wbytes - go);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(wpk + (int64_t)g * a.HWp * a.Copad, a.wbytes - go);
         unsigned char* dst = smem + (size_t)sb * a.stage_bytes + 16 * lane;
         const uint32_t lo = (uint32_t)(co0 + lane) * 16;
 #pragma unroll 4
@@ -282,7 +261,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
     auto gather_w = [&](int g, int sb) {
         constexpr int NPR = 8 * kCoW / kNTW;   // (k, c) pairs per thread
         constexpr int JC = 32 / NPR;           // taps per chunk
-        const __amdgpu_buffer_rsrc_t r = wbuf(w, a.worig);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(w, a.worig);
         unsigned short* F = reinterpret_cast<unsigned short*>(smem + (size_t)sb * a.stage_bytes);
         uint32_t base[NPR];
         int dst[NPR];
@@ -449,7 +428,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
     // writes 256 contiguous bytes of one channel plane (32-pixel stores into
     // two planes made the HBM writes about 1.3x the output).
     const int64_t plane = (int64_t)Ho * Wo;
-    const __amdgpu_buffer_rsrc_t yb = wbuf(y, a.ybytes);
+    const __amdgpu_buffer_rsrc_t yb = raw_rsrc(y, a.ybytes);
     const bool all_co = co0 + kCoW <= Co;
 #pragma unroll
     for (int p = 0; p < kNBW / 2; ++p) {

@@ -68,33 +68,8 @@ struct WsArgs {
     FastDiv divWo, divHo, divPlane;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rbuf(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
 
-// 16 bytes per lane from buffer r at vector offset voff into LDS at byte
-// lds + 16*lane (lds wave-uniform); an out-of-range lane writes zeros. M0 is
-// saved and restored around the load; the waits are explicit.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff)
-{
-    uint32_t save;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save)
-        : "s"(lds), "v"(voff), "s"(r)
-        : "memory");
-}
 
-template <int N>
-__device__ __forceinline__ void wait_loads()
-{
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 template <int NWV, int DMAX, bool ODD>
 __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* __restrict__ ws,
@@ -203,24 +178,24 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
     }
     auto issue = [&](int s, int sb) {
         const int64_t xo = (int64_t)s * a.Cg * Ho * L;
-        const __amdgpu_buffer_rsrc_t rx = rbuf(ws + xo, a.wsbytes - (uint32_t)(xo * 2));
+        const __amdgpu_buffer_rsrc_t rx = raw_rsrc(ws + xo, a.wsbytes - (uint32_t)(xo * 2));
         const uint32_t base = lbase + (uint32_t)sb * a.stage_bytes;
 #pragma unroll
         for (int i = 0; i < DMAX; ++i) {
             const int m = wave + NWV * i;
-            dma16(rx, m < a.NX ? base + (uint32_t)(a.S + m) * 1024 : lbase + a.dummy, voff[i]);
+            lds_dma16(rx, m < a.NX ? base + (uint32_t)(a.S + m) * 1024 : lbase + a.dummy, voff[i]);
         }
     };
     auto issue_none = [&]() {
-        const __amdgpu_buffer_rsrc_t rx = rbuf(ws, a.wsbytes);
+        const __amdgpu_buffer_rsrc_t rx = raw_rsrc(ws, a.wsbytes);
 #pragma unroll
-        for (int i = 0; i < DMAX; ++i) dma16(rx, lbase + a.dummy, kMiss);
+        for (int i = 0; i < DMAX; ++i) lds_dma16(rx, lbase + a.dummy, kMiss);
     };
     // Without direct loads (sync): the same row kilobytes copied through
     // registers into buffer sb, four at a time.
     auto copy_stage = [&](int s, int sb) {
         const int64_t xo = (int64_t)s * a.Cg * Ho * L;
-        const __amdgpu_buffer_rsrc_t rx = rbuf(ws + xo, a.wsbytes - (uint32_t)(xo * 2));
+        const __amdgpu_buffer_rsrc_t rx = raw_rsrc(ws + xo, a.wsbytes - (uint32_t)(xo * 2));
         unsigned char* base = smem + (size_t)sb * a.stage_bytes + (size_t)a.S * 1024 + 16 * lane;
 #pragma unroll
         for (int i0 = 0; i0 < DMAX; i0 += 4) {
@@ -245,7 +220,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
     // slice for window position jj = 8*(m % M) + p = kw*Hf + kh (zeros past
     // Wf*Hf and past Co).
     auto gather = [&](int sg, int sb) {
-        const __amdgpu_buffer_rsrc_t rw = rbuf(w, a.worig);
+        const __amdgpu_buffer_rsrc_t rw = raw_rsrc(w, a.worig);
         uint4* F = reinterpret_cast<uint4*>(smem + (size_t)sb * a.stage_bytes);
         const int ne = a.S * 64;
         for (int e0 = 0; e0 < ne; e0 += 2 * NT) {
@@ -362,7 +337,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
         } else {
             // This wave's loads of stage s have landed, and (barrier) every
             // wave's, and every wave is done with stage s-1's buffer.
-            wait_loads<0>();
+            wait_vm<0>();
             __syncthreads();
             if (s + 1 < a.NS) issue(s + 1, (s + 1) % kBufs); else issue_none();
         }
@@ -388,7 +363,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
         // The next stage's filter goes to the buffer freed by the barrier.
         if (!sync && s + 1 < a.NS) gather(s + 1, (s + 1) % kBufs);
     }
-    wait_loads<0>();
+    wait_vm<0>();
 
     // Output: lane holds pixel l32 of each block and channels
     // 8*(r/4) + 4*hl + r%4 of each 32-channel block. Blocks 2p and 2p+1 of a
@@ -396,7 +371,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
     // lanes 0-31 of the second (v_permlane32_swap) gives one register with
     // channel cu for all 64 pixels and one with channel cu+4, so every store
     // writes 256 contiguous bytes of one channel plane.
-    const __amdgpu_buffer_rsrc_t yb = rbuf(y, a.ybytes);
+    const __amdgpu_buffer_rsrc_t yb = raw_rsrc(y, a.ybytes);
     const bool all_co = co0 + kCoT <= Co;
 #pragma unroll
     for (int p = 0; p < kNB / 2; ++p) {

@@ -64,15 +64,11 @@ struct MArgs {
     FastDiv divWo, divHo, divS;
 };
 
-// Raw buffer resource over [base, base + bytes): loads at soffset + voffset
-// + offset >= bytes return 0 (the scalar offset counts in the range check).
+// Buffer resources (raw_rsrc) cover [base, base + bytes): loads at soffset +
+// voffset + offset >= bytes return 0 (the scalar offset counts in the range
+// check).
 // The staging loads below use one resource per tensor, so a load past the
 // end of a row reads the next row (or 0 past the tensor) and is not stored.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
 
 template <int NW, int KSW, int WCO, int XCH, int WCH>
 __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
@@ -201,7 +197,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
     float xv[RPW][XCH];
     float wv[WRW][WCH];
     const uint32_t wpitch = (uint32_t)Ci * HW * 4;   // bytes between filters
-    const __amdgpu_buffer_rsrc_t xr = buf(x, a.xbytes);
+    const __amdgpu_buffer_rsrc_t xr = raw_rsrc(x, a.xbytes);
 
     auto load_stage = [&](int st) {
         const int ci0 = st * CB;
@@ -222,7 +218,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
         // stored). Filters past Co read zeros (offset past the end).
         const int64_t wfirst = ((int64_t)L.co0 * Ci + ci0) * HW;
         const uint32_t wrange = a.wbytes - (uint32_t)(wfirst * 4);
-        const __amdgpu_buffer_rsrc_t wr = buf(w + wfirst, wrange);
+        const __amdgpu_buffer_rsrc_t wr = raw_rsrc(w + wfirst, wrange);
         int nco = Co - L.co0;   // filters left from co0
         asm volatile("" : "+s"(nco));
 #pragma unroll
@@ -393,7 +389,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f32_mfma_kernel(
         const bool all_co = co0 + COT <= Co;
         // Byte offset = per-lane part (image, pixel, 4*hl channels) +
         // uniform part (channel block row).
-        const __amdgpu_buffer_rsrc_t yb = buf(y, a.ybytes);
+        const __amdgpu_buffer_rsrc_t yb = raw_rsrc(y, a.ybytes);
         const uint32_t voff =
             (uint32_t)((((int64_t)n * Co + 4 * hl) * plane + (int64_t)ho * Wo + wo) * 4);
         if (qok) {

@@ -62,11 +62,6 @@ struct SArgs {
     FastDiv divWo, divWi, divWq, divRIN, divHW, divWf;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t sbuf(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
 
 // CPW: chunks per wave at most; AVEC: K % 4 == 0 (16-byte filter loads);
 // XVEC: Wi % 4 == 0 (16-byte row copies).
@@ -109,7 +104,7 @@ __global__ __launch_bounds__(kNT) void conv_f32_small_kernel(const float* __rest
 
     // ---- filter values of this wave's chunks [qa, qb), into registers ------
     const int qa = wave * a.KC / kNW, qb = (wave + 1) * a.KC / kNW;
-    const __amdgpu_buffer_rsrc_t wr = sbuf(w, a.wbytes);
+    const __amdgpu_buffer_rsrc_t wr = raw_rsrc(w, a.wbytes);
     const bool co_ok = co0 + j < Co;
     const uint32_t rowoff = (uint32_t)(co0 + j) * (uint32_t)K * 4;
     float av[CPW][4];
@@ -134,7 +129,7 @@ __global__ __launch_bounds__(kNT) void conv_f32_small_kernel(const float* __rest
     // ---- input rows row0 .. row0 + nrows - 1 of every channel -> LDS --------
     // Entry (c*RIN + r)*Wi + col; rows past nrows are not written (no pixel of
     // the tile reads them).
-    const __amdgpu_buffer_rsrc_t xr = sbuf(x, a.xbytes);
+    const __amdgpu_buffer_rsrc_t xr = raw_rsrc(x, a.xbytes);
     const int64_t img = (int64_t)n * Ci * Hi * Wi;
     if (XVEC) {
         const int wq = Wi >> 2;
@@ -245,7 +240,7 @@ __global__ __launch_bounds__(kNT) void conv_f32_small_kernel(const float* __rest
         const int co = co0 + 4 * (l >> 4) + r;
         const int p = p0 + 16 * b + (l & 15);
         if (co < Co && p < pend) {
-            const __amdgpu_buffer_rsrc_t yr = sbuf(y, a.ybytes);
+            const __amdgpu_buffer_rsrc_t yr = raw_rsrc(y, a.ybytes);
             __builtin_amdgcn_raw_buffer_store_b32(
                 __float_as_uint(s), yr, (int)((((int64_t)n * Co + co) * plane + p) * 4), 0, 0);
         }
