@@ -530,6 +530,99 @@ def fill_rate(key, sh, steps, warmup):
             "copy_TBps_read_plus_write": round(2 * n * 4 / c_us / 1e6, 3)}
 
 
+# Rates measured on this chip by measured_peaks() (filled in by main()).
+MEASURED = {}
+PROBE_ITERS = {"fp32_vector": 9000, "fp32_mfma": 4500, "fp16_mfma": 8000}
+
+
+def measured_peaks():
+    """The rates the chip sustains for each kind of arithmetic (the library's
+    register-only rate probe, best of 2 and 4 waves per SIMD, 5 launches
+    timed with HIP events after 2 warm-up) and the HBM rates of a 1 GiB fill
+    and copy: the measured peaks beside the published ones."""
+    import torch
+    import memory_efficient_im2win_amd as m
+    res = {}
+    for kind, iters in PROBE_ITERS.items():
+        best = 0.0
+        for blocks in (512, 1024):
+            out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            for _ in range(2):
+                m.peak_probe(kind, blocks, iters, out)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            ev[0].record()
+            flops = 0.0
+            for _ in range(5):
+                flops += m.peak_probe(kind, blocks, iters, out)[1]
+            ev[1].record()
+            torch.cuda.synchronize()
+            best = max(best, flops / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12)
+        res[kind + "_TFLOPs"] = round(best, 1)
+    n = 1 << 28
+    a = torch.empty(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        a.fill_(1.0)
+        b.copy_(a)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(5):
+        a.fill_(1.0)
+    ev[1].record()
+    for _ in range(5):
+        b.copy_(a)
+    ev[2].record()
+    torch.cuda.synchronize()
+    res["hbm_fill_GBps"] = round(5 * n * 4 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9, 1)
+    res["hbm_copy_GBps"] = round(5 * 2 * n * 4 / (ev[1].elapsed_time(ev[2]) * 1e-3) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
+def measured_peak_of(sh, mode):
+    """The measured rate of the arithmetic unit a layer's kernel runs on
+    (None before measured_peaks() has run)."""
+    bound, _ = peak_of(sh, mode)
+    key = "fp32_vector_TFLOPs" if bound == "alu" else \
+        "fp16_mfma_TFLOPs" if sh.dtype == "f16" else "fp32_mfma_TFLOPs"
+    return MEASURED.get(key)
+
+
+def alg_bytes(sh, mode):
+    """(bytes read, bytes written) in HBM by one call, algorithmically: every
+    tensor once. Fused: x, w read, y written (prepacked: plus the filter
+    pack's read of w and write of the packed filter, and its read). The
+    materialised mode: the transform reads x and writes the im2win tensor,
+    the convolution reads it and w and writes y."""
+    Ho = (sh.Hi - sh.Hf) // (sh.s[0] if isinstance(sh.s, tuple) else sh.s) + 1
+    Wo = (sh.Wi - sh.Wf) // (sh.s[1] if isinstance(sh.s, tuple) else sh.s) + 1
+    e = sh.elem_bytes
+    x = sh.N * sh.Ci * sh.Hi * sh.Wi * e
+    w = sh.Co * sh.Ci * sh.Hf * sh.Wf * e
+    y = sh.N * sh.Co * Ho * Wo * 4
+    ws = sh.N * sh.Ci * Ho * sh.Wi * sh.Hf * e
+    if mode == "materialized":
+        return x + ws + w, ws + y
+    if mode == "prepacked":
+        return x + 2 * w, y + w
+    return x + w, y
+
+
+def bound_of(sh, mode):
+    """The roofline bound of a call: HBM when its algorithmic bytes at the
+    HBM peak take longer than its flops at the arithmetic peak."""
+    _, peak = peak_of(sh, mode)
+    Ho = (sh.Hi - sh.Hf) // (sh.s[0] if isinstance(sh.s, tuple) else sh.s) + 1
+    Wo = (sh.Wi - sh.Wf) // (sh.s[1] if isinstance(sh.s, tuple) else sh.s) + 1
+    rd, wr = alg_bytes(sh, mode)
+    t_bytes = (rd + wr) / (PEAK_HBM_GBS * 1e9)
+    t_flops = flops(sh, Ho, Wo) / (peak * 1e12)
+    return "hbm" if t_bytes > t_flops else peak_of(sh, mode)[0]
+
+
 def peak_of(sh, mode):
     """(bound, peak TFLOP/s) of a layer's convolution kernel in a mode."""
     if sh.dtype == "f16":
@@ -555,15 +648,28 @@ def roofline_of(key, sh, mode, r):
     prepacked mode a call is the filter prepack plus the convolution kernel,
     and in the materialised mode the im2win transform plus the convolution
     kernel; their per-call time includes those launches."""
-    bound, peak = peak_of(sh, mode)
-    achieved = r["flops"] / (r["ms_per_launch_avg"] * 1e-3) / 1e12
     kern = kernel_of(sh, mode)
+    t = r["ms_per_launch_avg"] * 1e-3
+    bound = bound_of(sh, mode)
+    if bound == "hbm":
+        rd, wr = alg_bytes(sh, mode)
+        achieved = (rd + wr) / t / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+        mp = MEASURED.get("hbm_fill_GBps" if wr > rd else "hbm_copy_GBps")
+    else:
+        _, peak = peak_of(sh, mode)
+        achieved = r["flops"] / t / 1e12
+        unit = "TFLOP/s"
+        mp = measured_peak_of(sh, mode)
     return {
         "bound": bound,
         "achieved": round(achieved, 3),
         "peak": peak,
-        "unit": "TFLOP/s",
+        "unit": unit,
         "frac": round(achieved / peak, 4),
+        "measured_peak": mp,
+        "frac_of_measured": round(achieved / mp, 4) if mp else None,
+        "tflops": round(r["flops"] / t / 1e12, 3),
         "traffic": load_traffic(key, mode, kern),
         "kernel": kern,
         "launches_per_call": 1 if mode in ("fused", "fused_valu") else 2,
@@ -688,6 +794,8 @@ def main():
               flush=True)
         return
 
+    MEASURED.update(measured_peaks())
+    log(f"[bench] measured peaks {MEASURED}")
     sh = workloads.BY_KEY[args.workload]
     log(f"[bench] headline {sh.describe()} mode={args.mode} steps={args.steps} warmup={args.warmup}")
     head = time_layer(sh, args.mode, args.steps, args.warmup)
@@ -731,6 +839,7 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "measured_peaks": dict(MEASURED),
         "layers": layers,
     }
     print(json.dumps(out), flush=True)

@@ -277,6 +277,22 @@ const char *im2win_knob_name(int knob);
 const char *im2win_conv_kernel_name(int elem_bytes, int mode, int N, int Ci, int Hi, int Wi,
                                    int Co, int Hf, int Wf, int sh, int sw);
 
+/*
+ * Rate probe (a measurement helper, not part of the convolution): enqueues
+ * `blocks` workgroups of 4 waves, each running `iters` rounds of arithmetic
+ * on registers only, and writes one float per thread into out (device
+ * memory, blocks * 256 floats, caller-owned; the values are meaningless).
+ * kind 0: fp32 vector FMA (unpacked, 8 chains per lane), 1: fp32 matrix
+ * instruction v_mfma_f32_32x32x2_f32, 2: fp16 matrix instruction
+ * v_mfma_f32_32x32x16_f16 (4 independent accumulators per wave). Timed by
+ * the caller, it gives the rate the chip sustains for that kind of work
+ * (the measured peak beside the published one). im2win_peak_probe_flops
+ * returns the flops one launch performs (0 for invalid arguments).
+ * Returns IM2WIN_OK, IM2WIN_EINVAL or IM2WIN_ELAUNCH.
+ */
+int im2win_peak_probe(int kind, int blocks, int iters, float *out, void *stream);
+double im2win_peak_probe_flops(int kind, int blocks, int iters);
+
 /* Static, human-readable text for a status code. */
 const char *im2win_status_string(int status);
 

@@ -86,6 +86,26 @@ def conv_kernel_name(N, Ci, Hi, Wi, Co, Hf, Wf, s, elem_bytes, mode: str = "fuse
     return r.decode()
 
 
+PROBE_KINDS = {"fp32_vector": 0, "fp32_mfma": 1, "fp16_mfma": 2}
+
+
+def peak_probe(kind: str, blocks: int, iters: int, out=None):
+    """Enqueues the library's rate probe of `kind` (fp32_vector, fp32_mfma,
+    fp16_mfma) on torch's current stream; returns (out, flops of the launch).
+    out: a float32 device tensor of at least blocks * 256 elements."""
+    torch = _torch()
+    k = PROBE_KINDS[kind]
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    _check_tensor(out, "out", (torch.float32,), 1)
+    if out.numel() < blocks * 256:
+        raise ValueError("out holds fewer than blocks * 256 floats")
+    L = _lib.load()
+    _lib.check(L.im2win_peak_probe(k, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                   _stream_handle(out)), "im2win_peak_probe")
+    return out, L.im2win_peak_probe_flops(k, blocks, iters)
+
+
 # ---- tuning knobs ------------------------------------------------------------
 def knob_names():
     """Names of the library's tuning knobs, in the order of their ids."""

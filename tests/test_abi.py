@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
         single + [f + "_strided" for f in single] + ["im2win_status_string", "im2win_last_error"] +
         ["conv2d_im2win_fp16_fused_workspace_bytes", "conv2d_im2win_fp16_fused",
          "conv2d_im2win_fp16_fused_noalloc",
-         "im2win_set_knob", "im2win_get_knob", "im2win_knob_name", "im2win_conv_kernel_name"] +
+         "im2win_set_knob", "im2win_get_knob", "im2win_knob_name", "im2win_conv_kernel_name",
+         "im2win_peak_probe", "im2win_peak_probe_flops"] +
         ["conv2d_im2col_workspace_bytes", "im2col_pack", "conv2d_im2col_fp32", "conv2d_im2col_fp16",
          "conv2d_direct_fp32", "conv2d_direct_fp16", "conv2d_im2win_nhwc_workspace_bytes",
          "im2win_pack_nhwc", "conv2d_im2win_nhwc_fp32", "conv2d_im2win_nhwc_fp16"])
@@ -378,3 +379,16 @@ def test_noalloc_rejects_before_launch():
     big = (1, 512, 16, 16, 512, 7, 7, 1, 1)   # filter scratch > 4 MiB
     assert L.conv2d_im2win_fp16_fused_workspace_bytes(*big) > 4 << 20
     assert f(FAKE, FAKE, FAKE, *big, None) == _lib.IM2WIN_EWORKSPACE
+
+
+def test_peak_probe_host_side():
+    """The rate probe's flop count (host arithmetic) and its argument checks
+    (rejected before anything is enqueued)."""
+    L = m.load_library()
+    assert L.im2win_peak_probe_flops(2, 512, 10) == 512 * 4 * 10 * 4 * 32 * 32 * 16 * 2
+    assert L.im2win_peak_probe_flops(1, 1, 1) == 4 * 4 * 32 * 32 * 2 * 2
+    assert L.im2win_peak_probe_flops(0, 1, 1) == 4 * 64 * 4 * 8 * 2
+    assert L.im2win_peak_probe_flops(3, 1, 1) == 0.0
+    assert L.im2win_peak_probe(3, 1, 1, ctypes.c_void_p(256), None) == _lib.IM2WIN_EINVAL
+    assert L.im2win_peak_probe(2, 1, 1, None, None) == _lib.IM2WIN_EINVAL
+    assert L.im2win_peak_probe(2, 0, 1, ctypes.c_void_p(256), None) == _lib.IM2WIN_EINVAL

@@ -992,3 +992,15 @@ def test_conv_f32_small_problem_special_values(t, orc):
     assert np.array_equal(np.isposinf(y), np.isposinf(ref))
     assert np.array_equal(np.isneginf(y), np.isneginf(ref))
     assert_within(y[fin], ref[fin], absd[fin], TOL["f32"], "finite outputs")
+
+
+@pytest.mark.parametrize("kind", ["fp32_vector", "fp32_mfma", "fp16_mfma"])
+def test_peak_probe_runs(kind):
+    """The rate probe runs and reports finite values and a positive flop
+    count (its rate is a measurement, checked against nothing)."""
+    import torch
+    device()
+    out, flops = m.peak_probe(kind, 8, 16)
+    torch.cuda.synchronize()
+    assert flops > 0
+    assert torch.isfinite(out).all()
