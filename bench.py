@@ -188,26 +188,33 @@ def _layer_call(sh, mode):
 
 
 def _time_calls(call, steps, warmup, raw=False):
-    """HIP events around each of `steps` calls and around all of them, on
-    torch's current stream (the stream the binding passes to the library)."""
+    """Times `steps` calls on torch's current stream (the stream the binding
+    passes to the library). The timed region holds the calls only, bracketed
+    by two HIP events after a synchronisation: ms_per_step is its time per
+    call. A second pass of the same calls with an event pair around each
+    gives the per-call distribution (median, min, mean; per-call events add
+    their own few microseconds of gaps, so they stay out of the first pass)."""
     import torch
     for _ in range(warmup):
         call()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_all0.record()
+    for _ in range(steps):
+        call()
+    t_all1.record()
+    torch.cuda.synchronize()
+    total_ms = t_all0.elapsed_time(t_all1)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
     for i in range(steps):
         starts[i].record()
         call()
         ends[i].record()
-    t_all1.record()
     torch.cuda.synchronize()
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    total_ms = t_all0.elapsed_time(t_all1)
     res = {
         "ms_per_step": total_ms / steps,
         "ms_per_launch_avg": float(np.mean(per)),
@@ -643,13 +650,14 @@ def kernel_of(sh, mode):
 
 def roofline_of(key, sh, mode, r):
     """Roofline of a layer's dominant kernel. In the fused modes one call is
-    one kernel launch, so the per-call event time on the stream the library
-    launches on is that kernel's time (average over the timed calls). In the
+    one kernel launch, so the timed region's time per call (HIP events on the
+    stream the library launches on, around the back-to-back calls) is that
+    kernel's average launch time, gaps between launches included. In the
     prepacked mode a call is the filter prepack plus the convolution kernel,
     and in the materialised mode the im2win transform plus the convolution
     kernel; their per-call time includes those launches."""
     kern = kernel_of(sh, mode)
-    t = r["ms_per_launch_avg"] * 1e-3
+    t = r["ms_per_step"] * 1e-3   # the timed region's time per call
     bound = bound_of(sh, mode)
     if bound == "hbm":
         rd, wr = alg_bytes(sh, mode)
@@ -673,6 +681,7 @@ def roofline_of(key, sh, mode, r):
         "traffic": load_traffic(key, mode, kern),
         "kernel": kern,
         "launches_per_call": 1 if mode in ("fused", "fused_valu") else 2,
+        "timed_us_per_call": round(r["ms_per_step"] * 1e3, 2),
         "launch_avg_us": round(r["ms_per_launch_avg"] * 1e3, 2),
         "launch_median_us": round(r["ms_per_launch_median"] * 1e3, 2),
         "launch_min_us": round(r["ms_per_launch_min"] * 1e3, 2),
