@@ -50,6 +50,7 @@ KERNEL_FILE = {"conv_f32_mfma_kernel": "conv_f32_mfma.hip",
                "conv_f16_reuse_kernel": "conv_f16_reuse.hip",
                "conv_f16_thin_kernel": "conv_f16_thin.hip",
                "conv_f16_wide_kernel": "conv_f16_wide.hip", "conv_f16_ws_kernel": "conv_f16_ws.hip",
+               "conv_f16_res_kernel": "conv_f16_res.hip",
                "conv_f16_kernel": "conv_f16.hip"}
 # Modes: fused (no workspace), fused_valu (fp32 on the vector-ALU kernel),
 # prepacked (fp16 fused with the filter prepacked per call into a small
@@ -62,8 +63,8 @@ LAYER_STEPS = {"cv4_f16_n64": 20}
 
 CONV_KERNELS = ("conv_f32_mfma_kernel", "conv_f32_small_kernel", "conv_f32_kernel",
                 "conv_f16_fused_kernel", "conv_f16_rows_kernel", "conv_f16_reuse_kernel",
-                "conv_f16_thin_kernel", "conv_f16_wide_kernel", "conv_f16_ws_kernel",
-                "conv_f16_kernel")
+                "conv_f16_thin_kernel", "conv_f16_wide_kernel", "conv_f16_res_kernel",
+                "conv_f16_ws_kernel", "conv_f16_kernel")
 
 
 def log(msg):
@@ -404,7 +405,7 @@ def ingest_pmc(fetch_csv, write_csv, copy_bytes=1 << 30):
 # The knobs are the library's own planner overrides (im2win_set_knob); a row
 # is timed only on layers where the knobs route the call to `kernel` (None:
 # whatever the planner picks), so every row names the kernel it measured.
-_ALL_F16_OFF = {"f16_reuse": -1, "f16_rows": -1, "f16_thin": -1, "f16_wide": -1}
+_ALL_F16_OFF = {"f16_reuse": -1, "f16_rows": -1, "f16_thin": -1, "f16_wide": -1, "f16_res": -1}
 ABLATION = {
     "f32": [("matrix cores, planner's choice", "fused", {}, None),
             ("matrix cores, 4 waves/workgroup", "fused", {"f32_nw": 4, "f32_ksplit": 1}, None),
@@ -423,8 +424,10 @@ ABLATION = {
              {"f16_reuse": -1, "f16_rows_bufs": 2}, "conv_f16_rows_kernel"),
             ("thin-layer kernel, 512-pixel tiles", "prepacked", {"f16_thin_nb": 4},
              "conv_f16_thin_kernel"),
-            ("wide-tile kernel, 4 waves of 4 x 4 blocks", "prepacked", {"f16_wide_nw": 4},
+            ("wide-tile kernel (resident-input kernel off)", "prepacked", {"f16_res": -1},
              "conv_f16_wide_kernel"),
+            ("wide-tile kernel, 4 waves of 4 x 4 blocks", "prepacked",
+             {"f16_res": -1, "f16_wide_nw": 4}, "conv_f16_wide_kernel"),
             ("channel-interleaved kernel", "prepacked", dict(_ALL_F16_OFF),
              "conv_f16_fused_kernel"),
             ("channel-interleaved, 8 waves along pixels", "prepacked",
@@ -445,12 +448,13 @@ SWITCHES = [("default", {}), ("tiles in launch order", {"tile_order": 1}),
             ("synchronous staging", {"sync_staging": 1}),
             ("launch order + synchronous staging", {"tile_order": 1, "sync_staging": 1})]
 SWITCH_MODES = {"f32": ["fused"], "f16": ["fused", "prepacked", "materialized"]}
-# Kernels with both switches; the small-problem fp32 kernel stages once (no
-# copy can overlap its MFMAs) and has only the tile order.
+# Kernels with both switches; the small-problem fp32 kernel and the
+# resident-input fp16 kernel stage their input once (no copy of it can
+# overlap their MFMAs) and have only the tile order.
 SWITCH_KERNELS = ("conv_f32_mfma_kernel", "conv_f16_reuse_kernel", "conv_f16_rows_kernel",
                   "conv_f16_thin_kernel", "conv_f16_wide_kernel", "conv_f16_fused_kernel",
                   "conv_f16_ws_kernel")
-ORDER_ONLY_KERNELS = ("conv_f32_small_kernel",)
+ORDER_ONLY_KERNELS = ("conv_f32_small_kernel", "conv_f16_res_kernel")
 
 
 def ablation(keys, steps):

@@ -303,7 +303,7 @@ const char* const kKnobNames[KNOB_COUNT] = {
     "f32_valu", "f32_nw", "f32_wco", "f32_cb", "f32_ksplit", "f32_occ",
     "f16_rows", "f16_rows_nwv", "f16_rows_bufs", "f16_thin", "f16_thin_nb", "f16_wide",
     "f16_wide_nw", "f16_wpx", "f16_nwh", "tile_order", "f16_reuse", "f16_ws", "sync_staging",
-    "f32_small"};
+    "f32_small", "f16_res"};
 
 std::atomic<int> g_knobs[KNOB_COUNT];
 }  // namespace im2win
@@ -507,7 +507,7 @@ const char* im2win_conv_kernel_name(int elem_bytes, int mode, int N, int Ci, int
         return mfma ? mfma : "conv_f32_kernel";
     }
     if (mode == 2) return im2win::f16_ws_applies(c) ? "conv_f16_ws_kernel" : "conv_f16_kernel";
-    return im2win::f16_fused_kernel_name(c, reinterpret_cast<const void*>(uintptr_t(256)));
+    return im2win::f16_fused_kernel_name(c, reinterpret_cast<const void*>(uintptr_t(256)), mode == 1);
 }
 
 int im2win_set_knob(int knob, int value)

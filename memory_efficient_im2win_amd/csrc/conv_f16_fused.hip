@@ -673,9 +673,12 @@ size_t f16_filter_pack_bytes(const ConvShape& c)
     return b;
 }
 
-const char* f16_fused_kernel_name(const ConvShape& c, const void* x)
+const char* f16_fused_kernel_name(const ConvShape& c, const void* x, bool prepacked)
 {
-    switch (f16_route(c, x)) {
+    const F16Route r = f16_route(c, x);
+    if ((r == kRouteWide || r == kRouteFused) && prepacked && f16_res_applies(c, kCoPad, x, x))
+        return "conv_f16_res_kernel";
+    switch (r) {
     case kRouteReuse: return "conv_f16_reuse_kernel";
     case kRouteRows: return "conv_f16_rows_kernel";
     case kRouteThin: return "conv_f16_thin_kernel";
@@ -719,6 +722,7 @@ int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk,
     if (r == kRouteReuse) return launch_conv_f16_reuse(x, wpk, w, y, c, stream);
     if (r == kRouteRows) return launch_conv_f16_rows(x, wpk, w, y, c, stream);
     if (r == kRouteThin) return launch_conv_f16_thin(x, wpk, w, y, c, stream);
+    if (wpk && f16_res_applies(c, kCoPad, x, y)) return launch_conv_f16_res(x, wpk, y, c, kCoPad, stream);
     if (r == kRouteWide) return launch_conv_f16_wide(x, wpk, w, y, c, kCoPad, stream);
     FusedArgs a;
     int wco, wpx, nb;

@@ -70,7 +70,7 @@ size_t f16_filter_pack_bytes(const ConvShape& c);
 int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, const void* x,
                            hipStream_t stream);
 // Name of the kernel launch_conv_f16_fused runs for this shape and x.
-const char* f16_fused_kernel_name(const ConvShape& c, const void* x);
+const char* f16_fused_kernel_name(const ConvShape& c, const void* x, bool prepacked);
 
 // Raises kernel f's dynamic LDS limit to `bytes` on the current device, once
 // per (kernel, device); thread-safe. A failure is left for the launch to
@@ -119,6 +119,17 @@ int launch_conv_f16_thin(const uint16_t* x, const void* wp, const uint16_t* w, f
 bool f16_wide_applies(const ConvShape& c, size_t copad_mult);
 int launch_conv_f16_wide(const uint16_t* x, const void* wpk, const uint16_t* w, float* y,
                          const ConvShape& c, size_t copad_mult, hipStream_t stream);
+
+// fp16 convolution with a tile's input rows resident in LDS and the filter,
+// prepacked as for the wide-tile kernel (channels padded to a multiple of
+// copad_mult), read into registers: 256 output channels x whole output rows
+// of one image per workgroup. Used by launch_conv_f16_fused for prepacked
+// calls on the shapes it takes (f16_res_applies) that
+// would otherwise run on the wide-tile or channel-interleaved kernel (x and
+// y 16-byte aligned).
+bool f16_res_applies(const ConvShape& c, size_t copad_mult, const void* x, const void* y);
+int launch_conv_f16_res(const uint16_t* x, const void* wpk, float* y, const ConvShape& c,
+                        size_t copad_mult, hipStream_t stream);
 
 // im2col + GEMM baseline: elements per im2col row (Ci*Hf*Wf padded to 32
 // bytes); the transform of N images into N*Ho*Wo rows; the GEMM over those

@@ -32,6 +32,8 @@ enum Knob : int {
     KNOB_SYNC_STAGING,       // 1: each stage copied through registers and waited for before its
                              //    MFMAs (no copy in flight during them; no direct global-to-LDS loads)
     KNOB_F32_SMALL,          // -1: small-problem fp32 kernel off (K split across a workgroup instead)
+    KNOB_F16_RES,            // -1: resident-input fp16 kernel off (prepacked calls it takes run on the
+                             //     wide-tile or channel-interleaved kernel)
     KNOB_COUNT
 };
 

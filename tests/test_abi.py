@@ -352,6 +352,11 @@ def test_conv_kernel_name():
         assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2) == "conv_f16_rows_kernel"
     assert m.conv_kernel_name(64, 3, 227, 227, 64, 7, 7, 2, 2) == "conv_f16_thin_kernel"
     assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2) == "conv_f16_wide_kernel"
+    assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2, "prepacked") == \
+        "conv_f16_res_kernel"
+    with m.knobs(f16_res=-1):
+        assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2, "prepacked") == \
+            "conv_f16_wide_kernel"
     with m.knobs(f16_rows=-1, f16_thin=-1, f16_wide=-1):
         assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2, "prepacked") == \
             "conv_f16_fused_kernel"

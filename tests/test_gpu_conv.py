@@ -870,7 +870,8 @@ SWITCH_CASES = [
      "conv_f16_rows_kernel"),
     ((3, 3, 35, 64, 64, 7, 7, 2), "f16", "filter", {}, "conv_f16_thin_kernel"),
     ((2, 3, 47, 45, 37, 7, 7, 2), "f16", None, {}, "conv_f16_thin_kernel"),
-    ((2, 96, 24, 24, 256, 5, 5, 1), "f16", "filter", {}, "conv_f16_wide_kernel"),
+    ((2, 96, 24, 24, 256, 5, 5, 1), "f16", "filter", {}, "conv_f16_res_kernel"),
+    ((2, 96, 24, 24, 256, 5, 5, 1), "f16", "filter", {"f16_res": -1}, "conv_f16_wide_kernel"),
     ((3, 13, 19, 21, 130, 3, 3, 1), "f16", None, {}, "conv_f16_wide_kernel"),
     ((1, 64, 30, 30, 64, 7, 7, 2), "f16", "filter", {}, "conv_f16_fused_kernel"),
     ((2, 24, 14, 14, 96, 5, 5, 1), "f16", None, {"f16_nwh": 3}, "conv_f16_fused_kernel"),
@@ -1004,3 +1005,76 @@ def test_peak_probe_runs(kind):
     torch.cuda.synchronize()
     assert flops > 0
     assert torch.isfinite(out).all()
+
+
+# Shapes of the resident-input fp16 kernel (prepacked filter; 256 output
+# channels per tile, whole output rows of one image): the cv5 layer, a
+# channel count that pads its last octet, two channel tiles, row stride 2,
+# column stride 2, a last quad with a zero octet, a filter taller than wide,
+# row tiles that do not divide the output, and one-row tiles of 13 and 10
+# pixel blocks (wide outputs).
+RES_F16 = [
+    (3, 96, 24, 24, 256, 5, 5, 1),
+    (1, 32, 6, 200, 256, 5, 5, 1),
+    (1, 32, 5, 160, 256, 3, 9, 1),
+    (2, 60, 17, 16, 512, 3, 5, 1),
+    (2, 32, 21, 24, 256, 3, 5, (2, 1)),
+    (2, 31, 20, 24, 256, 3, 2, (1, 2)),
+    (1, 88, 13, 8, 256, 4, 5, 1),
+    (2, 32, 12, 16, 256, 7, 5, 1),
+]
+
+
+@pytest.mark.parametrize("t", RES_F16, ids=str)
+def test_conv_f16_resident_kernel(t, orc, knob):
+    """The resident-input fp16 kernel: exact on integer inputs, within
+    tolerance on uniform inputs, the same bits on repeated calls, and the
+    same (exact) integer results as the kernel it replaces (f16_res=-1)."""
+    import torch
+    sh = _shape(t, "f16")
+    dev = device()
+    name = lambda: m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 2,
+                                      "prepacked")
+    assert name() == "conv_f16_res_kernel"
+    x, w = workloads.make_inputs(sh, seed=91)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    xi, wi = workloads.make_inputs(sh, seed=92, mode="int")
+    refi = orc.conv_direct(xi, wi, sh.s)
+    note(f"conv fp16 resident-input {sh.describe()}")
+    xt, wt = to_dev(x, dev), to_dev(w, dev)
+    ws = workspace(sh, "filter", dev)
+    y = torch.full(ref.shape, float("nan"), dtype=torch.float32, device=dev)
+    a = call(sh, xt, wt, "filter", dev, ws=ws, out=y).clone()
+    assert_within(a.cpu().numpy(), ref, absd, TOL["f16"], sh.describe())
+    for _ in range(2):
+        assert torch.equal(call(sh, xt, wt, "filter", dev, ws=ws), a)
+    assert_exact(_run(sh, "f16", xi, wi, "filter"), refi, sh.describe())
+    knob("f16_res", -1)
+    assert name() != "conv_f16_res_kernel"
+    assert_exact(_run(sh, "f16", xi, wi, "filter"), refi, f"{sh.describe()} f16_res=-1")
+
+
+def test_conv_f16_resident_kernel_special_values(orc):
+    """Infinities and NaN in the input reach exactly the outputs whose windows
+    hold them: the zero octets and the zero filter fragments of the padded K
+    steps add nothing."""
+    sh = _shape((2, 88, 24, 24, 256, 5, 5, 1), "f16")
+    device()
+    assert m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 2,
+                              "prepacked") == "conv_f16_res_kernel"
+    x, w = workloads.make_inputs(sh, seed=93)
+    x[0, 1, 4, 5] = np.inf
+    x[1, 2, 7, 10] = -np.inf
+    x[0, 0, 0, 6] = np.nan
+    x[1, sh.Ci - 1, sh.Hi - 1, sh.Wi - 1] = np.inf
+    w = (np.abs(w.astype(np.float32)) + np.float32(0.25)).astype(w.dtype)
+    ref = orc.conv_direct(x, w, sh.s)
+    fin = np.isfinite(ref)
+    _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
+                              with_absdot=True)
+    note(f"conv fp16 resident-input special values {sh.describe()}")
+    y = _run(sh, "f16", x, w, "filter").astype(np.float64)
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+    assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
