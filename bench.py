@@ -151,7 +151,7 @@ def _layer_call(sh, mode):
     import memory_efficient_im2win_amd as m
     dev = torch.device("cuda:0")
     x, w = workloads.make_inputs(sh, seed=0)
-    if mode == "nhwc_materialized":
+    if mode in ("nhwc_materialized", "nhwc_fused"):
         x = np.ascontiguousarray(x.transpose(0, 2, 3, 1))
     xt = torch.from_numpy(x).to(dev)
     wt = torch.from_numpy(w).to(dev)
@@ -163,6 +163,9 @@ def _layer_call(sh, mode):
         y = torch.empty((sh.N, Ho, Wo, sh.Co), dtype=torch.float32, device=dev)
         wsb = m.nhwc_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
                                      sh.elem_bytes)
+    elif mode == "nhwc_fused":
+        y = torch.empty((sh.N, Ho, Wo, sh.Co), dtype=torch.float32, device=dev)
+        wsb = m.nhwc_fused_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s)
     elif mode == "im2col":
         wsb = m.im2col_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s,
                                        sh.elem_bytes)
@@ -176,6 +179,8 @@ def _layer_call(sh, mode):
     def call():
         if mode == "nhwc_materialized":
             m.conv2d_nhwc(xt, wt, sh.s, ws=ws, out=y)
+        elif mode == "nhwc_fused":
+            m.conv2d_nhwc_fused(xt, wt, sh.s, fws=ws, out=y)
         elif mode == "im2col":
             m.conv2d_im2col(xt, wt, sh.s, ws=ws, out=y)
         elif mode == "direct":
@@ -333,16 +338,28 @@ def _read_csv(path):
 
 def baselines(sh, entry):
     """Times the im2col + GEMM and direct-convolution baselines and the NHWC
-    materialised im2win mode on a layer and adds them, and the im2win/im2col
+    materialised im2win mode on a layer (and, for fp16 layers the fused NHWC
+    kernel takes, the fused NHWC call) and adds them, and the im2win/im2col
     ratios, to its entry. Memory is the bytes a call touches in HBM:
     x + w + y + workspace."""
+    import memory_efficient_im2win_amd as m
     peak = PEAK_FP32_MFMA_TFLOPS if sh.dtype == "f32" else PEAK_FP16_MFMA_TFLOPS
-    for mode in ("im2col", "direct", "nhwc_materialized"):
+    modes = ["im2col", "direct", "nhwc_materialized"]
+    if sh.dtype == "f16":
+        k = m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 2,
+                               "nhwc_prepacked")
+        if k == "conv_f16_res_kernel":
+            modes.append("nhwc_fused")
+        else:
+            entry["nhwc_fused"] = {"kernel": k, "skipped": "outside the fused NHWC kernel's envelope"}
+    for mode in modes:
         r = time_layer(sh, mode, 3, 1)
         entry[mode] = {"tflops": round(r["tflops_median"], 3),
                        "us_per_call": round(r["ms_per_launch_median"] * 1e3, 2),
                        "frac_of_peak": round(r["tflops"] / peak, 4),
                        "workspace_bytes": r["workspace_bytes"]}
+        if mode == "nhwc_fused":
+            entry[mode]["kernel"] = "conv_f16_res_kernel"
         log(f"[bench] {sh.name} {mode}: {r['tflops']:.2f} TFLOP/s "
             f"({r['ms_per_step']*1e3:.1f} us/call, ws {r['workspace_bytes']} B)")
     Ho = (sh.Hi - sh.Hf) // workloads_stride(sh)[0] + 1

@@ -252,6 +252,35 @@ int conv2d_im2win_nhwc_fp16(const uint16_t *x, const uint16_t *w, float *y, void
                             int sh, int sw, void *stream);
 
 /*
+ * The fused fp16 NHWC convolution (the half-precision path of "Enabling
+ * Memory-efficient Im2win Convolution with Multi-precision Support on GPU
+ * CUDA and Tensor Cores", Abstract, on NHWC tensors): no im2win tensor in
+ * HBM. In NHWC the 8 channels of one input pixel are 16 contiguous bytes,
+ * so a tile's input rows are copied into LDS as they lie; each workgroup
+ * keeps them there and multiplies them with the filter, prepacked into fws,
+ * on the matrix cores. x is N x Hi x Wi x Ci (fp16), y N x Ho x Wo x Co
+ * (fp32), w Co x Ci x Hf x Wf (fp16).
+ *
+ * conv2d_im2win_nhwc_fp16_fused_workspace_bytes: the bytes of the prepacked
+ *     filter (16-byte entries of 8 input channels of one tap for one output
+ *     channel); 0 for an invalid shape.
+ * conv2d_im2win_nhwc_fp16_fused: fws (16-byte aligned) with at least that
+ *     many bytes: the filter is packed into it, then the resident-input
+ *     kernel runs when the shape is in its envelope (Co a multiple of 256,
+ *     Ci of 8, at least 4 taps, x and y 16-byte aligned, a tile's input rows
+ *     within LDS; im2win_conv_kernel_name mode 3 names the kernel); other
+ *     shapes, and fws == NULL with fws_bytes == 0, take the direct NHWC
+ *     kernel. fws given but too small: IM2WIN_EWORKSPACE; fws not 16-byte
+ *     aligned: IM2WIN_EINVAL. The caller owns every buffer; fws holds the
+ *     packed filter afterwards.
+ */
+size_t conv2d_im2win_nhwc_fp16_fused_workspace_bytes(int N, int Ci, int Hi, int Wi, int Co,
+                                                     int Hf, int Wf, int sh, int sw);
+int conv2d_im2win_nhwc_fp16_fused(const uint16_t *x, const uint16_t *w, float *y, void *fws,
+                                  size_t fws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                                  int Wf, int sh, int sw, void *stream);
+
+/*
  * Tuning knobs of the kernel planners, for tests and the ablation study
  * (the pages' variant study, Table II and Fig. 4 of "Enabling
  * Memory-efficient Im2win Convolution ..."). Knob k is named by
@@ -271,8 +300,10 @@ const char *im2win_knob_name(int knob);
  * current knobs (for profiles and reports), assuming x 16-byte aligned.
  * elem_bytes 4 (conv2d_im2win_fp32) or 2 (the fp16 calls); mode 0: fused (no
  * workspace), 1: conv2d_im2win_fp16_fused with a filter workspace, 2:
- * materialised (the im2win_pack launches come first). Static string; NULL
- * for an invalid shape or mode. Host only.
+ * materialised (the im2win_pack launches come first), 3:
+ * conv2d_im2win_nhwc_fp16_fused with a filter workspace (fp16 only; y also
+ * 16-byte aligned). Static string; NULL for an invalid shape or mode. Host
+ * only.
  */
 const char *im2win_conv_kernel_name(int elem_bytes, int mode, int N, int Ci, int Hi, int Wi,
                                    int Co, int Hf, int Wf, int sh, int sw);

@@ -75,9 +75,10 @@ def fused_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s) -> int:
 
 def conv_kernel_name(N, Ci, Hi, Wi, Co, Hf, Wf, s, elem_bytes, mode: str = "fused") -> str:
     """Name of the main kernel a call runs (mode "fused", "prepacked" for
-    conv2d_fused with a filter workspace, or "materialized")."""
+    conv2d_fused with a filter workspace, "materialized", or "nhwc_prepacked"
+    for conv2d_nhwc_fused with a filter workspace, fp16)."""
     sh, sw = strides(s)
-    code = {"fused": 0, "prepacked": 1, "materialized": 2}[mode]
+    code = {"fused": 0, "prepacked": 1, "materialized": 2, "nhwc_prepacked": 3}[mode]
     if code == 1 and elem_bytes == 4:
         code = 0
     r = _lib.load().im2win_conv_kernel_name(elem_bytes, code, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw)
@@ -361,6 +362,44 @@ def pack_nhwc(x, Hf: int, Wf: int, s):
     _lib.check(_lib.load().im2win_pack_nhwc(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                                             N, Ci, Hi, Wi, Hf, Wf, sh, sw, x.element_size(),
                                             _stream_handle(x)), "im2win_pack_nhwc")
+    return out
+
+
+def nhwc_fused_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, s) -> int:
+    """Workspace of conv2d_nhwc_fused (fp16): the prepacked filter's bytes;
+    0 for an invalid shape."""
+    sh, sw = strides(s)
+    return _lib.load().conv2d_im2win_nhwc_fp16_fused_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf,
+                                                                     sh, sw)
+
+
+def conv2d_nhwc_fused(x, w, stride=1, fws=None, fws_bytes: int | None = None, out=None):
+    """fp16 NHWC convolution without an im2win tensor: x (N, Hi, Wi, Ci), w
+    (Co, Ci, Hf, Wf), fp32 NHWC output (N, Ho, Wo, Co). With ``fws`` (at
+    least nhwc_fused_workspace_bytes(...) bytes) the filter is prepacked into
+    it and the resident-input kernel runs where its envelope allows; without
+    it, and outside the envelope, the direct NHWC kernel."""
+    torch = _torch()
+    _check_tensor(x, "x", (torch.float16,), 4)
+    _check_tensor(w, "w", (torch.float16,), 4)
+    if w.device != x.device:
+        raise ValueError("x and w must be on the same device")
+    N, Hi, Wi, Ci = x.shape
+    Co, Ci2, Hf, Wf = w.shape
+    if Ci2 != Ci:
+        raise ValueError("x and w disagree on the input channel count")
+    Ho, Wo = output_dims(Hi, Wi, Hf, Wf, stride)
+    if out is None:
+        out = torch.empty((N, Ho, Wo, Co), dtype=torch.float32, device=x.device)
+    elif (tuple(out.shape) != (N, Ho, Wo, Co) or out.dtype != torch.float32
+          or not out.is_contiguous() or out.device != x.device):
+        raise ValueError("out has the wrong shape, dtype, device or layout")
+    ptr, nbytes = _ws_arg(fws, fws_bytes, x, "fws")
+    sh, sw = strides(stride)
+    _lib.check(_lib.load().conv2d_im2win_nhwc_fp16_fused(
+        ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        ptr, nbytes, N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, _stream_handle(x)),
+        "conv2d_im2win_nhwc_fp16_fused")
     return out
 
 

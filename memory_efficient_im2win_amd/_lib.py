@@ -50,6 +50,8 @@ EXPORTS = {
     "im2win_pack_nhwc": ([_p, _p] + [_i] * 8 + [_sz, _p], _i),
     "conv2d_im2win_nhwc_fp32": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
     "conv2d_im2win_nhwc_fp16": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
+    "conv2d_im2win_nhwc_fp16_fused_workspace_bytes": ([_i] * 9, _sz),
+    "conv2d_im2win_nhwc_fp16_fused": ([_p, _p, _p, _p, _sz] + [_i] * 9 + [_p], _i),
     "im2win_peak_probe": ([_i, _i, _i, _p, _p], _i),
     "im2win_peak_probe_flops": ([_i, _i, _i], ctypes.c_double),
 }

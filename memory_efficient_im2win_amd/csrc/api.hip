@@ -492,14 +492,49 @@ int conv2d_im2win_nhwc_fp16(const uint16_t* x, const uint16_t* w, float* y, void
                                  static_cast<hipStream_t>(stream));
 }
 
+size_t conv2d_im2win_nhwc_fp16_fused_workspace_bytes(int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                                                     int Wf, int sh, int sw)
+{
+    int Ho, Wo;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return 0;
+    return align_up(im2win::f16_interleaved_filter_bytes(ConvShape{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo}));
+}
+
+int conv2d_im2win_nhwc_fp16_fused(const uint16_t* x, const uint16_t* w, float* y, void* fws,
+                                  size_t fws_bytes, int N, int Ci, int Hi, int Wi, int Co, int Hf,
+                                  int Wf, int sh, int sw, void* stream)
+{
+    int Ho, Wo;
+    if (!x || !w || !y) return IM2WIN_EINVAL;
+    if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return IM2WIN_EINVAL;
+    if (!aligned(x, 2) || !aligned(w, 2) || !aligned(y, 4)) return IM2WIN_EINVAL;
+    const ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo};
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (fws == nullptr) {
+        if (fws_bytes != 0) return IM2WIN_EWORKSPACE;
+        return status_of(im2win::launch_conv_direct_nhwc(x, w, y, c, 2, st));
+    }
+    if (fws_bytes < im2win::f16_interleaved_filter_bytes(c)) return IM2WIN_EWORKSPACE;
+    if (!aligned(fws, 16)) return IM2WIN_EINVAL;
+    if (!im2win::f16_res_applies(c, im2win::kF16CoPad, x, y, true))
+        return status_of(im2win::launch_conv_direct_nhwc(x, w, y, c, 2, st));
+    int rc = im2win::launch_f16_interleaved_filter_pack(w, fws, c, st);
+    if (rc != 0) return status_of(rc);
+    return status_of(im2win::launch_conv_f16_res(x, fws, y, c, im2win::kF16CoPad, true, st));
+}
+
 const char* im2win_conv_kernel_name(int elem_bytes, int mode, int N, int Ci, int Hi, int Wi,
                                    int Co, int Hf, int Wf, int sh, int sw)
 {
     int Ho, Wo;
     if (elem_bytes != 2 && elem_bytes != 4) return nullptr;
-    if (mode < 0 || mode > 2 || (mode == 1 && elem_bytes != 2)) return nullptr;
+    if (mode < 0 || mode > 3 || ((mode == 1 || mode == 3) && elem_bytes != 2)) return nullptr;
     if (!check_shape(N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, &Ho, &Wo)) return nullptr;
     const ConvShape c{N, Ci, Hi, Wi, Co, Hf, Wf, sh, sw, Ho, Wo};
+    const void* al = reinterpret_cast<const void*>(uintptr_t(256));
+    if (mode == 3)
+        return im2win::f16_res_applies(c, im2win::kF16CoPad, al, al, true) ? "conv_f16_res_kernel"
+                                                                            : "conv_direct_nhwc_kernel";
     if (elem_bytes == 4) {
         if (mode == 2) return "conv_f32_kernel";
         const char* mfma =

@@ -40,7 +40,7 @@ namespace im2win {
 namespace {
 
 constexpr int kMaxLds = 160 * 1024;
-constexpr int kCoPad = 128;   // prepacked filter: channels padded to a multiple of this
+constexpr int kCoPad = kF16CoPad;   // prepacked filter: channels padded to a multiple of this
 
 struct FusedArgs {
     ConvShape c;
@@ -695,9 +695,24 @@ int launch_f16_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c, con
     if (r == kRouteNone) return -1;
     if (r == kRouteRows || r == kRouteReuse) return launch_f16_rows_filter_pack(w, wpk, c, stream);
     if (r == kRouteThin) return launch_f16_slices_filter_pack(w, wpk, c, stream);
-    FusedArgs a;
-    int wco, wpx, nb;
-    if (!plan(c, a, wco, wpx, nb)) return -1;
+    return launch_f16_interleaved_filter_pack(w, wpk, c, stream);
+}
+
+size_t f16_interleaved_filter_bytes(const ConvShape& c)
+{
+    return (size_t)ceil_div(c.Ci, 8) * (size_t)((c.Hf * c.Wf + 1) & ~1) *
+           (size_t)(ceil_div(c.Co, kCoPad) * kCoPad) * 16;
+}
+
+int launch_f16_interleaved_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c,
+                                       hipStream_t stream)
+{
+    FusedArgs a{};
+    a.c = c;
+    a.HW = c.Hf * c.Wf;
+    a.HWp = (a.HW + 1) & ~1;
+    a.CG = ceil_div(c.Ci, 8);
+    a.Copad = ceil_div(c.Co, kCoPad) * kCoPad;
     // LDS of one workgroup: kPackCo channels x 8 x HW taps (HW <= 256: 16 KB).
     const size_t lds = (size_t)kPackCo * 8 * a.HW * 2;
     if (a.HW <= 256 && a.CG <= 65535) {
@@ -722,7 +737,8 @@ int launch_conv_f16_fused(const uint16_t* x, const uint16_t* w, const void* wpk,
     if (r == kRouteReuse) return launch_conv_f16_reuse(x, wpk, w, y, c, stream);
     if (r == kRouteRows) return launch_conv_f16_rows(x, wpk, w, y, c, stream);
     if (r == kRouteThin) return launch_conv_f16_thin(x, wpk, w, y, c, stream);
-    if (wpk && f16_res_applies(c, kCoPad, x, y)) return launch_conv_f16_res(x, wpk, y, c, kCoPad, stream);
+    if (wpk && f16_res_applies(c, kCoPad, x, y))
+        return launch_conv_f16_res(x, wpk, y, c, kCoPad, false, stream);
     if (r == kRouteWide) return launch_conv_f16_wide(x, wpk, w, y, c, kCoPad, stream);
     FusedArgs a;
     int wco, wpx, nb;

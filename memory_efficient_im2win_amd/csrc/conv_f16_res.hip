@@ -57,12 +57,13 @@ struct ResArgs {
     int Q;            // channel quads of 32
     int OS;           // LDS entries per octet: Rin * Wi
     int ppo;          // column pairs per octet: OS / 2
+    int OCTP;         // NHWC: LDS entries per staged pixel, 4(Q + 1) + 1 (odd: no bank conflicts)
     int tasks;        // copy tasks: channel octets x ppo pairs
     int HW, HWp, Copad, S;   // taps; prepacked layout; K steps Q * HW
     int Spad;         // K steps run: S rounded up to a multiple of 3
     uint32_t lds_bytes;
     uint32_t xbytes, ybytes, wbytes;
-    FastDiv divCoT, divTpi, divWo, divWf, divHW, divPpo;
+    FastDiv divCoT, divTpi, divWo, divWf, divHW, divPpo, divOCTP;
     bool swz;         // XCD-grouped tile order
 };
 
@@ -101,7 +102,7 @@ __device__ __forceinline__ void store16(const floatx4_t& v, __amdgpu_buffer_rsrc
 // The reduction and the stores of one wave: channels co_base .. +63 (4
 // blocks of 16) x pixel blocks jb .. jb+NBW-1 of the tile, the input rows in
 // LDS (smem), the filter read from wpk.
-template <int NBW, int NCB>
+template <int NBW, int NCB, bool NHWC>
 __device__ __forceinline__ void res_compute(const unsigned char* smem, const uint4* __restrict__ wpk,
                                             float* __restrict__ y, const ResArgs& a, int co_base,
                                             int jb, int P, uint32_t n, int ho0, int lane)
@@ -119,7 +120,8 @@ __device__ __forceinline__ void res_compute(const unsigned char* smem, const uin
         if (p >= P) p = 0;
         const int r = (int)a.divWo.div((uint32_t)p);
         const int wo = p - r * Wo;
-        bb[j] = (uint32_t)((g * a.OS + r * sh * Wi + wo * sw) * 16);
+        bb[j] = NHWC ? (uint32_t)(((r * sh * Wi + wo * sw) * a.OCTP + g) * 16)
+                     : (uint32_t)((g * a.OS + r * sh * Wi + wo * sw) * 16);
     }
     // This lane's filter entry in K step (q, tap): ((4q + g) * HWp + tap) *
     // Copad + co_base + 16b + c16; the uniform part goes into the resource's
@@ -161,7 +163,8 @@ __device__ __forceinline__ void res_compute(const unsigned char* smem, const uin
         const int tap = s - q * a.HW;
         const int kh = (int)a.divWf.div((uint32_t)tap);
         const int kw = tap - kh * Wf;
-        return (uint32_t)((4 * q * a.OS + kh * Wi + kw) * 16);
+        return NHWC ? (uint32_t)(((kh * Wi + kw) * a.OCTP + 4 * q) * 16)
+                    : (uint32_t)((4 * q * a.OS + kh * Wi + kw) * 16);
     };
     // K step s: the filter of step s+2 is loaded (a ring of 3 steps); then
     // block by block, the 4 MFMAs of step s on pixel block j, and block j of
@@ -177,8 +180,12 @@ __device__ __forceinline__ void res_compute(const unsigned char* smem, const uin
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
 #pragma unroll
-            for (int b = 0; b < NCB; ++b)
-                mfma16(acc[j][b], bf[j], af[k][b]);
+            for (int b = 0; b < NCB; ++b) {
+                if (NHWC)
+                    mfma16(acc[j][b], af[k][b], bf[j]);   // rows: channels
+                else
+                    mfma16(acc[j][b], bf[j], af[k][b]);   // rows: pixels
+            }
             bf[j] = *reinterpret_cast<const half8_t*>(smem + bb[j] + o);
         }
     };
@@ -200,13 +207,29 @@ __device__ __forceinline__ void res_compute(const unsigned char* smem, const uin
 
     mfma_drain();
 
+    const __amdgpu_buffer_rsrc_t ry = raw_rsrc(y, a.ybytes);
+    if (NHWC) {
+        // Lane (g, c16) of block (j, b) holds channels co_base + 16b + 4g ..
+        // +3 of pixel 16j + c16: 16 contiguous bytes of y (N x Ho x Wo x Co).
+        const int64_t row0 = ((int64_t)n * Ho + ho0) * Wo;
+#pragma unroll
+        for (int b = 0; b < NCB; ++b) {
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+                const int p = 16 * (jb + j) + c16;
+                const uint32_t off =
+                    (uint32_t)(((row0 + p) * Co + co_base + 16 * b + 4 * g) * 4);
+                store16(acc[j][b], ry, p < P ? off : kMissR);
+            }
+        }
+        return;
+    }
     // Lane (g, c16) of block (j, b) holds pixels 16j + 4g .. +3 of channel
     // co_base + 16b + c16 (4 consecutive floats, 16-byte aligned as Wo % 4
     // == 0): one 16-byte store straight from the accumulator registers,
     // ordered after the wait states (the stores are statements of the same
     // kind as the MFMAs, which keep their order); pixels past the tile get
     // an offset out of range and are dropped.
-    const __amdgpu_buffer_rsrc_t ry = raw_rsrc(y, a.ybytes);
     const int64_t plane = (int64_t)Ho * Wo;
 #pragma unroll
     for (int b = 0; b < NCB; ++b) {
@@ -222,7 +245,8 @@ __device__ __forceinline__ void res_compute(const unsigned char* smem, const uin
 
 // NB pixel blocks per tile; NCB channel blocks per wave: 2 * 256 / (16 NCB)
 // waves (NCB = 8: 4 waves, one per SIMD; NCB = 4: 8 waves, two per SIMD).
-template <int NB, int NCB>
+// NHWC: x is N x Hi x Wi x Ci and y N x Ho x Wo x Co.
+template <int NB, int NCB, bool NHWC>
 __global__ __launch_bounds__(128 * kResCo / (16 * NCB)) void conv_f16_res_kernel(const uint16_t* __restrict__ x,
                                                              const uint4* __restrict__ wpk,
                                                              float* __restrict__ y, ResArgs a)
@@ -242,6 +266,40 @@ __global__ __launch_bounds__(128 * kResCo / (16 * NCB)) void conv_f16_res_kernel
     const int ih0 = ho0 * sh;
     const int tid = threadIdx.x;
 
+    if (NHWC) {
+        // NHWC: the tile's input rows are one contiguous block of x, whose 16
+        // bytes at (pixel, octet o) are exactly the entry of those 8 channels;
+        // entry e = pixel * OCTP + o takes them for o < Ci/8 and zeros
+        // otherwise (the octets padding the last quad, the 4 zero octets the
+        // K steps past S read, and the spare entry that makes OCTP odd).
+        // Consecutive threads write consecutive entries.
+        const __amdgpu_buffer_rsrc_t rx = raw_rsrc(x, a.xbytes);
+        const int octs = Ci >> 3;
+        const int pix = min(a.Rin, Hi - ih0) * Wi;   // staged pixels that exist
+        const int64_t base = ((int64_t)n * Hi + ih0) * Wi;
+        const int total = a.Rin * Wi * a.OCTP;
+        uint4* L = reinterpret_cast<uint4*>(smem);
+        constexpr int U = 4;
+        for (int e0 = 0; e0 < total; e0 += U * NT) {
+            uint4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + u * NT + tid;
+                const int px = (int)a.divOCTP.div((uint32_t)e);
+                const int o = e - px * a.OCTP;
+                const uint32_t off = e < total && o < octs && px < pix
+                                         ? (uint32_t)(((base + px) * Ci + 8 * o) * 2)
+                                         : kMissR;
+                const auto r = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+                v[u] = make_uint4(r[0], r[1], r[2], r[3]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + u * NT + tid;
+                if (e < total) L[e] = v[u];
+            }
+        }
+    } else
     // Copy the tile's input rows into LDS. Task (octet o, column pair m) of
     // the octets that hold channels: one dword (columns 2m and 2m+1 of the
     // staged rows, which are one contiguous run per channel) from each of
@@ -305,29 +363,32 @@ __global__ __launch_bounds__(128 * kResCo / (16 * NCB)) void conv_f16_res_kernel
     const int wave = uniform(tid >> 6);
     const int co_base = co_t * kResCo + (wave % G) * 16 * NCB;
     if (wave < G)
-        res_compute<(NB + 1) / 2, NCB>(smem, wpk, y, a, co_base, 0, P, n, ho0, tid & 63);
+        res_compute<(NB + 1) / 2, NCB, NHWC>(smem, wpk, y, a, co_base, 0, P, n, ho0, tid & 63);
     else
-        res_compute<NB / 2, NCB>(smem, wpk, y, a, co_base, (NB + 1) / 2, P, n, ho0, tid & 63);
+        res_compute<NB / 2, NCB, NHWC>(smem, wpk, y, a, co_base, (NB + 1) / 2, P, n, ho0,
+                                       tid & 63);
 }
 
 constexpr int kResNBs[] = {8, 10, 13};
 
-// Plans a launch; false outside the envelope: Co a multiple of 256, Wi a
-// multiple of 8 (whole 16-byte chunks per row), Wo a multiple of 4 (whole
-// 16-byte output stores), at least 4 taps (the steps
-// read past S stay within the zero octets), channel quads at most 1/8
-// padding, a tile's input rows and 4 zero octets within LDS, tensors
-// addressable with 32-bit buffer offsets. R is chosen for the fewest rounds
-// of tiles over the CUs times the pixel blocks per tile.
-bool plan(const ConvShape& c, ResArgs& a, size_t copad_mult)
+// Plans a launch; false outside the envelope: Co a multiple of 256, at least
+// 4 taps (the steps read past S stay within the zero octets), channel quads
+// at most 1/8 padding, a tile's input rows and 4 zero octets within LDS,
+// tensors addressable with 32-bit buffer offsets; NCHW: Wi a multiple of 8
+// (whole 16-byte chunks per row) and Wo of 4 (whole 16-byte output stores);
+// NHWC: Ci a multiple of 8 (whole 16-byte chunks per pixel). R is chosen for
+// the fewest rounds of tiles over the CUs times the pixel blocks per tile.
+bool plan(const ConvShape& c, ResArgs& a, size_t copad_mult, bool nhwc)
 {
     if (knob(KNOB_F16_RES) < 0) return false;
-    if (c.Co % kResCo != 0 || c.Wi % 8 != 0 || c.Wo % 4 != 0 || c.Hf * c.Wf < 4) return false;
+    if (c.Co % kResCo != 0 || c.Hf * c.Wf < 4) return false;
+    if (nhwc ? c.Ci % 8 != 0 : (c.Wi % 8 != 0 || c.Wo % 4 != 0)) return false;
     const int oct = ceil_div(c.Ci, 8);
     const int Q = ceil_div(oct, 4);
     if ((32 * Q - c.Ci) * 8 > 32 * Q) return false;
     a.c = c;
     a.Q = Q;
+    a.OCTP = 4 * (Q + 1) + 1;
     a.HW = c.Hf * c.Wf;
     a.HWp = (a.HW + 1) & ~1;
     a.Copad = (int)(ceil_div(c.Co, (int)copad_mult) * (int)copad_mult);
@@ -335,7 +396,8 @@ bool plan(const ConvShape& c, ResArgs& a, size_t copad_mult)
     a.S = Q * a.HW;
     a.Spad = (a.S + 2) / 3 * 3;
     const int cus = 256;
-    int best_R = 0, best_nb = 0;
+    const int per_pixel = nhwc ? a.OCTP : 4 * (Q + 1);   // LDS entries per staged pixel
+    int best_R = 0;
     double best = 0;
     for (int R = 1; R <= c.Ho; ++R) {
         const int need = ceil_div(R * c.Wo, 16);
@@ -347,13 +409,12 @@ bool plan(const ConvShape& c, ResArgs& a, size_t copad_mult)
             }
         if (nb == 0) break;
         const int Rin = (R - 1) * c.sh + c.Hf;
-        if ((int64_t)4 * (Q + 1) * Rin * c.Wi * 16 > kResLds) break;
+        if ((int64_t)per_pixel * Rin * c.Wi * 16 > kResLds) break;
         const int64_t tiles = (int64_t)c.N * ceil_div(c.Ho, R) * a.co_tiles;
         const double cost = (double)((tiles + cus - 1) / cus) * nb;
         if (best_R == 0 || cost <= best) {
             best = cost;
             best_R = R;
-            best_nb = nb;
         }
     }
     if (best_R == 0) return false;
@@ -363,7 +424,7 @@ bool plan(const ConvShape& c, ResArgs& a, size_t copad_mult)
     a.OS = a.Rin * c.Wi;
     a.ppo = a.OS / 2;
     a.tasks = oct * a.ppo;
-    a.lds_bytes = (uint32_t)(4 * (Q + 1) * a.OS * 16);
+    a.lds_bytes = (uint32_t)(per_pixel * a.OS * 16);
     const int64_t tiles = (int64_t)c.N * a.tpi * a.co_tiles;
     if (tiles > 0x7fffffff) return false;
     const int64_t xb = (int64_t)c.N * c.Ci * c.Hi * c.Wi * 2;
@@ -379,8 +440,8 @@ bool plan(const ConvShape& c, ResArgs& a, size_t copad_mult)
     a.divWf = FastDiv((uint32_t)c.Wf);
     a.divHW = FastDiv((uint32_t)a.HW);
     a.divPpo = FastDiv((uint32_t)a.ppo);
+    a.divOCTP = FastDiv((uint32_t)a.OCTP);
     a.swz = knob(KNOB_TILE_ORDER) != 1;
-    (void)best_nb;
     return true;
 }
 
@@ -392,40 +453,46 @@ int nb_of(const ResArgs& a)
     return 0;
 }
 
-template <int NB>
+template <int NB, bool NHWC>
 int launch_t(const uint16_t* x, const uint4* wpk, float* y, const ResArgs& a, hipStream_t stream)
 {
     constexpr int NCB = 4;   // 8 waves, two per SIMD: 1.06x faster on cv5 than NCB = 8
-    ensure_lds_limit((const void*)conv_f16_res_kernel<NB, NCB>, kResLds);
-    hipLaunchKernelGGL((conv_f16_res_kernel<NB, NCB>),
+    ensure_lds_limit((const void*)conv_f16_res_kernel<NB, NCB, NHWC>, kResLds);
+    hipLaunchKernelGGL((conv_f16_res_kernel<NB, NCB, NHWC>),
                        dim3((unsigned)((int64_t)a.c.N * a.tpi * a.co_tiles)),
-                       dim3(128 * kResCo / (16 * NCB)),
-                       a.lds_bytes, stream, x, wpk, y, a);
+                       dim3(128 * kResCo / (16 * NCB)), a.lds_bytes, stream, x, wpk, y, a);
     return launch_status();
+}
+
+template <bool NHWC>
+int launch_nb(const uint16_t* x, const uint4* wpk, float* y, const ResArgs& a, hipStream_t stream)
+{
+    switch (nb_of(a)) {
+    case 8: return launch_t<8, NHWC>(x, wpk, y, a, stream);
+    case 10: return launch_t<10, NHWC>(x, wpk, y, a, stream);
+    case 13: return launch_t<13, NHWC>(x, wpk, y, a, stream);
+    default: return -1;
+    }
 }
 
 }  // namespace
 
-bool f16_res_applies(const ConvShape& c, size_t copad_mult, const void* x, const void* y)
+bool f16_res_applies(const ConvShape& c, size_t copad_mult, const void* x, const void* y,
+                     bool nhwc)
 {
     ResArgs a;
-    return (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0 && plan(c, a, copad_mult);
+    return (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0 && plan(c, a, copad_mult, nhwc);
 }
 
 int launch_conv_f16_res(const uint16_t* x, const void* wpk, float* y, const ConvShape& c,
-                        size_t copad_mult, hipStream_t stream)
+                        size_t copad_mult, bool nhwc, hipStream_t stream)
 {
     ResArgs a;
     if (!wpk || (uintptr_t)wpk % 16 != 0 || (uintptr_t)x % 16 != 0 || (uintptr_t)y % 16 != 0)
         return -1;
-    if (!plan(c, a, copad_mult)) return -1;
+    if (!plan(c, a, copad_mult, nhwc)) return -1;
     const uint4* w4 = static_cast<const uint4*>(wpk);
-    switch (nb_of(a)) {
-    case 8: return launch_t<8>(x, w4, y, a, stream);
-    case 10: return launch_t<10>(x, w4, y, a, stream);
-    case 13: return launch_t<13>(x, w4, y, a, stream);
-    default: return -1;
-    }
+    return nhwc ? launch_nb<true>(x, w4, y, a, stream) : launch_nb<false>(x, w4, y, a, stream);
 }
 
 }  // namespace im2win

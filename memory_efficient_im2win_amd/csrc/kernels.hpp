@@ -126,10 +126,21 @@ int launch_conv_f16_wide(const uint16_t* x, const void* wpk, const uint16_t* w, 
 // of one image per workgroup. Used by launch_conv_f16_fused for prepacked
 // calls on the shapes it takes (f16_res_applies) that
 // would otherwise run on the wide-tile or channel-interleaved kernel (x and
-// y 16-byte aligned).
-bool f16_res_applies(const ConvShape& c, size_t copad_mult, const void* x, const void* y);
+// y 16-byte aligned). nhwc: x is N x Hi x Wi x Ci and y N x Ho x Wo x Co
+// (the fused NHWC call).
+bool f16_res_applies(const ConvShape& c, size_t copad_mult, const void* x, const void* y,
+                     bool nhwc = false);
 int launch_conv_f16_res(const uint16_t* x, const void* wpk, float* y, const ConvShape& c,
-                        size_t copad_mult, hipStream_t stream);
+                        size_t copad_mult, bool nhwc, hipStream_t stream);
+// The channel-interleaved filter entries of the wide-tile and resident-input
+// kernels, [(g*HWp + j)*Copad + co] = w[co][8g..8g+7][j], whatever kernel the
+// NCHW planner would pick for the shape.
+int launch_f16_interleaved_filter_pack(const uint16_t* w, void* wpk, const ConvShape& c,
+                                       hipStream_t stream);
+// Output channels of those entries are padded to a multiple of this; their
+// bytes: ceil(Ci/8) x HWp x Copad x 16.
+constexpr int kF16CoPad = 128;
+size_t f16_interleaved_filter_bytes(const ConvShape& c);
 
 // im2col + GEMM baseline: elements per im2col row (Ci*Hf*Wf padded to 32
 // bytes); the transform of N images into N*Ho*Wo rows; the GEMM over those

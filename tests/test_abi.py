@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
          "im2win_peak_probe", "im2win_peak_probe_flops"] +
         ["conv2d_im2col_workspace_bytes", "im2col_pack", "conv2d_im2col_fp32", "conv2d_im2col_fp16",
          "conv2d_direct_fp32", "conv2d_direct_fp16", "conv2d_im2win_nhwc_workspace_bytes",
-         "im2win_pack_nhwc", "conv2d_im2win_nhwc_fp32", "conv2d_im2win_nhwc_fp16"])
+         "im2win_pack_nhwc", "conv2d_im2win_nhwc_fp32", "conv2d_im2win_nhwc_fp16",
+         "conv2d_im2win_nhwc_fp16_fused_workspace_bytes", "conv2d_im2win_nhwc_fp16_fused"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -289,6 +290,27 @@ def test_nhwc_workspace_bytes():
     assert m.nhwc_workspace_bytes(1, 3, 4, 4, 2, 5, 5, 1, 2) == 0
 
 
+def test_nhwc_fused_workspace_bytes():
+    """The fused NHWC call's workspace is the channel-interleaved filter:
+    ceil(Ci/8) x (taps rounded up to even) x Co rounded up to 128 x 16 bytes,
+    256-aligned; 0 for an invalid shape."""
+    assert m.nhwc_fused_workspace_bytes(128, 96, 24, 24, 256, 5, 5, 1) == 12 * 26 * 256 * 16
+    assert m.nhwc_fused_workspace_bytes(2, 13, 9, 9, 40, 3, 3, 1) == \
+        -(-(2 * 10 * 128 * 16) // 256) * 256
+    assert m.nhwc_fused_workspace_bytes(1, 3, 4, 4, 2, 5, 5, 1) == 0
+
+
+def test_nhwc_fused_rejects_bad_arguments():
+    L = m.load_library()
+    f = L.conv2d_im2win_nhwc_fp16_fused
+    ok = (1, 96, 12, 12, 256, 5, 5, 1, 1)
+    assert f(None, FAKE, FAKE, None, 0, *ok, None) == _lib.IM2WIN_EINVAL
+    assert f(FAKE, FAKE, FAKE, None, 64, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    need = L.conv2d_im2win_nhwc_fp16_fused_workspace_bytes(*ok)
+    assert f(FAKE, FAKE, FAKE, FAKE, need - 16, *ok, None) == _lib.IM2WIN_EWORKSPACE
+    assert f(FAKE, FAKE, FAKE, None, 0, 1, 96, 12, 12, 256, 5, 5, 1, 0, None) == _lib.IM2WIN_EINVAL
+
+
 @pytest.mark.parametrize("fn", ["conv2d_im2win_nhwc_fp32", "conv2d_im2win_nhwc_fp16"])
 def test_nhwc_conv_rejects_bad_arguments(fn):
     L = m.load_library()
@@ -354,6 +376,10 @@ def test_conv_kernel_name():
     assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2) == "conv_f16_wide_kernel"
     assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2, "prepacked") == \
         "conv_f16_res_kernel"
+    assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2, "nhwc_prepacked") == \
+        "conv_f16_res_kernel"
+    assert m.conv_kernel_name(64, 64, 224, 224, 64, 7, 7, 2, 2, "nhwc_prepacked") == \
+        "conv_direct_nhwc_kernel"
     with m.knobs(f16_res=-1):
         assert m.conv_kernel_name(128, 96, 24, 24, 256, 5, 5, 1, 2, "prepacked") == \
             "conv_f16_wide_kernel"

@@ -111,3 +111,109 @@ def test_conv_nhwc_full_size_sampled(key, orc):
     got = y.permute(0, 3, 1, 2).reshape(-1)[torch.from_numpy(idx).to(dev)].cpu().numpy()
     assert_exact(got, ref, sh.describe())
     torch.cuda.synchronize()
+
+
+# Shapes of the fused NHWC kernel (resident input, prepacked filter): the
+# cv5 layer, two channel tiles with Wi and Wo odd, row stride 2, a channel
+# count that pads its last quad, 13- and 10-block one-row tiles, column
+# stride 2, and the NHWC pack shape above.
+RES_NHWC = [
+    (3, 96, 24, 24, 256, 5, 5, 1),
+    (2, 64, 17, 15, 512, 3, 5, 1),
+    (2, 56, 21, 23, 256, 3, 5, (2, 1)),
+    (1, 88, 13, 9, 256, 4, 5, 1),
+    (2, 32, 6, 200, 256, 5, 5, 1),
+    (1, 32, 5, 160, 256, 3, 9, 1),
+    (2, 32, 20, 24, 256, 3, 2, (1, 2)),
+    (1, 96, 12, 12, 256, 5, 5, (1, 2)),
+]
+
+
+def _run_fused(sh, x, w, out_nan=True):
+    import torch
+    dev = device()
+    nb = m.nhwc_fused_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s)
+    fws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    Ho, Wo = m.output_dims(sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s)
+    out = torch.full((sh.N, Ho, Wo, sh.Co), float("nan"), dtype=torch.float32, device=dev)
+    y = m.conv2d_nhwc_fused(to_dev(_nhwc(x), dev), to_dev(w, dev), sh.s, fws=fws, out=out)
+    y = y.cpu().numpy()
+    torch.cuda.synchronize()
+    return np.ascontiguousarray(y.transpose(0, 3, 1, 2))
+
+
+@pytest.mark.parametrize("t", RES_NHWC, ids=str)
+def test_conv_nhwc_fused(t, orc, knob):
+    """The fused NHWC fp16 call on the resident-input kernel: exact on
+    integer inputs, within tolerance on uniform ones, every output written
+    (NaN-filled output), the same bits on a repeated call; with the kernel
+    switched off (f16_res=-1) the call takes the direct kernel and gives the
+    same integers."""
+    sh = _shape(t, "f16")
+    device()
+    name = lambda: m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 2,
+                                      "nhwc_prepacked")
+    assert name() == "conv_f16_res_kernel"
+    x, w = workloads.make_inputs(sh, seed=71)
+    ref, absd = orc.conv_direct(x, w, sh.s, with_absdot=True)
+    xi, wi = workloads.make_inputs(sh, seed=72, mode="int")
+    refi = orc.conv_direct(xi, wi, sh.s)
+    note(f"conv nhwc fused {sh.describe()}")
+    a = _run_fused(sh, x, w)
+    assert_within(a, ref, absd, TOL["f16"], sh.describe())
+    assert np.array_equal(_run_fused(sh, x, w), a)
+    assert_exact(_run_fused(sh, xi, wi), refi, f"{sh.describe()} integer")
+    knob("f16_res", -1)
+    assert name() == "conv_direct_nhwc_kernel"
+    assert_exact(_run_fused(sh, xi, wi), refi, f"{sh.describe()} integer, direct kernel")
+
+
+def test_conv_nhwc_fused_special_values(orc):
+    """Infinities and NaN reach exactly the outputs whose windows hold them
+    through the fused NHWC kernel (its zero octets and padded K steps add
+    nothing)."""
+    sh = _shape((2, 88, 24, 24, 256, 5, 5, 1), "f16")
+    device()
+    assert m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 2,
+                              "nhwc_prepacked") == "conv_f16_res_kernel"
+    x, w = workloads.make_inputs(sh, seed=73)
+    x[0, 1, 4, 5] = np.inf
+    x[1, 2, 7, 10] = -np.inf
+    x[0, 0, 0, 6] = np.nan
+    x[1, sh.Ci - 1, sh.Hi - 1, sh.Wi - 1] = np.inf
+    w = (np.abs(w.astype(np.float32)) + np.float32(0.25)).astype(w.dtype)
+    ref = orc.conv_direct(x, w, sh.s)
+    fin = np.isfinite(ref)
+    _, absd = orc.conv_direct(np.where(np.isfinite(x), x, 0).astype(x.dtype), w, sh.s,
+                              with_absdot=True)
+    note(f"conv nhwc fused special values {sh.describe()}")
+    y = _run_fused(sh, x, w).astype(np.float64)
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+    assert_within(y[fin], ref[fin], absd[fin], TOL["f16"], "finite outputs")
+
+
+def test_conv_nhwc_fused_outside_envelope_and_errors(orc):
+    """Outside the kernel's envelope (Co not a multiple of 256) the fused
+    NHWC call takes the direct kernel; without a workspace too; a workspace
+    that is too small is refused before anything runs."""
+    import torch
+    dev = device()
+    sh = _shape((2, 16, 13, 14, 40, 3, 3, 1), "f16")
+    assert m.conv_kernel_name(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, 2,
+                              "nhwc_prepacked") == "conv_direct_nhwc_kernel"
+    xi, wi = workloads.make_inputs(sh, seed=74, mode="int")
+    refi = orc.conv_direct(xi, wi, sh.s)
+    note(f"conv nhwc fused fallback {sh.describe()}")
+    assert_exact(_run_fused(sh, xi, wi), refi, sh.describe())
+    xt, wt = to_dev(_nhwc(xi), dev), to_dev(wi, dev)
+    y = m.conv2d_nhwc_fused(xt, wt, sh.s).cpu().numpy()
+    assert_exact(np.ascontiguousarray(y.transpose(0, 3, 1, 2)), refi, f"{sh.describe()} no fws")
+    sh2 = _shape((1, 96, 12, 12, 256, 5, 5, 1), "f16")
+    nb = m.nhwc_fused_workspace_bytes(sh2.N, sh2.Ci, sh2.Hi, sh2.Wi, sh2.Co, sh2.Hf, sh2.Wf, sh2.s)
+    x2, w2 = workloads.make_inputs(sh2, seed=75, mode="int")
+    small = torch.empty(nb - 16, dtype=torch.uint8, device=dev)
+    with pytest.raises(RuntimeError):
+        m.conv2d_nhwc_fused(to_dev(_nhwc(x2), dev), to_dev(w2, dev), sh2.s, fws=small)
+    torch.cuda.synchronize()
