@@ -18,11 +18,16 @@
 //    rows Wi entries apart; cv5: 12 octets x 14 rows x 24 columns = 64.5 KB),
 //    and they stay there for the whole reduction: no stages, no barrier
 //    after the copy.
-//  * GEMM view: rows = the tile's pixels, columns = output channels, K =
-//    (channel quad q of 32, tap (kh, kw), channel). A K step of 32 is one tap
-//    of 32 channels; lanes 16g..16g+15 take octet 4q + g, so every lane's
-//    8-element slice is one aligned 16-byte read: from LDS for the pixels,
-//    from the prepacked filter for the channels. No tap is padded.
+//  * GEMM view: rows = the tile's pixels, columns = output channels (NHWC:
+//    the other way round, so a lane holds 4 consecutive channels of one
+//    output pixel), K = (channel quad q of 32, tap (kh, kw), channel). A K
+//    step of 32 is one tap of 32 channels; lanes 16g..16g+15 take octet
+//    4q + g, so every lane's 8-element slice is one aligned 16-byte read:
+//    from LDS for the pixels, from the prepacked filter for the channels. No
+//    tap is padded.
+//  * NHWC tensors (the fused NHWC call): the 8 channels of an input pixel
+//    are 16 contiguous bytes of x, so the tile's rows are copied into LDS as
+//    they lie, pixel-major with an odd number of entries per pixel.
 //  * 8 waves, two per SIMD. Waves w and w + 4 hold channels 64(w % 4) ..
 //    +63 (4 blocks of 16) and split the tile's pixel blocks of 16 (cv5: 13
 //    blocks as 7 + 6; 16 x 16 accumulators, 112 registers). Per K step a
@@ -33,7 +38,8 @@
 //    channels, which read half the LDS bytes).
 //  * The tile's input copy at the start and its 205 KB of output stores at
 //    the end are not overlapped with MFMAs: the 256 tiles of cv5 run in one
-//    round (cv5: 61 us, against 27 us of MFMA issue at the measured clock).
+//    round (cv5: 61-63 us, against 27-30 us of MFMA issue at the measured
+//    clock).
 #include <algorithm>
 
 #include "common.hpp"
@@ -44,7 +50,7 @@ namespace im2win {
 
 namespace {
 
-constexpr int kResCo = 256;               // output channels per tile (4 waves x 64)
+constexpr int kResCo = 256;               // output channels per tile (4 groups of 64)
 constexpr int kResLds = 160 * 1024;
 constexpr uint32_t kMissR = 0xFFFFFFF0u;  // vector offset past every accepted buffer
 
