@@ -47,7 +47,6 @@ constexpr int kNW = 4;                    // waves per workgroup
 constexpr int kNT = 64 * kNW;
 constexpr int kMaxSlices = 64;            // filter slices (c, kh) held in LDS
 constexpr int kBatch = 8;                 // row chunks a thread has in flight
-constexpr int kSlackT = 2048;             // A reads run one pair past the filter
 constexpr uint32_t kMissT = 0xFFFFFFF0u;  // vector offset past every accepted buffer
 constexpr int kGT = 16;                   // dword gather loads in flight per thread
 
@@ -81,10 +80,10 @@ struct ThinArgs {
 
 // NB: 32-pixel blocks per wave (2 x NB register tiles; NB = 2 leaves room
 // for four workgroups per CU, NB = 4 for two). XVEC: Wi % 8 == 0 and x
-// 16-byte aligned, so a row chunk is one 16-byte load; otherwise 8 two-byte
-// loads. M3: Wf >= 6, only the last B dword holds padded taps. WPK: the
-// filter comes prepacked (wp); otherwise each workgroup gathers its slices
-// from w.
+// 16-byte aligned, so a row chunk is one 16-byte load; otherwise a 16-byte
+// and a 4-byte load from the dword boundary at or below it, shifted. M3:
+// Wf >= 6, only the last B dword holds padded taps. WPK: the filter comes
+// prepacked (wp); otherwise each workgroup gathers its slices from w.
 template <int NB, bool XVEC, bool M3, bool WPK>
 __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16_t* __restrict__ x,
                                                                const uint4* __restrict__ wp,
@@ -259,10 +258,23 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
         T[j] = v;
     }
     // Rows: chunk e = (cl*RIN + i)*CH + cc holds columns 8cc .. 8cc+7 of LDS
-    // row i of channel cl (zeros past Wi and where no input row maps).
+    // row i of channel cl (zeros where no input row maps and from column Wi
+    // on, except in the chunk that holds column Wi - 1 of an odd-width row:
+    // its halves past the row hold the next elements of x, in columns >= Wi,
+    // which are only ever multiplied under the tap mask). Unaligned rows:
+    // the 8 halves of a chunk are the 20 bytes from the dword boundary at or
+    // below the chunk (a 16-byte and a 4-byte load, dword aligned), shifted
+    // down 2 bytes where the chunk starts between dwords, through a buffer
+    // that starts at the dword boundary at or below x; a chunk whose 20
+    // bytes would reach past x's end (only at x's last row) takes its halves
+    // one by one.
     {
         uint4* X = reinterpret_cast<uint4*>(smem + a.xoff);
         const __amdgpu_buffer_rsrc_t rx = raw_rsrc(x, a.xbytes);
+        const uint32_t xa = XVEC ? 0u : (uint32_t)((uintptr_t)x & 3);
+        const uint32_t rng = a.xbytes + xa;
+        const __amdgpu_buffer_rsrc_t ra =
+            raw_rsrc(reinterpret_cast<const unsigned char*>(x) - xa, rng);
         for (int e0 = 0; e0 < a.chunks; e0 += kBatch * kNT) {
             uint4 v[kBatch];
 #pragma unroll
@@ -284,7 +296,10 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
                 if (XVEC) {
                     const auto u = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)src, 0, 0);
                     v[k] = make_uint4(u[0], u[1], u[2], u[3]);
-                } else {
+                    continue;
+                }
+                const uint32_t sa = (src + xa) & ~3u;
+                if (src != kMissT && sa + 20 > rng) {
                     uint32_t d[4] = {0, 0, 0, 0};
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
@@ -292,6 +307,17 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
                                          rx, (int)(q < ncol ? src + 2 * q : kMissT), 0, 0)
                                      << (16 * (q & 1));
                     v[k] = make_uint4(d[0], d[1], d[2], d[3]);
+                } else {
+                    const bool hit = src != kMissT;
+                    const auto u = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(hit ? sa : kMissT),
+                                                                         0, 0);
+                    const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(
+                        ra, (int)(hit ? sa + 16 : kMissT), 0, 0);
+                    const uint32_t sh = ((src + xa) & 2u) * 8u;
+                    v[k] = make_uint4(__builtin_amdgcn_alignbit(u[1], u[0], sh),
+                                      __builtin_amdgcn_alignbit(u[2], u[1], sh),
+                                      __builtin_amdgcn_alignbit(u[3], u[2], sh),
+                                      __builtin_amdgcn_alignbit(t, u[3], sh));
                 }
             }
 #pragma unroll
@@ -447,7 +473,10 @@ bool plan(const ConvShape& c, ThinArgs& a)
     a.KT = (a.Sp + 8 + 3) & ~3;
     a.xoff = (uint32_t)a.Sp * 1024;
     const int64_t tab = a.xoff + chunks * 16;
-    const int64_t lds = tab + (a.KT * 4 + 15) / 16 * 16 + kSlackT;
+    // With an even slice count the A reads run one pair (2 KB) past the
+    // filter: within the rows when those are that large.
+    const int64_t lds = std::max<int64_t>(tab + (a.KT * 4 + 15) / 16 * 16,
+                                          ((int64_t)a.Sp + (a.S % 2 == 0 ? 2 : 0)) * 1024);
     if (lds > kThinLds) return false;
     a.chunks = (int)chunks;
     a.tab = (uint32_t)tab;

@@ -332,6 +332,7 @@ def test_conv_f16_row_staged_special_values(t, orc, knob):
     x[1, 3, 0, 6] = np.nan
     x[1, 0, 13, 15] = np.inf
     x[0, 0, 2, 7] = np.inf
+    x[-1, -1, -1, -1] = -np.inf     # x's last element
     w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
     ref = orc.conv_direct(x, w, sh.s)
     fin = np.isfinite(ref)
@@ -429,6 +430,7 @@ def test_conv_f16_row_reuse_special_values(t, orc):
     x[1, 3 % sh.Ci, 0, 6] = np.nan
     x[1, 0, sh.Hi - 1, sh.Wi - 1] = np.inf
     x[0, 0, 2, 7] = np.inf
+    x[-1, -1, -1, -1] = -np.inf     # x's last element
     w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
     ref = orc.conv_direct(x, w, sh.s)
     fin = np.isfinite(ref)
@@ -503,6 +505,7 @@ def test_conv_f16_materialised_staged_special_values(t, orc):
     x[1, 0, 0, 6] = np.nan
     x[1, 0, sh.Hi - 1, sh.Wi - 1] = np.inf
     x[0, 0, 2, 7] = np.inf
+    x[-1, -1, -1, -1] = -np.inf     # x's last element
     w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
     ref = orc.conv_direct(x, w, sh.s)
     fin = np.isfinite(ref)
@@ -598,6 +601,7 @@ def test_conv_f16_wide_special_values(t, orc):
     x[1, 3, 0, 6] = np.nan
     x[1, 0, 13, 13] = np.inf
     x[0, 0, 2, 7] = np.inf
+    x[-1, -1, -1, -1] = -np.inf     # x's last element
     w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
     ref = orc.conv_direct(x, w, sh.s)
     fin = np.isfinite(ref)
@@ -627,7 +631,7 @@ def test_conv_f16_filter_pack_tap_counts(t, orc):
 
 # Shapes the thin-layer fp16 kernel takes with a prepacked filter (Ci < 8,
 # Ci*Hf <= 64, Wf <= 8, even column stride; not taken by the row-staged
-# kernel): odd and even slice counts, odd widths (two-byte row loads) and
+# kernel): odd and even slice counts, odd widths (shifted dword-aligned row loads) and
 # widths that are multiples of 8 (16-byte row loads), several channel tiles,
 # row strides below and above the filter height, a 1x1 filter, cv3 images.
 THIN = [
@@ -660,7 +664,9 @@ def _thin_plan(sh, P=512):
     rin = (rows_max - 1) * sh_ + sh.Hf + kmax * max(0, sh.Hf - sh_)
     rp = -(-max(sh.Wi, (Wo - 1) * sw + 8) // 8) * 8
     kt = (Sp + 8 + 3) & ~3
-    lds = Sp * 1024 + sh.Ci * rin * (rp // 8) * 16 + (kt * 4 + 15) // 16 * 16 + 2048
+    # filter slices, rows, slice table; an even slice count reads 2 KB past the filter
+    lds = max(Sp * 1024 + sh.Ci * rin * (rp // 8) * 16 + (kt * 4 + 15) // 16 * 16,
+              (Sp + (2 if S % 2 == 0 else 0)) * 1024)
     return lds <= 160 * 1024, lds
 
 
@@ -707,6 +713,7 @@ def test_conv_f16_thin_special_values(t, orc):
     x[1, 1, 0, 6] = np.nan
     x[1, 0, 13, 15] = np.inf
     x[0, 0, 2, 7] = np.inf
+    x[-1, -1, -1, -1] = -np.inf     # x's last element (its row chunk is loaded half by half)
     w = np.abs(w) + np.asarray(0.25, dtype=w.dtype)
     ref = orc.conv_direct(x, w, sh.s)
     fin = np.isfinite(ref)
