@@ -52,7 +52,6 @@ constexpr int kJ = 4;                     // output rows per row group
 constexpr int kBufs = 3;                  // stage buffers: loads two stages ahead
 constexpr int kSlack = 2048;              // LDS past the last buffer (reads past a stage)
 constexpr uint32_t kMiss = 0xFFFFFFF0u;   // vector offset past every accepted buffer
-constexpr int kGL = 16;                   // most dword gather loads per thread and stage
 
 struct ReuseArgs {
     ConvShape c;
@@ -68,18 +67,11 @@ struct ReuseArgs {
     uint32_t dummy;                 // LDS byte offset of the landing kilobyte of unused loads
     uint32_t lds_bytes;
     uint32_t xbytes, ybytes, wbytes, worig;   // x, y, prepacked filter, filter in w's layout
-    uint32_t mask[4];               // B dwords: halves kw >= Wf cleared
-    // Dword filter gather (no prepacked filter, w 4-byte aligned): as in the
-    // row-staged kernel.
-    int gl, gjs, grs;
-    uint32_t RD, wco, wfm;
+    uint32_t mask[4];               // halves kw >= Wf cleared (B dwords, gathered filter entries)
     bool swz;                       // XCD-grouped tile order
     bool sync;                      // stages copied through registers, one buffer
     FastDiv divWo, divG;
 };
-
-
-
 
 template <int NWV, int DMAX, int HF, int SH, bool WPK>
 __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t* __restrict__ x,
@@ -327,96 +319,89 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
         }
     };
 
-    // Without a prepacked filter: entry (slice m, channel co0 + j) of stage
-    // sg holds the taps of w[co0 + j][sg*Cg + m/HF][m%HF][*] (zeros past Wf
-    // and Co).
-    auto gather = [&](int sg, int sb) {
-        const __amdgpu_buffer_rsrc_t rw = raw_rsrc(w, a.worig);
-        uint4* F = reinterpret_cast<uint4*>(smem + (size_t)sb * a.stage_bytes);
-        const int ne = a.S * 64;
-        for (int e0 = 0; e0 < ne; e0 += 2 * NT) {
-            uint32_t hv[2][8];
+    // Without a prepacked filter: entry e = (slice m, channel co0 + j), m =
+    // e / 64, j = e % 64, of stage sg holds the taps of
+    // w[co0 + j][sg*Cg + m/HF][m%HF][*] (zeros past Wf and Co), one run of
+    // Wf halves. Each thread builds kGE entries whole: a 16-byte load from
+    // the dword boundary at or below the run (and the next dword when Wf =
+    // 8) holds it, shifted down 2 bytes when the run starts between dwords;
+    // the halves kw >= Wf are cleared. A wave's 64 lanes take 16 consecutive
+    // channels x 4 consecutive slices (entry_of), so its loads touch few
+    // cache lines and each 8 lanes write 128 consecutive LDS bytes. w is
+    // read through a buffer that starts at the dword boundary at or below it;
+    // an entry whose loads would reach past w's end (only w's last run)
+    // takes its taps one by one. The loads of stage s+2 go out with stage
+    // s's direct loads and are written after its MFMAs.
+    constexpr int kGE = 4;   // entries per thread and stage (the planner keeps S*64 <= kGE*NT)
+    uint4 gu[kGE];
+    uint32_t gt[kGE], gs[kGE];
+    const uint32_t wal = (uint32_t)((uintptr_t)w & 3);
+    const uint32_t wrng = a.worig + wal;
+    // Byte offset in w of entry e's run in stage sg; kMiss past the stage's
+    // entries and channels.
+    // Entry k of this thread: lane l of wave v takes channel 16(v % 4) +
+    // l % 16 of slice 4(v / 4) + l / 16 + 8k (8 waves: slices 8k .. 8k+7).
+    static_assert(NWV % 4 == 0, "entry_of spreads 64 channels over groups of 4 waves");
+    auto entry_of = [&](int k) -> int {
+        const int lane = tid & 63, v = tid >> 6;
+        const int j = (lane & 15) + 16 * (v & 3);
+        const int m = (lane >> 4) + 4 * (v >> 2) + 4 * (NWV / 4) * k;
+        return m * 64 + j;
+    };
+    auto entry_src = [&](int sg, int e) -> uint32_t {
+        const int m = e >> 6, co = co0 + (e & 63);
+        const int c = sg * a.Cg + m / HF, kh = m - (m / HF) * HF;
+        return e < a.S * 64 && co < Co ? (uint32_t)((((co * Ci + c) * HF + kh) * a.c.Wf) * 2)
+                                       : kMiss;
+    };
+    auto gather_load = [&](int sg) {
+        const __amdgpu_buffer_rsrc_t ra =
+            raw_rsrc(reinterpret_cast<const unsigned char*>(w) - wal, wrng);
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int e = e0 + k * NT + tid;
-                const int m = e >> 6, co = co0 + (e & 63);
-                const int c = sg * a.Cg + m / HF, kh = m - (m / HF) * HF;
-                const uint32_t src = e < ne && co < Co
-                                         ? (uint32_t)((((co * Ci + c) * HF + kh) * a.c.Wf) * 2)
-                                         : kMiss;
+        for (int k = 0; k < kGE; ++k) {
+            const uint32_t src = entry_src(sg, entry_of(k));
+            const uint32_t sa = (src + wal) & ~3u;
+            const bool tail = src != kMiss && sa + 20 > wrng;
+            const bool hit = src != kMiss && !tail;
+            const auto u = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(hit ? sa : kMiss), 0, 0);
+            gu[k] = make_uint4(u[0], u[1], u[2], u[3]);
+            gt[k] = a.c.Wf == 8 ? __builtin_amdgcn_raw_buffer_load_b32(
+                                      ra, (int)(hit ? sa + 16 : kMiss), 0, 0)
+                                : 0u;
+            gs[k] = tail ? 1u : ((src + wal) & 2u) * 8u;
+        }
+    };
+    auto gather_store = [&](int sg, int sb) {
+        uint4* F = reinterpret_cast<uint4*>(smem + (size_t)sb * a.stage_bytes);
+        const __amdgpu_buffer_rsrc_t rw = raw_rsrc(w, a.worig);
+#pragma unroll
+        for (int k = 0; k < kGE; ++k) {
+            const int e = entry_of(k);
+            if (e >= a.S * 64) continue;
+            uint4 v;
+            if (gs[k] == 1u) {   // w's last run: tap by tap
+                const uint32_t src = entry_src(sg, e);
+                uint32_t hv[8];
 #pragma unroll
                 for (int q = 0; q < 8; ++q)
-                    hv[k][q] = __builtin_amdgcn_raw_buffer_load_b16(
+                    hv[q] = __builtin_amdgcn_raw_buffer_load_b16(
                         rw, (int)(q < a.c.Wf ? src + 2 * q : kMiss), 0, 0);
+                v = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                               hv[6] | (hv[7] << 16));
+            } else {
+                const uint4 u = gu[k];
+                v = make_uint4(__builtin_amdgcn_alignbit(u.y, u.x, gs[k]),
+                               __builtin_amdgcn_alignbit(u.z, u.y, gs[k]),
+                               __builtin_amdgcn_alignbit(u.w, u.z, gs[k]),
+                               __builtin_amdgcn_alignbit(gt[k], u.w, gs[k]));
             }
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int e = e0 + k * NT + tid;
-                if (e < ne)
-                    F[e] = make_uint4(hv[k][0] | (hv[k][1] << 16), hv[k][2] | (hv[k][3] << 16),
-                                      hv[k][4] | (hv[k][5] << 16), hv[k][6] | (hv[k][7] << 16));
-            }
+            v.x &= m0;
+            v.y &= m1;
+            v.z &= m2;
+            v.w &= m3;
+            F[e] = v;
         }
     };
-
-    // Dword gather (as in the row-staged kernel): a stage's taps for the
-    // tile's 64 channels are 64 runs of RD dwords in w, read with consecutive
-    // threads on consecutive dwords; each half goes to its slice's entry. The
-    // loads of stage s+2 go out with stage s's direct loads and are written
-    // to LDS after its MFMAs. Halves kw >= Wf of every entry are zeroed once.
-    uint32_t gv[kGL];
-    const int gj0 = tid / (int)a.RD, gq0 = tid - gj0 * (int)a.RD;
-    auto gather_load = [&](int sg) {
-        const __amdgpu_buffer_rsrc_t rw = raw_rsrc(w, a.worig);
-        const uint32_t base = (uint32_t)co0 * a.wco + (uint32_t)sg * a.RD * 4;
-        int j = gj0, r = gq0;
-        asm volatile("" : "+v"(j), "+v"(r));
-#pragma unroll
-        for (int i = 0; i < kGL; ++i) {
-            if (i < a.gl) {
-                const uint32_t src = j < 64 ? base + (uint32_t)j * a.wco + (uint32_t)r * 4 : kMiss;
-                gv[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, (int)src, 0, 0);
-            }
-            j += a.gjs;
-            r += a.grs;
-            if (r >= (int)a.RD) {
-                r -= (int)a.RD;
-                ++j;
-            }
-        }
-    };
-    auto gather_store = [&](int sb) {
-        uint16_t* F = reinterpret_cast<uint16_t*>(smem + (size_t)sb * a.stage_bytes);
-        int j = gj0, r = gq0;
-        asm volatile("" : "+v"(j), "+v"(r));
-#pragma unroll
-        for (int i = 0; i < kGL; ++i) {
-            if (i < a.gl && j < 64) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t t = 2 * (uint32_t)r + h;
-                    const uint32_t m = (t * a.wfm) >> 16;
-                    const uint32_t kw = t - m * (uint32_t)a.c.Wf;
-                    F[((m * 64 + j) << 3) + kw] = (uint16_t)(gv[i] >> (16 * h));
-                }
-            }
-            j += a.gjs;
-            r += a.grs;
-            if (r >= (int)a.RD) {
-                r -= (int)a.RD;
-                ++j;
-            }
-        }
-    };
-    const bool coal = !WPK && a.gl > 0;
-    if (coal && a.c.Wf < 8) {
-        for (int e = tid; e < kBufs * a.S * 64; e += NT) {
-            const int b = e / (a.S * 64);
-            uint16_t* F = reinterpret_cast<uint16_t*>(smem + (size_t)b * a.stage_bytes);
-            const int el = e - b * a.S * 64;
-            for (int kw = a.c.Wf; kw < 8; ++kw) F[el * 8 + kw] = 0;
-        }
-    }
 
     // sync: one buffer, each stage copied through registers after every
     // wave is done with the one before, and computed once it has landed (no
@@ -425,16 +410,13 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
     if (!sync) {
         issue(0, 0);
         if (a.NS > 1) issue(1, 1); else issue_none();
-        if (coal) {
+        if (!WPK) {
             gather_load(0);
-            gather_store(0);
+            gather_store(0, 0);
             if (a.NS > 1) {
                 gather_load(1);
-                gather_store(1);
+                gather_store(1, 1);
             }
-        } else if (!WPK) {
-            gather(0, 0);
-            if (a.NS > 1) gather(1, 1);
         }
     }
     const int npairs = a.Cg >> 1;
@@ -442,11 +424,9 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
         if (sync) {
             __syncthreads();   // every wave is done with the previous stage
             copy_stage(s, 0);
-            if (coal) {
+            if (!WPK) {
                 gather_load(s);
-                gather_store(0);
-            } else if (!WPK) {
-                gather(s, 0);
+                gather_store(s, 0);
             }
             __syncthreads();
         } else {
@@ -455,18 +435,13 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
             wait_vm<DMAX>();
             __syncthreads();      // every wave's; and stage s-1's buffer is free
             if (s + 2 < a.NS) issue(s + 2, (s + 2) % kBufs); else issue_none();
-            if (coal && s + 2 < a.NS) gather_load(s + 2);
+            if (!WPK && s + 2 < a.NS) gather_load(s + 2);
         }
         const unsigned char* A = smem + (size_t)(sync ? 0 : s % kBufs) * a.stage_bytes;
         const unsigned char* X = A + (size_t)a.S * 1024;
         for (int cp = 0; cp < npairs; ++cp) pair_mmas(A, X, cp);
         // Stage s+2's buffer was freed by the barrier above.
-        if (!sync && !WPK && s + 2 < a.NS) {
-            if (coal)
-                gather_store((s + 2) % kBufs);
-            else
-                gather(s + 2, (s + 2) % kBufs);
-        }
+        if (!sync && !WPK && s + 2 < a.NS) gather_store(s + 2, (s + 2) % kBufs);
     }
     wait_vm<0>();   // the last (unused) loads have landed before the workgroup ends
 
@@ -549,7 +524,8 @@ bool plan(const ConvShape& c, ReuseArgs& a, int& nwv, int& dmax)
         if (!dm) continue;
         const int64_t stage = (int64_t)(S + NX) * 1024;
         const int64_t lds = kBufs * stage + 1024 + kSlack;
-        if (lds > kLds) continue;
+        if (lds > kLds || S * 64 > 4 * 64 * nwv) continue;   // filter entries: 4 per thread
+
         a.Cg = cg;
         a.S = S;
         a.NX = NX;
@@ -646,25 +622,6 @@ int launch_conv_f16_reuse(const uint16_t* x, const void* wp, const uint16_t* w, 
     // Rows are fetched in 16-byte chunks from 16-byte boundaries.
     if ((uintptr_t)x % 16 != 0 || (uintptr_t)wp % 16 != 0) return -1;
     const uint4* w4 = static_cast<const uint4*>(wp);
-    a.gl = a.gjs = a.grs = 0;
-    a.RD = 1;
-    a.wco = a.wfm = 0;
-    if (!w4 && (uintptr_t)w % 4 == 0) {
-        // S is even (Cg even), so RD is whole; Ci is even, so every run
-        // starts on a dword.
-        const int nt = 64 * nwv;
-        const int rd = a.S * c.Wf / 2;
-        const int gl = ceil_div(64 * rd, nt);
-        const int64_t wco = (int64_t)c.Ci * c.Hf * c.Wf * 2;
-        if (gl <= kGL && (int64_t)ceil_div(c.Co, kCoT) * kCoT * wco < (int64_t)kMiss) {
-            a.gl = gl;
-            a.RD = (uint32_t)rd;
-            a.gjs = nt / rd;
-            a.grs = nt % rd;
-            a.wco = (uint32_t)wco;
-            a.wfm = (uint32_t)ceil_div(65536, c.Wf);
-        }
-    }
     return w4 ? launch_s<true>(dmax, x, w4, w, y, a, stream)
               : launch_s<false>(dmax, x, w4, w, y, a, stream);
 }

@@ -290,6 +290,66 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
         }
     };
 
+    // The same entries with each pair's run of taps read as whole dwords:
+    // the HW taps of w[co0 + k][8g + c][*] are one run of w, read from the
+    // dword boundary at or below it with four 16-byte loads (all issued
+    // before any is used; up to 29 taps) through a buffer that starts at the
+    // dword boundary at or below w, and shifted down 2 bytes when the run
+    // starts between dwords. A run whose 64 bytes would reach past w's end
+    // (only the last runs of w) is read tap by tap.
+    constexpr int kRunDW = 16;   // dwords loaded per run
+    const uint32_t wal = (uint32_t)((uintptr_t)w & 3);
+    const uint32_t wrng = a.worig + wal;
+    auto gather_w_runs = [&](int g, int sb) {
+        constexpr int NPR = 8 * kCoW / kNTW;
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(w, a.worig);
+        const __amdgpu_buffer_rsrc_t ra =
+            raw_rsrc(reinterpret_cast<const unsigned char*>(w) - wal, wrng);
+        unsigned short* F = reinterpret_cast<unsigned short*>(smem + (size_t)sb * a.stage_bytes);
+        uint32_t d[NPR][kRunDW];
+        uint32_t src[NPR], sh[NPR];
+        bool tail[NPR];
+#pragma unroll
+        for (int p = 0; p < NPR; ++p) {
+            const int pr = tid + p * kNTW, k = pr >> 3, c = pr & 7;
+            const int co = co0 + k, ch = 8 * g + c;
+            src[p] = co < Co && ch < Ci ? (uint32_t)(((int64_t)co * Ci + ch) * HW * 2) : kMissW;
+            const uint32_t sa = (src[p] + wal) & ~3u;
+            tail[p] = src[p] != kMissW && sa + 4 * kRunDW > wrng;
+            const bool hit = src[p] != kMissW && !tail[p];
+            sh[p] = ((src[p] + wal) & 2u) * 8u;
+#pragma unroll
+            for (int q = 0; q < kRunDW / 4; ++q) {
+                const auto u = __builtin_amdgcn_raw_buffer_load_b128(
+                    ra, (int)(hit ? sa + 16 * q : kMissW), 0, 0);
+                d[p][4 * q] = u[0];
+                d[p][4 * q + 1] = u[1];
+                d[p][4 * q + 2] = u[2];
+                d[p][4 * q + 3] = u[3];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < NPR; ++p) {
+            const int pr = tid + p * kNTW;
+            const int dst = pr;   // (k, c): half k*8 + c of each tap's 2 KB
+            if (tail[p]) {
+#pragma unroll
+                for (int j = 0; j < 2 * kRunDW - 2; ++j)
+                    if (j < a.HWp)
+                        F[j * kCoW * 8 + dst] = (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(
+                            r, (int)(j < HW ? src[p] + 2 * j : kMissW), 0, 0);
+                continue;
+            }
+#pragma unroll
+            for (int j = 0; j < 2 * kRunDW - 2; ++j) {
+                if (j >= a.HWp) break;
+                const uint32_t dw = __builtin_amdgcn_alignbit(d[p][(j >> 1) + 1], d[p][j >> 1], sh[p]);
+                const uint32_t hv = j < HW ? (dw >> (16 * (j & 1))) & 0xFFFFu : 0u;
+                F[j * kCoW * 8 + dst] = (unsigned short)hv;
+            }
+        }
+    };
+
     // Window offsets of the taps in filter order j = kh*Wf + kw, from the
     // pixel's tap (0, 0): kh*RS + (kw % sw)*NU + kw / sw. Entries from HW on
     // repeat tap HW-1 (reads of those are unused or zeroed).
@@ -351,7 +411,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
     if (WPK) {
         if (sync) copy_w(0, 0); else dma_w(0, 0);
     } else {
-        gather_w(0, 0);
+        if (HW <= 2 * kRunDW - 3) gather_w_runs(0, 0); else gather_w(0, 0);
     }
     load_x(0);
     store_x(0);
@@ -361,7 +421,7 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
     for (int g = 0; g < a.CG; ++g) {
         if (sync && g > 0) {
             __syncthreads();   // every wave is done with group g-1
-            if (WPK) copy_w(g, 0); else gather_w(g, 0);
+            if (WPK) copy_w(g, 0); else if (HW <= 2 * kRunDW - 3) gather_w_runs(g, 0); else gather_w(g, 0);
             load_x(g);
             store_x(0);
         }
@@ -416,7 +476,9 @@ __global__ __launch_bounds__(64 * NW) void conv_f16_wide_kernel(const uint16_t* 
         }
         if (!sync && g + 1 < a.CG) {
             store_x((g + 1) & 1);
-            if (!WPK) gather_w(g + 1, (g + 1) & 1);
+            if (!WPK) {
+                if (HW <= 2 * kRunDW - 3) gather_w_runs(g + 1, (g + 1) & 1); else gather_w(g + 1, (g + 1) & 1);
+            }
         }
     }
 
