@@ -48,7 +48,6 @@ constexpr int kNT = 64 * kNW;
 constexpr int kMaxSlices = 64;            // filter slices (c, kh) held in LDS
 constexpr int kBatch = 8;                 // row chunks a thread has in flight
 constexpr uint32_t kMissT = 0xFFFFFFF0u;  // vector offset past every accepted buffer
-constexpr int kGT = 16;                   // dword gather loads in flight per thread
 
 struct ThinArgs {
     ConvShape c;
@@ -66,12 +65,6 @@ struct ThinArgs {
     uint32_t xbytes, ybytes, wbytes, worig;   // x, y, prepacked filter, filter in w's layout
     uint32_t mask[4];               // B dwords: halves kw >= Wf cleared
     FastDiv divWo, divHo, divCH, divRIN;
-    // Dword filter gather (no prepacked filter, w 4-byte aligned, Ci*Hf*Wf
-    // and Wf at least 2): the tile's filter is one run of 64*chw halves
-    // (chw = Ci*Hf*Wf per channel); chwm = ceil(2^32 / chw), wfm =
-    // ceil(2^32 / Wf). gd = 0: one 16-byte entry per thread and load round.
-    int gd;
-    uint32_t chw, chwm, wfm;
     bool swz;                       // XCD-grouped tile order
     bool sync;                      // filter copied through registers
 };
@@ -177,70 +170,68 @@ __global__ __launch_bounds__(kNT, 8 / NB) void conv_f16_thin_kernel(const uint16
         const __amdgpu_buffer_rsrc_t r = raw_rsrc(wp, a.wbytes);
         for (int m = wave; m < a.S; m += kNW)
             lds_dma16(r, lbase + (uint32_t)m * 1024, (uint32_t)((m * a.Copad + co0 + lane) * 16));
-    } else if (a.gd) {
-        // The tile's 64 channels' taps are one run of w: consecutive
-        // threads read consecutive dwords of it, and each half goes to its
-        // entry (channel j = f / chw of the tile, slice t / Wf, column
-        // t % Wf, t = f % chw). Channels past Co fall outside w's range and
-        // read zeros; the halves kw >= Wf of every entry are zeroed here too.
-        const __amdgpu_buffer_rsrc_t r = raw_rsrc(w, a.worig);
-        unsigned short* F = reinterpret_cast<unsigned short*>(smem);
-        const uint32_t base = (uint32_t)co0 * a.chw * 2;
-        const int nd = 32 * (int)a.chw;
-        for (int d0 = 0; d0 < nd; d0 += kGT * kNT) {
-            int dd = d0 + tid;
-            // Opaque: keeps the per-round index math inside the round.
-            asm volatile("" : "+v"(dd));
-            uint32_t v[kGT];
-#pragma unroll
-            for (int k = 0; k < kGT; ++k) {
-                const int d = dd + k * kNT;
-                v[k] = __builtin_amdgcn_raw_buffer_load_b32(
-                    r, (int)(d < nd ? base + 4 * (uint32_t)d : kMissT), 0, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < kGT; ++k) {
-                const int d = dd + k * kNT;
-                if (d < nd) {
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const uint32_t f = 2 * (uint32_t)d + e;
-                        const uint32_t j = __umulhi(f, a.chwm);
-                        const uint32_t t = f - j * a.chw;
-                        const uint32_t m = __umulhi(t, a.wfm);
-                        const uint32_t kw = t - m * (uint32_t)a.c.Wf;
-                        F[(m * 64 + j) * 8 + kw] = (unsigned short)(v[k] >> (16 * e));
-                    }
-                }
-            }
-        }
-        if (a.c.Wf < 8)
-            for (int e = tid; e < a.S * 64; e += kNT)
-                for (int kw = a.c.Wf; kw < 8; ++kw) F[e * 8 + kw] = 0;
     } else {
+        // Without a prepacked filter: entry m*64 + j holds the Wf taps of
+        // w[co0 + j][c][kh][*] (m = c*Hf + kh), one run of w at element
+        // (co*S + m)*Wf: a 16-byte load from the dword boundary at or below
+        // it (and the next dword when Wf = 8), shifted down 2 bytes when the
+        // run starts between dwords, taps kw >= Wf cleared. w is read through
+        // a buffer that starts at the dword boundary at or below it; an entry
+        // whose loads would reach past w's end is read tap by tap. Wave v
+        // takes channels 16v .. 16v+15, lane l channel 16v + l % 16 of
+        // slices 4i + l / 16, so a wave's loads touch few cache lines and
+        // each 8 lanes write 128 consecutive LDS bytes.
         const __amdgpu_buffer_rsrc_t r = raw_rsrc(w, a.worig);
+        const uint32_t wal = (uint32_t)((uintptr_t)w & 3);
+        const uint32_t wrng = a.worig + wal;
+        const __amdgpu_buffer_rsrc_t ra =
+            raw_rsrc(reinterpret_cast<const unsigned char*>(w) - wal, wrng);
         uint4* F = reinterpret_cast<uint4*>(smem);
-        const int ne = a.S * 64;
-        for (int e0 = 0; e0 < ne; e0 += 4 * kNT) {
-            uint32_t hv[4][8];
+        const int jc = (lane & 15) + 16 * wave;
+        const int co = co0 + jc;
+        constexpr int kRE = 4;   // entries per thread with loads in flight together
+        for (int i0 = 0; 4 * i0 < a.S; i0 += kRE) {
+            uint4 u[kRE];
+            uint32_t t[kRE], sh[kRE], src[kRE];
+            bool tl[kRE];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int e = e0 + k * kNT + tid;
-                const int m = e >> 6, co = co0 + (e & 63);
-                const uint32_t src = e < ne && co < Co
-                                         ? (uint32_t)((co * Ci * Hf + m) * a.c.Wf * 2)
-                                         : kMissT;
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    hv[k][q] = __builtin_amdgcn_raw_buffer_load_b16(
-                        r, (int)(q < a.c.Wf ? src + 2 * q : kMissT), 0, 0);
+            for (int k = 0; k < kRE; ++k) {
+                const int m = 4 * (i0 + k) + (lane >> 4);
+                src[k] = m < a.S && co < Co ? (uint32_t)((co * a.S + m) * a.c.Wf * 2) : kMissT;
+                const uint32_t sa = (src[k] + wal) & ~3u;
+                tl[k] = src[k] != kMissT && sa + 20 > wrng;
+                const bool hit = src[k] != kMissT && !tl[k];
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(hit ? sa : kMissT), 0, 0);
+                u[k] = make_uint4(v[0], v[1], v[2], v[3]);
+                t[k] = a.c.Wf == 8 ? __builtin_amdgcn_raw_buffer_load_b32(
+                                         ra, (int)(hit ? sa + 16 : kMissT), 0, 0)
+                                   : 0u;
+                sh[k] = ((src[k] + wal) & 2u) * 8u;
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int e = e0 + k * kNT + tid;
-                if (e < ne)
-                    F[e] = make_uint4(hv[k][0] | (hv[k][1] << 16), hv[k][2] | (hv[k][3] << 16),
-                                      hv[k][4] | (hv[k][5] << 16), hv[k][6] | (hv[k][7] << 16));
+            for (int k = 0; k < kRE; ++k) {
+                const int m = 4 * (i0 + k) + (lane >> 4);
+                if (m >= a.S) continue;
+                uint4 e;
+                if (tl[k]) {
+                    uint32_t hv[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        hv[q] = __builtin_amdgcn_raw_buffer_load_b16(
+                            r, (int)(q < a.c.Wf ? src[k] + 2 * q : kMissT), 0, 0);
+                    e = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16),
+                                   hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
+                } else {
+                    e = make_uint4(__builtin_amdgcn_alignbit(u[k].y, u[k].x, sh[k]),
+                                   __builtin_amdgcn_alignbit(u[k].z, u[k].y, sh[k]),
+                                   __builtin_amdgcn_alignbit(u[k].w, u[k].z, sh[k]),
+                                   __builtin_amdgcn_alignbit(t[k], u[k].w, sh[k]));
+                }
+                e.x &= a.mask[0];
+                e.y &= a.mask[1];
+                e.z &= a.mask[2];
+                e.w &= a.mask[3];
+                F[m * 64 + jc] = e;
             }
         }
     }
@@ -550,21 +541,6 @@ int launch_conv_f16_thin(const uint16_t* x, const void* wp, const uint16_t* w, f
     const uint4* w4 = static_cast<const uint4*>(wp);
     const bool xvec = c.Wi % 8 == 0 && (uintptr_t)x % 16 == 0;
     const bool nb2 = a.P == 32 * kNW * 2;
-    a.gd = 0;
-    a.chw = (uint32_t)(c.Ci * c.Hf * c.Wf);
-    a.chwm = a.wfm = 0;
-    // The run of a tile starts at co0*chw halves, co0 a multiple of 64:
-    // on a dword when w is. Co*chw even: w ends on a dword, so no dword
-    // holds both a last tap and bytes past w (a range check zeroes such a
-    // dword whole). Offsets up to the last tile's end must stay below the
-    // miss offset.
-    if (!w4 && (uintptr_t)w % 4 == 0 && a.chw >= 2 && c.Wf >= 2 &&
-        ((int64_t)c.Co * a.chw) % 2 == 0 &&
-        (int64_t)a.co_tiles * 64 * a.chw * 2 < (int64_t)kMissT) {
-        a.gd = 1;
-        a.chwm = (uint32_t)(((uint64_t)1 << 32) / a.chw + 1);
-        a.wfm = (uint32_t)(((uint64_t)1 << 32) / (uint64_t)c.Wf + 1);
-    }
     if (w4) return nb2 ? launch_nb<2, true>(x, w4, w, y, a, xvec, stream)
                        : launch_nb<4, true>(x, w4, w, y, a, xvec, stream);
     return nb2 ? launch_nb<2, false>(x, w4, w, y, a, xvec, stream)
