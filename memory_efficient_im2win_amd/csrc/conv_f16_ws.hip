@@ -40,6 +40,11 @@ namespace im2win {
 
 namespace {
 
+template <int K>
+struct IC {
+    static constexpr int value = K;
+};
+
 constexpr int kWsLds = 160 * 1024;
 constexpr int kCoT = 64;                  // output channels per tile
 constexpr int kNB = 4;                    // 32-pixel blocks per wave
@@ -218,30 +223,39 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
     // Filter slices of stage sg in window order: entry (slice m, channel
     // co0 + e) holds w[co0 + e][sg*Cg + m/M][kh][kw] at position p of the
     // slice for window position jj = 8*(m % M) + p = kw*Hf + kh (zeros past
-    // Wf*Hf and past Co).
-    auto gather = [&](int sg, int sb) {
+    // Wf*Hf and past Co). gather_load issues the 2-byte loads of a thread's
+    // first entry (for the next stage, before this stage's MFMAs, so their
+    // latency is covered; the registers for more are not there);
+    // gather_store loads the rest and writes them all.
+    // The early loads need registers the 4-wave form and the forms with
+    // more than 10 direct loads per wave do not have.
+    constexpr bool kPre = NWV == 8 && DMAX <= 10;
+    uint32_t hv[2][8];
+    auto entry_loads = [&](int sg, int e, auto K) __attribute__((always_inline)) {
+        constexpr int k = decltype(K)::value;
         const __amdgpu_buffer_rsrc_t rw = raw_rsrc(w, a.worig);
+        const int m = e >> 6, co = co0 + (e & 63);
+        const int cl = m / M, ms = m - cl * M;
+        const int c = sg * a.Cg + cl;
+        const bool ok = e < a.S * 64 && co < Co;
+        const uint32_t base = (uint32_t)(((int64_t)co * Ci + c) * HW * 2);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int jj = 8 * ms + p;
+            const int kw = jj / Hf, kh = jj - kw * Hf;
+            hv[k][p] = __builtin_amdgcn_raw_buffer_load_b16(
+                rw, (int)(ok && jj < HW ? base + (uint32_t)(kh * Wf + kw) * 2 : kMiss), 0, 0);
+        }
+    };
+    auto gather_load = [&](int sg) __attribute__((always_inline)) {
+        entry_loads(sg, tid, IC<0>{});
+    };
+    auto gather_store = [&](int sg, int sb) __attribute__((always_inline)) {
         uint4* F = reinterpret_cast<uint4*>(smem + (size_t)sb * a.stage_bytes);
         const int ne = a.S * 64;
         for (int e0 = 0; e0 < ne; e0 += 2 * NT) {
-            uint32_t hv[2][8];
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int e = e0 + k * NT + tid;
-                const int m = e >> 6, co = co0 + (e & 63);
-                const int cl = m / M, ms = m - cl * M;
-                const int c = sg * a.Cg + cl;
-                const bool ok = e < ne && co < Co;
-                const uint32_t base = (uint32_t)(((int64_t)co * Ci + c) * HW * 2);
-#pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    const int jj = 8 * ms + p;
-                    const int kw = jj / Hf, kh = jj - kw * Hf;
-                    hv[k][p] = __builtin_amdgcn_raw_buffer_load_b16(
-                        rw, (int)(ok && jj < HW ? base + (uint32_t)(kh * Wf + kw) * 2 : kMiss), 0,
-                        0);
-                }
-            }
+            if (e0 > 0) entry_loads(sg, e0 + tid, IC<0>{});
+            entry_loads(sg, e0 + NT + tid, IC<1>{});
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int e = e0 + k * NT + tid;
@@ -250,6 +264,10 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
                                       hv[k][4] | (hv[k][5] << 16), hv[k][6] | (hv[k][7] << 16));
             }
         }
+    };
+    auto gather = [&](int sg, int sb) __attribute__((always_inline)) {
+        gather_load(sg);
+        gather_store(sg, sb);
     };
 
     floatx16_t acc[2][kNB];
@@ -340,6 +358,7 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
             wait_vm<0>();
             __syncthreads();
             if (s + 1 < a.NS) issue(s + 1, (s + 1) % kBufs); else issue_none();
+            if (kPre && s + 1 < a.NS) gather_load(s + 1);
         }
 
         const unsigned char* A = smem + (size_t)(sync ? 0 : s % kBufs) * a.stage_bytes;
@@ -361,7 +380,12 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_ws_kernel(const uint16_t* _
         }
         if (t < nk) mma(f0);
         // The next stage's filter goes to the buffer freed by the barrier.
-        if (!sync && s + 1 < a.NS) gather(s + 1, (s + 1) % kBufs);
+        if (!sync && s + 1 < a.NS) {
+            if (kPre)
+                gather_store(s + 1, (s + 1) % kBufs);
+            else
+                gather(s + 1, (s + 1) % kBufs);
+        }
     }
     wait_vm<0>();
 
