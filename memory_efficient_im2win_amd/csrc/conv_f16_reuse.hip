@@ -332,7 +332,9 @@ __global__ __launch_bounds__(64 * NWV) void conv_f16_reuse_kernel(const uint16_t
     // an entry whose loads would reach past w's end (only w's last run)
     // takes its taps one by one. The loads of stage s+2 go out with stage
     // s's direct loads and are written after its MFMAs.
-    constexpr int kGE = 4;   // entries per thread and stage (the planner keeps S*64 <= kGE*NT)
+    // Entries per thread and stage: S = Cg*HF <= 4*HF slices of 64 entries
+    // over NT threads.
+    constexpr int kGE = (4 * HF + NWV - 1) / NWV;
     uint4 gu[kGE];
     uint32_t gt[kGE], gs[kGE];
     const uint32_t wal = (uint32_t)((uintptr_t)w & 3);
@@ -524,7 +526,7 @@ bool plan(const ConvShape& c, ReuseArgs& a, int& nwv, int& dmax)
         if (!dm) continue;
         const int64_t stage = (int64_t)(S + NX) * 1024;
         const int64_t lds = kBufs * stage + 1024 + kSlack;
-        if (lds > kLds || S * 64 > 4 * 64 * nwv) continue;   // filter entries: 4 per thread
+        if (lds > kLds || S > (4 * c.Hf + nwv - 1) / nwv * nwv) continue;   // gather entries
 
         a.Cg = cg;
         a.S = S;
