@@ -302,6 +302,7 @@ int launch_conv_f32(const float* x, const float* ws, const float* w, float* y,
         best_px = px;
         if (tiles >= 2 * kCUs) break;
     }
+    if (best_px == 0) return -1;   // not even one row set of a 64-pixel tile fits LDS
     const int px = best_px;
     a.P = 64 * px;
     a.rows_max = (a.P - 1) / c.Wo + 2;

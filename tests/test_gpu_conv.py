@@ -90,6 +90,22 @@ def test_conv_f32_vector_alu_path(t, orc, knob):
     assert_exact(_run(sh, "f32", xi, wi), orc.conv_direct(xi, wi, sh.s), sh.describe())
 
 
+@pytest.mark.parametrize("t", [(1, 1, 12, 2000, 8, 11, 3, 1), (1, 2, 14, 1500, 4, 9, 5, (1, 2))],
+                         ids=str)
+def test_conv_f32_vector_alu_rows_past_lds(t, orc, knob):
+    """Rows too long for the vector-ALU kernel's LDS (one im2win row set of a
+    64-pixel tile above 64 KB): the call still gives the exact result, fused
+    and from the materialised tensor (the planner declines and the generic
+    kernel runs)."""
+    knob("f32_valu", 1)
+    sh = _shape(t, "f32")
+    xi, wi = workloads.make_inputs(sh, seed=22, mode="int")
+    ref = orc.conv_direct(xi, wi, sh.s)
+    for kind in (None, "full"):
+        note(f"conv fp32 vector ALU long rows {sh.describe()} ws={kind}")
+        assert_exact(_run(sh, "f32", xi, wi, kind), ref, f"{sh.describe()} ws={kind}")
+
+
 @pytest.mark.parametrize("ksplit", [1, 4, 8, 12])
 @pytest.mark.parametrize("t", [(1, 96, 12, 12, 256, 5, 5, 1), (2, 16, 20, 20, 40, 3, 3, 1),
                                (3, 7, 26, 26, 33, 5, 5, 1), (1, 3, 40, 40, 20, 11, 11, 4),
