@@ -231,14 +231,19 @@ int conv2d_direct_fp16(const uint16_t *x, const uint16_t *w, float *y, int N, in
  * im2win_pack_nhwc: that transform (bit copy, elem_bytes 2 or 4).
  * conv2d_im2win_nhwc_workspace_bytes: 0 without materialize; with it, the
  *     bytes of [filter in window order, rounded up to 256 | the NHWC im2win
- *     tensor of the whole batch].
+ *     tensor of the whole batch], where each column's run of Hf*Ci elements
+ *     is stored in pitch = Hf*Ci rounded up to 32 bytes (16 halves, 8
+ *     floats), zeros after it, and each filter row holds Wf such runs:
+ *         ws[((n*Ho + ho)*Wi + w)*pitch + kh*Ci + c] = x[n][ho*sh + kh][w][c]
+ *         wr[co*Wf*pitch + kw*pitch + kh*Ci + c]    = w[co][c][kh][kw]
+ *     (pitch == Hf*Ci, the tensor above unchanged, when Ci*elem_bytes is a
+ *     multiple of 32).
  * conv2d_im2win_nhwc_fp32 / _fp16: ws == NULL and ws_bytes == 0: direct
  *     convolution (one thread per output). ws (16-byte aligned) with at least
  *     the filter part and one image's tensor: materialised; the tensor of as
- *     many images as fit is packed and multiplied on the matrix cores, window
- *     runs as GEMM rows, when Ci is a multiple of 16 (fp16) or 8 (fp32) and x
- *     is 16-byte aligned; other shapes take the direct kernel. A workspace
- *     given but too small: IM2WIN_EWORKSPACE.
+ *     many images as fit is packed and multiplied on the matrix cores, the
+ *     padded window runs as GEMM rows, for every shape. A workspace given
+ *     but too small: IM2WIN_EWORKSPACE.
  */
 size_t conv2d_im2win_nhwc_workspace_bytes(int materialize, int N, int Ci, int Hi, int Wi, int Co,
                                           int Hf, int Wf, int sh, int sw, size_t elem_bytes);

@@ -220,12 +220,13 @@ int direct_driver(const T* x, const T* w, float* y, int N, int Ci, int Hi, int W
                              stream));
 }
 
-// NHWC workspace: [filter in window order, rounded up to 256 bytes | NHWC
-// im2win tensor of a chunk of images].
+// NHWC workspace: [filter in the padded window order, rounded up to 256
+// bytes | NHWC im2win tensor of a chunk of images, column runs padded to the
+// pitch].
 ColPlan nhwc_plan(const ConvShape& c, size_t elem)
 {
-    return ColPlan{align_up((size_t)c.Co * c.Ci * c.Hf * c.Wf * elem),
-                   (size_t)c.Ho * c.Wi * c.Hf * c.Ci * elem};
+    const size_t pitch = (size_t)im2win::nhwc_pitch(c, (int)elem);
+    return ColPlan{align_up((size_t)c.Co * c.Wf * pitch * elem), (size_t)c.Ho * c.Wi * pitch * elem};
 }
 
 template <typename T>
@@ -246,10 +247,6 @@ int nhwc_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int
     const ColPlan p = nhwc_plan(c, sizeof(T));
     if (ws_bytes < p.fbytes + p.per_image) return IM2WIN_EWORKSPACE;
     if (!aligned(ws, 16)) return IM2WIN_EINVAL;
-    // Window slices must be whole 16-byte loads (Ci a multiple of 16 halves or
-    // 8 floats, x 16-byte aligned); other shapes take the direct kernel.
-    if (!im2win::nhwc_gemm_applies(c, e) || !aligned(x, 16))
-        return status_of(im2win::launch_conv_direct_nhwc(x, w, y, c, e, stream));
     unsigned char* wsb = static_cast<unsigned char*>(ws);
     int rc = im2win::launch_filter_khwc(w, wsb, c, e, stream);
     if (rc != 0) return status_of(rc);
@@ -263,7 +260,7 @@ int nhwc_driver(const T* x, const T* w, float* y, void* ws, size_t ws_bytes, int
     for (int n0 = 0; n0 < N; n0 += chunk) {
         ConvShape cc = c;
         cc.N = std::min(chunk, N - n0);
-        rc = im2win::launch_pack_nhwc(x + n0 * x_img, wsb + p.fbytes, cc, e, stream);
+        rc = im2win::launch_pack_nhwc_padded(x + n0 * x_img, wsb + p.fbytes, cc, e, stream);
         if (rc != 0) return status_of(rc);
         rc = im2win::launch_nhwc_gemm(wsb + p.fbytes, wsb, y + n0 * y_img, cc, e, stream);
         if (rc != 0) return status_of(rc);

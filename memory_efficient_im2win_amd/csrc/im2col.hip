@@ -543,19 +543,12 @@ int launch_im2col_gemm(const void* col, const void* w, void* wpad, float* y, con
     return launch_gemm(col, wpad, y, g, c.Co, elem, stream);
 }
 
-bool nhwc_gemm_applies(const ConvShape& c, int elem)
-{
-    // Window runs of whole slices (K = Wf*Hf*Ci), each slice 16 aligned bytes.
-    return c.Ci % (elem == 2 ? 16 : 8) == 0;
-}
-
 int launch_nhwc_gemm(const void* ws, const void* wr, float* y, const ConvShape& c, int elem,
                      hipStream_t stream)
 {
-    if (!nhwc_gemm_applies(c, elem)) return -1;
     GemmArgs g{};
     g.Co = c.Co;
-    g.HfC = c.Hf * c.Ci;
+    g.HfC = nhwc_pitch(c, elem);   // runs padded to a multiple of 32 bytes
     g.KP = c.Wf * g.HfC;
     g.P = c.Ho * c.Wo;
     g.rows = (int64_t)c.N * g.P;

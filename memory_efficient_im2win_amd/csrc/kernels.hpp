@@ -151,12 +151,16 @@ int launch_im2col_gemm(const void* col, const void* w, void* wpad, float* y, con
                        int elem, hipStream_t stream);
 
 // NHWC (x: N x Hi x Wi x Ci, y: N x Ho x Wo x Co): the im2win transform
-// ws[n][ho][w][kh][c] = x[n][ho*sh + kh][w][c]; the filters reordered to
-// the window order wr[co][(kw*Hf + kh)*Ci + c]; the GEMM over the window
-// runs of ws (when nhwc_gemm_applies); the direct kernel.
+// ws[n][ho][w][kh][c] = x[n][ho*sh + kh][w][c] (unpadded, and with each
+// column's Hf*Ci run padded with zeros to nhwc_pitch elements, a multiple of
+// 32 bytes); the filters reordered to the padded window order
+// wr[co][kw*pitch + kh*Ci + c]; the GEMM over the padded window runs; the
+// direct kernel.
+int nhwc_pitch(const ConvShape& c, int elem);
 int launch_pack_nhwc(const void* x, void* ws, const ConvShape& c, int elem, hipStream_t stream);
+int launch_pack_nhwc_padded(const void* x, void* ws, const ConvShape& c, int elem,
+                            hipStream_t stream);
 int launch_filter_khwc(const void* w, void* wr, const ConvShape& c, int elem, hipStream_t stream);
-bool nhwc_gemm_applies(const ConvShape& c, int elem);
 int launch_nhwc_gemm(const void* ws, const void* wr, float* y, const ConvShape& c, int elem,
                      hipStream_t stream);
 int launch_conv_direct_nhwc(const void* x, const void* w, float* y, const ConvShape& c, int elem,

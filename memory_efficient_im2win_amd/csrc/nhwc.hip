@@ -5,14 +5,18 @@
 // the channels innermost:
 //     ws[n][ho][w][kh][c] = x[n][ho*sh + kh][w][c],
 // so the window of output (ho, wo) is the one contiguous run of Wf*Hf*Ci
-// elements at wo*sw*Hf*Ci in row (n, ho), ordered (kw, kh, c). With Ci a
-// multiple of the matrix-core slice, every 8- or 4-element K slice of a
-// window is 16 contiguous, aligned bytes, whatever the strides.
+// elements at wo*sw*Hf*Ci in row (n, ho), ordered (kw, kh, c). The
+// convolution packs each column's Hf*Ci run into `pitch` elements, Hf*Ci
+// rounded up to 32 bytes with zeros after it (no padding when Ci*elem is a
+// multiple of 32): every 32-byte K slice of a window is then contiguous and
+// aligned, whatever Ci and the strides, at the cost of multiplying the zeros.
 //
-//  * pack_nhwc_kernel: the transform (16-byte chunks when Ci*elem is a
-//    multiple of 16, elements otherwise).
-//  * filter_khwc_kernel: filters reordered to the window order,
-//    wr[co][(kw*Hf + kh)*Ci + c] = w[co][c][kh][kw].
+//  * pack_nhwc_kernel: the transform, unpadded (16-byte chunks when Ci*elem
+//    is a multiple of 16, elements otherwise).
+//  * pack_nhwc_pad_kernel: the transform with runs padded to the pitch.
+//  * filter_khwc_kernel: filters reordered to the window order, padded the
+//    same way: wr[co][kw*pitch + kh*Ci + c] = w[co][c][kh][kw], zero past
+//    Hf*Ci in each run.
 //  * conv_direct_nhwc_kernel: one thread per output, channels of an output
 //    pixel in consecutive lanes (they share its window).
 // The convolution over the packed tensor is the matrix-core GEMM of
@@ -42,19 +46,58 @@ __global__ __launch_bounds__(256) void pack_nhwc_kernel(const V* __restrict__ x,
     ws[e] = x[((n * c.Hi + (int64_t)ho * c.sh + kh) * c.Wi + w) * cv + cc];
 }
 
+// The transform with each column's run padded: chunk e (16 bytes, P
+// elements) of ws = elements e*P .. e*P+P-1 of the rows of `pitch`
+// elements, ws[((n*Ho + ho)*Wi + w)*pitch + kh*Ci + c] = x[n][ho*sh + kh][w][c]
+// and zero from Hf*Ci on. pitch is a multiple of P.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_nhwc_pad_kernel(const T* __restrict__ x,
+                                                            uint4* __restrict__ ws, ConvShape c,
+                                                            int pitch, int64_t total)
+{
+    constexpr int P = 16 / (int)sizeof(T);
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= total) return;
+    const int64_t run = e * P / pitch;
+    const int j0 = (int)(e * P - run * pitch);
+    const int w = (int)(run % c.Wi);
+    const int64_t r = run / c.Wi;
+    const int ho = (int)(r % c.Ho);
+    const int64_t n = r / c.Ho;
+    const int HC = c.Hf * c.Ci;
+    T v[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int j = j0 + i;
+        T t = 0;
+        if (j < HC) {
+            const int kh = j / c.Ci, cc = j - kh * c.Ci;
+            t = x[((n * c.Hi + (int64_t)ho * c.sh + kh) * c.Wi + w) * c.Ci + cc];
+        }
+        v[i] = t;
+    }
+    uint4 o;
+    __builtin_memcpy(&o, v, 16);
+    ws[e] = o;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void filter_khwc_kernel(const T* __restrict__ w,
-                                                          T* __restrict__ wr, ConvShape c)
+                                                          T* __restrict__ wr, ConvShape c,
+                                                          int pitch)
 {
-    const int64_t K = (int64_t)c.Wf * c.Hf * c.Ci;
+    const int64_t K = (int64_t)c.Wf * pitch;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= (int64_t)c.Co * K) return;
     const int co = (int)(e / K);
-    int k = (int)(e - (int64_t)co * K);
-    const int ci = k % c.Ci;
-    k /= c.Ci;
-    const int kh = k % c.Hf, kw = k / c.Hf;
-    wr[e] = w[(((int64_t)co * c.Ci + ci) * c.Hf + kh) * c.Wf + kw];
+    const int k = (int)(e - (int64_t)co * K);
+    const int kw = k / pitch, j = k - kw * pitch;
+    T t = 0;
+    if (j < c.Hf * c.Ci) {
+        const int kh = j / c.Ci, ci = j - kh * c.Ci;
+        t = w[(((int64_t)co * c.Ci + ci) * c.Hf + kh) * c.Wf + kw];
+    }
+    wr[e] = t;
 }
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
@@ -115,17 +158,42 @@ int launch_pack_nhwc(const void* x, void* ws, const ConvShape& c, int elem, hipS
     return launch_status();
 }
 
+int nhwc_pitch(const ConvShape& c, int elem)
+{
+    const int q = 32 / elem;
+    return (c.Hf * c.Ci + q - 1) / q * q;
+}
+
+int launch_pack_nhwc_padded(const void* x, void* ws, const ConvShape& c, int elem,
+                            hipStream_t stream)
+{
+    const int pitch = nhwc_pitch(c, elem);
+    if (pitch == c.Hf * c.Ci) return launch_pack_nhwc(x, ws, c, elem, stream);
+    if ((uintptr_t)ws % 16 != 0) return -1;
+    const int64_t total = (int64_t)c.N * c.Ho * c.Wi * pitch * elem / 16;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks <= 0 || blocks > 0x7fffffff) return -1;
+    if (elem == 2)
+        hipLaunchKernelGGL(pack_nhwc_pad_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0,
+                           stream, (const uint16_t*)x, (uint4*)ws, c, pitch, total);
+    else
+        hipLaunchKernelGGL(pack_nhwc_pad_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0,
+                           stream, (const uint32_t*)x, (uint4*)ws, c, pitch, total);
+    return launch_status();
+}
+
 int launch_filter_khwc(const void* w, void* wr, const ConvShape& c, int elem, hipStream_t stream)
 {
-    const int64_t total = (int64_t)c.Co * c.Wf * c.Hf * c.Ci;
+    const int pitch = nhwc_pitch(c, elem);
+    const int64_t total = (int64_t)c.Co * c.Wf * pitch;
     const int64_t blocks = (total + 255) / 256;
     if (blocks <= 0 || blocks > 0x7fffffff) return -1;
     if (elem == 2)
         hipLaunchKernelGGL(filter_khwc_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           (const uint16_t*)w, (uint16_t*)wr, c);
+                           (const uint16_t*)w, (uint16_t*)wr, c, pitch);
     else
         hipLaunchKernelGGL(filter_khwc_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           (const uint32_t*)w, (uint32_t*)wr, c);
+                           (const uint32_t*)w, (uint32_t*)wr, c, pitch);
     return launch_status();
 }
 

@@ -288,6 +288,11 @@ def test_nhwc_workspace_bytes():
         fb + m.workspace_bytes(64, 64, 224, 224, 7, 7, 2, 2)
     assert m.nhwc_workspace_bytes(64, 64, 224, 224, 64, 7, 7, 2, 2, materialize=False) == 0
     assert m.nhwc_workspace_bytes(1, 3, 4, 4, 2, 5, 5, 1, 2) == 0
+    # Ci = 3, Hf = 11: each column's 33-element run padded to 32 bytes, 40
+    # floats or 48 halves, in the filter rows and the tensor (Ho = 10).
+    for e, pitch in ((4, 40), (2, 48)):
+        fb = -(-37 * 11 * pitch * e // 256) * 256
+        assert m.nhwc_workspace_bytes(2, 3, 47, 45, 37, 11, 11, 4, e) == fb + 2 * 10 * 45 * pitch * e
 
 
 def test_nhwc_fused_workspace_bytes():

@@ -11,8 +11,10 @@ from parity import TOL, assert_exact, assert_within, device, note, to_dev
 
 pytestmark = pytest.mark.gpu
 
-# (N, Ci, Hi, Wi, Co, Hf, Wf, s): Ci a multiple of 16 (matrix-core path in
-# both precisions), of 8 only (fp32 matrix cores, fp16 direct), and neither.
+# (N, Ci, Hi, Wi, Co, Hf, Wf, s): Ci a multiple of 16 (window runs unpadded
+# in both precisions), of 8 only (unpadded in fp32, padded in fp16), and
+# neither (runs padded to 32 bytes in both: Hf*Ci = 33 -> 40 floats or 48
+# halves; 15 -> 16 in both).
 SHAPES = [
     (2, 16, 19, 23, 40, 3, 5, 2),
     (1, 32, 14, 14, 70, 5, 5, 1),
@@ -20,6 +22,7 @@ SHAPES = [
     (3, 8, 17, 21, 33, 4, 3, (3, 1)),
     (2, 3, 47, 45, 37, 11, 11, 4),
     (1, 96, 12, 12, 256, 5, 5, (1, 2)),
+    (2, 5, 13, 17, 20, 3, 2, (2, 1)),
 ]
 
 
@@ -94,22 +97,76 @@ def test_conv_nhwc_special_values(dt, orc):
     assert np.array_equal(np.isneginf(y), np.isneginf(ref))
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("t", [SHAPES[4], SHAPES[6], SHAPES[3]], ids=str)
+def test_conv_nhwc_padded_workspace_bits(t, dt, orc):
+    """After a materialised call over the whole batch the workspace holds
+    the filter rows and the im2win tensor with each column's Hf*Ci run padded
+    with zeros to the pitch (Hf*Ci rounded up to 32 bytes): stripped of the
+    padding, they are the oracle's NHWC transform and the filter in window
+    order, bit for bit."""
+    import torch
+    dev = device()
+    sh = _shape(t, dt)
+    N, Ci, Hi, Wi, Co, Hf, Wf = sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf
+    e = sh.elem_bytes
+    x, w = workloads.make_inputs(sh, seed=64, mode="int")
+    Ho, _ = m.output_dims(Hi, Wi, Hf, Wf, sh.s)
+    HC = Hf * Ci
+    q = 32 // e
+    pitch = -(-HC // q) * q
+    fb = -(-Co * Wf * pitch * e // 256) * 256
+    nb = m.nhwc_workspace_bytes(N, Ci, Hi, Wi, Co, Hf, Wf, sh.s, e)
+    assert nb == fb + N * Ho * Wi * pitch * e
+    ws = torch.full((nb,), 0x5A, dtype=torch.uint8, device=dev)
+    note(f"nhwc padded workspace {sh.describe()}")
+    y = m.conv2d_nhwc(to_dev(_nhwc(x), dev), to_dev(w, dev), sh.s, ws=ws).cpu().numpy()
+    assert_exact(np.ascontiguousarray(y.transpose(0, 3, 1, 2)), orc.conv_direct(x, w, sh.s),
+                 sh.describe())
+    ut = np.uint16 if e == 2 else np.uint32
+    b = ws.cpu().numpy()
+    wr = b[:Co * Wf * pitch * e].view(ut).reshape(Co, Wf, pitch)
+    t_ = b[fb:].view(ut).reshape(N, Ho, Wi, pitch)
+    xw = np.ascontiguousarray(w.transpose(0, 3, 2, 1)).view(ut).reshape(Co, Wf, HC)
+    pk = orc.im2win_pack_nhwc(_nhwc(x).view(ut), Hf, Wf, sh.s).reshape(N, Ho, Wi, HC)
+    assert np.array_equal(wr[..., :HC], xw) and not wr[..., HC:].any()
+    assert np.array_equal(t_[..., :HC], pk) and not t_[..., HC:].any()
+    torch.cuda.synchronize()
+
+
+NHWC_FULL = ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64", "cv4_f16_n64",
+             "cv2_f32_n32"]
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("key", ["cv4_f16_n64", "cv5_f16_n128"])
-def test_conv_nhwc_full_size_sampled(key, orc):
+@pytest.mark.parametrize("key", NHWC_FULL)
+def test_conv_nhwc_full_size_every_output(key, orc):
+    """The benchmark layers in NHWC at full size, as bench.py times them:
+    materialised over the whole batch (window runs padded for the Ci = 3
+    layers), and for cv5 fp16 the fused kernel with a prepacked filter.
+    Every output against the oracle on small-integer inputs (exact), into an
+    output pre-filled with NaN."""
     import torch
     dev = device()
     sh = workloads.BY_KEY[key]
     x, w = workloads.make_inputs(sh, seed=1, mode="int")
-    Ho, Wo = m.output_dims(sh.Hi, sh.Wi, sh.Hf, sh.Wf, sh.s)
-    idx = workloads.sample_output_indices(sh, Ho, Wo, 2000)
-    ref, _ = orc.conv_points(x, w, sh.s, idx)
+    note(f"nhwc full size {sh.describe()}: oracle")
+    ref = np.ascontiguousarray(orc.conv_direct(x, w, sh.s).transpose(0, 2, 3, 1))
+    xt, wt = to_dev(_nhwc(x), dev), to_dev(w, dev)
+    y = torch.full(ref.shape, float("nan"), dtype=torch.float32, device=dev)
     nb = m.nhwc_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
     ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-    note(f"conv nhwc full {sh.describe()}")
-    y = m.conv2d_nhwc(to_dev(_nhwc(x), dev), to_dev(w, dev), sh.s, ws=ws)
-    got = y.permute(0, 3, 1, 2).reshape(-1)[torch.from_numpy(idx).to(dev)].cpu().numpy()
-    assert_exact(got, ref, sh.describe())
+    note(f"conv nhwc materialised full {sh.describe()}")
+    m.conv2d_nhwc(xt, wt, sh.s, ws=ws, out=y)
+    assert_exact(y.cpu().numpy(), ref, f"{sh.describe()} nhwc materialised")
+    del ws
+    if key == "cv5_f16_n128":
+        nb = m.nhwc_fused_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s)
+        fws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        y.fill_(float("nan"))
+        note(f"conv nhwc fused full {sh.describe()}")
+        m.conv2d_nhwc_fused(xt, wt, sh.s, fws=fws, out=y)
+        assert_exact(y.cpu().numpy(), ref, f"{sh.describe()} nhwc fused")
     torch.cuda.synchronize()
 
 
