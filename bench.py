@@ -766,6 +766,9 @@ def main():
                     help="time a plain fill and a device copy of the workload's fp32 output "
                          "size (the write rate an HBM-bound kernel can reach), print one "
                          "JSON line and exit")
+    ap.add_argument("--baseline", choices=["im2col", "direct", "nhwc_materialized", "nhwc_fused"],
+                    help="time only this comparison mode on --workload (for a kernel trace of "
+                         "it), print one JSON line and exit")
     ap.add_argument("--ablation", action="store_true",
                     help="time every layer under the library's variant switches and print a "
                          "Markdown table instead of the JSON line")
@@ -822,6 +825,14 @@ def main():
         print(json.dumps(fill_rate(args.workload, workloads.BY_KEY[args.workload], args.steps,
                                    args.warmup)),
               flush=True)
+        return
+
+    if args.baseline:
+        r = time_layer(workloads.BY_KEY[args.workload], args.baseline, args.steps, args.warmup)
+        print(json.dumps({"workload": args.workload, "mode": args.baseline,
+                          "us_per_call_median": round(r["ms_per_launch_median"] * 1e3, 2),
+                          "us_per_call_min": round(r["ms_per_launch_min"] * 1e3, 2),
+                          "workspace_bytes": r.get("workspace_bytes")}), flush=True)
         return
 
     MEASURED.update(measured_peaks())

@@ -11,15 +11,17 @@
 //    That is the transpose of the usual K x P layout, with the same size; it
 //    makes each MFMA operand slice one contiguous 16-byte load.
 //    A workgroup writes the rows of up to 32 consecutive pixels of one
-//    output row from their input rows staged in LDS; shapes whose rows do not fit fall
-//    back to 128-byte column tiles of 32 rows, one 16-byte piece per thread.
+//    output row from their input rows, copied into LDS by direct dword
+//    loads; shapes whose rows do not fit fall back to 128-byte column tiles
+//    of 32 rows, one 16-byte piece per thread.
 //  * filter_pad_kernel copies the filters into rows of KP (zero tail).
 //  * gemm_tiled_kernel computes y[n][co][p] = sum_k w[co][k] * col[q][k] on
 //    the matrix cores with the same instructions and operand layouts as the
 //    im2win kernels (v_mfma_f32_32x32x16_f16, v_mfma_f32_32x32x2_f32). A
-//    workgroup owns 64 output channels x 256 pixels, each of its 4 waves 64
-//    x 64 (2 x 2 tiles of 32 x 32). A stage is 128 bytes of K of every row
-//    of both operands (64 filter rows + 256 im2col rows = 40 KB), copied
+//    workgroup owns 64 output channels x 256 pixels with 4 waves, or 128
+//    channels x 256 pixels with 8 (Co >= 128), each wave 64 x 64 (2 x 2
+//    tiles of 32 x 32). A stage is 128 bytes of K of every row of both
+//    operands (64 or 128 filter rows + 256 im2col rows = 40 or 48 KB), copied
 //    into LDS with buffer_load_dwordx4 ... lds, eight lanes per row (whole
 //    128-byte lines of the im2col matrix); three stage buffers, loads two
 //    stages ahead, one barrier per stage. The 16-byte pieces of a row are
@@ -126,6 +128,7 @@ __global__ __launch_bounds__(256) void im2col_vec_kernel(const T* __restrict__ x
 }
 
 constexpr int64_t kColLds = 40 * 1024;
+constexpr uint32_t kColMiss = 0xFFFFFFF0u;   // a load offset past any x buffer
 
 struct ColRArgs {
     ConvShape c;
@@ -134,6 +137,7 @@ struct ColRArgs {
     int seg;                  // pixels per row segment
     int wtiles;               // segments per output row
     int units;                // dwords per LDS row (cols * sizeof(T) / 4)
+    int64_t xbytes;           // bytes of x
     FastDiv divCpr, divHW, divWf, divUnits;
 };
 
@@ -162,28 +166,32 @@ __global__ __launch_bounds__(256) void im2col_rows_kernel(const T* __restrict__ 
     const int ncol = min(a.cols, Wi - c0);
 
     // Input rows (ci, ho*sh + kh), columns c0 .. c0 + ncol - 1, copied a
-    // dword at a time (Wi*sizeof(T) and c0*sizeof(T) are multiples of 4),
-    // eight loads in flight per thread. LDS row r = ci*Hf + kh.
-    const uint32_t* xr = reinterpret_cast<const uint32_t*>(
-        x + (((int64_t)n * Ci) * Hi + (int64_t)ho * a.c.sh) * Wi + c0);
-    uint32_t* Xu = reinterpret_cast<uint32_t*>(smem_c);
+    // dword at a time (Wi*sizeof(T) and c0*sizeof(T) are multiples of 4)
+    // straight into LDS by direct loads, all in flight at once: wave v takes
+    // the 64-dword pieces v, v+4, ... of the rows. LDS row r = ci*Hf + kh;
+    // dwords past a row's input columns, and past the last row up to the
+    // whole piece, load zeros (offsets past the buffer).
+    const uint32_t lbase =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem_c;
+    const T* xb = x + (((int64_t)n * Ci) * Hi + (int64_t)ho * a.c.sh) * Wi + c0;
+    const int64_t xoff = (int64_t)(xb - x) * (int64_t)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rx =
+        raw_rsrc(xb, (uint32_t)(a.xbytes - xoff < (int64_t)kColMiss ? a.xbytes - xoff
+                                                                   : (int64_t)kColMiss));
     constexpr int EPU = 4 / sizeof(T);
     const int uw = (ncol + EPU - 1) / EPU;      // dwords of a row to copy
-    const int wu = Wi / EPU;                    // dwords per input row
     const int total_u = Ci * Hf * a.units;
-    for (int e0 = threadIdx.x; e0 < total_u; e0 += 8 * 256) {
-        uint32_t v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int e = e0 + 256 * u;
-            const int r = (int)a.divUnits.div((uint32_t)e), j = e - r * a.units;
-            const int ci = r / Hf, kh = r - ci * Hf;
-            v[u] = e < total_u && j < uw ? xr[((int64_t)ci * Hi + kh) * wu + j] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (e0 + 256 * u < total_u) Xu[e0 + 256 * u] = v[u];
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    for (int pc = wave; pc * 64 < total_u; pc += 4) {
+        const int e = pc * 64 + lane;
+        const int r = (int)a.divUnits.div((uint32_t)e), j = e - r * a.units;
+        const int ci = r / Hf, kh = r - ci * Hf;
+        const uint32_t v = e < total_u && j < uw
+                               ? (uint32_t)((((int64_t)ci * Hi + kh) * Wi) * (int64_t)sizeof(T)) + 4u * j
+                               : kColMiss;
+        lds_dma4(rx, lbase + (uint32_t)pc * 256u, v);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     // Pieces of rows q0 .. q0 + npx - 1: piece e = (pixel e / cpr, piece e % cpr).
@@ -235,44 +243,52 @@ struct GemmArgs {
     int Ho, Wo, Wi, sw, HfC;
 };
 
-constexpr int kTM = 64;                    // output channels per tile
+// Tiles of TM output channels (64: 4 waves; 128: 8 waves, two 64-channel
+// halves) by kTN pixels.
 constexpr int kTN = 256;                   // pixels per tile
 constexpr int kSB = 128;                   // bytes of K per row and stage
 constexpr int kTBufs = 3;                  // stage buffers: loads two stages ahead
-constexpr int kTStage = (kTM + kTN) * kSB;           // 40 KB
-constexpr int kTSlots = kTStage / 1024 / 4;          // 1-KB loads per wave and stage (10)
-constexpr int kTLds = kTBufs * kTStage + 1024;       // + the landing kilobyte of unused loads
+template <int TM> struct TileCfg {
+    static constexpr int kNW = TM / 16;                         // waves
+    static constexpr int kStage = (TM + kTN) * kSB;             // 40 or 48 KB
+    static constexpr int kSlots = kStage / 1024 / kNW;          // 1-KB loads per wave and stage
+    static constexpr int kLds = kTBufs * kStage + 1024;         // + the landing kilobyte
+    static_assert(kStage % (1024 * kNW) == 0, "whole slots per wave");
+};
 constexpr uint32_t kTMiss = 0xFFFFFFF0u;
 
 // Byte offset of row `row`'s 16-byte piece c in a stage region (pieces
 // XOR-swizzled by the row's low 3 bits).
 __device__ __forceinline__ uint32_t tpos(int row, int c) { return row * kSB + ((c ^ (row & 7)) << 4); }
 
-template <bool F16>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(const void* __restrict__ colv,
-                                                         const void* __restrict__ wv,
-                                                         float* __restrict__ y, GemmArgs a)
+template <bool F16, int TM>
+__global__ __launch_bounds__(TM * 4) void gemm_tiled_kernel(const void* __restrict__ colv,
+                                                            const void* __restrict__ wv,
+                                                            float* __restrict__ y, GemmArgs a)
 {
     constexpr int E = F16 ? 2 : 4;
+    constexpr int kTM = TM, kNW = TileCfg<TM>::kNW, kTStage = TileCfg<TM>::kStage;
+    constexpr int kTSlots = TileCfg<TM>::kSlots;
     extern __shared__ __align__(16) unsigned char smem[];
     const uint32_t lbase =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     const int lane = threadIdx.x & 63, hl = lane >> 5, l32 = lane & 31;
     const int wave = uniform(threadIdx.x >> 6);
+    const int wc = wave >> 2, wp = wave & 3;   // 64-channel half, 64-pixel quarter
     const int co_tiles = (a.Co + kTM - 1) / kTM;
     const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, true);
     const int co0 = (int)(bid % co_tiles) * kTM;
     const int64_t q0 = (bid / co_tiles) * kTN;
 
     // Load slots: slot m of a stage is LDS kilobyte m = rows 8m .. 8m+7 of
-    // the stage region (filter rows 0-63 in kilobytes 0-7, im2col rows 0-255
-    // in kilobytes 8-39); wave v issues slots v, v+4, ... Lane l loads row
-    // 8m + l/8, its piece (l%8) ^ (l/8) to land at piece l%8 of the swizzle.
+    // the stage region (filter rows 0 .. TM-1 first, then im2col rows
+    // 0-255); wave v issues slots v, v+NW, ... Lane l loads row 8m + l/8,
+    // its piece (l%8) ^ (l/8) to land at piece l%8 of the swizzle.
     uint32_t voff[kTSlots];
     bool isw[kTSlots];
 #pragma unroll
     for (int i = 0; i < kTSlots; ++i) {
-        const int m = wave + 4 * i;
+        const int m = wave + kNW * i;
         const int row = 8 * m + (lane >> 3);
         const int pc = (lane & 7) ^ (lane >> 3);
         uint32_t v = kTMiss;
@@ -307,7 +323,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const void* __restrict_
         const uint32_t base = lbase + (uint32_t)sb * kTStage;
 #pragma unroll
         for (int i = 0; i < kTSlots; ++i)
-            lds_dma16(isw[i] ? rw : rc, base + (uint32_t)(wave + 4 * i) * 1024, voff[i]);
+            lds_dma16(isw[i] ? rw : rc, base + (uint32_t)(wave + kNW * i) * 1024, voff[i]);
     };
     auto issue_none = [&]() {
         const __amdgpu_buffer_rsrc_t rc = raw_rsrc(colv, 0u);
@@ -323,14 +339,14 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const void* __restrict_
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // A: filter rows i*32 + l32; B: im2col rows kTM + 64*wave + 32*j + l32.
+    // A: filter rows 64*wc + i*32 + l32; B: im2col rows kTM + 64*wp + 32*j + l32.
     // Slice t (32 bytes of K) of a stage: lane half hl reads piece 2t + hl.
     auto slice = [&](const unsigned char* S, int t) {
         uint4 A[2], B[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            __builtin_memcpy(&A[i], S + tpos(i * 32 + l32, 2 * t + hl), 16);
-            __builtin_memcpy(&B[i], S + tpos(kTM + 64 * wave + 32 * i + l32, 2 * t + hl), 16);
+            __builtin_memcpy(&A[i], S + tpos(64 * wc + i * 32 + l32, 2 * t + hl), 16);
+            __builtin_memcpy(&B[i], S + tpos(kTM + 64 * wp + 32 * i + l32, 2 * t + hl), 16);
         }
         if constexpr (F16) {
             half8_t ah[2], bh[2];
@@ -388,7 +404,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const void* __restrict_
     const __amdgpu_buffer_rsrc_t ry = gbuf(y, a.ybytes);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int64_t q = q0 + 64 * wave + j * 32 + l32;
+        const int64_t q = q0 + 64 * wp + j * 32 + l32;
         if (q >= a.rows) continue;
         const int64_t n = q / a.P;
         const int p = (int)(q - n * a.P);
@@ -396,7 +412,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const void* __restrict_
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int co = co0 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                const int co = co0 + 64 * wc + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
                 const int64_t off = a.y_nhwc ? q * a.Co + co : (n * a.Co + co) * a.P + p;
                 if (co < a.Co)
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ry,
@@ -411,16 +427,26 @@ int launch_gemm(const void* b, const void* a, float* y, const GemmArgs& g, int C
     // 32-bit buffer offsets: the chunk's matrix and output below 4 GiB.
     if (g.colbytes >= 0xFFFFFFF0ull || g.ybytes >= 0xFFFFFFF0ull || g.wbytes >= 0xFFFFFFF0ull)
         return -1;
-    const int64_t blocks = ((g.rows + kTN - 1) / kTN) * ((Co + kTM - 1) / kTM);
+    // 128-channel tiles (8 waves, two per SIMD) when the channels fill a
+    // whole one and the tiles still cover the 256 CUs: half the passes over
+    // the matrix (cv5 fp16: 217 against 270 us per im2col call). With 96
+    // channels either tile wastes a quarter, and the 64-channel one ran
+    // faster; a small batch (cv5 fp32, N = 1: 4 tiles of 128) needs the
+    // 64-channel tiles' parallelism.
+    const int64_t ptiles = (g.rows + kTN - 1) / kTN;
+    const int TM = Co >= 128 && ptiles * ((Co + 127) / 128) >= 256 ? 128 : 64;
+    const int64_t blocks = ptiles * ((Co + TM - 1) / TM);
     if (blocks <= 0 || blocks > 0x7fffffff) return -1;
+    auto go = [&](auto kern, int tm, int lds) {
+        ensure_lds_limit((const void*)kern, lds);
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(tm * 4), lds, stream, b, a, y, g);
+    };
     if (elem == 2) {
-        ensure_lds_limit((const void*)gemm_tiled_kernel<true>, kTLds);
-        hipLaunchKernelGGL(gemm_tiled_kernel<true>, dim3((unsigned)blocks), dim3(256), kTLds,
-                           stream, b, a, y, g);
+        if (TM == 128) go(gemm_tiled_kernel<true, 128>, 128, TileCfg<128>::kLds);
+        else go(gemm_tiled_kernel<true, 64>, 64, TileCfg<64>::kLds);
     } else {
-        ensure_lds_limit((const void*)gemm_tiled_kernel<false>, kTLds);
-        hipLaunchKernelGGL(gemm_tiled_kernel<false>, dim3((unsigned)blocks), dim3(256), kTLds,
-                           stream, b, a, y, g);
+        if (TM == 128) go(gemm_tiled_kernel<false, 128>, 128, TileCfg<128>::kLds);
+        else go(gemm_tiled_kernel<false, 64>, 64, TileCfg<64>::kLds);
     }
     return launch_status();
 }
@@ -461,7 +487,8 @@ int launch_im2col(const void* x, void* col, const ConvShape& c, int elem, hipStr
         for (int seg : {32, 16, 8}) {
             r.seg = seg;
             r.cols = (std::min((seg - 1) * c.sw + c.Wf, c.Wi) + epu - 1) / epu * epu;
-            lds = (int64_t)c.Ci * c.Hf * r.cols * elem;
+            // Whole 256-byte pieces: the direct loads fill the last one.
+            lds = ((int64_t)c.Ci * c.Hf * r.cols * elem + 255) / 256 * 256;
             if (lds <= kColLds) break;
         }
         r.units = r.cols / epu;
@@ -469,6 +496,7 @@ int launch_im2col(const void* x, void* col, const ConvShape& c, int elem, hipStr
         const int64_t rblocks = (int64_t)c.N * c.Ho * r.wtiles;
         if (lds <= 80 * 1024 && rblocks < 0x7fffffff && (uintptr_t)col % 16 == 0 &&
             c.Wi % epu == 0 && (uintptr_t)x % 4 == 0) {
+            r.xbytes = (int64_t)c.N * c.Ci * c.Hi * c.Wi * elem;
             r.divUnits = FastDiv((uint32_t)r.units);
             r.divCpr = FastDiv((uint32_t)cpr);
             r.divHW = FastDiv((uint32_t)(c.Hf * c.Wf));
