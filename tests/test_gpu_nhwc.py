@@ -134,6 +134,31 @@ def test_conv_nhwc_padded_workspace_bits(t, dt, orc):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("t", [SHAPES[0], SHAPES[4]], ids=str)
+def test_conv_nhwc_materialised_x_at_element_offset(t, dt, orc):
+    """x one element past a 16-byte boundary: the pack reads element by
+    element (unpadded runs, Ci = 16, and padded ones, Ci = 3) and the GEMM
+    runs on the packed tensor as for aligned x. Exact on integers."""
+    import torch
+    dev = device()
+    sh = _shape(t, dt)
+    xi, wi = workloads.make_inputs(sh, seed=65, mode="int")
+    xn = _nhwc(xi)
+    buf = torch.empty(xn.size + 1, dtype=torch.float16 if dt == "f16" else torch.float32,
+                      device=dev)
+    x_off = buf[1:].view(xn.shape)
+    x_off.copy_(to_dev(xn, dev))
+    assert x_off.data_ptr() % 16 != 0
+    nb = m.nhwc_workspace_bytes(sh.N, sh.Ci, sh.Hi, sh.Wi, sh.Co, sh.Hf, sh.Wf, sh.s, sh.elem_bytes)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    note(f"conv nhwc materialised, x at an element offset {sh.describe()}")
+    y = m.conv2d_nhwc(x_off, to_dev(wi, dev), sh.s, ws=ws).cpu().numpy()
+    assert_exact(np.ascontiguousarray(y.transpose(0, 3, 1, 2)), orc.conv_direct(xi, wi, sh.s),
+                 f"{sh.describe()} x offset")
+    torch.cuda.synchronize()
+
+
 NHWC_FULL = ["cv5_f32_n1", "cv1_f32_n32", "cv5_f16_n128", "cv3_f16_n64", "cv4_f16_n64",
              "cv2_f32_n32"]
 
