@@ -70,20 +70,6 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds
         : "memory");
 }
 
-// The same, one dword per lane (lane l lands at lds + 4*l).
-__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff)
-{
-    uint32_t save;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dword %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save)
-        : "s"(lds), "v"(voff), "s"(r)
-        : "memory");
-}
-
 // Waits until at most N of this wave's vector loads are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm()

@@ -127,6 +127,21 @@ __global__ __launch_bounds__(256) void im2col_vec_kernel(const T* __restrict__ x
     reinterpret_cast<uint4*>(col)[(int64_t)q * a.cpr + piece] = o;
 }
 
+// A direct global-to-LDS load of one dword per lane: lane l's dword at
+// voff in r lands at LDS byte lds + 4*l (zero for an offset past r).
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff)
+{
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
+}
+
 constexpr int64_t kColLds = 40 * 1024;
 constexpr uint32_t kColMiss = 0xFFFFFFF0u;   // a load offset past any x buffer
 
