@@ -23,8 +23,9 @@
 //    tiles of 32 x 32). A stage is 128 bytes of K of every row of both
 //    operands (64 or 128 filter rows + 256 im2col rows = 40 or 48 KB), copied
 //    into LDS with buffer_load_dwordx4 ... lds, eight lanes per row (whole
-//    128-byte lines of the im2col matrix); three stage buffers, loads two
-//    stages ahead, one barrier per stage. The 16-byte pieces of a row are
+//    128-byte lines of the im2col matrix); two stage buffers (80 KB for the
+//    64-channel tile: two workgroups per CU), loads one stage ahead, one
+//    barrier per stage. The 16-byte pieces of a row are
 //    stored XOR-swizzled by the row's low 3 bits, so the 8 lanes of a read
 //    group (8 rows, one piece) hit all banks.
 #include <algorithm>
@@ -262,12 +263,12 @@ struct GemmArgs {
 // halves) by kTN pixels.
 constexpr int kTN = 256;                   // pixels per tile
 constexpr int kSB = 128;                   // bytes of K per row and stage
-constexpr int kTBufs = 3;                  // stage buffers: loads two stages ahead
+constexpr int kTBufs = 2;                  // stage buffers: loads one stage ahead
 template <int TM> struct TileCfg {
     static constexpr int kNW = TM / 16;                         // waves
     static constexpr int kStage = (TM + kTN) * kSB;             // 40 or 48 KB
     static constexpr int kSlots = kStage / 1024 / kNW;          // 1-KB loads per wave and stage
-    static constexpr int kLds = kTBufs * kStage + 1024;         // + the landing kilobyte
+    static constexpr int kLds = kTBufs * kStage;               // 80 or 96 KB
     static_assert(kStage % (1024 * kNW) == 0, "whole slots per wave");
 };
 constexpr uint32_t kTMiss = 0xFFFFFFF0u;
@@ -340,11 +341,6 @@ __global__ __launch_bounds__(TM * 4) void gemm_tiled_kernel(const void* __restri
         for (int i = 0; i < kTSlots; ++i)
             lds_dma16(isw[i] ? rw : rc, base + (uint32_t)(wave + kNW * i) * 1024, voff[i]);
     };
-    auto issue_none = [&]() {
-        const __amdgpu_buffer_rsrc_t rc = raw_rsrc(colv, 0u);
-#pragma unroll
-        for (int i = 0; i < kTSlots; ++i) lds_dma16(rc, lbase + kTBufs * kTStage, kTMiss);
-    };
 
     floatx16_t acc[2][2];
 #pragma unroll
@@ -398,11 +394,10 @@ __global__ __launch_bounds__(TM * 4) void gemm_tiled_kernel(const void* __restri
     };
 
     issue(0, 0);
-    if (NS > 1) issue(1, 1); else issue_none();
     for (int s = 0; s < NS; ++s) {
-        wait_vm<kTSlots>();   // this wave's loads of stage s have landed
+        wait_vm<0>();         // this wave's loads of stage s have landed
         __syncthreads();      // every wave's; and stage s-1's buffer is free
-        if (s + 2 < NS) issue(s + 2, (s + 2) % kTBufs); else issue_none();
+        if (s + 1 < NS) issue(s + 1, (s + 1) % kTBufs);
         const unsigned char* S = smem + (size_t)(s % kTBufs) * kTStage;
         const int ns = min(kSB, nbytes - s * kSB) / 32;   // 32-byte slices in this stage
         if (ns == kSB / 32) {
